@@ -1,0 +1,49 @@
+"""CPU oracle for scale-only fake-quant MoE grouped GEMM -- TEST INFRASTRUCTURE ONLY.
+
+A plain, slow, obviously-correct NumPy implementation of what the HIP path
+computes. Only the test suite, the smoke check and the benchmark's CPU-baseline
+leg may import it; the product path (``moe_fake_quant_amd``) never does, and
+this package imports nothing from it. The two share only the seeded input
+generators in ``workloads``, which hold none of the method's arithmetic.
+
+Sources (cited by page title and section):
+  * "AngelSlim mcore_qad" article (hnwysp.cn news 88453): frozen BF16 weights,
+    fake-quant (quantize->dequantize) of weights and activations, only the
+    quantizer scales trainable (section 一); weights fake-quantized through a
+    parametrization and inputs through a forward pre-hook, gradient reaching
+    the scales by autograd (section 二.3); each MoE layer's experts stacked into
+    one 3D tensor, fake-quantized as a whole, then one grouped GEMM (section
+    二.4); the formats nvfp4 / fp8 / w4a16 / w8a8 (section 三).
+  * "QAT + DeepSpeed ZeRO-3" page of the AngelSlim docs: the PTQ weight scale
+    max|W|/448 (section "Quantizer 初始值"), fake_quant casting its output back
+    to the input dtype and F.linear on bf16 operands (section "Quantizer 的变更"),
+    learnable flags weight_scale true / act_scale false (example yaml).
+  * msmodelslim multi-card quantisation page: observers keep per-channel
+    min / max and turn them into quantisation parameters (FA3 observer section).
+  * Format grids: OCP Microscaling Formats spec v1.0 (E4M3, E2M1) -- the
+    definitions the spec formats name; the pages give no bit layouts.
+
+Every point the pages leave open is a numbered reading (R-1 ... R-18) listed in
+the design doc; the code names the reading where it applies.
+
+Parity status: every function here is pinned by the ``-m "not gpu"`` tests
+(exhaustive code grids, tie tables, library special cases, closed forms,
+brute force, an independent torch-autograd derivation of the STE gradients),
+except SwiGLU's exp and the routing generator, which are compared by
+tolerance only ("parity unpinned" beyond the stated tolerances).
+"""
+from .numerics import bf16_to_f32, f32_to_bf16, f64_to_bf16  # noqa: F401
+from .codecs import (  # noqa: F401
+    FMT_NONE, FMT_INT8, FMT_INT4, FMT_FP8, FMT_NVFP4, FMT_NAMES,
+    E4M3_POS, E2M1_POS, E4M3_MAX, E2M1_MAX,
+    e4m3_round, e2m1_round, e4m3_value_of_code, e2m1_value_of_code,
+    fq_int8, fq_int4, fq_fp8, fq_nvfp4, fq_nvfp4_act_dynamic,
+    fq_weight_stack, fq_act,
+)
+from .observer import observer_weight, observer_act  # noqa: F401
+from .permute import moe_permute  # noqa: F401
+from .gemm import grouped_gemm_fwd, grouped_gemm_bwd  # noqa: F401
+from .moe import (  # noqa: F401
+    gather_actfq, swiglu_fwd, swiglu_actfq, swiglu_bwd, combine, combine_bwd,
+    unpermute_reduce, moe_layer,
+)

@@ -1,0 +1,155 @@
+"""The routed-expert path of one MoE layer, forward and scale-only backward
+(test infrastructure only).
+
+Structure: the experts of a layer are one gate_up stack [E, 2F, H] and one
+down stack [E, H, F] (mcore_qad article, section 二.4); inputs of each
+projection are fake-quantised before the matmul (section 二.3); the activation
+between them is SwiGLU (the experts' act_fn, QAT + ZeRO-3 page, architecture
+notes on fused MoE experts). The router is unquantised and outside the path
+(section 二.3): expert ids and routing weights are inputs (R-11, R-12).
+
+Forward, per routed row r of expert e (token t = perm[r] // k):
+  Xq[r] = FQ_a1(X[t])                                   gather + act FQ
+  H     = Xq . FQ(W_gu[e])^T                            bf16
+  A     = bf16(silu(H[:, :F]) * H[:, F:])               gate first (R-10)
+  Aq    = FQ_a2(A)
+  O     = Aq . FQ(W_d[e])^T                             bf16
+  out[t] = bf16(sum_j p[t,j] * O[row_of[t,j]])           slots ascending
+Backward (dX and the weight-scale gradients only; activation scales frozen):
+  dO[r]  = bf16(p[t,j] * dOut[t])
+  dA     = bf16(m_a2 * (dO . FQ(W_d[e])))               + dS_d from dO^T . Aq
+  dH     = bf16(SwiGLU'(H) applied to dA)
+  dXq    = bf16(dH . FQ(W_gu[e]))                       + dS_gu from dH^T . Xq
+  dX[t]  = bf16(m_a1(X[t]) * sum_j dXq[row_of[t,j]])
+Float64 everywhere except where the GPU stores bf16.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from .codecs import FMT_NONE, fq_act
+from .gemm import grouped_gemm_bwd, grouped_gemm_fwd
+from .numerics import bf16_to_f32, f64_to_bf16
+from .observer import observer_act, observer_weight
+from .permute import moe_permute
+
+
+def gather_actfq(x_bits, perm, topk: int, afmt: int, act_scale):
+    """Xq[r] = FQ_a(X[perm[r] // topk]). Returns the FQ record of the gathered rows."""
+    tok = np.asarray(perm, dtype=np.int64) // topk
+    return fq_act(np.asarray(x_bits)[tok], afmt, act_scale)
+
+
+def _sigmoid(g):
+    return 1.0 / (1.0 + np.exp(-g))
+
+
+def swiglu_fwd(h_bits):
+    """A = bf16(silu(gate) * up), gate = H[:, :F], up = H[:, F:] (R-10)."""
+    h = bf16_to_f32(h_bits).astype(np.float64)
+    F = h.shape[1] // 2
+    g, u = h[:, :F], h[:, F:]
+    return f64_to_bf16(g * _sigmoid(g) * u)
+
+
+def swiglu_actfq(h_bits, afmt: int, act_scale):
+    a = swiglu_fwd(h_bits)
+    return a, fq_act(a, afmt, act_scale)
+
+
+def swiglu_bwd(dq_bits, h_bits, afmt: int, act_scale, a_bits=None):
+    """dH from dAq (the unmasked dgrad of the down projection).
+
+    dA = m_a2 * dAq, m_a2 the activation-FQ mask of A (recomputed from H, or from
+    ``a_bits`` when given); dgate = dA*up*s*(1 + g*(1-s)), dup = dA*g*s, s = sigmoid(g).
+    """
+    h = bf16_to_f32(h_bits).astype(np.float64)
+    F = h.shape[1] // 2
+    g, u = h[:, :F], h[:, F:]
+    if a_bits is None:
+        a_bits = swiglu_fwd(h_bits)
+    m = fq_act(a_bits, afmt, act_scale).mask if afmt != FMT_NONE else 1.0
+    da = bf16_to_f32(dq_bits).astype(np.float64) * m
+    s = _sigmoid(g)
+    dgate = da * u * s * (1.0 + g * (1.0 - s))
+    dup = da * g * s
+    return f64_to_bf16(np.concatenate([dgate, dup], axis=1))
+
+
+def combine(o_bits, probs, row_of):
+    """out[t] = bf16(sum over local slots j of p[t,j] * O[row_of[t,j]])."""
+    o = bf16_to_f32(o_bits).astype(np.float64)
+    row_of = np.asarray(row_of, dtype=np.int64)
+    p = np.asarray(probs, dtype=np.float32).astype(np.float64)
+    T, k = row_of.shape
+    out = np.zeros((T, o.shape[1]), dtype=np.float64)
+    for j in range(k):
+        r = row_of[:, j]
+        ok = r >= 0
+        out[ok] += p[ok, j:j + 1] * o[r[ok]]
+    return f64_to_bf16(out)
+
+
+def combine_bwd(dout_bits, probs, perm, topk: int):
+    """dO[r] = bf16(p[t,j] * dOut[t]) with f = perm[r], t = f // k, j = f % k."""
+    perm = np.asarray(perm, dtype=np.int64)
+    t, j = perm // topk, perm % topk
+    d = bf16_to_f32(dout_bits).astype(np.float64)[t]
+    p = np.asarray(probs, dtype=np.float32).astype(np.float64)[t, j]
+    return f64_to_bf16(d * p[:, None])
+
+
+def unpermute_reduce(dxq_bits, row_of, x_bits, afmt: int, act_scale):
+    """dX[t] = bf16(m_a1(X[t]) * sum over local slots of dXq[row_of[t,j]])."""
+    dxq = bf16_to_f32(dxq_bits).astype(np.float64)
+    row_of = np.asarray(row_of, dtype=np.int64)
+    T, k = row_of.shape
+    acc = np.zeros((T, dxq.shape[1]), dtype=np.float64)
+    for j in range(k):
+        r = row_of[:, j]
+        ok = r >= 0
+        acc[ok] += dxq[r[ok]]
+    m = fq_act(x_bits, afmt, act_scale).mask if afmt != FMT_NONE else 1.0
+    return f64_to_bf16(acc * m)
+
+
+def moe_layer(case, wfmt: int, group: int, afmt: int, wq_gu=None, wq_d=None,
+              act_scales=None):
+    """Full forward + scale-only backward of one MoE layer's routed-expert path.
+
+    wq_gu / wq_d: (scale, zero_point, global_scale) of each stack; observer
+    init when None. act_scales: (s_a1, s_a2); calibrated on this batch when
+    None (s_a1 from X, s_a2 from the calibration A). Returns a dict of every
+    intermediate (bf16 bits unless noted).
+    """
+    E = case.w_gu.shape[0]
+    k = case.expert_ids.shape[1]
+    if wq_gu is None:
+        wq_gu = observer_weight(case.w_gu, wfmt, group)
+    if wq_d is None:
+        wq_d = observer_weight(case.w_d, wfmt, group)
+    perm, row_of, seg = moe_permute(case.expert_ids, case.expert_begin, E)
+    calibrated = act_scales is None
+    if calibrated:
+        s1 = observer_act(case.x, afmt) if afmt != FMT_NONE else np.float32(1.0)
+    else:
+        s1 = act_scales[0]
+    xq = gather_actfq(case.x, perm, k, afmt, s1)
+    h = grouped_gemm_fwd(xq.bits, seg, case.w_gu, wfmt, group, *wq_gu)
+    if calibrated:
+        a_cal = swiglu_fwd(h)
+        s2 = observer_act(a_cal, afmt) if afmt != FMT_NONE else np.float32(1.0)
+    else:
+        s2 = act_scales[1]
+    a, aq = swiglu_actfq(h, afmt, s2)
+    o = grouped_gemm_fwd(aq.bits, seg, case.w_d, wfmt, group, *wq_d)
+    out = combine(o, case.probs, row_of)
+    do = combine_bwd(case.dout, case.probs, perm, k)
+    daq, ds_d, dzp_d = grouped_gemm_bwd(do, aq.bits, seg, case.w_d, wfmt, group, *wq_d)
+    dh = swiglu_bwd(daq, h, afmt, s2, a_bits=a)
+    dxq, ds_gu, dzp_gu = grouped_gemm_bwd(dh, xq.bits, seg, case.w_gu, wfmt, group, *wq_gu)
+    dx = unpermute_reduce(dxq, row_of, case.x, afmt, s1)
+    return dict(perm=perm, row_of=row_of, seg=seg, s_a1=np.float32(s1), s_a2=np.float32(s2),
+                wq_gu=wq_gu, wq_d=wq_d, xq=xq.bits, h=h, a=a, aq=aq.bits, o=o, out=out,
+                do=do, daq=daq, dh=dh, dxq=dxq, dx=dx, ds_gu=ds_gu, ds_d=ds_d,
+                dzp_gu=dzp_gu, dzp_d=dzp_d)

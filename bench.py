@@ -1,0 +1,269 @@
+"""Benchmark of the scale-only fake-quant MoE hot path on one MI355X.
+
+One step = the whole routed-expert path of one MoE layer: the stacked
+fake-quant pass over both weight stacks, permutation, gather + activation FQ,
+gate_up grouped GEMM, SwiGLU + activation FQ, down grouped GEMM, combine, and
+the backward to dX and the weight-scale gradients (dScale) only.
+
+Workload (default): Qwen3-30B-A3B-shaped layer, 128 experts, hidden 2048,
+expert FFN 768, 16384 tokens x top-8, NVFP4 weights and activations,
+synthetic seeded inputs. Inputs are resident in HBM before timing starts.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 4]
+
+Prints one JSON line (rank 0). Per-kernel times are measured with HIP events
+on the launch stream inside the timed region.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+MI355X_BF16_PEAK_TFLOPS = 2500.0     # dense bf16 MFMA
+MI355X_HBM_PEAK_GBS = 8000.0
+FLOPS_PER_ROW = 6 * (2 * 768 * 2048 + 2048 * 768)   # 28,311,552 per routed row (fwd+bwd GEMMs)
+
+# Copy-kernel calibration of the FETCH_SIZE / WRITE_SIZE counters and the
+# counters of the dominant kernel, from the committed profile summaries.
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_nvfp4_moe_c4.json")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", type=int, default=4, choices=[3, 4, 5])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-experts", type=int, default=6)
+    ap.add_argument("--seed", type=int, default=0)
+    return ap.parse_args()
+
+
+class KernelTimer:
+    """HIP events (torch.cuda.Event on the current stream, which is the stream
+    every libfq call is enqueued on) around named ABI calls."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.pending = []
+        self.enabled = False
+
+    def wrap(self, key, fn):
+        def inner(*a, **k):
+            if not self.enabled:
+                return fn(*a, **k)
+            s = self.torch.cuda.Event(enable_timing=True)
+            e = self.torch.cuda.Event(enable_timing=True)
+            s.record()
+            r = fn(*a, **k)
+            e.record()
+            self.pending.append((key(a), s, e))
+            return r
+        return inner
+
+    def collect(self):
+        out = {}
+        for name, s, e in self.pending:
+            out.setdefault(name, []).append(s.elapsed_time(e))
+        self.pending = []
+        return out
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the expert-parallel "
+              "multi-GPU path is a design, not part of this build.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import moe_fake_quant_amd as F
+    import workloads as W
+
+    dev = torch.device("cuda:0")
+    t_gen = time.time()
+    case = W.config(args.config, seed=args.seed)
+    fmt = {3: F.FMT_FP8_E4M3, 4: F.FMT_NVFP4, 5: F.FMT_NVFP4}[args.config]
+    group = None if fmt == F.FMT_FP8_E4M3 else 16
+    bf = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)  # noqa: E731
+    w_gu, w_d = bf(case.w_gu), bf(case.w_d)
+    x = bf(case.x)
+    ids = torch.from_numpy(case.expert_ids).to(dev)
+    probs = torch.from_numpy(case.probs).to(dev)
+    dout = bf(case.dout)
+    t_gen = time.time() - t_gen
+
+    layer = F.MoEFakeQuantLayer(w_gu, w_d, fmt, fmt, case.T, case.topk, case.expert_begin, group)
+    layer.init_weight_scales()
+    layer.calibrate(x, ids)
+    torch.cuda.synchronize()
+    R = int(layer.seg[layer.E].item())
+    E, H, Fh = layer.E, layer.H, layer.F
+
+    # Events around every ABI call the layer makes. Each GEMM call launches one
+    # kernel: fwd -> k_grouped_gemm<FWD>, bwd with dx -> <DGRAD>, bwd with
+    # dscale -> <WGRAD> (dScale epilogue); the FQ pass is one kernel per stack.
+    timer = KernelTimer(torch)
+    import moe_fake_quant_amd.layer as LM
+    keys = {
+        "fq_grouped_gemm_fwd": lambda a: "gemm_fwd",
+        "fq_grouped_gemm_bwd_scale": lambda a: "gemm_dgrad" if a[9] is not None else "gemm_wgrad_dscale",
+        "fq_quantize_stacked": lambda a: "fq_quantize_stacked",
+    }
+    for name in ("fq_quantize_stacked", "fq_moe_permute", "fq_moe_gather_actfq",
+                 "fq_grouped_gemm_fwd", "fq_swiglu_actfq", "fq_moe_combine",
+                 "fq_moe_combine_bwd", "fq_grouped_gemm_bwd_scale", "fq_swiglu_bwd",
+                 "fq_moe_unpermute_reduce"):
+        setattr(LM, name, timer.wrap(keys.get(name, lambda a, n=name: n), getattr(LM, name)))
+
+    for _ in range(args.warmup):
+        layer.step(x, ids, probs, dout)
+    torch.cuda.synchronize()
+
+    # timed region: K whole steps bracketed by device syncs, events on the stream
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    timer.enabled = True
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record()
+    for _ in range(args.steps):
+        layer.step(x, ids, probs, dout)
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    timer.enabled = False
+    ms_step = start.elapsed_time(end) / args.steps
+    per = timer.collect()
+
+    flops_step = FLOPS_PER_ROW * R
+    tflops = flops_step / (ms_step * 1e-3) / 1e12
+    # each GEMM kind runs twice per step (gate_up and down); together
+    # 2*R*(2F*H + H*F) flops
+    kind_flops = 2 * R * (2 * Fh * H + H * Fh)
+    kernels = {}
+    for kind in ("gemm_fwd", "gemm_dgrad", "gemm_wgrad_dscale"):
+        t = per.get(kind, [])
+        ms = sum(t) / args.steps
+        kernels[kind] = {"launches_per_step": len(t) // args.steps, "ms_per_step": round(ms, 4),
+                         "avg_launch_ms": round(sum(t) / max(len(t), 1), 4),
+                         "TFLOP/s": round(kind_flops / (ms * 1e-3) / 1e12, 2)}
+    dom = max(kernels, key=lambda k: kernels[k]["ms_per_step"])
+    achieved = kernels[dom]["TFLOP/s"]
+
+    # FQ pass over both stacks: read bf16 + write bf16 + read the scales
+    nel = E * (2 * Fh * H + H * Fh)
+    if fmt == F.FMT_NVFP4:
+        scale_bytes = (nel // 16) * 4 + 2 * E * 4
+    else:
+        scale_bytes = E * (2 * Fh + H) * 4
+    fq_bytes = nel * 4 + scale_bytes
+    fq_ms = sum(per.get("fq_quantize_stacked", [0.0])) / args.steps
+    fq_gbs = fq_bytes / (fq_ms * 1e-3) / 1e9
+
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        with open(TRAFFIC_FILE) as f:
+            tr = json.load(f)
+        if tr.get("kernel") == dom:
+            traffic = tr.get("bytes_per_launch")
+
+    breakdown = {n: round(sum(v) / args.steps, 4) for n, v in sorted(per.items())}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(case, fmt, group, args.cpu_sample_experts)
+
+    line = {
+        "metric": "MoE fake-quant grouped-GEMM fwd+bwd TFLOP/s; % bf16 MFMA peak; FQ pass GB/s",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": W.CONFIG_NAMES[args.config],
+            "experts": E, "hidden": H, "expert_ffn": Fh, "tokens": case.T, "topk": case.topk,
+            "routed_rows": R, "weight_format": {3: "fp8_e4m3", 4: "nvfp4", 5: "nvfp4"}[args.config],
+            "act_format": {3: "fp8_e4m3", 4: "nvfp4", 5: "nvfp4"}[args.config],
+            "flops_per_step": flops_step,
+        },
+        "pct_bf16_peak": round(100 * tflops / MI355X_BF16_PEAK_TFLOPS, 2),
+        "fq_pass": {"GB/s": round(fq_gbs, 1), "pct_hbm_peak": round(100 * fq_gbs / MI355X_HBM_PEAK_GBS, 2),
+                    "bytes_per_step": fq_bytes, "ms_per_step": round(fq_ms, 4)},
+        "roofline": {
+            "kernel": dom,
+            "bound": "mfma",
+            "achieved": achieved,
+            "peak": MI355X_BF16_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / MI355X_BF16_PEAK_TFLOPS, 4),
+            "traffic": traffic,
+        },
+        "gemm_kernels": kernels,
+        "ms_per_step_by_call": breakdown,
+        "cpu_baseline": cpu,
+        "input_gen_s": round(t_gen, 1),
+        "wall_s_timed": round(wall, 3),
+    }
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline(case, fmt, group, n_experts):
+    """The oracle, untuned, on the host cores: the same layer restricted to the
+    first n_experts experts and their routed rows (a bounded sample)."""
+    import oracle as O
+    import workloads as W
+    E = n_experts
+    sub = W.MoECase(name=case.name, fmt=case.fmt, n_experts_global=case.n_experts_global,
+                    expert_begin=0, w_gu=case.w_gu[:E], w_d=case.w_d[:E], x=case.x,
+                    expert_ids=case.expert_ids, probs=case.probs, dout=case.dout)
+    wfmt = O.FMT_NVFP4 if fmt == 4 else O.FMT_FP8
+    g = 16 if group else None
+    perm, row_of, seg = O.moe_permute(case.expert_ids, 0, E)
+    R = int(seg[-1])
+    cores = len(os.sched_getaffinity(0))
+    t0 = time.perf_counter()
+    if g:
+        O.moe_layer(sub, wfmt, g, wfmt)
+    else:
+        # per-channel scales: group = K of each stack
+        from oracle import moe as M
+        wq_gu = O.observer_weight(sub.w_gu, wfmt, sub.w_gu.shape[2])
+        wq_d = O.observer_weight(sub.w_d, wfmt, sub.w_d.shape[2])
+        s1 = O.observer_act(sub.x, wfmt)
+        xq = M.gather_actfq(sub.x, perm, sub.topk, wfmt, s1)
+        h = O.grouped_gemm_fwd(xq.bits, seg, sub.w_gu, wfmt, sub.w_gu.shape[2], *wq_gu)
+        s2 = O.observer_act(M.swiglu_fwd(h), wfmt)
+        a, aq = M.swiglu_actfq(h, wfmt, s2)
+        o = O.grouped_gemm_fwd(aq.bits, seg, sub.w_d, wfmt, sub.w_d.shape[2], *wq_d)
+        M.combine(o, sub.probs, row_of)
+        do = M.combine_bwd(sub.dout, sub.probs, perm, sub.topk)
+        daq, _, _ = O.grouped_gemm_bwd(do, aq.bits, seg, sub.w_d, wfmt, sub.w_d.shape[2], *wq_d)
+        dh = M.swiglu_bwd(daq, h, wfmt, s2, a_bits=a)
+        dxq, _, _ = O.grouped_gemm_bwd(dh, xq.bits, seg, sub.w_gu, wfmt, sub.w_gu.shape[2], *wq_gu)
+        M.unpermute_reduce(dxq, row_of, sub.x, wfmt, s1)
+    dt = time.perf_counter() - t0
+    flops = FLOPS_PER_ROW * R
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": cores,
+            "kind": "oracle", "seconds": round(dt, 2),
+            "sample": f"experts 0..{E - 1} of the same layer and their {R} routed rows "
+                      f"(full fwd+bwd incl. observer init), {flops / 1e9:.1f} GFLOP"}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,270 @@
+/*
+ * fq.h -- C ABI of libfq: scale-only fake-quant MoE grouped GEMM on gfx950.
+ *
+ * The method (AngelSlim mcore_qad article, hnwysp.cn news 88453):
+ *   section 一   BF16 weights are frozen; the forward fake-quantizes weights
+ *               and activations (quantize -> dequantize); only the quantizer
+ *               scales are trained.
+ *   section 二.3 weights are fake-quantized transparently (parametrization)
+ *               and each linear's input by a forward pre-hook; the gradient
+ *               reaches the scales through autograd; router and output layer
+ *               stay unquantized.
+ *   section 二.4 each MoE layer's experts become one 3D weight stack
+ *               [E, N, K]; the whole stack is fake-quantized in one
+ *               vectorized pass and all experts run as one grouped GEMM.
+ *   section 三   formats nvfp4 (W4A4), fp8 (W8A8), w4a16 (int4), w8a8 (int8).
+ * The QAT + DeepSpeed ZeRO-3 page of the AngelSlim docs fixes that the
+ * fake-quant output is cast back to the input dtype (bf16) and that the
+ * matmul runs on bf16 operands ("Quantizer 的变更"), and that weight scales
+ * are learnable while activation scales are not (example yaml).
+ *
+ * Numerics shared by every entry point (fp32, round-to-nearest-even, no
+ * fused multiply-add in codec arithmetic):
+ *   r = 1/s (one correctly rounded fp32 division per scale), z = x * r,
+ *   c = Q(clamp(z, lo, hi)) on the format's grid (ties to even),
+ *   v = fp32(value(c) * s), output bf16 = RNE(v).
+ *   int8  : symmetric, lo/hi = -128/127, value(c) = c, +0.0 for c = 0.
+ *   int4  : asymmetric, codes 0..15, zp' = clamp(rne(zp), 0, 15),
+ *           value = c - zp', +0.0 for a zero value.
+ *   fp8   : OCP E4M3 (bias 7, max 448, subnormals kept, saturating); the
+ *           sign of z is kept (-0.0 possible).
+ *   nvfp4 : E2M1 values {0, .5, 1, 1.5, 2, 3, 4, 6} in blocks of 16 along K;
+ *           block scale s_b = fp32(E4M3(clamp(theta_b, 0, 448)) * g), with
+ *           theta_b the learnable fp32 block parameter and g an fp32 tensor
+ *           scale (one per expert for weights, one scalar for activations);
+ *           s_b == 0 makes the block +0.0. Activation blocks are dynamic:
+ *           theta_b = E4M3(clamp(amax_b * (1/(6*g)), 0, 448)).
+ * Backward (straight-through estimator): mask m = [lo <= z <= hi] on the
+ * unrounded z (inclusive); dv/dx = m; dv/ds = value(c) - m*z; int4
+ * dv/dzp = -s*(1-m); nvfp4 dv/dtheta = g*[0 <= theta <= 448]*(value(c)-m*z).
+ *
+ * Conventions for every call:
+ *   - Tensor pointers are DEVICE memory owned by the caller (contiguous,
+ *     row-major, 16-byte aligned). bf16 tensors are raw 16-bit storage.
+ *   - The library keeps no state between calls and allocates nothing inside
+ *     a call; scratch memory comes from the caller's workspace (`ws`,
+ *     `ws_bytes`, sized by fq_workspace_bytes). Calls enqueue work on
+ *     `stream` (a hipStream_t; NULL = the default stream) and never
+ *     synchronize it. Row counts of routed tensors are read on the device
+ *     from seg_offsets[E], so no device-to-host copy happens.
+ *   - Host-checkable problems return a status before any launch: NULL
+ *     required pointer, non-positive or unsupported sizes, misalignment,
+ *     an unsupported format, a workspace that is too small. A launch failure
+ *     returns FQ_ERR_HIP. fq_last_error() gives a thread-local message for
+ *     the last non-OK status. On error, outputs are undefined.
+ *   - Device-data preconditions are NOT checked: scales finite and > 0
+ *     (nvfp4 theta >= 0 and g > 0), expert ids valid, seg_offsets
+ *     non-decreasing with seg_offsets[E] <= R_max.
+ *   - Results are deterministic (bitwise reproducible run to run).
+ */
+#ifndef FQ_H
+#define FQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FQ_ABI_VERSION 1
+
+typedef enum {
+  FQ_OK = 0,
+  FQ_ERR_INVALID_ARGUMENT = 1,
+  FQ_ERR_UNSUPPORTED = 2,
+  FQ_ERR_WORKSPACE_TOO_SMALL = 3,
+  FQ_ERR_HIP = 4
+} fq_status;
+
+typedef enum {
+  FQ_FMT_NONE = 0,      /* no fake-quant (identity, mask 1)              */
+  FQ_FMT_INT8 = 1,      /* int8 symmetric                                 */
+  FQ_FMT_INT4 = 2,      /* int4 asymmetric with integer zero point        */
+  FQ_FMT_FP8_E4M3 = 3,  /* OCP FP8 E4M3                                   */
+  FQ_FMT_NVFP4 = 4      /* E2M1 + block-16 E4M3 scale + fp32 tensor scale */
+} fq_format;
+
+/* A stacked weight [E, N, K] (E experts, N output channels, K inputs; K
+ * contiguous). A dense linear is E = 1. */
+typedef struct {
+  int32_t E, N, K;
+} fq_shape;
+
+/* Weight quantizer (learnable scales).
+ *   group       : elements per scale along K. int8 / fp8: K (per output
+ *                 channel) or a divisor of K that is a multiple of 16;
+ *                 int4: 128 (any multiple of 16 dividing K); nvfp4: 16.
+ *   scale       : [E, N, K/group] fp32. nvfp4: the block parameter theta.
+ *   zero_point  : [E, N, K/group] fp32 holding integers; int4 only, else NULL.
+ *   global_scale: [E] fp32 tensor scale g; nvfp4 only, else NULL. */
+typedef struct {
+  int32_t fmt;
+  int32_t group;
+  const float *scale;
+  const float *zero_point;
+  const float *global_scale;
+} fq_weight_q;
+
+/* Activation quantizer (frozen). fmt NONE, FP8_E4M3 (scale = per-tensor
+ * s_a, one device float), NVFP4 (scale = g_a, one device float; block
+ * scales dynamic per 16 elements along K), INT8 (per-tensor s_a). */
+typedef struct {
+  int32_t fmt;
+  const float *scale;
+} fq_act_q;
+
+typedef void *fq_stream; /* hipStream_t */
+
+/* ------------------------------------------------------------------------
+ * observer_absmax_init -- initial scales from observed statistics.
+ * Sources: the PTQ weight scale max|W|/448 (QAT + ZeRO-3 page, "Quantizer
+ * 初始值"); activation scales from a calibration forward (same page,
+ * overview); per-channel min/max turned into quantization parameters
+ * (msmodelslim multi-card page, FA3 observer section).
+ *
+ * per_tensor == 0 (weights): x is a stack [E, N, K] and
+ *   int8 : scale[e,n,g] = amax_g / 127
+ *   fp8  : scale[e,n,g] = amax_g / 448
+ *   int4 : lo = min(0, min_g), hi = max(0, max_g), scale = (hi-lo)/15,
+ *          zero_point = clamp(rne(-lo * (1/scale)), 0, 15)
+ *   nvfp4: global_scale[e] = amax_e / 2688,
+ *          scale[e,n,b] = E4M3(clamp(amax_b * (1/(6*g_e)), 0, 448))
+ * per_tensor == 1 (activations): x is any tensor of E*N*K elements and
+ *   scale[0] = amax / D with D = 448 (fp8), 2688 (nvfp4), 127 (int8).
+ * Each division is one IEEE fp32 division; a zero amax gives scale 1.0.
+ * Outputs (device, caller-owned) are overwritten. ws may be NULL
+ * (needs 0 bytes). Requires K % 8 == 0 and K % group == 0.
+ * ---------------------------------------------------------------------- */
+fq_status observer_absmax_init(const uint16_t *x_bf16, fq_shape shape, int32_t fmt,
+                               int32_t group, int32_t per_tensor, float *scale,
+                               float *zero_point, float *global_scale, void *ws,
+                               size_t ws_bytes, fq_stream stream);
+
+/* ------------------------------------------------------------------------
+ * fq_quantize_stacked -- one vectorized fake-quant pass over a whole
+ * weight stack [E, N, K] (mcore_qad article, section 二.4).
+ *   w_fq_bf16 : [E, N, K] bf16 dequantized values, or NULL.
+ *   codes     : integer codes, or NULL. int8 / fp8: one byte per element
+ *               (int8 two's complement, E4M3 byte); int4 / nvfp4: two
+ *               4-bit codes per byte, even k in the low nibble (int4 codes
+ *               0..15, E2M1 nibble with the sign in bit 3).
+ * At least one output must be non-NULL. Requires K % 8 == 0.
+ * ---------------------------------------------------------------------- */
+fq_status fq_quantize_stacked(const uint16_t *w_bf16, fq_shape shape, const fq_weight_q *q,
+                              uint16_t *w_fq_bf16, uint8_t *codes, fq_stream stream);
+
+/* ------------------------------------------------------------------------
+ * fq_moe_permute -- routed-token permutation for one grouped GEMM over all
+ * local experts (mcore_qad article, section 二.4: one GEMM over routed
+ * tokens needs each expert's rows contiguous).
+ *   expert_ids [T, topk] int32 global expert ids. Pair f = t*topk + j.
+ *   Local pairs have expert in [expert_begin, expert_begin + E_local).
+ *   perm[r]        (r < R): the local pairs sorted by (local expert, f),
+ *                  a stable counting sort; perm has room for T*topk.
+ *   row_of[t, j]   position of pair f in perm, -1 if not local.
+ *   seg_offsets    [E_local + 1]: exclusive prefix sum of per-expert
+ *                  counts; seg_offsets[E_local] = R.
+ * Workspace: fq_workspace_bytes(FQ_OP_PERMUTE, {E_local, 0, 0}, T*topk, 0).
+ * T == 0 is valid (all offsets 0).
+ * ---------------------------------------------------------------------- */
+fq_status fq_moe_permute(const int32_t *expert_ids, int32_t T, int32_t topk,
+                         int32_t expert_begin, int32_t E_local, int32_t *perm,
+                         int32_t *row_of, int32_t *seg_offsets, void *ws, size_t ws_bytes,
+                         fq_stream stream);
+
+/* ------------------------------------------------------------------------
+ * fq_grouped_gemm_fwd -- Y[r, :] = FQ_a(X)[r, :] . FQ_w(W[e])^T for every
+ * routed row r in segment e = [seg_offsets[e], seg_offsets[e+1]), fp32
+ * accumulation on bf16 MFMA, bf16 output (mcore_qad article, sections 二.3
+ * and 二.4).
+ *   x_bf16  [R_max, K] rows in expert order; rows >= seg_offsets[E] are
+ *           ignored and the matching rows of y are left untouched.
+ *   w_bf16  [E, N, K] raw frozen weights with quantizer wq.
+ *   w_fq    NULL, or FQ_w(W) already materialized by fq_quantize_stacked
+ *           with the same quantizer (then w_bf16 is not read). With NULL
+ *           the call materializes it in the workspace.
+ *   aq      activation quantizer applied to x first (NULL = NONE).
+ *   y_bf16  [R_max, N].
+ * Requires N % 256 == 0 and K % 64 == 0 (K % 16 for nvfp4 activations).
+ * Workspace: fq_workspace_bytes(FQ_OP_GEMM_FWD, shape, R_max, wq->fmt | aq->fmt << 8).
+ * ---------------------------------------------------------------------- */
+fq_status fq_grouped_gemm_fwd(const uint16_t *x_bf16, int32_t R_max, const int32_t *seg_offsets,
+                              fq_shape shape, const uint16_t *w_bf16, const uint16_t *w_fq,
+                              const fq_weight_q *wq, const fq_act_q *aq, uint16_t *y_bf16,
+                              void *ws, size_t ws_bytes, fq_stream stream);
+
+/* ------------------------------------------------------------------------
+ * fq_grouped_gemm_bwd_scale -- backward of fq_grouped_gemm_fwd with the
+ * weights frozen: dX and the weight-quantizer gradients only (mcore_qad
+ * article, section 一: only scales train; section 二.3: the gradient flows
+ * to the scale).
+ *   dx    = m_x * (dY_e . FQ_w(W[e]))                     [R_max, K] bf16
+ *   dWq_e = dY_e^T . FQ_a(X)_e                            (never stored)
+ *   dscale[e,n,g]     = sum_{k in g} dWq_e[n,k] * dv/ds(e,n,k)   fp32
+ *   dzero_point[e,n,g]= sum_{k in g} dWq_e[n,k] * dv/dzp(e,n,k)  (int4)
+ * dx, dscale, dzero_point may each be NULL (not computed). dscale is
+ * overwritten (not accumulated); experts without rows get 0. dScale is
+ * reduced in a fixed order (no float atomics).
+ *   dy_bf16 [R_max, N]; x_bf16 [R_max, K] raw (pre activation fake-quant).
+ * Requires N % 64 == 0 and K % 256 == 0.
+ * Workspace: fq_workspace_bytes(FQ_OP_GEMM_BWD, shape, R_max, wq->fmt | aq->fmt << 8).
+ * ---------------------------------------------------------------------- */
+fq_status fq_grouped_gemm_bwd_scale(const uint16_t *dy_bf16, const uint16_t *x_bf16,
+                                    int32_t R_max, const int32_t *seg_offsets, fq_shape shape,
+                                    const uint16_t *w_bf16, const uint16_t *w_fq,
+                                    const fq_weight_q *wq, const fq_act_q *aq,
+                                    uint16_t *dx_bf16, float *dscale, float *dzero_point,
+                                    void *ws, size_t ws_bytes, fq_stream stream);
+
+/* ------------------------------------------------------------------------
+ * MoE-layer elementwise steps around the grouped GEMMs (the routed-expert
+ * path of one layer: gather -> gate_up GEMM -> SwiGLU -> down GEMM ->
+ * combine, and its backward). R = seg_offsets[E] is read on the device
+ * through `n_rows` (= &seg_offsets[E]); rows >= R are not touched.
+ *
+ * fq_moe_gather_actfq: xq[r] = FQ_a(x[perm[r] / topk])   (forward pre-hook
+ *   on the expert input, mcore_qad article section 二.3). x [T, H].
+ * fq_swiglu_actfq: a = bf16(silu(h[:, :F]) * h[:, F:]), aq = FQ_a(a).
+ *   h [R_max, 2F]; a_out may be NULL; aq_out [R_max, F]. The gate half is
+ *   the first F columns. silu(g) = g / (1 + exp(-g)) in fp32.
+ * fq_swiglu_bwd: da = m_a * daq (m_a the activation-FQ mask of a, recomputed
+ *   from h), dh = [da*u*s*(1+g*(1-s)), da*g*s] with s = sigmoid(g).
+ * fq_moe_combine: out[t] = bf16(sum_j p[t,j] * o[row_of[t,j]]) over local
+ *   slots j ascending (fp32); tokens without local slots get 0.
+ * fq_moe_combine_bwd: do[r] = bf16(p[t,j] * dout[t]), f = perm[r] = t*topk+j.
+ * fq_moe_unpermute_reduce: dx[t] = bf16(m_a(x[t]) * sum_j dxq[row_of[t,j]]).
+ * All require H (resp. F) % 16 == 0.
+ * ---------------------------------------------------------------------- */
+fq_status fq_moe_gather_actfq(const uint16_t *x_bf16, int32_t T, int32_t H, const int32_t *perm,
+                              int32_t topk, int32_t R_max, const int32_t *n_rows,
+                              const fq_act_q *aq, uint16_t *xq_bf16, fq_stream stream);
+fq_status fq_swiglu_actfq(const uint16_t *h_bf16, int32_t R_max, const int32_t *n_rows, int32_t F,
+                          const fq_act_q *aq, uint16_t *a_bf16, uint16_t *aq_bf16,
+                          fq_stream stream);
+fq_status fq_swiglu_bwd(const uint16_t *daq_bf16, const uint16_t *h_bf16, int32_t R_max,
+                        const int32_t *n_rows, int32_t F, const fq_act_q *aq, uint16_t *dh_bf16,
+                        fq_stream stream);
+fq_status fq_moe_combine(const uint16_t *o_bf16, const float *probs, const int32_t *row_of,
+                         int32_t T, int32_t topk, int32_t H, uint16_t *out_bf16,
+                         fq_stream stream);
+fq_status fq_moe_combine_bwd(const uint16_t *dout_bf16, const float *probs, const int32_t *perm,
+                             int32_t topk, int32_t H, int32_t R_max, const int32_t *n_rows,
+                             uint16_t *do_bf16, fq_stream stream);
+fq_status fq_moe_unpermute_reduce(const uint16_t *dxq_bf16, const int32_t *row_of,
+                                  const uint16_t *x_bf16, int32_t T, int32_t topk, int32_t H,
+                                  const fq_act_q *aq, uint16_t *dx_bf16, fq_stream stream);
+
+/* Workspace sizing. op: one of FQ_OP_*. fmts = weight fmt | act fmt << 8. */
+#define FQ_OP_PERMUTE 1
+#define FQ_OP_GEMM_FWD 2
+#define FQ_OP_GEMM_BWD 3
+size_t fq_workspace_bytes(int32_t op, fq_shape shape, int32_t R_max, int32_t fmts);
+
+const char *fq_last_error(void);
+int32_t fq_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* FQ_H */

@@ -1,0 +1,63 @@
+"""Build libfq.so (all HIP sources of csrc/) for gfx950 with hipcc, in-tree.
+
+    python -m moe_fake_quant_amd.build          # or build() from Python
+
+The library lands next to this file; the Python binding loads it from there.
+"""
+from __future__ import annotations
+
+import glob
+import os
+import shutil
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+CSRC = os.path.join(HERE, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+LIB = os.path.join(HERE, "libfq.so")
+ARCH = "gfx950"
+
+
+def hipcc() -> str:
+    p = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+    if not os.path.exists(p):
+        raise RuntimeError("hipcc not found (ROCm toolchain required to build libfq)")
+    return p
+
+
+def flags(extra=()):
+    return [
+        f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+        # codec arithmetic is specified without fused multiply-adds
+        "-ffp-contract=off",
+        # no packed fp32 VALU ops (v_pk_*_f32) in generated code
+        "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        f"-I{INCLUDE}", f"-I{CSRC}",
+        *extra,
+    ]
+
+
+def build(verbose: bool = False, extra=()) -> str:
+    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+    tmp = LIB + ".tmp"
+    cmd = [hipcc(), *flags(extra), "-o", tmp, *srcs]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    out = res.stdout + res.stderr
+    # hipcc's host pass does not know the packed-fp32 feature and says so
+    noise = "is not a recognized feature for this target"
+    lines = [ln for ln in out.splitlines() if noise not in ln]
+    if res.returncode != 0:
+        raise RuntimeError("hipcc failed:\n" + "\n".join(lines))
+    if verbose and lines:
+        print("\n".join(lines))
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    build(verbose=True, extra=sys.argv[1:])
+    print(LIB)

@@ -1,0 +1,359 @@
+// The C ABI of libfq: argument checks, workspace carving and launches.
+// Every entry point validates what the host can see before enqueuing
+// anything, launches on the caller's stream and never synchronizes it.
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <string>
+
+#include "internal.hpp"
+
+namespace fq {
+
+static thread_local std::string g_last_error;
+
+void set_error(const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+}
+
+fq_status hip_status(hipError_t e, const char *what) {
+  set_error("%s: HIP error %d (%s)", what, (int)e, hipGetErrorString(e));
+  return FQ_ERR_HIP;
+}
+
+namespace {
+
+constexpr size_t kAlign = 256;
+inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+struct Carver {
+  char *base;
+  size_t used = 0;
+  explicit Carver(void *p) : base(static_cast<char *>(p)) {}
+  template <class T>
+  T *take(size_t bytes) {
+    T *p = reinterpret_cast<T *>(base + used);
+    used += align_up(bytes);
+    return p;
+  }
+};
+
+bool valid_weight_fmt(int f) {
+  return f == FQ_FMT_INT8 || f == FQ_FMT_INT4 || f == FQ_FMT_FP8_E4M3 || f == FQ_FMT_NVFP4;
+}
+bool valid_act_fmt(int f) {
+  return f == FQ_FMT_NONE || f == FQ_FMT_INT8 || f == FQ_FMT_FP8_E4M3 || f == FQ_FMT_NVFP4;
+}
+
+// group sizes the fused dScale epilogue reduces: 16/32/64 inside a sub-tile,
+// multiples of 128 per wave (and across tiles through partials)
+bool group_ok_for_dscale(int g) { return g == 16 || g == 32 || g == 64 || (g % 128 == 0); }
+
+fq_status check_shape(fq_shape s) {
+  FQ_CHECK_ARG(s.E > 0 && s.N > 0 && s.K > 0, "shape must be positive (E=%d N=%d K=%d)", s.E, s.N,
+               s.K);
+  FQ_CHECK_ARG((size_t)s.E * s.N * s.K < (1ull << 32), "stack too large for 32-bit indexing");
+  return FQ_OK;
+}
+
+fq_status check_weight_q(const fq_weight_q *q, fq_shape s, bool need_scales) {
+  FQ_CHECK_ARG(q != nullptr, "weight quantizer is NULL");
+  FQ_CHECK_ARG(valid_weight_fmt(q->fmt), "unsupported weight format %d", q->fmt);
+  FQ_CHECK_ARG(q->group > 0 && s.K % q->group == 0, "group %d must divide K=%d", q->group, s.K);
+  FQ_CHECK_ARG(q->group % 16 == 0, "group %d must be a multiple of 16", q->group);
+  if (q->fmt == FQ_FMT_NVFP4) FQ_CHECK_ARG(q->group == 16, "nvfp4 blocks are 16 elements");
+  if (need_scales) {
+    FQ_CHECK_ARG(q->scale != nullptr, "scale is NULL");
+    if (q->fmt == FQ_FMT_INT4) FQ_CHECK_ARG(q->zero_point != nullptr, "int4 needs zero_point");
+    if (q->fmt == FQ_FMT_NVFP4) FQ_CHECK_ARG(q->global_scale != nullptr, "nvfp4 needs global_scale");
+  }
+  return FQ_OK;
+}
+
+fq_status check_act_q(const fq_act_q *aq, int K) {
+  if (!aq) return FQ_OK;
+  FQ_CHECK_ARG(valid_act_fmt(aq->fmt), "unsupported activation format %d", aq->fmt);
+  if (aq->fmt != FQ_FMT_NONE) {
+    FQ_CHECK_ARG(aq->scale != nullptr, "activation scale is NULL");
+    FQ_CHECK_ARG(K % 16 == 0, "activation fake-quant needs K %% 16 == 0 (K=%d)", K);
+  }
+  return FQ_OK;
+}
+
+inline int act_fmt(const fq_act_q *aq) { return aq ? aq->fmt : FQ_FMT_NONE; }
+inline hipStream_t S(fq_stream s) { return reinterpret_cast<hipStream_t>(s); }
+
+#define FQ_TRY(x)                    \
+  do {                               \
+    fq_status st_ = (x);             \
+    if (st_ != FQ_OK) return st_;    \
+  } while (0)
+
+size_t gemm_ws(int op, fq_shape s, int R_max, int fmts) {
+  int wfmt = fmts & 0xFF, afmt = (fmts >> 8) & 0xFF;
+  size_t b = 0;
+  if (wfmt != FQ_FMT_NONE) b += align_up((size_t)s.E * s.N * s.K * 2);
+  if (afmt != FQ_FMT_NONE) b += align_up((size_t)R_max * s.K * 2);
+  if (op == FQ_OP_GEMM_BWD) b += 2 * align_up((size_t)s.E * s.N * (s.K / 128 + 1) * 4);
+  return b;
+}
+
+}  // namespace
+}  // namespace fq
+
+using namespace fq;
+
+extern "C" {
+
+int32_t fq_abi_version(void) { return FQ_ABI_VERSION; }
+
+const char *fq_last_error(void) { return g_last_error.c_str(); }
+
+size_t fq_workspace_bytes(int32_t op, fq_shape shape, int32_t R_max, int32_t fmts) {
+  if (op == FQ_OP_PERMUTE) return permute_workspace_bytes(shape.E > 0 ? shape.E : 1, R_max);
+  if (op == FQ_OP_GEMM_FWD || op == FQ_OP_GEMM_BWD) return gemm_ws(op, shape, R_max, fmts);
+  return 0;
+}
+
+fq_status observer_absmax_init(const uint16_t *x, fq_shape s, int32_t fmt, int32_t group,
+                               int32_t per_tensor, float *scale, float *zero_point,
+                               float *global_scale, void *ws, size_t ws_bytes, fq_stream stream) {
+  (void)ws;
+  (void)ws_bytes;
+  FQ_TRY(check_shape(s));
+  FQ_CHECK_ARG(x && scale, "x and scale must be non-NULL");
+  FQ_CHECK_ARG(aligned16(x), "x must be 16-byte aligned");
+  FQ_CHECK_ARG(s.K % 8 == 0, "K must be a multiple of 8 (K=%d)", s.K);
+  if (per_tensor) {
+    FQ_CHECK_ARG(fmt == FQ_FMT_INT8 || fmt == FQ_FMT_FP8_E4M3 || fmt == FQ_FMT_NVFP4,
+                 "unsupported activation format %d", fmt);
+    launch_observer_tensor(x, (size_t)s.E * s.N * s.K, fmt, scale, S(stream));
+    FQ_CHECK_LAUNCH("observer_absmax_init");
+    return FQ_OK;
+  }
+  fq_weight_q q{fmt, group, scale, zero_point, global_scale};
+  FQ_TRY(check_weight_q(&q, s, true));
+  launch_observer_weight(x, s, fmt, group, scale, zero_point, global_scale, S(stream));
+  FQ_CHECK_LAUNCH("observer_absmax_init");
+  return FQ_OK;
+}
+
+fq_status fq_quantize_stacked(const uint16_t *w, fq_shape s, const fq_weight_q *q, uint16_t *w_fq,
+                              uint8_t *codes, fq_stream stream) {
+  FQ_TRY(check_shape(s));
+  FQ_TRY(check_weight_q(q, s, true));
+  FQ_CHECK_ARG(w != nullptr, "w is NULL");
+  FQ_CHECK_ARG(w_fq || codes, "at least one of w_fq and codes must be non-NULL");
+  FQ_CHECK_ARG(aligned16(w) && (!w_fq || aligned16(w_fq)), "bf16 tensors must be 16-byte aligned");
+  FQ_CHECK_ARG(!codes || ((uintptr_t)codes & 7) == 0, "codes must be 8-byte aligned");
+  launch_quantize_stacked(w, s, *q, w_fq, codes, S(stream));
+  FQ_CHECK_LAUNCH("fq_quantize_stacked");
+  return FQ_OK;
+}
+
+fq_status fq_moe_permute(const int32_t *ids, int32_t T, int32_t topk, int32_t ebegin, int32_t E,
+                         int32_t *perm, int32_t *row_of, int32_t *seg, void *ws, size_t ws_bytes,
+                         fq_stream stream) {
+  FQ_CHECK_ARG(T >= 0 && topk > 0 && E > 0 && ebegin >= 0, "bad sizes T=%d topk=%d E=%d", T, topk, E);
+  FQ_CHECK_ARG(seg != nullptr, "seg_offsets is NULL");
+  FQ_CHECK_ARG(T == 0 || (ids && perm && row_of), "expert_ids, perm and row_of must be non-NULL");
+  FQ_CHECK_ARG((long)T * topk < (1l << 31), "too many pairs");
+  size_t need = permute_workspace_bytes(E, (long)T * topk);
+  if (ws_bytes < need || !ws) {
+    set_error("fq_moe_permute: workspace %zu bytes < %zu needed", ws_bytes, need);
+    return FQ_ERR_WORKSPACE_TOO_SMALL;
+  }
+  launch_permute(ids, T, topk, ebegin, E, perm, row_of, seg, ws, S(stream));
+  FQ_CHECK_LAUNCH("fq_moe_permute");
+  return FQ_OK;
+}
+
+fq_status fq_grouped_gemm_fwd(const uint16_t *x, int32_t R_max, const int32_t *seg, fq_shape s,
+                              const uint16_t *w, const uint16_t *w_fq, const fq_weight_q *wq,
+                              const fq_act_q *aq, uint16_t *y, void *ws, size_t ws_bytes,
+                              fq_stream stream) {
+  FQ_TRY(check_shape(s));
+  FQ_CHECK_ARG(R_max >= 0, "R_max < 0");
+  FQ_CHECK_ARG(seg && y && (x || R_max == 0), "x, seg_offsets and y must be non-NULL");
+  FQ_CHECK_ARG(w || w_fq, "w or w_fq must be non-NULL");
+  FQ_TRY(check_weight_q(wq, s, w_fq == nullptr));
+  FQ_TRY(check_act_q(aq, s.K));
+  FQ_CHECK_SUPPORTED(s.N % 256 == 0 && s.K % 64 == 0,
+                     "grouped GEMM forward needs N %% 256 == 0 and K %% 64 == 0 (N=%d K=%d)", s.N, s.K);
+  FQ_CHECK_ARG((!x || aligned16(x)) && aligned16(y) && (!w || aligned16(w)) &&
+                   (!w_fq || aligned16(w_fq)),
+               "bf16 tensors must be 16-byte aligned");
+  const int afmt = act_fmt(aq);
+  size_t need = gemm_ws(FQ_OP_GEMM_FWD, s, R_max,
+                        (w_fq ? 0 : wq->fmt) | (afmt << 8));
+  if (need > 0 && (ws_bytes < need || !ws)) {
+    set_error("fq_grouped_gemm_fwd: workspace %zu bytes < %zu needed", ws_bytes, need);
+    return FQ_ERR_WORKSPACE_TOO_SMALL;
+  }
+  hipStream_t st = S(stream);
+  Carver c(ws);
+  const uint16_t *wfq = w_fq;
+  if (!wfq) {
+    uint16_t *t = c.take<uint16_t>((size_t)s.E * s.N * s.K * 2);
+    launch_quantize_stacked(w, s, *wq, t, nullptr, st);
+    wfq = t;
+  }
+  const uint16_t *xq = x;
+  if (afmt != FQ_FMT_NONE && R_max > 0) {
+    uint16_t *t = c.take<uint16_t>((size_t)R_max * s.K * 2);
+    launch_act_fq(x, R_max, s.K, seg + s.E, afmt, aq->scale, t, st);
+    xq = t;
+  }
+  launch_gemm_fwd(xq, R_max, seg, s, wfq, y, st);
+  FQ_CHECK_LAUNCH("fq_grouped_gemm_fwd");
+  return FQ_OK;
+}
+
+fq_status fq_grouped_gemm_bwd_scale(const uint16_t *dy, const uint16_t *x, int32_t R_max,
+                                    const int32_t *seg, fq_shape s, const uint16_t *w,
+                                    const uint16_t *w_fq, const fq_weight_q *wq, const fq_act_q *aq,
+                                    uint16_t *dx, float *dscale, float *dzp, void *ws,
+                                    size_t ws_bytes, fq_stream stream) {
+  FQ_TRY(check_shape(s));
+  FQ_CHECK_ARG(R_max >= 0, "R_max < 0");
+  FQ_CHECK_ARG(seg != nullptr, "seg_offsets is NULL");
+  FQ_CHECK_ARG(dy || R_max == 0, "dy is NULL");
+  const bool want_ds = dscale || dzp;
+  FQ_TRY(check_weight_q(wq, s, true));
+  FQ_TRY(check_act_q(aq, s.K));
+  FQ_CHECK_ARG(w != nullptr, "w (raw weights) is NULL");
+  FQ_CHECK_ARG(!want_ds || x || R_max == 0, "x is NULL");
+  FQ_CHECK_ARG(!dzp || wq->fmt == FQ_FMT_INT4, "dzero_point only exists for int4");
+  FQ_CHECK_ARG(!dzp || dscale, "dzero_point needs dscale too");
+  FQ_CHECK_SUPPORTED(s.N % 256 == 0 && s.K % 256 == 0,
+                     "grouped GEMM backward needs N %% 256 == 0 and K %% 256 == 0 (N=%d K=%d)", s.N,
+                     s.K);
+  FQ_CHECK_SUPPORTED(!want_ds || group_ok_for_dscale(wq->group),
+                     "dScale needs group 16, 32, 64 or a multiple of 128 (group=%d)", wq->group);
+  FQ_CHECK_ARG((!dy || aligned16(dy)) && (!x || aligned16(x)) && aligned16(w) &&
+                   (!w_fq || aligned16(w_fq)) && (!dx || aligned16(dx)),
+               "bf16 tensors must be 16-byte aligned");
+  const int afmt = act_fmt(aq);
+  size_t need = gemm_ws(FQ_OP_GEMM_BWD, s, R_max, (w_fq ? 0 : wq->fmt) | (afmt << 8));
+  if (ws_bytes < need || !ws) {
+    set_error("fq_grouped_gemm_bwd_scale: workspace %zu bytes < %zu needed", ws_bytes, need);
+    return FQ_ERR_WORKSPACE_TOO_SMALL;
+  }
+  hipStream_t st = S(stream);
+  Carver c(ws);
+  const uint16_t *wfq = w_fq;
+  if (!wfq && dx) {
+    uint16_t *t = c.take<uint16_t>((size_t)s.E * s.N * s.K * 2);
+    launch_quantize_stacked(w, s, *wq, t, nullptr, st);
+    wfq = t;
+  }
+  if (dx && R_max > 0) {
+    launch_gemm_dgrad(dy, R_max, seg, s, wfq, dx, st);
+    if (afmt != FQ_FMT_NONE) launch_act_mask(dx, x, R_max, s.K, seg + s.E, afmt, aq->scale, st);
+  }
+  if (want_ds) {
+    const uint16_t *xq = x;
+    if (afmt != FQ_FMT_NONE && R_max > 0) {
+      uint16_t *t = c.take<uint16_t>((size_t)R_max * s.K * 2);
+      launch_act_fq(x, R_max, s.K, seg + s.E, afmt, aq->scale, t, st);
+      xq = t;
+    }
+    const size_t nsc = (size_t)s.E * s.N * (s.K / wq->group);
+    float *ds_out = dscale;
+    float *ps = nullptr, *pz = nullptr;
+    const int P = wq->group / 128;
+    if (wq->group > 128) {
+      ps = c.take<float>((size_t)s.E * s.N * (s.K / 128) * 4);
+      if (dzp) pz = c.take<float>((size_t)s.E * s.N * (s.K / 128) * 4);
+    }
+    launch_gemm_wgrad_dscale(dy, xq, seg, s, w, *wq, ds_out, dzp, ps, pz, st);
+    if (wq->group > 128) {
+      launch_reduce_partials(ps, P, nsc, ds_out, st);
+      if (dzp) launch_reduce_partials(pz, P, nsc, dzp, st);
+    }
+  }
+  FQ_CHECK_LAUNCH("fq_grouped_gemm_bwd_scale");
+  return FQ_OK;
+}
+
+fq_status fq_moe_gather_actfq(const uint16_t *x, int32_t T, int32_t H, const int32_t *perm,
+                              int32_t topk, int32_t R_max, const int32_t *n_rows, const fq_act_q *aq,
+                              uint16_t *xq, fq_stream stream) {
+  FQ_CHECK_ARG(T >= 0 && H > 0 && topk > 0 && R_max >= 0, "bad sizes");
+  FQ_CHECK_ARG(H % 16 == 0, "H must be a multiple of 16");
+  FQ_CHECK_ARG(n_rows && (R_max == 0 || (x && perm && xq)), "NULL pointer");
+  FQ_CHECK_ARG((!x || aligned16(x)) && (!xq || aligned16(xq)), "bf16 tensors must be 16-byte aligned");
+  FQ_TRY(check_act_q(aq, H));
+  launch_gather_actfq(x, H, perm, topk, R_max, n_rows, act_fmt(aq), aq ? aq->scale : nullptr, xq,
+                      S(stream));
+  FQ_CHECK_LAUNCH("fq_moe_gather_actfq");
+  return FQ_OK;
+}
+
+fq_status fq_swiglu_actfq(const uint16_t *h, int32_t R_max, const int32_t *n_rows, int32_t F,
+                          const fq_act_q *aq, uint16_t *a, uint16_t *aqo, fq_stream stream) {
+  FQ_CHECK_ARG(R_max >= 0 && F > 0 && F % 16 == 0, "bad sizes (F must be a multiple of 16)");
+  FQ_CHECK_ARG(n_rows && (R_max == 0 || (h && aqo)), "NULL pointer");
+  FQ_CHECK_ARG((!h || aligned16(h)) && (!a || aligned16(a)) && (!aqo || aligned16(aqo)),
+               "bf16 tensors must be 16-byte aligned");
+  FQ_TRY(check_act_q(aq, F));
+  launch_swiglu_actfq(h, R_max, n_rows, F, act_fmt(aq), aq ? aq->scale : nullptr, a, aqo, S(stream));
+  FQ_CHECK_LAUNCH("fq_swiglu_actfq");
+  return FQ_OK;
+}
+
+fq_status fq_swiglu_bwd(const uint16_t *daq, const uint16_t *h, int32_t R_max, const int32_t *n_rows,
+                        int32_t F, const fq_act_q *aq, uint16_t *dh, fq_stream stream) {
+  FQ_CHECK_ARG(R_max >= 0 && F > 0 && F % 16 == 0, "bad sizes (F must be a multiple of 16)");
+  FQ_CHECK_ARG(n_rows && (R_max == 0 || (h && daq && dh)), "NULL pointer");
+  FQ_CHECK_ARG((!h || aligned16(h)) && (!daq || aligned16(daq)) && (!dh || aligned16(dh)),
+               "bf16 tensors must be 16-byte aligned");
+  FQ_TRY(check_act_q(aq, F));
+  launch_swiglu_bwd(daq, h, R_max, n_rows, F, act_fmt(aq), aq ? aq->scale : nullptr, dh, S(stream));
+  FQ_CHECK_LAUNCH("fq_swiglu_bwd");
+  return FQ_OK;
+}
+
+fq_status fq_moe_combine(const uint16_t *o, const float *probs, const int32_t *row_of, int32_t T,
+                         int32_t topk, int32_t H, uint16_t *out, fq_stream stream) {
+  FQ_CHECK_ARG(T >= 0 && topk > 0 && H > 0 && H % 16 == 0, "bad sizes (H must be a multiple of 16)");
+  FQ_CHECK_ARG(T == 0 || (o && probs && row_of && out), "NULL pointer");
+  FQ_CHECK_ARG((!o || aligned16(o)) && (!out || aligned16(out)), "bf16 tensors must be 16-byte aligned");
+  launch_combine(o, probs, row_of, T, topk, H, out, S(stream));
+  FQ_CHECK_LAUNCH("fq_moe_combine");
+  return FQ_OK;
+}
+
+fq_status fq_moe_combine_bwd(const uint16_t *dout, const float *probs, const int32_t *perm,
+                             int32_t topk, int32_t H, int32_t R_max, const int32_t *n_rows,
+                             uint16_t *dO, fq_stream stream) {
+  FQ_CHECK_ARG(topk > 0 && H > 0 && H % 16 == 0 && R_max >= 0, "bad sizes");
+  FQ_CHECK_ARG(n_rows && (R_max == 0 || (dout && probs && perm && dO)), "NULL pointer");
+  FQ_CHECK_ARG((!dout || aligned16(dout)) && (!dO || aligned16(dO)),
+               "bf16 tensors must be 16-byte aligned");
+  launch_combine_bwd(dout, probs, perm, topk, H, R_max, n_rows, dO, S(stream));
+  FQ_CHECK_LAUNCH("fq_moe_combine_bwd");
+  return FQ_OK;
+}
+
+fq_status fq_moe_unpermute_reduce(const uint16_t *dxq, const int32_t *row_of, const uint16_t *x,
+                                  int32_t T, int32_t topk, int32_t H, const fq_act_q *aq,
+                                  uint16_t *dx, fq_stream stream) {
+  FQ_CHECK_ARG(T >= 0 && topk > 0 && H > 0 && H % 16 == 0, "bad sizes (H must be a multiple of 16)");
+  FQ_CHECK_ARG(T == 0 || (dxq && row_of && dx), "NULL pointer");
+  FQ_TRY(check_act_q(aq, H));
+  FQ_CHECK_ARG(act_fmt(aq) == FQ_FMT_NONE || T == 0 || x, "x is NULL");
+  FQ_CHECK_ARG((!dxq || aligned16(dxq)) && (!dx || aligned16(dx)) && (!x || aligned16(x)),
+               "bf16 tensors must be 16-byte aligned");
+  launch_unpermute_reduce(dxq, row_of, x, T, topk, H, act_fmt(aq), aq ? aq->scale : nullptr, dx,
+                          S(stream));
+  FQ_CHECK_LAUNCH("fq_moe_unpermute_reduce");
+  return FQ_OK;
+}
+
+}  // extern "C"

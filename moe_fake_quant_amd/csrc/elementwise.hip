@@ -1,0 +1,650 @@
+// HBM-bound passes of libfq on gfx950: the stacked weight fake-quant, the
+// observers, activation fake-quant (plain, gathered, after SwiGLU), SwiGLU
+// backward, combine / unpermute, and the fixed-order dScale partial reduce.
+//
+// Every pass moves 16-byte vectors per lane (8 bf16), so a wavefront touches
+// 1 KiB of contiguous memory per load; indexes are 32-bit with precomputed
+// fast division. Launches use enough blocks to cover all 256 CUs several
+// times and grid-stride beyond that.
+#include "internal.hpp"
+
+namespace fq {
+
+namespace {
+
+constexpr int kThreads = 256;
+
+inline int grid_for(long work_items, int per_block = kThreads, int max_blocks = 256 * 32) {
+  long b = (work_items + per_block - 1) / per_block;
+  if (b < 1) b = 1;
+  if (b > max_blocks) b = max_blocks;
+  return (int)b;
+}
+
+// ------------------------------------------------------------- fill --------
+__global__ void k_fill_u32(uint32_t *p, uint32_t v, long n) {
+  for (long i = blockIdx.x * (long)blockDim.x + threadIdx.x; i < n; i += (long)gridDim.x * blockDim.x)
+    p[i] = v;
+}
+
+// ------------------------------------------- stacked weight fake-quant -----
+// One thread-iteration handles one 8-element vector of one row. Requires
+// group % 8 == 0 so a vector never straddles a scale group.
+template <int FMT>
+__global__ __launch_bounds__(kThreads) void k_quantize_stacked(
+    const bf16x8_t *__restrict__ w, uint32_t nvec, FastDiv vec_per_row, FastDiv rows_per_expert,
+    FastDiv vec_per_group, uint32_t groups_per_row, const float *__restrict__ scale,
+    const float *__restrict__ zero_point, const float *__restrict__ gscale,
+    bf16x8_t *__restrict__ out, uint8_t *__restrict__ codes) {
+  const uint32_t stride = gridDim.x * blockDim.x;
+  for (uint32_t i = blockIdx.x * blockDim.x + threadIdx.x; i < nvec; i += stride) {
+    bf16x8_t v = w[i];
+    uint32_t row = vec_per_row.div(i);
+    uint32_t kv = i - row * vec_per_row.d;
+    uint32_t gidx = row * groups_per_row + vec_per_group.div(kv);
+    float s = scale[gidx];
+    float zpi = 0.0f, g = 1.0f;
+    if (FMT == FQ_FMT_INT4) zpi = fminf(fmaxf(rintf(zero_point[gidx]), 0.0f), 15.0f);
+    if (FMT == FQ_FMT_NVFP4) {
+      g = gscale[rows_per_expert.div(row)];
+      s = nvfp4_block_scale(s, g);
+    }
+    float r = safe_recip(s);
+    float x[8], y[8];
+    unpack8(v, x);
+    uint32_t c[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      FQElem e = fq_weight_elem(FMT, x[j], s, r, zpi);
+      y[j] = e.v;
+      c[j] = e.code;
+    }
+    if (out) out[i] = pack8(y);
+    if (codes) {
+      if (FMT == FQ_FMT_INT8 || FMT == FQ_FMT_FP8_E4M3) {
+        uint2 b;
+        b.x = c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24);
+        b.y = c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24);
+        reinterpret_cast<uint2 *>(codes)[i] = b;
+      } else {
+        uint32_t b = 0;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) b |= (c[j] & 0xFu) << (4 * j);
+        reinterpret_cast<uint32_t *>(codes)[i] = b;
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------ observer -----
+// Groups that span 2..64 vectors are reduced across adjacent lanes; one
+// vector per lane, vectors of a group on consecutive lanes of one wave.
+template <int FMT>
+__global__ __launch_bounds__(kThreads) void k_observer_lanes(
+    const bf16x8_t *__restrict__ w, uint32_t nvec, int lanes_per_group, FastDiv vec_per_expert,
+    float *__restrict__ scale, float *__restrict__ zero_point, uint32_t *__restrict__ expert_amax) {
+  const uint32_t stride = gridDim.x * blockDim.x;
+  // uniform trip count so every lane takes part in the shuffles
+  for (uint32_t base = blockIdx.x * blockDim.x; base < nvec; base += stride) {
+    uint32_t i = base + threadIdx.x;
+    bool ok = i < nvec;
+    float x[8];
+    bf16x8_t v = ok ? w[i] : bf16x8_t{{0, 0, 0, 0}};
+    unpack8(v, x);
+    float amax = 0.0f, mn = 0.0f, mx = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      amax = fmaxf(amax, fabsf(x[j]));
+      mn = fminf(mn, x[j]);
+      mx = fmaxf(mx, x[j]);
+    }
+    for (int o = 1; o < lanes_per_group; o <<= 1) {
+      amax = fmaxf(amax, __shfl_xor(amax, o, 64));
+      mn = fminf(mn, __shfl_xor(mn, o, 64));
+      mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+    }
+    if (ok && (threadIdx.x & (lanes_per_group - 1)) == 0) {
+      uint32_t gi = i / (uint32_t)lanes_per_group;
+      if (FMT == FQ_FMT_INT8 || FMT == FQ_FMT_FP8_E4M3) {
+        float s = amax / (FMT == FQ_FMT_INT8 ? 127.0f : kE4M3Max);
+        scale[gi] = s == 0.0f ? 1.0f : s;
+      } else if (FMT == FQ_FMT_INT4) {
+        float s = (mx - mn) / 15.0f;  // mn <= 0 <= mx
+        s = s == 0.0f ? 1.0f : s;
+        float r = 1.0f / s;
+        scale[gi] = s;
+        zero_point[gi] = fminf(fmaxf(rintf(-mn * r), 0.0f), 15.0f);
+      } else {  // nvfp4: block amax now, theta after the expert amax is known
+        scale[gi] = amax;
+        atomicMax(expert_amax + vec_per_expert.div(i), __float_as_uint(amax));
+      }
+    }
+  }
+}
+
+// Groups longer than 64 vectors (per-channel scales): one block per group.
+template <int FMT>
+__global__ __launch_bounds__(kThreads) void k_observer_block(const bf16x8_t *__restrict__ w,
+                                                             int vec_per_group,
+                                                             float *__restrict__ scale,
+                                                             float *__restrict__ zero_point) {
+  const bf16x8_t *p = w + (size_t)blockIdx.x * vec_per_group;
+  float amax = 0.0f, mn = 0.0f, mx = 0.0f;
+  for (int i = threadIdx.x; i < vec_per_group; i += blockDim.x) {
+    float x[8];
+    unpack8(p[i], x);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      amax = fmaxf(amax, fabsf(x[j]));
+      mn = fminf(mn, x[j]);
+      mx = fmaxf(mx, x[j]);
+    }
+  }
+  __shared__ float red[3][kThreads / 64];
+  amax = warp_max(amax);
+  mx = warp_max(mx);
+  mn = -warp_max(-mn);
+  if ((threadIdx.x & 63) == 0) {
+    red[0][threadIdx.x >> 6] = amax;
+    red[1][threadIdx.x >> 6] = mn;
+    red[2][threadIdx.x >> 6] = mx;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int k = 1; k < kThreads / 64; ++k) {
+      amax = fmaxf(amax, red[0][k]);
+      mn = fminf(mn, red[1][k]);
+      mx = fmaxf(mx, red[2][k]);
+    }
+    if (FMT == FQ_FMT_INT8 || FMT == FQ_FMT_FP8_E4M3) {
+      float s = amax / (FMT == FQ_FMT_INT8 ? 127.0f : kE4M3Max);
+      scale[blockIdx.x] = s == 0.0f ? 1.0f : s;
+    } else {  // int4
+      float s = (mx - mn) / 15.0f;
+      s = s == 0.0f ? 1.0f : s;
+      float r = 1.0f / s;
+      scale[blockIdx.x] = s;
+      zero_point[blockIdx.x] = fminf(fmaxf(rintf(-mn * r), 0.0f), 15.0f);
+    }
+  }
+}
+
+// theta_b = E4M3(clamp(amax_b * (1/(6 g)), 0, 448)), g = amax_e / 2688 (1 if 0)
+__global__ void k_nvfp4_theta(float *__restrict__ theta, uint32_t n, FastDiv blocks_per_expert,
+                              const uint32_t *__restrict__ expert_amax) {
+  for (uint32_t i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) {
+    float ae = __uint_as_float(expert_amax[blocks_per_expert.div(i)]);
+    float g = ae / (kE2M1Max * kE4M3Max);
+    g = g == 0.0f ? 1.0f : g;
+    float d = 6.0f * g;
+    float rd = 1.0f / d;
+    float t = fminf(theta[i] * rd, kE4M3Max);
+    theta[i] = e4m3_round_mag(t);
+  }
+}
+
+__global__ void k_nvfp4_global(uint32_t *__restrict__ g_bits, int E) {
+  int e = blockIdx.x * blockDim.x + threadIdx.x;
+  if (e < E) {
+    float g = __uint_as_float(g_bits[e]) / (kE2M1Max * kE4M3Max);
+    reinterpret_cast<float *>(g_bits)[e] = g == 0.0f ? 1.0f : g;
+  }
+}
+
+// per-tensor absmax into out_bits[0] (zeroed before)
+__global__ __launch_bounds__(kThreads) void k_absmax_tensor(const bf16x8_t *__restrict__ x,
+                                                            uint32_t nvec,
+                                                            uint32_t *__restrict__ out_bits) {
+  float amax = 0.0f;
+  for (uint32_t i = blockIdx.x * blockDim.x + threadIdx.x; i < nvec; i += gridDim.x * blockDim.x) {
+    float f[8];
+    unpack8(x[i], f);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(f[j]));
+  }
+  amax = warp_max(amax);
+  if ((threadIdx.x & 63) == 0) atomicMax(out_bits, __float_as_uint(amax));
+}
+
+__global__ void k_act_scale_finalize(uint32_t *bits, float div) {
+  if (threadIdx.x == 0 && blockIdx.x == 0) {
+    float s = __uint_as_float(bits[0]) / div;
+    reinterpret_cast<float *>(bits)[0] = s == 0.0f ? 1.0f : s;
+  }
+}
+
+// ------------------------------------------------ activation fake-quant -----
+// Per-tensor frozen activation quantizer, resolved once per thread.
+struct ActQ {
+  int fmt;
+  float s;  // s_a (fp8 / int8) or g_a (nvfp4)
+  float r;  // 1/s_a
+};
+
+__device__ __forceinline__ ActQ load_actq(int fmt, const float *scale) {
+  ActQ q;
+  q.fmt = fmt;
+  q.s = (fmt == FQ_FMT_NONE) ? 1.0f : scale[0];
+  q.r = (fmt == FQ_FMT_NONE) ? 1.0f : 1.0f / q.s;
+  return q;
+}
+
+// 16 consecutive elements along K (one NVFP4 block): values in place, mask bits out.
+__device__ __forceinline__ uint32_t act_fq16(const ActQ &q, float *x) {
+  uint32_t mask = 0;
+  if (q.fmt == FQ_FMT_NONE) return 0xFFFFu;
+  if (q.fmt == FQ_FMT_NVFP4) {
+    float amax = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) amax = fmaxf(amax, fabsf(x[j]));
+    float s = nvfp4_dynamic_scale(amax, q.s);
+    float r = safe_recip(s);
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      FQElem e = fq_e2m1(x[j], s, r);
+      x[j] = e.v;
+      mask |= (uint32_t)e.m << j;
+    }
+    return mask;
+  }
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    FQElem e = (q.fmt == FQ_FMT_FP8_E4M3) ? fq_fp8(x[j], q.s, q.r) : fq_int8(x[j], q.s, q.r);
+    x[j] = e.v;
+    mask |= (uint32_t)e.m << j;
+  }
+  return mask;
+}
+
+__device__ __forceinline__ void load16(const bf16x8_t *p, float *x) {
+  bf16x8_t a = p[0], b = p[1];
+  unpack8(a, x);
+  unpack8(b, x + 8);
+}
+__device__ __forceinline__ void store16(bf16x8_t *p, const float *x) {
+  p[0] = pack8(x);
+  p[1] = pack8(x + 8);
+}
+// round each value to bf16 in place (what a bf16 store then reload would give)
+__device__ __forceinline__ void round_bf16_16(float *x) {
+#pragma unroll
+  for (int j = 0; j < 16; ++j) x[j] = bf16_to_f32(f32_to_bf16(x[j]));
+}
+
+// number of 16-element chunks to process: all of them, or only the first
+// n_rows[0] rows (rows past the routed count are left untouched)
+__device__ __forceinline__ uint32_t live_chunks(uint32_t max_chunks, const int32_t *n_rows,
+                                                uint32_t chunks_per_row) {
+  return n_rows ? min((uint32_t)n_rows[0] * chunks_per_row, max_chunks) : max_chunks;
+}
+
+// x [M, K] -> xq [M, K]; chunks of 16 elements
+__global__ __launch_bounds__(kThreads) void k_act_fq(const bf16x8_t *__restrict__ x, uint32_t max_chunks,
+                                                     const int32_t *__restrict__ n_rows, uint32_t cpr,
+                                                     int afmt, const float *__restrict__ ascale,
+                                                     bf16x8_t *__restrict__ xq) {
+  ActQ q = load_actq(afmt, ascale);
+  const uint32_t nchunk = live_chunks(max_chunks, n_rows, cpr);
+  for (uint32_t c = blockIdx.x * blockDim.x + threadIdx.x; c < nchunk; c += gridDim.x * blockDim.x) {
+    float f[16];
+    load16(x + 2 * (size_t)c, f);
+    act_fq16(q, f);
+    store16(xq + 2 * (size_t)c, f);
+  }
+}
+
+// dx[M, K] *= mask(FQ_a(x))   (in place)
+__global__ __launch_bounds__(kThreads) void k_act_mask(bf16x8_t *__restrict__ dx,
+                                                       const bf16x8_t *__restrict__ x,
+                                                       uint32_t max_chunks,
+                                                       const int32_t *__restrict__ n_rows,
+                                                       uint32_t cpr, int afmt,
+                                                       const float *__restrict__ ascale) {
+  ActQ q = load_actq(afmt, ascale);
+  const uint32_t nchunk = live_chunks(max_chunks, n_rows, cpr);
+  for (uint32_t c = blockIdx.x * blockDim.x + threadIdx.x; c < nchunk; c += gridDim.x * blockDim.x) {
+    float f[16], d[16];
+    load16(x + 2 * (size_t)c, f);
+    uint32_t m = act_fq16(q, f);
+    load16(dx + 2 * (size_t)c, d);
+#pragma unroll
+    for (int j = 0; j < 16; ++j) d[j] = ((m >> j) & 1u) ? d[j] : 0.0f;
+    store16(dx + 2 * (size_t)c, d);
+  }
+}
+
+// xq[r] = FQ_a(x[perm[r] / topk]) for r < n_rows[0]
+__global__ __launch_bounds__(kThreads) void k_gather_actfq(
+    const bf16x8_t *__restrict__ x, const int32_t *__restrict__ perm, int topk, FastDiv chunks_per_row,
+    uint32_t max_chunks, const int32_t *__restrict__ n_rows, int afmt, const float *__restrict__ ascale,
+    bf16x8_t *__restrict__ xq) {
+  ActQ q = load_actq(afmt, ascale);
+  const uint32_t nchunk = min((uint32_t)n_rows[0] * chunks_per_row.d, max_chunks);
+  for (uint32_t c = blockIdx.x * blockDim.x + threadIdx.x; c < nchunk; c += gridDim.x * blockDim.x) {
+    uint32_t r = chunks_per_row.div(c);
+    uint32_t cc = c - r * chunks_per_row.d;
+    uint32_t t = (uint32_t)perm[r] / (uint32_t)topk;
+    float f[16];
+    load16(x + 2 * ((size_t)t * chunks_per_row.d + cc), f);
+    act_fq16(q, f);
+    store16(xq + 2 * (size_t)c, f);
+  }
+}
+
+// SwiGLU value of 16 elements in fp32, rounded to bf16 (the stored A).
+__device__ __forceinline__ void swiglu16(const float *g, const float *u, float *a) {
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    float sg = g[j] / (1.0f + expf(-g[j]));
+    a[j] = bf16_to_f32(f32_to_bf16(sg * u[j]));
+  }
+}
+
+// h [R, 2F] -> a [R, F] (optional), aq [R, F]
+__global__ __launch_bounds__(kThreads) void k_swiglu_actfq(
+    const bf16x8_t *__restrict__ h, FastDiv chunks_per_row, uint32_t max_chunks,
+    const int32_t *__restrict__ n_rows, int afmt, const float *__restrict__ ascale,
+    bf16x8_t *__restrict__ a_out, bf16x8_t *__restrict__ aq_out) {
+  ActQ q = load_actq(afmt, ascale);
+  const uint32_t cpr = chunks_per_row.d;  // F / 16
+  const uint32_t nchunk = min((uint32_t)n_rows[0] * cpr, max_chunks);
+  for (uint32_t c = blockIdx.x * blockDim.x + threadIdx.x; c < nchunk; c += gridDim.x * blockDim.x) {
+    uint32_t r = chunks_per_row.div(c);
+    uint32_t cc = c - r * cpr;
+    const bf16x8_t *hr = h + 2 * ((size_t)r * 2 * cpr);
+    float g[16], u[16], a[16];
+    load16(hr + 2 * cc, g);
+    load16(hr + 2 * (cpr + cc), u);
+    swiglu16(g, u, a);
+    if (a_out) store16(a_out + 2 * (size_t)c, a);
+    act_fq16(q, a);
+    store16(aq_out + 2 * (size_t)c, a);
+  }
+}
+
+// dh = SwiGLU'(h) applied to da = m_a * daq
+__global__ __launch_bounds__(kThreads) void k_swiglu_bwd(
+    const bf16x8_t *__restrict__ daq, const bf16x8_t *__restrict__ h, FastDiv chunks_per_row,
+    uint32_t max_chunks, const int32_t *__restrict__ n_rows, int afmt,
+    const float *__restrict__ ascale, bf16x8_t *__restrict__ dh) {
+  ActQ q = load_actq(afmt, ascale);
+  const uint32_t cpr = chunks_per_row.d;
+  const uint32_t nchunk = min((uint32_t)n_rows[0] * cpr, max_chunks);
+  for (uint32_t c = blockIdx.x * blockDim.x + threadIdx.x; c < nchunk; c += gridDim.x * blockDim.x) {
+    uint32_t r = chunks_per_row.div(c);
+    uint32_t cc = c - r * cpr;
+    const bf16x8_t *hr = h + 2 * ((size_t)r * 2 * cpr);
+    float g[16], u[16], a[16], d[16], dg[16], du[16];
+    load16(hr + 2 * cc, g);
+    load16(hr + 2 * (cpr + cc), u);
+    swiglu16(g, u, a);
+    uint32_t m = act_fq16(q, a);
+    load16(daq + 2 * (size_t)c, d);
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      float da = ((m >> j) & 1u) ? d[j] : 0.0f;
+      float s = 1.0f / (1.0f + expf(-g[j]));
+      dg[j] = da * u[j] * s * (1.0f + g[j] * (1.0f - s));
+      du[j] = da * g[j] * s;
+    }
+    bf16x8_t *dr = dh + 2 * ((size_t)r * 2 * cpr);
+    store16(dr + 2 * cc, dg);
+    store16(dr + 2 * (cpr + cc), du);
+  }
+}
+
+// out[t] = bf16(sum_j p[t,j] * o[row_of[t,j]]), j ascending, local slots only
+__global__ __launch_bounds__(kThreads) void k_combine(const bf16x8_t *__restrict__ o,
+                                                      const float *__restrict__ probs,
+                                                      const int32_t *__restrict__ row_of, int topk,
+                                                      FastDiv chunks_per_row, uint32_t nchunk,
+                                                      bf16x8_t *__restrict__ out) {
+  const uint32_t cpr = chunks_per_row.d;
+  for (uint32_t c = blockIdx.x * blockDim.x + threadIdx.x; c < nchunk; c += gridDim.x * blockDim.x) {
+    uint32_t t = chunks_per_row.div(c);
+    uint32_t cc = c - t * cpr;
+    float acc[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) acc[j] = 0.0f;
+    for (int j = 0; j < topk; ++j) {
+      int r = row_of[t * topk + j];
+      if (r < 0) continue;
+      float p = probs[t * topk + j];
+      float f[16];
+      load16(o + 2 * ((size_t)r * cpr + cc), f);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[i] = acc[i] + p * f[i];
+    }
+    store16(out + 2 * (size_t)c, acc);
+  }
+}
+
+// do[r] = bf16(p[t,j] * dout[t]), f = perm[r]
+__global__ __launch_bounds__(kThreads) void k_combine_bwd(
+    const bf16x8_t *__restrict__ dout, const float *__restrict__ probs, const int32_t *__restrict__ perm,
+    int topk, FastDiv chunks_per_row, uint32_t max_chunks, const int32_t *__restrict__ n_rows,
+    bf16x8_t *__restrict__ dO) {
+  const uint32_t cpr = chunks_per_row.d;
+  const uint32_t nchunk = min((uint32_t)n_rows[0] * cpr, max_chunks);
+  for (uint32_t c = blockIdx.x * blockDim.x + threadIdx.x; c < nchunk; c += gridDim.x * blockDim.x) {
+    uint32_t r = chunks_per_row.div(c);
+    uint32_t cc = c - r * cpr;
+    uint32_t f = (uint32_t)perm[r];
+    uint32_t t = f / (uint32_t)topk;
+    float p = probs[f];
+    float d[16];
+    load16(dout + 2 * ((size_t)t * cpr + cc), d);
+#pragma unroll
+    for (int j = 0; j < 16; ++j) d[j] = p * d[j];
+    store16(dO + 2 * (size_t)c, d);
+  }
+}
+
+// dx[t] = bf16(m_a(x[t]) * sum_j dxq[row_of[t,j]])
+__global__ __launch_bounds__(kThreads) void k_unpermute_reduce(
+    const bf16x8_t *__restrict__ dxq, const int32_t *__restrict__ row_of,
+    const bf16x8_t *__restrict__ x, int topk, FastDiv chunks_per_row, uint32_t nchunk, int afmt,
+    const float *__restrict__ ascale, bf16x8_t *__restrict__ dx) {
+  ActQ q = load_actq(afmt, ascale);
+  const uint32_t cpr = chunks_per_row.d;
+  for (uint32_t c = blockIdx.x * blockDim.x + threadIdx.x; c < nchunk; c += gridDim.x * blockDim.x) {
+    uint32_t t = chunks_per_row.div(c);
+    uint32_t cc = c - t * cpr;
+    float acc[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) acc[j] = 0.0f;
+    for (int j = 0; j < topk; ++j) {
+      int r = row_of[t * topk + j];
+      if (r < 0) continue;
+      float f[16];
+      load16(dxq + 2 * ((size_t)r * cpr + cc), f);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[i] = acc[i] + f[i];
+    }
+    uint32_t m = 0xFFFFu;
+    if (afmt != FQ_FMT_NONE) {
+      float xf[16];
+      load16(x + 2 * (size_t)c, xf);
+      m = act_fq16(q, xf);
+    }
+#pragma unroll
+    for (int j = 0; j < 16; ++j) acc[j] = ((m >> j) & 1u) ? acc[j] : 0.0f;
+    store16(dx + 2 * (size_t)c, acc);
+  }
+}
+
+// out[i] = sum_p part[i * P + p] in order p = 0..P-1
+__global__ void k_reduce_partials(const float *__restrict__ part, int P, uint32_t n,
+                                  float *__restrict__ out) {
+  for (uint32_t i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) {
+    float s = 0.0f;
+    for (int p = 0; p < P; ++p) s += part[(size_t)i * P + p];
+    out[i] = s;
+  }
+}
+
+}  // namespace
+
+// ========================================================= launchers =======
+void launch_fill_u32(uint32_t *p, uint32_t v, long n, hipStream_t st) {
+  if (n <= 0) return;
+  hipLaunchKernelGGL(k_fill_u32, dim3(grid_for(n)), dim3(kThreads), 0, st, p, v, n);
+}
+
+void launch_quantize_stacked(const uint16_t *w, fq_shape s, const fq_weight_q &q, uint16_t *out,
+                             uint8_t *codes, hipStream_t st) {
+  uint32_t nvec = (uint32_t)((size_t)s.E * s.N * s.K / 8);
+  FastDiv vpr(s.K / 8), rpe(s.N), vpg(q.group / 8);
+  uint32_t gpr = s.K / q.group;
+  dim3 grid(grid_for(nvec)), block(kThreads);
+  auto wv = reinterpret_cast<const bf16x8_t *>(w);
+  auto ov = reinterpret_cast<bf16x8_t *>(out);
+#define FQ_QS(F)                                                                                \
+  hipLaunchKernelGGL(k_quantize_stacked<F>, grid, block, 0, st, wv, nvec, vpr, rpe, vpg, gpr, \
+                     q.scale, q.zero_point, q.global_scale, ov, codes)
+  switch (q.fmt) {
+    case FQ_FMT_INT8: FQ_QS(FQ_FMT_INT8); break;
+    case FQ_FMT_INT4: FQ_QS(FQ_FMT_INT4); break;
+    case FQ_FMT_FP8_E4M3: FQ_QS(FQ_FMT_FP8_E4M3); break;
+    default: FQ_QS(FQ_FMT_NVFP4); break;
+  }
+#undef FQ_QS
+}
+
+void launch_observer_weight(const uint16_t *w, fq_shape s, int fmt, int group, float *scale,
+                            float *zero_point, float *gscale, hipStream_t st) {
+  auto wv = reinterpret_cast<const bf16x8_t *>(w);
+  uint32_t nvec = (uint32_t)((size_t)s.E * s.N * s.K / 8);
+  int vpg = group / 8;
+  if (fmt == FQ_FMT_NVFP4) {
+    auto gbits = reinterpret_cast<uint32_t *>(gscale);
+    launch_fill_u32(gbits, 0u, s.E, st);
+    FastDiv vpe((uint32_t)((size_t)s.N * s.K / 8));
+    hipLaunchKernelGGL(k_observer_lanes<FQ_FMT_NVFP4>, dim3(grid_for(nvec)), dim3(kThreads), 0, st,
+                       wv, nvec, vpg, vpe, scale, zero_point, gbits);
+    uint32_t nb = (uint32_t)((size_t)s.E * s.N * (s.K / group));
+    FastDiv bpe((uint32_t)((size_t)s.N * (s.K / group)));
+    hipLaunchKernelGGL(k_nvfp4_theta, dim3(grid_for(nb)), dim3(kThreads), 0, st, scale, nb, bpe,
+                       gbits);
+    hipLaunchKernelGGL(k_nvfp4_global, dim3(ceil_div(s.E, kThreads)), dim3(kThreads), 0, st, gbits,
+                       s.E);
+    return;
+  }
+  bool lanes = vpg <= 64 && (vpg & (vpg - 1)) == 0;
+  if (lanes) {
+    FastDiv one(1);
+#define FQ_OBL(F)                                                                               \
+  hipLaunchKernelGGL(k_observer_lanes<F>, dim3(grid_for(nvec)), dim3(kThreads), 0, st, wv, nvec, \
+                     vpg, one, scale, zero_point, nullptr)
+    switch (fmt) {
+      case FQ_FMT_INT8: FQ_OBL(FQ_FMT_INT8); break;
+      case FQ_FMT_INT4: FQ_OBL(FQ_FMT_INT4); break;
+      default: FQ_OBL(FQ_FMT_FP8_E4M3); break;
+    }
+#undef FQ_OBL
+  } else {
+    uint32_t ngroups = nvec / vpg;
+#define FQ_OBB(F) \
+  hipLaunchKernelGGL(k_observer_block<F>, dim3(ngroups), dim3(kThreads), 0, st, wv, vpg, scale, zero_point)
+    switch (fmt) {
+      case FQ_FMT_INT8: FQ_OBB(FQ_FMT_INT8); break;
+      case FQ_FMT_INT4: FQ_OBB(FQ_FMT_INT4); break;
+      default: FQ_OBB(FQ_FMT_FP8_E4M3); break;
+    }
+#undef FQ_OBB
+  }
+}
+
+void launch_observer_tensor(const uint16_t *x, size_t n, int fmt, float *scale, hipStream_t st) {
+  auto bits = reinterpret_cast<uint32_t *>(scale);
+  launch_fill_u32(bits, 0u, 1, st);
+  uint32_t nvec = (uint32_t)(n / 8);
+  if (nvec)
+    hipLaunchKernelGGL(k_absmax_tensor, dim3(grid_for(nvec, kThreads, 2048)), dim3(kThreads), 0, st,
+                       reinterpret_cast<const bf16x8_t *>(x), nvec, bits);
+  float div = fmt == FQ_FMT_FP8_E4M3 ? kE4M3Max : fmt == FQ_FMT_NVFP4 ? kE2M1Max * kE4M3Max : 127.0f;
+  hipLaunchKernelGGL(k_act_scale_finalize, dim3(1), dim3(64), 0, st, bits, div);
+}
+
+void launch_act_fq(const uint16_t *x, size_t M, int K, const int32_t *n_rows, int afmt,
+                   const float *ascale, uint16_t *xq, hipStream_t st) {
+  uint32_t nchunk = (uint32_t)(M * K / 16);
+  if (!nchunk) return;
+  hipLaunchKernelGGL(k_act_fq, dim3(grid_for(nchunk)), dim3(kThreads), 0, st,
+                     reinterpret_cast<const bf16x8_t *>(x), nchunk, n_rows, (uint32_t)(K / 16), afmt,
+                     ascale, reinterpret_cast<bf16x8_t *>(xq));
+}
+
+void launch_act_mask(uint16_t *dx, const uint16_t *x, size_t M, int K, const int32_t *n_rows,
+                     int afmt, const float *ascale, hipStream_t st) {
+  uint32_t nchunk = (uint32_t)(M * K / 16);
+  if (!nchunk) return;
+  hipLaunchKernelGGL(k_act_mask, dim3(grid_for(nchunk)), dim3(kThreads), 0, st,
+                     reinterpret_cast<bf16x8_t *>(dx), reinterpret_cast<const bf16x8_t *>(x), nchunk,
+                     n_rows, (uint32_t)(K / 16), afmt, ascale);
+}
+
+void launch_gather_actfq(const uint16_t *x, int H, const int32_t *perm, int topk, int R_max,
+                         const int32_t *n_rows, int afmt, const float *ascale, uint16_t *xq,
+                         hipStream_t st) {
+  uint32_t maxc = (uint32_t)((size_t)R_max * H / 16);
+  if (!maxc) return;
+  hipLaunchKernelGGL(k_gather_actfq, dim3(grid_for(maxc)), dim3(kThreads), 0, st,
+                     reinterpret_cast<const bf16x8_t *>(x), perm, topk, FastDiv(H / 16), maxc, n_rows,
+                     afmt, ascale, reinterpret_cast<bf16x8_t *>(xq));
+}
+
+void launch_swiglu_actfq(const uint16_t *h, int R_max, const int32_t *n_rows, int F, int afmt,
+                         const float *ascale, uint16_t *a, uint16_t *aq, hipStream_t st) {
+  uint32_t maxc = (uint32_t)((size_t)R_max * F / 16);
+  if (!maxc) return;
+  hipLaunchKernelGGL(k_swiglu_actfq, dim3(grid_for(maxc)), dim3(kThreads), 0, st,
+                     reinterpret_cast<const bf16x8_t *>(h), FastDiv(F / 16), maxc, n_rows, afmt, ascale,
+                     reinterpret_cast<bf16x8_t *>(a), reinterpret_cast<bf16x8_t *>(aq));
+}
+
+void launch_swiglu_bwd(const uint16_t *daq, const uint16_t *h, int R_max, const int32_t *n_rows,
+                       int F, int afmt, const float *ascale, uint16_t *dh, hipStream_t st) {
+  uint32_t maxc = (uint32_t)((size_t)R_max * F / 16);
+  if (!maxc) return;
+  hipLaunchKernelGGL(k_swiglu_bwd, dim3(grid_for(maxc)), dim3(kThreads), 0, st,
+                     reinterpret_cast<const bf16x8_t *>(daq), reinterpret_cast<const bf16x8_t *>(h),
+                     FastDiv(F / 16), maxc, n_rows, afmt, ascale, reinterpret_cast<bf16x8_t *>(dh));
+}
+
+void launch_combine(const uint16_t *o, const float *probs, const int32_t *row_of, int T, int topk,
+                    int H, uint16_t *out, hipStream_t st) {
+  uint32_t nchunk = (uint32_t)((size_t)T * H / 16);
+  if (!nchunk) return;
+  hipLaunchKernelGGL(k_combine, dim3(grid_for(nchunk)), dim3(kThreads), 0, st,
+                     reinterpret_cast<const bf16x8_t *>(o), probs, row_of, topk, FastDiv(H / 16),
+                     nchunk, reinterpret_cast<bf16x8_t *>(out));
+}
+
+void launch_combine_bwd(const uint16_t *dout, const float *probs, const int32_t *perm, int topk,
+                        int H, int R_max, const int32_t *n_rows, uint16_t *dO, hipStream_t st) {
+  uint32_t maxc = (uint32_t)((size_t)R_max * H / 16);
+  if (!maxc) return;
+  hipLaunchKernelGGL(k_combine_bwd, dim3(grid_for(maxc)), dim3(kThreads), 0, st,
+                     reinterpret_cast<const bf16x8_t *>(dout), probs, perm, topk, FastDiv(H / 16), maxc,
+                     n_rows, reinterpret_cast<bf16x8_t *>(dO));
+}
+
+void launch_unpermute_reduce(const uint16_t *dxq, const int32_t *row_of, const uint16_t *x, int T,
+                             int topk, int H, int afmt, const float *ascale, uint16_t *dx,
+                             hipStream_t st) {
+  uint32_t nchunk = (uint32_t)((size_t)T * H / 16);
+  if (!nchunk) return;
+  hipLaunchKernelGGL(k_unpermute_reduce, dim3(grid_for(nchunk)), dim3(kThreads), 0, st,
+                     reinterpret_cast<const bf16x8_t *>(dxq), row_of,
+                     reinterpret_cast<const bf16x8_t *>(x), topk, FastDiv(H / 16), nchunk, afmt, ascale,
+                     reinterpret_cast<bf16x8_t *>(dx));
+}
+
+void launch_reduce_partials(const float *part, int P, size_t n, float *out, hipStream_t st) {
+  if (!n) return;
+  hipLaunchKernelGGL(k_reduce_partials, dim3(grid_for((long)n)), dim3(kThreads), 0, st, part, P,
+                     (uint32_t)n, out);
+}
+
+}  // namespace fq

@@ -1,0 +1,492 @@
+// Grouped GEMM over routed rows on gfx950 bf16 MFMA (v_mfma_f32_32x32x16_bf16),
+// fp32 accumulation: all experts of a stack in one launch (AngelSlim mcore_qad
+// article, section 二.4), forward and the scale-only backward (section 一).
+//
+// One kernel computes C[i][j] = sum_c P[i][c] * Q[j][c] on a 256 x 256 tile
+// with a 64-deep contraction step; four waves, each 128 x 128 (4 x 4 MFMA
+// 32x32 sub-tiles). Operands are staged global -> registers -> LDS (double
+// buffered), LDS rows are 128 B with a 16-byte-slot XOR swizzle so that both
+// the staging writes and the MFMA fragment reads are bank-conflict free.
+//
+//   mode   P (row operand, i)          Q (column operand, j)     contraction
+//   FWD    W_fq[e] rows n   (K-contig) X rows r of segment e      k
+//   DGRAD  W_fq[e] as [n][k] -> i = k  dY rows r (N-contig)       n
+//          (transposed on the way into LDS)
+//   WGRAD  X rows -> i = k (transposed) dY rows -> j = n (transp.) routed rows r
+//
+// A "transposed" operand is read as 8 contraction rows x 8 contiguous
+// columns per lane (eight 16-byte loads) and turned into eight 8-long
+// contraction vectors with v_perm_b32 before its LDS write.
+//
+// FWD / DGRAD store bf16 rows; WGRAD never stores dW: its epilogue
+// multiplies each dWq element by the straight-through factor dv/ds
+// (recomputed from the raw weight and its scale) and reduces over the
+// quantization group (dScale), deterministically.
+//
+// Scheduling: FWD / DGRAD tiles are (expert, row tile, i tile); the number of
+// row tiles of each expert comes from seg_offsets on the device (a block-wide
+// scan in LDS), so empty experts cost nothing and no host sync is needed.
+// Block ids are remapped so that consecutive tiles land on the same XCD (the
+// hardware deals blocks round-robin over the 8 XCDs), keeping an expert's
+// weights and rows in one XCD's L2.
+#include "internal.hpp"
+
+namespace fq {
+
+namespace {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8v;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+
+constexpr int BI = 256;   // tile rows (i)
+constexpr int BJ = 256;   // tile cols (j)
+constexpr int BK = 64;    // contraction step
+constexpr int NT = 256;   // threads per block (4 waves)
+constexpr int kTileBytes = 256 * BK * 2;  // one operand tile in LDS (32 KiB)
+
+enum Mode { FWD = 0, DGRAD = 1, WGRAD = 2 };
+
+// byte offset of 16-byte slot kc (0..7) of LDS row idx (0..255)
+__device__ __forceinline__ uint32_t lds_off(uint32_t idx, uint32_t kc) {
+  uint32_t swz = (idx ^ (idx >> 3)) & 7u;
+  return idx * 128u + ((kc ^ swz) << 4);
+}
+
+__device__ __forceinline__ bf16x8_t ldg16(const uint16_t *p) {
+  return *reinterpret_cast<const bf16x8_t *>(p);
+}
+
+// ---- normal operand: 256 rows of a row-major matrix, 64 contiguous contraction
+// elements each. Thread t: rows u*32 + t/8 (u = 0..7), 16-byte slot t%8.
+__device__ __forceinline__ void load_normal(bf16x8_t (&v)[8], const uint16_t *base, size_t ld,
+                                            int row0, int row_last, int c0) {
+  const int t = threadIdx.x;
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    int r = min(row0 + u * 32 + (t >> 3), row_last);
+    v[u] = ldg16(base + (size_t)r * ld + c0 + (t & 7) * 8);
+  }
+}
+__device__ __forceinline__ void store_normal(char *lds, const bf16x8_t (&v)[8]) {
+  const int t = threadIdx.x;
+#pragma unroll
+  for (int u = 0; u < 8; ++u)
+    *reinterpret_cast<bf16x8_t *>(lds + lds_off(u * 32 + (t >> 3), t & 7)) = v[u];
+}
+
+// ---- transposed operand: element (c, idx) at base[c * ld + idx]; the tile is
+// contraction rows c0..c0+63 x idx idx0..idx0+255. Thread t: idx block t%32
+// (8 columns), contraction block t/32 (8 rows). Rows c >= c_end read as 0.
+__device__ __forceinline__ void load_trans(bf16x8_t (&v)[8], const uint16_t *base, size_t ld, int c0,
+                                           int c_end, int idx0) {
+  const int t = threadIdx.x;
+  const int col = idx0 + (t & 31) * 8;
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    int c = c0 + (t >> 5) * 8 + q;
+    bool ok = c < c_end;
+    int cc = ok ? c : c0;  // c0 < c_end whenever this tile is loaded
+    bf16x8_t x = ldg16(base + (size_t)cc * ld + col);
+    v[q].w[0] = ok ? x.w[0] : 0u;
+    v[q].w[1] = ok ? x.w[1] : 0u;
+    v[q].w[2] = ok ? x.w[2] : 0u;
+    v[q].w[3] = ok ? x.w[3] : 0u;
+  }
+}
+__device__ __forceinline__ void store_trans(char *lds, const bf16x8_t (&v)[8]) {
+  const int t = threadIdx.x;
+  const uint32_t idxb = (t & 31) * 8, kc = t >> 5;
+  // out[j] (column idxb + j) gathers element j of the 8 input rows
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    bf16x8_t lo, hi;  // columns 2p and 2p+1
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      lo.w[q] = __builtin_amdgcn_perm(v[2 * q + 1].w[p], v[2 * q].w[p], 0x05040100u);
+      hi.w[q] = __builtin_amdgcn_perm(v[2 * q + 1].w[p], v[2 * q].w[p], 0x07060302u);
+    }
+    *reinterpret_cast<bf16x8_t *>(lds + lds_off(idxb + 2 * p, kc)) = lo;
+    *reinterpret_cast<bf16x8_t *>(lds + lds_off(idxb + 2 * p + 1, kc)) = hi;
+  }
+}
+
+struct GemmArgs {
+  const uint16_t *p;   // FWD/DGRAD: W_fq [E,N,K]; WGRAD: Xq [R_max, K]
+  const uint16_t *q;   // FWD: Xq [R_max, K]; DGRAD/WGRAD: dY [R_max, N]
+  const int32_t *seg;  // [E+1]
+  int E, N, K;
+  int n_it;            // i tiles
+  int n_jt;            // WGRAD: j tiles
+  // FWD/DGRAD output [R_max, ldo]
+  uint16_t *out;
+  // WGRAD epilogue
+  const uint16_t *w;   // raw weights [E,N,K]
+  int wfmt, group;
+  const float *scale, *zero_point, *gscale;
+  float *dscale, *dzp;     // final outputs (group <= 128), or NULL
+  float *pscale, *pzp;     // partials per 128-chunk of K (group > 128), or NULL
+};
+
+// Expert and first row of this block's row tile: block-wide scan of per-expert
+// row-tile counts (E <= 256 per pass, looped). Returns false when the block
+// has no tile.
+__device__ bool find_row_tile(const int32_t *seg, int E, int tile, int &e_out, int &row0,
+                              int &row_end) {
+  __shared__ int s_found[3];
+  __shared__ int s_wsum[NT / 64];
+  if (threadIdx.x == 0) s_found[0] = -1;
+  __syncthreads();
+  int base_tiles = 0;
+  for (int e0 = 0; e0 < E; e0 += NT) {
+    int e = e0 + threadIdx.x;
+    int lo = 0, hi = 0, nt = 0;
+    if (e < E) {
+      lo = seg[e];
+      hi = seg[e + 1];
+      nt = (hi - lo + BJ - 1) / BJ;
+    }
+    // inclusive scan of nt
+    int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    int x = nt;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      int y = __shfl_up(x, o, 64);
+      if (lane >= o) x += y;
+    }
+    if (lane == 63) s_wsum[w] = x;
+    __syncthreads();
+    int before = base_tiles, total = base_tiles;
+#pragma unroll
+    for (int k = 0; k < NT / 64; ++k) {
+      if (k < w) before += s_wsum[k];
+      total += s_wsum[k];
+    }
+    int start = before + x - nt;
+    if (e < E && tile >= start && tile < start + nt) {
+      s_found[0] = e;
+      s_found[1] = lo + (tile - start) * BJ;
+      s_found[2] = hi;
+    }
+    __syncthreads();
+    base_tiles = total;
+  }
+  e_out = s_found[0];
+  row0 = s_found[1];
+  row_end = s_found[2];
+  return e_out >= 0;
+}
+
+// dS of the 128 (k) x 32 (n) slab of dWq that column sub-tile U of one wave
+// holds: lane n = n0 + lane%32, k = k0 + 32s + 8q + 4(lane/32) + v for
+// acc[s][U][4q + v]. Each dWq element is weighted by its straight-through
+// factor and summed over its quantization group in a fixed order.
+template <int WFMT, int U>
+__device__ __forceinline__ void wgrad_epilogue(const GemmArgs &a, const f32x16 (&acc)[4][4], int e,
+                                               int k0, int n0, int lane) {
+  const int n = n0 + (lane & 31);
+  const int G = a.K / a.group;
+  const float g_e = (WFMT == FQ_FMT_NVFP4) ? a.gscale[e] : 1.0f;
+  const uint16_t *wrow = a.w + ((size_t)e * a.N + n) * a.K;
+  const size_t srow = ((size_t)e * a.N + n) * G;
+  float part_s[4], part_z[4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    float ps16[2] = {0.0f, 0.0f}, pz16[2] = {0.0f, 0.0f};  // the sub-tile's two 16-blocks
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int k = k0 + s * 32 + 8 * q + 4 * (lane >> 5);
+      const uint2 wv = *reinterpret_cast<const uint2 *>(wrow + k);
+      const float x4[4] = {lo_bf16(wv.x), hi_bf16(wv.x), lo_bf16(wv.y), hi_bf16(wv.y)};
+      const int gi = k / a.group;
+      float sc = a.scale[srow + gi];
+      float zpi = 0.0f, fac = 1.0f;
+      if (WFMT == FQ_FMT_INT4) zpi = fminf(fmaxf(rintf(a.zero_point[srow + gi]), 0.0f), 15.0f);
+      if (WFMT == FQ_FMT_NVFP4) {
+        fac = nvfp4_theta_factor(sc, g_e);
+        sc = nvfp4_block_scale(sc, g_e);
+      }
+      const float r = safe_recip(sc);
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const FQElem fe = fq_weight_elem(WFMT, x4[v], sc, r, zpi);
+        const float d = acc[s][U][4 * q + v];
+        ps16[q >> 1] += d * (fe.dvds * fac);
+        if (WFMT == FQ_FMT_INT4) pz16[q >> 1] += d * fe.dvdzp;
+      }
+    }
+    // a 16-block is split between this lane (k%8 < 4 or >= 4) and lane ^ 32
+#pragma unroll
+    for (int b2 = 0; b2 < 2; ++b2) {
+      ps16[b2] += __shfl_xor(ps16[b2], 32, 64);
+      if (WFMT == FQ_FMT_INT4) pz16[b2] += __shfl_xor(pz16[b2], 32, 64);
+    }
+    if (a.group == 16 && lane < 32) {
+      const int kb = (k0 + s * 32) / 16;
+      a.dscale[srow + kb] = ps16[0];
+      a.dscale[srow + kb + 1] = ps16[1];
+      if (WFMT == FQ_FMT_INT4 && a.dzp) {
+        a.dzp[srow + kb] = pz16[0];
+        a.dzp[srow + kb + 1] = pz16[1];
+      }
+    }
+    part_s[s] = ps16[0] + ps16[1];
+    part_z[s] = pz16[0] + pz16[1];
+  }
+  if (lane < 32 && a.group != 16) {
+    if (a.group == 32) {
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const int kb = (k0 + s * 32) / 32;
+        a.dscale[srow + kb] = part_s[s];
+        if (WFMT == FQ_FMT_INT4 && a.dzp) a.dzp[srow + kb] = part_z[s];
+      }
+    } else if (a.group == 64) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int kb = (k0 + h * 64) / 64;
+        a.dscale[srow + kb] = part_s[2 * h] + part_s[2 * h + 1];
+        if (WFMT == FQ_FMT_INT4 && a.dzp) a.dzp[srow + kb] = part_z[2 * h] + part_z[2 * h + 1];
+      }
+    } else {
+      const float s128 = (part_s[0] + part_s[1]) + (part_s[2] + part_s[3]);
+      const float z128 = (part_z[0] + part_z[1]) + (part_z[2] + part_z[3]);
+      const int kb = k0 / 128;
+      if (a.group == 128) {
+        a.dscale[srow + kb] = s128;
+        if (WFMT == FQ_FMT_INT4 && a.dzp) a.dzp[srow + kb] = z128;
+      } else {
+        const size_t prow = ((size_t)e * a.N + n) * (a.K / 128);
+        a.pscale[prow + kb] = s128;
+        if (WFMT == FQ_FMT_INT4 && a.pzp) a.pzp[prow + kb] = z128;
+      }
+    }
+  }
+}
+
+template <int MODE, int WFMT>
+__global__ __launch_bounds__(NT, 1) void k_grouped_gemm(GemmArgs a) {
+  __shared__ __attribute__((aligned(16))) char smem[4 * kTileBytes];  // P0 Q0 P1 Q1 = 128 KiB
+  const int t = threadIdx.x;
+  const int lane = t & 63, wave = t >> 6;
+  const int wi = wave & 1, wj = wave >> 1;
+
+  // XCD-aware remap of the block id
+  const uint32_t nb = gridDim.x, b = blockIdx.x;
+  const uint32_t wid = (b & 7u) * (nb >> 3) + (b >> 3);
+
+  int e, it, j0 = 0, j_end = 0, i0;
+  int c_total;  // contraction length
+  if (MODE == WGRAD) {
+    const int per_e = a.n_it * a.n_jt;
+    e = wid / per_e;
+    if (e >= a.E) return;
+    int rem = wid - e * per_e;
+    int jt = rem / a.n_it;
+    it = rem - jt * a.n_it;
+    j0 = jt * BJ;
+    i0 = it * BI;
+  } else {
+    int tile = wid / a.n_it;
+    it = wid - tile * a.n_it;
+    i0 = it * BI;
+    if (!find_row_tile(a.seg, a.E, tile, e, j0, j_end)) return;
+  }
+  const int seg_lo = a.seg[e], seg_hi = a.seg[e + 1];
+  if (MODE == WGRAD) c_total = seg_hi - seg_lo;
+  else c_total = (MODE == FWD) ? a.K : a.N;
+
+  // operand base pointers
+  const size_t NK = (size_t)a.N * a.K;
+  const uint16_t *pbase, *qbase;
+  size_t pld, qld;
+  if (MODE == FWD) {
+    pbase = a.p + e * NK;                 // W_fq[e] [N][K], rows i = n
+    pld = a.K;
+    qbase = a.q;                          // Xq rows, row index absolute
+    qld = a.K;
+  } else if (MODE == DGRAD) {
+    pbase = a.p + e * NK;                 // W_fq[e] as (c = n, idx = k)
+    pld = a.K;
+    qbase = a.q;                          // dY rows
+    qld = a.N;
+  } else {
+    pbase = a.p + (size_t)seg_lo * a.K;   // Xq rows of the segment: (c = r, idx = k)
+    pld = a.K;
+    qbase = a.q + (size_t)seg_lo * a.N;   // dY rows of the segment: (c = r, idx = n)
+    qld = a.N;
+  }
+
+  f32x16 acc[4][4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s)
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[s][u][v] = 0.0f;
+
+  const int nk = (c_total + BK - 1) / BK;
+  bf16x8_t rp[8], rq[8];
+
+  auto load_tile = [&](int kt) {
+    const int c0 = kt * BK;
+    if (MODE == FWD) {
+      load_normal(rp, pbase, pld, i0, a.N - 1, c0);
+      load_normal(rq, qbase, qld, j0, j_end - 1, c0);
+    } else if (MODE == DGRAD) {
+      load_trans(rp, pbase, pld, c0, c_total, i0);
+      load_normal(rq, qbase, qld, j0, j_end - 1, c0);
+    } else {
+      load_trans(rp, pbase, pld, c0, c_total, i0);
+      load_trans(rq, qbase, qld, c0, c_total, j0);
+    }
+  };
+  auto store_tile = [&](int buf) {
+    char *sp = smem + (2 * buf) * kTileBytes;
+    char *sq = smem + (2 * buf + 1) * kTileBytes;
+    if (MODE == FWD) {
+      store_normal(sp, rp);
+      store_normal(sq, rq);
+    } else if (MODE == DGRAD) {
+      store_trans(sp, rp);
+      store_normal(sq, rq);
+    } else {
+      store_trans(sp, rp);
+      store_trans(sq, rq);
+    }
+  };
+
+  if (nk > 0) {
+    load_tile(0);
+    store_tile(0);
+    __syncthreads();
+  }
+  for (int kt = 0; kt < nk; ++kt) {
+    const int cur = kt & 1;
+    if (kt + 1 < nk) load_tile(kt + 1);
+    const char *sp = smem + (2 * cur) * kTileBytes;
+    const char *sq = smem + (2 * cur + 1) * kTileBytes;
+#pragma unroll
+    for (int ks = 0; ks < BK / 16; ++ks) {
+      const uint32_t kc = ks * 2 + (lane >> 5);
+      bf16x8v fp[4], fq_[4];
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+        fp[s] = *reinterpret_cast<const bf16x8v *>(sp + lds_off(wi * 128 + s * 32 + (lane & 31), kc));
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        fq_[u] = *reinterpret_cast<const bf16x8v *>(sq + lds_off(wj * 128 + u * 32 + (lane & 31), kc));
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          acc[s][u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fp[s], fq_[u], acc[s][u], 0, 0, 0);
+    }
+    if (kt + 1 < nk) store_tile(cur ^ 1);
+    __syncthreads();
+  }
+
+  // accumulator (s, u, v) of this lane: i = i0 + wi*128 + s*32 + 8*(v/4) + 4*(lane/32) + v%4,
+  //                                     j = j0 + wj*128 + u*32 + lane%32
+  if (MODE != WGRAD) {
+    const int ldo = (MODE == FWD) ? a.N : a.K;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int j = j0 + wj * 128 + u * 32 + (lane & 31);
+      if (j >= j_end) continue;
+      uint16_t *orow = a.out + (size_t)j * ldo;
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int i = i0 + wi * 128 + s * 32 + 8 * q + 4 * (lane >> 5);
+          uint2 pk;
+          pk.x = pack_bf16(acc[s][u][4 * q + 0], acc[s][u][4 * q + 1]);
+          pk.y = pack_bf16(acc[s][u][4 * q + 2], acc[s][u][4 * q + 3]);
+          *reinterpret_cast<uint2 *>(orow + i) = pk;
+        }
+    }
+    return;
+  }
+
+  // ---- WGRAD epilogue: i = k, j = n of expert e. dS over groups along k.
+  {
+    const int k0 = i0 + wi * 128, n0 = j0 + wj * 128;
+    wgrad_epilogue<WFMT, 0>(a, acc, e, k0, n0, lane);
+    wgrad_epilogue<WFMT, 1>(a, acc, e, k0, n0 + 32, lane);
+    wgrad_epilogue<WFMT, 2>(a, acc, e, k0, n0 + 64, lane);
+    wgrad_epilogue<WFMT, 3>(a, acc, e, k0, n0 + 96, lane);
+  }
+}
+
+}  // namespace
+
+// ============================================================ launchers ====
+static int round8(long x) { return (int)((x + 7) / 8 * 8); }
+
+void launch_gemm_fwd(const uint16_t *xq, int R_max, const int32_t *seg, fq_shape s,
+                     const uint16_t *wfq, uint16_t *y, hipStream_t st) {
+  GemmArgs a{};
+  a.p = wfq;
+  a.q = xq;
+  a.seg = seg;
+  a.E = s.E;
+  a.N = s.N;
+  a.K = s.K;
+  a.n_it = s.N / BI;
+  a.out = y;
+  long tiles = (long)(R_max / BJ + s.E) * a.n_it;
+  if (tiles <= 0 || R_max <= 0) return;
+  hipLaunchKernelGGL((k_grouped_gemm<FWD, 0>), dim3(round8(tiles)), dim3(NT), 0, st, a);
+}
+
+void launch_gemm_dgrad(const uint16_t *dy, int R_max, const int32_t *seg, fq_shape s,
+                       const uint16_t *wfq, uint16_t *dx, hipStream_t st) {
+  GemmArgs a{};
+  a.p = wfq;
+  a.q = dy;
+  a.seg = seg;
+  a.E = s.E;
+  a.N = s.N;
+  a.K = s.K;
+  a.n_it = s.K / BI;
+  a.out = dx;
+  long tiles = (long)(R_max / BJ + s.E) * a.n_it;
+  if (tiles <= 0 || R_max <= 0) return;
+  hipLaunchKernelGGL((k_grouped_gemm<DGRAD, 0>), dim3(round8(tiles)), dim3(NT), 0, st, a);
+}
+
+void launch_gemm_wgrad_dscale(const uint16_t *dy, const uint16_t *xq, const int32_t *seg, fq_shape s,
+                              const uint16_t *w, const fq_weight_q &q, float *dscale, float *dzp,
+                              float *pscale, float *pzp, hipStream_t st) {
+  GemmArgs a{};
+  a.p = xq;
+  a.q = dy;
+  a.seg = seg;
+  a.E = s.E;
+  a.N = s.N;
+  a.K = s.K;
+  a.n_it = s.K / BI;
+  a.n_jt = s.N / BJ;
+  a.w = w;
+  a.wfmt = q.fmt;
+  a.group = q.group;
+  a.scale = q.scale;
+  a.zero_point = q.zero_point;
+  a.gscale = q.global_scale;
+  a.dscale = dscale;
+  a.dzp = dzp;
+  a.pscale = pscale;
+  a.pzp = pzp;
+  long tiles = (long)s.E * a.n_it * a.n_jt;
+  dim3 grid(round8(tiles)), block(NT);
+  switch (q.fmt) {
+    case FQ_FMT_INT8: hipLaunchKernelGGL((k_grouped_gemm<WGRAD, FQ_FMT_INT8>), grid, block, 0, st, a); break;
+    case FQ_FMT_INT4: hipLaunchKernelGGL((k_grouped_gemm<WGRAD, FQ_FMT_INT4>), grid, block, 0, st, a); break;
+    case FQ_FMT_FP8_E4M3:
+      hipLaunchKernelGGL((k_grouped_gemm<WGRAD, FQ_FMT_FP8_E4M3>), grid, block, 0, st, a);
+      break;
+    default: hipLaunchKernelGGL((k_grouped_gemm<WGRAD, FQ_FMT_NVFP4>), grid, block, 0, st, a); break;
+  }
+}
+
+}  // namespace fq

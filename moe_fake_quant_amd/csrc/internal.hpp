@@ -1,0 +1,48 @@
+// Internal launchers of libfq (not part of the C ABI).
+#pragma once
+
+#include "codec.hpp"
+#include "common.hpp"
+
+namespace fq {
+
+void launch_fill_u32(uint32_t *p, uint32_t v, long n, hipStream_t st);
+void launch_quantize_stacked(const uint16_t *w, fq_shape s, const fq_weight_q &q, uint16_t *out,
+                             uint8_t *codes, hipStream_t st);
+void launch_observer_weight(const uint16_t *w, fq_shape s, int fmt, int group, float *scale,
+                            float *zero_point, float *gscale, hipStream_t st);
+void launch_observer_tensor(const uint16_t *x, size_t n, int fmt, float *scale, hipStream_t st);
+// n_rows (device, may be NULL): only the first n_rows[0] of the M rows are processed
+void launch_act_fq(const uint16_t *x, size_t M, int K, const int32_t *n_rows, int afmt,
+                   const float *ascale, uint16_t *xq, hipStream_t st);
+void launch_act_mask(uint16_t *dx, const uint16_t *x, size_t M, int K, const int32_t *n_rows,
+                     int afmt, const float *ascale, hipStream_t st);
+void launch_gather_actfq(const uint16_t *x, int H, const int32_t *perm, int topk, int R_max,
+                         const int32_t *n_rows, int afmt, const float *ascale, uint16_t *xq,
+                         hipStream_t st);
+void launch_swiglu_actfq(const uint16_t *h, int R_max, const int32_t *n_rows, int F, int afmt,
+                         const float *ascale, uint16_t *a, uint16_t *aq, hipStream_t st);
+void launch_swiglu_bwd(const uint16_t *daq, const uint16_t *h, int R_max, const int32_t *n_rows,
+                       int F, int afmt, const float *ascale, uint16_t *dh, hipStream_t st);
+void launch_combine(const uint16_t *o, const float *probs, const int32_t *row_of, int T, int topk,
+                    int H, uint16_t *out, hipStream_t st);
+void launch_combine_bwd(const uint16_t *dout, const float *probs, const int32_t *perm, int topk,
+                        int H, int R_max, const int32_t *n_rows, uint16_t *dO, hipStream_t st);
+void launch_unpermute_reduce(const uint16_t *dxq, const int32_t *row_of, const uint16_t *x, int T,
+                             int topk, int H, int afmt, const float *ascale, uint16_t *dx,
+                             hipStream_t st);
+void launch_reduce_partials(const float *part, int P, size_t n, float *out, hipStream_t st);
+
+size_t permute_workspace_bytes(int E, long P);
+void launch_permute(const int32_t *ids, int T, int topk, int ebegin, int E, int32_t *perm,
+                    int32_t *row_of, int32_t *seg, void *ws, hipStream_t st);
+
+void launch_gemm_fwd(const uint16_t *xq, int R_max, const int32_t *seg, fq_shape s,
+                     const uint16_t *wfq, uint16_t *y, hipStream_t st);
+void launch_gemm_dgrad(const uint16_t *dy, int R_max, const int32_t *seg, fq_shape s,
+                       const uint16_t *wfq, uint16_t *dx, hipStream_t st);
+void launch_gemm_wgrad_dscale(const uint16_t *dy, const uint16_t *xq, const int32_t *seg, fq_shape s,
+                              const uint16_t *w, const fq_weight_q &q, float *dscale, float *dzp,
+                              float *pscale, float *pzp, hipStream_t st);
+
+}  // namespace fq

@@ -1,0 +1,169 @@
+"""One MoE layer's routed-expert path through libfq (orchestration only).
+
+The AngelSlim mcore_qad article (section 二.4) replaces a layer's experts with
+3D stacks, fake-quantizes each stack in one pass and runs all experts as one
+grouped GEMM; weights are frozen and only quantizer scales train (section 一).
+This class holds the device buffers of that path and calls the C ABI in
+order; it computes nothing itself.
+
+Forward:  FQ pass on both stacks -> permute -> gather + act FQ -> gate_up GEMM
+          -> SwiGLU + act FQ -> down GEMM -> combine
+Backward: combine bwd -> down dgrad + dScale -> SwiGLU bwd (with the act-FQ
+          mask) -> gate_up dgrad + dScale -> unpermute-reduce (with the input
+          act-FQ mask)
+All buffers are allocated once; a step allocates nothing.
+"""
+from __future__ import annotations
+
+from typing import Optional
+
+import torch
+
+from . import (ActQ, FMT_INT4, FMT_NONE, FMT_NVFP4, FQ_OP_GEMM_BWD, FQ_OP_GEMM_FWD,
+               FQ_OP_PERMUTE, WeightQ, fq_grouped_gemm_bwd_scale, fq_grouped_gemm_fwd,
+               fq_moe_combine, fq_moe_combine_bwd, fq_moe_gather_actfq, fq_moe_permute,
+               fq_moe_unpermute_reduce, fq_quantize_stacked, fq_swiglu_actfq, fq_swiglu_bwd,
+               fq_workspace_bytes, observer_absmax_init)
+
+
+def _weight_q(E, N, K, fmt, group, dev) -> WeightQ:
+    G = K // group
+    q = WeightQ(fmt=fmt, group=group, scale=torch.empty(E, N, G, dtype=torch.float32, device=dev))
+    if fmt == FMT_INT4:
+        q.zero_point = torch.empty(E, N, G, dtype=torch.float32, device=dev)
+    if fmt == FMT_NVFP4:
+        q.global_scale = torch.empty(E, dtype=torch.float32, device=dev)
+    return q
+
+
+class MoEFakeQuantLayer:
+    def __init__(self, w_gu: torch.Tensor, w_d: torch.Tensor, wfmt: int, afmt: int, T_max: int,
+                 topk: int, expert_begin: int = 0, group: Optional[int] = None):
+        """w_gu [E, 2F, H], w_d [E, H, F] bf16 on the device (frozen). group None =
+        one scale per output channel (group = K of each stack)."""
+        assert w_gu.dtype == torch.bfloat16 and w_d.dtype == torch.bfloat16
+        self.dev = w_gu.device
+        self.E, F2, self.H = w_gu.shape
+        self.F = F2 // 2
+        assert tuple(w_d.shape) == (self.E, self.H, self.F)
+        self.wfmt, self.afmt = wfmt, afmt
+        self.topk, self.expert_begin = topk, expert_begin
+        self.T_max = T_max
+        self.R_max = T_max * topk
+        self.w_gu, self.w_d = w_gu.contiguous(), w_d.contiguous()
+        self.shape_gu = (self.E, 2 * self.F, self.H)
+        self.shape_d = (self.E, self.H, self.F)
+        g_gu = group or self.H
+        g_d = group or self.F
+        self.q_gu = _weight_q(*self.shape_gu, wfmt, g_gu, self.dev)
+        self.q_d = _weight_q(*self.shape_d, wfmt, g_d, self.dev)
+        f32 = dict(dtype=torch.float32, device=self.dev)
+        bf = dict(dtype=torch.bfloat16, device=self.dev)
+        i32 = dict(dtype=torch.int32, device=self.dev)
+        self.aq1 = ActQ(afmt, torch.ones(1, **f32))
+        self.aq2 = ActQ(afmt, torch.ones(1, **f32))
+        self.wfq_gu = torch.empty(self.shape_gu, **bf)
+        self.wfq_d = torch.empty(self.shape_d, **bf)
+        R, H, F = self.R_max, self.H, self.F
+        self.perm = torch.empty(R, **i32)
+        self.row_of = torch.empty(T_max, topk, **i32)
+        self.seg = torch.empty(self.E + 1, **i32)
+        self.n_rows = self.seg[self.E:]
+        self.xq = torch.empty(R, H, **bf)
+        self.h = torch.empty(R, 2 * F, **bf)
+        self.a = torch.empty(R, F, **bf)
+        self.aq = torch.empty(R, F, **bf)
+        self.o = torch.empty(R, H, **bf)
+        self.out = torch.empty(T_max, H, **bf)
+        self.do = torch.empty(R, H, **bf)
+        self.daq = torch.empty(R, F, **bf)
+        self.dh = torch.empty(R, 2 * F, **bf)
+        self.dxq = torch.empty(R, H, **bf)
+        self.dx = torch.empty(T_max, H, **bf)
+        self.ds_gu = torch.empty_like(self.q_gu.scale)
+        self.ds_d = torch.empty_like(self.q_d.scale)
+        self.dzp_gu = torch.empty_like(self.q_gu.scale) if wfmt == FMT_INT4 else None
+        self.dzp_d = torch.empty_like(self.q_d.scale) if wfmt == FMT_INT4 else None
+        ws = max(fq_workspace_bytes(FQ_OP_PERMUTE, (self.E, 0, 0), self.R_max, 0),
+                 fq_workspace_bytes(FQ_OP_GEMM_FWD, self.shape_gu, R, 0),
+                 fq_workspace_bytes(FQ_OP_GEMM_FWD, self.shape_d, R, 0),
+                 fq_workspace_bytes(FQ_OP_GEMM_BWD, self.shape_gu, R, 0),
+                 fq_workspace_bytes(FQ_OP_GEMM_BWD, self.shape_d, R, 0), 256)
+        self.ws = torch.empty(ws, dtype=torch.uint8, device=self.dev)
+        self.T = 0
+
+    # ------------------------------------------------------------- setup --
+    def init_weight_scales(self):
+        """Observer init of both stacks' learnable scales."""
+        for w, shape, q in ((self.w_gu, self.shape_gu, self.q_gu), (self.w_d, self.shape_d, self.q_d)):
+            observer_absmax_init(w, shape, q.fmt, q.group, 0, q.scale, q.zero_point, q.global_scale)
+
+    def quantize_weights(self):
+        """One fake-quant pass over each whole stack."""
+        fq_quantize_stacked(self.w_gu, self.shape_gu, self.q_gu, self.wfq_gu)
+        fq_quantize_stacked(self.w_d, self.shape_d, self.q_d, self.wfq_d)
+
+    def route(self, expert_ids: torch.Tensor):
+        T = expert_ids.shape[0]
+        assert T <= self.T_max and expert_ids.shape[1] == self.topk
+        self.T = T
+        fq_moe_permute(expert_ids, T, self.topk, self.expert_begin, self.E, self.perm,
+                       self.row_of[:T], self.seg, self.ws)
+
+    def calibrate(self, x: torch.Tensor, expert_ids: torch.Tensor):
+        """Frozen activation scales from one calibration forward (reads R on the host)."""
+        if self.afmt == FMT_NONE:
+            return
+        T = x.shape[0]
+        observer_absmax_init(x, (1, T, self.H), self.afmt, 16, 1, self.aq1.scale)
+        self.quantize_weights()
+        self.route(expert_ids)
+        R = int(self.seg[self.E].item())
+        fq_moe_gather_actfq(x, T, self.H, self.perm, self.topk, self.R_max, self.n_rows, self.aq1,
+                            self.xq)
+        fq_grouped_gemm_fwd(self.xq, self.R_max, self.seg, self.shape_gu, None, self.wfq_gu,
+                            self.q_gu, None, self.h, self.ws)
+        fq_swiglu_actfq(self.h, self.R_max, self.n_rows, self.F, None, self.a, self.aq)
+        if R > 0:
+            observer_absmax_init(self.a[:R], (1, R, self.F), self.afmt, 16, 1, self.aq2.scale)
+
+    # ---------------------------------------------------------- hot path --
+    def forward(self, x: torch.Tensor, expert_ids: torch.Tensor, probs: torch.Tensor,
+                keep_a: bool = False) -> torch.Tensor:
+        T = x.shape[0]
+        self.route(expert_ids)
+        fq_moe_gather_actfq(x, T, self.H, self.perm, self.topk, self.R_max, self.n_rows, self.aq1,
+                            self.xq)
+        fq_grouped_gemm_fwd(self.xq, self.R_max, self.seg, self.shape_gu, None, self.wfq_gu,
+                            self.q_gu, None, self.h, self.ws)
+        fq_swiglu_actfq(self.h, self.R_max, self.n_rows, self.F, self.aq2,
+                        self.a if keep_a else None, self.aq)
+        fq_grouped_gemm_fwd(self.aq, self.R_max, self.seg, self.shape_d, None, self.wfq_d,
+                            self.q_d, None, self.o, self.ws)
+        fq_moe_combine(self.o, probs, self.row_of[:T], T, self.topk, self.H, self.out[:T])
+        return self.out[:T]
+
+    def backward(self, x: torch.Tensor, probs: torch.Tensor, dout: torch.Tensor):
+        T = x.shape[0]
+        fq_moe_combine_bwd(dout, probs, self.perm, self.topk, self.H, self.R_max, self.n_rows,
+                           self.do)
+        # dgrad and wgrad -> dScale as two calls (one GEMM kernel each)
+        fq_grouped_gemm_bwd_scale(self.do, self.aq, self.R_max, self.seg, self.shape_d, self.w_d,
+                                  self.wfq_d, self.q_d, None, self.daq, None, None, self.ws)
+        fq_grouped_gemm_bwd_scale(self.do, self.aq, self.R_max, self.seg, self.shape_d, self.w_d,
+                                  self.wfq_d, self.q_d, None, None, self.ds_d, self.dzp_d, self.ws)
+        fq_swiglu_bwd(self.daq, self.h, self.R_max, self.n_rows, self.F, self.aq2, self.dh)
+        fq_grouped_gemm_bwd_scale(self.dh, self.xq, self.R_max, self.seg, self.shape_gu, self.w_gu,
+                                  self.wfq_gu, self.q_gu, None, self.dxq, None, None, self.ws)
+        fq_grouped_gemm_bwd_scale(self.dh, self.xq, self.R_max, self.seg, self.shape_gu, self.w_gu,
+                                  self.wfq_gu, self.q_gu, None, None, self.ds_gu, self.dzp_gu,
+                                  self.ws)
+        fq_moe_unpermute_reduce(self.dxq, self.row_of[:T], x, T, self.topk, self.H, self.aq1,
+                                self.dx[:T])
+        return self.dx[:T], self.ds_gu, self.ds_d
+
+    def step(self, x, expert_ids, probs, dout):
+        """The whole hot path once: FQ pass, forward, scale-only backward."""
+        self.quantize_weights()
+        self.forward(x, expert_ids, probs)
+        return self.backward(x, probs, dout)

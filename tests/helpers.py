@@ -1,0 +1,55 @@
+"""Shared helpers of the test suite (bf16 bits <-> torch device tensors,
+tolerance checks, code packing as libfq lays it out)."""
+import numpy as np
+import torch
+
+GEMM_TOL = 2e-2      # max|gpu - ref| <= 2e-2 * max|ref|  (GEMM outputs, dX)
+DSCALE_TOL = 1e-3    # max|gpu - ref| / max|ref| <= 1e-3  (dScale, normwise)
+
+
+def dev_bf16(bits: np.ndarray) -> torch.Tensor:
+    t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16)
+    return t.cuda()
+
+
+def host_bits(t: torch.Tensor) -> np.ndarray:
+    return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def bf16_vals(bits: np.ndarray) -> np.ndarray:
+    return (np.asarray(bits, np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def dev_f32(a) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(np.asarray(a, np.float32))).cuda()
+
+
+def dev_i32(a) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(np.asarray(a, np.int32))).cuda()
+
+
+def check_gemm_tol(gpu_bits, ref_bits, what=""):
+    g, r = bf16_vals(gpu_bits), bf16_vals(ref_bits)
+    err = np.abs(g - r).max() if g.size else 0.0
+    scale = np.abs(r).max() if r.size else 0.0
+    assert err <= GEMM_TOL * scale, f"{what}: max|err| {err:.4g} > {GEMM_TOL} * {scale:.4g}"
+    return err / max(scale, 1e-30)
+
+
+def check_dscale_tol(gpu, ref, what=""):
+    g = np.asarray(gpu, np.float64)
+    r = np.asarray(ref, np.float64)
+    scale = np.abs(r).max()
+    err = np.abs(g - r).max()
+    assert err <= DSCALE_TOL * scale, f"{what}: max|err| {err:.4g} > {DSCALE_TOL} * {scale:.4g}"
+    return err / max(scale, 1e-30)
+
+
+def pack_codes(code: np.ndarray, fmt: int) -> np.ndarray:
+    """Codes as libfq writes them: one byte per element for int8 / fp8; two
+    4-bit codes per byte (even k low nibble) for int4 / nvfp4."""
+    c = np.asarray(code, np.int64).reshape(-1)
+    if fmt in (1, 3):
+        return (c & 0xFF).astype(np.uint8)
+    c = (c & 0xF).astype(np.uint8)
+    return (c[0::2] | (c[1::2] << 4)).astype(np.uint8)

@@ -1,0 +1,324 @@
+"""GPU parity of each libfq entry point against the CPU oracle on identical
+inputs (bit-exact for codes, fake-quant values, observer outputs and the
+permutation; the stated tolerances for GEMM outputs, dX and dScale).
+Calls go through the C ABI (ctypes binding)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import workloads as W
+from helpers import (bf16_vals, check_dscale_tol, check_gemm_tol, dev_bf16, dev_f32, dev_i32,
+                     host_bits, pack_codes)
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    import moe_fake_quant_amd as F
+else:  # collected on CPU only to be deselected by -m "not gpu"
+    F = None
+
+FMTS = [("int8", O.FMT_INT8), ("int4", O.FMT_INT4), ("fp8", O.FMT_FP8), ("nvfp4", O.FMT_NVFP4)]
+
+
+def _group(fmt, K):
+    return {O.FMT_INT8: K, O.FMT_FP8: K, O.FMT_INT4: 128, O.FMT_NVFP4: 16}[fmt]
+
+
+def _rand_w(rng, E, N, K, std=0.02):
+    w = rng.standard_normal((E, N, K)).astype(np.float32) * std
+    # outliers, exact zeros, negative zeros, tiny values
+    flat = w.reshape(-1)
+    idx = rng.choice(flat.size, flat.size // 200, replace=False)
+    flat[idx] *= 20.0
+    flat[idx[: len(idx) // 4]] = 0.0
+    flat[idx[len(idx) // 4: len(idx) // 2]] = -0.0
+    flat[idx[len(idx) // 2: 3 * len(idx) // 4]] *= 1e-6
+    return O.f32_to_bf16(w)
+
+
+def _wq(fmt, group, s, zp, g):
+    return F.WeightQ(fmt=fmt, group=group, scale=dev_f32(s),
+                     zero_point=None if zp is None else dev_f32(zp),
+                     global_scale=None if g is None else dev_f32(g))
+
+
+# --------------------------------------------------------------- FQ pass --
+@pytest.mark.parametrize("name,fmt", FMTS)
+def test_quantize_stacked_bitexact_observer_scales(name, fmt):
+    rng = np.random.default_rng(100 + fmt)
+    E, N, K = 3, 48, 256
+    group = _group(fmt, K)
+    w = _rand_w(rng, E, N, K)
+    s, zp, g = O.observer_weight(w, fmt, group)
+    s = (s * rng.uniform(0.5, 1.2, s.shape)).astype(np.float32)    # saturate some elements
+    if fmt == O.FMT_NVFP4:
+        s[0, 0, :2] = 0.0          # zero blocks
+        s[1, 1, 0] = 600.0         # above the E4M3 max
+    ref = O.fq_weight_stack(w, fmt, group, s, zp, g)
+    wd = dev_bf16(w)
+    out = torch.empty_like(wd)
+    ncode = E * N * K if fmt in (O.FMT_INT8, O.FMT_FP8) else E * N * K // 2
+    codes = torch.zeros(ncode, dtype=torch.uint8, device="cuda")
+    F.fq_quantize_stacked(wd, (E, N, K), _wq(fmt, group, s, zp, g), out, codes)
+    torch.cuda.synchronize()
+    assert np.array_equal(host_bits(out), ref.bits)
+    assert np.array_equal(codes.cpu().numpy(), pack_codes(ref.code, fmt))
+
+
+@pytest.mark.parametrize("name,fmt", FMTS)
+def test_quantize_stacked_bitexact_grid_ties(name, fmt):
+    """Power-of-two scales, weights at grid points and exact midpoints (ties)."""
+    rng = np.random.default_rng(200 + fmt)
+    E, N, K = 2, 32, 256
+    group = _group(fmt, K)
+    G = K // group
+    zp = g = None
+    if fmt == O.FMT_INT8:
+        grid = np.arange(-128, 128, dtype=np.float64)
+        mids = np.arange(-128, 127) + 0.5
+    elif fmt == O.FMT_INT4:
+        grid = np.arange(-8, 8, dtype=np.float64)
+        mids = np.arange(-8, 7) + 0.5
+        zp = np.full((E, N, G), 8.0, np.float32)
+    elif fmt == O.FMT_FP8:
+        grid = O.e4m3_value_of_code(np.array([c for c in range(256) if c & 0x7F != 0x7F]))
+        pos = np.unique(np.abs(grid))
+        mids = np.concatenate([(pos[:-1] + pos[1:]) / 2, -(pos[:-1] + pos[1:]) / 2])
+    else:
+        pos = O.E2M1_POS
+        grid = np.concatenate([pos, -pos])
+        mids = np.concatenate([(pos[:-1] + pos[1:]) / 2, -(pos[:-1] + pos[1:]) / 2])
+    vals = np.concatenate([grid, mids, [8192.0, -8192.0]])   # saturating, bf16-exact
+    z = rng.choice(vals, (E, N, K))
+    if fmt == O.FMT_NVFP4:
+        s = np.full((E, N, G), 2.0 ** -3, np.float32)
+        g = np.full(E, 2.0 ** -4, np.float32)
+        eff = 2.0 ** -7
+    else:
+        s = np.full((E, N, G), 2.0 ** -7, np.float32)
+        eff = 2.0 ** -7
+    w = O.f32_to_bf16((z * eff).astype(np.float32))
+    assert np.array_equal(bf16_vals(w), z * eff)       # exactly representable
+    ref = O.fq_weight_stack(w, fmt, group, s, zp, g)
+    out = torch.empty(E, N, K, dtype=torch.bfloat16, device="cuda")
+    F.fq_quantize_stacked(dev_bf16(w), (E, N, K), _wq(fmt, group, s, zp, g), out, None)
+    torch.cuda.synchronize()
+    assert np.array_equal(host_bits(out), ref.bits)
+
+
+# -------------------------------------------------------------- observer --
+@pytest.mark.parametrize("name,fmt", FMTS)
+@pytest.mark.parametrize("per_channel", [True, False])
+def test_observer_weight_bitexact(name, fmt, per_channel):
+    if fmt == O.FMT_NVFP4 and per_channel:
+        pytest.skip("nvfp4 scales are per 16-block")
+    rng = np.random.default_rng(300 + fmt)
+    E, N = 3, 40
+    K = 1024 if per_channel else 512     # per-channel 1024: one block per row
+    group = K if per_channel else (16 if fmt == O.FMT_NVFP4 else 128 if fmt == O.FMT_INT4 else 32)
+    w = _rand_w(rng, E, N, K)
+    w[1, 2] = 0                      # an all-zero row
+    s_ref, zp_ref, g_ref = O.observer_weight(w, fmt, group)
+    G = K // group
+    s = torch.full((E, N, G), -1.0, device="cuda")
+    zp = torch.full((E, N, G), -1.0, device="cuda") if fmt == O.FMT_INT4 else None
+    g = torch.full((E,), -1.0, device="cuda") if fmt == O.FMT_NVFP4 else None
+    F.observer_absmax_init(dev_bf16(w), (E, N, K), fmt, group, 0, s, zp, g)
+    torch.cuda.synchronize()
+    assert np.array_equal(s.cpu().numpy().view(np.uint32), s_ref.view(np.uint32))
+    if zp is not None:
+        assert np.array_equal(zp.cpu().numpy(), zp_ref)
+    if g is not None:
+        assert np.array_equal(g.cpu().numpy().view(np.uint32), g_ref.view(np.uint32))
+
+
+@pytest.mark.parametrize("name,fmt", [("fp8", O.FMT_FP8), ("nvfp4", O.FMT_NVFP4), ("int8", O.FMT_INT8)])
+def test_observer_activation_bitexact(name, fmt):
+    rng = np.random.default_rng(400 + fmt)
+    x = O.f32_to_bf16(rng.standard_normal((333, 64)).astype(np.float32))
+    s = torch.zeros(1, device="cuda")
+    F.observer_absmax_init(dev_bf16(x), (1, 333, 64), fmt, 16, 1, s)
+    torch.cuda.synchronize()
+    assert s.cpu().numpy()[0] == O.observer_act(x, fmt)
+
+
+# --------------------------------------------------------------- permute --
+@pytest.mark.parametrize("T,k,Eg,begin,El,zipf", [
+    (1000, 8, 128, 0, 128, None), (777, 8, 128, 16, 16, None), (5000, 8, 128, 0, 16, 1.2),
+    (1, 8, 16, 0, 16, None), (0, 8, 16, 0, 16, None), (300, 2, 6, 0, 6, None)])
+def test_permute_bitexact(T, k, Eg, begin, El, zipf):
+    if T > 0:
+        case = W.moe_case(T=T, fmt="nvfp4", E_global=Eg, H=16, F=16, topk=k, seed=T,
+                          expert_begin=begin, E_local=El, zipf_s=zipf,
+                          zero_experts=(3, 7) if zipf else ())
+        ids = case.expert_ids
+    else:
+        ids = np.zeros((0, k), np.int32)
+    perm_ref, row_ref, seg_ref = O.moe_permute(ids, begin, El)
+    P = max(T * k, 1)
+    perm = torch.full((P,), -7, dtype=torch.int32, device="cuda")
+    row_of = torch.full((max(T, 1), k), -7, dtype=torch.int32, device="cuda")
+    seg = torch.full((El + 1,), -7, dtype=torch.int32, device="cuda")
+    wsb = F.fq_workspace_bytes(F.FQ_OP_PERMUTE, (El, 0, 0), T * k, 0)
+    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+    F.fq_moe_permute(dev_i32(ids) if T else None, T, k, begin, El, perm, row_of, seg, ws)
+    torch.cuda.synchronize()
+    R = int(seg_ref[-1])
+    assert np.array_equal(seg.cpu().numpy(), seg_ref)
+    assert np.array_equal(perm.cpu().numpy()[:R], perm_ref)
+    if T:
+        assert np.array_equal(row_of.cpu().numpy(), row_ref)
+
+
+# ---------------------------------------------------- grouped GEMM forward --
+def _segments(rng, E, sizes):
+    seg = np.zeros(E + 1, np.int32)
+    seg[1:] = np.cumsum(sizes)
+    return seg
+
+
+@pytest.mark.parametrize("name,fmt", FMTS)
+@pytest.mark.parametrize("afmt", [O.FMT_NONE, O.FMT_FP8, O.FMT_NVFP4])
+def test_gemm_fwd_parity(name, fmt, afmt):
+    rng = np.random.default_rng(500 + 10 * fmt + afmt)
+    E, N, K = 5, 512, 384 if fmt != O.FMT_INT4 else 512
+    sizes = [70, 0, 300, 1, 257]                      # empty, single-row, multi-tile, ragged
+    seg = _segments(rng, E, sizes)
+    R = int(seg[-1])
+    R_max = R + 40
+    group = _group(fmt, K)
+    w = _rand_w(rng, E, N, K)
+    s, zp, g = O.observer_weight(w, fmt, group)
+    x = O.f32_to_bf16(rng.standard_normal((R_max, K)).astype(np.float32))
+    sa = O.observer_act(x[:R], afmt) if afmt else np.float32(1.0)
+    y_ref = O.grouped_gemm_fwd(x, seg, w, fmt, group, s, zp, g, afmt, sa)
+    y = torch.full((R_max, N), 7.0, dtype=torch.bfloat16, device="cuda")
+    wq = _wq(fmt, group, s, zp, g)
+    aq = F.ActQ(afmt, dev_f32([sa])) if afmt else None
+    wsb = F.fq_workspace_bytes(F.FQ_OP_GEMM_FWD, (E, N, K), R_max, fmt | (afmt << 8))
+    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device="cuda")
+    F.fq_grouped_gemm_fwd(dev_bf16(x), R_max, dev_i32(seg), (E, N, K), dev_bf16(w), None, wq, aq,
+                          y, ws)
+    torch.cuda.synchronize()
+    yb = host_bits(y)
+    check_gemm_tol(yb[:R], y_ref, "y")
+    assert np.all(bf16_vals(yb[R:]) == 7.0)           # rows past R untouched
+
+
+def test_gemm_fwd_prequantized_weights_match():
+    """w_fq from fq_quantize_stacked gives the same bits as the in-call FQ."""
+    rng = np.random.default_rng(600)
+    E, N, K = 3, 256, 256
+    seg = _segments(rng, E, [100, 200, 50])
+    R = int(seg[-1])
+    w = _rand_w(rng, E, N, K)
+    s, _, g = O.observer_weight(w, O.FMT_NVFP4, 16)
+    x = O.f32_to_bf16(rng.standard_normal((R, K)).astype(np.float32))
+    wq = _wq(O.FMT_NVFP4, 16, s, None, g)
+    wd = dev_bf16(w)
+    wfq = torch.empty_like(wd)
+    F.fq_quantize_stacked(wd, (E, N, K), wq, wfq)
+    ws = torch.empty(F.fq_workspace_bytes(F.FQ_OP_GEMM_FWD, (E, N, K), R, O.FMT_NVFP4),
+                     dtype=torch.uint8, device="cuda")
+    y1 = torch.empty(R, N, dtype=torch.bfloat16, device="cuda")
+    y2 = torch.empty_like(y1)
+    F.fq_grouped_gemm_fwd(dev_bf16(x), R, dev_i32(seg), (E, N, K), wd, None, wq, None, y1, ws)
+    F.fq_grouped_gemm_fwd(dev_bf16(x), R, dev_i32(seg), (E, N, K), None, wfq, wq, None, y2, None)
+    torch.cuda.synchronize()
+    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
+    # rows are independent: a row's output does not depend on its neighbours
+    x2 = x.copy()
+    x2[1::2] = 0
+    y3 = torch.empty_like(y1)
+    F.fq_grouped_gemm_fwd(dev_bf16(x2), R, dev_i32(seg), (E, N, K), None, wfq, wq, None, y3, None)
+    torch.cuda.synchronize()
+    assert torch.equal(y3[0::2].view(torch.int16), y2[0::2].view(torch.int16))
+
+
+# --------------------------------------------------- grouped GEMM backward --
+@pytest.mark.parametrize("name,fmt", FMTS)
+@pytest.mark.parametrize("afmt", [O.FMT_NONE, O.FMT_FP8, O.FMT_NVFP4])
+@pytest.mark.parametrize("grouping", ["default", "per_channel"])
+def test_gemm_bwd_parity(name, fmt, afmt, grouping):
+    if grouping == "per_channel" and fmt in (O.FMT_NVFP4, O.FMT_INT4):
+        pytest.skip("block / group formats")
+    rng = np.random.default_rng(700 + 10 * fmt + afmt)
+    E, N, K = 4, 256, 512
+    sizes = [90, 0, 301, 33]
+    seg = _segments(rng, E, sizes)
+    R = int(seg[-1])
+    R_max = R + 17
+    group = K if grouping == "per_channel" else _group(fmt, K)
+    if fmt in (O.FMT_INT8, O.FMT_FP8) and grouping == "default":
+        group = 64
+    w = _rand_w(rng, E, N, K)
+    s, zp, g = O.observer_weight(w, fmt, group)
+    s = (s * rng.uniform(0.7, 1.1, s.shape)).astype(np.float32)
+    x = O.f32_to_bf16(rng.standard_normal((R_max, K)).astype(np.float32))
+    dy = O.f32_to_bf16(rng.standard_normal((R_max, N)).astype(np.float32))
+    sa = O.observer_act(x[:R], afmt) if afmt else np.float32(1.0)
+    if afmt:
+        sa = np.float32(sa * 0.8)          # some activations clamp: mask zeros in dX
+    dx_ref, ds_ref, dzp_ref = O.grouped_gemm_bwd(dy, x, seg, w, fmt, group, s, zp, g, afmt, sa)
+    wq = _wq(fmt, group, s, zp, g)
+    aq = F.ActQ(afmt, dev_f32([sa])) if afmt else None
+    G = K // group
+    dx = torch.full((R_max, K), 7.0, dtype=torch.bfloat16, device="cuda")
+    ds = torch.full((E, N, G), 7.0, device="cuda")
+    dzp = torch.full((E, N, G), 7.0, device="cuda") if fmt == O.FMT_INT4 else None
+    wsb = F.fq_workspace_bytes(F.FQ_OP_GEMM_BWD, (E, N, K), R_max, fmt | (afmt << 8))
+    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+    F.fq_grouped_gemm_bwd_scale(dev_bf16(dy), dev_bf16(x), R_max, dev_i32(seg), (E, N, K),
+                                dev_bf16(w), None, wq, aq, dx, ds, dzp, ws)
+    torch.cuda.synchronize()
+    dxb = host_bits(dx)
+    check_gemm_tol(dxb[:R], dx_ref, "dx")
+    assert np.all(bf16_vals(dxb[R:]) == 7.0)
+    dsh = ds.cpu().numpy()
+    check_dscale_tol(dsh, ds_ref, "dscale")
+    assert np.all(dsh[1] == 0)                         # empty expert
+    if dzp is not None:
+        check_dscale_tol(dzp.cpu().numpy(), dzp_ref, "dzero_point")
+
+
+def test_bwd_deterministic_run_to_run():
+    rng = np.random.default_rng(800)
+    E, N, K = 3, 256, 256
+    seg = _segments(rng, E, [500, 20, 270])
+    R = int(seg[-1])
+    w = _rand_w(rng, E, N, K)
+    s, _, _ = O.observer_weight(w, O.FMT_FP8, K)
+    x = dev_bf16(O.f32_to_bf16(rng.standard_normal((R, K)).astype(np.float32)))
+    dy = dev_bf16(O.f32_to_bf16(rng.standard_normal((R, N)).astype(np.float32)))
+    wq = _wq(O.FMT_FP8, K, s, None, None)
+    ws = torch.empty(F.fq_workspace_bytes(F.FQ_OP_GEMM_BWD, (E, N, K), R, O.FMT_FP8),
+                     dtype=torch.uint8, device="cuda")
+    outs = []
+    for _ in range(2):
+        dx = torch.empty(R, K, dtype=torch.bfloat16, device="cuda")
+        ds = torch.empty(E, N, 1, device="cuda")
+        F.fq_grouped_gemm_bwd_scale(dy, x, R, dev_i32(seg), (E, N, K), dev_bf16(w), None, wq, None,
+                                    dx, ds, None, ws)
+        outs.append((dx.clone(), ds.clone()))
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0][0].view(torch.int16), outs[1][0].view(torch.int16))
+    assert torch.equal(outs[0][1], outs[1][1])
+
+
+# ------------------------------------------------------- error handling --
+def test_errors_are_reported_before_launch():
+    E, N, K = 2, 256, 250      # K not a multiple of 16
+    w = torch.zeros(E, N, K, dtype=torch.bfloat16, device="cuda")
+    q = F.WeightQ(F.FMT_NVFP4, 16, torch.ones(E, N, 16, device="cuda"),
+                  None, torch.ones(E, device="cuda"))
+    with pytest.raises(F.FQError) as ei:
+        F.fq_quantize_stacked(w, (E, N, K), q, torch.empty_like(w))
+    assert ei.value.status == F.FQ_ERR_INVALID_ARGUMENT
+    with pytest.raises(F.FQError) as ei:
+        F.fq_moe_permute(torch.zeros(4, 8, dtype=torch.int32, device="cuda"), 4, 8, 0, 16,
+                         torch.empty(32, dtype=torch.int32, device="cuda"),
+                         torch.empty(4, 8, dtype=torch.int32, device="cuda"),
+                         torch.empty(17, dtype=torch.int32, device="cuda"),
+                         torch.empty(4, dtype=torch.uint8, device="cuda"))
+    assert ei.value.status == F.FQ_ERR_WORKSPACE_TOO_SMALL

@@ -1,0 +1,107 @@
+"""GPU parity of the whole routed-expert path of one MoE layer (forward and
+scale-only backward through the C ABI), stage by stage against the oracle fed
+the GPU's own inputs of that stage, and end to end against the oracle given
+the GPU-calibrated activation scales."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import workloads as W
+from helpers import (bf16_vals, check_dscale_tol, check_gemm_tol, dev_bf16, dev_f32, dev_i32,
+                     host_bits)
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    import moe_fake_quant_amd as F
+else:
+    F = None
+
+CASES = [
+    # name, weight fmt, act fmt, group (None = per channel), T, E_global, E_local, begin, zipf
+    ("fp8", O.FMT_FP8, O.FMT_FP8, None, 300, 8, 8, 0, None),
+    ("nvfp4", O.FMT_NVFP4, O.FMT_NVFP4, 16, 300, 8, 8, 0, None),
+    ("nvfp4-local-zipf", O.FMT_NVFP4, O.FMT_NVFP4, 16, 700, 32, 8, 0, 1.2),
+    ("int4-a16", O.FMT_INT4, O.FMT_NONE, 128, 200, 8, 8, 0, None),
+]
+
+
+def _run_layer(case, wfmt, afmt, group):
+    E = case.E
+    layer = F.MoEFakeQuantLayer(dev_bf16(case.w_gu), dev_bf16(case.w_d), wfmt, afmt, case.T,
+                                case.topk, case.expert_begin, group)
+    x, ids = dev_bf16(case.x), dev_i32(case.expert_ids)
+    p, dout = dev_f32(case.probs), dev_bf16(case.dout)
+    layer.init_weight_scales()
+    layer.calibrate(x, ids)
+    layer.quantize_weights()
+    layer.forward(x, ids, p, keep_a=True)
+    layer.backward(x, p, dout)
+    torch.cuda.synchronize()
+    return layer
+
+
+@pytest.mark.parametrize("name,wfmt,afmt,group,T,Eg,El,begin,zipf", CASES)
+def test_moe_layer_stagewise_and_end_to_end(name, wfmt, afmt, group, T, Eg, El, begin, zipf):
+    case = W.moe_case(T=T, fmt=name, E_global=Eg, H=256, F=256, topk=4, seed=11,
+                      expert_begin=begin, E_local=El, zipf_s=zipf,
+                      zero_experts=(3,) if zipf else ())
+    L = _run_layer(case, wfmt, afmt, group)
+    E, k = El, case.topk
+    g_gu = group or case.w_gu.shape[2]
+    g_d = group or case.w_d.shape[2]
+    # weight scales from the GPU observer == oracle observer
+    wq_gu = O.observer_weight(case.w_gu, wfmt, g_gu)
+    wq_d = O.observer_weight(case.w_d, wfmt, g_d)
+    assert np.array_equal(L.q_gu.scale.cpu().numpy(), wq_gu[0])
+    assert np.array_equal(L.q_d.scale.cpu().numpy(), wq_d[0])
+    # routing
+    perm, row_of, seg = O.moe_permute(case.expert_ids, begin, E)
+    R = int(seg[-1])
+    assert np.array_equal(L.seg.cpu().numpy(), seg)
+    assert np.array_equal(L.perm.cpu().numpy()[:R], perm)
+    assert np.array_equal(L.row_of.cpu().numpy()[:T], row_of)
+    s1 = L.aq1.scale.cpu().numpy()[0]
+    s2 = L.aq2.scale.cpu().numpy()[0]
+    if afmt:
+        assert s1 == O.observer_act(case.x, afmt)
+    # stage by stage, each oracle step fed the GPU's inputs of that step
+    xq = host_bits(L.xq)[:R]
+    assert np.array_equal(xq, O.gather_actfq(case.x, perm, k, afmt, s1).bits)
+    h = host_bits(L.h)[:R]
+    check_gemm_tol(h, O.grouped_gemm_fwd(xq, seg, case.w_gu, wfmt, g_gu, *wq_gu), "h")
+    a = host_bits(L.a)[:R]
+    check_gemm_tol(a, O.swiglu_fwd(h), "a")
+    if afmt:
+        assert s2 == O.observer_act(a, afmt)
+    aq = host_bits(L.aq)[:R]
+    assert np.array_equal(aq, O.fq_act(a, afmt, s2).bits)
+    o = host_bits(L.o)[:R]
+    check_gemm_tol(o, O.grouped_gemm_fwd(aq, seg, case.w_d, wfmt, g_d, *wq_d), "o")
+    check_gemm_tol(host_bits(L.out)[:T], O.combine(o, case.probs, row_of), "out")
+    do = host_bits(L.do)[:R]
+    assert np.array_equal(do, O.combine_bwd(case.dout, case.probs, perm, k))
+    daq_ref, ds_d_ref, dzp_d_ref = O.grouped_gemm_bwd(do, aq, seg, case.w_d, wfmt, g_d, *wq_d)
+    daq = host_bits(L.daq)[:R]
+    check_gemm_tol(daq, daq_ref, "daq")
+    check_dscale_tol(L.ds_d.cpu().numpy(), ds_d_ref, "ds_d")
+    dh = host_bits(L.dh)[:R]
+    check_gemm_tol(dh, O.swiglu_bwd(daq, h, afmt, s2, a_bits=a), "dh")
+    dxq_ref, ds_gu_ref, dzp_gu_ref = O.grouped_gemm_bwd(dh, xq, seg, case.w_gu, wfmt, g_gu, *wq_gu)
+    dxq = host_bits(L.dxq)[:R]
+    check_gemm_tol(dxq, dxq_ref, "dxq")
+    check_dscale_tol(L.ds_gu.cpu().numpy(), ds_gu_ref, "ds_gu")
+    if wfmt == O.FMT_INT4:
+        check_dscale_tol(L.dzp_gu.cpu().numpy(), dzp_gu_ref, "dzp_gu")
+        check_dscale_tol(L.dzp_d.cpu().numpy(), dzp_d_ref, "dzp_d")
+    dx = host_bits(L.dx)[:T]
+    check_gemm_tol(dx, O.unpermute_reduce(dxq, row_of, case.x, afmt, s1), "dx")
+    # end to end: the oracle's own chain with the GPU-calibrated activation scales
+    ref = O.moe_layer(case, wfmt, g_gu if g_gu == g_d else None, afmt, wq_gu, wq_d, (s1, s2)) \
+        if g_gu == g_d else None
+    if ref is not None:
+        check_gemm_tol(host_bits(L.out)[:T], ref["out"], "out e2e")
+        check_gemm_tol(dx, ref["dx"], "dx e2e")
+        check_dscale_tol(L.ds_gu.cpu().numpy(), ref["ds_gu"], "ds_gu e2e")
+        check_dscale_tol(L.ds_d.cpu().numpy(), ref["ds_d"], "ds_d e2e")

@@ -45,6 +45,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-experts", type=int, default=6)
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--copy-calibration-mb", type=int, default=0,
+                    help="after timing, run one plain device copy of this many MiB (a known "
+                         "traffic reference for HBM byte counters)")
     return ap.parse_args()
 
 
@@ -177,6 +180,15 @@ def main():
             traffic = tr.get("bytes_per_launch")
 
     breakdown = {n: round(sum(v) / args.steps, 4) for n, v in sorted(per.items())}
+
+    if args.copy_calibration_mb > 0:
+        n = args.copy_calibration_mb * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     cpu = None
     if not args.no_cpu_baseline:

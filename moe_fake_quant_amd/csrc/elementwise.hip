@@ -80,9 +80,10 @@ __global__ __launch_bounds__(kThreads) void k_quantize_stacked(
 // Groups that span 2..64 vectors are reduced across adjacent lanes; one
 // vector per lane, vectors of a group on consecutive lanes of one wave.
 template <int FMT>
-__global__ __launch_bounds__(kThreads) void k_observer_lanes(
-    const bf16x8_t *__restrict__ w, uint32_t nvec, int lanes_per_group, FastDiv vec_per_expert,
-    float *__restrict__ scale, float *__restrict__ zero_point, uint32_t *__restrict__ expert_amax) {
+__global__ __launch_bounds__(kThreads) void k_observer_lanes(const bf16x8_t *__restrict__ w,
+                                                             uint32_t nvec, int lanes_per_group,
+                                                             float *__restrict__ scale,
+                                                             float *__restrict__ zero_point) {
   const uint32_t stride = gridDim.x * blockDim.x;
   // uniform trip count so every lane takes part in the shuffles
   for (uint32_t base = blockIdx.x * blockDim.x; base < nvec; base += stride) {
@@ -116,7 +117,6 @@ __global__ __launch_bounds__(kThreads) void k_observer_lanes(
         zero_point[gi] = fminf(fmaxf(rintf(-mn * r), 0.0f), 15.0f);
       } else {  // nvfp4: block amax now, theta after the expert amax is known
         scale[gi] = amax;
-        atomicMax(expert_amax + vec_per_expert.div(i), __float_as_uint(amax));
       }
     }
   }
@@ -169,6 +169,23 @@ __global__ __launch_bounds__(kThreads) void k_observer_block(const bf16x8_t *__r
   }
 }
 
+// Per-expert amax from the block amaxes (one block per expert, no atomics):
+// out_bits[e] = bits of max over blocks [e*nb, (e+1)*nb).
+__global__ __launch_bounds__(kThreads) void k_expert_amax(const float *__restrict__ block_amax,
+                                                          uint32_t nb, uint32_t *__restrict__ out_bits) {
+  const float *p = block_amax + (size_t)blockIdx.x * nb;
+  float m = 0.0f;
+  for (uint32_t i = threadIdx.x; i < nb; i += blockDim.x) m = fmaxf(m, p[i]);
+  m = warp_max(m);
+  __shared__ float red[kThreads / 64];
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int k = 1; k < kThreads / 64; ++k) m = fmaxf(m, red[k]);
+    out_bits[blockIdx.x] = __float_as_uint(m);
+  }
+}
+
 // theta_b = E4M3(clamp(amax_b * (1/(6 g)), 0, 448)), g = amax_e / 2688 (1 if 0)
 __global__ void k_nvfp4_theta(float *__restrict__ theta, uint32_t n, FastDiv blocks_per_expert,
                               const uint32_t *__restrict__ expert_amax) {
@@ -203,7 +220,13 @@ __global__ __launch_bounds__(kThreads) void k_absmax_tensor(const bf16x8_t *__re
     for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(f[j]));
   }
   amax = warp_max(amax);
-  if ((threadIdx.x & 63) == 0) atomicMax(out_bits, __float_as_uint(amax));
+  __shared__ float red[kThreads / 64];
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = amax;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int k = 1; k < kThreads / 64; ++k) amax = fmaxf(amax, red[k]);
+    atomicMax(out_bits, __float_as_uint(amax));  // max is order independent
+  }
 }
 
 __global__ void k_act_scale_finalize(uint32_t *bits, float div) {
@@ -518,11 +541,11 @@ void launch_observer_weight(const uint16_t *w, fq_shape s, int fmt, int group, f
   int vpg = group / 8;
   if (fmt == FQ_FMT_NVFP4) {
     auto gbits = reinterpret_cast<uint32_t *>(gscale);
-    launch_fill_u32(gbits, 0u, s.E, st);
-    FastDiv vpe((uint32_t)((size_t)s.N * s.K / 8));
     hipLaunchKernelGGL(k_observer_lanes<FQ_FMT_NVFP4>, dim3(grid_for(nvec)), dim3(kThreads), 0, st,
-                       wv, nvec, vpg, vpe, scale, zero_point, gbits);
+                       wv, nvec, vpg, scale, zero_point);
     uint32_t nb = (uint32_t)((size_t)s.E * s.N * (s.K / group));
+    hipLaunchKernelGGL(k_expert_amax, dim3(s.E), dim3(kThreads), 0, st, scale,
+                       (uint32_t)((size_t)s.N * (s.K / group)), gbits);
     FastDiv bpe((uint32_t)((size_t)s.N * (s.K / group)));
     hipLaunchKernelGGL(k_nvfp4_theta, dim3(grid_for(nb)), dim3(kThreads), 0, st, scale, nb, bpe,
                        gbits);
@@ -532,10 +555,9 @@ void launch_observer_weight(const uint16_t *w, fq_shape s, int fmt, int group, f
   }
   bool lanes = vpg <= 64 && (vpg & (vpg - 1)) == 0;
   if (lanes) {
-    FastDiv one(1);
 #define FQ_OBL(F)                                                                               \
   hipLaunchKernelGGL(k_observer_lanes<F>, dim3(grid_for(nvec)), dim3(kThreads), 0, st, wv, nvec, \
-                     vpg, one, scale, zero_point, nullptr)
+                     vpg, scale, zero_point)
     switch (fmt) {
       case FQ_FMT_INT8: FQ_OBL(FQ_FMT_INT8); break;
       case FQ_FMT_INT4: FQ_OBL(FQ_FMT_INT4); break;

@@ -41,7 +41,8 @@ typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
 constexpr int BI = 256;   // tile rows (i)
 constexpr int BJ = 256;   // tile cols (j)
 constexpr int BK = 64;    // contraction step
-constexpr int NT = 256;   // threads per block (4 waves)
+constexpr int NT = 512;   // threads per block (8 waves, 2 per SIMD)
+constexpr int WJ_TILE = 64;  // j extent of one wave (waves: 2 along i x 4 along j)
 constexpr int kTileBytes = 256 * BK * 2;  // one operand tile in LDS (32 KiB)
 
 enum Mode { FWD = 0, DGRAD = 1, WGRAD = 2 };
@@ -52,61 +53,69 @@ __device__ __forceinline__ uint32_t lds_off(uint32_t idx, uint32_t kc) {
   return idx * 128u + ((kc ^ swz) << 4);
 }
 
-__device__ __forceinline__ bf16x8_t ldg16(const uint16_t *p) {
-  return *reinterpret_cast<const bf16x8_t *>(p);
+__device__ __forceinline__ bf16x8_t ldg16(const char *base, uint32_t byte_off) {
+  return *reinterpret_cast<const bf16x8_t *>(base + byte_off);
 }
 
 // ---- normal operand: 256 rows of a row-major matrix, 64 contiguous contraction
 // elements each. Thread t: rows u*32 + t/8 (u = 0..7), 16-byte slot t%8.
-__device__ __forceinline__ void load_normal(bf16x8_t (&v)[8], const uint16_t *base, size_t ld,
-                                            int row0, int row_last, int c0) {
-  const int t = threadIdx.x;
+// The per-thread row byte offsets are fixed for a tile; the contraction step
+// adds c0*2 bytes. Offsets are 32-bit from a block-uniform base pointer.
+struct NormalRows {
+  uint32_t off[4];
+  __device__ __forceinline__ void init(size_t ld, int row0, int row_last) {
+    const int t = threadIdx.x;
 #pragma unroll
-  for (int u = 0; u < 8; ++u) {
-    int r = min(row0 + u * 32 + (t >> 3), row_last);
-    v[u] = ldg16(base + (size_t)r * ld + c0 + (t & 7) * 8);
+    for (int u = 0; u < 4; ++u) {
+      int r = min(row0 + u * 64 + (t >> 3), row_last);
+      off[u] = (uint32_t)(((size_t)r * ld + (t & 7) * 8) * 2);
+    }
   }
-}
-__device__ __forceinline__ void store_normal(char *lds, const bf16x8_t (&v)[8]) {
+  __device__ __forceinline__ void load(bf16x8_t (&v)[4], const char *base, int c0) const {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) v[u] = ldg16(base, off[u] + c0 * 2);
+  }
+};
+__device__ __forceinline__ void store_normal(char *lds, const bf16x8_t (&v)[4]) {
   const int t = threadIdx.x;
 #pragma unroll
-  for (int u = 0; u < 8; ++u)
-    *reinterpret_cast<bf16x8_t *>(lds + lds_off(u * 32 + (t >> 3), t & 7)) = v[u];
+  for (int u = 0; u < 4; ++u)
+    *reinterpret_cast<bf16x8_t *>(lds + lds_off(u * 64 + (t >> 3), t & 7)) = v[u];
 }
 
 // ---- transposed operand: element (c, idx) at base[c * ld + idx]; the tile is
 // contraction rows c0..c0+63 x idx idx0..idx0+255. Thread t: idx block t%32
-// (8 columns), contraction block t/32 (8 rows). Rows c >= c_end read as 0.
-__device__ __forceinline__ void load_trans(bf16x8_t (&v)[8], const uint16_t *base, size_t ld, int c0,
+// (8 columns), contraction block t/32 (4 rows). Rows c >= c_end read as 0.
+__device__ __forceinline__ void load_trans(bf16x8_t (&v)[4], const char *base, uint32_t ld, int c0,
                                            int c_end, int idx0) {
   const int t = threadIdx.x;
-  const int col = idx0 + (t & 31) * 8;
+  const uint32_t col = idx0 + (t & 31) * 8;
 #pragma unroll
-  for (int q = 0; q < 8; ++q) {
-    int c = c0 + (t >> 5) * 8 + q;
+  for (int q = 0; q < 4; ++q) {
+    int c = c0 + (t >> 5) * 4 + q;
     bool ok = c < c_end;
     int cc = ok ? c : c0;  // c0 < c_end whenever this tile is loaded
-    bf16x8_t x = ldg16(base + (size_t)cc * ld + col);
+    bf16x8_t x = ldg16(base, ((uint32_t)cc * ld + col) * 2);
     v[q].w[0] = ok ? x.w[0] : 0u;
     v[q].w[1] = ok ? x.w[1] : 0u;
     v[q].w[2] = ok ? x.w[2] : 0u;
     v[q].w[3] = ok ? x.w[3] : 0u;
   }
 }
-__device__ __forceinline__ void store_trans(char *lds, const bf16x8_t (&v)[8]) {
+// 4 contraction rows x 8 columns -> 8 columns x 4 contraction values (8 bytes
+// each, half of a 16-byte LDS slot)
+__device__ __forceinline__ void store_trans(char *lds, const bf16x8_t (&v)[4]) {
   const int t = threadIdx.x;
-  const uint32_t idxb = (t & 31) * 8, kc = t >> 5;
-  // out[j] (column idxb + j) gathers element j of the 8 input rows
+  const uint32_t idxb = (t & 31) * 8, cb = t >> 5, kc = cb >> 1, half = (cb & 1) * 8;
 #pragma unroll
   for (int p = 0; p < 4; ++p) {
-    bf16x8_t lo, hi;  // columns 2p and 2p+1
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      lo.w[q] = __builtin_amdgcn_perm(v[2 * q + 1].w[p], v[2 * q].w[p], 0x05040100u);
-      hi.w[q] = __builtin_amdgcn_perm(v[2 * q + 1].w[p], v[2 * q].w[p], 0x07060302u);
-    }
-    *reinterpret_cast<bf16x8_t *>(lds + lds_off(idxb + 2 * p, kc)) = lo;
-    *reinterpret_cast<bf16x8_t *>(lds + lds_off(idxb + 2 * p + 1, kc)) = hi;
+    uint2 lo, hi;  // columns 2p and 2p+1
+    lo.x = __builtin_amdgcn_perm(v[1].w[p], v[0].w[p], 0x05040100u);
+    lo.y = __builtin_amdgcn_perm(v[3].w[p], v[2].w[p], 0x05040100u);
+    hi.x = __builtin_amdgcn_perm(v[1].w[p], v[0].w[p], 0x07060302u);
+    hi.y = __builtin_amdgcn_perm(v[3].w[p], v[2].w[p], 0x07060302u);
+    *reinterpret_cast<uint2 *>(lds + lds_off(idxb + 2 * p, kc) + half) = lo;
+    *reinterpret_cast<uint2 *>(lds + lds_off(idxb + 2 * p + 1, kc) + half) = hi;
   }
 }
 
@@ -176,12 +185,12 @@ __device__ bool find_row_tile(const int32_t *seg, int E, int tile, int &e_out, i
   return e_out >= 0;
 }
 
-// dS of the 128 (k) x 32 (n) slab of dWq that column sub-tile U of one wave
+// dS of the 128 (k) x 32 (n) slab of dWq that column sub-tile U (0..1) of one wave
 // holds: lane n = n0 + lane%32, k = k0 + 32s + 8q + 4(lane/32) + v for
 // acc[s][U][4q + v]. Each dWq element is weighted by its straight-through
 // factor and summed over its quantization group in a fixed order.
 template <int WFMT, int U>
-__device__ __forceinline__ void wgrad_epilogue(const GemmArgs &a, const f32x16 (&acc)[4][4], int e,
+__device__ __forceinline__ void wgrad_epilogue(const GemmArgs &a, const f32x16 (&acc)[4][2], int e,
                                                int k0, int n0, int lane) {
   const int n = n0 + (lane & 31);
   const int G = a.K / a.group;
@@ -264,11 +273,11 @@ __device__ __forceinline__ void wgrad_epilogue(const GemmArgs &a, const f32x16 (
 }
 
 template <int MODE, int WFMT>
-__global__ __launch_bounds__(NT, 1) void k_grouped_gemm(GemmArgs a) {
+__global__ __launch_bounds__(NT) void k_grouped_gemm(GemmArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[4 * kTileBytes];  // P0 Q0 P1 Q1 = 128 KiB
   const int t = threadIdx.x;
   const int lane = t & 63, wave = t >> 6;
-  const int wi = wave & 1, wj = wave >> 1;
+  const int wi = wave & 1, wj = wave >> 1;  // 2 x 4 waves: 128 (i) x 64 (j) each
 
   // XCD-aware remap of the block id
   const uint32_t nb = gridDim.x, b = blockIdx.x;
@@ -295,49 +304,46 @@ __global__ __launch_bounds__(NT, 1) void k_grouped_gemm(GemmArgs a) {
   if (MODE == WGRAD) c_total = seg_hi - seg_lo;
   else c_total = (MODE == FWD) ? a.K : a.N;
 
-  // operand base pointers
+  // operand base pointers (block-uniform) and leading dimensions
   const size_t NK = (size_t)a.N * a.K;
-  const uint16_t *pbase, *qbase;
-  size_t pld, qld;
+  const char *pbase, *qbase;
   if (MODE == FWD) {
-    pbase = a.p + e * NK;                 // W_fq[e] [N][K], rows i = n
-    pld = a.K;
-    qbase = a.q;                          // Xq rows, row index absolute
-    qld = a.K;
+    pbase = reinterpret_cast<const char *>(a.p + e * NK);   // W_fq[e] [N][K], rows i = n
+    qbase = reinterpret_cast<const char *>(a.q);            // Xq rows (absolute)
   } else if (MODE == DGRAD) {
-    pbase = a.p + e * NK;                 // W_fq[e] as (c = n, idx = k)
-    pld = a.K;
-    qbase = a.q;                          // dY rows
-    qld = a.N;
+    pbase = reinterpret_cast<const char *>(a.p + e * NK);   // W_fq[e] as (c = n, idx = k)
+    qbase = reinterpret_cast<const char *>(a.q);            // dY rows (absolute)
   } else {
-    pbase = a.p + (size_t)seg_lo * a.K;   // Xq rows of the segment: (c = r, idx = k)
-    pld = a.K;
-    qbase = a.q + (size_t)seg_lo * a.N;   // dY rows of the segment: (c = r, idx = n)
-    qld = a.N;
+    pbase = reinterpret_cast<const char *>(a.p + (size_t)seg_lo * a.K);  // Xq: (c = r, idx = k)
+    qbase = reinterpret_cast<const char *>(a.q + (size_t)seg_lo * a.N);  // dY: (c = r, idx = n)
   }
+  NormalRows prow, qrow;
+  if (MODE == FWD) prow.init(a.K, i0, a.N - 1);
+  if (MODE == FWD) qrow.init(a.K, j0, j_end - 1);
+  if (MODE == DGRAD) qrow.init(a.N, j0, j_end - 1);
 
-  f32x16 acc[4][4];
+  f32x16 acc[4][2];
 #pragma unroll
   for (int s = 0; s < 4; ++s)
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
+    for (int u = 0; u < 2; ++u)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[s][u][v] = 0.0f;
 
   const int nk = (c_total + BK - 1) / BK;
-  bf16x8_t rp[8], rq[8];
+  bf16x8_t rp[4], rq[4];
 
   auto load_tile = [&](int kt) {
     const int c0 = kt * BK;
     if (MODE == FWD) {
-      load_normal(rp, pbase, pld, i0, a.N - 1, c0);
-      load_normal(rq, qbase, qld, j0, j_end - 1, c0);
+      prow.load(rp, pbase, c0);
+      qrow.load(rq, qbase, c0);
     } else if (MODE == DGRAD) {
-      load_trans(rp, pbase, pld, c0, c_total, i0);
-      load_normal(rq, qbase, qld, j0, j_end - 1, c0);
+      load_trans(rp, pbase, a.K, c0, c_total, i0);
+      qrow.load(rq, qbase, c0);
     } else {
-      load_trans(rp, pbase, pld, c0, c_total, i0);
-      load_trans(rq, qbase, qld, c0, c_total, j0);
+      load_trans(rp, pbase, a.K, c0, c_total, i0);
+      load_trans(rq, qbase, a.N, c0, c_total, j0);
     }
   };
   auto store_tile = [&](int buf) {
@@ -354,44 +360,55 @@ __global__ __launch_bounds__(NT, 1) void k_grouped_gemm(GemmArgs a) {
       store_trans(sq, rq);
     }
   };
+  // MFMA fragments of one 16-deep step: [0..3] P sub-tiles, [4..5] Q sub-tiles
+  auto read_frags = [&](int buf, int ks, bf16x8v (&f)[6]) {
+    const char *sp = smem + (2 * buf) * kTileBytes;
+    const char *sq = smem + (2 * buf + 1) * kTileBytes;
+    const uint32_t kc = ks * 2 + (lane >> 5);
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+      f[s] = *reinterpret_cast<const bf16x8v *>(sp + lds_off(wi * 128 + s * 32 + (lane & 31), kc));
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+      f[4 + u] = *reinterpret_cast<const bf16x8v *>(sq + lds_off(wj * WJ_TILE + u * 32 + (lane & 31), kc));
+  };
 
+  // Pipeline: global loads of tile kt+1 are in flight during the MFMAs of
+  // tile kt; the fragments of step ks+1 are read from LDS during the MFMAs
+  // of step ks.
+  bf16x8v fr[2][6];
   if (nk > 0) {
     load_tile(0);
     store_tile(0);
     __syncthreads();
+    read_frags(0, 0, fr[0]);
   }
   for (int kt = 0; kt < nk; ++kt) {
     const int cur = kt & 1;
-    if (kt + 1 < nk) load_tile(kt + 1);
-    const char *sp = smem + (2 * cur) * kTileBytes;
-    const char *sq = smem + (2 * cur + 1) * kTileBytes;
+    const bool more = kt + 1 < nk;
+    if (more) load_tile(kt + 1);
 #pragma unroll
     for (int ks = 0; ks < BK / 16; ++ks) {
-      const uint32_t kc = ks * 2 + (lane >> 5);
-      bf16x8v fp[4], fq_[4];
-#pragma unroll
-      for (int s = 0; s < 4; ++s)
-        fp[s] = *reinterpret_cast<const bf16x8v *>(sp + lds_off(wi * 128 + s * 32 + (lane & 31), kc));
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-        fq_[u] = *reinterpret_cast<const bf16x8v *>(sq + lds_off(wj * 128 + u * 32 + (lane & 31), kc));
+      if (ks + 1 < BK / 16) read_frags(cur, ks + 1, fr[(ks + 1) & 1]);
 #pragma unroll
       for (int s = 0; s < 4; ++s)
 #pragma unroll
-        for (int u = 0; u < 4; ++u)
-          acc[s][u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fp[s], fq_[u], acc[s][u], 0, 0, 0);
+        for (int u = 0; u < 2; ++u)
+          acc[s][u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[ks & 1][s], fr[ks & 1][4 + u],
+                                                              acc[s][u], 0, 0, 0);
     }
-    if (kt + 1 < nk) store_tile(cur ^ 1);
+    if (more) store_tile(cur ^ 1);
     __syncthreads();
+    if (more) read_frags(cur ^ 1, 0, fr[0]);
   }
 
   // accumulator (s, u, v) of this lane: i = i0 + wi*128 + s*32 + 8*(v/4) + 4*(lane/32) + v%4,
-  //                                     j = j0 + wj*128 + u*32 + lane%32
+  //                                     j = j0 + wj*64 + u*32 + lane%32
   if (MODE != WGRAD) {
     const int ldo = (MODE == FWD) ? a.N : a.K;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int j = j0 + wj * 128 + u * 32 + (lane & 31);
+    for (int u = 0; u < 2; ++u) {
+      const int j = j0 + wj * WJ_TILE + u * 32 + (lane & 31);
       if (j >= j_end) continue;
       uint16_t *orow = a.out + (size_t)j * ldo;
 #pragma unroll
@@ -410,11 +427,9 @@ __global__ __launch_bounds__(NT, 1) void k_grouped_gemm(GemmArgs a) {
 
   // ---- WGRAD epilogue: i = k, j = n of expert e. dS over groups along k.
   {
-    const int k0 = i0 + wi * 128, n0 = j0 + wj * 128;
+    const int k0 = i0 + wi * 128, n0 = j0 + wj * WJ_TILE;
     wgrad_epilogue<WFMT, 0>(a, acc, e, k0, n0, lane);
     wgrad_epilogue<WFMT, 1>(a, acc, e, k0, n0 + 32, lane);
-    wgrad_epilogue<WFMT, 2>(a, acc, e, k0, n0 + 64, lane);
-    wgrad_epilogue<WFMT, 3>(a, acc, e, k0, n0 + 96, lane);
   }
 }
 

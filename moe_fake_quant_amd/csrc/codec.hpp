@@ -9,8 +9,9 @@
 // with -ffp-contract=off so no multiply-add is fused: z = x * r and
 // v = value * s are each one rounded multiply, exactly as specified.
 //
-// Grid rounding here is bit arithmetic (E4M3: round the fp32 mantissa to 3
-// bits; E2M1: threshold comparisons at the midpoints), not a table search.
+// Grid rounding here is bit arithmetic on the fp32 encoding (E4M3: round the
+// mantissa to 3 bits, E2M1: to 1 bit; multiples of the smallest step below the
+// normal range), not a table search.
 #pragma once
 
 #include "common.hpp"
@@ -21,35 +22,38 @@ constexpr float kE4M3Max = 448.0f;
 constexpr float kE2M1Max = 6.0f;
 
 // |a| <= 448 -> nearest E4M3 magnitude (ties to even mantissa); code 0..126.
+// Normal range: the fp32 mantissa rounded to 3 bits; below 2^-6: multiples of
+// 2^-9 (scaling by 512 is exact). Both are computed and one selected.
 __device__ __forceinline__ float e4m3_round_mag(float a, uint32_t &code) {
-  if (a < 0x1p-6f) {
-    // subnormal range: multiples of 2^-9; scaling by 512 is exact
-    float q = rintf(a * 512.0f);
-    code = (uint32_t)q;  // 0..8 (8 is the smallest normal, 2^-6, code 0x08)
-    return q * 0x1p-9f;
-  }
-  uint32_t u = __float_as_uint(a);
-  uint32_t r = (u + 0x7FFFFu + ((u >> 20) & 1u)) & 0xFFF00000u;
-  code = ((((r >> 23) & 0xFFu) - 120u) << 3) | ((r >> 20) & 7u);
-  return __uint_as_float(r);
+  const float qs = rintf(a * 512.0f);  // subnormal: 0..8 (8 = 2^-6, code 0x08)
+  const uint32_t u = __float_as_uint(a);
+  const uint32_t r = (u + 0x7FFFFu + ((u >> 20) & 1u)) & 0xFFF00000u;
+  const bool sub = a < 0x1p-6f;
+  code = sub ? (uint32_t)qs : (((((r >> 23) & 0xFFu) - 120u) << 3) | ((r >> 20) & 7u));
+  return sub ? qs * 0x1p-9f : __uint_as_float(r);
 }
 
 __device__ __forceinline__ float e4m3_round_mag(float a) {
-  uint32_t c;
-  return e4m3_round_mag(a, c);
+  const float qs = rintf(a * 512.0f) * 0x1p-9f;
+  const uint32_t u = __float_as_uint(a);
+  const float qn = __uint_as_float((u + 0x7FFFFu + ((u >> 20) & 1u)) & 0xFFF00000u);
+  return a < 0x1p-6f ? qs : qn;
 }
 
-// |a| <= 6 -> E2M1 magnitude code 0..7 (ties to even code).
-__device__ __forceinline__ uint32_t e2m1_code_mag(float a) {
-  return (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) +
-         (uint32_t)(a >= 1.75f) + (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) +
-         (uint32_t)(a > 5.0f);
+// |a| <= 6 -> nearest E2M1 magnitude {0, .5, 1, 1.5, 2, 3, 4, 6}, ties to the
+// even code: multiples of 0.5 below 1, otherwise the fp32 mantissa rounded to
+// one bit (RNE on bit 22).
+__device__ __forceinline__ float e2m1_round_mag(float a) {
+  const float lo = rintf(a * 2.0f) * 0.5f;
+  const uint32_t u = __float_as_uint(a);
+  const float hi = __uint_as_float((u + 0x1FFFFFu + ((u >> 22) & 1u)) & 0xFFC00000u);
+  return a < 1.0f ? lo : hi;
 }
-__device__ __forceinline__ float e2m1_value_mag(uint32_t c) {
-  // 0, .5, 1, 1.5 for c < 4; then 2, 3, 4, 6
-  float lo = (float)c * 0.5f;
-  float hi = (c == 4u) ? 2.0f : (c == 5u) ? 3.0f : (c == 6u) ? 4.0f : 6.0f;
-  return c < 4u ? lo : hi;
+// E2M1 magnitude -> 3-bit code: 2 * v below 1, else (exponent - 126) << 1 | mantissa bit
+__device__ __forceinline__ uint32_t e2m1_code_of_mag(float v) {
+  const uint32_t u = __float_as_uint(v);
+  const uint32_t c_hi = (((u >> 23) - 126u) << 1) | ((u >> 22) & 1u);
+  return v < 1.0f ? (uint32_t)(v * 2.0f) : c_hi;
 }
 
 // One fake-quantized element: dequantized value, code, and STE terms.
@@ -59,13 +63,6 @@ struct FQElem {
   bool m;       // STE mask [lo <= z <= hi]
   float dvds;   // dv/ds (nvfp4: dv/dtheta before the g*[0<=theta<=448] factor)
   float dvdzp;  // int4 only
-};
-
-// Quantizer parameters for one element (already resolved from its group).
-struct ElemQ {
-  float s;    // effective scale (nvfp4: s_b; 0 -> zero block)
-  float r;    // 1/s
-  float zp;   // int4: clamp(rne(zp), 0, 15); else 0
 };
 
 // int8 symmetric
@@ -124,14 +121,14 @@ __device__ __forceinline__ FQElem fq_e2m1(float x, float s, float r) {
     o.dvdzp = 0.0f;
     return o;
   }
-  float z = x * r;
-  uint32_t c = e2m1_code_mag(fminf(fabsf(z), kE2M1Max));
-  bool neg = (__float_as_uint(z) >> 31) != 0;
-  float mag = e2m1_value_mag(c);
-  float val = neg ? -mag : mag;
-  o.m = (z >= -kE2M1Max) && (z <= kE2M1Max);
+  const float z = x * r;
+  const float az = fabsf(z);
+  const float mag = e2m1_round_mag(fminf(az, kE2M1Max));
+  const bool neg = (__float_as_uint(z) >> 31) != 0;
+  const float val = neg ? -mag : mag;
+  o.m = az <= kE2M1Max;
   o.v = val * s;
-  o.code = c | (neg ? 0x8u : 0u);
+  o.code = e2m1_code_of_mag(mag) | (neg ? 0x8u : 0u);
   o.dvds = val - (o.m ? z : 0.0f);
   o.dvdzp = 0.0f;
   return o;
@@ -157,6 +154,31 @@ __device__ __forceinline__ float nvfp4_dynamic_scale(float amax, float g) {
 }
 
 __device__ __forceinline__ float safe_recip(float s) { return s != 0.0f ? 1.0f / s : 0.0f; }
+
+// Straight-through factor dv/ds = value(c) - m*z of one element, without the
+// dequantized value or the code (what the dScale reduction needs). For NVFP4
+// the caller applies g*[0 <= theta <= 448] per block; a zero block scale comes
+// in as r = 0, which gives z = 0, value 0 and factor 0. int4 also returns
+// dv/dzp = -s*(1-m).
+template <int FMT>
+__device__ __forceinline__ float ste_factor(float x, float s, float r, float zpi, float &dvdzp) {
+  const float z = x * r;
+  if (FMT == FQ_FMT_NVFP4 || FMT == FQ_FMT_FP8_E4M3) {
+    const float mx = FMT == FQ_FMT_NVFP4 ? kE2M1Max : kE4M3Max;
+    const float az = fabsf(z);
+    const float ac = fminf(az, mx);
+    const float mag = FMT == FQ_FMT_NVFP4 ? e2m1_round_mag(ac) : e4m3_round_mag(ac);
+    const float val = __builtin_copysignf(mag, z);
+    dvdzp = 0.0f;
+    return val - (az <= mx ? z : 0.0f);
+  }
+  const float lo = FMT == FQ_FMT_INT4 ? -zpi : -128.0f;
+  const float hi = FMT == FQ_FMT_INT4 ? 15.0f - zpi : 127.0f;
+  const float zc = fminf(fmaxf(z, lo), hi);
+  const bool m = zc == z;
+  dvdzp = m ? 0.0f : -s;
+  return rintf(zc) - (m ? z : 0.0f);
+}
 
 // Generic per-element dispatch for weights (fmt known at runtime).
 __device__ __forceinline__ FQElem fq_weight_elem(int fmt, float x, float s, float r, float zpi) {

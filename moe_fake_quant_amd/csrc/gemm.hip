@@ -193,20 +193,26 @@ template <int WFMT, int U>
 __device__ __forceinline__ void wgrad_epilogue(const GemmArgs &a, const f32x16 (&acc)[4][2], int e,
                                                int k0, int n0, int lane) {
   const int n = n0 + (lane & 31);
+  const int h = lane >> 5;
   const int G = a.K / a.group;
   const float g_e = (WFMT == FQ_FMT_NVFP4) ? a.gscale[e] : 1.0f;
   const uint16_t *wrow = a.w + ((size_t)e * a.N + n) * a.K;
   const size_t srow = ((size_t)e * a.N + n) * G;
+  // this lane's raw weights of the slab: k = k0 + 32s + 8q + 4h + v
+  uint2 wv[4][4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s)
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      wv[s][q] = *reinterpret_cast<const uint2 *>(wrow + k0 + s * 32 + 8 * q + 4 * h);
   float part_s[4], part_z[4];
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
-    float ps16[2] = {0.0f, 0.0f}, pz16[2] = {0.0f, 0.0f};  // the sub-tile's two 16-blocks
+    float ps16[2], pz16[2];  // the sub-tile's two 16-blocks
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int k = k0 + s * 32 + 8 * q + 4 * (lane >> 5);
-      const uint2 wv = *reinterpret_cast<const uint2 *>(wrow + k);
-      const float x4[4] = {lo_bf16(wv.x), hi_bf16(wv.x), lo_bf16(wv.y), hi_bf16(wv.y)};
-      const int gi = k / a.group;
+    for (int b = 0; b < 2; ++b) {
+      // every group is a multiple of 16 long: one scale per 16-block
+      const int gi = (k0 + s * 32 + 16 * b) / a.group;
       float sc = a.scale[srow + gi];
       float zpi = 0.0f, fac = 1.0f;
       if (WFMT == FQ_FMT_INT4) zpi = fminf(fmaxf(rintf(a.zero_point[srow + gi]), 0.0f), 15.0f);
@@ -215,13 +221,23 @@ __device__ __forceinline__ void wgrad_epilogue(const GemmArgs &a, const f32x16 (
         sc = nvfp4_block_scale(sc, g_e);
       }
       const float r = safe_recip(sc);
+      float accs = 0.0f, accz = 0.0f;
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const FQElem fe = fq_weight_elem(WFMT, x4[v], sc, r, zpi);
-        const float d = acc[s][U][4 * q + v];
-        ps16[q >> 1] += d * (fe.dvds * fac);
-        if (WFMT == FQ_FMT_INT4) pz16[q >> 1] += d * fe.dvdzp;
+      for (int qq = 0; qq < 2; ++qq) {
+        const int q = 2 * b + qq;
+        const float x4[4] = {lo_bf16(wv[s][q].x), hi_bf16(wv[s][q].x), lo_bf16(wv[s][q].y),
+                             hi_bf16(wv[s][q].y)};
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          float dzp;
+          const float phi = ste_factor<WFMT>(x4[v], sc, r, zpi, dzp);
+          const float d = acc[s][U][4 * q + v];
+          accs += d * phi;
+          if (WFMT == FQ_FMT_INT4) accz += d * dzp;
+        }
       }
+      ps16[b] = (WFMT == FQ_FMT_NVFP4) ? accs * fac : accs;
+      pz16[b] = accz;
     }
     // a 16-block is split between this lane (k%8 < 4 or >= 4) and lane ^ 32
 #pragma unroll
@@ -251,10 +267,10 @@ __device__ __forceinline__ void wgrad_epilogue(const GemmArgs &a, const f32x16 (
       }
     } else if (a.group == 64) {
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int kb = (k0 + h * 64) / 64;
-        a.dscale[srow + kb] = part_s[2 * h] + part_s[2 * h + 1];
-        if (WFMT == FQ_FMT_INT4 && a.dzp) a.dzp[srow + kb] = part_z[2 * h] + part_z[2 * h + 1];
+      for (int h2 = 0; h2 < 2; ++h2) {
+        const int kb = (k0 + h2 * 64) / 64;
+        a.dscale[srow + kb] = part_s[2 * h2] + part_s[2 * h2 + 1];
+        if (WFMT == FQ_FMT_INT4 && a.dzp) a.dzp[srow + kb] = part_z[2 * h2] + part_z[2 * h2 + 1];
       }
     } else {
       const float s128 = (part_s[0] + part_s[1]) + (part_s[2] + part_s[3]);

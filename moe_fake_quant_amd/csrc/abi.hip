@@ -185,6 +185,7 @@ fq_status fq_grouped_gemm_fwd(const uint16_t *x, int32_t R_max, const int32_t *s
   FQ_TRY(check_act_q(aq, s.K));
   FQ_CHECK_SUPPORTED(s.N % 256 == 0 && s.K % 64 == 0,
                      "grouped GEMM forward needs N %% 256 == 0 and K %% 64 == 0 (N=%d K=%d)", s.N, s.K);
+  FQ_CHECK_SUPPORTED(s.E <= 1024, "grouped GEMM supports up to 1024 experts per stack (E=%d)", s.E);
   FQ_CHECK_SUPPORTED((size_t)R_max * s.K * 2 < (1ull << 32) && (size_t)s.N * s.K * 2 < (1ull << 32),
                      "operands must stay below 4 GiB (32-bit tile offsets)");
   FQ_CHECK_ARG((!x || aligned16(x)) && aligned16(y) && (!w || aligned16(w)) &&
@@ -235,6 +236,7 @@ fq_status fq_grouped_gemm_bwd_scale(const uint16_t *dy, const uint16_t *x, int32
   FQ_CHECK_SUPPORTED(s.N % 256 == 0 && s.K % 256 == 0,
                      "grouped GEMM backward needs N %% 256 == 0 and K %% 256 == 0 (N=%d K=%d)", s.N,
                      s.K);
+  FQ_CHECK_SUPPORTED(s.E <= 1024, "grouped GEMM supports up to 1024 experts per stack (E=%d)", s.E);
   FQ_CHECK_SUPPORTED((size_t)R_max * (s.K > s.N ? s.K : s.N) * 2 < (1ull << 32) &&
                          (size_t)s.N * s.K * 2 < (1ull << 32),
                      "operands must stay below 4 GiB (32-bit tile offsets)");

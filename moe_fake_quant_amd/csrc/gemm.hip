@@ -2,33 +2,37 @@
 // fp32 accumulation: all experts of a stack in one launch (AngelSlim mcore_qad
 // article, section 二.4), forward and the scale-only backward (section 一).
 //
-// One kernel computes C[i][j] = sum_c P[i][c] * Q[j][c] on a 256 x 256 tile
-// with a 64-deep contraction step; four waves, each 128 x 128 (4 x 4 MFMA
-// 32x32 sub-tiles). Operands are staged global -> registers -> LDS (double
-// buffered), LDS rows are 128 B with a 16-byte-slot XOR swizzle so that both
-// the staging writes and the MFMA fragment reads are bank-conflict free.
+// One kernel computes C[i][j] = sum_c P[i][c] * Q[j][c] on a 256 x 256 tile.
+// Eight waves (two per SIMD), each 128 (i) x 64 (j) = 4 x 2 MFMA 32x32 tiles.
 //
-//   mode   P (row operand, i)          Q (column operand, j)     contraction
-//   FWD    W_fq[e] rows n   (K-contig) X rows r of segment e      k
-//   DGRAD  W_fq[e] as [n][k] -> i = k  dY rows r (N-contig)       n
-//          (transposed on the way into LDS)
-//   WGRAD  X rows -> i = k (transposed) dY rows -> j = n (transp.) routed rows r
+//   mode   P (row operand, i)            Q (column operand, j)        contraction
+//   FWD    W_fq[e] rows n (K-contig)     X rows r of segment e         k
+//   DGRAD  W_fq[e] [n][k]: i = k         dY rows r (N-contig)          n
+//   WGRAD  X rows: i = k                 dY rows: j = n                routed rows r
 //
-// A "transposed" operand is read as 8 contraction rows x 8 contiguous
-// columns per lane (eight 16-byte loads) and turned into eight 8-long
-// contraction vectors with v_perm_b32 before its LDS write.
+// Operands stream from global memory straight into LDS (global_load_lds,
+// 16 bytes per lane, no staging registers) through a ring of 4 stages of 32
+// contraction elements, three stages ahead of the MFMAs; one barrier per
+// stage. A contraction-contiguous operand is stored as 256 rows x 64 B and
+// read with ds_read_b128; a transposed operand (contraction is its row) keeps
+// its natural layout, 32 rows x 512 B, and the MFMA fragments are gathered
+// with ds_read_tr16_b64 (a 4 x 16 -> 16 x 4 transpose inside each 16-lane
+// group). Both layouts XOR-swizzle 16-byte chunks so the fragment reads are
+// bank-conflict free.
 //
 // FWD / DGRAD store bf16 rows; WGRAD never stores dW: its epilogue
 // multiplies each dWq element by the straight-through factor dv/ds
 // (recomputed from the raw weight and its scale) and reduces over the
 // quantization group (dScale), deterministically.
 //
-// Scheduling: FWD / DGRAD tiles are (expert, row tile, i tile); the number of
-// row tiles of each expert comes from seg_offsets on the device (a block-wide
-// scan in LDS), so empty experts cost nothing and no host sync is needed.
-// Block ids are remapped so that consecutive tiles land on the same XCD (the
-// hardware deals blocks round-robin over the 8 XCDs), keeping an expert's
-// weights and rows in one XCD's L2.
+// Scheduling: a persistent grid of one block per CU walks the tile list.
+// FWD / DGRAD tiles are (expert, row tile, i tile); the number of row tiles of
+// each expert comes from seg_offsets on the device (a block-wide scan in
+// LDS), so empty experts cost nothing and no host sync is needed. Each of the
+// 8 XCDs owns a contiguous eighth of the tiles, keeping the panels its blocks
+// share in its own L2.
+#include <type_traits>
+
 #include "internal.hpp"
 
 namespace fq {
@@ -37,86 +41,75 @@ namespace {
 
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8v;
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 
 constexpr int BI = 256;   // tile rows (i)
 constexpr int BJ = 256;   // tile cols (j)
-constexpr int BK = 64;    // contraction step
+constexpr int BK = 32;    // contraction elements per stage
+constexpr int NSTAGE = 4;
 constexpr int NT = 512;   // threads per block (8 waves, 2 per SIMD)
 constexpr int WJ_TILE = 64;  // j extent of one wave (waves: 2 along i x 4 along j)
-constexpr int kTileBytes = 256 * BK * 2;  // one operand tile in LDS (32 KiB)
+constexpr int kStageBytes = 256 * BK * 2;  // one operand, one stage: 16 KiB
 
 enum Mode { FWD = 0, DGRAD = 1, WGRAD = 2 };
 
-// byte offset of 16-byte slot kc (0..7) of LDS row idx (0..255)
-__device__ __forceinline__ uint32_t lds_off(uint32_t idx, uint32_t kc) {
-  uint32_t swz = (idx ^ (idx >> 3)) & 7u;
-  return idx * 128u + ((kc ^ swz) << 4);
+// The ring: distinct LDS objects per stage and operand, so that the compiler
+// can tell a stage being read from the stages being filled.
+__shared__ __attribute__((aligned(1024))) char g_p0[kStageBytes];
+__shared__ __attribute__((aligned(1024))) char g_p1[kStageBytes];
+__shared__ __attribute__((aligned(1024))) char g_p2[kStageBytes];
+__shared__ __attribute__((aligned(1024))) char g_p3[kStageBytes];
+__shared__ __attribute__((aligned(1024))) char g_q0[kStageBytes];
+__shared__ __attribute__((aligned(1024))) char g_q1[kStageBytes];
+__shared__ __attribute__((aligned(1024))) char g_q2[kStageBytes];
+__shared__ __attribute__((aligned(1024))) char g_q3[kStageBytes];
+
+template <int S>
+__device__ __forceinline__ char *stage_p() {
+  return S == 0 ? g_p0 : S == 1 ? g_p1 : S == 2 ? g_p2 : g_p3;
+}
+template <int S>
+__device__ __forceinline__ char *stage_q() {
+  return S == 0 ? g_q0 : S == 1 ? g_q1 : S == 2 ? g_q2 : g_q3;
 }
 
-__device__ __forceinline__ bf16x8_t ldg16(const char *base, uint32_t byte_off) {
-  return *reinterpret_cast<const bf16x8_t *>(base + byte_off);
+// Contraction-contiguous layout: row idx (0..255) of 4 16-byte chunks (8
+// contraction elements each); chunk kc sits at kc ^ sw(idx).
+__device__ __forceinline__ uint32_t nrm_sw(uint32_t idx) { return ((idx >> 1) ^ (idx >> 3)) & 3u; }
+__device__ __forceinline__ uint32_t nrm_off(uint32_t idx, uint32_t kc) {
+  return idx * 64u + ((kc ^ nrm_sw(idx)) << 4);
+}
+// Transposed layout: contraction row c (0..31) of 32 16-byte chunks (8 columns
+// each); column chunk q sits at q ^ tr_sw(c). Within the four rows a
+// ds_read_tr16_b64 group touches, the swizzle spreads their chunks over
+// distinct banks.
+__device__ __forceinline__ uint32_t tr_sw(uint32_t c) {
+  const uint32_t r = c & 3u;
+  return 4u * r + 2u * (r >> 1);
+}
+__device__ __forceinline__ uint32_t trn_off(uint32_t c, uint32_t chunk) {
+  return c * 512u + ((chunk ^ tr_sw(c)) << 4);
 }
 
-// ---- normal operand: 256 rows of a row-major matrix, 64 contiguous contraction
-// elements each. Thread t: rows u*32 + t/8 (u = 0..7), 16-byte slot t%8.
-// The per-thread row byte offsets are fixed for a tile; the contraction step
-// adds c0*2 bytes. Offsets are 32-bit from a block-uniform base pointer.
-struct NormalRows {
-  uint32_t off[4];
-  __device__ __forceinline__ void init(size_t ld, int row0, int row_last) {
-    const int t = threadIdx.x;
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      int r = min(row0 + u * 64 + (t >> 3), row_last);
-      off[u] = (uint32_t)(((size_t)r * ld + (t & 7) * 8) * 2);
-    }
-  }
-  __device__ __forceinline__ void load(bf16x8_t (&v)[4], const char *base, int c0) const {
-#pragma unroll
-    for (int u = 0; u < 4; ++u) v[u] = ldg16(base, off[u] + c0 * 2);
-  }
-};
-__device__ __forceinline__ void store_normal(char *lds, const bf16x8_t (&v)[4]) {
-  const int t = threadIdx.x;
-#pragma unroll
-  for (int u = 0; u < 4; ++u)
-    *reinterpret_cast<bf16x8_t *>(lds + lds_off(u * 64 + (t >> 3), t & 7)) = v[u];
+// 16 bytes per lane from global memory into LDS at lds_wave_base + 16 * lane.
+// Issued as inline asm: the compiler then does not model the LDS write and
+// inserts no wait before reads of the other stages; the ring's own
+// vmcnt waits and barriers order the accesses.
+__device__ __forceinline__ void dma16(const char *g, char *lds_wave_base) {
+  const uint32_t m0v = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_wave_base);
+  asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(g), "{m0}"(m0v) : "memory");
 }
 
-// ---- transposed operand: element (c, idx) at base[c * ld + idx]; the tile is
-// contraction rows c0..c0+63 x idx idx0..idx0+255. Thread t: idx block t%32
-// (8 columns), contraction block t/32 (4 rows). Rows c >= c_end read as 0.
-__device__ __forceinline__ void load_trans(bf16x8_t (&v)[4], const char *base, uint32_t ld, int c0,
-                                           int c_end, int idx0) {
-  const int t = threadIdx.x;
-  const uint32_t col = idx0 + (t & 31) * 8;
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    int c = c0 + (t >> 5) * 4 + q;
-    bool ok = c < c_end;
-    int cc = ok ? c : c0;  // c0 < c_end whenever this tile is loaded
-    bf16x8_t x = ldg16(base, ((uint32_t)cc * ld + col) * 2);
-    v[q].w[0] = ok ? x.w[0] : 0u;
-    v[q].w[1] = ok ? x.w[1] : 0u;
-    v[q].w[2] = ok ? x.w[2] : 0u;
-    v[q].w[3] = ok ? x.w[3] : 0u;
-  }
-}
-// 4 contraction rows x 8 columns -> 8 columns x 4 contraction values (8 bytes
-// each, half of a 16-byte LDS slot)
-__device__ __forceinline__ void store_trans(char *lds, const bf16x8_t (&v)[4]) {
-  const int t = threadIdx.x;
-  const uint32_t idxb = (t & 31) * 8, cb = t >> 5, kc = cb >> 1, half = (cb & 1) * 8;
-#pragma unroll
-  for (int p = 0; p < 4; ++p) {
-    uint2 lo, hi;  // columns 2p and 2p+1
-    lo.x = __builtin_amdgcn_perm(v[1].w[p], v[0].w[p], 0x05040100u);
-    lo.y = __builtin_amdgcn_perm(v[3].w[p], v[2].w[p], 0x05040100u);
-    hi.x = __builtin_amdgcn_perm(v[1].w[p], v[0].w[p], 0x07060302u);
-    hi.y = __builtin_amdgcn_perm(v[3].w[p], v[2].w[p], 0x07060302u);
-    *reinterpret_cast<uint2 *>(lds + lds_off(idxb + 2 * p, kc) + half) = lo;
-    *reinterpret_cast<uint2 *>(lds + lds_off(idxb + 2 * p + 1, kc) + half) = hi;
-  }
+// One barrier for the whole block without a memory fence (a fence would wait
+// for every outstanding load, draining the ring).
+__device__ __forceinline__ void block_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+// s_waitcnt vmcnt(n) leaving the other counters alone (gfx9 encoding)
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
 struct GemmArgs {
@@ -136,53 +129,48 @@ struct GemmArgs {
   float *pscale, *pzp;     // partials per 128-chunk of K (group > 128), or NULL
 };
 
-// Expert and first row of this block's row tile: block-wide scan of per-expert
-// row-tile counts (E <= 256 per pass, looped). Returns false when the block
-// has no tile.
-__device__ bool find_row_tile(const int32_t *seg, int E, int tile, int &e_out, int &row0,
-                              int &row_end) {
-  __shared__ int s_found[3];
+constexpr int kMaxExperts = 1024;
+
+// tile_start[e] = number of BJ-row tiles of experts 0..e-1 (e = 0..E), from
+// seg_offsets on the device: a block-wide exclusive scan in LDS.
+__device__ void build_tile_prefix(const int32_t *seg, int E, int *tile_start) {
   __shared__ int s_wsum[NT / 64];
-  if (threadIdx.x == 0) s_found[0] = -1;
-  __syncthreads();
-  int base_tiles = 0;
+  int base = 0;
   for (int e0 = 0; e0 < E; e0 += NT) {
-    int e = e0 + threadIdx.x;
-    int lo = 0, hi = 0, nt = 0;
-    if (e < E) {
-      lo = seg[e];
-      hi = seg[e + 1];
-      nt = (hi - lo + BJ - 1) / BJ;
-    }
-    // inclusive scan of nt
-    int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int e = e0 + threadIdx.x;
+    const int nt = e < E ? (seg[e + 1] - seg[e] + BJ - 1) / BJ : 0;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     int x = nt;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
-      int y = __shfl_up(x, o, 64);
+      const int y = __shfl_up(x, o, 64);
       if (lane >= o) x += y;
     }
     if (lane == 63) s_wsum[w] = x;
     __syncthreads();
-    int before = base_tiles, total = base_tiles;
+    int before = base, total = base;
 #pragma unroll
     for (int k = 0; k < NT / 64; ++k) {
       if (k < w) before += s_wsum[k];
       total += s_wsum[k];
     }
-    int start = before + x - nt;
-    if (e < E && tile >= start && tile < start + nt) {
-      s_found[0] = e;
-      s_found[1] = lo + (tile - start) * BJ;
-      s_found[2] = hi;
-    }
+    if (e < E) tile_start[e] = before + x - nt;
     __syncthreads();
-    base_tiles = total;
+    base = total;
   }
-  e_out = s_found[0];
-  row0 = s_found[1];
-  row_end = s_found[2];
-  return e_out >= 0;
+  if (threadIdx.x == 0) tile_start[E] = base;
+  __syncthreads();
+}
+
+// expert of row tile `tile`: the last e with tile_start[e] <= tile
+__device__ __forceinline__ int expert_of_tile(const int *tile_start, int E, int tile) {
+  int lo = 0, hi = E;  // tile_start[lo] <= tile < tile_start[hi]
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (tile_start[mid] <= tile) lo = mid;
+    else hi = mid;
+  }
+  return lo;
 }
 
 // dS of the 128 (k) x 32 (n) slab of dWq that column sub-tile U (0..1) of one wave
@@ -288,39 +276,92 @@ __device__ __forceinline__ void wgrad_epilogue(const GemmArgs &a, const f32x16 (
   }
 }
 
+// Per-lane global byte offsets of the operand rows this lane streams, fixed
+// for a tile. A wave issues 2 DMA instructions per operand per stage, each
+// filling 1 KiB of LDS (lane l -> byte 16 l of it).
+struct NormalDMA {  // contraction-contiguous: instr covers 16 rows x 64 B
+  uint32_t off[2];
+  __device__ __forceinline__ void init(size_t ld, int row0, int row_last, int wave, int lane) {
+#pragma unroll
+    for (int ii = 0; ii < 2; ++ii) {
+      const uint32_t idx = 16 * (2 * wave + ii) + (lane >> 2);
+      const uint32_t kc = (lane & 3) ^ nrm_sw(idx);
+      const int r = min(row0 + (int)idx, row_last);
+      off[ii] = (uint32_t)(((size_t)r * ld + kc * 8) * 2);
+    }
+  }
+  template <int S>
+  __device__ __forceinline__ void issue(const char *base, char *stage, int c0, int wave) const {
+#pragma unroll
+    for (int ii = 0; ii < 2; ++ii) dma16(base + off[ii] + c0 * 2, stage + (2 * wave + ii) * 1024);
+  }
+};
+struct TransDMA {  // transposed: instr covers 2 contraction rows x 512 B
+  uint32_t col_off[2];
+  int crow[2];
+  __device__ __forceinline__ void init(int idx0, int wave, int lane) {
+#pragma unroll
+    for (int ii = 0; ii < 2; ++ii) {
+      crow[ii] = 2 * (2 * wave + ii) + (lane >> 5);
+      const uint32_t q = (lane & 31) ^ tr_sw(crow[ii]);
+      col_off[ii] = (uint32_t)((idx0 + 8 * q) * 2);
+    }
+  }
+  // rows c >= c_end are read from row c0 (valid memory) and zeroed later
+  __device__ __forceinline__ void issue(const char *base, uint32_t ld, char *stage, int c0,
+                                        int c_end, int wave) const {
+#pragma unroll
+    for (int ii = 0; ii < 2; ++ii) {
+      const int c = c0 + crow[ii];
+      const int cc = c < c_end ? c : c0;
+      dma16(base + (size_t)cc * ld * 2 + col_off[ii], stage + (2 * wave + ii) * 1024);
+    }
+  }
+};
+
+// MFMA fragment (8 contraction elements of one row / column) from a stage
+__device__ __forceinline__ bf16x8v frag_normal(const char *stage, int base, int ks, int lane) {
+  return *reinterpret_cast<const bf16x8v *>(stage + nrm_off(base + (lane & 31), 2 * ks + (lane >> 5)));
+}
+__device__ __forceinline__ bf16x8v frag_trans(const char *stage, int base, int ks, int lane) {
+  const int g = lane >> 4, j = lane & 15;
+  const uint32_t chunk = (uint32_t)(base >> 3) + 2 * (g & 1) + ((j & 3) >> 1);
+  const uint32_t half = (j & 1) * 8;
+  const uint32_t c = 16 * ks + 8 * (g >> 1) + (j >> 2);
+  const v4i16 lo =
+      __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(stage + trn_off(c, chunk) + half));
+  const v4i16 hi =
+      __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(stage + trn_off(c + 4, chunk) + half));
+  const v4i16 a[2] = {lo, hi};
+  bf16x8v r;
+  __builtin_memcpy(&r, a, 16);
+  return r;
+}
+// zero the contraction elements c0 + 16 ks + 8 (lane/32) + t >= c_end
+__device__ __forceinline__ bf16x8v zero_tail(bf16x8v f, int cfirst, int c_end) {
+  uint32_t w[4];
+  __builtin_memcpy(w, &f, 16);
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const int c = cfirst + 2 * t;
+    const uint32_t keep = (c < c_end ? 0x0000FFFFu : 0u) | (c + 1 < c_end ? 0xFFFF0000u : 0u);
+    w[t] &= keep;
+  }
+  bf16x8v r;
+  __builtin_memcpy(&r, w, 16);
+  return r;
+}
+
+// One 256 x 256 output tile: the contraction loop and the epilogue.
 template <int MODE, int WFMT>
-__global__ __launch_bounds__(NT) void k_grouped_gemm(GemmArgs a) {
-  __shared__ __attribute__((aligned(16))) char smem[4 * kTileBytes];  // P0 Q0 P1 Q1 = 128 KiB
+__device__ __forceinline__ void run_tile(const GemmArgs &a, int e, int i0, int j0, int j_end) {
   const int t = threadIdx.x;
   const int lane = t & 63, wave = t >> 6;
   const int wi = wave & 1, wj = wave >> 1;  // 2 x 4 waves: 128 (i) x 64 (j) each
-
-  // XCD-aware remap of the block id
-  const uint32_t nb = gridDim.x, b = blockIdx.x;
-  const uint32_t wid = (b & 7u) * (nb >> 3) + (b >> 3);
-
-  int e, it, j0 = 0, j_end = 0, i0;
-  int c_total;  // contraction length
-  if (MODE == WGRAD) {
-    const int per_e = a.n_it * a.n_jt;
-    e = wid / per_e;
-    if (e >= a.E) return;
-    int rem = wid - e * per_e;
-    int jt = rem / a.n_it;
-    it = rem - jt * a.n_it;
-    j0 = jt * BJ;
-    i0 = it * BI;
-  } else {
-    int tile = wid / a.n_it;
-    it = wid - tile * a.n_it;
-    i0 = it * BI;
-    if (!find_row_tile(a.seg, a.E, tile, e, j0, j_end)) return;
-  }
   const int seg_lo = a.seg[e], seg_hi = a.seg[e + 1];
-  if (MODE == WGRAD) c_total = seg_hi - seg_lo;
-  else c_total = (MODE == FWD) ? a.K : a.N;
+  const int c_total = (MODE == WGRAD) ? seg_hi - seg_lo : (MODE == FWD) ? a.K : a.N;
 
-  // operand base pointers (block-uniform) and leading dimensions
+  // operand bases (block-uniform)
   const size_t NK = (size_t)a.N * a.K;
   const char *pbase, *qbase;
   if (MODE == FWD) {
@@ -333,10 +374,34 @@ __global__ __launch_bounds__(NT) void k_grouped_gemm(GemmArgs a) {
     pbase = reinterpret_cast<const char *>(a.p + (size_t)seg_lo * a.K);  // Xq: (c = r, idx = k)
     qbase = reinterpret_cast<const char *>(a.q + (size_t)seg_lo * a.N);  // dY: (c = r, idx = n)
   }
-  NormalRows prow, qrow;
-  if (MODE == FWD) prow.init(a.K, i0, a.N - 1);
-  if (MODE == FWD) qrow.init(a.K, j0, j_end - 1);
-  if (MODE == DGRAD) qrow.init(a.N, j0, j_end - 1);
+  NormalDMA pn, qn;
+  TransDMA pt, qt;
+  if (MODE == FWD) {
+    pn.init(a.K, i0, a.N - 1, wave, lane);
+    qn.init(a.K, j0, j_end - 1, wave, lane);
+  } else if (MODE == DGRAD) {
+    pt.init(i0, wave, lane);
+    qn.init(a.N, j0, j_end - 1, wave, lane);
+  } else {
+    pt.init(i0, wave, lane);
+    qt.init(j0, wave, lane);
+  }
+  const int nk = (c_total + BK - 1) / BK;
+
+  auto issue = [&](auto stage_tag, int kt) {
+    constexpr int S = decltype(stage_tag)::value;
+    const int c0 = kt * BK;
+    if (MODE == FWD) {
+      pn.template issue<S>(pbase, stage_p<S>(), c0, wave);
+      qn.template issue<S>(qbase, stage_q<S>(), c0, wave);
+    } else if (MODE == DGRAD) {
+      pt.issue(pbase, a.K, stage_p<S>(), c0, c_total, wave);
+      qn.template issue<S>(qbase, stage_q<S>(), c0, wave);
+    } else {
+      pt.issue(pbase, a.K, stage_p<S>(), c0, c_total, wave);
+      qt.issue(qbase, a.N, stage_q<S>(), c0, c_total, wave);
+    }
+  };
 
   f32x16 acc[4][2];
 #pragma unroll
@@ -346,76 +411,51 @@ __global__ __launch_bounds__(NT) void k_grouped_gemm(GemmArgs a) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[s][u][v] = 0.0f;
 
-  const int nk = (c_total + BK - 1) / BK;
-  bf16x8_t rp[4], rq[4];
-
-  auto load_tile = [&](int kt) {
-    const int c0 = kt * BK;
-    if (MODE == FWD) {
-      prow.load(rp, pbase, c0);
-      qrow.load(rq, qbase, c0);
-    } else if (MODE == DGRAD) {
-      load_trans(rp, pbase, a.K, c0, c_total, i0);
-      qrow.load(rq, qbase, c0);
-    } else {
-      load_trans(rp, pbase, a.K, c0, c_total, i0);
-      load_trans(rq, qbase, a.N, c0, c_total, j0);
-    }
-  };
-  auto store_tile = [&](int buf) {
-    char *sp = smem + (2 * buf) * kTileBytes;
-    char *sq = smem + (2 * buf + 1) * kTileBytes;
-    if (MODE == FWD) {
-      store_normal(sp, rp);
-      store_normal(sq, rq);
-    } else if (MODE == DGRAD) {
-      store_trans(sp, rp);
-      store_normal(sq, rq);
-    } else {
-      store_trans(sp, rp);
-      store_trans(sq, rq);
-    }
-  };
-  // MFMA fragments of one 16-deep step: [0..3] P sub-tiles, [4..5] Q sub-tiles
-  auto read_frags = [&](int buf, int ks, bf16x8v (&f)[6]) {
-    const char *sp = smem + (2 * buf) * kTileBytes;
-    const char *sq = smem + (2 * buf + 1) * kTileBytes;
-    const uint32_t kc = ks * 2 + (lane >> 5);
-#pragma unroll
-    for (int s = 0; s < 4; ++s)
-      f[s] = *reinterpret_cast<const bf16x8v *>(sp + lds_off(wi * 128 + s * 32 + (lane & 31), kc));
-#pragma unroll
-    for (int u = 0; u < 2; ++u)
-      f[4 + u] = *reinterpret_cast<const bf16x8v *>(sq + lds_off(wj * WJ_TILE + u * 32 + (lane & 31), kc));
-  };
-
-  // Pipeline: global loads of tile kt+1 are in flight during the MFMAs of
-  // tile kt; the fragments of step ks+1 are read from LDS during the MFMAs
-  // of step ks.
-  bf16x8v fr[2][6];
-  if (nk > 0) {
-    load_tile(0);
-    store_tile(0);
-    __syncthreads();
-    read_frags(0, 0, fr[0]);
-  }
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    const bool more = kt + 1 < nk;
-    if (more) load_tile(kt + 1);
+  // one stage: wait for its data, let every wave pass, refill the stage that
+  // was computed last (S + 3), then 2 x 16-deep MFMA steps on stage S
+  auto step = [&](auto stage_tag, int kt) {
+    constexpr int S = decltype(stage_tag)::value;
+    if (kt + 2 < nk) wait_vm<8>();  // this wave's loads of stages kt+1, kt+2 may stay in flight
+    else wait_vm<0>();
+    block_barrier();
+    if (kt + 3 < nk) issue(std::integral_constant<int, (S + 3) & 3>{}, kt + 3);
+    const char *sp = stage_p<S>();
+    const char *sq = stage_q<S>();
+    const bool tail = MODE == WGRAD && (kt + 1) * BK > c_total;
 #pragma unroll
     for (int ks = 0; ks < BK / 16; ++ks) {
-      if (ks + 1 < BK / 16) read_frags(cur, ks + 1, fr[(ks + 1) & 1]);
+      bf16x8v fp[4], fq[2];
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+        fp[s] = (MODE == FWD) ? frag_normal(sp, wi * 128 + s * 32, ks, lane)
+                              : frag_trans(sp, wi * 128 + s * 32, ks, lane);
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+        fq[u] = (MODE == WGRAD) ? frag_trans(sq, wj * WJ_TILE + u * 32, ks, lane)
+                                : frag_normal(sq, wj * WJ_TILE + u * 32, ks, lane);
+      if (tail) {
+        const int cfirst = kt * BK + 16 * ks + 8 * (lane >> 5);
+#pragma unroll
+        for (int s = 0; s < 4; ++s) fp[s] = zero_tail(fp[s], cfirst, c_total);
+#pragma unroll
+        for (int u = 0; u < 2; ++u) fq[u] = zero_tail(fq[u], cfirst, c_total);
+      }
 #pragma unroll
       for (int s = 0; s < 4; ++s)
 #pragma unroll
         for (int u = 0; u < 2; ++u)
-          acc[s][u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[ks & 1][s], fr[ks & 1][4 + u],
-                                                              acc[s][u], 0, 0, 0);
+          acc[s][u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fp[s], fq[u], acc[s][u], 0, 0, 0);
     }
-    if (more) store_tile(cur ^ 1);
-    __syncthreads();
-    if (more) read_frags(cur ^ 1, 0, fr[0]);
+  };
+
+  if (nk > 0) issue(std::integral_constant<int, 0>{}, 0);
+  if (nk > 1) issue(std::integral_constant<int, 1>{}, 1);
+  if (nk > 2) issue(std::integral_constant<int, 2>{}, 2);
+  for (int kt = 0; kt < nk; kt += NSTAGE) {
+    step(std::integral_constant<int, 0>{}, kt);
+    if (kt + 1 < nk) step(std::integral_constant<int, 1>{}, kt + 1);
+    if (kt + 2 < nk) step(std::integral_constant<int, 2>{}, kt + 2);
+    if (kt + 3 < nk) step(std::integral_constant<int, 3>{}, kt + 3);
   }
 
   // accumulator (s, u, v) of this lane: i = i0 + wi*128 + s*32 + 8*(v/4) + 4*(lane/32) + v%4,
@@ -449,10 +489,58 @@ __global__ __launch_bounds__(NT) void k_grouped_gemm(GemmArgs a) {
   }
 }
 
+// Persistent grid: one block per CU (the 128 KiB LDS ring allows one). The
+// hardware deals block b to XCD b % 8, so XCD x runs blocks x, x+8, ...; it
+// owns one contiguous eighth of the tile list and its blocks take tiles
+// round-robin, so the tiles in flight on an XCD are neighbours that share
+// operand panels in that XCD's L2. FWD / DGRAD tiles: (row tile, i tile)
+// with i fastest; the row tiles of each expert follow from seg_offsets.
+// WGRAD tiles: (expert, j tile, i tile).
+template <int MODE, int WFMT>
+__global__ __launch_bounds__(NT) void k_grouped_gemm(GemmArgs a) {
+  __shared__ int tile_start[kMaxExperts + 1];
+  int total;
+  if (MODE == WGRAD) {
+    total = a.E * a.n_it * a.n_jt;
+  } else {
+    build_tile_prefix(a.seg, a.E, tile_start);
+    total = tile_start[a.E] * a.n_it;
+  }
+  const int nslot = gridDim.x >> 3, xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+  const int chunk = (total + 7) >> 3;
+  const int w_end = min((xcd + 1) * chunk, total);
+  for (int w = xcd * chunk + slot; w < w_end; w += nslot) {
+    int e, i0, j0, j_end = 0;
+    if (MODE == WGRAD) {
+      const int per_e = a.n_it * a.n_jt;
+      e = w / per_e;
+      const int rem = w - e * per_e;
+      const int jt = rem / a.n_it;
+      i0 = (rem - jt * a.n_it) * BI;
+      j0 = jt * BJ;
+    } else {
+      const int tile = w / a.n_it;
+      i0 = (w - tile * a.n_it) * BI;
+      e = expert_of_tile(tile_start, a.E, tile);
+      j0 = a.seg[e] + (tile - tile_start[e]) * BJ;
+      j_end = a.seg[e + 1];
+    }
+    run_tile<MODE, WFMT>(a, e, i0, j0, j_end);
+    __syncthreads();  // the next tile reuses the LDS buffers
+  }
+}
+
 }  // namespace
 
 // ============================================================ launchers ====
-static int round8(long x) { return (int)((x + 7) / 8 * 8); }
+// one block per CU, a multiple of 8 (the XCD count)
+static int persistent_grid() {
+  int dev = 0, cus = 256;
+  if (hipGetDevice(&dev) == hipSuccess)
+    (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  cus = cus / 8 * 8;
+  return cus > 0 ? cus : 8;
+}
 
 void launch_gemm_fwd(const uint16_t *xq, int R_max, const int32_t *seg, fq_shape s,
                      const uint16_t *wfq, uint16_t *y, hipStream_t st) {
@@ -465,9 +553,8 @@ void launch_gemm_fwd(const uint16_t *xq, int R_max, const int32_t *seg, fq_shape
   a.K = s.K;
   a.n_it = s.N / BI;
   a.out = y;
-  long tiles = (long)(R_max / BJ + s.E) * a.n_it;
-  if (tiles <= 0 || R_max <= 0) return;
-  hipLaunchKernelGGL((k_grouped_gemm<FWD, 0>), dim3(round8(tiles)), dim3(NT), 0, st, a);
+  if (R_max <= 0) return;
+  hipLaunchKernelGGL((k_grouped_gemm<FWD, 0>), dim3(persistent_grid()), dim3(NT), 0, st, a);
 }
 
 void launch_gemm_dgrad(const uint16_t *dy, int R_max, const int32_t *seg, fq_shape s,
@@ -481,9 +568,8 @@ void launch_gemm_dgrad(const uint16_t *dy, int R_max, const int32_t *seg, fq_sha
   a.K = s.K;
   a.n_it = s.K / BI;
   a.out = dx;
-  long tiles = (long)(R_max / BJ + s.E) * a.n_it;
-  if (tiles <= 0 || R_max <= 0) return;
-  hipLaunchKernelGGL((k_grouped_gemm<DGRAD, 0>), dim3(round8(tiles)), dim3(NT), 0, st, a);
+  if (R_max <= 0) return;
+  hipLaunchKernelGGL((k_grouped_gemm<DGRAD, 0>), dim3(persistent_grid()), dim3(NT), 0, st, a);
 }
 
 void launch_gemm_wgrad_dscale(const uint16_t *dy, const uint16_t *xq, const int32_t *seg, fq_shape s,
@@ -508,8 +594,7 @@ void launch_gemm_wgrad_dscale(const uint16_t *dy, const uint16_t *xq, const int3
   a.dzp = dzp;
   a.pscale = pscale;
   a.pzp = pzp;
-  long tiles = (long)s.E * a.n_it * a.n_jt;
-  dim3 grid(round8(tiles)), block(NT);
+  dim3 grid(persistent_grid()), block(NT);
   switch (q.fmt) {
     case FQ_FMT_INT8: hipLaunchKernelGGL((k_grouped_gemm<WGRAD, FQ_FMT_INT8>), grid, block, 0, st, a); break;
     case FQ_FMT_INT4: hipLaunchKernelGGL((k_grouped_gemm<WGRAD, FQ_FMT_INT4>), grid, block, 0, st, a); break;

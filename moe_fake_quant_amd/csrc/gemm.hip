@@ -76,8 +76,10 @@ __device__ __forceinline__ char *stage_q() {
 }
 
 // Contraction-contiguous layout: row idx (0..255) of 4 16-byte chunks (8
-// contraction elements each); chunk kc sits at kc ^ sw(idx).
-__device__ __forceinline__ uint32_t nrm_sw(uint32_t idx) { return ((idx >> 1) ^ (idx >> 3)) & 3u; }
+// contraction elements each); chunk kc sits at kc ^ sw(idx). The swizzle
+// (rows in fours share one) was chosen by measuring the LDS bank-conflict
+// counter for the fragment read pattern (32 consecutive rows, one chunk).
+__device__ __forceinline__ uint32_t nrm_sw(uint32_t idx) { return (idx >> 2) & 3u; }
 __device__ __forceinline__ uint32_t nrm_off(uint32_t idx, uint32_t kc) {
   return idx * 64u + ((kc ^ nrm_sw(idx)) << 4);
 }
@@ -411,51 +413,122 @@ __device__ __forceinline__ void run_tile(const GemmArgs &a, int e, int i0, int j
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[s][u][v] = 0.0f;
 
-  // one stage: wait for its data, let every wave pass, refill the stage that
-  // was computed last (S + 3), then 2 x 16-deep MFMA steps on stage S
-  auto step = [&](auto stage_tag, int kt) {
+  // FWD / DGRAD: a wave whose 64 rows all lie past the expert's last row (the
+  // ragged last row tile) skips its fragment reads and MFMAs; it still takes
+  // part in the loads and barriers.
+  const bool live = MODE == WGRAD || j0 + wj * WJ_TILE < j_end;
+
+  // MFMA fragments of one 16-deep step: 4 P sub-tiles, 2 Q sub-tiles
+  struct Frags {
+    bf16x8v p[4], q[2];
+  };
+  auto read_frags = [&](auto stage_tag, int kt, int ks, Frags &f) {
     constexpr int S = decltype(stage_tag)::value;
-    if (kt + 2 < nk) wait_vm<8>();  // this wave's loads of stages kt+1, kt+2 may stay in flight
-    else wait_vm<0>();
-    block_barrier();
-    if (kt + 3 < nk) issue(std::integral_constant<int, (S + 3) & 3>{}, kt + 3);
+    if (!live) return;
     const char *sp = stage_p<S>();
     const char *sq = stage_q<S>();
-    const bool tail = MODE == WGRAD && (kt + 1) * BK > c_total;
 #pragma unroll
-    for (int ks = 0; ks < BK / 16; ++ks) {
-      bf16x8v fp[4], fq[2];
+    for (int s = 0; s < 4; ++s)
+      f.p[s] = (MODE == FWD) ? frag_normal(sp, wi * 128 + s * 32, ks, lane)
+                             : frag_trans(sp, wi * 128 + s * 32, ks, lane);
 #pragma unroll
-      for (int s = 0; s < 4; ++s)
-        fp[s] = (MODE == FWD) ? frag_normal(sp, wi * 128 + s * 32, ks, lane)
-                              : frag_trans(sp, wi * 128 + s * 32, ks, lane);
+    for (int u = 0; u < 2; ++u)
+      f.q[u] = (MODE == WGRAD) ? frag_trans(sq, wj * WJ_TILE + u * 32, ks, lane)
+                               : frag_normal(sq, wj * WJ_TILE + u * 32, ks, lane);
+    if (MODE == WGRAD && (kt + 1) * BK > c_total) {  // ragged tail of the routed rows
+      const int cfirst = kt * BK + 16 * ks + 8 * (lane >> 5);
 #pragma unroll
-      for (int u = 0; u < 2; ++u)
-        fq[u] = (MODE == WGRAD) ? frag_trans(sq, wj * WJ_TILE + u * 32, ks, lane)
-                                : frag_normal(sq, wj * WJ_TILE + u * 32, ks, lane);
-      if (tail) {
-        const int cfirst = kt * BK + 16 * ks + 8 * (lane >> 5);
+      for (int s = 0; s < 4; ++s) f.p[s] = zero_tail(f.p[s], cfirst, c_total);
 #pragma unroll
-        for (int s = 0; s < 4; ++s) fp[s] = zero_tail(fp[s], cfirst, c_total);
-#pragma unroll
-        for (int u = 0; u < 2; ++u) fq[u] = zero_tail(fq[u], cfirst, c_total);
-      }
-#pragma unroll
-      for (int s = 0; s < 4; ++s)
-#pragma unroll
-        for (int u = 0; u < 2; ++u)
-          acc[s][u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fp[s], fq[u], acc[s][u], 0, 0, 0);
+      for (int u = 0; u < 2; ++u) f.q[u] = zero_tail(f.q[u], cfirst, c_total);
     }
   };
+  auto mfmas = [&](const Frags &f) {
+    if (!live) return;
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+        acc[s][u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.p[s], f.q[u], acc[s][u], 0, 0, 0);
+  };
+  // ask the scheduler to alternate MFMAs with the LDS reads of the next step
+  auto interleave = [&]() {
+#pragma unroll
+    for (int i = 0; i < 6; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // up to 2 LDS reads
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+  };
 
-  if (nk > 0) issue(std::integral_constant<int, 0>{}, 0);
-  if (nk > 1) issue(std::integral_constant<int, 1>{}, 1);
-  if (nk > 2) issue(std::integral_constant<int, 2>{}, 2);
-  for (int kt = 0; kt < nk; kt += NSTAGE) {
-    step(std::integral_constant<int, 0>{}, kt);
-    if (kt + 1 < nk) step(std::integral_constant<int, 1>{}, kt + 1);
-    if (kt + 2 < nk) step(std::integral_constant<int, 2>{}, kt + 2);
-    if (kt + 3 < nk) step(std::integral_constant<int, 3>{}, kt + 3);
+  if (MODE == FWD) {
+    // Stage kt lives in buffer kt % 4. The barrier that publishes stage kt+1
+    // sits between the two 16-deep steps of stage kt, so step 1 of stage kt
+    // overlaps the first fragment reads of stage kt+1; right after that barrier
+    // the buffer of stage kt-1 (read by every wave before it) is refilled with
+    // stage kt+3. Loads run two to three stages ahead of the MFMAs.
+    Frags f0, f1;
+    auto stage = [&](auto stage_tag, int kt) {
+      constexpr int S = decltype(stage_tag)::value;
+      constexpr int S1 = (S + 1) & 3;
+      // step 0 of stage kt (fragments in f0), reading step 1 into f1
+      read_frags(stage_tag, kt, 1, f1);
+      mfmas(f0);
+      interleave();
+      // publish stage kt+1: this wave's loads of it are done (stage kt+2 may
+      // still be in flight), then every wave's
+      if (kt + 1 < nk) {
+        if (kt + 2 < nk) wait_vm<4>();
+        else wait_vm<0>();
+        block_barrier();
+        if (kt + 3 < nk) issue(std::integral_constant<int, (S + 3) & 3>{}, kt + 3);
+        read_frags(std::integral_constant<int, S1>{}, kt + 1, 0, f0);
+      }
+      mfmas(f1);
+      interleave();
+    };
+
+    if (nk > 0) issue(std::integral_constant<int, 0>{}, 0);
+    if (nk > 1) issue(std::integral_constant<int, 1>{}, 1);
+    if (nk > 2) issue(std::integral_constant<int, 2>{}, 2);
+    if (nk > 0) {
+      if (nk > 2) wait_vm<8>();
+      else if (nk > 1) wait_vm<4>();
+      else wait_vm<0>();
+      block_barrier();
+      read_frags(std::integral_constant<int, 0>{}, 0, 0, f0);
+    }
+    for (int kt = 0; kt < nk; kt += NSTAGE) {
+      stage(std::integral_constant<int, 0>{}, kt);
+      if (kt + 1 < nk) stage(std::integral_constant<int, 1>{}, kt + 1);
+      if (kt + 2 < nk) stage(std::integral_constant<int, 2>{}, kt + 2);
+      if (kt + 3 < nk) stage(std::integral_constant<int, 3>{}, kt + 3);
+    }
+  } else {
+    // Transposed-operand modes keep one stage per barrier (their fragment
+    // transposes need the registers a second fragment set would take).
+    auto step = [&](auto stage_tag, int kt) {
+      constexpr int S = decltype(stage_tag)::value;
+      if (kt + 2 < nk) wait_vm<8>();  // this wave's loads of stages kt+1, kt+2 may stay in flight
+      else wait_vm<0>();
+      block_barrier();
+      if (kt + 3 < nk) issue(std::integral_constant<int, (S + 3) & 3>{}, kt + 3);
+#pragma unroll
+      for (int ks = 0; ks < BK / 16; ++ks) {
+        Frags f;
+        read_frags(stage_tag, kt, ks, f);
+        mfmas(f);
+      }
+    };
+    if (nk > 0) issue(std::integral_constant<int, 0>{}, 0);
+    if (nk > 1) issue(std::integral_constant<int, 1>{}, 1);
+    if (nk > 2) issue(std::integral_constant<int, 2>{}, 2);
+    for (int kt = 0; kt < nk; kt += NSTAGE) {
+      step(std::integral_constant<int, 0>{}, kt);
+      if (kt + 1 < nk) step(std::integral_constant<int, 1>{}, kt + 1);
+      if (kt + 2 < nk) step(std::integral_constant<int, 2>{}, kt + 2);
+      if (kt + 3 < nk) step(std::integral_constant<int, 3>{}, kt + 3);
+    }
   }
 
   // accumulator (s, u, v) of this lane: i = i0 + wi*128 + s*32 + 8*(v/4) + 4*(lane/32) + v%4,

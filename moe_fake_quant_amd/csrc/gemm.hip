@@ -11,11 +11,13 @@
 //   WGRAD  X rows: i = k                 dY rows: j = n                routed rows r
 //
 // Operands stream from global memory straight into LDS (global_load_lds,
-// 16 bytes per lane, no staging registers) through a ring of 4 stages of 32
-// contraction elements, three stages ahead of the MFMAs; one barrier per
-// stage. A contraction-contiguous operand is stored as 256 rows x 64 B and
-// read with ds_read_b128; a transposed operand (contraction is its row) keeps
-// its natural layout, 32 rows x 512 B, and the MFMA fragments are gathered
+// 16 bytes per lane, no staging registers) through two stages of 64
+// contraction elements, one stage ahead of the MFMAs; one barrier per stage.
+// (Measured against four 32-deep stages: full 128-byte row segments per load
+// and half the barriers gain more than the deeper lookahead.) A
+// contraction-contiguous operand is stored as 256 rows x 128 B and read with
+// ds_read_b128; a transposed operand (contraction is its row) keeps its
+// natural layout, 64 rows x 512 B, and the MFMA fragments are gathered
 // with ds_read_tr16_b64 (a 4 x 16 -> 16 x 4 transpose inside each 16-lane
 // group). Both layouts XOR-swizzle 16-byte chunks so the fragment reads are
 // bank-conflict free.
@@ -47,11 +49,11 @@ typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 
 constexpr int BI = 256;   // tile rows (i)
 constexpr int BJ = 256;   // tile cols (j)
-constexpr int BK = 32;    // contraction elements per stage
-constexpr int NSTAGE = 4;
+constexpr int BK = 64;    // contraction elements per stage
+constexpr int NSTAGE = 2;
 constexpr int NT = 512;   // threads per block (8 waves, 2 per SIMD)
 constexpr int WJ_TILE = 64;  // j extent of one wave (waves: 2 along i x 4 along j)
-constexpr int kStageBytes = 256 * BK * 2;  // one operand, one stage: 16 KiB
+constexpr int kStageBytes = 256 * BK * 2;  // one operand, one stage: 32 KiB
 
 enum Mode { FWD = 0, DGRAD = 1, WGRAD = 2 };
 
@@ -59,31 +61,29 @@ enum Mode { FWD = 0, DGRAD = 1, WGRAD = 2 };
 // can tell a stage being read from the stages being filled.
 __shared__ __attribute__((aligned(1024))) char g_p0[kStageBytes];
 __shared__ __attribute__((aligned(1024))) char g_p1[kStageBytes];
-__shared__ __attribute__((aligned(1024))) char g_p2[kStageBytes];
-__shared__ __attribute__((aligned(1024))) char g_p3[kStageBytes];
+
 __shared__ __attribute__((aligned(1024))) char g_q0[kStageBytes];
 __shared__ __attribute__((aligned(1024))) char g_q1[kStageBytes];
-__shared__ __attribute__((aligned(1024))) char g_q2[kStageBytes];
-__shared__ __attribute__((aligned(1024))) char g_q3[kStageBytes];
+
 
 template <int S>
 __device__ __forceinline__ char *stage_p() {
-  return S == 0 ? g_p0 : S == 1 ? g_p1 : S == 2 ? g_p2 : g_p3;
+  return S == 0 ? g_p0 : g_p1;
 }
 template <int S>
 __device__ __forceinline__ char *stage_q() {
-  return S == 0 ? g_q0 : S == 1 ? g_q1 : S == 2 ? g_q2 : g_q3;
+  return S == 0 ? g_q0 : g_q1;
 }
 
-// Contraction-contiguous layout: row idx (0..255) of 4 16-byte chunks (8
+// Contraction-contiguous layout: row idx (0..255) of 8 16-byte chunks (8
 // contraction elements each); chunk kc sits at kc ^ sw(idx). The swizzle
-// (rows in fours share one) was chosen by measuring the LDS bank-conflict
+// (rows in pairs share one) was chosen by measuring the LDS bank-conflict
 // counter for the fragment read pattern (32 consecutive rows, one chunk).
-__device__ __forceinline__ uint32_t nrm_sw(uint32_t idx) { return (idx >> 2) & 3u; }
+__device__ __forceinline__ uint32_t nrm_sw(uint32_t idx) { return (idx >> 1) & 7u; }
 __device__ __forceinline__ uint32_t nrm_off(uint32_t idx, uint32_t kc) {
-  return idx * 64u + ((kc ^ nrm_sw(idx)) << 4);
+  return idx * 128u + ((kc ^ nrm_sw(idx)) << 4);
 }
-// Transposed layout: contraction row c (0..31) of 32 16-byte chunks (8 columns
+// Transposed layout: contraction row c (0..63) of 32 16-byte chunks (8 columns
 // each); column chunk q sits at q ^ tr_sw(c). Within the four rows a
 // ds_read_tr16_b64 group touches, the swizzle spreads their chunks over
 // distinct banks.
@@ -279,15 +279,15 @@ __device__ __forceinline__ void wgrad_epilogue(const GemmArgs &a, const f32x16 (
 }
 
 // Per-lane global byte offsets of the operand rows this lane streams, fixed
-// for a tile. A wave issues 2 DMA instructions per operand per stage, each
+// for a tile. A wave issues 4 DMA instructions per operand per stage, each
 // filling 1 KiB of LDS (lane l -> byte 16 l of it).
-struct NormalDMA {  // contraction-contiguous: instr covers 16 rows x 64 B
-  uint32_t off[2];
+struct NormalDMA {  // contraction-contiguous: instr covers 8 rows x 128 B
+  uint32_t off[4];
   __device__ __forceinline__ void init(size_t ld, int row0, int row_last, int wave, int lane) {
 #pragma unroll
-    for (int ii = 0; ii < 2; ++ii) {
-      const uint32_t idx = 16 * (2 * wave + ii) + (lane >> 2);
-      const uint32_t kc = (lane & 3) ^ nrm_sw(idx);
+    for (int ii = 0; ii < 4; ++ii) {
+      const uint32_t idx = 8 * (4 * wave + ii) + (lane >> 3);
+      const uint32_t kc = (lane & 7) ^ nrm_sw(idx);
       const int r = min(row0 + (int)idx, row_last);
       off[ii] = (uint32_t)(((size_t)r * ld + kc * 8) * 2);
     }
@@ -295,16 +295,16 @@ struct NormalDMA {  // contraction-contiguous: instr covers 16 rows x 64 B
   template <int S>
   __device__ __forceinline__ void issue(const char *base, char *stage, int c0, int wave) const {
 #pragma unroll
-    for (int ii = 0; ii < 2; ++ii) dma16(base + off[ii] + c0 * 2, stage + (2 * wave + ii) * 1024);
+    for (int ii = 0; ii < 4; ++ii) dma16(base + off[ii] + c0 * 2, stage + (4 * wave + ii) * 1024);
   }
 };
 struct TransDMA {  // transposed: instr covers 2 contraction rows x 512 B
-  uint32_t col_off[2];
-  int crow[2];
+  uint32_t col_off[4];
+  int crow[4];
   __device__ __forceinline__ void init(int idx0, int wave, int lane) {
 #pragma unroll
-    for (int ii = 0; ii < 2; ++ii) {
-      crow[ii] = 2 * (2 * wave + ii) + (lane >> 5);
+    for (int ii = 0; ii < 4; ++ii) {
+      crow[ii] = 2 * (4 * wave + ii) + (lane >> 5);
       const uint32_t q = (lane & 31) ^ tr_sw(crow[ii]);
       col_off[ii] = (uint32_t)((idx0 + 8 * q) * 2);
     }
@@ -313,10 +313,10 @@ struct TransDMA {  // transposed: instr covers 2 contraction rows x 512 B
   __device__ __forceinline__ void issue(const char *base, uint32_t ld, char *stage, int c0,
                                         int c_end, int wave) const {
 #pragma unroll
-    for (int ii = 0; ii < 2; ++ii) {
+    for (int ii = 0; ii < 4; ++ii) {
       const int c = c0 + crow[ii];
       const int cc = c < c_end ? c : c0;
-      dma16(base + (size_t)cc * ld * 2 + col_off[ii], stage + (2 * wave + ii) * 1024);
+      dma16(base + (size_t)cc * ld * 2 + col_off[ii], stage + (4 * wave + ii) * 1024);
     }
   }
 };
@@ -451,84 +451,26 @@ __device__ __forceinline__ void run_tile(const GemmArgs &a, int e, int i0, int j
       for (int u = 0; u < 2; ++u)
         acc[s][u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.p[s], f.q[u], acc[s][u], 0, 0, 0);
   };
-  // ask the scheduler to alternate MFMAs with the LDS reads of the next step
-  auto interleave = [&]() {
+  // Two-stage ring: stage kt lives in buffer kt % 2. After this wave's loads
+  // of stage kt have landed, one barrier both publishes stage kt to every wave
+  // and retires the reads of stage kt-1, whose buffer then takes stage kt+1
+  // while stage kt is multiplied.
+  auto step = [&](auto stage_tag, int kt) {
+    constexpr int S = decltype(stage_tag)::value;
+    wait_vm<0>();
+    block_barrier();
+    if (kt + 1 < nk) issue(std::integral_constant<int, S ^ 1>{}, kt + 1);
 #pragma unroll
-    for (int i = 0; i < 6; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // up to 2 LDS reads
+    for (int ks = 0; ks < BK / 16; ++ks) {
+      Frags f;
+      read_frags(stage_tag, kt, ks, f);
+      mfmas(f);
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
   };
-
-  if (MODE == FWD) {
-    // Stage kt lives in buffer kt % 4. The barrier that publishes stage kt+1
-    // sits between the two 16-deep steps of stage kt, so step 1 of stage kt
-    // overlaps the first fragment reads of stage kt+1; right after that barrier
-    // the buffer of stage kt-1 (read by every wave before it) is refilled with
-    // stage kt+3. Loads run two to three stages ahead of the MFMAs.
-    Frags f0, f1;
-    auto stage = [&](auto stage_tag, int kt) {
-      constexpr int S = decltype(stage_tag)::value;
-      constexpr int S1 = (S + 1) & 3;
-      // step 0 of stage kt (fragments in f0), reading step 1 into f1
-      read_frags(stage_tag, kt, 1, f1);
-      mfmas(f0);
-      interleave();
-      // publish stage kt+1: this wave's loads of it are done (stage kt+2 may
-      // still be in flight), then every wave's
-      if (kt + 1 < nk) {
-        if (kt + 2 < nk) wait_vm<4>();
-        else wait_vm<0>();
-        block_barrier();
-        if (kt + 3 < nk) issue(std::integral_constant<int, (S + 3) & 3>{}, kt + 3);
-        read_frags(std::integral_constant<int, S1>{}, kt + 1, 0, f0);
-      }
-      mfmas(f1);
-      interleave();
-    };
-
-    if (nk > 0) issue(std::integral_constant<int, 0>{}, 0);
-    if (nk > 1) issue(std::integral_constant<int, 1>{}, 1);
-    if (nk > 2) issue(std::integral_constant<int, 2>{}, 2);
-    if (nk > 0) {
-      if (nk > 2) wait_vm<8>();
-      else if (nk > 1) wait_vm<4>();
-      else wait_vm<0>();
-      block_barrier();
-      read_frags(std::integral_constant<int, 0>{}, 0, 0, f0);
-    }
-    for (int kt = 0; kt < nk; kt += NSTAGE) {
-      stage(std::integral_constant<int, 0>{}, kt);
-      if (kt + 1 < nk) stage(std::integral_constant<int, 1>{}, kt + 1);
-      if (kt + 2 < nk) stage(std::integral_constant<int, 2>{}, kt + 2);
-      if (kt + 3 < nk) stage(std::integral_constant<int, 3>{}, kt + 3);
-    }
-  } else {
-    // Transposed-operand modes keep one stage per barrier (their fragment
-    // transposes need the registers a second fragment set would take).
-    auto step = [&](auto stage_tag, int kt) {
-      constexpr int S = decltype(stage_tag)::value;
-      if (kt + 2 < nk) wait_vm<8>();  // this wave's loads of stages kt+1, kt+2 may stay in flight
-      else wait_vm<0>();
-      block_barrier();
-      if (kt + 3 < nk) issue(std::integral_constant<int, (S + 3) & 3>{}, kt + 3);
-#pragma unroll
-      for (int ks = 0; ks < BK / 16; ++ks) {
-        Frags f;
-        read_frags(stage_tag, kt, ks, f);
-        mfmas(f);
-      }
-    };
-    if (nk > 0) issue(std::integral_constant<int, 0>{}, 0);
-    if (nk > 1) issue(std::integral_constant<int, 1>{}, 1);
-    if (nk > 2) issue(std::integral_constant<int, 2>{}, 2);
-    for (int kt = 0; kt < nk; kt += NSTAGE) {
-      step(std::integral_constant<int, 0>{}, kt);
-      if (kt + 1 < nk) step(std::integral_constant<int, 1>{}, kt + 1);
-      if (kt + 2 < nk) step(std::integral_constant<int, 2>{}, kt + 2);
-      if (kt + 3 < nk) step(std::integral_constant<int, 3>{}, kt + 3);
-    }
+  if (nk > 0) issue(std::integral_constant<int, 0>{}, 0);
+  for (int kt = 0; kt < nk; kt += NSTAGE) {
+    step(std::integral_constant<int, 0>{}, kt);
+    if (kt + 1 < nk) step(std::integral_constant<int, 1>{}, kt + 1);
   }
 
   // accumulator (s, u, v) of this lane: i = i0 + wi*128 + s*32 + 8*(v/4) + 4*(lane/32) + v%4,

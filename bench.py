@@ -31,16 +31,41 @@ MI355X_BF16_PEAK_TFLOPS = 2500.0     # dense bf16 MFMA
 MI355X_HBM_PEAK_GBS = 8000.0
 FLOPS_PER_ROW = 6 * (2 * 768 * 2048 + 2048 * 768)   # 28,311,552 per routed row (fwd+bwd GEMMs)
 
-# Copy-kernel calibration of the FETCH_SIZE / WRITE_SIZE counters and the
-# counters of the dominant kernel, from the committed profile summaries.
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_nvfp4_moe_c4.json")
+# HBM bytes per GEMM launch from rocprofv3 FETCH_SIZE / WRITE_SIZE runs,
+# scaled by a plain copy kernel's readings, recorded with a hash of the GEMM
+# sources they were taken on; a kernel changed since then reports null.
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_gemm_{workload}.json")
+GEMM_SOURCES = ("gemm.hip", "codec.hpp", "common.hpp", "internal.hpp")
+
+
+def gemm_source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for name in GEMM_SOURCES:
+        with open(os.path.join(ROOT, "moe_fake_quant_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def hbm_pass_bytes(T, H, Fh, R, topk):
+    """Algorithmic HBM bytes of each elementwise call: every operand read
+    once, every output written once (bf16 2 B, fp32 / int32 4 B)."""
+    return {
+        "fq_moe_permute": 12 * T * topk,
+        "fq_moe_gather_actfq": 2 * T * H + 2 * R * H + 4 * R,
+        "fq_swiglu_actfq": R * (4 * Fh + 2 * Fh),
+        "fq_moe_combine": 2 * R * H + 8 * T * topk + 2 * T * H,
+        "fq_moe_combine_bwd": 2 * T * H + 8 * R + 2 * R * H,
+        "fq_swiglu_bwd": R * (2 * Fh + 4 * Fh + 4 * Fh),
+        "fq_moe_unpermute_reduce": 2 * R * H + 4 * T * topk + 2 * T * H + 2 * T * H,
+    }
 
 
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=4, choices=[3, 4, 5])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-experts", type=int, default=6)
@@ -173,11 +198,21 @@ def main():
     fq_gbs = fq_bytes / (fq_ms * 1e-3) / 1e9
 
     traffic = None
-    if os.path.exists(TRAFFIC_FILE):
-        with open(TRAFFIC_FILE) as f:
+    tfile = TRAFFIC_FILE.format(workload=W.CONFIG_NAMES[args.config])
+    if os.path.exists(tfile):
+        with open(tfile) as f:
             tr = json.load(f)
-        if tr.get("kernel") == dom:
-            traffic = tr.get("bytes_per_launch")
+        if tr.get("gemm_sources_sha256") == gemm_source_hash() and dom in tr.get("kernels", {}):
+            traffic = tr["kernels"][dom]["hbm_bytes_per_launch"]
+
+    passes = {}
+    for name, nbytes in hbm_pass_bytes(case.T, H, Fh, R, case.topk).items():
+        ms = sum(per.get(name, [0.0])) / args.steps
+        if ms > 0:
+            passes[name] = {"bytes": nbytes, "ms": round(ms, 4),
+                            "GB/s": round(nbytes / (ms * 1e-3) / 1e9, 1),
+                            "pct_hbm_peak": round(100 * nbytes / (ms * 1e-3) / 1e9 / MI355X_HBM_PEAK_GBS, 1)}
+    gemm_ms = sum(kernels[k]["ms_per_step"] for k in kernels)
 
     breakdown = {n: round(sum(v) / args.steps, 4) for n, v in sorted(per.items())}
 
@@ -227,6 +262,9 @@ def main():
             "traffic": traffic,
         },
         "gemm_kernels": kernels,
+        "gemm_only": {"ms_per_step": round(gemm_ms, 4),
+                      "TFLOP/s": round(flops_step / (gemm_ms * 1e-3) / 1e12, 2)},
+        "hbm_passes": passes,
         "ms_per_step_by_call": breakdown,
         "cpu_baseline": cpu,
         "input_gen_s": round(t_gen, 1),
@@ -248,7 +286,12 @@ def cpu_baseline(case, fmt, group, n_experts):
     g = 16 if group else None
     perm, row_of, seg = O.moe_permute(case.expert_ids, 0, E)
     R = int(seg[-1])
-    cores = len(os.sched_getaffinity(0))
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p["num_threads"] for p in threadpool_info() if p.get("user_api") == "blas"]
+                    or [1])
+    except Exception:
+        cores = 1
     t0 = time.perf_counter()
     if g:
         O.moe_layer(sub, wfmt, g, wfmt)

@@ -20,11 +20,31 @@ Sources (cited by page title and section):
     learnable flags weight_scale true / act_scale false (example yaml).
   * msmodelslim multi-card quantisation page: observers keep per-channel
     min / max and turn them into quantisation parameters (FA3 observer section).
-  * Format grids: OCP Microscaling Formats spec v1.0 (E4M3, E2M1) -- the
-    definitions the spec formats name; the pages give no bit layouts.
+  * Format grids: OCP Microscaling Formats spec v1.0 (E4M3, E2M1), the
+    standard definitions of the formats the pages name; the pages give no bit
+    layouts.
 
-Every point the pages leave open is a numbered reading (R-1 ... R-18) listed in
-the design doc; the code names the reading where it applies.
+Every point the pages leave open is a numbered reading; the code names the
+reading where it applies:
+  R-1  z = x * r with r = 1/s rounded once per scale (not x / s per element)
+  R-2  integer formats dequantize to +0.0; FP formats keep the sign of z
+  R-3  int8 symmetric range [-128, 127]
+  R-4  an all-zero row / group / tensor gets scale 1
+  R-5  int4 asymmetric: min / max widened to include 0, integer zero point
+  R-6  E4M3 saturates at +-448, subnormals kept
+  R-7  E2M1 ties go to the even code
+  R-8  NVFP4: learnable fp32 theta re-rounded to E4M3 each forward; tensor
+       scale g per expert per stack; one activation g_a per projection input
+  R-9  a zero NVFP4 block scale makes the block +0.0 with mask and grad 0
+  R-10 gate is the first F rows of the fused gate_up stack
+  R-11 routing: softmax, top-k (ties to the lower id), renormalised
+  R-12 no gradient into the router (logits are given data)
+  R-13 STE mask lo <= z <= hi on the unrounded z, inclusive
+  R-14 no LSQ gradient-scale factor
+  R-15 dScale compared normwise (max |diff| / max |ref|)
+  R-16 chained tests feed the GPU-calibrated activation scales to the oracle
+  R-17 MoE weights drawn N(0, 0.02)
+  R-18 the skewed local-share workload forces experts {3, 7, 11, 15} empty
 
 Parity status: every function here is pinned by the ``-m "not gpu"`` tests
 (exhaustive code grids, tie tables, library special cases, closed forms,

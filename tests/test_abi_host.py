@@ -1,0 +1,208 @@
+"""Host-side tests of the C ABI (no GPU needed).
+
+- libfq.so loads and exports, under its plain C name, every function that
+  include/fq.h declares, and the Python binding exposes the same names;
+- the pure host queries (version, workspace sizes) answer as documented;
+- argument checks reject bad calls with the documented status before any
+  launch. These use placeholder pointers and therefore run only where no GPU
+  is visible; the GPU suite repeats the error cases with real tensors.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fq.h")
+LIB_PATH = os.path.join(ROOT, "moe_fake_quant_amd", "libfq.so")
+
+
+def _declared():
+    """Names of the functions fq.h declares (prototypes start at column 0)."""
+    names = []
+    with open(HEADER) as f:
+        for line in f:
+            m = re.match(r"^(?!typedef|#|\s)[A-Za-z_][\w\s\*]*?\b([a-z_][a-z0-9_]*)\s*\(", line)
+            if m:
+                names.append(m.group(1))
+    return names
+
+
+@pytest.fixture(scope="module")
+def pkg():
+    if not os.path.exists(LIB_PATH):
+        from moe_fake_quant_amd.build import build
+        build()
+    import moe_fake_quant_amd as F
+    return F
+
+
+def _no_gpu_visible():
+    try:
+        import torch
+        return torch.cuda.device_count() == 0
+    except Exception:
+        return True
+
+
+host_only = pytest.mark.skipif(not _no_gpu_visible(),
+                               reason="placeholder pointers: host-check cases run where no GPU is "
+                                      "visible; the GPU suite covers them with device tensors")
+
+
+def test_header_declares_the_boundary():
+    names = _declared()
+    for required in ("fq_quantize_stacked", "fq_grouped_gemm_fwd", "fq_grouped_gemm_bwd_scale",
+                     "observer_absmax_init", "fq_moe_permute", "fq_workspace_bytes",
+                     "fq_last_error", "fq_abi_version"):
+        assert required in names
+    assert len(names) == len(set(names))
+
+
+def test_library_exports_every_declared_symbol(pkg):
+    lib = ctypes.CDLL(LIB_PATH)
+    for name in _declared():
+        assert hasattr(lib, name), f"libfq.so does not export {name}"
+    # exported as unmangled dynamic symbols
+    out = subprocess.run(["nm", "-D", "--defined-only", LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    dyn = {ln.split()[-1] for ln in out.splitlines() if ln.strip()}
+    missing = [n for n in _declared() if n not in dyn]
+    assert not missing, missing
+
+
+def test_binding_matches_header(pkg):
+    assert set(pkg.EXPORTED) == set(_declared())
+    for name in pkg.EXPORTED:
+        if name in ("fq_last_error", "fq_abi_version"):
+            continue
+        assert callable(getattr(pkg, name)), name
+
+
+def test_version_and_error_string(pkg):
+    lib = pkg.lib()
+    assert lib.fq_abi_version() == 1
+    assert isinstance(lib.fq_last_error(), bytes)
+
+
+def _ws(pkg, op, shape, R, wfmt=0, afmt=0):
+    return pkg.lib().fq_workspace_bytes(op, pkg.fq_shape(*shape), R, wfmt | (afmt << 8))
+
+
+def _up(x):
+    return (x + 255) // 256 * 256
+
+
+def test_workspace_sizes(pkg):
+    E, N, K, R = 8, 512, 256, 1000
+    # forward: prequantized weights and no activation FQ need nothing
+    assert _ws(pkg, pkg.FQ_OP_GEMM_FWD, (E, N, K), R) == 0
+    # weight FQ inside the call: one bf16 W_fq stack; act FQ: one bf16 [R, K]
+    assert _ws(pkg, pkg.FQ_OP_GEMM_FWD, (E, N, K), R, pkg.FMT_NVFP4) == _up(E * N * K * 2)
+    assert _ws(pkg, pkg.FQ_OP_GEMM_FWD, (E, N, K), R, pkg.FMT_NVFP4, pkg.FMT_FP8_E4M3) == \
+        _up(E * N * K * 2) + _up(R * K * 2)
+    # backward adds two fp32 partial buffers per 128-chunk of K
+    part = _up(E * N * (K // 128 + 1) * 4)
+    assert _ws(pkg, pkg.FQ_OP_GEMM_BWD, (E, N, K), R) == 2 * part
+    # permute: grows with the pair count, positive for any expert count
+    a = _ws(pkg, pkg.FQ_OP_PERMUTE, (4, 0, 0), 1000)
+    b = _ws(pkg, pkg.FQ_OP_PERMUTE, (4, 0, 0), 100000)
+    assert 0 < a <= b
+    assert _ws(pkg, 99, (E, N, K), R) == 0
+
+
+# ----------------------------------------------------------------- checks --
+FAKE = 0x100000  # 16-byte aligned placeholder, never dereferenced: every case fails a check
+
+
+def _status(pkg, fn, *args):
+    return getattr(pkg.lib(), fn)(*args)
+
+
+def _wq(pkg, fmt, group, scale=FAKE, zp=None, g=None):
+    return ctypes.byref(pkg.fq_weight_q(fmt, group, scale, zp, g))
+
+
+@host_only
+def test_quantize_stacked_rejects_bad_arguments(pkg):
+    S = pkg.fq_shape
+    bad = [
+        (S(0, 16, 16), _wq(pkg, pkg.FMT_INT8, 16), pkg.FQ_ERR_INVALID_ARGUMENT),   # empty shape
+        (S(1, 16, 32), _wq(pkg, pkg.FMT_NVFP4, 32, g=FAKE), pkg.FQ_ERR_INVALID_ARGUMENT),  # nvfp4 group
+        (S(1, 16, 32), _wq(pkg, pkg.FMT_NVFP4, 16), pkg.FQ_ERR_INVALID_ARGUMENT),  # no global scale
+        (S(1, 16, 256), _wq(pkg, pkg.FMT_INT4, 128), pkg.FQ_ERR_INVALID_ARGUMENT),  # no zero point
+        (S(1, 16, 48), _wq(pkg, pkg.FMT_INT8, 32), pkg.FQ_ERR_INVALID_ARGUMENT),   # group !| K
+        (S(1, 16, 32), _wq(pkg, 7, 32), pkg.FQ_ERR_INVALID_ARGUMENT),             # unknown format
+    ]
+    for shape, q, want in bad:
+        assert _status(pkg, "fq_quantize_stacked", FAKE, shape, q, FAKE, None, None) == want
+        assert pkg.lib().fq_last_error()
+    # neither output requested
+    assert _status(pkg, "fq_quantize_stacked", FAKE, S(1, 16, 32), _wq(pkg, pkg.FMT_INT8, 32),
+                   None, None, None) == pkg.FQ_ERR_INVALID_ARGUMENT
+    # misaligned input
+    assert _status(pkg, "fq_quantize_stacked", FAKE + 2, S(1, 16, 32), _wq(pkg, pkg.FMT_INT8, 32),
+                   FAKE, None, None) == pkg.FQ_ERR_INVALID_ARGUMENT
+
+
+@host_only
+def test_grouped_gemm_rejects_unsupported_shapes(pkg):
+    S = pkg.fq_shape
+    q = _wq(pkg, pkg.FMT_FP8_E4M3, 256)
+    # forward tiles need N % 256 and K % 64
+    st = _status(pkg, "fq_grouped_gemm_fwd", FAKE, 64, FAKE, S(2, 128, 256), None, FAKE, q, None,
+                 FAKE, None, 0, None)
+    assert st == pkg.FQ_ERR_UNSUPPORTED
+    assert b"256" in pkg.lib().fq_last_error()
+    # more experts than the tile scheduler holds
+    st = _status(pkg, "fq_grouped_gemm_fwd", FAKE, 64, FAKE, S(1025, 256, 256), None, FAKE, q,
+                 None, FAKE, None, 0, None)
+    assert st == pkg.FQ_ERR_UNSUPPORTED
+    # backward needs K % 256; dScale group must be reducible by the epilogue
+    st = _status(pkg, "fq_grouped_gemm_bwd_scale", FAKE, FAKE, 64, FAKE, S(2, 256, 192), FAKE,
+                 FAKE, _wq(pkg, pkg.FMT_FP8_E4M3, 192), None, FAKE, None, None, FAKE, 1 << 30, None)
+    assert st == pkg.FQ_ERR_UNSUPPORTED
+    st = _status(pkg, "fq_grouped_gemm_bwd_scale", FAKE, FAKE, 64, FAKE, S(2, 256, 768), FAKE,
+                 FAKE, _wq(pkg, pkg.FMT_INT8, 48), None, None, FAKE, None, FAKE, 1 << 30, None)
+    assert st == pkg.FQ_ERR_UNSUPPORTED
+    # dzero_point exists only for int4, and needs dscale
+    st = _status(pkg, "fq_grouped_gemm_bwd_scale", FAKE, FAKE, 64, FAKE, S(2, 256, 256), FAKE,
+                 FAKE, _wq(pkg, pkg.FMT_INT8, 256), None, None, None, FAKE, FAKE, 1 << 30, None)
+    assert st == pkg.FQ_ERR_INVALID_ARGUMENT
+    # workspace too small for weight FQ inside the call
+    st = _status(pkg, "fq_grouped_gemm_fwd", FAKE, 64, FAKE, S(2, 256, 256), FAKE, None, q, None,
+                 FAKE, FAKE, 16, None)
+    assert st == pkg.FQ_ERR_WORKSPACE_TOO_SMALL
+    # activation FQ format without a scale
+    aq = ctypes.byref(pkg.fq_act_q(pkg.FMT_NVFP4, None))
+    st = _status(pkg, "fq_grouped_gemm_fwd", FAKE, 64, FAKE, S(2, 256, 256), None, FAKE, q, aq,
+                 FAKE, FAKE, 1 << 30, None)
+    assert st == pkg.FQ_ERR_INVALID_ARGUMENT
+
+
+@host_only
+def test_permute_and_elementwise_reject_bad_arguments(pkg):
+    L = pkg.lib()
+    assert L.fq_moe_permute(FAKE, 16, 0, 0, 4, FAKE, FAKE, FAKE, FAKE, 1 << 20, None) == \
+        pkg.FQ_ERR_INVALID_ARGUMENT                                   # topk 0
+    assert L.fq_moe_permute(FAKE, 16, 8, 0, 4, FAKE, FAKE, None, FAKE, 1 << 20, None) == \
+        pkg.FQ_ERR_INVALID_ARGUMENT                                   # no seg_offsets
+    assert L.fq_moe_permute(FAKE, 16, 8, 0, 4, FAKE, FAKE, FAKE, FAKE, 8, None) == \
+        pkg.FQ_ERR_WORKSPACE_TOO_SMALL
+    assert L.fq_moe_gather_actfq(FAKE, 16, 40, FAKE, 8, 128, FAKE, None, FAKE, None) == \
+        pkg.FQ_ERR_INVALID_ARGUMENT                                   # H % 16
+    assert L.fq_swiglu_actfq(FAKE, 128, None, 64, None, None, FAKE, None) == \
+        pkg.FQ_ERR_INVALID_ARGUMENT                                   # no n_rows
+    assert L.fq_swiglu_bwd(FAKE, FAKE, 128, FAKE, 24, None, FAKE, None) == \
+        pkg.FQ_ERR_INVALID_ARGUMENT                                   # F % 16
+    assert L.fq_moe_combine(FAKE, FAKE, FAKE, 16, 8, 64, FAKE + 8, None) == \
+        pkg.FQ_ERR_INVALID_ARGUMENT                                   # misaligned out
+    assert L.fq_moe_combine_bwd(FAKE, FAKE, FAKE, 0, 64, 128, FAKE, FAKE, None) == \
+        pkg.FQ_ERR_INVALID_ARGUMENT                                   # topk 0
+    aq = ctypes.byref(pkg.fq_act_q(pkg.FMT_FP8_E4M3, FAKE))
+    assert L.fq_moe_unpermute_reduce(FAKE, FAKE, None, 16, 8, 64, aq, FAKE, None) == \
+        pkg.FQ_ERR_INVALID_ARGUMENT                                   # act mask needs x
+    assert L.observer_absmax_init(FAKE, pkg.fq_shape(1, 4, 12), pkg.FMT_INT8, 12, 0, FAKE, None,
+                                  None, None, 0, None) == pkg.FQ_ERR_INVALID_ARGUMENT  # K % 8

@@ -225,6 +225,7 @@ fq_status fq_grouped_gemm_bwd_scale(const uint16_t *dy_bf16, const uint16_t *x_b
  *
  * fq_moe_gather_actfq: xq[r] = FQ_a(x[perm[r] / topk])   (forward pre-hook
  *   on the expert input, mcore_qad article section 二.3). x [T, H].
+ *   T == 0 gathers nothing and launches nothing (x may then be NULL).
  * fq_swiglu_actfq: a = bf16(silu(h[:, :F]) * h[:, F:]), aq = FQ_a(a).
  *   h [R_max, 2F]; a_out may be NULL; aq_out [R_max, F]. The gate half is
  *   the first F columns. silu(g) = g / (1 + exp(-g)) in fp32.

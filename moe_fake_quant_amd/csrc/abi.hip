@@ -293,9 +293,10 @@ fq_status fq_moe_gather_actfq(const uint16_t *x, int32_t T, int32_t H, const int
                               uint16_t *xq, fq_stream stream) {
   FQ_CHECK_ARG(T >= 0 && H > 0 && topk > 0 && R_max >= 0, "bad sizes");
   FQ_CHECK_ARG(H % 16 == 0, "H must be a multiple of 16");
-  FQ_CHECK_ARG(n_rows && (R_max == 0 || (x && perm && xq)), "NULL pointer");
+  FQ_CHECK_ARG(n_rows && (R_max == 0 || T == 0 || (x && perm && xq)), "NULL pointer");
   FQ_CHECK_ARG((!x || aligned16(x)) && (!xq || aligned16(xq)), "bf16 tensors must be 16-byte aligned");
   FQ_TRY(check_act_q(aq, H));
+  if (T == 0) return FQ_OK;  // no tokens: no routed row exists, nothing to gather
   launch_gather_actfq(x, H, perm, topk, R_max, n_rows, act_fmt(aq), aq ? aq->scale : nullptr, xq,
                       S(stream));
   FQ_CHECK_LAUNCH("fq_moe_gather_actfq");

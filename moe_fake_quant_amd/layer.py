@@ -145,8 +145,9 @@ class MoEFakeQuantLayer:
 
     def backward(self, x: torch.Tensor, probs: torch.Tensor, dout: torch.Tensor):
         T = x.shape[0]
-        fq_moe_combine_bwd(dout, probs, self.perm, self.topk, self.H, self.R_max, self.n_rows,
-                           self.do)
+        if T > 0:  # an empty batch has no routed rows to scatter into
+            fq_moe_combine_bwd(dout, probs, self.perm, self.topk, self.H, self.R_max,
+                               self.n_rows, self.do)
         # dgrad and wgrad -> dScale as two calls (one GEMM kernel each)
         fq_grouped_gemm_bwd_scale(self.do, self.aq, self.R_max, self.seg, self.shape_d, self.w_d,
                                   self.wfq_d, self.q_d, None, self.daq, None, None, self.ws)

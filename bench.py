@@ -52,10 +52,10 @@ def hbm_pass_bytes(T, H, Fh, R, topk):
     once, every output written once (bf16 2 B, fp32 / int32 4 B)."""
     return {
         "fq_moe_permute": 12 * T * topk,
-        "fq_moe_gather_actfq": 2 * T * H + 2 * R * H + 4 * R,
+        "fq_moe_gather_actfq": 2 * T * H + 2 * R * H + 4 * T * topk,
         "fq_swiglu_actfq": R * (4 * Fh + 2 * Fh),
         "fq_moe_combine": 2 * R * H + 8 * T * topk + 2 * T * H,
-        "fq_moe_combine_bwd": 2 * T * H + 8 * R + 2 * R * H,
+        "fq_moe_combine_bwd": 2 * T * H + 8 * T * topk + 2 * R * H,
         "fq_swiglu_bwd": R * (2 * Fh + 4 * Fh + 4 * Fh),
         "fq_moe_unpermute_reduce": 2 * R * H + 4 * T * topk + 2 * T * H + 2 * T * H,
     }

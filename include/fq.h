@@ -223,9 +223,10 @@ fq_status fq_grouped_gemm_bwd_scale(const uint16_t *dy_bf16, const uint16_t *x_b
  * combine, and its backward). R = seg_offsets[E] is read on the device
  * through `n_rows` (= &seg_offsets[E]); rows >= R are not touched.
  *
- * fq_moe_gather_actfq: xq[r] = FQ_a(x[perm[r] / topk])   (forward pre-hook
- *   on the expert input, mcore_qad article section 二.3). x [T, H].
- *   T == 0 gathers nothing and launches nothing (x may then be NULL).
+ * fq_moe_gather_actfq: xq[row_of[t,j]] = FQ_a(x[t]) for every routed slot
+ *   (row_of[t,j] >= 0; forward pre-hook on the expert input, mcore_qad
+ *   article section 二.3). x [T, H]; row_of [T, topk] from fq_moe_permute;
+ *   xq [R, H]. Each token row is read and fake-quantized once.
  * fq_swiglu_actfq: a = bf16(silu(h[:, :F]) * h[:, F:]), aq = FQ_a(a).
  *   h [R_max, 2F]; a_out may be NULL; aq_out [R_max, F]. The gate half is
  *   the first F columns. silu(g) = g / (1 + exp(-g)) in fp32.
@@ -233,13 +234,15 @@ fq_status fq_grouped_gemm_bwd_scale(const uint16_t *dy_bf16, const uint16_t *x_b
  *   from h), dh = [da*u*s*(1+g*(1-s)), da*g*s] with s = sigmoid(g).
  * fq_moe_combine: out[t] = bf16(sum_j p[t,j] * o[row_of[t,j]]) over local
  *   slots j ascending (fp32); tokens without local slots get 0.
- * fq_moe_combine_bwd: do[r] = bf16(p[t,j] * dout[t]), f = perm[r] = t*topk+j.
+ * fq_moe_combine_bwd: do[row_of[t,j]] = bf16(p[t,j] * dout[t]) for every
+ *   routed slot; each dout row is read once.
  * fq_moe_unpermute_reduce: dx[t] = bf16(m_a(x[t]) * sum_j dxq[row_of[t,j]]).
- * All require H (resp. F) % 16 == 0.
+ * All require H (resp. F) % 16 == 0 and T * H < 2^36. T == 0 launches
+ * nothing (the token pointers may then be NULL).
  * ---------------------------------------------------------------------- */
-fq_status fq_moe_gather_actfq(const uint16_t *x_bf16, int32_t T, int32_t H, const int32_t *perm,
-                              int32_t topk, int32_t R_max, const int32_t *n_rows,
-                              const fq_act_q *aq, uint16_t *xq_bf16, fq_stream stream);
+fq_status fq_moe_gather_actfq(const uint16_t *x_bf16, int32_t T, int32_t H, const int32_t *row_of,
+                              int32_t topk, const fq_act_q *aq, uint16_t *xq_bf16,
+                              fq_stream stream);
 fq_status fq_swiglu_actfq(const uint16_t *h_bf16, int32_t R_max, const int32_t *n_rows, int32_t F,
                           const fq_act_q *aq, uint16_t *a_bf16, uint16_t *aq_bf16,
                           fq_stream stream);
@@ -249,9 +252,9 @@ fq_status fq_swiglu_bwd(const uint16_t *daq_bf16, const uint16_t *h_bf16, int32_
 fq_status fq_moe_combine(const uint16_t *o_bf16, const float *probs, const int32_t *row_of,
                          int32_t T, int32_t topk, int32_t H, uint16_t *out_bf16,
                          fq_stream stream);
-fq_status fq_moe_combine_bwd(const uint16_t *dout_bf16, const float *probs, const int32_t *perm,
-                             int32_t topk, int32_t H, int32_t R_max, const int32_t *n_rows,
-                             uint16_t *do_bf16, fq_stream stream);
+fq_status fq_moe_combine_bwd(const uint16_t *dout_bf16, const float *probs, const int32_t *row_of,
+                             int32_t T, int32_t topk, int32_t H, uint16_t *do_bf16,
+                             fq_stream stream);
 fq_status fq_moe_unpermute_reduce(const uint16_t *dxq_bf16, const int32_t *row_of,
                                   const uint16_t *x_bf16, int32_t T, int32_t topk, int32_t H,
                                   const fq_act_q *aq, uint16_t *dx_bf16, fq_stream stream);

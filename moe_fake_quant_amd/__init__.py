@@ -81,11 +81,11 @@ def _load() -> ctypes.CDLL:
         "fq_grouped_gemm_bwd_scale": (st, [P, P, I32, P, fq_shape, P, P,
                                            ctypes.POINTER(fq_weight_q), ctypes.POINTER(fq_act_q),
                                            P, P, P, P, SZ, P]),
-        "fq_moe_gather_actfq": (st, [P, I32, I32, P, I32, I32, P, ctypes.POINTER(fq_act_q), P, P]),
+        "fq_moe_gather_actfq": (st, [P, I32, I32, P, I32, ctypes.POINTER(fq_act_q), P, P]),
         "fq_swiglu_actfq": (st, [P, I32, P, I32, ctypes.POINTER(fq_act_q), P, P, P]),
         "fq_swiglu_bwd": (st, [P, P, I32, P, I32, ctypes.POINTER(fq_act_q), P, P]),
         "fq_moe_combine": (st, [P, P, P, I32, I32, I32, P, P]),
-        "fq_moe_combine_bwd": (st, [P, P, P, I32, I32, I32, P, P, P]),
+        "fq_moe_combine_bwd": (st, [P, P, P, I32, I32, I32, P, P]),
         "fq_moe_unpermute_reduce": (st, [P, P, P, I32, I32, I32, ctypes.POINTER(fq_act_q), P, P]),
         "fq_workspace_bytes": (SZ, [I32, fq_shape, I32, I32]),
         "fq_last_error": (ctypes.c_char_p, []),
@@ -202,9 +202,9 @@ def fq_grouped_gemm_bwd_scale(dy, x, R_max, seg_offsets, shape, w, w_fq, wq: Wei
                                           _nbytes(ws), _stream()))
 
 
-def fq_moe_gather_actfq(x, T, H, perm, topk, R_max, n_rows, aq: Optional[ActQ], xq):
-    _check(_lib.fq_moe_gather_actfq(_p(x), int(T), int(H), _p(perm), int(topk), int(R_max),
-                                    _p(n_rows), _aq(aq), _p(xq), _stream()))
+def fq_moe_gather_actfq(x, T, H, row_of, topk, aq: Optional[ActQ], xq):
+    _check(_lib.fq_moe_gather_actfq(_p(x), int(T), int(H), _p(row_of), int(topk), _aq(aq),
+                                    _p(xq), _stream()))
 
 
 def fq_swiglu_actfq(h, R_max, n_rows, F, aq: Optional[ActQ], a, aq_out):
@@ -222,9 +222,9 @@ def fq_moe_combine(o, probs, row_of, T, topk, H, out):
                                _stream()))
 
 
-def fq_moe_combine_bwd(dout, probs, perm, topk, H, R_max, n_rows, dO):
-    _check(_lib.fq_moe_combine_bwd(_p(dout), _p(probs), _p(perm), int(topk), int(H), int(R_max),
-                                   _p(n_rows), _p(dO), _stream()))
+def fq_moe_combine_bwd(dout, probs, row_of, T, topk, H, dO):
+    _check(_lib.fq_moe_combine_bwd(_p(dout), _p(probs), _p(row_of), int(T), int(topk), int(H),
+                                   _p(dO), _stream()))
 
 
 def fq_moe_unpermute_reduce(dxq, row_of, x, T, topk, H, aq: Optional[ActQ], dx):

@@ -288,17 +288,15 @@ fq_status fq_grouped_gemm_bwd_scale(const uint16_t *dy, const uint16_t *x, int32
   return FQ_OK;
 }
 
-fq_status fq_moe_gather_actfq(const uint16_t *x, int32_t T, int32_t H, const int32_t *perm,
-                              int32_t topk, int32_t R_max, const int32_t *n_rows, const fq_act_q *aq,
-                              uint16_t *xq, fq_stream stream) {
-  FQ_CHECK_ARG(T >= 0 && H > 0 && topk > 0 && R_max >= 0, "bad sizes");
+fq_status fq_moe_gather_actfq(const uint16_t *x, int32_t T, int32_t H, const int32_t *row_of,
+                              int32_t topk, const fq_act_q *aq, uint16_t *xq, fq_stream stream) {
+  FQ_CHECK_ARG(T >= 0 && H > 0 && topk > 0, "bad sizes");
   FQ_CHECK_ARG(H % 16 == 0, "H must be a multiple of 16");
-  FQ_CHECK_ARG(n_rows && (R_max == 0 || T == 0 || (x && perm && xq)), "NULL pointer");
+  FQ_CHECK_ARG(T == 0 || (x && row_of && xq), "NULL pointer");
   FQ_CHECK_ARG((!x || aligned16(x)) && (!xq || aligned16(xq)), "bf16 tensors must be 16-byte aligned");
+  FQ_CHECK_ARG((long)T * H < (1l << 36), "too many elements");
   FQ_TRY(check_act_q(aq, H));
-  if (T == 0) return FQ_OK;  // no tokens: no routed row exists, nothing to gather
-  launch_gather_actfq(x, H, perm, topk, R_max, n_rows, act_fmt(aq), aq ? aq->scale : nullptr, xq,
-                      S(stream));
+  launch_gather_actfq(x, T, H, row_of, topk, act_fmt(aq), aq ? aq->scale : nullptr, xq, S(stream));
   FQ_CHECK_LAUNCH("fq_moe_gather_actfq");
   return FQ_OK;
 }
@@ -330,6 +328,7 @@ fq_status fq_swiglu_bwd(const uint16_t *daq, const uint16_t *h, int32_t R_max, c
 fq_status fq_moe_combine(const uint16_t *o, const float *probs, const int32_t *row_of, int32_t T,
                          int32_t topk, int32_t H, uint16_t *out, fq_stream stream) {
   FQ_CHECK_ARG(T >= 0 && topk > 0 && H > 0 && H % 16 == 0, "bad sizes (H must be a multiple of 16)");
+  FQ_CHECK_ARG((long)T * H < (1l << 36), "too many elements");
   FQ_CHECK_ARG(T == 0 || (o && probs && row_of && out), "NULL pointer");
   FQ_CHECK_ARG((!o || aligned16(o)) && (!out || aligned16(out)), "bf16 tensors must be 16-byte aligned");
   launch_combine(o, probs, row_of, T, topk, H, out, S(stream));
@@ -337,14 +336,14 @@ fq_status fq_moe_combine(const uint16_t *o, const float *probs, const int32_t *r
   return FQ_OK;
 }
 
-fq_status fq_moe_combine_bwd(const uint16_t *dout, const float *probs, const int32_t *perm,
-                             int32_t topk, int32_t H, int32_t R_max, const int32_t *n_rows,
-                             uint16_t *dO, fq_stream stream) {
-  FQ_CHECK_ARG(topk > 0 && H > 0 && H % 16 == 0 && R_max >= 0, "bad sizes");
-  FQ_CHECK_ARG(n_rows && (R_max == 0 || (dout && probs && perm && dO)), "NULL pointer");
+fq_status fq_moe_combine_bwd(const uint16_t *dout, const float *probs, const int32_t *row_of,
+                             int32_t T, int32_t topk, int32_t H, uint16_t *dO, fq_stream stream) {
+  FQ_CHECK_ARG(T >= 0 && topk > 0 && H > 0 && H % 16 == 0, "bad sizes (H must be a multiple of 16)");
+  FQ_CHECK_ARG((long)T * H < (1l << 36), "too many elements");
+  FQ_CHECK_ARG(T == 0 || (dout && probs && row_of && dO), "NULL pointer");
   FQ_CHECK_ARG((!dout || aligned16(dout)) && (!dO || aligned16(dO)),
                "bf16 tensors must be 16-byte aligned");
-  launch_combine_bwd(dout, probs, perm, topk, H, R_max, n_rows, dO, S(stream));
+  launch_combine_bwd(dout, probs, row_of, T, topk, H, dO, S(stream));
   FQ_CHECK_LAUNCH("fq_moe_combine_bwd");
   return FQ_OK;
 }
@@ -353,6 +352,7 @@ fq_status fq_moe_unpermute_reduce(const uint16_t *dxq, const int32_t *row_of, co
                                   int32_t T, int32_t topk, int32_t H, const fq_act_q *aq,
                                   uint16_t *dx, fq_stream stream) {
   FQ_CHECK_ARG(T >= 0 && topk > 0 && H > 0 && H % 16 == 0, "bad sizes (H must be a multiple of 16)");
+  FQ_CHECK_ARG((long)T * H < (1l << 36), "too many elements");
   FQ_CHECK_ARG(T == 0 || (dxq && row_of && dx), "NULL pointer");
   FQ_TRY(check_act_q(aq, H));
   FQ_CHECK_ARG(act_fmt(aq) == FQ_FMT_NONE || T == 0 || x, "x is NULL");

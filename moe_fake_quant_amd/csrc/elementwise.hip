@@ -337,20 +337,24 @@ __global__ __launch_bounds__(kThreads) void k_act_mask(bf16x8_t *__restrict__ dx
 }
 
 // xq[r] = FQ_a(x[perm[r] / topk]) for r < n_rows[0]
+// Per token: x[t] is read and fake-quantized once, then stored to each of its
+// routed rows xq[row_of[t, j]] (j ascending; -1 = not routed here).
 __global__ __launch_bounds__(kThreads) void k_gather_actfq(
-    const bf16x8_t *__restrict__ x, const int32_t *__restrict__ perm, int topk, FastDiv chunks_per_row,
-    uint32_t max_chunks, const int32_t *__restrict__ n_rows, int afmt, const float *__restrict__ ascale,
+    const bf16x8_t *__restrict__ x, const int32_t *__restrict__ row_of, int topk,
+    FastDiv chunks_per_row, uint32_t nchunk, int afmt, const float *__restrict__ ascale,
     bf16x8_t *__restrict__ xq) {
   ActQ q = load_actq(afmt, ascale);
-  const uint32_t nchunk = min((uint32_t)n_rows[0] * chunks_per_row.d, max_chunks);
+  const uint32_t cpr = chunks_per_row.d;
   for (uint32_t c = blockIdx.x * blockDim.x + threadIdx.x; c < nchunk; c += gridDim.x * blockDim.x) {
-    uint32_t r = chunks_per_row.div(c);
-    uint32_t cc = c - r * chunks_per_row.d;
-    uint32_t t = (uint32_t)perm[r] / (uint32_t)topk;
+    const uint32_t t = chunks_per_row.div(c);
+    const uint32_t cc = c - t * cpr;
     float f[16];
-    load16(x + 2 * ((size_t)t * chunks_per_row.d + cc), f);
+    load16(x + 2 * (size_t)c, f);
     act_fq16(q, f);
-    store16(xq + 2 * (size_t)c, f);
+    for (int j = 0; j < topk; ++j) {
+      const int r = row_of[t * topk + j];
+      if (r >= 0) store16(xq + 2 * ((size_t)r * cpr + cc), f);
+    }
   }
 }
 
@@ -443,23 +447,27 @@ __global__ __launch_bounds__(kThreads) void k_combine(const bf16x8_t *__restrict
 }
 
 // do[r] = bf16(p[t,j] * dout[t]), f = perm[r]
+// Per token: dout[t] is read once and dO[row_of[t, j]] = bf16(p[t,j] * dout[t])
+// stored for each routed slot j.
 __global__ __launch_bounds__(kThreads) void k_combine_bwd(
-    const bf16x8_t *__restrict__ dout, const float *__restrict__ probs, const int32_t *__restrict__ perm,
-    int topk, FastDiv chunks_per_row, uint32_t max_chunks, const int32_t *__restrict__ n_rows,
+    const bf16x8_t *__restrict__ dout, const float *__restrict__ probs,
+    const int32_t *__restrict__ row_of, int topk, FastDiv chunks_per_row, uint32_t nchunk,
     bf16x8_t *__restrict__ dO) {
   const uint32_t cpr = chunks_per_row.d;
-  const uint32_t nchunk = min((uint32_t)n_rows[0] * cpr, max_chunks);
   for (uint32_t c = blockIdx.x * blockDim.x + threadIdx.x; c < nchunk; c += gridDim.x * blockDim.x) {
-    uint32_t r = chunks_per_row.div(c);
-    uint32_t cc = c - r * cpr;
-    uint32_t f = (uint32_t)perm[r];
-    uint32_t t = f / (uint32_t)topk;
-    float p = probs[f];
+    const uint32_t t = chunks_per_row.div(c);
+    const uint32_t cc = c - t * cpr;
     float d[16];
-    load16(dout + 2 * ((size_t)t * cpr + cc), d);
+    load16(dout + 2 * (size_t)c, d);
+    for (int j = 0; j < topk; ++j) {
+      const int r = row_of[t * topk + j];
+      if (r < 0) continue;
+      const float p = probs[t * topk + j];
+      float o[16];
 #pragma unroll
-    for (int j = 0; j < 16; ++j) d[j] = p * d[j];
-    store16(dO + 2 * (size_t)c, d);
+      for (int i = 0; i < 16; ++i) o[i] = p * d[i];
+      store16(dO + 2 * ((size_t)r * cpr + cc), o);
+    }
   }
 }
 
@@ -606,13 +614,12 @@ void launch_act_mask(uint16_t *dx, const uint16_t *x, size_t M, int K, const int
                      n_rows, (uint32_t)(K / 16), afmt, ascale);
 }
 
-void launch_gather_actfq(const uint16_t *x, int H, const int32_t *perm, int topk, int R_max,
-                         const int32_t *n_rows, int afmt, const float *ascale, uint16_t *xq,
-                         hipStream_t st) {
-  uint32_t maxc = (uint32_t)((size_t)R_max * H / 16);
-  if (!maxc) return;
-  hipLaunchKernelGGL(k_gather_actfq, dim3(grid_for(maxc)), dim3(kThreads), 0, st,
-                     reinterpret_cast<const bf16x8_t *>(x), perm, topk, FastDiv(H / 16), maxc, n_rows,
+void launch_gather_actfq(const uint16_t *x, int T, int H, const int32_t *row_of, int topk,
+                         int afmt, const float *ascale, uint16_t *xq, hipStream_t st) {
+  const uint32_t nchunk = (uint32_t)((size_t)T * H / 16);
+  if (!nchunk) return;
+  hipLaunchKernelGGL(k_gather_actfq, dim3(grid_for(nchunk)), dim3(kThreads), 0, st,
+                     reinterpret_cast<const bf16x8_t *>(x), row_of, topk, FastDiv(H / 16), nchunk,
                      afmt, ascale, reinterpret_cast<bf16x8_t *>(xq));
 }
 
@@ -643,13 +650,13 @@ void launch_combine(const uint16_t *o, const float *probs, const int32_t *row_of
                      nchunk, reinterpret_cast<bf16x8_t *>(out));
 }
 
-void launch_combine_bwd(const uint16_t *dout, const float *probs, const int32_t *perm, int topk,
-                        int H, int R_max, const int32_t *n_rows, uint16_t *dO, hipStream_t st) {
-  uint32_t maxc = (uint32_t)((size_t)R_max * H / 16);
-  if (!maxc) return;
-  hipLaunchKernelGGL(k_combine_bwd, dim3(grid_for(maxc)), dim3(kThreads), 0, st,
-                     reinterpret_cast<const bf16x8_t *>(dout), probs, perm, topk, FastDiv(H / 16), maxc,
-                     n_rows, reinterpret_cast<bf16x8_t *>(dO));
+void launch_combine_bwd(const uint16_t *dout, const float *probs, const int32_t *row_of, int T,
+                        int topk, int H, uint16_t *dO, hipStream_t st) {
+  const uint32_t nchunk = (uint32_t)((size_t)T * H / 16);
+  if (!nchunk) return;
+  hipLaunchKernelGGL(k_combine_bwd, dim3(grid_for(nchunk)), dim3(kThreads), 0, st,
+                     reinterpret_cast<const bf16x8_t *>(dout), probs, row_of, topk, FastDiv(H / 16),
+                     nchunk, reinterpret_cast<bf16x8_t *>(dO));
 }
 
 void launch_unpermute_reduce(const uint16_t *dxq, const int32_t *row_of, const uint16_t *x, int T,

@@ -17,17 +17,16 @@ void launch_act_fq(const uint16_t *x, size_t M, int K, const int32_t *n_rows, in
                    const float *ascale, uint16_t *xq, hipStream_t st);
 void launch_act_mask(uint16_t *dx, const uint16_t *x, size_t M, int K, const int32_t *n_rows,
                      int afmt, const float *ascale, hipStream_t st);
-void launch_gather_actfq(const uint16_t *x, int H, const int32_t *perm, int topk, int R_max,
-                         const int32_t *n_rows, int afmt, const float *ascale, uint16_t *xq,
-                         hipStream_t st);
+void launch_gather_actfq(const uint16_t *x, int T, int H, const int32_t *row_of, int topk,
+                         int afmt, const float *ascale, uint16_t *xq, hipStream_t st);
 void launch_swiglu_actfq(const uint16_t *h, int R_max, const int32_t *n_rows, int F, int afmt,
                          const float *ascale, uint16_t *a, uint16_t *aq, hipStream_t st);
 void launch_swiglu_bwd(const uint16_t *daq, const uint16_t *h, int R_max, const int32_t *n_rows,
                        int F, int afmt, const float *ascale, uint16_t *dh, hipStream_t st);
 void launch_combine(const uint16_t *o, const float *probs, const int32_t *row_of, int T, int topk,
                     int H, uint16_t *out, hipStream_t st);
-void launch_combine_bwd(const uint16_t *dout, const float *probs, const int32_t *perm, int topk,
-                        int H, int R_max, const int32_t *n_rows, uint16_t *dO, hipStream_t st);
+void launch_combine_bwd(const uint16_t *dout, const float *probs, const int32_t *row_of, int T,
+                        int topk, int H, uint16_t *dO, hipStream_t st);
 void launch_unpermute_reduce(const uint16_t *dxq, const int32_t *row_of, const uint16_t *x, int T,
                              int topk, int H, int afmt, const float *ascale, uint16_t *dx,
                              hipStream_t st);

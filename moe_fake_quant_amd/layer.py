@@ -119,8 +119,7 @@ class MoEFakeQuantLayer:
         self.quantize_weights()
         self.route(expert_ids)
         R = int(self.seg[self.E].item())
-        fq_moe_gather_actfq(x, T, self.H, self.perm, self.topk, self.R_max, self.n_rows, self.aq1,
-                            self.xq)
+        fq_moe_gather_actfq(x, T, self.H, self.row_of[:T], self.topk, self.aq1, self.xq)
         fq_grouped_gemm_fwd(self.xq, self.R_max, self.seg, self.shape_gu, None, self.wfq_gu,
                             self.q_gu, None, self.h, self.ws)
         fq_swiglu_actfq(self.h, self.R_max, self.n_rows, self.F, None, self.a, self.aq)
@@ -132,8 +131,7 @@ class MoEFakeQuantLayer:
                 keep_a: bool = False) -> torch.Tensor:
         T = x.shape[0]
         self.route(expert_ids)
-        fq_moe_gather_actfq(x, T, self.H, self.perm, self.topk, self.R_max, self.n_rows, self.aq1,
-                            self.xq)
+        fq_moe_gather_actfq(x, T, self.H, self.row_of[:T], self.topk, self.aq1, self.xq)
         fq_grouped_gemm_fwd(self.xq, self.R_max, self.seg, self.shape_gu, None, self.wfq_gu,
                             self.q_gu, None, self.h, self.ws)
         fq_swiglu_actfq(self.h, self.R_max, self.n_rows, self.F, self.aq2,
@@ -145,9 +143,7 @@ class MoEFakeQuantLayer:
 
     def backward(self, x: torch.Tensor, probs: torch.Tensor, dout: torch.Tensor):
         T = x.shape[0]
-        if T > 0:  # an empty batch has no routed rows to scatter into
-            fq_moe_combine_bwd(dout, probs, self.perm, self.topk, self.H, self.R_max,
-                               self.n_rows, self.do)
+        fq_moe_combine_bwd(dout, probs, self.row_of[:T], T, self.topk, self.H, self.do)
         # dgrad and wgrad -> dScale as two calls (one GEMM kernel each)
         fq_grouped_gemm_bwd_scale(self.do, self.aq, self.R_max, self.seg, self.shape_d, self.w_d,
                                   self.wfq_d, self.q_d, None, self.daq, None, None, self.ws)

@@ -191,15 +191,17 @@ def test_permute_and_elementwise_reject_bad_arguments(pkg):
         pkg.FQ_ERR_INVALID_ARGUMENT                                   # no seg_offsets
     assert L.fq_moe_permute(FAKE, 16, 8, 0, 4, FAKE, FAKE, FAKE, FAKE, 8, None) == \
         pkg.FQ_ERR_WORKSPACE_TOO_SMALL
-    assert L.fq_moe_gather_actfq(FAKE, 16, 40, FAKE, 8, 128, FAKE, None, FAKE, None) == \
+    assert L.fq_moe_gather_actfq(FAKE, 16, 40, FAKE, 8, None, FAKE, None) == \
         pkg.FQ_ERR_INVALID_ARGUMENT                                   # H % 16
+    assert L.fq_moe_gather_actfq(FAKE, 16, 64, None, 8, None, FAKE, None) == \
+        pkg.FQ_ERR_INVALID_ARGUMENT                                   # no row map
     assert L.fq_swiglu_actfq(FAKE, 128, None, 64, None, None, FAKE, None) == \
         pkg.FQ_ERR_INVALID_ARGUMENT                                   # no n_rows
     assert L.fq_swiglu_bwd(FAKE, FAKE, 128, FAKE, 24, None, FAKE, None) == \
         pkg.FQ_ERR_INVALID_ARGUMENT                                   # F % 16
     assert L.fq_moe_combine(FAKE, FAKE, FAKE, 16, 8, 64, FAKE + 8, None) == \
         pkg.FQ_ERR_INVALID_ARGUMENT                                   # misaligned out
-    assert L.fq_moe_combine_bwd(FAKE, FAKE, FAKE, 0, 64, 128, FAKE, FAKE, None) == \
+    assert L.fq_moe_combine_bwd(FAKE, FAKE, FAKE, 16, 0, 64, FAKE, None) == \
         pkg.FQ_ERR_INVALID_ARGUMENT                                   # topk 0
     aq = ctypes.byref(pkg.fq_act_q(pkg.FMT_FP8_E4M3, FAKE))
     assert L.fq_moe_unpermute_reduce(FAKE, FAKE, None, 16, 8, 64, aq, FAKE, None) == \

@@ -9,9 +9,13 @@
 // with -ffp-contract=off so no multiply-add is fused: z = x * r and
 // v = value * s are each one rounded multiply, exactly as specified.
 //
-// Grid rounding here is bit arithmetic on the fp32 encoding (E4M3: round the
+// Grid rounding is bit arithmetic on the fp32 encoding (E4M3: round the
 // mantissa to 3 bits, E2M1: to 1 bit; multiples of the smallest step below the
-// normal range), not a table search.
+// normal range), not a table search. The hot paths round two values per
+// instruction on gfx950's FP4 / FP8 converters instead (e2m1_pair, e4m3_pair);
+// over every non-NaN fp32 input these give the same codes and values as the
+// bit-arithmetic forms below (saturating, ties to even, sign kept,
+// subnormals kept).
 #pragma once
 
 #include "common.hpp"
@@ -55,6 +59,26 @@ __device__ __forceinline__ uint32_t e2m1_code_of_mag(float v) {
   const uint32_t c_hi = (((u >> 23) - 126u) << 1) | ((u >> 22) & 1u);
   return v < 1.0f ? (uint32_t)(v * 2.0f) : c_hi;
 }
+
+// Two values z0, z1 rounded to E2M1 on the converter: values (sign of z kept,
+// |z| > 6 saturates) and the packed codes, z0 in the low nibble.
+__device__ __forceinline__ uint32_t e2m1_pair(float z0, float z1, float &v0, float &v1) {
+  const uint32_t c = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, z0, z1, 1.0f, 0);
+  const f32x2_t v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, 1.0f, 0);
+  v0 = v.x;
+  v1 = v.y;
+  return c & 0xFFu;
+}
+// Two values already clamped to [-448, 448] rounded to E4M3: values and the
+// packed codes, z0 in the low byte.
+__device__ __forceinline__ uint32_t e4m3_pair(float z0, float z1, float &v0, float &v1) {
+  const uint32_t c = __builtin_amdgcn_cvt_pk_fp8_f32(z0, z1, 0u, false);
+  const f32x2_t v = __builtin_amdgcn_cvt_pk_f32_fp8(c, false);
+  v0 = v.x;
+  v1 = v.y;
+  return c & 0xFFFFu;
+}
+__device__ __forceinline__ float clamp448(float z) { return fminf(fmaxf(z, -kE4M3Max), kE4M3Max); }
 
 // One fake-quantized element: dequantized value, code, and STE terms.
 struct FQElem {
@@ -178,6 +202,30 @@ __device__ __forceinline__ float ste_factor(float x, float s, float r, float zpi
   const bool m = zc == z;
   dvdzp = m ? 0.0f : -s;
   return rintf(zc) - (m ? z : 0.0f);
+}
+
+// ste_factor of two elements sharing a scale (FP formats round on the
+// converter; the integer formats use the per-element form).
+template <int FMT>
+__device__ __forceinline__ void ste_factor2(float x0, float x1, float s, float r, float zpi,
+                                            float &f0, float &f1, float &dz0, float &dz1) {
+  if (FMT == FQ_FMT_NVFP4 || FMT == FQ_FMT_FP8_E4M3) {
+    const float z0 = x0 * r, z1 = x1 * r;
+    float v0, v1;
+    if (FMT == FQ_FMT_NVFP4) {
+      e2m1_pair(z0, z1, v0, v1);
+      f0 = v0 - (fabsf(z0) <= kE2M1Max ? z0 : 0.0f);
+      f1 = v1 - (fabsf(z1) <= kE2M1Max ? z1 : 0.0f);
+    } else {
+      e4m3_pair(clamp448(z0), clamp448(z1), v0, v1);
+      f0 = v0 - (fabsf(z0) <= kE4M3Max ? z0 : 0.0f);
+      f1 = v1 - (fabsf(z1) <= kE4M3Max ? z1 : 0.0f);
+    }
+    dz0 = dz1 = 0.0f;
+  } else {
+    f0 = ste_factor<FMT>(x0, s, r, zpi, dz0);
+    f1 = ste_factor<FMT>(x1, s, r, zpi, dz1);
+  }
 }
 
 // Generic per-element dispatch for weights (fmt known at runtime).

@@ -39,20 +39,22 @@ fq_status hip_status(hipError_t e, const char *what);
 inline bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 // ----------------------------------------------------------------- bf16 --
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
 __device__ __forceinline__ float bf16_to_f32(uint32_t b) {
   return __uint_as_float(b << 16);
 }
-// Round to nearest even on the dropped 16 bits (finite inputs).
-__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return u >> 16;
+// fp32 -> bf16, round to nearest even, two at a time on the hardware
+// converter (v_cvt_pk_bf16_f32: the same bits as adding 0x7FFF + lsb to the
+// fp32 encoding and truncating, for every non-NaN input).
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+  const f32x2_t x = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(x, bf16x2_t));
 }
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) { return pack_bf16(f, 0.0f) & 0xFFFFu; }
 __device__ __forceinline__ float lo_bf16(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float hi_bf16(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
-__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
-  return f32_to_bf16(a) | (f32_to_bf16(b) << 16);
-}
 
 // 8 bf16 in 16 bytes
 struct alignas(16) bf16x8_t {

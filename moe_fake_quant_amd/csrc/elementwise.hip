@@ -31,46 +31,96 @@ __global__ void k_fill_u32(uint32_t *p, uint32_t v, long n) {
 // One thread-iteration handles one 8-element vector of one row. Requires
 // group % 8 == 0 so a vector never straddles a scale group.
 template <int FMT>
+__device__ __forceinline__ void quantize_vec(const bf16x8_t v, float s, float zpi, uint32_t i,
+                                             bf16x8_t *__restrict__ out,
+                                             uint8_t *__restrict__ codes) {
+  const float r = safe_recip(s);
+  float x[8], y[8];
+  unpack8(v, x);
+  if (FMT == FQ_FMT_NVFP4 || FMT == FQ_FMT_FP8_E4M3) {
+    uint32_t cw[2] = {0u, 0u};
+    if (FMT == FQ_FMT_NVFP4 && s == 0.0f) {  // zero block: +0.0, code 0
+#pragma unroll
+      for (int j = 0; j < 8; ++j) y[j] = 0.0f;
+    } else {
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        float v0, v1;
+        if (FMT == FQ_FMT_NVFP4) {
+          cw[0] |= e2m1_pair(x[2 * p] * r, x[2 * p + 1] * r, v0, v1) << (8 * p);
+        } else {
+          cw[p >> 1] |= e4m3_pair(clamp448(x[2 * p] * r), clamp448(x[2 * p + 1] * r), v0, v1)
+                        << (16 * (p & 1));
+        }
+        y[2 * p] = v0 * s;
+        y[2 * p + 1] = v1 * s;
+      }
+    }
+    if (out) out[i] = pack8(y);
+    if (codes) {
+      if (FMT == FQ_FMT_NVFP4) reinterpret_cast<uint32_t *>(codes)[i] = cw[0];
+      else reinterpret_cast<uint2 *>(codes)[i] = make_uint2(cw[0], cw[1]);
+    }
+    return;
+  }
+  uint32_t c[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    FQElem e = fq_weight_elem(FMT, x[j], s, r, zpi);
+    y[j] = e.v;
+    c[j] = e.code;
+  }
+  if (out) out[i] = pack8(y);
+  if (codes) {
+    if (FMT == FQ_FMT_INT8) {
+      uint2 b;
+      b.x = c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24);
+      b.y = c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24);
+      reinterpret_cast<uint2 *>(codes)[i] = b;
+    } else {
+      uint32_t b = 0;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) b |= (c[j] & 0xFu) << (4 * j);
+      reinterpret_cast<uint32_t *>(codes)[i] = b;
+    }
+  }
+}
+
+// Each thread takes kQU vectors a grid stride apart per iteration and issues
+// all their loads before any arithmetic, so enough bytes are in flight per CU
+// to cover the HBM latency.
+constexpr int kQU = 4;
+template <int FMT>
 __global__ __launch_bounds__(kThreads) void k_quantize_stacked(
     const bf16x8_t *__restrict__ w, uint32_t nvec, FastDiv vec_per_row, FastDiv rows_per_expert,
     FastDiv vec_per_group, uint32_t groups_per_row, const float *__restrict__ scale,
     const float *__restrict__ zero_point, const float *__restrict__ gscale,
     bf16x8_t *__restrict__ out, uint8_t *__restrict__ codes) {
   const uint32_t stride = gridDim.x * blockDim.x;
-  for (uint32_t i = blockIdx.x * blockDim.x + threadIdx.x; i < nvec; i += stride) {
-    bf16x8_t v = w[i];
-    uint32_t row = vec_per_row.div(i);
-    uint32_t kv = i - row * vec_per_row.d;
-    uint32_t gidx = row * groups_per_row + vec_per_group.div(kv);
-    float s = scale[gidx];
-    float zpi = 0.0f, g = 1.0f;
-    if (FMT == FQ_FMT_INT4) zpi = fminf(fmaxf(rintf(zero_point[gidx]), 0.0f), 15.0f);
-    if (FMT == FQ_FMT_NVFP4) {
-      g = gscale[rows_per_expert.div(row)];
-      s = nvfp4_block_scale(s, g);
-    }
-    float r = safe_recip(s);
-    float x[8], y[8];
-    unpack8(v, x);
-    uint32_t c[8];
+  for (uint32_t i0 = blockIdx.x * blockDim.x + threadIdx.x; i0 < nvec; i0 += kQU * stride) {
+    bf16x8_t v[kQU];
+    float sc[kQU], zp[kQU], g[kQU];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      FQElem e = fq_weight_elem(FMT, x[j], s, r, zpi);
-      y[j] = e.v;
-      c[j] = e.code;
+    for (int u = 0; u < kQU; ++u) {
+      const uint32_t i = i0 + u * stride;
+      if (i < nvec) {
+        v[u] = w[i];
+        const uint32_t row = vec_per_row.div(i);
+        const uint32_t kv = i - row * vec_per_row.d;
+        const uint32_t gidx = row * groups_per_row + vec_per_group.div(kv);
+        sc[u] = scale[gidx];
+        zp[u] = (FMT == FQ_FMT_INT4) ? zero_point[gidx] : 0.0f;
+        g[u] = (FMT == FQ_FMT_NVFP4) ? gscale[rows_per_expert.div(row)] : 1.0f;
+      }
     }
-    if (out) out[i] = pack8(y);
-    if (codes) {
-      if (FMT == FQ_FMT_INT8 || FMT == FQ_FMT_FP8_E4M3) {
-        uint2 b;
-        b.x = c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24);
-        b.y = c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24);
-        reinterpret_cast<uint2 *>(codes)[i] = b;
-      } else {
-        uint32_t b = 0;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) b |= (c[j] & 0xFu) << (4 * j);
-        reinterpret_cast<uint32_t *>(codes)[i] = b;
+    for (int u = 0; u < kQU; ++u) {
+      const uint32_t i = i0 + u * stride;
+      if (i < nvec) {
+        float s = sc[u], zpi = 0.0f;
+        if (FMT == FQ_FMT_INT4) zpi = fminf(fmaxf(rintf(zp[u]), 0.0f), 15.0f);
+        if (FMT == FQ_FMT_NVFP4) s = nvfp4_block_scale(s, g[u]);
+        quantize_vec<FMT>(v[u], s, zpi, i, out, codes);
       }
     }
   }
@@ -256,23 +306,37 @@ __device__ __forceinline__ ActQ load_actq(int fmt, const float *scale) {
 __device__ __forceinline__ uint32_t act_fq16(const ActQ &q, float *x) {
   uint32_t mask = 0;
   if (q.fmt == FQ_FMT_NONE) return 0xFFFFu;
-  if (q.fmt == FQ_FMT_NVFP4) {
-    float amax = 0.0f;
+  if (q.fmt == FQ_FMT_NVFP4 || q.fmt == FQ_FMT_FP8_E4M3) {
+    float s = q.s, r = q.r;
+    const float mx = q.fmt == FQ_FMT_NVFP4 ? kE2M1Max : kE4M3Max;
+    if (q.fmt == FQ_FMT_NVFP4) {
+      float amax = 0.0f;
 #pragma unroll
-    for (int j = 0; j < 16; ++j) amax = fmaxf(amax, fabsf(x[j]));
-    float s = nvfp4_dynamic_scale(amax, q.s);
-    float r = safe_recip(s);
+      for (int j = 0; j < 16; ++j) amax = fmaxf(amax, fabsf(x[j]));
+      s = nvfp4_dynamic_scale(amax, q.s);
+      if (s == 0.0f) {  // zero block: +0.0, mask 0
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      FQElem e = fq_e2m1(x[j], s, r);
-      x[j] = e.v;
-      mask |= (uint32_t)e.m << j;
+        for (int j = 0; j < 16; ++j) x[j] = 0.0f;
+        return 0u;
+      }
+      r = 1.0f / s;
+    }
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+      const float z0 = x[2 * p] * r, z1 = x[2 * p + 1] * r;
+      float v0, v1;
+      if (q.fmt == FQ_FMT_NVFP4) e2m1_pair(z0, z1, v0, v1);
+      else e4m3_pair(clamp448(z0), clamp448(z1), v0, v1);
+      mask |= (uint32_t)(fabsf(z0) <= mx) << (2 * p);
+      mask |= (uint32_t)(fabsf(z1) <= mx) << (2 * p + 1);
+      x[2 * p] = v0 * s;
+      x[2 * p + 1] = v1 * s;
     }
     return mask;
   }
 #pragma unroll
   for (int j = 0; j < 16; ++j) {
-    FQElem e = (q.fmt == FQ_FMT_FP8_E4M3) ? fq_fp8(x[j], q.s, q.r) : fq_int8(x[j], q.s, q.r);
+    FQElem e = fq_int8(x[j], q.s, q.r);
     x[j] = e.v;
     mask |= (uint32_t)e.m << j;
   }
@@ -527,7 +591,7 @@ void launch_quantize_stacked(const uint16_t *w, fq_shape s, const fq_weight_q &q
   uint32_t nvec = (uint32_t)((size_t)s.E * s.N * s.K / 8);
   FastDiv vpr(s.K / 8), rpe(s.N), vpg(q.group / 8);
   uint32_t gpr = s.K / q.group;
-  dim3 grid(grid_for(nvec)), block(kThreads);
+  dim3 grid(grid_for(ceil_div((long)nvec, kQU))), block(kThreads);
   auto wv = reinterpret_cast<const bf16x8_t *>(w);
   auto ov = reinterpret_cast<bf16x8_t *>(out);
 #define FQ_QS(F)                                                                                \

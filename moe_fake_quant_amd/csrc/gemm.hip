@@ -217,13 +217,14 @@ __device__ __forceinline__ void wgrad_epilogue(const GemmArgs &a, const f32x16 (
         const int q = 2 * b + qq;
         const float x4[4] = {lo_bf16(wv[s][q].x), hi_bf16(wv[s][q].x), lo_bf16(wv[s][q].y),
                              hi_bf16(wv[s][q].y)};
+        float phi[4], dzp[4];
+        ste_factor2<WFMT>(x4[0], x4[1], sc, r, zpi, phi[0], phi[1], dzp[0], dzp[1]);
+        ste_factor2<WFMT>(x4[2], x4[3], sc, r, zpi, phi[2], phi[3], dzp[2], dzp[3]);
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-          float dzp;
-          const float phi = ste_factor<WFMT>(x4[v], sc, r, zpi, dzp);
           const float d = acc[s][U][4 * q + v];
-          accs += d * phi;
-          if (WFMT == FQ_FMT_INT4) accz += d * dzp;
+          accs += d * phi[v];
+          if (WFMT == FQ_FMT_INT4) accz += d * dzp[v];
         }
       }
       ps16[b] = (WFMT == FQ_FMT_NVFP4) ? accs * fac : accs;

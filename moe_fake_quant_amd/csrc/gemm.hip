@@ -179,22 +179,25 @@ __device__ __forceinline__ int expert_of_tile(const int *tile_start, int E, int 
 // holds: lane n = n0 + lane%32, k = k0 + 32s + 8q + 4(lane/32) + v for
 // acc[s][U][4q + v]. Each dWq element is weighted by its straight-through
 // factor and summed over its quantization group in a fixed order.
-template <int WFMT, int U>
-__device__ __forceinline__ void wgrad_epilogue(const GemmArgs &a, const f32x16 (&acc)[4][2], int e,
-                                               int k0, int n0, int lane) {
+// this lane's raw weights of the slab: k = k0 + 32s + 8q + 4h + v
+__device__ __forceinline__ void wgrad_load_w(const GemmArgs &a, int e, int k0, int n0, int lane,
+                                             uint2 (&wv)[4][4]) {
   const int n = n0 + (lane & 31);
   const int h = lane >> 5;
-  const int G = a.K / a.group;
-  const float g_e = (WFMT == FQ_FMT_NVFP4) ? a.gscale[e] : 1.0f;
   const uint16_t *wrow = a.w + ((size_t)e * a.N + n) * a.K;
-  const size_t srow = ((size_t)e * a.N + n) * G;
-  // this lane's raw weights of the slab: k = k0 + 32s + 8q + 4h + v
-  uint2 wv[4][4];
 #pragma unroll
   for (int s = 0; s < 4; ++s)
 #pragma unroll
     for (int q = 0; q < 4; ++q)
       wv[s][q] = *reinterpret_cast<const uint2 *>(wrow + k0 + s * 32 + 8 * q + 4 * h);
+}
+template <int WFMT, int U>
+__device__ __forceinline__ void wgrad_epilogue(const GemmArgs &a, const f32x16 (&acc)[4][2], int e,
+                                               int k0, int n0, int lane, const uint2 (&wv)[4][4]) {
+  const int n = n0 + (lane & 31);
+  const int G = a.K / a.group;
+  const float g_e = (WFMT == FQ_FMT_NVFP4) ? a.gscale[e] : 1.0f;
+  const size_t srow = ((size_t)e * a.N + n) * G;
   float part_s[4], part_z[4];
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
@@ -355,44 +358,67 @@ __device__ __forceinline__ bf16x8v zero_tail(bf16x8v f, int cfirst, int c_end) {
   return r;
 }
 
-// One 256 x 256 output tile: the contraction loop and the epilogue.
-template <int MODE, int WFMT>
-__device__ __forceinline__ void run_tile(const GemmArgs &a, int e, int i0, int j0, int j_end) {
-  const int t = threadIdx.x;
-  const int lane = t & 63, wave = t >> 6;
-  const int wi = wave & 1, wj = wave >> 1;  // 2 x 4 waves: 128 (i) x 64 (j) each
-  const int seg_lo = a.seg[e], seg_hi = a.seg[e + 1];
-  const int c_total = (MODE == WGRAD) ? seg_hi - seg_lo : (MODE == FWD) ? a.K : a.N;
+// One output tile: expert e, i range [i0, i0+256), j range [j0, j0+256)
+// (FWD / DGRAD: routed rows, valid below j_end).
+struct Tile {
+  int e, i0, j0, j_end;
+};
 
-  // operand bases (block-uniform)
-  const size_t NK = (size_t)a.N * a.K;
-  const char *pbase, *qbase;
-  if (MODE == FWD) {
-    pbase = reinterpret_cast<const char *>(a.p + e * NK);   // W_fq[e] [N][K], rows i = n
-    qbase = reinterpret_cast<const char *>(a.q);            // Xq rows (absolute)
-  } else if (MODE == DGRAD) {
-    pbase = reinterpret_cast<const char *>(a.p + e * NK);   // W_fq[e] as (c = n, idx = k)
-    qbase = reinterpret_cast<const char *>(a.q);            // dY rows (absolute)
+// Tile w of the list. FWD / DGRAD tiles: (row tile, i tile) with i fastest,
+// the row tiles of each expert from tile_start; WGRAD: (expert, j tile, i tile).
+template <int MODE>
+__device__ __forceinline__ Tile decode_tile(const GemmArgs &a, const int *tile_start, int w) {
+  Tile t;
+  t.j_end = 0;
+  if (MODE == WGRAD) {
+    const int per_e = a.n_it * a.n_jt;
+    t.e = w / per_e;
+    const int rem = w - t.e * per_e;
+    const int jt = rem / a.n_it;
+    t.i0 = (rem - jt * a.n_it) * BI;
+    t.j0 = jt * BJ;
   } else {
-    pbase = reinterpret_cast<const char *>(a.p + (size_t)seg_lo * a.K);  // Xq: (c = r, idx = k)
-    qbase = reinterpret_cast<const char *>(a.q + (size_t)seg_lo * a.N);  // dY: (c = r, idx = n)
+    const int tile = w / a.n_it;
+    t.i0 = (w - tile * a.n_it) * BI;
+    t.e = expert_of_tile(tile_start, a.E, tile);
+    t.j0 = a.seg[t.e] + (tile - tile_start[t.e]) * BJ;
+    t.j_end = a.seg[t.e + 1];
   }
+  return t;
+}
+
+// The operand streams of one tile: bases, per-lane offsets and the
+// contraction length. issue<S>(kt) loads stage kt into LDS buffer S.
+template <int MODE>
+struct TileLoads {
+  const char *pbase, *qbase;
+  int c_total, nk;
   NormalDMA pn, qn;
   TransDMA pt, qt;
-  if (MODE == FWD) {
-    pn.init(a.K, i0, a.N - 1, wave, lane);
-    qn.init(a.K, j0, j_end - 1, wave, lane);
-  } else if (MODE == DGRAD) {
-    pt.init(i0, wave, lane);
-    qn.init(a.N, j0, j_end - 1, wave, lane);
-  } else {
-    pt.init(i0, wave, lane);
-    qt.init(j0, wave, lane);
+  __device__ __forceinline__ TileLoads(const GemmArgs &a, const Tile &t, int wave, int lane) {
+    const int seg_lo = a.seg[t.e];
+    c_total = (MODE == WGRAD) ? a.seg[t.e + 1] - seg_lo : (MODE == FWD) ? a.K : a.N;
+    nk = (c_total + BK - 1) / BK;
+    const size_t NK = (size_t)a.N * a.K;
+    if (MODE == FWD) {
+      pbase = reinterpret_cast<const char *>(a.p + t.e * NK);  // W_fq[e] [N][K], rows i = n
+      qbase = reinterpret_cast<const char *>(a.q);             // Xq rows (absolute)
+      pn.init(a.K, t.i0, a.N - 1, wave, lane);
+      qn.init(a.K, t.j0, t.j_end - 1, wave, lane);
+    } else if (MODE == DGRAD) {
+      pbase = reinterpret_cast<const char *>(a.p + t.e * NK);  // W_fq[e] as (c = n, idx = k)
+      qbase = reinterpret_cast<const char *>(a.q);             // dY rows (absolute)
+      pt.init(t.i0, wave, lane);
+      qn.init(a.N, t.j0, t.j_end - 1, wave, lane);
+    } else {
+      pbase = reinterpret_cast<const char *>(a.p + (size_t)seg_lo * a.K);  // Xq: (c = r, idx = k)
+      qbase = reinterpret_cast<const char *>(a.q + (size_t)seg_lo * a.N);  // dY: (c = r, idx = n)
+      pt.init(t.i0, wave, lane);
+      qt.init(t.j0, wave, lane);
+    }
   }
-  const int nk = (c_total + BK - 1) / BK;
-
-  auto issue = [&](auto stage_tag, int kt) {
-    constexpr int S = decltype(stage_tag)::value;
+  template <int S>
+  __device__ __forceinline__ void issue(const GemmArgs &a, int kt, int wave) const {
     const int c0 = kt * BK;
     if (MODE == FWD) {
       pn.template issue<S>(pbase, stage_p<S>(), c0, wave);
@@ -404,6 +430,34 @@ __device__ __forceinline__ void run_tile(const GemmArgs &a, int e, int i0, int j
       pt.issue(pbase, a.K, stage_p<S>(), c0, c_total, wave);
       qt.issue(qbase, a.N, stage_q<S>(), c0, c_total, wave);
     }
+  }
+};
+
+// One 256 x 256 output tile: the contraction loop and the epilogue. If
+// `pre` is set, stage 0 of this tile is already in flight; if next_w >= 0,
+// stage 0 of tile next_w is issued once every wave is done with this tile's
+// LDS buffers, so that its loads run under this tile's epilogue.
+template <int MODE, int WFMT>
+__device__ __forceinline__ void run_tile(const GemmArgs &a, const int *tile_start, const Tile &tl,
+                                         bool pre, int next_w) {
+  const int t = threadIdx.x;
+  const int lane = t & 63, wave = t >> 6;
+  const int wi = wave & 1, wj = wave >> 1;  // 2 x 4 waves: 128 (i) x 64 (j) each
+  const int e = tl.e, i0 = tl.i0, j0 = tl.j0, j_end = tl.j_end;
+  const TileLoads<MODE> ld(a, tl, wave, lane);
+  const int c_total = ld.c_total, nk = ld.nk;
+
+  auto issue = [&](auto stage_tag, int kt) {
+    constexpr int S = decltype(stage_tag)::value;
+    ld.template issue<S>(a, kt, wave);
+  };
+  // stage 0 of the next tile, after every wave has left this tile's buffers
+  auto prefetch_next = [&]() {
+    if (next_w < 0) return;
+    block_barrier();
+    const Tile nt = decode_tile<MODE>(a, tile_start, next_w);
+    const TileLoads<MODE> nl(a, nt, wave, lane);
+    if (nl.nk > 0) nl.template issue<0>(a, 0, wave);
   };
 
   f32x16 acc[4][2];
@@ -468,7 +522,7 @@ __device__ __forceinline__ void run_tile(const GemmArgs &a, int e, int i0, int j
       mfmas(f);
     }
   };
-  if (nk > 0) issue(std::integral_constant<int, 0>{}, 0);
+  if (nk > 0 && !pre) issue(std::integral_constant<int, 0>{}, 0);
   for (int kt = 0; kt < nk; kt += NSTAGE) {
     step(std::integral_constant<int, 0>{}, kt);
     if (kt + 1 < nk) step(std::integral_constant<int, 1>{}, kt + 1);
@@ -477,6 +531,7 @@ __device__ __forceinline__ void run_tile(const GemmArgs &a, int e, int i0, int j
   // accumulator (s, u, v) of this lane: i = i0 + wi*128 + s*32 + 8*(v/4) + 4*(lane/32) + v%4,
   //                                     j = j0 + wj*64 + u*32 + lane%32
   if (MODE != WGRAD) {
+    prefetch_next();
     const int ldo = (MODE == FWD) ? a.N : a.K;
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
@@ -500,8 +555,12 @@ __device__ __forceinline__ void run_tile(const GemmArgs &a, int e, int i0, int j
   // ---- WGRAD epilogue: i = k, j = n of expert e. dS over groups along k.
   {
     const int k0 = i0 + wi * 128, n0 = j0 + wj * WJ_TILE;
-    wgrad_epilogue<WFMT, 0>(a, acc, e, k0, n0, lane);
-    wgrad_epilogue<WFMT, 1>(a, acc, e, k0, n0 + 32, lane);
+    uint2 wv[4][4];
+    wgrad_load_w(a, e, k0, n0, lane, wv);  // issued before the prefetch: its waits stay short
+    prefetch_next();
+    wgrad_epilogue<WFMT, 0>(a, acc, e, k0, n0, lane, wv);
+    wgrad_load_w(a, e, k0, n0 + 32, lane, wv);
+    wgrad_epilogue<WFMT, 1>(a, acc, e, k0, n0 + 32, lane, wv);
   }
 }
 
@@ -525,24 +584,11 @@ __global__ __launch_bounds__(NT) void k_grouped_gemm(GemmArgs a) {
   const int nslot = gridDim.x >> 3, xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
   const int chunk = (total + 7) >> 3;
   const int w_end = min((xcd + 1) * chunk, total);
+  bool pre = false;
   for (int w = xcd * chunk + slot; w < w_end; w += nslot) {
-    int e, i0, j0, j_end = 0;
-    if (MODE == WGRAD) {
-      const int per_e = a.n_it * a.n_jt;
-      e = w / per_e;
-      const int rem = w - e * per_e;
-      const int jt = rem / a.n_it;
-      i0 = (rem - jt * a.n_it) * BI;
-      j0 = jt * BJ;
-    } else {
-      const int tile = w / a.n_it;
-      i0 = (w - tile * a.n_it) * BI;
-      e = expert_of_tile(tile_start, a.E, tile);
-      j0 = a.seg[e] + (tile - tile_start[e]) * BJ;
-      j_end = a.seg[e + 1];
-    }
-    run_tile<MODE, WFMT>(a, e, i0, j0, j_end);
-    __syncthreads();  // the next tile reuses the LDS buffers
+    const int next = w + nslot < w_end ? w + nslot : -1;
+    run_tile<MODE, WFMT>(a, tile_start, decode_tile<MODE>(a, tile_start, w), pre, next);
+    pre = next >= 0;
   }
 }
 

@@ -99,7 +99,12 @@ size_t gemm_ws(int op, fq_shape s, int R_max, int fmts) {
   size_t b = 0;
   if (wfmt != FQ_FMT_NONE) b += align_up((size_t)s.E * s.N * s.K * 2);
   if (afmt != FQ_FMT_NONE) b += align_up((size_t)R_max * s.K * 2);
-  if (op == FQ_OP_GEMM_BWD) b += 2 * align_up((size_t)s.E * s.N * (s.K / 128 + 1) * 4);
+  if (op == FQ_OP_GEMM_BWD) {
+    // dScale partials per row chunk and 16-block (the finest group), for the
+    // scale and the zero point, and the chunk prefix
+    b += 2 * align_up(wgrad_max_chunks(s.E, R_max) * s.N * (s.K / 16) * 4);
+    b += align_up((size_t)(s.E + 1) * 4);
+  }
   return b;
 }
 
@@ -270,19 +275,11 @@ fq_status fq_grouped_gemm_bwd_scale(const uint16_t *dy, const uint16_t *x, int32
       launch_act_fq(x, R_max, s.K, seg + s.E, afmt, aq->scale, t, st);
       xq = t;
     }
-    const size_t nsc = (size_t)s.E * s.N * (s.K / wq->group);
-    float *ds_out = dscale;
-    float *ps = nullptr, *pz = nullptr;
-    const int P = wq->group / 128;
-    if (wq->group > 128) {
-      ps = c.take<float>((size_t)s.E * s.N * (s.K / 128) * 4);
-      if (dzp) pz = c.take<float>((size_t)s.E * s.N * (s.K / 128) * 4);
-    }
-    launch_gemm_wgrad_dscale(dy, xq, seg, s, w, *wq, ds_out, dzp, ps, pz, st);
-    if (wq->group > 128) {
-      launch_reduce_partials(ps, P, nsc, ds_out, st);
-      if (dzp) launch_reduce_partials(pz, P, nsc, dzp, st);
-    }
+    const size_t part = wgrad_max_chunks(s.E, R_max) * s.N * (s.K / 16) * 4;
+    float *ps = c.take<float>(part);
+    float *pz = c.take<float>(part);
+    int *cs = c.take<int>((size_t)(s.E + 1) * 4);
+    launch_gemm_wgrad_dscale(dy, xq, seg, s, w, *wq, dscale, dzp, ps, dzp ? pz : nullptr, cs, st);
   }
   FQ_CHECK_LAUNCH("fq_grouped_gemm_bwd_scale");
   return FQ_OK;

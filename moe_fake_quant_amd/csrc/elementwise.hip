@@ -571,16 +571,6 @@ __global__ __launch_bounds__(kThreads) void k_unpermute_reduce(
   }
 }
 
-// out[i] = sum_p part[i * P + p] in order p = 0..P-1
-__global__ void k_reduce_partials(const float *__restrict__ part, int P, uint32_t n,
-                                  float *__restrict__ out) {
-  for (uint32_t i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) {
-    float s = 0.0f;
-    for (int p = 0; p < P; ++p) s += part[(size_t)i * P + p];
-    out[i] = s;
-  }
-}
-
 }  // namespace
 
 // ========================================================= launchers =======
@@ -736,10 +726,5 @@ void launch_unpermute_reduce(const uint16_t *dxq, const int32_t *row_of, const u
                      reinterpret_cast<bf16x8_t *>(dx));
 }
 
-void launch_reduce_partials(const float *part, int P, size_t n, float *out, hipStream_t st) {
-  if (!n) return;
-  hipLaunchKernelGGL(k_reduce_partials, dim3(grid_for((long)n)), dim3(kThreads), 0, st, part, P,
-                     (uint32_t)n, out);
-}
 
 }  // namespace fq

@@ -127,20 +127,30 @@ struct GemmArgs {
   const uint16_t *w;   // raw weights [E,N,K]
   int wfmt, group;
   const float *scale, *zero_point, *gscale;
-  float *dscale, *dzp;     // final outputs (group <= 128), or NULL
-  float *pscale, *pzp;     // partials per 128-chunk of K (group > 128), or NULL
+  float *dscale, *dzp;     // final outputs [E, N, K/group]
+  // Row chunks: the contraction over an expert's rows is split into chunks of
+  // at most chunk_rows rows (every expert has at least one). An expert with
+  // one chunk and group <= 128 writes dScale directly; otherwise each chunk
+  // writes partial sums per block of min(group, 128) along K to
+  // part_s / part_z [chunk, N, K / block], summed afterwards in chunk order.
+  int chunk_rows;
+  float *part_s, *part_z;
+  int *chunk_start_out;    // [E+1] chunk prefix, written by block 0
 };
 
 constexpr int kMaxExperts = 1024;
 
-// tile_start[e] = number of BJ-row tiles of experts 0..e-1 (e = 0..E), from
-// seg_offsets on the device: a block-wide exclusive scan in LDS.
-__device__ void build_tile_prefix(const int32_t *seg, int E, int *tile_start) {
+// tile_start[e] = number of work units of experts 0..e-1 (e = 0..E), from
+// seg_offsets on the device: a block-wide exclusive scan in LDS. Units per
+// expert: ceil(rows / rows_per_unit), at least min_units.
+__device__ void build_tile_prefix(const int32_t *seg, int E, int rows_per_unit, int min_units,
+                                  int *tile_start) {
   __shared__ int s_wsum[NT / 64];
   int base = 0;
   for (int e0 = 0; e0 < E; e0 += NT) {
     const int e = e0 + threadIdx.x;
-    const int nt = e < E ? (seg[e + 1] - seg[e] + BJ - 1) / BJ : 0;
+    const int nt =
+        e < E ? max((seg[e + 1] - seg[e] + rows_per_unit - 1) / rows_per_unit, min_units) : 0;
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     int x = nt;
 #pragma unroll
@@ -191,13 +201,20 @@ __device__ __forceinline__ void wgrad_load_w(const GemmArgs &a, int e, int k0, i
     for (int q = 0; q < 4; ++q)
       wv[s][q] = *reinterpret_cast<const uint2 *>(wrow + k0 + s * 32 + 8 * q + 4 * h);
 }
+// `chunk` < 0: this tile's dScale sums are final and go to dscale / dzp;
+// otherwise they are partials of row chunk `chunk` (blocks of min(group, 128)).
 template <int WFMT, int U>
 __device__ __forceinline__ void wgrad_epilogue(const GemmArgs &a, const f32x16 (&acc)[4][2], int e,
-                                               int k0, int n0, int lane, const uint2 (&wv)[4][4]) {
+                                               int k0, int n0, int lane, const uint2 (&wv)[4][4],
+                                               int chunk) {
   const int n = n0 + (lane & 31);
   const int G = a.K / a.group;
   const float g_e = (WFMT == FQ_FMT_NVFP4) ? a.gscale[e] : 1.0f;
   const size_t srow = ((size_t)e * a.N + n) * G;
+  const int blk = a.group < 128 ? a.group : 128;
+  const size_t orow = chunk < 0 ? srow : ((size_t)chunk * a.N + n) * (a.K / blk);
+  float *ds_out = chunk < 0 ? a.dscale : a.part_s;
+  float *dz_out = chunk < 0 ? a.dzp : a.part_z;
   float part_s[4], part_z[4];
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
@@ -241,11 +258,11 @@ __device__ __forceinline__ void wgrad_epilogue(const GemmArgs &a, const f32x16 (
     }
     if (a.group == 16 && lane < 32) {
       const int kb = (k0 + s * 32) / 16;
-      a.dscale[srow + kb] = ps16[0];
-      a.dscale[srow + kb + 1] = ps16[1];
-      if (WFMT == FQ_FMT_INT4 && a.dzp) {
-        a.dzp[srow + kb] = pz16[0];
-        a.dzp[srow + kb + 1] = pz16[1];
+      ds_out[orow + kb] = ps16[0];
+      ds_out[orow + kb + 1] = ps16[1];
+      if (WFMT == FQ_FMT_INT4 && dz_out) {
+        dz_out[orow + kb] = pz16[0];
+        dz_out[orow + kb + 1] = pz16[1];
       }
     }
     part_s[s] = ps16[0] + ps16[1];
@@ -256,28 +273,22 @@ __device__ __forceinline__ void wgrad_epilogue(const GemmArgs &a, const f32x16 (
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
         const int kb = (k0 + s * 32) / 32;
-        a.dscale[srow + kb] = part_s[s];
-        if (WFMT == FQ_FMT_INT4 && a.dzp) a.dzp[srow + kb] = part_z[s];
+        ds_out[orow + kb] = part_s[s];
+        if (WFMT == FQ_FMT_INT4 && dz_out) dz_out[orow + kb] = part_z[s];
       }
     } else if (a.group == 64) {
 #pragma unroll
       for (int h2 = 0; h2 < 2; ++h2) {
         const int kb = (k0 + h2 * 64) / 64;
-        a.dscale[srow + kb] = part_s[2 * h2] + part_s[2 * h2 + 1];
-        if (WFMT == FQ_FMT_INT4 && a.dzp) a.dzp[srow + kb] = part_z[2 * h2] + part_z[2 * h2 + 1];
+        ds_out[orow + kb] = part_s[2 * h2] + part_s[2 * h2 + 1];
+        if (WFMT == FQ_FMT_INT4 && dz_out) dz_out[orow + kb] = part_z[2 * h2] + part_z[2 * h2 + 1];
       }
-    } else {
+    } else {  // group 128 (final or partial) or a 128-block of a longer group (partial)
       const float s128 = (part_s[0] + part_s[1]) + (part_s[2] + part_s[3]);
       const float z128 = (part_z[0] + part_z[1]) + (part_z[2] + part_z[3]);
       const int kb = k0 / 128;
-      if (a.group == 128) {
-        a.dscale[srow + kb] = s128;
-        if (WFMT == FQ_FMT_INT4 && a.dzp) a.dzp[srow + kb] = z128;
-      } else {
-        const size_t prow = ((size_t)e * a.N + n) * (a.K / 128);
-        a.pscale[prow + kb] = s128;
-        if (WFMT == FQ_FMT_INT4 && a.pzp) a.pzp[prow + kb] = z128;
-      }
+      ds_out[orow + kb] = s128;
+      if (WFMT == FQ_FMT_INT4 && dz_out) dz_out[orow + kb] = z128;
     }
   }
 }
@@ -362,6 +373,8 @@ __device__ __forceinline__ bf16x8v zero_tail(bf16x8v f, int cfirst, int c_end) {
 // (FWD / DGRAD: routed rows, valid below j_end).
 struct Tile {
   int e, i0, j0, j_end;
+  int r0, r1;  // WGRAD: the routed rows [r0, r1) of this row chunk
+  int chunk;   // WGRAD: -1 = dScale written directly, else the partial row
 };
 
 // Tile w of the list. FWD / DGRAD tiles: (row tile, i tile) with i fastest,
@@ -370,13 +383,21 @@ template <int MODE>
 __device__ __forceinline__ Tile decode_tile(const GemmArgs &a, const int *tile_start, int w) {
   Tile t;
   t.j_end = 0;
+  t.chunk = -1;
   if (MODE == WGRAD) {
-    const int per_e = a.n_it * a.n_jt;
-    t.e = w / per_e;
-    const int rem = w - t.e * per_e;
+    // unit (row chunk c, j tile, i tile); tile_start holds the chunk prefix
+    const int per_c = a.n_it * a.n_jt;
+    const int c = w / per_c;
+    const int rem = w - c * per_c;
     const int jt = rem / a.n_it;
     t.i0 = (rem - jt * a.n_it) * BI;
     t.j0 = jt * BJ;
+    t.e = expert_of_tile(tile_start, a.E, c);
+    const int lc = c - tile_start[t.e];
+    t.r0 = a.seg[t.e] + lc * a.chunk_rows;
+    t.r1 = min(t.r0 + a.chunk_rows, a.seg[t.e + 1]);
+    const bool single = tile_start[t.e + 1] - tile_start[t.e] == 1;
+    t.chunk = (single && a.group <= 128) ? -1 : c;
   } else {
     const int tile = w / a.n_it;
     t.i0 = (w - tile * a.n_it) * BI;
@@ -396,8 +417,8 @@ struct TileLoads {
   NormalDMA pn, qn;
   TransDMA pt, qt;
   __device__ __forceinline__ TileLoads(const GemmArgs &a, const Tile &t, int wave, int lane) {
-    const int seg_lo = a.seg[t.e];
-    c_total = (MODE == WGRAD) ? a.seg[t.e + 1] - seg_lo : (MODE == FWD) ? a.K : a.N;
+    const int seg_lo = (MODE == WGRAD) ? t.r0 : 0;
+    c_total = (MODE == WGRAD) ? t.r1 - t.r0 : (MODE == FWD) ? a.K : a.N;
     nk = (c_total + BK - 1) / BK;
     const size_t NK = (size_t)a.N * a.K;
     if (MODE == FWD) {
@@ -558,9 +579,9 @@ __device__ __forceinline__ void run_tile(const GemmArgs &a, const int *tile_star
     uint2 wv[4][4];
     wgrad_load_w(a, e, k0, n0, lane, wv);  // issued before the prefetch: its waits stay short
     prefetch_next();
-    wgrad_epilogue<WFMT, 0>(a, acc, e, k0, n0, lane, wv);
+    wgrad_epilogue<WFMT, 0>(a, acc, e, k0, n0, lane, wv, tl.chunk);
     wgrad_load_w(a, e, k0, n0 + 32, lane, wv);
-    wgrad_epilogue<WFMT, 1>(a, acc, e, k0, n0 + 32, lane, wv);
+    wgrad_epilogue<WFMT, 1>(a, acc, e, k0, n0 + 32, lane, wv, tl.chunk);
   }
 }
 
@@ -576,9 +597,12 @@ __global__ __launch_bounds__(NT) void k_grouped_gemm(GemmArgs a) {
   __shared__ int tile_start[kMaxExperts + 1];
   int total;
   if (MODE == WGRAD) {
-    total = a.E * a.n_it * a.n_jt;
+    build_tile_prefix(a.seg, a.E, a.chunk_rows, 1, tile_start);
+    total = tile_start[a.E] * a.n_it * a.n_jt;
+    if (blockIdx.x == 0 && a.chunk_start_out)
+      for (int e = threadIdx.x; e <= a.E; e += NT) a.chunk_start_out[e] = tile_start[e];
   } else {
-    build_tile_prefix(a.seg, a.E, tile_start);
+    build_tile_prefix(a.seg, a.E, BJ, 0, tile_start);
     total = tile_start[a.E] * a.n_it;
   }
   const int nslot = gridDim.x >> 3, xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
@@ -589,6 +613,39 @@ __global__ __launch_bounds__(NT) void k_grouped_gemm(GemmArgs a) {
     const int next = w + nslot < w_end ? w + nslot : -1;
     run_tile<MODE, WFMT>(a, tile_start, decode_tile<MODE>(a, tile_start, w), pre, next);
     pre = next >= 0;
+  }
+}
+
+// dscale[e, n, g] = sum over the row chunks c of expert e (in order) of the
+// sums over the blocks b of group g (in order) of part[c, n, b]; experts
+// whose dScale the GEMM wrote directly are skipped. Grid: (N*G / (256*4), E),
+// 4 outputs a block stride apart per thread.
+__global__ __launch_bounds__(256) void k_reduce_dscale(const float *__restrict__ part_s,
+                                                       const float *__restrict__ part_z,
+                                                       const int *__restrict__ chunk_start, int N,
+                                                       int K, int group, float *__restrict__ dscale,
+                                                       float *__restrict__ dzp) {
+  const int e = blockIdx.y;
+  const int c0 = chunk_start[e], c1 = chunk_start[e + 1];
+  if (c1 - c0 == 1 && group <= 128) return;
+  const int blk = group < 128 ? group : 128;
+  const int G = K / group, Gb = K / blk, per = group / blk;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int i = (blockIdx.x * 4 + u) * blockDim.x + threadIdx.x;  // n * G + g
+    if (i >= N * G) return;
+    const int n = i / G, g = i - n * G;
+    float acc_s = 0.0f, acc_z = 0.0f;
+    for (int c = c0; c < c1; ++c) {
+      const size_t base = ((size_t)c * N + n) * Gb + (size_t)g * per;
+      for (int b = 0; b < per; ++b) {
+        acc_s += part_s[base + b];
+        if (dzp) acc_z += part_z[base + b];
+      }
+    }
+    const size_t o = (size_t)e * N * G + i;
+    dscale[o] = acc_s;
+    if (dzp) dzp[o] = acc_z;
   }
 }
 
@@ -634,9 +691,13 @@ void launch_gemm_dgrad(const uint16_t *dy, int R_max, const int32_t *seg, fq_sha
   hipLaunchKernelGGL((k_grouped_gemm<DGRAD, 0>), dim3(persistent_grid()), dim3(NT), 0, st, a);
 }
 
+size_t wgrad_max_chunks(int E, int R_max) {
+  return (size_t)(R_max + kWgradChunkRows - 1) / kWgradChunkRows + E;
+}
+
 void launch_gemm_wgrad_dscale(const uint16_t *dy, const uint16_t *xq, const int32_t *seg, fq_shape s,
                               const uint16_t *w, const fq_weight_q &q, float *dscale, float *dzp,
-                              float *pscale, float *pzp, hipStream_t st) {
+                              float *part_s, float *part_z, int *chunk_start, hipStream_t st) {
   GemmArgs a{};
   a.p = xq;
   a.q = dy;
@@ -654,8 +715,10 @@ void launch_gemm_wgrad_dscale(const uint16_t *dy, const uint16_t *xq, const int3
   a.gscale = q.global_scale;
   a.dscale = dscale;
   a.dzp = dzp;
-  a.pscale = pscale;
-  a.pzp = pzp;
+  a.chunk_rows = kWgradChunkRows;
+  a.part_s = part_s;
+  a.part_z = part_z;
+  a.chunk_start_out = chunk_start;
   dim3 grid(persistent_grid()), block(NT);
   switch (q.fmt) {
     case FQ_FMT_INT8: hipLaunchKernelGGL((k_grouped_gemm<WGRAD, FQ_FMT_INT8>), grid, block, 0, st, a); break;
@@ -665,6 +728,9 @@ void launch_gemm_wgrad_dscale(const uint16_t *dy, const uint16_t *xq, const int3
       break;
     default: hipLaunchKernelGGL((k_grouped_gemm<WGRAD, FQ_FMT_NVFP4>), grid, block, 0, st, a); break;
   }
+  const int G = s.K / q.group;
+  hipLaunchKernelGGL(k_reduce_dscale, dim3(ceil_div((long)s.N * G, 256 * 4), s.E), dim3(256), 0, st,
+                     part_s, part_z, chunk_start, s.N, s.K, q.group, dscale, dzp);
 }
 
 }  // namespace fq

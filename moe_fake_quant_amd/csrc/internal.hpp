@@ -30,7 +30,6 @@ void launch_combine_bwd(const uint16_t *dout, const float *probs, const int32_t 
 void launch_unpermute_reduce(const uint16_t *dxq, const int32_t *row_of, const uint16_t *x, int T,
                              int topk, int H, int afmt, const float *ascale, uint16_t *dx,
                              hipStream_t st);
-void launch_reduce_partials(const float *part, int P, size_t n, float *out, hipStream_t st);
 
 size_t permute_workspace_bytes(int E, long P);
 void launch_permute(const int32_t *ids, int T, int topk, int ebegin, int E, int32_t *perm,
@@ -40,8 +39,15 @@ void launch_gemm_fwd(const uint16_t *xq, int R_max, const int32_t *seg, fq_shape
                      const uint16_t *wfq, uint16_t *y, hipStream_t st);
 void launch_gemm_dgrad(const uint16_t *dy, int R_max, const int32_t *seg, fq_shape s,
                        const uint16_t *wfq, uint16_t *dx, hipStream_t st);
+// The wgrad contraction over an expert's rows runs in chunks of at most this
+// many rows, so that one hot expert cannot serialize the grid.
+constexpr int kWgradChunkRows = 2048;
+// chunks over all experts for at most R_max routed rows
+size_t wgrad_max_chunks(int E, int R_max);
+// part_s / part_z: [wgrad_max_chunks, N, K / min(group, 128)] fp32 scratch;
+// chunk_start: [E+1] int scratch. dzp / part_z only for int4.
 void launch_gemm_wgrad_dscale(const uint16_t *dy, const uint16_t *xq, const int32_t *seg, fq_shape s,
                               const uint16_t *w, const fq_weight_q &q, float *dscale, float *dzp,
-                              float *pscale, float *pzp, hipStream_t st);
+                              float *part_s, float *part_z, int *chunk_start, hipStream_t st);
 
 }  // namespace fq

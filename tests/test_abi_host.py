@@ -103,9 +103,12 @@ def test_workspace_sizes(pkg):
     assert _ws(pkg, pkg.FQ_OP_GEMM_FWD, (E, N, K), R, pkg.FMT_NVFP4) == _up(E * N * K * 2)
     assert _ws(pkg, pkg.FQ_OP_GEMM_FWD, (E, N, K), R, pkg.FMT_NVFP4, pkg.FMT_FP8_E4M3) == \
         _up(E * N * K * 2) + _up(R * K * 2)
-    # backward adds two fp32 partial buffers per 128-chunk of K
-    part = _up(E * N * (K // 128 + 1) * 4)
-    assert _ws(pkg, pkg.FQ_OP_GEMM_BWD, (E, N, K), R) == 2 * part
+    # backward: dScale partials (scale and zero point) per wgrad row chunk of
+    # at most 2048 rows (every expert has at least one) and 16-block of K,
+    # plus the chunk prefix
+    chunks = (R + 2047) // 2048 + E
+    part = _up(chunks * N * (K // 16) * 4)
+    assert _ws(pkg, pkg.FQ_OP_GEMM_BWD, (E, N, K), R) == 2 * part + _up((E + 1) * 4)
     # permute: grows with the pair count, positive for any expert count
     a = _ws(pkg, pkg.FQ_OP_PERMUTE, (4, 0, 0), 1000)
     b = _ws(pkg, pkg.FQ_OP_PERMUTE, (4, 0, 0), 100000)

@@ -425,12 +425,19 @@ __global__ __launch_bounds__(kThreads) void k_gather_actfq(
   }
 }
 
-// SwiGLU value of 16 elements in fp32, rounded to bf16 (the stored A).
-__device__ __forceinline__ void swiglu16(const float *g, const float *u, float *a) {
+// sigmoid(g) = 1 / (1 + exp(-g)) on the hardware exp and reciprocal (a few
+// ulp; 0 and 1 at the extremes). The forward and the backward both call it,
+// so the backward sees exactly the forward's A.
+__device__ __forceinline__ float sigmoid_hw(float g) {
+  return __builtin_amdgcn_rcpf(1.0f + __expf(-g));
+}
+// SwiGLU value of 16 elements in fp32, silu(g) = g * sigmoid(g), rounded to
+// bf16 (the stored A); sig receives sigmoid(g).
+__device__ __forceinline__ void swiglu16(const float *g, const float *u, float *a, float *sig) {
 #pragma unroll
   for (int j = 0; j < 16; ++j) {
-    float sg = g[j] / (1.0f + expf(-g[j]));
-    a[j] = bf16_to_f32(f32_to_bf16(sg * u[j]));
+    sig[j] = sigmoid_hw(g[j]);
+    a[j] = bf16_to_f32(f32_to_bf16((g[j] * sig[j]) * u[j]));
   }
 }
 
@@ -446,10 +453,10 @@ __global__ __launch_bounds__(kThreads) void k_swiglu_actfq(
     uint32_t r = chunks_per_row.div(c);
     uint32_t cc = c - r * cpr;
     const bf16x8_t *hr = h + 2 * ((size_t)r * 2 * cpr);
-    float g[16], u[16], a[16];
+    float g[16], u[16], a[16], sg[16];
     load16(hr + 2 * cc, g);
     load16(hr + 2 * (cpr + cc), u);
-    swiglu16(g, u, a);
+    swiglu16(g, u, a, sg);
     if (a_out) store16(a_out + 2 * (size_t)c, a);
     act_fq16(q, a);
     store16(aq_out + 2 * (size_t)c, a);
@@ -468,16 +475,16 @@ __global__ __launch_bounds__(kThreads) void k_swiglu_bwd(
     uint32_t r = chunks_per_row.div(c);
     uint32_t cc = c - r * cpr;
     const bf16x8_t *hr = h + 2 * ((size_t)r * 2 * cpr);
-    float g[16], u[16], a[16], d[16], dg[16], du[16];
+    float g[16], u[16], a[16], sg[16], d[16], dg[16], du[16];
     load16(hr + 2 * cc, g);
     load16(hr + 2 * (cpr + cc), u);
-    swiglu16(g, u, a);
+    swiglu16(g, u, a, sg);
     uint32_t m = act_fq16(q, a);
     load16(daq + 2 * (size_t)c, d);
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
-      float da = ((m >> j) & 1u) ? d[j] : 0.0f;
-      float s = 1.0f / (1.0f + expf(-g[j]));
+      const float da = ((m >> j) & 1u) ? d[j] : 0.0f;
+      const float s = sg[j];
       dg[j] = da * u[j] * s * (1.0f + g[j] * (1.0f - s));
       du[j] = da * g[j] * s;
     }

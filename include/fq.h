@@ -205,9 +205,12 @@ fq_status fq_grouped_gemm_fwd(const uint16_t *x_bf16, int32_t R_max, const int32
  *   dzero_point[e,n,g]= sum_{k in g} dWq_e[n,k] * dv/dzp(e,n,k)  (int4)
  * dx, dscale, dzero_point may each be NULL (not computed). dscale is
  * overwritten (not accumulated); experts without rows get 0. dScale is
- * reduced in a fixed order (no float atomics).
+ * reduced in a fixed order (no float atomics): an expert's rows are
+ * contracted in chunks of at most 2048, each chunk's partial sums summed in
+ * chunk order.
  *   dy_bf16 [R_max, N]; x_bf16 [R_max, K] raw (pre activation fake-quant).
- * Requires N % 64 == 0 and K % 256 == 0.
+ * Requires N % 256 == 0 and K % 256 == 0; for dScale a group of 16, 32, 64
+ * or a multiple of 128, and (nvfp4) theta 16-byte aligned.
  * Workspace: fq_workspace_bytes(FQ_OP_GEMM_BWD, shape, R_max, wq->fmt | aq->fmt << 8).
  * ---------------------------------------------------------------------- */
 fq_status fq_grouped_gemm_bwd_scale(const uint16_t *dy_bf16, const uint16_t *x_bf16,

@@ -247,6 +247,8 @@ fq_status fq_grouped_gemm_bwd_scale(const uint16_t *dy, const uint16_t *x, int32
                      "operands must stay below 4 GiB (32-bit tile offsets)");
   FQ_CHECK_SUPPORTED(!want_ds || group_ok_for_dscale(wq->group),
                      "dScale needs group 16, 32, 64 or a multiple of 128 (group=%d)", wq->group);
+  FQ_CHECK_ARG(!want_ds || wq->fmt != FQ_FMT_NVFP4 || aligned16(wq->scale),
+               "nvfp4 theta must be 16-byte aligned");
   FQ_CHECK_ARG((!dy || aligned16(dy)) && (!x || aligned16(x)) && aligned16(w) &&
                    (!w_fq || aligned16(w_fq)) && (!dx || aligned16(dx)),
                "bf16 tensors must be 16-byte aligned");

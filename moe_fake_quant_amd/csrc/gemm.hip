@@ -134,6 +134,7 @@ struct GemmArgs {
   // writes partial sums per block of min(group, 128) along K to
   // part_s / part_z [chunk, N, K / block], summed afterwards in chunk order.
   int chunk_rows;
+  FastDiv gdiv16;          // division by group / 16
   float *part_s, *part_z;
   int *chunk_start_out;    // [E+1] chunk prefix, written by block 0
 };
@@ -215,22 +216,45 @@ __device__ __forceinline__ void wgrad_epilogue(const GemmArgs &a, const f32x16 (
   const size_t orow = chunk < 0 ? srow : ((size_t)chunk * a.N + n) * (a.K / blk);
   float *ds_out = chunk < 0 ? a.dscale : a.part_s;
   float *dz_out = chunk < 0 ? a.dzp : a.part_z;
+  // scale, reciprocal, theta factor and zero point of this lane's eight
+  // 16-blocks k0 + 16 j (every group is a multiple of 16 long)
+  float sc8[8], r8[8], fac8[8], zp8[8];
+  if (WFMT == FQ_FMT_NVFP4) {
+    // theta of the eight blocks in two 16-byte loads, rounded to E4M3 two at a time
+    const float4 *tp = reinterpret_cast<const float4 *>(a.scale + srow + k0 / 16);
+    const float4 t0 = tp[0], t1 = tp[1];
+    const float th[8] = {t0.x, t0.y, t0.z, t0.w, t1.x, t1.y, t1.z, t1.w};
+#pragma unroll
+    for (int j = 0; j < 8; j += 2) {
+      float v0, v1;
+      e4m3_pair(fminf(fmaxf(th[j], 0.0f), kE4M3Max), fminf(fmaxf(th[j + 1], 0.0f), kE4M3Max), v0, v1);
+      sc8[j] = v0 * g_e;
+      sc8[j + 1] = v1 * g_e;
+      fac8[j] = nvfp4_theta_factor(th[j], g_e);
+      fac8[j + 1] = nvfp4_theta_factor(th[j + 1], g_e);
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint32_t gi = a.gdiv16.div((uint32_t)(k0 / 16 + j));
+      sc8[j] = a.scale[srow + gi];
+      if (WFMT == FQ_FMT_INT4) zp8[j] = fminf(fmaxf(rintf(a.zero_point[srow + gi]), 0.0f), 15.0f);
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    r8[j] = safe_recip(sc8[j]);
+    if (WFMT != FQ_FMT_INT4) zp8[j] = 0.0f;
+    if (WFMT != FQ_FMT_NVFP4) fac8[j] = 1.0f;
+  }
   float part_s[4], part_z[4];
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
     float ps16[2], pz16[2];  // the sub-tile's two 16-blocks
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
-      // every group is a multiple of 16 long: one scale per 16-block
-      const int gi = (k0 + s * 32 + 16 * b) / a.group;
-      float sc = a.scale[srow + gi];
-      float zpi = 0.0f, fac = 1.0f;
-      if (WFMT == FQ_FMT_INT4) zpi = fminf(fmaxf(rintf(a.zero_point[srow + gi]), 0.0f), 15.0f);
-      if (WFMT == FQ_FMT_NVFP4) {
-        fac = nvfp4_theta_factor(sc, g_e);
-        sc = nvfp4_block_scale(sc, g_e);
-      }
-      const float r = safe_recip(sc);
+      const float sc = sc8[2 * s + b], r = r8[2 * s + b], zpi = zp8[2 * s + b];
+      const float fac = fac8[2 * s + b];
       float accs = 0.0f, accz = 0.0f;
 #pragma unroll
       for (int qq = 0; qq < 2; ++qq) {
@@ -243,8 +267,8 @@ __device__ __forceinline__ void wgrad_epilogue(const GemmArgs &a, const f32x16 (
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
           const float d = acc[s][U][4 * q + v];
-          accs += d * phi[v];
-          if (WFMT == FQ_FMT_INT4) accz += d * dzp[v];
+          accs = fmaf(d, phi[v], accs);
+          if (WFMT == FQ_FMT_INT4) accz = fmaf(d, dzp[v], accz);
         }
       }
       ps16[b] = (WFMT == FQ_FMT_NVFP4) ? accs * fac : accs;
@@ -716,6 +740,7 @@ void launch_gemm_wgrad_dscale(const uint16_t *dy, const uint16_t *xq, const int3
   a.dscale = dscale;
   a.dzp = dzp;
   a.chunk_rows = kWgradChunkRows;
+  a.gdiv16 = FastDiv((uint32_t)(q.group / 16));
   a.part_s = part_s;
   a.part_z = part_z;
   a.chunk_start_out = chunk_start;

@@ -45,6 +45,10 @@ reading where it applies:
   R-16 chained tests feed the GPU-calibrated activation scales to the oracle
   R-17 MoE weights drawn N(0, 0.02)
   R-18 the skewed local-share workload forces experts {3, 7, 11, 15} empty
+  R-19 a learnable activation scale exists for the static per-tensor formats
+       (FP8, INT8) only; its gradient uses the weights' STE factor, summed
+       over every element the quantizer saw in the step. NVFP4 activations
+       derive their block scales from the data and keep g_a at calibration.
 
 Parity status: every function here is pinned by the ``-m "not gpu"`` tests
 (exhaustive code grids, tie tables, library special cases, closed forms,
@@ -65,5 +69,5 @@ from .permute import moe_permute  # noqa: F401
 from .gemm import grouped_gemm_fwd, grouped_gemm_bwd  # noqa: F401
 from .moe import (  # noqa: F401
     gather_actfq, swiglu_fwd, swiglu_actfq, swiglu_bwd, combine, combine_bwd,
-    unpermute_reduce, moe_layer,
+    unpermute_reduce, unpermute_sum, act_scale_grad, moe_layer,
 )

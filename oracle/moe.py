@@ -15,19 +15,22 @@ Forward, per routed row r of expert e (token t = perm[r] // k):
   Aq    = FQ_a2(A)
   O     = Aq . FQ(W_d[e])^T                             bf16
   out[t] = bf16(sum_j p[t,j] * O[row_of[t,j]])           slots ascending
-Backward (dX and the weight-scale gradients only; activation scales frozen):
+Backward (dX and the weight-scale gradients; activation scales frozen unless
+learnable, R-19):
   dO[r]  = bf16(p[t,j] * dOut[t])
   dA     = bf16(m_a2 * (dO . FQ(W_d[e])))               + dS_d from dO^T . Aq
   dH     = bf16(SwiGLU'(H) applied to dA)
   dXq    = bf16(dH . FQ(W_gu[e]))                       + dS_gu from dH^T . Xq
   dX[t]  = bf16(m_a1(X[t]) * sum_j dXq[row_of[t,j]])
+  dS_a1  = sum over t, h of (sum_j dXq[row_of[t,j], h]) * dv/ds(X[t, h])  (R-19)
+  dS_a2  = sum over r, f of dAq[r, f] * dv/ds(A[r, f])
 Float64 everywhere except where the GPU stores bf16.
 """
 from __future__ import annotations
 
 import numpy as np
 
-from .codecs import FMT_NONE, fq_act
+from .codecs import FMT_FP8, FMT_INT8, FMT_NONE, fq_act
 from .gemm import grouped_gemm_bwd, grouped_gemm_fwd
 from .numerics import bf16_to_f32, f64_to_bf16
 from .observer import observer_act, observer_weight
@@ -99,8 +102,9 @@ def combine_bwd(dout_bits, probs, perm, topk: int):
     return f64_to_bf16(d * p[:, None])
 
 
-def unpermute_reduce(dxq_bits, row_of, x_bits, afmt: int, act_scale):
-    """dX[t] = bf16(m_a1(X[t]) * sum over local slots of dXq[row_of[t,j]])."""
+def unpermute_sum(dxq_bits, row_of):
+    """The gradient reaching FQ_a1(X[t]): sum over local slots of dXq[row_of[t,j]]
+    (float64; tokens routed to no local expert get 0)."""
     dxq = bf16_to_f32(dxq_bits).astype(np.float64)
     row_of = np.asarray(row_of, dtype=np.int64)
     T, k = row_of.shape
@@ -109,25 +113,51 @@ def unpermute_reduce(dxq_bits, row_of, x_bits, afmt: int, act_scale):
         r = row_of[:, j]
         ok = r >= 0
         acc[ok] += dxq[r[ok]]
+    return acc
+
+
+def unpermute_reduce(dxq_bits, row_of, x_bits, afmt: int, act_scale):
+    """dX[t] = bf16(m_a1(X[t]) * sum over local slots of dXq[row_of[t,j]])."""
+    acc = unpermute_sum(dxq_bits, row_of)
     m = fq_act(x_bits, afmt, act_scale).mask if afmt != FMT_NONE else 1.0
     return f64_to_bf16(acc * m)
 
 
-def moe_layer(case, wfmt: int, group: int, afmt: int, wq_gu=None, wq_d=None,
+def act_scale_grad(x_bits, g, afmt: int, act_scale) -> float:
+    """Gradient of a learnable per-tensor activation scale s_a (R-19).
+
+    FQ_a maps every element x of the tensor to v = q(x / s_a) * s_a; with the
+    round passed straight through (R-13, R-14) dv/ds_a is the same factor as for
+    a weight scale, q - z inside the range and the bound outside it. The chain
+    rule sums it against ``g``, the gradient reaching FQ_a's output, over all
+    elements (float64). Only the static per-tensor formats FP8 and INT8 have such
+    a scale."""
+    if afmt not in (FMT_FP8, FMT_INT8):
+        raise ValueError(f"no learnable per-tensor scale for activation format {afmt}")
+    fq = fq_act(x_bits, afmt, act_scale)
+    return float(np.sum(np.asarray(g, dtype=np.float64) * fq.dv_ds))
+
+
+def moe_layer(case, wfmt: int, group, afmt: int, wq_gu=None, wq_d=None,
               act_scales=None):
     """Full forward + scale-only backward of one MoE layer's routed-expert path.
 
-    wq_gu / wq_d: (scale, zero_point, global_scale) of each stack; observer
-    init when None. act_scales: (s_a1, s_a2); calibrated on this batch when
-    None (s_a1 from X, s_a2 from the calibration A). Returns a dict of every
-    intermediate (bf16 bits unless noted).
+    group: elements per weight scale, or None for one scale per output
+    channel (the K of each stack). wq_gu / wq_d: (scale, zero_point,
+    global_scale) of each stack; observer init when None. act_scales: (s_a1,
+    s_a2); calibrated on this batch when None (s_a1 from X, s_a2 from the
+    calibration A). Returns a dict of every
+    intermediate (bf16 bits unless noted); ds_a1 / ds_a2 are the gradients of
+    the two activation scales (float, FP8 / INT8 activations only, else None).
     """
     E = case.w_gu.shape[0]
     k = case.expert_ids.shape[1]
+    g_gu = group or case.w_gu.shape[2]
+    g_d = group or case.w_d.shape[2]
     if wq_gu is None:
-        wq_gu = observer_weight(case.w_gu, wfmt, group)
+        wq_gu = observer_weight(case.w_gu, wfmt, g_gu)
     if wq_d is None:
-        wq_d = observer_weight(case.w_d, wfmt, group)
+        wq_d = observer_weight(case.w_d, wfmt, g_d)
     perm, row_of, seg = moe_permute(case.expert_ids, case.expert_begin, E)
     calibrated = act_scales is None
     if calibrated:
@@ -135,21 +165,25 @@ def moe_layer(case, wfmt: int, group: int, afmt: int, wq_gu=None, wq_d=None,
     else:
         s1 = act_scales[0]
     xq = gather_actfq(case.x, perm, k, afmt, s1)
-    h = grouped_gemm_fwd(xq.bits, seg, case.w_gu, wfmt, group, *wq_gu)
+    h = grouped_gemm_fwd(xq.bits, seg, case.w_gu, wfmt, g_gu, *wq_gu)
     if calibrated:
         a_cal = swiglu_fwd(h)
         s2 = observer_act(a_cal, afmt) if afmt != FMT_NONE else np.float32(1.0)
     else:
         s2 = act_scales[1]
     a, aq = swiglu_actfq(h, afmt, s2)
-    o = grouped_gemm_fwd(aq.bits, seg, case.w_d, wfmt, group, *wq_d)
+    o = grouped_gemm_fwd(aq.bits, seg, case.w_d, wfmt, g_d, *wq_d)
     out = combine(o, case.probs, row_of)
     do = combine_bwd(case.dout, case.probs, perm, k)
-    daq, ds_d, dzp_d = grouped_gemm_bwd(do, aq.bits, seg, case.w_d, wfmt, group, *wq_d)
+    daq, ds_d, dzp_d = grouped_gemm_bwd(do, aq.bits, seg, case.w_d, wfmt, g_d, *wq_d)
     dh = swiglu_bwd(daq, h, afmt, s2, a_bits=a)
-    dxq, ds_gu, dzp_gu = grouped_gemm_bwd(dh, xq.bits, seg, case.w_gu, wfmt, group, *wq_gu)
+    dxq, ds_gu, dzp_gu = grouped_gemm_bwd(dh, xq.bits, seg, case.w_gu, wfmt, g_gu, *wq_gu)
     dx = unpermute_reduce(dxq, row_of, case.x, afmt, s1)
+    ds_a1 = ds_a2 = None
+    if afmt in (FMT_FP8, FMT_INT8):
+        ds_a1 = act_scale_grad(case.x, unpermute_sum(dxq, row_of), afmt, s1)
+        ds_a2 = act_scale_grad(a, bf16_to_f32(daq), afmt, s2)
     return dict(perm=perm, row_of=row_of, seg=seg, s_a1=np.float32(s1), s_a2=np.float32(s2),
                 wq_gu=wq_gu, wq_d=wq_d, xq=xq.bits, h=h, a=a, aq=aq.bits, o=o, out=out,
                 do=do, daq=daq, dh=dh, dxq=dxq, dx=dx, ds_gu=ds_gu, ds_d=ds_d,
-                dzp_gu=dzp_gu, dzp_d=dzp_d)
+                dzp_gu=dzp_gu, dzp_d=dzp_d, ds_a1=ds_a1, ds_a2=ds_a2)

@@ -106,7 +106,8 @@ def _tiny_moe(fmt, seed=0):
     return case
 
 
-@pytest.mark.parametrize("fmt,afmt,group", [("fp8", O.FMT_FP8, None), ("nvfp4", O.FMT_NVFP4, 16)])
+@pytest.mark.parametrize("fmt,afmt,group", [("fp8", O.FMT_FP8, None), ("nvfp4", O.FMT_NVFP4, 16),
+                                            ("int8", O.FMT_INT8, None), ("int4", O.FMT_FP8, 16)])
 def test_moe_chain_matches_per_token_brute_force(fmt, afmt, group):
     case = _tiny_moe(fmt)
     wfmt = O.FMT_NAMES[fmt]
@@ -115,7 +116,7 @@ def test_moe_chain_matches_per_token_brute_force(fmt, afmt, group):
     # one group size per call: per-channel uses K of each stack
     wq_gu = O.observer_weight(case.w_gu, wfmt, grp_gu)
     wq_d = O.observer_weight(case.w_d, wfmt, grp_d)
-    out = _moe_layer_groups(case, wfmt, grp_gu, grp_d, afmt, wq_gu, wq_d)
+    out = O.moe_layer(case, wfmt, group, afmt, wq_gu, wq_d)
     # ---- brute force, one (token, slot) at a time
     F = case.w_d.shape[2]
     Wgu = O.bf16_to_f32(O.fq_weight_stack(case.w_gu, wfmt, grp_gu, *wq_gu).bits).astype(np.float64)
@@ -129,6 +130,7 @@ def test_moe_chain_matches_per_token_brute_force(fmt, afmt, group):
     wfq_d = O.fq_weight_stack(case.w_d, wfmt, grp_d, *wq_d)
     ds_gu = np.zeros_like(out["ds_gu"])
     ds_d = np.zeros_like(out["ds_d"])
+    ds_a1 = ds_a2 = 0.0
     for t in range(T):
         xq = O.fq_act(case.x[t:t + 1], afmt, s1)
         xv = O.bf16_to_f32(xq.bits)[0].astype(np.float64)
@@ -151,7 +153,11 @@ def test_moe_chain_matches_per_token_brute_force(fmt, afmt, group):
             dgate = da * u_ * sig * (1 + g_ * (1 - sig))
             dup = da * g_ * sig
             dh = O.bf16_to_f32(O.f64_to_bf16(np.concatenate([dgate, dup]))).astype(np.float64)
-            dxt += O.bf16_to_f32(O.f64_to_bf16(dh @ Wgu[e])).astype(np.float64)
+            dxq_row = O.bf16_to_f32(O.f64_to_bf16(dh @ Wgu[e])).astype(np.float64)
+            dxt += dxq_row
+            # each routed row's own contribution to the activation-scale gradients
+            ds_a1 += float(np.sum(dxq_row * xq.dv_ds[0]))
+            ds_a2 += float(np.sum(O.bf16_to_f32(O.f64_to_bf16(do @ Wd[e])) * aq.dv_ds[0]))
             ds_d[e] += (np.outer(do, av) * wfq_d.dv_ds[e]).reshape(ds_d.shape[1:] + (-1,)).sum(-1)
             ds_gu[e] += (np.outer(dh, xv) * wfq_gu.dv_ds[e]).reshape(ds_gu.shape[1:] + (-1,)).sum(-1)
         dx[t] = dxt * xq.mask[0]
@@ -160,30 +166,11 @@ def test_moe_chain_matches_per_token_brute_force(fmt, afmt, group):
     assert np.all(np.abs(O.bf16_to_f32(out["dx"]) - O.bf16_to_f32(O.f64_to_bf16(dx))) <= ulp(out["dx"]))
     for got, ref in ((out["ds_gu"], ds_gu), (out["ds_d"], ds_d)):
         assert np.abs(got - ref).max() <= 1e-9 * np.abs(ref).max()
-
-
-def _moe_layer_groups(case, wfmt, grp_gu, grp_d, afmt, wq_gu, wq_d):
-    """moe_layer with possibly different group sizes per stack (per-channel)."""
-    if grp_gu == grp_d:
-        return O.moe_layer(case, wfmt, grp_gu, afmt, wq_gu, wq_d)
-    # per-channel formats: run the chain explicitly with each stack's K as group
-    from oracle import moe as M
-    E = case.w_gu.shape[0]
-    k = case.expert_ids.shape[1]
-    perm, row_of, seg = O.moe_permute(case.expert_ids, case.expert_begin, E)
-    s1 = O.observer_act(case.x, afmt)
-    xq = M.gather_actfq(case.x, perm, k, afmt, s1)
-    h = O.grouped_gemm_fwd(xq.bits, seg, case.w_gu, wfmt, grp_gu, *wq_gu)
-    s2 = O.observer_act(M.swiglu_fwd(h), afmt)
-    a, aq = M.swiglu_actfq(h, afmt, s2)
-    o = O.grouped_gemm_fwd(aq.bits, seg, case.w_d, wfmt, grp_d, *wq_d)
-    out = M.combine(o, case.probs, row_of)
-    do = M.combine_bwd(case.dout, case.probs, perm, k)
-    daq, ds_d, _ = O.grouped_gemm_bwd(do, aq.bits, seg, case.w_d, wfmt, grp_d, *wq_d)
-    dh = M.swiglu_bwd(daq, h, afmt, s2, a_bits=a)
-    dxq, ds_gu, _ = O.grouped_gemm_bwd(dh, xq.bits, seg, case.w_gu, wfmt, grp_gu, *wq_gu)
-    dx = M.unpermute_reduce(dxq, row_of, case.x, afmt, s1)
-    return dict(out=out, dx=dx, ds_gu=ds_gu, ds_d=ds_d, s_a1=s1, s_a2=s2)
+    if afmt in (O.FMT_FP8, O.FMT_INT8):
+        assert abs(out["ds_a1"] - ds_a1) <= 1e-9 * abs(ds_a1) and ds_a1 != 0.0
+        assert abs(out["ds_a2"] - ds_a2) <= 1e-9 * abs(ds_a2) and ds_a2 != 0.0
+    else:
+        assert out["ds_a1"] is None and out["ds_a2"] is None
 
 
 def test_combine_bwd_is_exact_product():

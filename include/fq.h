@@ -67,7 +67,7 @@
 extern "C" {
 #endif
 
-#define FQ_ABI_VERSION 1
+#define FQ_ABI_VERSION 2
 
 typedef enum {
   FQ_OK = 0,
@@ -106,9 +106,11 @@ typedef struct {
   const float *global_scale;
 } fq_weight_q;
 
-/* Activation quantizer (frozen). fmt NONE, FP8_E4M3 (scale = per-tensor
- * s_a, one device float), NVFP4 (scale = g_a, one device float; block
- * scales dynamic per 16 elements along K), INT8 (per-tensor s_a). */
+/* Activation quantizer. fmt NONE, FP8_E4M3 (scale = per-tensor s_a, one
+ * device float), NVFP4 (scale = g_a, one device float; block scales dynamic
+ * per 16 elements along K), INT8 (per-tensor s_a). The scale is frozen
+ * (calibrated) by default; for FP8 and INT8 it may be learnable, and then
+ * fq_swiglu_bwd / fq_moe_unpermute_reduce also return its gradient. */
 typedef struct {
   int32_t fmt;
   const float *scale;
@@ -240,8 +242,23 @@ fq_status fq_grouped_gemm_bwd_scale(const uint16_t *dy_bf16, const uint16_t *x_b
  * fq_moe_combine_bwd: do[row_of[t,j]] = bf16(p[t,j] * dout[t]) for every
  *   routed slot; each dout row is read once.
  * fq_moe_unpermute_reduce: dx[t] = bf16(m_a(x[t]) * sum_j dxq[row_of[t,j]]).
- * All require H (resp. F) % 16 == 0 and T * H < 2^36. T == 0 launches
- * nothing (the token pointers may then be NULL).
+ * All require H (resp. F) % 16 == 0 and T * H (resp. R_max * F) < 2^36.
+ * T == 0 launches nothing (the token pointers may then be NULL).
+ *
+ * Learnable activation scale (fq_swiglu_bwd, fq_moe_unpermute_reduce): the
+ * gradient reaches a quantizer scale through autograd (mcore_qad article,
+ * section 二.3), here with the weights' straight-through factor dv/ds =
+ * value(c) - m*z. dscale_a (one device float, or NULL = scale frozen, no
+ * extra work) is OVERWRITTEN with
+ *   swiglu_bwd       : dS_a2 = sum over rows < R and f of daq * dv/ds(a)
+ *   unpermute_reduce : dS_a1 = sum over t, h of
+ *                      (sum_j dxq[row_of[t,j], h]) * dv/ds(x[t, h])
+ * (0 for an empty batch). Only FP8 and INT8 activations have such a scale
+ * (else FQ_ERR_UNSUPPORTED). Each block's fp32 partial goes to the
+ * workspace `ws` (at least fq_workspace_bytes(FQ_OP_ACT_SCALE_GRAD,
+ * {1, rows, cols}, 0, 0) bytes with rows x cols = R_max x F, resp. T x H),
+ * then one block sums them in a fixed order, so the result is bitwise
+ * reproducible. ws / ws_bytes are ignored when dscale_a is NULL.
  * ---------------------------------------------------------------------- */
 fq_status fq_moe_gather_actfq(const uint16_t *x_bf16, int32_t T, int32_t H, const int32_t *row_of,
                               int32_t topk, const fq_act_q *aq, uint16_t *xq_bf16,
@@ -251,7 +268,7 @@ fq_status fq_swiglu_actfq(const uint16_t *h_bf16, int32_t R_max, const int32_t *
                           fq_stream stream);
 fq_status fq_swiglu_bwd(const uint16_t *daq_bf16, const uint16_t *h_bf16, int32_t R_max,
                         const int32_t *n_rows, int32_t F, const fq_act_q *aq, uint16_t *dh_bf16,
-                        fq_stream stream);
+                        float *dscale_a, void *ws, size_t ws_bytes, fq_stream stream);
 fq_status fq_moe_combine(const uint16_t *o_bf16, const float *probs, const int32_t *row_of,
                          int32_t T, int32_t topk, int32_t H, uint16_t *out_bf16,
                          fq_stream stream);
@@ -260,12 +277,14 @@ fq_status fq_moe_combine_bwd(const uint16_t *dout_bf16, const float *probs, cons
                              fq_stream stream);
 fq_status fq_moe_unpermute_reduce(const uint16_t *dxq_bf16, const int32_t *row_of,
                                   const uint16_t *x_bf16, int32_t T, int32_t topk, int32_t H,
-                                  const fq_act_q *aq, uint16_t *dx_bf16, fq_stream stream);
+                                  const fq_act_q *aq, uint16_t *dx_bf16, float *dscale_a,
+                                  void *ws, size_t ws_bytes, fq_stream stream);
 
 /* Workspace sizing. op: one of FQ_OP_*. fmts = weight fmt | act fmt << 8. */
 #define FQ_OP_PERMUTE 1
 #define FQ_OP_GEMM_FWD 2
 #define FQ_OP_GEMM_BWD 3
+#define FQ_OP_ACT_SCALE_GRAD 4 /* shape = {1, rows, cols}; R_max, fmts unused */
 size_t fq_workspace_bytes(int32_t op, fq_shape shape, int32_t R_max, int32_t fmts);
 
 const char *fq_last_error(void);

@@ -37,6 +37,7 @@ FMT_BY_NAME = {"none": FMT_NONE, "int8": FMT_INT8, "int4": FMT_INT4, "fp8": FMT_
 FQ_OP_PERMUTE = 1
 FQ_OP_GEMM_FWD = 2
 FQ_OP_GEMM_BWD = 3
+FQ_OP_ACT_SCALE_GRAD = 4
 
 EXPORTED = (
     "observer_absmax_init", "fq_quantize_stacked", "fq_moe_permute", "fq_grouped_gemm_fwd",
@@ -68,7 +69,7 @@ class fq_act_q(ctypes.Structure):
 def _load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"libfq.so not found at {LIB_PATH}; build it with "
-                          "`python -m moe_fake_quant_amd.build` (hipcc, gfx950)")
+                          "`python moe_fake_quant_amd/build.py` (hipcc, gfx950)")
     lib = ctypes.CDLL(LIB_PATH)
     P, I32, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
     st = ctypes.c_int
@@ -83,10 +84,11 @@ def _load() -> ctypes.CDLL:
                                            P, P, P, P, SZ, P]),
         "fq_moe_gather_actfq": (st, [P, I32, I32, P, I32, ctypes.POINTER(fq_act_q), P, P]),
         "fq_swiglu_actfq": (st, [P, I32, P, I32, ctypes.POINTER(fq_act_q), P, P, P]),
-        "fq_swiglu_bwd": (st, [P, P, I32, P, I32, ctypes.POINTER(fq_act_q), P, P]),
+        "fq_swiglu_bwd": (st, [P, P, I32, P, I32, ctypes.POINTER(fq_act_q), P, P, P, SZ, P]),
         "fq_moe_combine": (st, [P, P, P, I32, I32, I32, P, P]),
         "fq_moe_combine_bwd": (st, [P, P, P, I32, I32, I32, P, P]),
-        "fq_moe_unpermute_reduce": (st, [P, P, P, I32, I32, I32, ctypes.POINTER(fq_act_q), P, P]),
+        "fq_moe_unpermute_reduce": (st, [P, P, P, I32, I32, I32, ctypes.POINTER(fq_act_q), P, P,
+                                         P, SZ, P]),
         "fq_workspace_bytes": (SZ, [I32, fq_shape, I32, I32]),
         "fq_last_error": (ctypes.c_char_p, []),
         "fq_abi_version": (I32, []),
@@ -212,9 +214,9 @@ def fq_swiglu_actfq(h, R_max, n_rows, F, aq: Optional[ActQ], a, aq_out):
                                 _p(aq_out), _stream()))
 
 
-def fq_swiglu_bwd(daq, h, R_max, n_rows, F, aq: Optional[ActQ], dh):
+def fq_swiglu_bwd(daq, h, R_max, n_rows, F, aq: Optional[ActQ], dh, dscale_a=None, ws=None):
     _check(_lib.fq_swiglu_bwd(_p(daq), _p(h), int(R_max), _p(n_rows), int(F), _aq(aq), _p(dh),
-                              _stream()))
+                              _p(dscale_a), _p(ws), _nbytes(ws), _stream()))
 
 
 def fq_moe_combine(o, probs, row_of, T, topk, H, out):
@@ -227,9 +229,11 @@ def fq_moe_combine_bwd(dout, probs, row_of, T, topk, H, dO):
                                    _p(dO), _stream()))
 
 
-def fq_moe_unpermute_reduce(dxq, row_of, x, T, topk, H, aq: Optional[ActQ], dx):
+def fq_moe_unpermute_reduce(dxq, row_of, x, T, topk, H, aq: Optional[ActQ], dx, dscale_a=None,
+                            ws=None):
     _check(_lib.fq_moe_unpermute_reduce(_p(dxq), _p(row_of), _p(x), int(T), int(topk), int(H),
-                                        _aq(aq), _p(dx), _stream()))
+                                        _aq(aq), _p(dx), _p(dscale_a), _p(ws), _nbytes(ws),
+                                        _stream()))
 
 
 from .layer import MoEFakeQuantLayer  # noqa: E402,F401

@@ -1,6 +1,6 @@
 """Build libfq.so (all HIP sources of csrc/) for gfx950 with hipcc, in-tree.
 
-    python -m moe_fake_quant_amd.build          # or build() from Python
+    python moe_fake_quant_amd/build.py          # or build() from Python
 
 The library lands next to this file; the Python binding loads it from there.
 """

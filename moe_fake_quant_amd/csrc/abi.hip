@@ -108,6 +108,21 @@ size_t gemm_ws(int op, fq_shape s, int R_max, int fmts) {
   return b;
 }
 
+// A learnable activation scale's gradient: only the static per-tensor formats
+// have one; the block partials live in the caller's workspace.
+fq_status check_dscale_a(const char *fn, const fq_act_q *aq, long rows, int cols, void *ws,
+                         size_t ws_bytes) {
+  FQ_CHECK_SUPPORTED(act_fmt(aq) == FQ_FMT_FP8_E4M3 || act_fmt(aq) == FQ_FMT_INT8,
+                     "%s: a learnable activation scale needs fp8 or int8 activations (fmt %d)", fn,
+                     act_fmt(aq));
+  const size_t need = align_up((size_t)act_grad_partials(rows, cols) * sizeof(float));
+  if (!ws || ws_bytes < need) {
+    set_error("%s: workspace %zu bytes < %zu needed", fn, ws_bytes, need);
+    return FQ_ERR_WORKSPACE_TOO_SMALL;
+  }
+  return FQ_OK;
+}
+
 }  // namespace
 }  // namespace fq
 
@@ -122,6 +137,10 @@ const char *fq_last_error(void) { return g_last_error.c_str(); }
 size_t fq_workspace_bytes(int32_t op, fq_shape shape, int32_t R_max, int32_t fmts) {
   if (op == FQ_OP_PERMUTE) return permute_workspace_bytes(shape.E > 0 ? shape.E : 1, R_max);
   if (op == FQ_OP_GEMM_FWD || op == FQ_OP_GEMM_BWD) return gemm_ws(op, shape, R_max, fmts);
+  if (op == FQ_OP_ACT_SCALE_GRAD) {
+    if (shape.N < 0 || shape.K <= 0) return 0;
+    return align_up((size_t)act_grad_partials(shape.N, shape.K) * sizeof(float));
+  }
   return 0;
 }
 
@@ -313,13 +332,17 @@ fq_status fq_swiglu_actfq(const uint16_t *h, int32_t R_max, const int32_t *n_row
 }
 
 fq_status fq_swiglu_bwd(const uint16_t *daq, const uint16_t *h, int32_t R_max, const int32_t *n_rows,
-                        int32_t F, const fq_act_q *aq, uint16_t *dh, fq_stream stream) {
+                        int32_t F, const fq_act_q *aq, uint16_t *dh, float *dscale_a, void *ws,
+                        size_t ws_bytes, fq_stream stream) {
   FQ_CHECK_ARG(R_max >= 0 && F > 0 && F % 16 == 0, "bad sizes (F must be a multiple of 16)");
+  FQ_CHECK_ARG((long)R_max * F < (1l << 36), "too many elements");
   FQ_CHECK_ARG(n_rows && (R_max == 0 || (h && daq && dh)), "NULL pointer");
   FQ_CHECK_ARG((!h || aligned16(h)) && (!daq || aligned16(daq)) && (!dh || aligned16(dh)),
                "bf16 tensors must be 16-byte aligned");
   FQ_TRY(check_act_q(aq, F));
-  launch_swiglu_bwd(daq, h, R_max, n_rows, F, act_fmt(aq), aq ? aq->scale : nullptr, dh, S(stream));
+  if (dscale_a) FQ_TRY(check_dscale_a("fq_swiglu_bwd", aq, R_max, F, ws, ws_bytes));
+  launch_swiglu_bwd(daq, h, R_max, n_rows, F, act_fmt(aq), aq ? aq->scale : nullptr, dh, dscale_a,
+                    static_cast<float *>(ws), S(stream));
   FQ_CHECK_LAUNCH("fq_swiglu_bwd");
   return FQ_OK;
 }
@@ -349,7 +372,8 @@ fq_status fq_moe_combine_bwd(const uint16_t *dout, const float *probs, const int
 
 fq_status fq_moe_unpermute_reduce(const uint16_t *dxq, const int32_t *row_of, const uint16_t *x,
                                   int32_t T, int32_t topk, int32_t H, const fq_act_q *aq,
-                                  uint16_t *dx, fq_stream stream) {
+                                  uint16_t *dx, float *dscale_a, void *ws, size_t ws_bytes,
+                                  fq_stream stream) {
   FQ_CHECK_ARG(T >= 0 && topk > 0 && H > 0 && H % 16 == 0, "bad sizes (H must be a multiple of 16)");
   FQ_CHECK_ARG((long)T * H < (1l << 36), "too many elements");
   FQ_CHECK_ARG(T == 0 || (dxq && row_of && dx), "NULL pointer");
@@ -357,8 +381,9 @@ fq_status fq_moe_unpermute_reduce(const uint16_t *dxq, const int32_t *row_of, co
   FQ_CHECK_ARG(act_fmt(aq) == FQ_FMT_NONE || T == 0 || x, "x is NULL");
   FQ_CHECK_ARG((!dxq || aligned16(dxq)) && (!dx || aligned16(dx)) && (!x || aligned16(x)),
                "bf16 tensors must be 16-byte aligned");
+  if (dscale_a) FQ_TRY(check_dscale_a("fq_moe_unpermute_reduce", aq, T, H, ws, ws_bytes));
   launch_unpermute_reduce(dxq, row_of, x, T, topk, H, act_fmt(aq), aq ? aq->scale : nullptr, dx,
-                          S(stream));
+                          dscale_a, static_cast<float *>(ws), S(stream));
   FQ_CHECK_LAUNCH("fq_moe_unpermute_reduce");
   return FQ_OK;
 }

@@ -1,6 +1,7 @@
 // HBM-bound passes of libfq on gfx950: the stacked weight fake-quant, the
 // observers, activation fake-quant (plain, gathered, after SwiGLU), SwiGLU
-// backward, combine / unpermute, and the fixed-order dScale partial reduce.
+// backward, combine / unpermute (the last two optionally with the gradient of
+// a learnable activation scale, summed in a fixed order).
 //
 // Every pass moves 16-byte vectors per lane (8 bf16), so a wavefront touches
 // 1 KiB of contiguous memory per load; indexes are 32-bit with precomputed
@@ -361,6 +362,63 @@ __device__ __forceinline__ void round_bf16_16(float *x) {
   for (int j = 0; j < 16; ++j) x[j] = bf16_to_f32(f32_to_bf16(x[j]));
 }
 
+// FP8 / INT8 activation fake-quant of 16 elements that also yields each
+// element's straight-through factor dv/ds_a = value(c) - m*z (the factor of a
+// learnable per-tensor scale, the same as a weight scale's). Values in place,
+// factors to dvds, mask bits returned.
+__device__ __forceinline__ uint32_t act_fq16_ds(const ActQ &q, float *x, float *dvds) {
+  uint32_t mask = 0;
+  if (q.fmt == FQ_FMT_FP8_E4M3) {
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+      const float z0 = x[2 * p] * q.r, z1 = x[2 * p + 1] * q.r;
+      float v0, v1;
+      e4m3_pair(clamp448(z0), clamp448(z1), v0, v1);
+      const bool m0 = fabsf(z0) <= kE4M3Max, m1 = fabsf(z1) <= kE4M3Max;
+      mask |= ((uint32_t)m0 << (2 * p)) | ((uint32_t)m1 << (2 * p + 1));
+      dvds[2 * p] = v0 - (m0 ? z0 : 0.0f);
+      dvds[2 * p + 1] = v1 - (m1 ? z1 : 0.0f);
+      x[2 * p] = v0 * q.s;
+      x[2 * p + 1] = v1 * q.s;
+    }
+    return mask;
+  }
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    FQElem e = fq_int8(x[j], q.s, q.r);
+    x[j] = e.v;
+    dvds[j] = e.dvds;
+    mask |= (uint32_t)e.m << j;
+  }
+  return mask;
+}
+
+// Sum of v over the block, the same in every thread and bitwise reproducible:
+// a butterfly inside each wave (both partners of a step add the same two
+// values, so every lane ends with the same sum), then the waves in index order.
+template <int NT>
+__device__ __forceinline__ float block_sum_fixed(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  __shared__ float red[NT / 64];
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  float s = red[0];
+#pragma unroll
+  for (int k = 1; k < NT / 64; ++k) s += red[k];
+  return s;
+}
+
+// out[0] = sum of the n block partials (one block, fixed order).
+constexpr int kSumThreads = 1024;
+__global__ __launch_bounds__(kSumThreads) void k_sum_partials(const float *__restrict__ part,
+                                                              uint32_t n, float *__restrict__ out) {
+  float v = 0.0f;
+  for (uint32_t i = threadIdx.x; i < n; i += kSumThreads) v += part[i];
+  v = block_sum_fixed<kSumThreads>(v);
+  if (threadIdx.x == 0) out[0] = v;
+}
+
 // number of 16-element chunks to process: all of them, or only the first
 // n_rows[0] rows (rows past the routed count are left untouched)
 __device__ __forceinline__ uint32_t live_chunks(uint32_t max_chunks, const int32_t *n_rows,
@@ -463,14 +521,18 @@ __global__ __launch_bounds__(kThreads) void k_swiglu_actfq(
   }
 }
 
-// dh = SwiGLU'(h) applied to da = m_a * daq
+// dh = SwiGLU'(h) applied to da = m_a * daq. DS: also the block's share of
+// dS_a = sum daq * dv/ds_a(A) into ds_part[blockIdx.x] (A recomputed as in the
+// forward, so its FQ factors are the forward's).
+template <bool DS>
 __global__ __launch_bounds__(kThreads) void k_swiglu_bwd(
     const bf16x8_t *__restrict__ daq, const bf16x8_t *__restrict__ h, FastDiv chunks_per_row,
     uint32_t max_chunks, const int32_t *__restrict__ n_rows, int afmt,
-    const float *__restrict__ ascale, bf16x8_t *__restrict__ dh) {
+    const float *__restrict__ ascale, bf16x8_t *__restrict__ dh, float *__restrict__ ds_part) {
   ActQ q = load_actq(afmt, ascale);
   const uint32_t cpr = chunks_per_row.d;
   const uint32_t nchunk = min((uint32_t)n_rows[0] * cpr, max_chunks);
+  float part = 0.0f;
   for (uint32_t c = blockIdx.x * blockDim.x + threadIdx.x; c < nchunk; c += gridDim.x * blockDim.x) {
     uint32_t r = chunks_per_row.div(c);
     uint32_t cc = c - r * cpr;
@@ -479,8 +541,17 @@ __global__ __launch_bounds__(kThreads) void k_swiglu_bwd(
     load16(hr + 2 * cc, g);
     load16(hr + 2 * (cpr + cc), u);
     swiglu16(g, u, a, sg);
-    uint32_t m = act_fq16(q, a);
-    load16(daq + 2 * (size_t)c, d);
+    uint32_t m;
+    if (DS) {
+      float dv[16];
+      m = act_fq16_ds(q, a, dv);
+      load16(daq + 2 * (size_t)c, d);
+#pragma unroll
+      for (int j = 0; j < 16; ++j) part = fmaf(d[j], dv[j], part);
+    } else {
+      m = act_fq16(q, a);
+      load16(daq + 2 * (size_t)c, d);
+    }
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
       const float da = ((m >> j) & 1u) ? d[j] : 0.0f;
@@ -491,6 +562,10 @@ __global__ __launch_bounds__(kThreads) void k_swiglu_bwd(
     bf16x8_t *dr = dh + 2 * ((size_t)r * 2 * cpr);
     store16(dr + 2 * cc, dg);
     store16(dr + 2 * (cpr + cc), du);
+  }
+  if (DS) {
+    part = block_sum_fixed<kThreads>(part);
+    if (threadIdx.x == 0) ds_part[blockIdx.x] = part;
   }
 }
 
@@ -545,13 +620,17 @@ __global__ __launch_bounds__(kThreads) void k_combine_bwd(
   }
 }
 
-// dx[t] = bf16(m_a(x[t]) * sum_j dxq[row_of[t,j]])
+// dx[t] = bf16(m_a(x[t]) * sum_j dxq[row_of[t,j]]). DS: also the block's
+// share of dS_a = sum over (t, h) of (sum_j dxq[row_of[t,j], h]) * dv/ds_a(x[t, h])
+// into ds_part[blockIdx.x].
+template <bool DS>
 __global__ __launch_bounds__(kThreads) void k_unpermute_reduce(
     const bf16x8_t *__restrict__ dxq, const int32_t *__restrict__ row_of,
     const bf16x8_t *__restrict__ x, int topk, FastDiv chunks_per_row, uint32_t nchunk, int afmt,
-    const float *__restrict__ ascale, bf16x8_t *__restrict__ dx) {
+    const float *__restrict__ ascale, bf16x8_t *__restrict__ dx, float *__restrict__ ds_part) {
   ActQ q = load_actq(afmt, ascale);
   const uint32_t cpr = chunks_per_row.d;
+  float part = 0.0f;
   for (uint32_t c = blockIdx.x * blockDim.x + threadIdx.x; c < nchunk; c += gridDim.x * blockDim.x) {
     uint32_t t = chunks_per_row.div(c);
     uint32_t cc = c - t * cpr;
@@ -567,7 +646,13 @@ __global__ __launch_bounds__(kThreads) void k_unpermute_reduce(
       for (int i = 0; i < 16; ++i) acc[i] = acc[i] + f[i];
     }
     uint32_t m = 0xFFFFu;
-    if (afmt != FQ_FMT_NONE) {
+    if (DS) {
+      float xf[16], dv[16];
+      load16(x + 2 * (size_t)c, xf);
+      m = act_fq16_ds(q, xf, dv);
+#pragma unroll
+      for (int j = 0; j < 16; ++j) part = fmaf(acc[j], dv[j], part);
+    } else if (afmt != FQ_FMT_NONE) {
       float xf[16];
       load16(x + 2 * (size_t)c, xf);
       m = act_fq16(q, xf);
@@ -575,6 +660,10 @@ __global__ __launch_bounds__(kThreads) void k_unpermute_reduce(
 #pragma unroll
     for (int j = 0; j < 16; ++j) acc[j] = ((m >> j) & 1u) ? acc[j] : 0.0f;
     store16(dx + 2 * (size_t)c, acc);
+  }
+  if (DS) {
+    part = block_sum_fixed<kThreads>(part);
+    if (threadIdx.x == 0) ds_part[blockIdx.x] = part;
   }
 }
 
@@ -695,13 +784,27 @@ void launch_swiglu_actfq(const uint16_t *h, int R_max, const int32_t *n_rows, in
                      reinterpret_cast<bf16x8_t *>(a), reinterpret_cast<bf16x8_t *>(aq));
 }
 
+long act_grad_partials(long rows, int cols) { return grid_for(rows * cols / 16); }
+
 void launch_swiglu_bwd(const uint16_t *daq, const uint16_t *h, int R_max, const int32_t *n_rows,
-                       int F, int afmt, const float *ascale, uint16_t *dh, hipStream_t st) {
+                       int F, int afmt, const float *ascale, uint16_t *dh, float *dscale_a,
+                       float *part, hipStream_t st) {
   uint32_t maxc = (uint32_t)((size_t)R_max * F / 16);
-  if (!maxc) return;
-  hipLaunchKernelGGL(k_swiglu_bwd, dim3(grid_for(maxc)), dim3(kThreads), 0, st,
-                     reinterpret_cast<const bf16x8_t *>(daq), reinterpret_cast<const bf16x8_t *>(h),
-                     FastDiv(F / 16), maxc, n_rows, afmt, ascale, reinterpret_cast<bf16x8_t *>(dh));
+  const int grid = grid_for(maxc);
+  auto dq = reinterpret_cast<const bf16x8_t *>(daq);
+  auto hv = reinterpret_cast<const bf16x8_t *>(h);
+  auto dv = reinterpret_cast<bf16x8_t *>(dh);
+  if (!dscale_a) {
+    if (!maxc) return;
+    hipLaunchKernelGGL(k_swiglu_bwd<false>, dim3(grid), dim3(kThreads), 0, st, dq, hv,
+                       FastDiv(F / 16), maxc, n_rows, afmt, ascale, dv, nullptr);
+    return;
+  }
+  if (maxc)
+    hipLaunchKernelGGL(k_swiglu_bwd<true>, dim3(grid), dim3(kThreads), 0, st, dq, hv,
+                       FastDiv(F / 16), maxc, n_rows, afmt, ascale, dv, part);
+  hipLaunchKernelGGL(k_sum_partials, dim3(1), dim3(kSumThreads), 0, st, part,
+                     maxc ? (uint32_t)grid : 0u, dscale_a);
 }
 
 void launch_combine(const uint16_t *o, const float *probs, const int32_t *row_of, int T, int topk,
@@ -724,14 +827,23 @@ void launch_combine_bwd(const uint16_t *dout, const float *probs, const int32_t 
 
 void launch_unpermute_reduce(const uint16_t *dxq, const int32_t *row_of, const uint16_t *x, int T,
                              int topk, int H, int afmt, const float *ascale, uint16_t *dx,
-                             hipStream_t st) {
+                             float *dscale_a, float *part, hipStream_t st) {
   uint32_t nchunk = (uint32_t)((size_t)T * H / 16);
-  if (!nchunk) return;
-  hipLaunchKernelGGL(k_unpermute_reduce, dim3(grid_for(nchunk)), dim3(kThreads), 0, st,
-                     reinterpret_cast<const bf16x8_t *>(dxq), row_of,
-                     reinterpret_cast<const bf16x8_t *>(x), topk, FastDiv(H / 16), nchunk, afmt, ascale,
-                     reinterpret_cast<bf16x8_t *>(dx));
+  const int grid = grid_for(nchunk);
+  auto dq = reinterpret_cast<const bf16x8_t *>(dxq);
+  auto xv = reinterpret_cast<const bf16x8_t *>(x);
+  auto dv = reinterpret_cast<bf16x8_t *>(dx);
+  if (!dscale_a) {
+    if (!nchunk) return;
+    hipLaunchKernelGGL(k_unpermute_reduce<false>, dim3(grid), dim3(kThreads), 0, st, dq, row_of,
+                       xv, topk, FastDiv(H / 16), nchunk, afmt, ascale, dv, nullptr);
+    return;
+  }
+  if (nchunk)
+    hipLaunchKernelGGL(k_unpermute_reduce<true>, dim3(grid), dim3(kThreads), 0, st, dq, row_of,
+                       xv, topk, FastDiv(H / 16), nchunk, afmt, ascale, dv, part);
+  hipLaunchKernelGGL(k_sum_partials, dim3(1), dim3(kSumThreads), 0, st, part,
+                     nchunk ? (uint32_t)grid : 0u, dscale_a);
 }
-
 
 }  // namespace fq

@@ -21,15 +21,20 @@ void launch_gather_actfq(const uint16_t *x, int T, int H, const int32_t *row_of,
                          int afmt, const float *ascale, uint16_t *xq, hipStream_t st);
 void launch_swiglu_actfq(const uint16_t *h, int R_max, const int32_t *n_rows, int F, int afmt,
                          const float *ascale, uint16_t *a, uint16_t *aq, hipStream_t st);
+// Block partials of a learnable activation scale's gradient over a
+// rows x cols tensor (one float each, summed into dscale_a[0] in a fixed order).
+long act_grad_partials(long rows, int cols);
+// dscale_a (may be NULL): overwritten with dS_a; part: act_grad_partials floats
 void launch_swiglu_bwd(const uint16_t *daq, const uint16_t *h, int R_max, const int32_t *n_rows,
-                       int F, int afmt, const float *ascale, uint16_t *dh, hipStream_t st);
+                       int F, int afmt, const float *ascale, uint16_t *dh, float *dscale_a,
+                       float *part, hipStream_t st);
 void launch_combine(const uint16_t *o, const float *probs, const int32_t *row_of, int T, int topk,
                     int H, uint16_t *out, hipStream_t st);
 void launch_combine_bwd(const uint16_t *dout, const float *probs, const int32_t *row_of, int T,
                         int topk, int H, uint16_t *dO, hipStream_t st);
 void launch_unpermute_reduce(const uint16_t *dxq, const int32_t *row_of, const uint16_t *x, int T,
                              int topk, int H, int afmt, const float *ascale, uint16_t *dx,
-                             hipStream_t st);
+                             float *dscale_a, float *part, hipStream_t st);
 
 size_t permute_workspace_bytes(int E, long P);
 void launch_permute(const int32_t *ids, int T, int topk, int ebegin, int E, int32_t *perm,

@@ -9,8 +9,11 @@ order; it computes nothing itself.
 Forward:  FQ pass on both stacks -> permute -> gather + act FQ -> gate_up GEMM
           -> SwiGLU + act FQ -> down GEMM -> combine
 Backward: combine bwd -> down dgrad + dScale -> SwiGLU bwd (with the act-FQ
-          mask) -> gate_up dgrad + dScale -> unpermute-reduce (with the input
-          act-FQ mask)
+          mask; + dS_a2) -> gate_up dgrad + dScale -> unpermute-reduce (with
+          the input act-FQ mask; + dS_a1)
+Activation scales are frozen after calibration unless ``learn_act_scales``
+(FP8 / INT8 activations), in which case the backward also returns their
+gradients in ``ds_a1`` (input of gate_up) and ``ds_a2`` (input of down).
 All buffers are allocated once; a step allocates nothing.
 """
 from __future__ import annotations
@@ -19,8 +22,8 @@ from typing import Optional
 
 import torch
 
-from . import (ActQ, FMT_INT4, FMT_NONE, FMT_NVFP4, FQ_OP_GEMM_BWD, FQ_OP_GEMM_FWD,
-               FQ_OP_PERMUTE, WeightQ, fq_grouped_gemm_bwd_scale, fq_grouped_gemm_fwd,
+from . import (ActQ, FMT_FP8_E4M3, FMT_INT4, FMT_INT8, FMT_NONE, FMT_NVFP4, FQ_OP_ACT_SCALE_GRAD,
+               FQ_OP_GEMM_BWD, FQ_OP_GEMM_FWD, FQ_OP_PERMUTE, WeightQ, fq_grouped_gemm_bwd_scale, fq_grouped_gemm_fwd,
                fq_moe_combine, fq_moe_combine_bwd, fq_moe_gather_actfq, fq_moe_permute,
                fq_moe_unpermute_reduce, fq_quantize_stacked, fq_swiglu_actfq, fq_swiglu_bwd,
                fq_workspace_bytes, observer_absmax_init)
@@ -38,9 +41,11 @@ def _weight_q(E, N, K, fmt, group, dev) -> WeightQ:
 
 class MoEFakeQuantLayer:
     def __init__(self, w_gu: torch.Tensor, w_d: torch.Tensor, wfmt: int, afmt: int, T_max: int,
-                 topk: int, expert_begin: int = 0, group: Optional[int] = None):
+                 topk: int, expert_begin: int = 0, group: Optional[int] = None,
+                 learn_act_scales: bool = False):
         """w_gu [E, 2F, H], w_d [E, H, F] bf16 on the device (frozen). group None =
-        one scale per output channel (group = K of each stack)."""
+        one scale per output channel (group = K of each stack). learn_act_scales:
+        the backward also produces the activation-scale gradients (FP8 / INT8)."""
         assert w_gu.dtype == torch.bfloat16 and w_d.dtype == torch.bfloat16
         self.dev = w_gu.device
         self.E, F2, self.H = w_gu.shape
@@ -84,7 +89,14 @@ class MoEFakeQuantLayer:
         self.ds_d = torch.empty_like(self.q_d.scale)
         self.dzp_gu = torch.empty_like(self.q_gu.scale) if wfmt == FMT_INT4 else None
         self.dzp_d = torch.empty_like(self.q_d.scale) if wfmt == FMT_INT4 else None
+        if learn_act_scales and afmt not in (FMT_FP8_E4M3, FMT_INT8):
+            raise ValueError("learnable activation scales need fp8 or int8 activations")
+        self.learn_act_scales = learn_act_scales
+        self.ds_a1 = torch.zeros(1, **f32) if learn_act_scales else None
+        self.ds_a2 = torch.zeros(1, **f32) if learn_act_scales else None
         ws = max(fq_workspace_bytes(FQ_OP_PERMUTE, (self.E, 0, 0), self.R_max, 0),
+                 fq_workspace_bytes(FQ_OP_ACT_SCALE_GRAD, (1, T_max, H), 0, 0),
+                 fq_workspace_bytes(FQ_OP_ACT_SCALE_GRAD, (1, R, F), 0, 0),
                  fq_workspace_bytes(FQ_OP_GEMM_FWD, self.shape_gu, R, 0),
                  fq_workspace_bytes(FQ_OP_GEMM_FWD, self.shape_d, R, 0),
                  fq_workspace_bytes(FQ_OP_GEMM_BWD, self.shape_gu, R, 0),
@@ -149,14 +161,15 @@ class MoEFakeQuantLayer:
                                   self.wfq_d, self.q_d, None, self.daq, None, None, self.ws)
         fq_grouped_gemm_bwd_scale(self.do, self.aq, self.R_max, self.seg, self.shape_d, self.w_d,
                                   self.wfq_d, self.q_d, None, None, self.ds_d, self.dzp_d, self.ws)
-        fq_swiglu_bwd(self.daq, self.h, self.R_max, self.n_rows, self.F, self.aq2, self.dh)
+        fq_swiglu_bwd(self.daq, self.h, self.R_max, self.n_rows, self.F, self.aq2, self.dh,
+                      self.ds_a2, self.ws)
         fq_grouped_gemm_bwd_scale(self.dh, self.xq, self.R_max, self.seg, self.shape_gu, self.w_gu,
                                   self.wfq_gu, self.q_gu, None, self.dxq, None, None, self.ws)
         fq_grouped_gemm_bwd_scale(self.dh, self.xq, self.R_max, self.seg, self.shape_gu, self.w_gu,
                                   self.wfq_gu, self.q_gu, None, None, self.ds_gu, self.dzp_gu,
                                   self.ws)
         fq_moe_unpermute_reduce(self.dxq, self.row_of[:T], x, T, self.topk, self.H, self.aq1,
-                                self.dx[:T])
+                                self.dx[:T], self.ds_a1, self.ws)
         return self.dx[:T], self.ds_gu, self.ds_d
 
     def step(self, x, expert_ids, probs, dout):

@@ -5,6 +5,10 @@ import torch
 
 GEMM_TOL = 2e-2      # max|gpu - ref| <= 2e-2 * max|ref|  (GEMM outputs, dX)
 DSCALE_TOL = 1e-3    # max|gpu - ref| / max|ref| <= 1e-3  (dScale, normwise)
+# A learnable activation scale's gradient is one fp32 sum of n products,
+# accumulated per thread and then in fixed-order trees: its rounding error is
+# below (16 + log2 n) * 2^-24 * sum|terms| < 1e-5 * sum|terms| for any n < 2^100.
+ACT_DSCALE_TOL = 1e-5
 
 
 def dev_bf16(bits: np.ndarray) -> torch.Tensor:
@@ -43,6 +47,13 @@ def check_dscale_tol(gpu, ref, what=""):
     err = np.abs(g - r).max()
     assert err <= DSCALE_TOL * scale, f"{what}: max|err| {err:.4g} > {DSCALE_TOL} * {scale:.4g}"
     return err / max(scale, 1e-30)
+
+
+def check_act_dscale_tol(gpu, ref, abs_terms, what="", tol=ACT_DSCALE_TOL):
+    """|gpu - ref| <= tol * sum|g * dv/ds| (abs_terms), the sum's own scale."""
+    err = abs(float(gpu) - float(ref))
+    assert err <= tol * abs_terms, f"{what}: |err| {err:.4g} > {tol} * {abs_terms:.4g}"
+    return err / max(abs_terms, 1e-30)
 
 
 def pack_codes(code: np.ndarray, fmt: int) -> np.ndarray:

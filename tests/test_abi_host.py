@@ -33,8 +33,13 @@ def _declared():
 @pytest.fixture(scope="module")
 def pkg():
     if not os.path.exists(LIB_PATH):
-        from moe_fake_quant_amd.build import build
-        build()
+        # by path: importing the package needs the library being built
+        import importlib.util
+        spec = importlib.util.spec_from_file_location("_fq_build", os.path.join(
+            os.path.dirname(LIB_PATH), "build.py"))
+        mod = importlib.util.module_from_spec(spec)
+        spec.loader.exec_module(mod)
+        mod.build()
     import moe_fake_quant_amd as F
     return F
 
@@ -83,7 +88,7 @@ def test_binding_matches_header(pkg):
 
 def test_version_and_error_string(pkg):
     lib = pkg.lib()
-    assert lib.fq_abi_version() == 1
+    assert lib.fq_abi_version() == 2
     assert isinstance(lib.fq_last_error(), bytes)
 
 
@@ -200,14 +205,38 @@ def test_permute_and_elementwise_reject_bad_arguments(pkg):
         pkg.FQ_ERR_INVALID_ARGUMENT                                   # no row map
     assert L.fq_swiglu_actfq(FAKE, 128, None, 64, None, None, FAKE, None) == \
         pkg.FQ_ERR_INVALID_ARGUMENT                                   # no n_rows
-    assert L.fq_swiglu_bwd(FAKE, FAKE, 128, FAKE, 24, None, FAKE, None) == \
+    assert L.fq_swiglu_bwd(FAKE, FAKE, 128, FAKE, 24, None, FAKE, None, None, 0, None) == \
         pkg.FQ_ERR_INVALID_ARGUMENT                                   # F % 16
     assert L.fq_moe_combine(FAKE, FAKE, FAKE, 16, 8, 64, FAKE + 8, None) == \
         pkg.FQ_ERR_INVALID_ARGUMENT                                   # misaligned out
     assert L.fq_moe_combine_bwd(FAKE, FAKE, FAKE, 16, 0, 64, FAKE, None) == \
         pkg.FQ_ERR_INVALID_ARGUMENT                                   # topk 0
     aq = ctypes.byref(pkg.fq_act_q(pkg.FMT_FP8_E4M3, FAKE))
-    assert L.fq_moe_unpermute_reduce(FAKE, FAKE, None, 16, 8, 64, aq, FAKE, None) == \
-        pkg.FQ_ERR_INVALID_ARGUMENT                                   # act mask needs x
+    assert L.fq_moe_unpermute_reduce(FAKE, FAKE, None, 16, 8, 64, aq, FAKE, None, None, 0,
+                                     None) == pkg.FQ_ERR_INVALID_ARGUMENT  # act mask needs x
     assert L.observer_absmax_init(FAKE, pkg.fq_shape(1, 4, 12), pkg.FMT_INT8, 12, 0, FAKE, None,
                                   None, None, 0, None) == pkg.FQ_ERR_INVALID_ARGUMENT  # K % 8
+
+
+@host_only
+def test_learnable_act_scale_arguments(pkg):
+    """A learnable activation scale needs a static per-tensor format and a
+    workspace of one float per block (sized by FQ_OP_ACT_SCALE_GRAD)."""
+    L = pkg.lib()
+    T, H, R, F = 300, 256, 1200, 768
+    need_x = _ws(pkg, pkg.FQ_OP_ACT_SCALE_GRAD, (1, T, H), 0)
+    need_a = _ws(pkg, pkg.FQ_OP_ACT_SCALE_GRAD, (1, R, F), 0)
+    # one fp32 partial per 256-thread block of 16-element chunks
+    assert need_x == _up(4 * -(-T * H // 16 // 256))
+    assert need_a == _up(4 * -(-R * F // 16 // 256))
+    fp8 = ctypes.byref(pkg.fq_act_q(pkg.FMT_FP8_E4M3, FAKE))
+    nv = ctypes.byref(pkg.fq_act_q(pkg.FMT_NVFP4, FAKE))
+    for aq, ws, nb, want in ((nv, FAKE, need_x, pkg.FQ_ERR_UNSUPPORTED),
+                             (None, FAKE, need_x, pkg.FQ_ERR_UNSUPPORTED),
+                             (fp8, FAKE, need_x - 256, pkg.FQ_ERR_WORKSPACE_TOO_SMALL),
+                             (fp8, None, need_x, pkg.FQ_ERR_WORKSPACE_TOO_SMALL)):
+        assert L.fq_moe_unpermute_reduce(FAKE, FAKE, FAKE, T, 8, H, aq, FAKE, FAKE, ws, nb,
+                                         None) == want
+    for aq, ws, nb, want in ((nv, FAKE, need_a, pkg.FQ_ERR_UNSUPPORTED),
+                             (fp8, FAKE, need_a - 256, pkg.FQ_ERR_WORKSPACE_TOO_SMALL)):
+        assert L.fq_swiglu_bwd(FAKE, FAKE, R, FAKE, F, aq, FAKE, FAKE, ws, nb, None) == want

@@ -116,3 +116,21 @@ def test_layer_step_with_zero_tokens():
     assert dx.shape[0] == 0
     assert np.all(L.seg.cpu().numpy() == 0)
     assert np.all(ds_gu.cpu().numpy() == 0) and np.all(ds_d.cpu().numpy() == 0)
+
+
+def test_learnable_act_scales_with_zero_tokens():
+    """An empty batch gives activation-scale gradients of exactly 0 (the
+    outputs are overwritten, not accumulated)."""
+    print("[edge] zero tokens, learnable fp8 act scales", flush=True)
+    case = W.moe_case(T=64, fmt="fp8", E_global=8, H=256, F=256, topk=4, seed=4)
+    L = F.MoEFakeQuantLayer(dev_bf16(case.w_gu), dev_bf16(case.w_d), F.FMT_FP8_E4M3,
+                            F.FMT_FP8_E4M3, case.T, case.topk, 0, None, learn_act_scales=True)
+    x, ids = dev_bf16(case.x), dev_i32(case.expert_ids)
+    L.init_weight_scales()
+    L.calibrate(x, ids)
+    L.step(x, ids, dev_f32(case.probs), dev_bf16(case.dout))
+    torch.cuda.synchronize()
+    assert float(L.ds_a1.cpu()[0]) != 0.0 and float(L.ds_a2.cpu()[0]) != 0.0
+    L.step(x[:0], ids[:0], dev_f32(case.probs)[:0], dev_bf16(case.dout)[:0])
+    torch.cuda.synchronize()
+    assert float(L.ds_a1.cpu()[0]) == 0.0 and float(L.ds_a2.cpu()[0]) == 0.0

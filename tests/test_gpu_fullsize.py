@@ -14,7 +14,11 @@ stage:
   * dScale: sampled output channels of sampled experts, reduced over all of
     that expert's rows (a channel's dScale depends on no other channel);
   * combine and unpermute-reduce: sampled tokens;
-  * empty experts: dScale exactly 0.
+  * empty experts: dScale exactly 0;
+  * learnable FP8 activation scales: each gradient is one sum over a whole
+    tensor, so the full-size result is checked by additivity (the kernel run
+    on eight disjoint slices sums to the full-size value) and one slice
+    against the oracle.
 """
 import numpy as np
 import pytest
@@ -22,7 +26,8 @@ import torch
 
 import oracle as O
 import workloads as W
-from helpers import (check_dscale_tol, check_gemm_tol, dev_bf16, dev_f32, dev_i32, host_bits)
+from helpers import (ACT_DSCALE_TOL, bf16_vals, check_act_dscale_tol, check_dscale_tol,
+                     check_gemm_tol, dev_bf16, dev_f32, dev_i32, host_bits)
 
 pytestmark = pytest.mark.gpu
 
@@ -174,6 +179,73 @@ def test_moe_full_size_sampled(cfg, fmt, group):
     check_gemm_tol(host_bits(L.out)[tok], O.combine(o_all[used], case.probs[tok], ro_sub), "out")
     check_gemm_tol(host_bits(L.dx)[tok],
                    O.unpermute_reduce(dxq_all[used], ro_sub, case.x[tok], fmt, s1), "dx")
+
+
+def test_fp8_learnable_act_scales_full_size():
+    """The FP8 MoE workload with learnable activation scales, in the layer's
+    launch configuration."""
+    case = W.config(3, seed=0)
+    _say(f"[fullsize] {W.CONFIG_NAMES[3]} learnable act scales")
+    E, T, k = case.E, case.T, case.topk
+    H, Fh = case.w_gu.shape[2], case.w_d.shape[2]
+    ffmt = F.FMT_FP8_E4M3
+    L = F.MoEFakeQuantLayer(dev_bf16(case.w_gu), dev_bf16(case.w_d), ffmt, ffmt, T, k,
+                            case.expert_begin, None, learn_act_scales=True)
+    x, ids = dev_bf16(case.x), dev_i32(case.expert_ids)
+    L.init_weight_scales()
+    L.calibrate(x, ids)
+    L.step(x, ids, dev_f32(case.probs), dev_bf16(case.dout))
+    a_dev = torch.empty_like(L.a)
+    F.fq_swiglu_actfq(L.h, L.R_max, L.n_rows, Fh, L.aq2, a_dev, torch.empty_like(L.aq))
+    torch.cuda.synchronize()
+    R = int(L.seg[E].item())
+    s1 = L.aq1.scale.cpu().numpy()[0]
+    s2 = L.aq2.scale.cpu().numpy()[0]
+    full1, full2 = float(L.ds_a1.cpu()[0]), float(L.ds_a2.cpu()[0])
+    ds = torch.empty(1, device="cuda")
+    ws = L.ws
+    # eight disjoint token slices of the unpermute-reduce
+    tb = np.linspace(0, T, 9).astype(int)
+    parts1 = []
+    dx_tmp = torch.empty_like(L.dx)
+    for t0, t1 in zip(tb[:-1], tb[1:]):
+        F.fq_moe_unpermute_reduce(L.dxq, L.row_of[t0:t1], x[t0:t1], t1 - t0, k, H, L.aq1,
+                                  dx_tmp[t0:t1], ds, ws)
+        parts1.append(float(ds.cpu()[0]))
+    # eight disjoint row slices of the SwiGLU backward (n_rows = the slice length)
+    rb = np.linspace(0, R, 9).astype(int)
+    parts2 = []
+    dh_tmp = torch.empty_like(L.dh)
+    for r0, r1 in zip(rb[:-1], rb[1:]):
+        n = dev_i32([r1 - r0])
+        F.fq_swiglu_bwd(L.daq[r0:r1], L.h[r0:r1], r1 - r0, n, Fh, L.aq2, dh_tmp[r0:r1], ds, ws)
+        parts2.append(float(ds.cpu()[0]))
+    torch.cuda.synchronize()
+    # the oracle on the first slice of each, from the GPU's own dXq / dAq / A
+    row_of = L.row_of.cpu().numpy()[:T]
+    t1 = int(tb[1])
+    ro = row_of[:t1]
+    used = np.maximum(ro, 0).reshape(-1)
+    ro_sub = np.where(ro >= 0, np.arange(ro.size).reshape(ro.shape), -1)
+    dxq_used = host_bits(L.dxq)[used]
+    fx = O.fq_act(case.x[:t1], O.FMT_FP8, s1)
+    g1 = O.unpermute_sum(dxq_used, ro_sub)
+    sc1 = float(np.sum(O.unpermute_sum(dxq_used & np.uint16(0x7FFF), ro_sub) * np.abs(fx.dv_ds)))
+    check_act_dscale_tol(parts1[0], float(np.sum(g1 * fx.dv_ds)), sc1, "ds_a1 slice 0")
+    r1 = int(rb[1])
+    a_sl = host_bits(a_dev)[:r1]
+    g2 = bf16_vals(host_bits(L.daq)[:r1])
+    fa = O.fq_act(a_sl, O.FMT_FP8, s2)
+    sc2 = float(np.sum(np.abs(g2 * fa.dv_ds)))
+    check_act_dscale_tol(parts2[0], O.act_scale_grad(a_sl, g2, O.FMT_FP8, s2), sc2,
+                         "ds_a2 slice 0")
+    # additivity at full size; sum|terms| extrapolated from the first slice
+    # (the slices are equal in size and identically distributed)
+    check_act_dscale_tol(sum(parts1), full1, 8 * sc1, "ds_a1 additivity",
+                         tol=2 * ACT_DSCALE_TOL)
+    check_act_dscale_tol(sum(parts2), full2, 8 * sc2, "ds_a2 additivity",
+                         tol=2 * ACT_DSCALE_TOL)
+    assert full1 != 0.0 and full2 != 0.0
 
 
 def _dense_run(case, fmt, group):

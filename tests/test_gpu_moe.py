@@ -8,8 +8,8 @@ import torch
 
 import oracle as O
 import workloads as W
-from helpers import (bf16_vals, check_dscale_tol, check_gemm_tol, dev_bf16, dev_f32, dev_i32,
-                     host_bits)
+from helpers import (bf16_vals, check_act_dscale_tol, check_dscale_tol, check_gemm_tol, dev_bf16,
+                     dev_f32, dev_i32, host_bits)
 
 pytestmark = pytest.mark.gpu
 
@@ -19,18 +19,23 @@ else:
     F = None
 
 CASES = [
-    # name, weight fmt, act fmt, group (None = per channel), T, E_global, E_local, begin, zipf
-    ("fp8", O.FMT_FP8, O.FMT_FP8, None, 300, 8, 8, 0, None),
-    ("nvfp4", O.FMT_NVFP4, O.FMT_NVFP4, 16, 300, 8, 8, 0, None),
-    ("nvfp4-local-zipf", O.FMT_NVFP4, O.FMT_NVFP4, 16, 700, 32, 8, 0, 1.2),
-    ("int4-a16", O.FMT_INT4, O.FMT_NONE, 128, 200, 8, 8, 0, None),
+    # name, weight fmt, act fmt, group (None = per channel), T, E_global, E_local, begin, zipf,
+    # learnable activation scales
+    ("fp8", O.FMT_FP8, O.FMT_FP8, None, 300, 8, 8, 0, None, False),
+    ("nvfp4", O.FMT_NVFP4, O.FMT_NVFP4, 16, 300, 8, 8, 0, None, False),
+    ("nvfp4-local-zipf", O.FMT_NVFP4, O.FMT_NVFP4, 16, 700, 32, 8, 0, 1.2, False),
+    ("int4-a16", O.FMT_INT4, O.FMT_NONE, 128, 200, 8, 8, 0, None, False),
+    # the other format pairings the pages list, on the same kernels
+    ("nvfp4a16", O.FMT_NVFP4, O.FMT_NONE, 16, 260, 8, 8, 0, None, False),
+    ("w4afp8", O.FMT_INT4, O.FMT_FP8, 128, 260, 8, 8, 0, None, True),
+    ("w8a8-int8", O.FMT_INT8, O.FMT_INT8, None, 260, 8, 8, 0, None, True),
+    ("fp8-learn-act-local", O.FMT_FP8, O.FMT_FP8, None, 500, 16, 8, 4, None, True),
 ]
 
 
-def _run_layer(case, wfmt, afmt, group):
-    E = case.E
+def _run_layer(case, wfmt, afmt, group, learn=False):
     layer = F.MoEFakeQuantLayer(dev_bf16(case.w_gu), dev_bf16(case.w_d), wfmt, afmt, case.T,
-                                case.topk, case.expert_begin, group)
+                                case.topk, case.expert_begin, group, learn_act_scales=learn)
     x, ids = dev_bf16(case.x), dev_i32(case.expert_ids)
     p, dout = dev_f32(case.probs), dev_bf16(case.dout)
     layer.init_weight_scales()
@@ -42,12 +47,18 @@ def _run_layer(case, wfmt, afmt, group):
     return layer
 
 
-@pytest.mark.parametrize("name,wfmt,afmt,group,T,Eg,El,begin,zipf", CASES)
-def test_moe_layer_stagewise_and_end_to_end(name, wfmt, afmt, group, T, Eg, El, begin, zipf):
+def _abs_bits(bits):
+    return np.asarray(bits, np.uint16) & np.uint16(0x7FFF)
+
+
+@pytest.mark.parametrize("name,wfmt,afmt,group,T,Eg,El,begin,zipf,learn", CASES)
+def test_moe_layer_stagewise_and_end_to_end(name, wfmt, afmt, group, T, Eg, El, begin, zipf,
+                                            learn):
+    print(f"[moe] {name}", flush=True)
     case = W.moe_case(T=T, fmt=name, E_global=Eg, H=256, F=256, topk=4, seed=11,
                       expert_begin=begin, E_local=El, zipf_s=zipf,
                       zero_experts=(3,) if zipf else ())
-    L = _run_layer(case, wfmt, afmt, group)
+    L = _run_layer(case, wfmt, afmt, group, learn)
     E, k = El, case.topk
     g_gu = group or case.w_gu.shape[2]
     g_d = group or case.w_d.shape[2]
@@ -97,6 +108,22 @@ def test_moe_layer_stagewise_and_end_to_end(name, wfmt, afmt, group, T, Eg, El, 
         check_dscale_tol(L.dzp_d.cpu().numpy(), dzp_d_ref, "dzp_d")
     dx = host_bits(L.dx)[:T]
     check_gemm_tol(dx, O.unpermute_reduce(dxq, row_of, case.x, afmt, s1), "dx")
+    if learn:
+        # activation-scale gradients from the GPU's own dXq / dAq
+        fx = O.fq_act(case.x, afmt, s1)
+        g1 = O.unpermute_sum(dxq, row_of)
+        sc1 = float(np.sum(O.unpermute_sum(_abs_bits(dxq), row_of) * np.abs(fx.dv_ds)))
+        ds_a1 = float(L.ds_a1.cpu()[0])
+        check_act_dscale_tol(ds_a1, O.act_scale_grad(case.x, g1, afmt, s1), sc1, "ds_a1")
+        fa = O.fq_act(a, afmt, s2)
+        g2 = bf16_vals(daq)
+        sc2 = float(np.sum(np.abs(g2 * fa.dv_ds)))
+        ds_a2 = float(L.ds_a2.cpu()[0])
+        check_act_dscale_tol(ds_a2, O.act_scale_grad(a, g2, afmt, s2), sc2, "ds_a2")
+        # bitwise reproducible: the same backward again
+        L.backward(dev_bf16(case.x), dev_f32(case.probs), dev_bf16(case.dout))
+        torch.cuda.synchronize()
+        assert float(L.ds_a1.cpu()[0]) == ds_a1 and float(L.ds_a2.cpu()[0]) == ds_a2
     # end to end: the oracle's own chain with the GPU-calibrated activation scales
     ref = O.moe_layer(case, wfmt, g_gu if g_gu == g_d else None, afmt, wq_gu, wq_d, (s1, s2)) \
         if g_gu == g_d else None
@@ -105,3 +132,7 @@ def test_moe_layer_stagewise_and_end_to_end(name, wfmt, afmt, group, T, Eg, El, 
         check_gemm_tol(dx, ref["dx"], "dx e2e")
         check_dscale_tol(L.ds_gu.cpu().numpy(), ref["ds_gu"], "ds_gu e2e")
         check_dscale_tol(L.ds_d.cpu().numpy(), ref["ds_d"], "ds_d e2e")
+        if learn:
+            # the oracle's own dXq / dAq differ from the GPU's by GEMM rounding
+            check_act_dscale_tol(ds_a1, ref["ds_a1"], sc1, "ds_a1 e2e", tol=1e-2)
+            check_act_dscale_tol(ds_a2, ref["ds_a2"], sc2, "ds_a2 e2e", tol=1e-2)

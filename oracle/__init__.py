@@ -49,6 +49,8 @@ reading where it applies:
        (FP8, INT8) only; its gradient uses the weights' STE factor, summed
        over every element the quantizer saw in the step. NVFP4 activations
        derive their block scales from the data and keep g_a at calibration.
+  R-20 a per-tensor weight scale is one scale per expert matrix [N, K] of a
+       stack (each expert is its own linear); INT8 / FP8 only
 
 Parity status: every function here is pinned by the ``-m "not gpu"`` tests
 (exhaustive code grids, tie tables, library special cases, closed forms,
@@ -58,7 +60,7 @@ tolerance only ("parity unpinned" beyond the stated tolerances).
 """
 from .numerics import bf16_to_f32, f32_to_bf16, f64_to_bf16  # noqa: F401
 from .codecs import (  # noqa: F401
-    FMT_NONE, FMT_INT8, FMT_INT4, FMT_FP8, FMT_NVFP4, FMT_NAMES,
+    FMT_NONE, FMT_INT8, FMT_INT4, FMT_FP8, FMT_NVFP4, FMT_NAMES, GROUP_TENSOR,
     E4M3_POS, E2M1_POS, E4M3_MAX, E2M1_MAX,
     e4m3_round, e2m1_round, e4m3_value_of_code, e2m1_value_of_code,
     fq_int8, fq_int4, fq_fp8, fq_nvfp4, fq_nvfp4_act_dynamic,

@@ -45,6 +45,9 @@ FMT_NAMES = {"none": FMT_NONE, "int8": FMT_INT8, "int4": FMT_INT4, "fp8": FMT_FP
 INT8_LO, INT8_HI = -128.0, 127.0      # full two's-complement range (R-3)
 INT4_LO, INT4_HI = 0.0, 15.0          # unsigned codes, integer zero point
 NVFP4_BLOCK = 16
+# One weight scale per expert matrix [N, K] (the per-tensor weight preset of
+# the QAT + ZeRO-3 page's fp8_static example; INT8 / FP8 only, R-20).
+GROUP_TENSOR = -1
 INT4_GROUP = 128
 
 
@@ -258,11 +261,17 @@ def fq_weight_stack(w_bits, fmt: int, group: int, scale, zero_point=None,
                     global_scale=None) -> FQ:
     """Fake-quantise a stacked weight [E, N, K] (mcore_qad article, section 二.4).
 
-    scale: [E, N, K/group] (NVFP4: theta); zero_point: [E, N, K/group] (int4);
+    scale: [E, N, K/group] (NVFP4: theta), or [E] for group GROUP_TENSOR (one
+    scale per expert matrix, INT8 / FP8); zero_point: [E, N, K/group] (int4);
     global_scale: [E] (NVFP4 tensor scale g, one per expert, R-8).
     """
     w = bf16_to_f32(w_bits)
     E, N, K = w.shape
+    if group == GROUP_TENSOR:
+        if fmt not in (FMT_INT8, FMT_FP8):
+            raise ValueError("a per-tensor weight scale exists for int8 / fp8 only")
+        s = np.broadcast_to(np.asarray(scale, dtype=np.float32).reshape(E, 1, 1), (E, N, K))
+        return fq_int8(w, s) if fmt == FMT_INT8 else fq_fp8(w, s)
     assert K % group == 0
     s = _expand_groups(np.asarray(scale, dtype=np.float32).reshape(E, N, K // group), group, K)
     if fmt == FMT_INT8:

@@ -14,13 +14,14 @@ gradient reaches the scale through autograd), with the STE factors of
     dWq[e]   = dY_e^T . Xq_e                (never stored)
     dS[e,n,g] = sum_{k in g} dWq[e,n,k] * dv/ds(e,n,k)
     dZP[e,n,g] = sum_{k in g} dWq[e,n,k] * dv/dzp(e,n,k)   (int4 only)
+    dS[e]     = sum_{n,k} dWq[e,n,k] * dv/ds(e,n,k)        (per-tensor scale)
 An expert with no rows gets dS = 0.
 """
 from __future__ import annotations
 
 import numpy as np
 
-from .codecs import FMT_INT4, fq_act, fq_weight_stack
+from .codecs import FMT_INT4, GROUP_TENSOR, fq_act, fq_weight_stack
 from .numerics import bf16_to_f32, f64_to_bf16
 
 
@@ -44,7 +45,8 @@ def grouped_gemm_fwd(x_bits, seg, w_bits, wfmt: int, group: int, scale, zero_poi
 
 def grouped_gemm_bwd(dy_bits, x_bits, seg, w_bits, wfmt: int, group: int, scale,
                      zero_point=None, global_scale=None, afmt: int = 0, act_scale=None):
-    """Returns (dx bits [R, K], dscale float64 [E, N, K/group], dzp float64 or None)."""
+    """Returns (dx bits [R, K], dscale float64 [E, N, K/group] (per-tensor: [E]),
+    dzp float64 or None)."""
     seg = np.asarray(seg, dtype=np.int64)
     R = int(seg[-1])
     xq = fq_act(np.asarray(x_bits)[:R], afmt, act_scale)
@@ -53,9 +55,10 @@ def grouped_gemm_bwd(dy_bits, x_bits, seg, w_bits, wfmt: int, group: int, scale,
     b = bf16_to_f32(wq.bits).astype(np.float64)
     dy = bf16_to_f32(np.asarray(dy_bits)[:R]).astype(np.float64)
     E, N, K = b.shape
-    G = K // group
+    per_tensor = group == GROUP_TENSOR
+    G = 1 if per_tensor else K // group
     dx = np.zeros((R, K), dtype=np.float64)
-    ds = np.zeros((E, N, G), dtype=np.float64)
+    ds = np.zeros((E,) if per_tensor else (E, N, G), dtype=np.float64)
     dzp = np.zeros((E, N, G), dtype=np.float64) if wfmt == FMT_INT4 else None
     for e in range(E):
         lo, hi = seg[e], seg[e + 1]
@@ -63,7 +66,10 @@ def grouped_gemm_bwd(dy_bits, x_bits, seg, w_bits, wfmt: int, group: int, scale,
             continue
         dx[lo:hi] = dy[lo:hi] @ b[e]
         dwq = dy[lo:hi].T @ a[lo:hi]                       # [N, K]
-        ds[e] = (dwq * wq.dv_ds[e]).reshape(N, G, group).sum(axis=-1)
+        if per_tensor:
+            ds[e] = np.sum(dwq * wq.dv_ds[e])
+        else:
+            ds[e] = (dwq * wq.dv_ds[e]).reshape(N, G, group).sum(axis=-1)
         if dzp is not None:
             dzp[e] = (dwq * wq.dv_dzp[e]).reshape(N, G, group).sum(axis=-1)
     dx = dx * xq.mask

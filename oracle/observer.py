@@ -15,7 +15,7 @@ from __future__ import annotations
 import numpy as np
 
 from .codecs import (E4M3_MAX, E2M1_MAX, FMT_FP8, FMT_INT4, FMT_INT8, FMT_NVFP4,
-                     NVFP4_BLOCK, e4m3_round)
+                     GROUP_TENSOR, NVFP4_BLOCK, e4m3_round)
 from .numerics import bf16_to_f32
 
 NVFP4_DIV = np.float32(E2M1_MAX * E4M3_MAX)   # 2688
@@ -32,6 +32,7 @@ def observer_weight(w_bits, fmt: int, group: int):
     Returns (scale [E,N,K/group] fp32, zero_point or None, global_scale or None).
       int8 : s = amax_group / 127
       fp8  : s = amax_group / 448
+      group GROUP_TENSOR (int8 / fp8): the amax of each expert matrix, scale [E]
       int4 : lo = min(0, min), hi = max(0, max); s = (hi - lo) / 15;
              zp = clamp(rne(-lo * (1/s)), 0, 15)                      (R-5)
       nvfp4: g_e = amax_expert / 2688;
@@ -39,6 +40,10 @@ def observer_weight(w_bits, fmt: int, group: int):
     """
     w = bf16_to_f32(w_bits)
     E, N, K = w.shape
+    if fmt in (FMT_INT8, FMT_FP8) and group == GROUP_TENSOR:
+        amax = np.abs(w).reshape(E, -1).max(axis=-1).astype(np.float32)
+        div = np.float32(127.0) if fmt == FMT_INT8 else np.float32(E4M3_MAX)
+        return _safe_scale(amax / div), None, None
     if fmt in (FMT_INT8, FMT_FP8):
         amax = np.abs(w).reshape(E, N, K // group, group).max(axis=-1).astype(np.float32)
         div = np.float32(127.0) if fmt == FMT_INT8 else np.float32(E4M3_MAX)

@@ -107,7 +107,8 @@ def _tiny_moe(fmt, seed=0):
 
 
 @pytest.mark.parametrize("fmt,afmt,group", [("fp8", O.FMT_FP8, None), ("nvfp4", O.FMT_NVFP4, 16),
-                                            ("int8", O.FMT_INT8, None), ("int4", O.FMT_FP8, 16)])
+                                            ("int8", O.FMT_INT8, None), ("int4", O.FMT_FP8, 16),
+                                            ("fp8", O.FMT_FP8, O.GROUP_TENSOR)])
 def test_moe_chain_matches_per_token_brute_force(fmt, afmt, group):
     case = _tiny_moe(fmt)
     wfmt = O.FMT_NAMES[fmt]

@@ -104,3 +104,19 @@ def test_activation_per_tensor(fmt, div):
     x = O.f32_to_bf16(rng.standard_normal((32, 64)).astype(np.float32))
     s = O.observer_act(x, fmt)
     assert s == np.float32(np.abs(O.bf16_to_f32(x)).max() / np.float32(div))
+
+
+@pytest.mark.parametrize("fmt,top", [(O.FMT_FP8, 448.0), (O.FMT_INT8, 127.0)])
+def test_per_tensor_weight_scale_is_matrix_amax(fmt, top):
+    """Per-tensor weights: one scale per expert matrix, the matrix's amax over
+    the grid maximum; exactly the amax elements reach the top code."""
+    w = _w(3, 8, 64, seed=5)
+    s, zp, g = O.observer_weight(w, fmt, O.GROUP_TENSOR)
+    x = O.bf16_to_f32(w)
+    amax = np.abs(x).reshape(3, -1).max(axis=1).astype(np.float32)
+    assert zp is None and g is None
+    assert np.array_equal(s, (amax / np.float32(top)).astype(np.float32))
+    fq = O.fq_weight_stack(w, fmt, O.GROUP_TENSOR, s)
+    am = np.abs(x) == amax[:, None, None]
+    assert np.all(np.abs(fq.q[am]) == top)
+    assert np.all(np.abs(fq.q[~am]) <= top)

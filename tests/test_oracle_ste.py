@@ -195,3 +195,61 @@ def test_int8_scale_grad_matches_torch_learnable_fake_quant_away_from_bounds():
     # torch reduces its per-element terms in fp32: compare normwise at 1e-4
     ref = st.grad.numpy().astype(np.float64)
     assert np.abs(ours - ref).max() <= 1e-4 * np.abs(ref).max()
+
+
+@pytest.mark.parametrize("fmt", [O.FMT_INT8, O.FMT_FP8])
+def test_per_tensor_dscale_matches_torch_autograd(fmt):
+    """One scale per expert matrix (a [E] leaf broadcast over [N, K]): autograd
+    sums the straight-through factors over the whole matrix."""
+    rng = np.random.default_rng(31)
+    E, N, K, R = 3, 8, 64, 21
+    w = O.f32_to_bf16((rng.standard_normal((E, N, K)) * 0.02).astype(np.float32))
+    s, _, _ = O.observer_weight(w, fmt, O.GROUP_TENSOR)
+    assert s.shape == (E,)
+    s = (s * rng.uniform(0.5, 1.0, E)).astype(np.float32)    # some elements saturate
+    seg = np.array([0, 8, 8, R], np.int32)                     # expert 1 empty
+    x = O.f32_to_bf16(rng.standard_normal((R, K)).astype(np.float32))
+    dy = O.f32_to_bf16(rng.standard_normal((R, N)).astype(np.float32))
+    dx_o, ds_o, _ = O.grouped_gemm_bwd(dy, x, seg, w, fmt, O.GROUP_TENSOR, s)
+    assert ds_o.shape == (E,) and ds_o[1] == 0.0
+
+    wt = torch.from_numpy(O.bf16_to_f32(w).copy())
+    st = torch.from_numpy(s.copy()).requires_grad_(True)
+    s_e = st.view(E, 1, 1)
+    z = wt * (1.0 / s_e)
+    bound = 127.0 if fmt == O.FMT_INT8 else 448.0
+    zc = z.clamp(-128.0 if fmt == O.FMT_INT8 else -448.0, bound)
+    rq = torch.round(zc.detach()) if fmt == O.FMT_INT8 else \
+        zc.detach().to(torch.float8_e4m3fn).to(torch.float32)
+    v = _ste(zc, rq) * s_e
+    vq = v.to(torch.float64) + (v.to(torch.bfloat16).to(torch.float64) - v.to(torch.float64)).detach()
+    assert np.array_equal(O.f32_to_bf16(v.detach().numpy()),
+                          O.fq_weight_stack(w, fmt, O.GROUP_TENSOR, s).bits)
+    xt = torch.from_numpy(O.bf16_to_f32(x).astype(np.float64))
+    dyt = torch.from_numpy(O.bf16_to_f32(dy).astype(np.float64))
+    y = torch.cat([xt[seg[e]:seg[e + 1]] @ vq[e].T for e in range(E)])
+    (y * dyt).sum().backward()
+    ds_t = st.grad.double().numpy()
+    assert np.abs(ds_o - ds_t).max() <= 1e-6 * np.abs(ds_t).max()
+
+
+@pytest.mark.parametrize("fmt", [O.FMT_INT8, O.FMT_FP8])
+def test_per_tensor_is_per_channel_with_one_shared_scale(fmt):
+    """The same values as per-channel quantization whose N scales all equal the
+    expert's one scale; the per-tensor gradient is the sum of the N channel
+    gradients."""
+    rng = np.random.default_rng(32)
+    E, N, K, R = 2, 16, 32, 30
+    w = O.f32_to_bf16((rng.standard_normal((E, N, K)) * 0.05).astype(np.float32))
+    s = np.array([0.02 / 127, 0.05 / 448], np.float32)
+    rep = np.repeat(s[:, None, None], N, axis=1)              # [E, N, 1]
+    a = O.fq_weight_stack(w, fmt, O.GROUP_TENSOR, s)
+    b = O.fq_weight_stack(w, fmt, K, rep)
+    assert np.array_equal(a.bits, b.bits) and np.array_equal(a.dv_ds, b.dv_ds)
+    seg = np.array([0, 13, R], np.int32)
+    x = O.f32_to_bf16(rng.standard_normal((R, K)).astype(np.float32))
+    dy = O.f32_to_bf16(rng.standard_normal((R, N)).astype(np.float32))
+    dx_t, ds_t, _ = O.grouped_gemm_bwd(dy, x, seg, w, fmt, O.GROUP_TENSOR, s)
+    dx_c, ds_c, _ = O.grouped_gemm_bwd(dy, x, seg, w, fmt, K, rep)
+    assert np.array_equal(dx_t, dx_c)
+    assert np.allclose(ds_t, ds_c.sum(axis=(1, 2)), rtol=1e-12, atol=0)

@@ -95,9 +95,15 @@ typedef struct {
  *   group       : elements per scale along K. int8 / fp8: K (per output
  *                 channel) or a divisor of K that is a multiple of 16;
  *                 int4: 128 (any multiple of 16 dividing K); nvfp4: 16.
+ *                 int8 / fp8 also FQ_GROUP_TENSOR: one scale per expert
+ *                 matrix [N, K] (the per-tensor weights of the fp8_static
+ *                 preset, QAT + ZeRO-3 page, example configs); scale and
+ *                 dscale are then [E].
  *   scale       : [E, N, K/group] fp32. nvfp4: the block parameter theta.
  *   zero_point  : [E, N, K/group] fp32 holding integers; int4 only, else NULL.
  *   global_scale: [E] fp32 tensor scale g; nvfp4 only, else NULL. */
+#define FQ_GROUP_TENSOR (-1)
+
 typedef struct {
   int32_t fmt;
   int32_t group;
@@ -132,11 +138,13 @@ typedef void *fq_stream; /* hipStream_t */
  *          zero_point = clamp(rne(-lo * (1/scale)), 0, 15)
  *   nvfp4: global_scale[e] = amax_e / 2688,
  *          scale[e,n,b] = E4M3(clamp(amax_b * (1/(6*g_e)), 0, 448))
+ *   group FQ_GROUP_TENSOR (int8 / fp8): scale[e] = amax over expert e's
+ *          matrix / 127 resp. 448
  * per_tensor == 1 (activations): x is any tensor of E*N*K elements and
  *   scale[0] = amax / D with D = 448 (fp8), 2688 (nvfp4), 127 (int8).
  * Each division is one IEEE fp32 division; a zero amax gives scale 1.0.
  * Outputs (device, caller-owned) are overwritten. ws may be NULL
- * (needs 0 bytes). Requires K % 8 == 0 and K % group == 0.
+ * (needs 0 bytes). Requires K % 8 == 0 and K % group == 0 (weights).
  * ---------------------------------------------------------------------- */
 fq_status observer_absmax_init(const uint16_t *x_bf16, fq_shape shape, int32_t fmt,
                                int32_t group, int32_t per_tensor, float *scale,
@@ -205,6 +213,9 @@ fq_status fq_grouped_gemm_fwd(const uint16_t *x_bf16, int32_t R_max, const int32
  *   dWq_e = dY_e^T . FQ_a(X)_e                            (never stored)
  *   dscale[e,n,g]     = sum_{k in g} dWq_e[n,k] * dv/ds(e,n,k)   fp32
  *   dzero_point[e,n,g]= sum_{k in g} dWq_e[n,k] * dv/dzp(e,n,k)  (int4)
+ *   per-tensor scale  : dscale[e] = sum over n of the per-channel sums
+ *                       (each channel's in the order above, the channels
+ *                       in a fixed-order tree)
  * dx, dscale, dzero_point may each be NULL (not computed). dscale is
  * overwritten (not accumulated); experts without rows get 0. dScale is
  * reduced in a fixed order (no float atomics): an expert's rows are

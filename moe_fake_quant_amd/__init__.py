@@ -38,6 +38,7 @@ FQ_OP_PERMUTE = 1
 FQ_OP_GEMM_FWD = 2
 FQ_OP_GEMM_BWD = 3
 FQ_OP_ACT_SCALE_GRAD = 4
+FQ_GROUP_TENSOR = -1     # one weight scale per expert matrix (int8 / fp8)
 
 EXPORTED = (
     "observer_absmax_init", "fq_quantize_stacked", "fq_moe_permute", "fq_grouped_gemm_fwd",

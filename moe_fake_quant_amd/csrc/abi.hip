@@ -64,6 +64,14 @@ fq_status check_shape(fq_shape s) {
 fq_status check_weight_q(const fq_weight_q *q, fq_shape s, bool need_scales) {
   FQ_CHECK_ARG(q != nullptr, "weight quantizer is NULL");
   FQ_CHECK_ARG(valid_weight_fmt(q->fmt), "unsupported weight format %d", q->fmt);
+  if (q->group == FQ_GROUP_TENSOR) {
+    FQ_CHECK_ARG(q->fmt == FQ_FMT_INT8 || q->fmt == FQ_FMT_FP8_E4M3,
+                 "a per-tensor weight scale needs int8 or fp8 (fmt %d)", q->fmt);
+    FQ_CHECK_ARG(s.K % 16 == 0, "K must be a multiple of 16 (K=%d)", s.K);
+    FQ_CHECK_ARG((size_t)s.N * s.K < (1ull << 31), "matrix too large for a per-tensor scale");
+    FQ_CHECK_ARG(!need_scales || q->scale != nullptr, "scale is NULL");
+    return FQ_OK;
+  }
   FQ_CHECK_ARG(q->group > 0 && s.K % q->group == 0, "group %d must divide K=%d", q->group, s.K);
   FQ_CHECK_ARG(q->group % 16 == 0, "group %d must be a multiple of 16", q->group);
   if (q->fmt == FQ_FMT_NVFP4) FQ_CHECK_ARG(q->group == 16, "nvfp4 blocks are 16 elements");
@@ -85,6 +93,14 @@ fq_status check_act_q(const fq_act_q *aq, int K) {
   return FQ_OK;
 }
 
+// The elementwise kernels see a per-tensor weight quantizer as one group
+// spanning the whole expert matrix (scale index = expert).
+fq_weight_q as_groups(const fq_weight_q &q, fq_shape s) {
+  fq_weight_q g = q;
+  if (q.group == FQ_GROUP_TENSOR) g.group = s.N * s.K;
+  return g;
+}
+
 inline int act_fmt(const fq_act_q *aq) { return aq ? aq->fmt : FQ_FMT_NONE; }
 inline hipStream_t S(fq_stream s) { return reinterpret_cast<hipStream_t>(s); }
 
@@ -104,6 +120,9 @@ size_t gemm_ws(int op, fq_shape s, int R_max, int fmts) {
     // scale and the zero point, and the chunk prefix
     b += 2 * align_up(wgrad_max_chunks(s.E, R_max) * s.N * (s.K / 16) * 4);
     b += align_up((size_t)(s.E + 1) * 4);
+    // per-tensor weight scales: the scale repeated per channel, and the
+    // per-channel dScale before its sum over channels
+    b += 2 * align_up((size_t)s.E * s.N * 4);
   }
   return b;
 }
@@ -162,7 +181,8 @@ fq_status observer_absmax_init(const uint16_t *x, fq_shape s, int32_t fmt, int32
   }
   fq_weight_q q{fmt, group, scale, zero_point, global_scale};
   FQ_TRY(check_weight_q(&q, s, true));
-  launch_observer_weight(x, s, fmt, group, scale, zero_point, global_scale, S(stream));
+  launch_observer_weight(x, s, fmt, as_groups(q, s).group, scale, zero_point, global_scale,
+                         S(stream));
   FQ_CHECK_LAUNCH("observer_absmax_init");
   return FQ_OK;
 }
@@ -175,7 +195,7 @@ fq_status fq_quantize_stacked(const uint16_t *w, fq_shape s, const fq_weight_q *
   FQ_CHECK_ARG(w_fq || codes, "at least one of w_fq and codes must be non-NULL");
   FQ_CHECK_ARG(aligned16(w) && (!w_fq || aligned16(w_fq)), "bf16 tensors must be 16-byte aligned");
   FQ_CHECK_ARG(!codes || ((uintptr_t)codes & 7) == 0, "codes must be 8-byte aligned");
-  launch_quantize_stacked(w, s, *q, w_fq, codes, S(stream));
+  launch_quantize_stacked(w, s, as_groups(*q, s), w_fq, codes, S(stream));
   FQ_CHECK_LAUNCH("fq_quantize_stacked");
   return FQ_OK;
 }
@@ -227,7 +247,7 @@ fq_status fq_grouped_gemm_fwd(const uint16_t *x, int32_t R_max, const int32_t *s
   const uint16_t *wfq = w_fq;
   if (!wfq) {
     uint16_t *t = c.take<uint16_t>((size_t)s.E * s.N * s.K * 2);
-    launch_quantize_stacked(w, s, *wq, t, nullptr, st);
+    launch_quantize_stacked(w, s, as_groups(*wq, s), t, nullptr, st);
     wfq = t;
   }
   const uint16_t *xq = x;
@@ -264,7 +284,8 @@ fq_status fq_grouped_gemm_bwd_scale(const uint16_t *dy, const uint16_t *x, int32
   FQ_CHECK_SUPPORTED((size_t)R_max * (s.K > s.N ? s.K : s.N) * 2 < (1ull << 32) &&
                          (size_t)s.N * s.K * 2 < (1ull << 32),
                      "operands must stay below 4 GiB (32-bit tile offsets)");
-  FQ_CHECK_SUPPORTED(!want_ds || group_ok_for_dscale(wq->group),
+  const bool per_tensor = wq->group == FQ_GROUP_TENSOR;
+  FQ_CHECK_SUPPORTED(!want_ds || per_tensor || group_ok_for_dscale(wq->group),
                      "dScale needs group 16, 32, 64 or a multiple of 128 (group=%d)", wq->group);
   FQ_CHECK_ARG(!want_ds || wq->fmt != FQ_FMT_NVFP4 || aligned16(wq->scale),
                "nvfp4 theta must be 16-byte aligned");
@@ -282,7 +303,7 @@ fq_status fq_grouped_gemm_bwd_scale(const uint16_t *dy, const uint16_t *x, int32
   const uint16_t *wfq = w_fq;
   if (!wfq && dx) {
     uint16_t *t = c.take<uint16_t>((size_t)s.E * s.N * s.K * 2);
-    launch_quantize_stacked(w, s, *wq, t, nullptr, st);
+    launch_quantize_stacked(w, s, as_groups(*wq, s), t, nullptr, st);
     wfq = t;
   }
   if (dx && R_max > 0) {
@@ -300,7 +321,18 @@ fq_status fq_grouped_gemm_bwd_scale(const uint16_t *dy, const uint16_t *x, int32
     float *ps = c.take<float>(part);
     float *pz = c.take<float>(part);
     int *cs = c.take<int>((size_t)(s.E + 1) * 4);
-    launch_gemm_wgrad_dscale(dy, xq, seg, s, w, *wq, dscale, dzp, ps, dzp ? pz : nullptr, cs, st);
+    if (per_tensor) {
+      // per channel over the repeated scale, then the fixed-order sum over channels
+      float *rep = c.take<float>((size_t)s.E * s.N * 4);
+      float *dch = c.take<float>((size_t)s.E * s.N * 4);
+      launch_repeat_rows(wq->scale, s.E, s.N, rep, st);
+      fq_weight_q qc{wq->fmt, s.K, rep, nullptr, nullptr};
+      launch_gemm_wgrad_dscale(dy, xq, seg, s, w, qc, dch, nullptr, ps, nullptr, cs, st);
+      launch_sum_rows(dch, s.E, s.N, dscale, st);
+    } else {
+      launch_gemm_wgrad_dscale(dy, xq, seg, s, w, *wq, dscale, dzp, ps, dzp ? pz : nullptr, cs,
+                               st);
+    }
   }
   FQ_CHECK_LAUNCH("fq_grouped_gemm_bwd_scale");
   return FQ_OK;

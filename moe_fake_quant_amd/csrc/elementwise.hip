@@ -32,6 +32,12 @@ __global__ void k_fill_u32(uint32_t *p, uint32_t v, long n) {
     p[i] = v;
 }
 
+__global__ void k_repeat_rows(const float *__restrict__ v, uint32_t total, FastDiv n,
+                              float *__restrict__ out) {
+  for (uint32_t i = blockIdx.x * blockDim.x + threadIdx.x; i < total; i += gridDim.x * blockDim.x)
+    out[i] = v[n.div(i)];
+}
+
 // ------------------------------------------- stacked weight fake-quant -----
 // One thread-iteration handles one 8-element vector of one row. Requires
 // group % 8 == 0 so a vector never straddles a scale group.
@@ -409,6 +415,16 @@ __device__ __forceinline__ float block_sum_fixed(float v) {
   return s;
 }
 
+// out[row] = sum of in[row, 0:n], one block per row, fixed order.
+__global__ __launch_bounds__(kThreads) void k_sum_rows(const float *__restrict__ in, uint32_t n,
+                                                       float *__restrict__ out) {
+  const float *p = in + (size_t)blockIdx.x * n;
+  float v = 0.0f;
+  for (uint32_t i = threadIdx.x; i < n; i += kThreads) v += p[i];
+  v = block_sum_fixed<kThreads>(v);
+  if (threadIdx.x == 0) out[blockIdx.x] = v;
+}
+
 // out[0] = sum of the n block partials (one block, fixed order).
 constexpr int kSumThreads = 1024;
 __global__ __launch_bounds__(kSumThreads) void k_sum_partials(const float *__restrict__ part,
@@ -673,6 +689,18 @@ __global__ __launch_bounds__(kThreads) void k_unpermute_reduce(
 void launch_fill_u32(uint32_t *p, uint32_t v, long n, hipStream_t st) {
   if (n <= 0) return;
   hipLaunchKernelGGL(k_fill_u32, dim3(grid_for(n)), dim3(kThreads), 0, st, p, v, n);
+}
+
+void launch_repeat_rows(const float *v, int rows, int n, float *out, hipStream_t st) {
+  const uint32_t total = (uint32_t)((size_t)rows * n);
+  if (!total) return;
+  hipLaunchKernelGGL(k_repeat_rows, dim3(grid_for(total)), dim3(kThreads), 0, st, v, total,
+                     FastDiv((uint32_t)n), out);
+}
+
+void launch_sum_rows(const float *in, int rows, int n, float *out, hipStream_t st) {
+  if (rows <= 0) return;
+  hipLaunchKernelGGL(k_sum_rows, dim3(rows), dim3(kThreads), 0, st, in, (uint32_t)n, out);
 }
 
 void launch_quantize_stacked(const uint16_t *w, fq_shape s, const fq_weight_q &q, uint16_t *out,

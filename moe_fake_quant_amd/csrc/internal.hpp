@@ -7,6 +7,10 @@
 namespace fq {
 
 void launch_fill_u32(uint32_t *p, uint32_t v, long n, hipStream_t st);
+// out[r * n + i] = v[r] for r < rows, i < n
+void launch_repeat_rows(const float *v, int rows, int n, float *out, hipStream_t st);
+// out[r] = sum over i < n of in[r * n + i], in a fixed order (bitwise reproducible)
+void launch_sum_rows(const float *in, int rows, int n, float *out, hipStream_t st);
 void launch_quantize_stacked(const uint16_t *w, fq_shape s, const fq_weight_q &q, uint16_t *out,
                              uint8_t *codes, hipStream_t st);
 void launch_observer_weight(const uint16_t *w, fq_shape s, int fmt, int group, float *scale,

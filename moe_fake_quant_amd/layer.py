@@ -22,18 +22,18 @@ from typing import Optional
 
 import torch
 
-from . import (ActQ, FMT_FP8_E4M3, FMT_INT4, FMT_INT8, FMT_NONE, FMT_NVFP4, FQ_OP_ACT_SCALE_GRAD,
-               FQ_OP_GEMM_BWD, FQ_OP_GEMM_FWD, FQ_OP_PERMUTE, WeightQ, fq_grouped_gemm_bwd_scale, fq_grouped_gemm_fwd,
+from . import (ActQ, FMT_FP8_E4M3, FMT_INT4, FMT_INT8, FMT_NONE, FMT_NVFP4, FQ_GROUP_TENSOR,
+               FQ_OP_ACT_SCALE_GRAD, FQ_OP_GEMM_BWD, FQ_OP_GEMM_FWD, FQ_OP_PERMUTE, WeightQ, fq_grouped_gemm_bwd_scale, fq_grouped_gemm_fwd,
                fq_moe_combine, fq_moe_combine_bwd, fq_moe_gather_actfq, fq_moe_permute,
                fq_moe_unpermute_reduce, fq_quantize_stacked, fq_swiglu_actfq, fq_swiglu_bwd,
                fq_workspace_bytes, observer_absmax_init)
 
 
 def _weight_q(E, N, K, fmt, group, dev) -> WeightQ:
-    G = K // group
-    q = WeightQ(fmt=fmt, group=group, scale=torch.empty(E, N, G, dtype=torch.float32, device=dev))
+    shape = (E,) if group == FQ_GROUP_TENSOR else (E, N, K // group)
+    q = WeightQ(fmt=fmt, group=group, scale=torch.empty(shape, dtype=torch.float32, device=dev))
     if fmt == FMT_INT4:
-        q.zero_point = torch.empty(E, N, G, dtype=torch.float32, device=dev)
+        q.zero_point = torch.empty(shape, dtype=torch.float32, device=dev)
     if fmt == FMT_NVFP4:
         q.global_scale = torch.empty(E, dtype=torch.float32, device=dev)
     return q
@@ -44,7 +44,8 @@ class MoEFakeQuantLayer:
                  topk: int, expert_begin: int = 0, group: Optional[int] = None,
                  learn_act_scales: bool = False):
         """w_gu [E, 2F, H], w_d [E, H, F] bf16 on the device (frozen). group None =
-        one scale per output channel (group = K of each stack). learn_act_scales:
+        one scale per output channel (group = K of each stack); FQ_GROUP_TENSOR =
+        one scale per expert matrix (int8 / fp8). learn_act_scales:
         the backward also produces the activation-scale gradients (FP8 / INT8)."""
         assert w_gu.dtype == torch.bfloat16 and w_d.dtype == torch.bfloat16
         self.dev = w_gu.device

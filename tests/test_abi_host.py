@@ -110,10 +110,12 @@ def test_workspace_sizes(pkg):
         _up(E * N * K * 2) + _up(R * K * 2)
     # backward: dScale partials (scale and zero point) per wgrad row chunk of
     # at most 2048 rows (every expert has at least one) and 16-block of K,
-    # plus the chunk prefix
+    # plus the chunk prefix, plus (per-tensor scales) the scale repeated per
+    # channel and the per-channel dScale
     chunks = (R + 2047) // 2048 + E
     part = _up(chunks * N * (K // 16) * 4)
-    assert _ws(pkg, pkg.FQ_OP_GEMM_BWD, (E, N, K), R) == 2 * part + _up((E + 1) * 4)
+    assert _ws(pkg, pkg.FQ_OP_GEMM_BWD, (E, N, K), R) == \
+        2 * part + _up((E + 1) * 4) + 2 * _up(E * N * 4)
     # permute: grows with the pair count, positive for any expert count
     a = _ws(pkg, pkg.FQ_OP_PERMUTE, (4, 0, 0), 1000)
     b = _ws(pkg, pkg.FQ_OP_PERMUTE, (4, 0, 0), 100000)
@@ -216,6 +218,20 @@ def test_permute_and_elementwise_reject_bad_arguments(pkg):
                                      None) == pkg.FQ_ERR_INVALID_ARGUMENT  # act mask needs x
     assert L.observer_absmax_init(FAKE, pkg.fq_shape(1, 4, 12), pkg.FMT_INT8, 12, 0, FAKE, None,
                                   None, None, 0, None) == pkg.FQ_ERR_INVALID_ARGUMENT  # K % 8
+
+
+@host_only
+def test_per_tensor_weight_scale_arguments(pkg):
+    """FQ_GROUP_TENSOR: int8 / fp8 only, scale required."""
+    L = pkg.lib()
+    shape = pkg.fq_shape(2, 256, 256)
+    for fmt, scale, want in ((pkg.FMT_INT4, FAKE, pkg.FQ_ERR_INVALID_ARGUMENT),
+                             (pkg.FMT_NVFP4, FAKE, pkg.FQ_ERR_INVALID_ARGUMENT),
+                             (pkg.FMT_FP8_E4M3, None, pkg.FQ_ERR_INVALID_ARGUMENT)):
+        q = pkg.fq_weight_q(fmt, pkg.FQ_GROUP_TENSOR, scale, FAKE, FAKE)
+        assert L.fq_quantize_stacked(FAKE, shape, ctypes.byref(q), FAKE, None, None) == want
+    assert L.observer_absmax_init(FAKE, shape, pkg.FMT_INT4, pkg.FQ_GROUP_TENSOR, 0, FAKE, FAKE,
+                                  None, None, 0, None) == pkg.FQ_ERR_INVALID_ARGUMENT
 
 
 @host_only

@@ -282,6 +282,58 @@ def test_gemm_bwd_parity(name, fmt, afmt, grouping):
         check_dscale_tol(dzp.cpu().numpy(), dzp_ref, "dzero_point")
 
 
+@pytest.mark.parametrize("name,fmt", [("int8", O.FMT_INT8), ("fp8", O.FMT_FP8)])
+def test_per_tensor_weight_scales(name, fmt):
+    """One scale per expert matrix: observer and FQ pass bit-exact, forward
+    and backward (dX, dScale [E]) to the GEMM / dScale tolerances."""
+    rng = np.random.default_rng(750 + fmt)
+    E, N, K = 4, 256, 512
+    seg = _segments(rng, E, [90, 0, 301, 33])
+    R = int(seg[-1])
+    R_max = R + 17
+    GT = F.FQ_GROUP_TENSOR
+    w = _rand_w(rng, E, N, K)
+    s_ref, _, _ = O.observer_weight(w, fmt, O.GROUP_TENSOR)
+    s_dev = torch.full((E,), -1.0, device="cuda")
+    wd = dev_bf16(w)
+    F.observer_absmax_init(wd, (E, N, K), fmt, GT, 0, s_dev)
+    torch.cuda.synchronize()
+    assert np.array_equal(s_dev.cpu().numpy().view(np.uint32), s_ref.view(np.uint32))
+    s = (s_ref * rng.uniform(0.3, 0.9, E)).astype(np.float32)     # saturate the outliers
+    wq = F.WeightQ(fmt=fmt, group=GT, scale=dev_f32(s))
+    ref = O.fq_weight_stack(w, fmt, O.GROUP_TENSOR, s)
+    assert not ref.mask.all()
+    wfq = torch.empty_like(wd)
+    codes = torch.zeros(E * N * K, dtype=torch.uint8, device="cuda")
+    F.fq_quantize_stacked(wd, (E, N, K), wq, wfq, codes)
+    torch.cuda.synchronize()
+    assert np.array_equal(host_bits(wfq), ref.bits)
+    assert np.array_equal(codes.cpu().numpy(), pack_codes(ref.code, fmt))
+    afmt = O.FMT_FP8
+    x = O.f32_to_bf16(rng.standard_normal((R_max, K)).astype(np.float32))
+    dy = O.f32_to_bf16(rng.standard_normal((R_max, N)).astype(np.float32))
+    sa = np.float32(O.observer_act(x[:R], afmt) * 0.8)
+    aq = F.ActQ(afmt, dev_f32([sa]))
+    ws = torch.empty(max(F.fq_workspace_bytes(F.FQ_OP_GEMM_FWD, (E, N, K), R_max, fmt | afmt << 8),
+                         F.fq_workspace_bytes(F.FQ_OP_GEMM_BWD, (E, N, K), R_max, fmt | afmt << 8)),
+                     dtype=torch.uint8, device="cuda")
+    y = torch.empty(R_max, N, dtype=torch.bfloat16, device="cuda")
+    F.fq_grouped_gemm_fwd(dev_bf16(x), R_max, dev_i32(seg), (E, N, K), wd, None, wq, aq, y, ws)
+    dx = torch.empty(R_max, K, dtype=torch.bfloat16, device="cuda")
+    ds = torch.full((E,), 7.0, device="cuda")
+    F.fq_grouped_gemm_bwd_scale(dev_bf16(dy), dev_bf16(x), R_max, dev_i32(seg), (E, N, K), wd,
+                                None, wq, aq, dx, ds, None, ws)
+    torch.cuda.synchronize()
+    check_gemm_tol(host_bits(y)[:R], O.grouped_gemm_fwd(x, seg, w, fmt, O.GROUP_TENSOR, s,
+                                                        afmt=afmt, act_scale=sa), "y")
+    dx_ref, ds_ref, _ = O.grouped_gemm_bwd(dy, x, seg, w, fmt, O.GROUP_TENSOR, s, afmt=afmt,
+                                           act_scale=sa)
+    check_gemm_tol(host_bits(dx)[:R], dx_ref, "dx")
+    dsh = ds.cpu().numpy()
+    assert dsh.shape == (E,) and dsh[1] == 0.0
+    check_dscale_tol(dsh, ds_ref, "dscale per tensor")
+
+
 def test_bwd_deterministic_run_to_run():
     rng = np.random.default_rng(800)
     E, N, K = 3, 256, 256

@@ -30,6 +30,8 @@ CASES = [
     ("w4afp8", O.FMT_INT4, O.FMT_FP8, 128, 260, 8, 8, 0, None, True),
     ("w8a8-int8", O.FMT_INT8, O.FMT_INT8, None, 260, 8, 8, 0, None, True),
     ("fp8-learn-act-local", O.FMT_FP8, O.FMT_FP8, None, 500, 16, 8, 4, None, True),
+    # fp8_static: per-tensor weights and activations
+    ("fp8-static", O.FMT_FP8, O.FMT_FP8, O.GROUP_TENSOR, 260, 8, 8, 0, None, True),
 ]
 
 

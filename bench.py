@@ -67,6 +67,11 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=4, choices=[3, 4, 5])
+    ap.add_argument("--act-scales", choices=["frozen", "learnable"], default="frozen",
+                    help="learnable: the backward also forms the activation-scale gradients "
+                         "(fp8 workload only)")
+    ap.add_argument("--weight-scales", choices=["default", "per-tensor"], default="default",
+                    help="per-tensor: one scale per expert matrix (fp8 workload only)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-experts", type=int, default=6)
     ap.add_argument("--seed", type=int, default=0)
@@ -117,10 +122,16 @@ def main():
     import workloads as W
 
     dev = torch.device("cuda:0")
+    fmt = {3: F.FMT_FP8_E4M3, 4: F.FMT_NVFP4, 5: F.FMT_NVFP4}[args.config]
+    learn = args.act_scales == "learnable"
+    per_tensor = args.weight_scales == "per-tensor"
+    if (learn or per_tensor) and fmt != F.FMT_FP8_E4M3:
+        print("learnable activation scales and per-tensor weight scales exist for the fp8 "
+              "workload (--config 3) only", file=sys.stderr)
+        sys.exit(2)
+    group = (F.FQ_GROUP_TENSOR if per_tensor else None) if fmt == F.FMT_FP8_E4M3 else 16
     t_gen = time.time()
     case = W.config(args.config, seed=args.seed)
-    fmt = {3: F.FMT_FP8_E4M3, 4: F.FMT_NVFP4, 5: F.FMT_NVFP4}[args.config]
-    group = None if fmt == F.FMT_FP8_E4M3 else 16
     bf = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)  # noqa: E731
     w_gu, w_d = bf(case.w_gu), bf(case.w_d)
     x = bf(case.x)
@@ -129,7 +140,8 @@ def main():
     dout = bf(case.dout)
     t_gen = time.time() - t_gen
 
-    layer = F.MoEFakeQuantLayer(w_gu, w_d, fmt, fmt, case.T, case.topk, case.expert_begin, group)
+    layer = F.MoEFakeQuantLayer(w_gu, w_d, fmt, fmt, case.T, case.topk, case.expert_begin, group,
+                                learn_act_scales=learn)
     layer.init_weight_scales()
     layer.calibrate(x, ids)
     torch.cuda.synchronize()
@@ -191,6 +203,8 @@ def main():
     nel = E * (2 * Fh * H + H * Fh)
     if fmt == F.FMT_NVFP4:
         scale_bytes = (nel // 16) * 4 + 2 * E * 4
+    elif per_tensor:
+        scale_bytes = 2 * E * 4
     else:
         scale_bytes = E * (2 * Fh + H) * 4
     fq_bytes = nel * 4 + scale_bytes
@@ -247,6 +261,9 @@ def main():
             "experts": E, "hidden": H, "expert_ffn": Fh, "tokens": case.T, "topk": case.topk,
             "routed_rows": R, "weight_format": {3: "fp8_e4m3", 4: "nvfp4", 5: "nvfp4"}[args.config],
             "act_format": {3: "fp8_e4m3", 4: "nvfp4", 5: "nvfp4"}[args.config],
+            "weight_scales": ("per-tensor" if per_tensor else "per-channel")
+            if fmt == F.FMT_FP8_E4M3 else "block16",
+            "act_scales": args.act_scales,
             "flops_per_step": flops_step,
         },
         "pct_bf16_peak": round(100 * tflops / MI355X_BF16_PEAK_TFLOPS, 2),
@@ -283,8 +300,7 @@ def cpu_baseline(case, fmt, group, n_experts):
                     expert_begin=0, w_gu=case.w_gu[:E], w_d=case.w_d[:E], x=case.x,
                     expert_ids=case.expert_ids, probs=case.probs, dout=case.dout)
     wfmt = O.FMT_NVFP4 if fmt == 4 else O.FMT_FP8
-    g = 16 if group else None
-    perm, row_of, seg = O.moe_permute(case.expert_ids, 0, E)
+    _, _, seg = O.moe_permute(case.expert_ids, 0, E)
     R = int(seg[-1])
     try:
         from threadpoolctl import threadpool_info
@@ -293,25 +309,9 @@ def cpu_baseline(case, fmt, group, n_experts):
     except Exception:
         cores = 1
     t0 = time.perf_counter()
-    if g:
-        O.moe_layer(sub, wfmt, g, wfmt)
-    else:
-        # per-channel scales: group = K of each stack
-        from oracle import moe as M
-        wq_gu = O.observer_weight(sub.w_gu, wfmt, sub.w_gu.shape[2])
-        wq_d = O.observer_weight(sub.w_d, wfmt, sub.w_d.shape[2])
-        s1 = O.observer_act(sub.x, wfmt)
-        xq = M.gather_actfq(sub.x, perm, sub.topk, wfmt, s1)
-        h = O.grouped_gemm_fwd(xq.bits, seg, sub.w_gu, wfmt, sub.w_gu.shape[2], *wq_gu)
-        s2 = O.observer_act(M.swiglu_fwd(h), wfmt)
-        a, aq = M.swiglu_actfq(h, wfmt, s2)
-        o = O.grouped_gemm_fwd(aq.bits, seg, sub.w_d, wfmt, sub.w_d.shape[2], *wq_d)
-        M.combine(o, sub.probs, row_of)
-        do = M.combine_bwd(sub.dout, sub.probs, perm, sub.topk)
-        daq, _, _ = O.grouped_gemm_bwd(do, aq.bits, seg, sub.w_d, wfmt, sub.w_d.shape[2], *wq_d)
-        dh = M.swiglu_bwd(daq, h, wfmt, s2, a_bits=a)
-        dxq, _, _ = O.grouped_gemm_bwd(dh, xq.bits, seg, sub.w_gu, wfmt, sub.w_gu.shape[2], *wq_gu)
-        M.unpermute_reduce(dxq, row_of, sub.x, wfmt, s1)
+    # group: 16 (nvfp4 blocks), None (one scale per output channel) or the
+    # per-tensor marker, the same values the oracle takes
+    O.moe_layer(sub, wfmt, group, wfmt)
     dt = time.perf_counter() - t0
     flops = FLOPS_PER_ROW * R
     return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": cores,

@@ -45,11 +45,17 @@ reading where it applies:
   R-16 chained tests feed the GPU-calibrated activation scales to the oracle
   R-17 MoE weights drawn N(0, 0.02)
   R-18 the skewed local-share workload forces experts {3, 7, 11, 15} empty
-  R-19 a learnable activation scale exists for the static per-tensor formats
+  R-19 FP8 scales: weights per output channel amax/448, activations one
+       frozen per-tensor amax/448 per projection input
+  R-20 every stored intermediate is bf16; accumulation in fp64 here
+  R-21 empty experts get dScale (and dZP) exactly 0
+  R-22 in the layer, dA is masked by the act-FQ mask of A and dX by that of
+       X; dynamic NVFP4 activation block scales are constants
+  R-23 a learnable activation scale exists for the static per-tensor formats
        (FP8, INT8) only; its gradient uses the weights' STE factor, summed
        over every element the quantizer saw in the step. NVFP4 activations
        derive their block scales from the data and keep g_a at calibration.
-  R-20 a per-tensor weight scale is one scale per expert matrix [N, K] of a
+  R-24 a per-tensor weight scale is one scale per expert matrix [N, K] of a
        stack (each expert is its own linear); INT8 / FP8 only
 
 Parity status: every function here is pinned by the ``-m "not gpu"`` tests

@@ -46,7 +46,7 @@ INT8_LO, INT8_HI = -128.0, 127.0      # full two's-complement range (R-3)
 INT4_LO, INT4_HI = 0.0, 15.0          # unsigned codes, integer zero point
 NVFP4_BLOCK = 16
 # One weight scale per expert matrix [N, K] (the per-tensor weight preset of
-# the QAT + ZeRO-3 page's fp8_static example; INT8 / FP8 only, R-20).
+# the QAT + ZeRO-3 page's fp8_static example; INT8 / FP8 only, R-24).
 GROUP_TENSOR = -1
 INT4_GROUP = 128
 

@@ -16,13 +16,13 @@ Forward, per routed row r of expert e (token t = perm[r] // k):
   O     = Aq . FQ(W_d[e])^T                             bf16
   out[t] = bf16(sum_j p[t,j] * O[row_of[t,j]])           slots ascending
 Backward (dX and the weight-scale gradients; activation scales frozen unless
-learnable, R-19):
+learnable, R-23):
   dO[r]  = bf16(p[t,j] * dOut[t])
   dA     = bf16(m_a2 * (dO . FQ(W_d[e])))               + dS_d from dO^T . Aq
   dH     = bf16(SwiGLU'(H) applied to dA)
   dXq    = bf16(dH . FQ(W_gu[e]))                       + dS_gu from dH^T . Xq
   dX[t]  = bf16(m_a1(X[t]) * sum_j dXq[row_of[t,j]])
-  dS_a1  = sum over t, h of (sum_j dXq[row_of[t,j], h]) * dv/ds(X[t, h])  (R-19)
+  dS_a1  = sum over t, h of (sum_j dXq[row_of[t,j], h]) * dv/ds(X[t, h])  (R-23)
   dS_a2  = sum over r, f of dAq[r, f] * dv/ds(A[r, f])
 Float64 everywhere except where the GPU stores bf16.
 """
@@ -124,7 +124,7 @@ def unpermute_reduce(dxq_bits, row_of, x_bits, afmt: int, act_scale):
 
 
 def act_scale_grad(x_bits, g, afmt: int, act_scale) -> float:
-    """Gradient of a learnable per-tensor activation scale s_a (R-19).
+    """Gradient of a learnable per-tensor activation scale s_a (R-23).
 
     FQ_a maps every element x of the tensor to v = q(x / s_a) * s_a; with the
     round passed straight through (R-13, R-14) dv/ds_a is the same factor as for

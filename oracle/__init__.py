@@ -75,6 +75,7 @@ from .codecs import (  # noqa: F401
 from .observer import observer_weight, observer_act  # noqa: F401
 from .permute import moe_permute  # noqa: F401
 from .gemm import grouped_gemm_fwd, grouped_gemm_bwd  # noqa: F401
+from .export import pack_codes, unpack_codes, export_scales, dequantize  # noqa: F401
 from .moe import (  # noqa: F401
     gather_actfq, swiglu_fwd, swiglu_actfq, swiglu_bwd, combine, combine_bwd,
     unpermute_reduce, unpermute_sum, act_scale_grad, moe_layer,

@@ -1,5 +1,5 @@
 """Shared helpers of the test suite (bf16 bits <-> torch device tensors,
-tolerance checks, code packing as libfq lays it out)."""
+tolerance checks)."""
 import numpy as np
 import torch
 
@@ -54,13 +54,3 @@ def check_act_dscale_tol(gpu, ref, abs_terms, what="", tol=ACT_DSCALE_TOL):
     err = abs(float(gpu) - float(ref))
     assert err <= tol * abs_terms, f"{what}: |err| {err:.4g} > {tol} * {abs_terms:.4g}"
     return err / max(abs_terms, 1e-30)
-
-
-def pack_codes(code: np.ndarray, fmt: int) -> np.ndarray:
-    """Codes as libfq writes them: one byte per element for int8 / fp8; two
-    4-bit codes per byte (even k low nibble) for int4 / nvfp4."""
-    c = np.asarray(code, np.int64).reshape(-1)
-    if fmt in (1, 3):
-        return (c & 0xFF).astype(np.uint8)
-    c = (c & 0xF).astype(np.uint8)
-    return (c[0::2] | (c[1::2] << 4)).astype(np.uint8)

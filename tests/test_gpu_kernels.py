@@ -9,7 +9,7 @@ import torch
 import oracle as O
 import workloads as W
 from helpers import (bf16_vals, check_dscale_tol, check_gemm_tol, dev_bf16, dev_f32, dev_i32,
-                     host_bits, pack_codes)
+                     host_bits)
 
 pytestmark = pytest.mark.gpu
 
@@ -63,7 +63,7 @@ def test_quantize_stacked_bitexact_observer_scales(name, fmt):
     F.fq_quantize_stacked(wd, (E, N, K), _wq(fmt, group, s, zp, g), out, codes)
     torch.cuda.synchronize()
     assert np.array_equal(host_bits(out), ref.bits)
-    assert np.array_equal(codes.cpu().numpy(), pack_codes(ref.code, fmt))
+    assert np.array_equal(codes.cpu().numpy(), O.pack_codes(ref.code, fmt))
 
 
 @pytest.mark.parametrize("name,fmt", FMTS)
@@ -308,7 +308,7 @@ def test_per_tensor_weight_scales(name, fmt):
     F.fq_quantize_stacked(wd, (E, N, K), wq, wfq, codes)
     torch.cuda.synchronize()
     assert np.array_equal(host_bits(wfq), ref.bits)
-    assert np.array_equal(codes.cpu().numpy(), pack_codes(ref.code, fmt))
+    assert np.array_equal(codes.cpu().numpy(), O.pack_codes(ref.code, fmt))
     afmt = O.FMT_FP8
     x = O.f32_to_bf16(rng.standard_normal((R_max, K)).astype(np.float32))
     dy = O.f32_to_bf16(rng.standard_normal((R_max, N)).astype(np.float32))

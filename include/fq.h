@@ -165,6 +165,39 @@ fq_status fq_quantize_stacked(const uint16_t *w_bf16, fq_shape shape, const fq_w
                               uint16_t *w_fq_bf16, uint8_t *codes, fq_stream stream);
 
 /* ------------------------------------------------------------------------
+ * Real-quantized export (QAT + ZeRO-3 page, convert / save_format=real: each
+ * quantized linear keeps its codes with its weight scale; mcore_qad article,
+ * section 三: the formats' stored layouts are the deployment side's).
+ * The codes are fq_quantize_stacked's `codes` output. The stored tensors:
+ *   int8 : codes int8 [E,N,K]; scale fp32 [E,N,K/group] (or [E] per tensor)
+ *   fp8  : codes E4M3 bytes [E,N,K]; scale fp32 as int8
+ *   int4 : codes [E,N,K/2] (even k in the low nibble); scale fp32
+ *          [E,N,K/group]; zero point uint8 [E,N,K/group]
+ *   nvfp4: codes [E,N,K/2] (E2M1, sign in bit 3, even k low); block scale
+ *          E4M3 bytes [E,N,K/16]; tensor scale fp32 [E] (global_scale)
+ *
+ * fq_export_scales: the parameters that change form.
+ *   nvfp4: scale_bytes[e,n,b] = E4M3 code of clamp(theta, 0, 448) (the
+ *          rounding the forward applies to theta); theta 16-byte aligned,
+ *          scale_bytes 4-byte aligned.
+ *   int4 : zero_point_bytes[e,n,g] = clamp(rne(zp), 0, 15).
+ *   int8 / fp8 store their fp32 scale unchanged: FQ_ERR_INVALID_ARGUMENT.
+ * fq_dequantize_stacked: w_bf16[e,n,k] = bf16(fp32(value(code) * s)) with s
+ *   the group scale (int4: value = code - zero point, +0.0 for 0; nvfp4:
+ *   s = fp32(E4M3 value(scale byte) * global_scale[e])), the FQ pass's own
+ *   arithmetic: decoding an export gives exactly the fake-quant values.
+ *   group as in fq_weight_q (FQ_GROUP_TENSOR for int8 / fp8 per tensor);
+ *   unused pointers may be NULL. Requires K % 16 == 0, codes 8-byte and
+ *   w_bf16 16-byte aligned.
+ * ---------------------------------------------------------------------- */
+fq_status fq_export_scales(fq_shape shape, const fq_weight_q *q, uint8_t *scale_bytes,
+                           uint8_t *zero_point_bytes, fq_stream stream);
+fq_status fq_dequantize_stacked(const uint8_t *codes, fq_shape shape, int32_t fmt, int32_t group,
+                                const float *scale, const uint8_t *scale_bytes,
+                                const uint8_t *zero_point_bytes, const float *global_scale,
+                                uint16_t *w_bf16, fq_stream stream);
+
+/* ------------------------------------------------------------------------
  * fq_moe_permute -- routed-token permutation for one grouped GEMM over all
  * local experts (mcore_qad article, section 二.4: one GEMM over routed
  * tokens needs each expert's rows contiguous).

@@ -44,7 +44,7 @@ EXPORTED = (
     "observer_absmax_init", "fq_quantize_stacked", "fq_moe_permute", "fq_grouped_gemm_fwd",
     "fq_grouped_gemm_bwd_scale", "fq_moe_gather_actfq", "fq_swiglu_actfq", "fq_swiglu_bwd",
     "fq_moe_combine", "fq_moe_combine_bwd", "fq_moe_unpermute_reduce", "fq_workspace_bytes",
-    "fq_last_error", "fq_abi_version",
+    "fq_last_error", "fq_abi_version", "fq_export_scales", "fq_dequantize_stacked",
 )
 
 
@@ -90,6 +90,8 @@ def _load() -> ctypes.CDLL:
         "fq_moe_combine_bwd": (st, [P, P, P, I32, I32, I32, P, P]),
         "fq_moe_unpermute_reduce": (st, [P, P, P, I32, I32, I32, ctypes.POINTER(fq_act_q), P, P,
                                          P, SZ, P]),
+        "fq_export_scales": (st, [fq_shape, ctypes.POINTER(fq_weight_q), P, P, P]),
+        "fq_dequantize_stacked": (st, [P, fq_shape, I32, I32, P, P, P, P, P, P]),
         "fq_workspace_bytes": (SZ, [I32, fq_shape, I32, I32]),
         "fq_last_error": (ctypes.c_char_p, []),
         "fq_abi_version": (I32, []),
@@ -235,6 +237,18 @@ def fq_moe_unpermute_reduce(dxq, row_of, x, T, topk, H, aq: Optional[ActQ], dx, 
     _check(_lib.fq_moe_unpermute_reduce(_p(dxq), _p(row_of), _p(x), int(T), int(topk), int(H),
                                         _aq(aq), _p(dx), _p(dscale_a), _p(ws), _nbytes(ws),
                                         _stream()))
+
+
+def fq_export_scales(shape, q: WeightQ, scale_bytes=None, zero_point_bytes=None):
+    _check(_lib.fq_export_scales(_shape(*shape), ctypes.byref(q.c()), _p(scale_bytes),
+                                 _p(zero_point_bytes), _stream()))
+
+
+def fq_dequantize_stacked(codes, shape, fmt, group, w_bf16, scale=None, scale_bytes=None,
+                          zero_point_bytes=None, global_scale=None):
+    _check(_lib.fq_dequantize_stacked(_p(codes), _shape(*shape), int(fmt), int(group), _p(scale),
+                                      _p(scale_bytes), _p(zero_point_bytes), _p(global_scale),
+                                      _p(w_bf16), _stream()))
 
 
 from .layer import MoEFakeQuantLayer  # noqa: E402,F401

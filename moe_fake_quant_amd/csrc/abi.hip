@@ -200,6 +200,59 @@ fq_status fq_quantize_stacked(const uint16_t *w, fq_shape s, const fq_weight_q *
   return FQ_OK;
 }
 
+fq_status fq_export_scales(fq_shape s, const fq_weight_q *q, uint8_t *scale_bytes,
+                           uint8_t *zero_point_bytes, fq_stream stream) {
+  FQ_TRY(check_shape(s));
+  FQ_TRY(check_weight_q(q, s, true));
+  FQ_CHECK_ARG(q->fmt == FQ_FMT_NVFP4 || q->fmt == FQ_FMT_INT4,
+               "only nvfp4 (block scale bytes) and int4 (zero-point bytes) have parameters to "
+               "convert (fmt %d)", q->fmt);
+  const size_t ng = (size_t)s.E * s.N * (s.K / q->group);
+  if (q->fmt == FQ_FMT_NVFP4) {
+    FQ_CHECK_ARG(scale_bytes != nullptr, "scale_bytes is NULL");
+    FQ_CHECK_ARG(aligned16(q->scale) && ((uintptr_t)scale_bytes & 3) == 0,
+                 "theta must be 16-byte and scale_bytes 4-byte aligned");
+    launch_export_theta(q->scale, ng, scale_bytes, S(stream));
+  } else {
+    FQ_CHECK_ARG(zero_point_bytes != nullptr, "zero_point_bytes is NULL");
+    launch_export_zp(q->zero_point, ng, zero_point_bytes, S(stream));
+  }
+  FQ_CHECK_LAUNCH("fq_export_scales");
+  return FQ_OK;
+}
+
+fq_status fq_dequantize_stacked(const uint8_t *codes, fq_shape s, int32_t fmt, int32_t group,
+                                const float *scale, const uint8_t *scale_bytes,
+                                const uint8_t *zero_point_bytes, const float *global_scale,
+                                uint16_t *w_bf16, fq_stream stream) {
+  FQ_TRY(check_shape(s));
+  FQ_CHECK_ARG(codes && w_bf16, "codes and w_bf16 must be non-NULL");
+  FQ_CHECK_ARG(s.K % 16 == 0, "K must be a multiple of 16 (K=%d)", s.K);
+  FQ_CHECK_ARG(((uintptr_t)codes & 7) == 0 && aligned16(w_bf16),
+               "codes must be 8-byte and w_bf16 16-byte aligned");
+  FQ_CHECK_ARG(valid_weight_fmt(fmt), "unsupported weight format %d", fmt);
+  int g = group;
+  if (fmt == FQ_FMT_NVFP4) {
+    FQ_CHECK_ARG(group == 16, "nvfp4 blocks are 16 elements");
+    FQ_CHECK_ARG(scale_bytes && global_scale, "nvfp4 needs scale_bytes and global_scale");
+  } else if (group == FQ_GROUP_TENSOR) {
+    FQ_CHECK_ARG(fmt == FQ_FMT_INT8 || fmt == FQ_FMT_FP8_E4M3,
+                 "a per-tensor weight scale needs int8 or fp8 (fmt %d)", fmt);
+    FQ_CHECK_ARG((size_t)s.N * s.K < (1ull << 31), "matrix too large for a per-tensor scale");
+    FQ_CHECK_ARG(scale != nullptr, "scale is NULL");
+    g = s.N * s.K;
+  } else {
+    FQ_CHECK_ARG(group > 0 && s.K % group == 0 && group % 16 == 0,
+                 "group %d must divide K=%d and be a multiple of 16", group, s.K);
+    FQ_CHECK_ARG(scale != nullptr, "scale is NULL");
+    FQ_CHECK_ARG(fmt != FQ_FMT_INT4 || zero_point_bytes, "int4 needs zero_point_bytes");
+  }
+  launch_dequantize(codes, s, fmt, g, scale, scale_bytes, zero_point_bytes, global_scale, w_bf16,
+                    S(stream));
+  FQ_CHECK_LAUNCH("fq_dequantize_stacked");
+  return FQ_OK;
+}
+
 fq_status fq_moe_permute(const int32_t *ids, int32_t T, int32_t topk, int32_t ebegin, int32_t E,
                          int32_t *perm, int32_t *row_of, int32_t *seg, void *ws, size_t ws_bytes,
                          fq_stream stream) {

@@ -40,6 +40,14 @@ void launch_unpermute_reduce(const uint16_t *dxq, const int32_t *row_of, const u
                              int topk, int H, int afmt, const float *ascale, uint16_t *dx,
                              float *dscale_a, float *part, hipStream_t st);
 
+// real-quantized export: E4M3 bytes of clamp(theta, 0, 448); zero-point bytes;
+// decode of stored codes + scales to bf16 (group = N*K for one scale per matrix)
+void launch_export_theta(const float *theta, size_t n, uint8_t *out, hipStream_t st);
+void launch_export_zp(const float *zp, size_t n, uint8_t *out, hipStream_t st);
+void launch_dequantize(const uint8_t *codes, fq_shape s, int fmt, int group, const float *scale,
+                       const uint8_t *scale_bytes, const uint8_t *zp_bytes, const float *gscale,
+                       uint16_t *out, hipStream_t st);
+
 size_t permute_workspace_bytes(int E, long P);
 void launch_permute(const int32_t *ids, int T, int topk, int ebegin, int E, int32_t *perm,
                     int32_t *row_of, int32_t *seg, void *ws, hipStream_t st);

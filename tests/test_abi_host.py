@@ -235,6 +235,31 @@ def test_per_tensor_weight_scale_arguments(pkg):
 
 
 @host_only
+def test_export_arguments(pkg):
+    """fq_export_scales only converts nvfp4 / int4 parameters; the decode checks
+    its format, group and the pointers that format needs."""
+    L = pkg.lib()
+    shape = pkg.fq_shape(2, 64, 256)
+    q8 = pkg.fq_weight_q(pkg.FMT_INT8, 256, FAKE, None, None)
+    assert L.fq_export_scales(shape, ctypes.byref(q8), FAKE, FAKE, None) == \
+        pkg.FQ_ERR_INVALID_ARGUMENT
+    qn = pkg.fq_weight_q(pkg.FMT_NVFP4, 16, FAKE, None, FAKE)
+    assert L.fq_export_scales(shape, ctypes.byref(qn), None, None, None) == \
+        pkg.FQ_ERR_INVALID_ARGUMENT                                   # no scale_bytes
+    dq = L.fq_dequantize_stacked
+    assert dq(FAKE, shape, pkg.FMT_NVFP4, 32, None, FAKE, None, FAKE, FAKE, None) == \
+        pkg.FQ_ERR_INVALID_ARGUMENT                                   # nvfp4 group
+    assert dq(FAKE, shape, pkg.FMT_INT4, 128, FAKE, None, None, None, FAKE, None) == \
+        pkg.FQ_ERR_INVALID_ARGUMENT                                   # no zero-point bytes
+    assert dq(FAKE, shape, pkg.FMT_INT4, pkg.FQ_GROUP_TENSOR, FAKE, None, FAKE, None, FAKE,
+              None) == pkg.FQ_ERR_INVALID_ARGUMENT                    # per tensor: int8 / fp8
+    assert dq(FAKE + 4, shape, pkg.FMT_FP8_E4M3, 256, FAKE, None, None, None, FAKE, None) == \
+        pkg.FQ_ERR_INVALID_ARGUMENT                                   # codes alignment
+    assert dq(FAKE, pkg.fq_shape(2, 64, 40), pkg.FMT_FP8_E4M3, 40, FAKE, None, None, None, FAKE,
+              None) == pkg.FQ_ERR_INVALID_ARGUMENT                    # K % 16
+
+
+@host_only
 def test_learnable_act_scale_arguments(pkg):
     """A learnable activation scale needs a static per-tensor format and a
     workspace of one float per block (sized by FQ_OP_ACT_SCALE_GRAD)."""

@@ -111,6 +111,47 @@ class KernelTimer:
         return out
 
 
+def measure_export(torch, F, layer, fmt, reps=10):
+    """Real-quantized export of both stacks, outside the training step: the
+    codes from the FQ pass, the stored scale bytes, and the decode back to
+    bf16. Reports the decode kernel's HBM rate (codes + scale bytes read,
+    bf16 written) over `reps` launches per stack."""
+    out = {}
+    total_b, total_ms = 0, 0.0
+    for name, w, shape, q in (("gate_up", layer.w_gu, layer.shape_gu, layer.q_gu),
+                              ("down", layer.w_d, layer.shape_d, layer.q_d)):
+        E, N, K = shape
+        nel = E * N * K
+        four_bit = fmt in (F.FMT_NVFP4, F.FMT_INT4)
+        codes = torch.empty(nel // 2 if four_bit else nel, dtype=torch.uint8, device=w.device)
+        sb = torch.empty(nel // 16, dtype=torch.uint8, device=w.device) \
+            if fmt == F.FMT_NVFP4 else None
+        F.fq_quantize_stacked(w, shape, q, None, codes)
+        if sb is not None:
+            F.fq_export_scales(shape, q, sb, None)
+        dec = torch.empty_like(w)
+        scale = None if fmt == F.FMT_NVFP4 else q.scale
+        F.fq_dequantize_stacked(codes, shape, fmt, q.group, dec, scale, sb, None, q.global_scale)
+        torch.cuda.synchronize()
+        s = torch.cuda.Event(enable_timing=True)
+        e = torch.cuda.Event(enable_timing=True)
+        s.record()
+        for _ in range(reps):
+            F.fq_dequantize_stacked(codes, shape, fmt, q.group, dec, scale, sb, None,
+                                    q.global_scale)
+        e.record()
+        torch.cuda.synchronize()
+        ms = s.elapsed_time(e) / reps
+        nbytes = codes.numel() + (sb.numel() if sb is not None else q.scale.numel() * 4) + 2 * nel
+        out[name] = {"bytes": nbytes, "ms": round(ms, 4),
+                     "GB/s": round(nbytes / (ms * 1e-3) / 1e9, 1)}
+        total_b += nbytes
+        total_ms += ms
+    out["decode_GB/s"] = round(total_b / (total_ms * 1e-3) / 1e9, 1)
+    out["pct_hbm_peak"] = round(100 * out["decode_GB/s"] / MI355X_HBM_PEAK_GBS, 1)
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -239,6 +280,8 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
+    export = measure_export(torch, F, layer, fmt)
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(case, fmt, group, args.cpu_sample_experts)
@@ -282,6 +325,7 @@ def main():
         "gemm_only": {"ms_per_step": round(gemm_ms, 4),
                       "TFLOP/s": round(flops_step / (gemm_ms * 1e-3) / 1e12, 2)},
         "hbm_passes": passes,
+        "export_decode": export,
         "ms_per_step_by_call": breakdown,
         "cpu_baseline": cpu,
         "input_gen_s": round(t_gen, 1),

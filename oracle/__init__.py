@@ -57,6 +57,9 @@ reading where it applies:
        derive their block scales from the data and keep g_a at calibration.
   R-24 a per-tensor weight scale is one scale per expert matrix [N, K] of a
        stack (each expert is its own linear); INT8 / FP8 only
+  R-25 top-K KL: the teacher's K largest logits per token (equal logits: lower
+       index first), both distributions renormalised over that set, mean
+       over valid tokens; only the student's logits get a gradient
 
 Parity status: every function here is pinned by the ``-m "not gpu"`` tests
 (exhaustive code grids, tie tables, library special cases, closed forms,
@@ -76,7 +79,8 @@ from .observer import observer_weight, observer_act  # noqa: F401
 from .permute import moe_permute  # noqa: F401
 from .gemm import grouped_gemm_fwd, grouped_gemm_bwd  # noqa: F401
 from .export import pack_codes, unpack_codes, export_scales, dequantize  # noqa: F401
+from .distill import topk_set, topk_kl  # noqa: F401
 from .moe import (  # noqa: F401
     gather_actfq, swiglu_fwd, swiglu_actfq, swiglu_bwd, combine, combine_bwd,
-    unpermute_reduce, unpermute_sum, act_scale_grad, moe_layer,
+    unpermute_reduce, unpermute_sum, act_scale_grad, moe_layer, teacher_forward,
 )

@@ -261,12 +261,15 @@ def fq_weight_stack(w_bits, fmt: int, group: int, scale, zero_point=None,
                     global_scale=None) -> FQ:
     """Fake-quantise a stacked weight [E, N, K] (mcore_qad article, section 二.4).
 
+    fmt FMT_NONE: quantization off (the self-teacher), scale unused.
     scale: [E, N, K/group] (NVFP4: theta), or [E] for group GROUP_TENSOR (one
     scale per expert matrix, INT8 / FP8); zero_point: [E, N, K/group] (int4);
     global_scale: [E] (NVFP4 tensor scale g, one per expert, R-8).
     """
     w = bf16_to_f32(w_bits)
     E, N, K = w.shape
+    if fmt == FMT_NONE:             # quantization off: the weights as they are
+        return fq_act(w_bits, FMT_NONE, None)
     if group == GROUP_TENSOR:
         if fmt not in (FMT_INT8, FMT_FP8):
             raise ValueError("a per-tensor weight scale exists for int8 / fp8 only")

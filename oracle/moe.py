@@ -138,6 +138,20 @@ def act_scale_grad(x_bits, g, afmt: int, act_scale) -> float:
     return float(np.sum(np.asarray(g, dtype=np.float64) * fq.dv_ds))
 
 
+def teacher_forward(case):
+    """The self-teacher: the same layer with quantization off (mcore_qad article,
+    section 一): plain gather, bf16 grouped GEMMs on the frozen weights,
+    SwiGLU, combine. Returns out bits [T, H]."""
+    E = case.w_gu.shape[0]
+    k = case.expert_ids.shape[1]
+    perm, row_of, seg = moe_permute(case.expert_ids, case.expert_begin, E)
+    xg = np.asarray(case.x)[np.asarray(perm, dtype=np.int64) // k]
+    h = grouped_gemm_fwd(xg, seg, case.w_gu, FMT_NONE, None, None)
+    a = swiglu_fwd(h)
+    o = grouped_gemm_fwd(a, seg, case.w_d, FMT_NONE, None, None)
+    return combine(o, case.probs, row_of)
+
+
 def moe_layer(case, wfmt: int, group, afmt: int, wq_gu=None, wq_d=None,
               act_scales=None):
     """Full forward + scale-only backward of one MoE layer's routed-expert path.

@@ -173,6 +173,36 @@ def moe_case(T: int, fmt: str, E_global: int = N_EXPERTS, H: int = HIDDEN, F: in
                    w_gu=w_gu, w_d=w_d, x=x, expert_ids=ids, probs=p, dout=dout)
 
 
+def kd_logits(T: int, V: int, seed: int = 0, device: str = "cpu", teacher_std: float = 2.0,
+              peaks: int = 4, peak_boost: float = 8.0, student_noise: float = 0.3):
+    """Synthetic teacher / student logits [T, V] (bf16) for the top-K KL
+    distillation kernel: teacher ~ N(0, teacher_std^2) with `peaks` random
+    vocabulary entries per token raised by peak_boost (a peaked next-token
+    distribution); student = teacher + N(0, student_noise^2) (the quantized
+    copy of the same model). Draw order: teacher, peak positions, student
+    noise. On device "cpu" the draws are the CPU generator's; on "cuda" the
+    device generator's (same seed, same bits on a given torch build).
+    Returns two torch bfloat16 tensors on `device`."""
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed))
+    t = torch.randn(T, V, generator=g, device=device, dtype=torch.float32).mul_(teacher_std)
+    if peaks > 0:
+        pos = torch.randint(0, V, (T, peaks), generator=g, device=device)
+        t.scatter_add_(1, pos, torch.full((T, peaks), peak_boost, device=device))
+    s = torch.randn(T, V, generator=g, device=device, dtype=torch.float32).mul_(student_noise)
+    s.add_(t)
+    return s.to(torch.bfloat16), t.to(torch.bfloat16)
+
+
+# Shape of the distillation kernel's workload: one 4096-token micro-batch over
+# the Qwen3 vocabulary (151936 entries), teacher top-1000 (the kl_top_1000
+# example of the QAT + ZeRO-3 page's loss table).
+KD_TOKENS = 4096
+KD_VOCAB = 151936
+KD_TOPK = 1000
+KD_NAME = "kd-topk1000-t4096-v151936"
+
+
 # ---------------------------------------------------------------------------
 # The five workloads, full size.
 # ---------------------------------------------------------------------------

@@ -198,6 +198,34 @@ fq_status fq_dequantize_stacked(const uint8_t *codes, fq_shape shape, int32_t fm
                                 uint16_t *w_bf16, fq_stream stream);
 
 /* ------------------------------------------------------------------------
+ * fq_topk_kl -- top-K KL distillation between student and teacher logits
+ * (mcore_qad article, section 二.5: the KL only over the teacher's top-k
+ * tokens, so the [tokens, vocab] probabilities are never formed; QAT +
+ * ZeRO-3 page, loss table: kl_top_K forward, r_kl_top_K reverse, averaged
+ * over the valid tokens). Per token t:
+ *   S    = the K largest teacher logits (equal logits: lower index first),
+ *          written to topk_idx[t, 0:K] in increasing vocabulary order;
+ *   p, q = softmax of the teacher's / student's logits restricted to S;
+ *   loss_tok[t] = sum_S p (log p - log q)   (reverse != 0: sum_S q (log q -
+ *                 log p)); 0 for an invalid token;
+ *   grad[t, i]  = d loss_mean / d student logit at topk_idx[t, i]:
+ *                 (q - p) / n (reverse: q ((log q - log p) - loss_tok) / n),
+ *                 0 for an invalid token; every other logit's gradient is 0;
+ *   loss_mean[0] = sum_t loss_tok[t] / n, n = number of valid tokens
+ *                 (valid[t] != 0; valid NULL = all; n = 0 counts as 1).
+ * student_bf16, teacher_bf16 [T, V] bf16 (16-byte aligned); topk_idx
+ * [T, K] int32; grad [T, K] fp32; loss_tok [T] fp32; loss_mean one float.
+ * Requires V % 8 == 0 and 1 <= K <= min(V, 4096). Workspace:
+ * fq_workspace_bytes(FQ_OP_TOPK_KL, ...) bytes (one float). Sums are
+ * taken in a fixed order (bitwise reproducible); exp / log are the
+ * hardware's (relative error a few 2^-24).
+ * ---------------------------------------------------------------------- */
+fq_status fq_topk_kl(const uint16_t *student_bf16, const uint16_t *teacher_bf16, int32_t T,
+                     int32_t V, int32_t K, int32_t reverse, const uint8_t *valid,
+                     int32_t *topk_idx, float *grad, float *loss_tok, float *loss_mean, void *ws,
+                     size_t ws_bytes, fq_stream stream);
+
+/* ------------------------------------------------------------------------
  * fq_moe_permute -- routed-token permutation for one grouped GEMM over all
  * local experts (mcore_qad article, section 二.4: one GEMM over routed
  * tokens needs each expert's rows contiguous).
@@ -226,7 +254,10 @@ fq_status fq_moe_permute(const int32_t *expert_ids, int32_t T, int32_t topk,
  *   w_bf16  [E, N, K] raw frozen weights with quantizer wq.
  *   w_fq    NULL, or FQ_w(W) already materialized by fq_quantize_stacked
  *           with the same quantizer (then w_bf16 is not read). With NULL
- *           the call materializes it in the workspace.
+ *           the call materializes it in the workspace. With wq NULL, w_fq
+ *           is used as given: passing the raw weights there is the
+ *           quantization-off forward of the self-teacher (mcore_qad
+ *           article, section 一).
  *   aq      activation quantizer applied to x first (NULL = NONE).
  *   y_bf16  [R_max, N].
  * Requires N % 256 == 0 and K % 64 == 0 (K % 16 for nvfp4 activations).
@@ -329,6 +360,7 @@ fq_status fq_moe_unpermute_reduce(const uint16_t *dxq_bf16, const int32_t *row_o
 #define FQ_OP_GEMM_FWD 2
 #define FQ_OP_GEMM_BWD 3
 #define FQ_OP_ACT_SCALE_GRAD 4 /* shape = {1, rows, cols}; R_max, fmts unused */
+#define FQ_OP_TOPK_KL 5        /* shape, R_max, fmts unused */
 size_t fq_workspace_bytes(int32_t op, fq_shape shape, int32_t R_max, int32_t fmts);
 
 const char *fq_last_error(void);

@@ -38,13 +38,14 @@ FQ_OP_PERMUTE = 1
 FQ_OP_GEMM_FWD = 2
 FQ_OP_GEMM_BWD = 3
 FQ_OP_ACT_SCALE_GRAD = 4
+FQ_OP_TOPK_KL = 5
 FQ_GROUP_TENSOR = -1     # one weight scale per expert matrix (int8 / fp8)
 
 EXPORTED = (
     "observer_absmax_init", "fq_quantize_stacked", "fq_moe_permute", "fq_grouped_gemm_fwd",
     "fq_grouped_gemm_bwd_scale", "fq_moe_gather_actfq", "fq_swiglu_actfq", "fq_swiglu_bwd",
     "fq_moe_combine", "fq_moe_combine_bwd", "fq_moe_unpermute_reduce", "fq_workspace_bytes",
-    "fq_last_error", "fq_abi_version", "fq_export_scales", "fq_dequantize_stacked",
+    "fq_last_error", "fq_abi_version", "fq_export_scales", "fq_dequantize_stacked", "fq_topk_kl",
 )
 
 
@@ -92,6 +93,7 @@ def _load() -> ctypes.CDLL:
                                          P, SZ, P]),
         "fq_export_scales": (st, [fq_shape, ctypes.POINTER(fq_weight_q), P, P, P]),
         "fq_dequantize_stacked": (st, [P, fq_shape, I32, I32, P, P, P, P, P, P]),
+        "fq_topk_kl": (st, [P, P, I32, I32, I32, I32, P, P, P, P, P, P, SZ, P]),
         "fq_workspace_bytes": (SZ, [I32, fq_shape, I32, I32]),
         "fq_last_error": (ctypes.c_char_p, []),
         "fq_abi_version": (I32, []),
@@ -192,10 +194,11 @@ def fq_moe_permute(expert_ids, T, topk, expert_begin, E_local, perm, row_of, seg
                                _nbytes(ws), _stream()))
 
 
-def fq_grouped_gemm_fwd(x, R_max, seg_offsets, shape, w, w_fq, wq: WeightQ,
+def fq_grouped_gemm_fwd(x, R_max, seg_offsets, shape, w, w_fq, wq: Optional[WeightQ],
                         aq: Optional[ActQ], y, ws=None):
     _check(_lib.fq_grouped_gemm_fwd(_p(x), int(R_max), _p(seg_offsets), _shape(*shape), _p(w),
-                                    _p(w_fq), ctypes.byref(wq.c()), _aq(aq), _p(y), _p(ws),
+                                    _p(w_fq), ctypes.byref(wq.c()) if wq is not None else None,
+                                    _aq(aq), _p(y), _p(ws),
                                     _nbytes(ws), _stream()))
 
 
@@ -249,6 +252,12 @@ def fq_dequantize_stacked(codes, shape, fmt, group, w_bf16, scale=None, scale_by
     _check(_lib.fq_dequantize_stacked(_p(codes), _shape(*shape), int(fmt), int(group), _p(scale),
                                       _p(scale_bytes), _p(zero_point_bytes), _p(global_scale),
                                       _p(w_bf16), _stream()))
+
+
+def fq_topk_kl(student, teacher, T, V, K, reverse, valid, topk_idx, grad, loss_tok, loss_mean, ws):
+    _check(_lib.fq_topk_kl(_p(student), _p(teacher), int(T), int(V), int(K), int(bool(reverse)),
+                           _p(valid), _p(topk_idx), _p(grad), _p(loss_tok), _p(loss_mean), _p(ws),
+                           _nbytes(ws), _stream()))
 
 
 from .layer import MoEFakeQuantLayer  # noqa: E402,F401

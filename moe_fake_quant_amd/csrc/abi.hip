@@ -156,6 +156,7 @@ const char *fq_last_error(void) { return g_last_error.c_str(); }
 size_t fq_workspace_bytes(int32_t op, fq_shape shape, int32_t R_max, int32_t fmts) {
   if (op == FQ_OP_PERMUTE) return permute_workspace_bytes(shape.E > 0 ? shape.E : 1, R_max);
   if (op == FQ_OP_GEMM_FWD || op == FQ_OP_GEMM_BWD) return gemm_ws(op, shape, R_max, fmts);
+  if (op == FQ_OP_TOPK_KL) return kAlign;
   if (op == FQ_OP_ACT_SCALE_GRAD) {
     if (shape.N < 0 || shape.K <= 0) return 0;
     return align_up((size_t)act_grad_partials(shape.N, shape.K) * sizeof(float));
@@ -253,6 +254,28 @@ fq_status fq_dequantize_stacked(const uint8_t *codes, fq_shape s, int32_t fmt, i
   return FQ_OK;
 }
 
+fq_status fq_topk_kl(const uint16_t *student, const uint16_t *teacher, int32_t T, int32_t V,
+                     int32_t K, int32_t reverse, const uint8_t *valid, int32_t *topk_idx,
+                     float *grad, float *loss_tok, float *loss_mean, void *ws, size_t ws_bytes,
+                     fq_stream stream) {
+  FQ_CHECK_ARG(T >= 0 && V > 0 && V % 8 == 0, "bad sizes T=%d V=%d (V must be a multiple of 8)",
+               T, V);
+  FQ_CHECK_ARG(K >= 1 && K <= V, "K=%d must be in [1, V]", K);
+  FQ_CHECK_SUPPORTED(K <= kTopKMax, "K=%d above the supported %d", K, kTopKMax);
+  FQ_CHECK_ARG(loss_mean != nullptr, "loss_mean is NULL");
+  FQ_CHECK_ARG(T == 0 || (student && teacher && topk_idx && grad && loss_tok), "NULL pointer");
+  FQ_CHECK_ARG((!student || aligned16(student)) && (!teacher || aligned16(teacher)),
+               "logits must be 16-byte aligned");
+  if (!ws || ws_bytes < kAlign) {
+    set_error("fq_topk_kl: workspace %zu bytes < %zu needed", ws_bytes, (size_t)kAlign);
+    return FQ_ERR_WORKSPACE_TOO_SMALL;
+  }
+  launch_topk_kl(student, teacher, T, V, K, reverse != 0, valid, topk_idx, grad, loss_tok,
+                 loss_mean, static_cast<float *>(ws), S(stream));
+  FQ_CHECK_LAUNCH("fq_topk_kl");
+  return FQ_OK;
+}
+
 fq_status fq_moe_permute(const int32_t *ids, int32_t T, int32_t topk, int32_t ebegin, int32_t E,
                          int32_t *perm, int32_t *row_of, int32_t *seg, void *ws, size_t ws_bytes,
                          fq_stream stream) {
@@ -278,7 +301,8 @@ fq_status fq_grouped_gemm_fwd(const uint16_t *x, int32_t R_max, const int32_t *s
   FQ_CHECK_ARG(R_max >= 0, "R_max < 0");
   FQ_CHECK_ARG(seg && y && (x || R_max == 0), "x, seg_offsets and y must be non-NULL");
   FQ_CHECK_ARG(w || w_fq, "w or w_fq must be non-NULL");
-  FQ_TRY(check_weight_q(wq, s, w_fq == nullptr));
+  FQ_CHECK_ARG(wq || w_fq, "wq may be NULL only with w_fq (weights used as given)");
+  if (wq) FQ_TRY(check_weight_q(wq, s, w_fq == nullptr));
   FQ_TRY(check_act_q(aq, s.K));
   FQ_CHECK_SUPPORTED(s.N % 256 == 0 && s.K % 64 == 0,
                      "grouped GEMM forward needs N %% 256 == 0 and K %% 64 == 0 (N=%d K=%d)", s.N, s.K);

@@ -48,6 +48,13 @@ void launch_dequantize(const uint8_t *codes, fq_shape s, int fmt, int group, con
                        const uint8_t *scale_bytes, const uint8_t *zp_bytes, const float *gscale,
                        uint16_t *out, hipStream_t st);
 
+// top-K KL distillation: K <= kTopKMax (the selected entries live in LDS);
+// inv_n: one device float of scratch (1 / number of valid tokens)
+constexpr int kTopKMax = 4096;
+void launch_topk_kl(const uint16_t *student, const uint16_t *teacher, int T, int V, int K,
+                    bool reverse, const uint8_t *valid, int32_t *idx, float *grad, float *loss_tok,
+                    float *loss_mean, float *inv_n, hipStream_t st);
+
 size_t permute_workspace_bytes(int E, long P);
 void launch_permute(const int32_t *ids, int T, int topk, int ebegin, int E, int32_t *perm,
                     int32_t *row_of, int32_t *seg, void *ws, hipStream_t st);

@@ -154,6 +154,30 @@ class MoEFakeQuantLayer:
         fq_moe_combine(self.o, probs, self.row_of[:T], T, self.topk, self.H, self.out[:T])
         return self.out[:T]
 
+    def teacher_forward(self, x: torch.Tensor, expert_ids: torch.Tensor,
+                        probs: torch.Tensor) -> torch.Tensor:
+        """The self-teacher: this layer with quantization off (plain gather, the
+        frozen bf16 weights as the GEMM operands, SwiGLU, combine), into
+        buffers of its own so a student forward's saved activations survive."""
+        T = x.shape[0]
+        if not hasattr(self, "t_xq"):
+            bf = dict(dtype=torch.bfloat16, device=self.dev)
+            R, H, F = self.R_max, self.H, self.F
+            self.t_xq = torch.empty(R, H, **bf)
+            self.t_h = torch.empty(R, 2 * F, **bf)
+            self.t_a = torch.empty(R, F, **bf)
+            self.t_o = torch.empty(R, H, **bf)
+            self.t_out = torch.empty(self.T_max, H, **bf)
+        self.route(expert_ids)
+        fq_moe_gather_actfq(x, T, self.H, self.row_of[:T], self.topk, None, self.t_xq)
+        fq_grouped_gemm_fwd(self.t_xq, self.R_max, self.seg, self.shape_gu, None, self.w_gu, None,
+                            None, self.t_h, None)
+        fq_swiglu_actfq(self.t_h, self.R_max, self.n_rows, self.F, None, None, self.t_a)
+        fq_grouped_gemm_fwd(self.t_a, self.R_max, self.seg, self.shape_d, None, self.w_d, None,
+                            None, self.t_o, None)
+        fq_moe_combine(self.t_o, probs, self.row_of[:T], T, self.topk, self.H, self.t_out[:T])
+        return self.t_out[:T]
+
     def backward(self, x: torch.Tensor, probs: torch.Tensor, dout: torch.Tensor):
         T = x.shape[0]
         fq_moe_combine_bwd(dout, probs, self.row_of[:T], T, self.topk, self.H, self.do)

@@ -260,6 +260,28 @@ def test_export_arguments(pkg):
 
 
 @host_only
+def test_topk_kl_and_teacher_arguments(pkg):
+    L = pkg.lib()
+    kl = L.fq_topk_kl
+    ok = (FAKE, FAKE, 16, 4096, 100, 0, None, FAKE, FAKE, FAKE, FAKE, FAKE, 256, None)
+    for i, bad, want in ((3, 4100, pkg.FQ_ERR_INVALID_ARGUMENT),      # V % 8
+                         (4, 0, pkg.FQ_ERR_INVALID_ARGUMENT),         # K = 0
+                         (4, 5000, pkg.FQ_ERR_INVALID_ARGUMENT),      # K > V
+                         (12, 16, pkg.FQ_ERR_WORKSPACE_TOO_SMALL),
+                         (10, None, pkg.FQ_ERR_INVALID_ARGUMENT)):    # no loss_mean
+        args = list(ok)
+        args[i] = bad
+        assert kl(*args) == want, i
+    args = list(ok)
+    args[3], args[4] = 16384, 4097
+    assert kl(*args) == pkg.FQ_ERR_UNSUPPORTED                        # K above 4096
+    # a forward GEMM without a quantizer needs the weights to use as given
+    st = _status(pkg, "fq_grouped_gemm_fwd", FAKE, 64, FAKE, pkg.fq_shape(2, 256, 256), FAKE,
+                 None, None, None, FAKE, None, 0, None)
+    assert st == pkg.FQ_ERR_INVALID_ARGUMENT
+
+
+@host_only
 def test_learnable_act_scale_arguments(pkg):
     """A learnable activation scale needs a static per-tensor format and a
     workspace of one float per block (sized by FQ_OP_ACT_SCALE_GRAD)."""

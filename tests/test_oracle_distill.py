@@ -28,6 +28,7 @@ def _logits(rng, T, V, step=0.25):
 def test_topk_set_matches_python_sort_with_ties():
     rng = np.random.default_rng(1)
     t = _logits(rng, 12, 97, step=0.5)
+    t[:, ::3] = np.where(rng.random((12, 33)) < 0.5, 0x8000, 0x0000)   # -0 and +0: equal logits
     tv = O.bf16_to_f32(t)
     for K in (1, 5, 30, 97):
         idx = O.topk_set(t, K)

@@ -152,6 +152,56 @@ def measure_export(torch, F, layer, fmt, reps=10):
     return out
 
 
+def measure_distill(torch, F, W, layer, x, ids, probs, reps=10):
+    """The self-distillation pieces, outside the training step: the layer's
+    quantization-off teacher forward on the same batch, and the top-K KL
+    kernel on synthetic [4096, 151936] logits (teacher top-1000). The KL
+    kernel's algorithmic bytes per token: the teacher row once (2V), the
+    student at the K entries (2K), the outputs (8K + 4)."""
+    for _ in range(2):
+        layer.teacher_forward(x, ids, probs)
+    torch.cuda.synchronize()
+    s0 = torch.cuda.Event(enable_timing=True)
+    e0 = torch.cuda.Event(enable_timing=True)
+    s0.record()
+    for _ in range(reps):
+        layer.teacher_forward(x, ids, probs)
+    e0.record()
+    torch.cuda.synchronize()
+    t_ms = s0.elapsed_time(e0) / reps
+    R = int(layer.seg[layer.E].item())
+    fwd_flops = 2 * R * (2 * layer.F * layer.H + layer.H * layer.F)
+
+    T, V, K = W.KD_TOKENS, W.KD_VOCAB, W.KD_TOPK
+    st, te = W.kd_logits(T, V, seed=0, device="cuda")
+    idx = torch.empty(T, K, dtype=torch.int32, device="cuda")
+    g = torch.empty(T, K, device="cuda")
+    lt = torch.empty(T, device="cuda")
+    lm = torch.empty(1, device="cuda")
+    ws = torch.empty(256, dtype=torch.uint8, device="cuda")
+    out = {"teacher_forward": {"ms": round(t_ms, 4),
+                               "TFLOP/s": round(fwd_flops / (t_ms * 1e-3) / 1e12, 2)}}
+    nbytes = T * (2 * V + 2 * K + 8 * K + 4)
+    for reverse in (False, True):
+        F.fq_topk_kl(st, te, T, V, K, reverse, None, idx, g, lt, lm, ws)
+        torch.cuda.synchronize()
+        s1 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        s1.record()
+        for _ in range(reps):
+            F.fq_topk_kl(st, te, T, V, K, reverse, None, idx, g, lt, lm, ws)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = s1.elapsed_time(e1) / reps
+        out["r_kl_top_K" if reverse else "kl_top_K"] = {
+            "workload": W.KD_NAME, "ms": round(ms, 4), "bytes": nbytes,
+            "GB/s": round(nbytes / (ms * 1e-3) / 1e9, 1),
+            "pct_hbm_peak": round(100 * nbytes / (ms * 1e-3) / 1e9 / MI355X_HBM_PEAK_GBS, 1),
+            "loss_mean": round(float(lm.cpu()[0]), 6)}
+    del st, te
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -281,6 +331,7 @@ def main():
         del src, dst
 
     export = measure_export(torch, F, layer, fmt)
+    distill = measure_distill(torch, F, W, layer, x, ids, probs)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -326,6 +377,7 @@ def main():
                       "TFLOP/s": round(flops_step / (gemm_ms * 1e-3) / 1e12, 2)},
         "hbm_passes": passes,
         "export_decode": export,
+        "distill": distill,
         "ms_per_step_by_call": breakdown,
         "cpu_baseline": cpu,
         "input_gen_s": round(t_gen, 1),

@@ -4,30 +4,49 @@
 // [tokens, vocab] probabilities (AngelSlim mcore_qad article, section 二.5;
 // the forward / reverse top-K variants of the QAT + ZeRO-3 page's loss table).
 //
-// One workgroup per token row. The K-th largest teacher logit is found
-// exactly with two 256-bin histogram passes over an order-preserving 16-bit
-// key of the bf16 logits (high byte, then low byte inside the chosen high
-// bin); a third pass compacts the selected entries in vocabulary order into
-// LDS (equal logits at the threshold: the lower indices first) and stops as
-// soon as K are found. The student logits are gathered at those K indices;
-// both restricted softmaxes, the loss and the gradient come from LDS.
+// One workgroup per token row; the teacher row is streamed once. A strided
+// sample bounds the K-th largest logit from below; the stream keeps the
+// (few) entries above that bound, in vocabulary order, and the exact K-th
+// largest, the ties (lower index first) and the selection come from them
+// (k_topk_kl). Rows where the bound fails are selected exactly by histograms
+// over an order-preserving 16-bit key of the bf16 logits (select_hist). The
+// student logits are gathered at the K selected indices; both restricted
+// softmaxes, the loss and the gradient come from LDS.
 #include "internal.hpp"
 
 namespace fq {
 
 namespace {
 
-constexpr int kKT = 1024;          // threads per row
+constexpr int kKT = 512;           // threads per row
 constexpr int kKW = kKT / 64;      // waves per row
 
+// Reduction scratch.
 struct KLShared {
-  uint32_t hist[kKW][256];         // per-wave histograms
   uint32_t scan[kKW];
-  float red[kKW];
-  uint32_t sel_bin, sel_above;
+  uint32_t cnt[2][kKW];
+  float red2[2][kKW][2];
+};
+// The selected entries of a row.
+struct KLSel {
   int32_t idx[kTopKMax];
   float tv[kTopKMax];
   float sv[kTopKMax];
+};
+// Histograms of the histogram selection.
+struct KLHist {
+  uint32_t hist[kKW][256];         // per-wave histograms
+  uint32_t sel_bin, sel_above;
+};
+constexpr int kCandMax = 8192;     // candidates of the sampled selection
+constexpr int kWaveCand = kCandMax / kKW;   // one part per wave
+constexpr int kHistBins = 4096;    // key-value counters of the threshold search
+// The big LDS arrays share one region: candidates (or histograms) while the
+// row is selected, then the selected entries.
+union KLBig {
+  uint32_t cand[kCandMax];             // vocabulary indices
+  KLHist hs;
+  KLSel sel;
 };
 
 // bf16 bits -> 16-bit key whose unsigned order is the value order (-0 and +0
@@ -35,6 +54,11 @@ struct KLShared {
 __device__ __forceinline__ uint32_t order_key(uint32_t b) {
   b = (b == 0x8000u) ? 0u : b;
   return (b & 0x8000u) ? (~b & 0xFFFFu) : (b | 0x8000u);
+}
+
+// inverse of order_key (key 0x8000 -> +0)
+__device__ __forceinline__ uint32_t raw_of_key(uint32_t k) {
+  return (k & 0x8000u) ? (k ^ 0x8000u) : (~k & 0xFFFFu);
 }
 
 __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v, int lane) {
@@ -47,6 +71,7 @@ __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v, int lane) {
 }
 
 // Exclusive prefix sum over the block in thread order; total to every thread.
+template <int NT>
 __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t &total, KLShared &sh) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const uint32_t incl = wave_incl_scan(v, lane);
@@ -54,7 +79,7 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t &total,
   __syncthreads();
   uint32_t before = 0, tot = 0;
 #pragma unroll
-  for (int w = 0; w < kKW; ++w) {
+  for (int w = 0; w < NT / 64; ++w) {
     const uint32_t x = sh.scan[w];
     before += (w < wave) ? x : 0u;
     tot += x;
@@ -64,32 +89,32 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t &total,
   return before + incl - v;
 }
 
-// Block sum / max in a fixed order (butterfly in each wave, then the waves in
-// index order); the result in every thread.
-__device__ __forceinline__ float block_sum(float v, KLShared &sh) {
+// Two block reductions (max if MAX, else sum) at once, in a fixed order, with
+// one barrier (alternating scratch rows, `par` flips).
+template <int NT, bool MAX>
+__device__ __forceinline__ void block_reduce2(float &a, float &b, KLShared &sh, int &par) {
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-  if ((threadIdx.x & 63) == 0) sh.red[threadIdx.x >> 6] = v;
+  for (int o = 32; o > 0; o >>= 1) {
+    const float x = __shfl_xor(a, o, 64), y = __shfl_xor(b, o, 64);
+    a = MAX ? fmaxf(a, x) : a + x;
+    b = MAX ? fmaxf(b, y) : b + y;
+  }
+  if ((threadIdx.x & 63) == 0) {
+    sh.red2[par][threadIdx.x >> 6][0] = a;
+    sh.red2[par][threadIdx.x >> 6][1] = b;
+  }
   __syncthreads();
-  float s = sh.red[0];
+  a = sh.red2[par][0][0];
+  b = sh.red2[par][0][1];
 #pragma unroll
-  for (int w = 1; w < kKW; ++w) s += sh.red[w];
-  __syncthreads();
-  return s;
-}
-__device__ __forceinline__ float block_max(float v, KLShared &sh) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-  if ((threadIdx.x & 63) == 0) sh.red[threadIdx.x >> 6] = v;
-  __syncthreads();
-  float s = sh.red[0];
-#pragma unroll
-  for (int w = 1; w < kKW; ++w) s = fmaxf(s, sh.red[w]);
-  __syncthreads();
-  return s;
+  for (int w = 1; w < NT / 64; ++w) {
+    a = MAX ? fmaxf(a, sh.red2[par][w][0]) : a + sh.red2[par][w][0];
+    b = MAX ? fmaxf(b, sh.red2[par][w][1]) : b + sh.red2[par][w][1];
+  }
+  par ^= 1;
 }
 
-__device__ __forceinline__ void zero_hist(KLShared &sh) {
+__device__ __forceinline__ void zero_hist(KLHist &sh) {
   uint32_t *h = &sh.hist[0][0];
   for (int i = threadIdx.x; i < kKW * 256; i += kKT) h[i] = 0u;
   __syncthreads();
@@ -98,7 +123,7 @@ __device__ __forceinline__ void zero_hist(KLShared &sh) {
 // Sum the per-wave histograms into hist[0], then find the bin b (scanning
 // from 255 down) with above(b) < need <= above(b) + count(b), where above(b)
 // counts the entries of the higher bins. Requires need <= total.
-__device__ __forceinline__ void find_bin(KLShared &sh, uint32_t need) {
+__device__ __forceinline__ void find_bin(KLHist &sh, uint32_t need) {
   if (threadIdx.x < 256) {
     uint32_t s = 0;
 #pragma unroll
@@ -142,50 +167,96 @@ __global__ __launch_bounds__(256) void k_count_valid(const uint8_t *__restrict__
   }
 }
 
-template <bool REVERSE>
-__global__ __launch_bounds__(kKT) void k_topk_kl(const uint16_t *__restrict__ student,
-                                                 const uint16_t *__restrict__ teacher, int V, int K,
-                                                 const uint8_t *__restrict__ valid,
-                                                 const float *__restrict__ inv_n,
-                                                 int32_t *__restrict__ out_idx,
-                                                 float *__restrict__ out_grad,
-                                                 float *__restrict__ loss_tok) {
-  __shared__ KLShared sh;
-  const int t = threadIdx.x, wave = t >> 6;
-  const size_t row = blockIdx.x;
-  const uint4 *trow = reinterpret_cast<const uint4 *>(teacher + row * (size_t)V);
-  const uint32_t nvec = (uint32_t)V / 8u;
+// The K selected entries (se.idx, se.tv) of one row -> the student's logits
+// there, both restricted softmaxes, the loss and the scaled gradient.
+template <int NT, bool REVERSE>
+__device__ __forceinline__ void kl_tail(KLShared &sh, KLSel &se,
+                                        const uint16_t *__restrict__ student,
+                                        size_t row, int V, int K,
+                                        const uint8_t *__restrict__ valid,
+                                        const float *__restrict__ inv_n,
+                                        int32_t *__restrict__ out_idx,
+                                        float *__restrict__ out_grad,
+                                        float *__restrict__ loss_tok) {
+  const int t = threadIdx.x;
+  // the student's logits at the selected entries; both restricted softmaxes
+  const uint16_t *srow = student + row * (size_t)V;
+  float mt = -INFINITY, ms = -INFINITY;
+  for (int i = t; i < K; i += NT) {
+    // (the clamp only guards the address; every index is in [0, V) by construction)
+    const float zs = bf16_to_f32(srow[min(max(se.idx[i], 0), V - 1)]);
+    se.sv[i] = zs;
+    mt = fmaxf(mt, se.tv[i]);
+    ms = fmaxf(ms, zs);
+  }
+  int par = 0;
+  block_reduce2<NT, true>(mt, ms, sh, par);
+  float et = 0.0f, es = 0.0f;
+  for (int i = t; i < K; i += NT) {
+    et += __expf(se.tv[i] - mt);
+    es += __expf(se.sv[i] - ms);
+  }
+  block_reduce2<NT, false>(et, es, sh, par);
+  const float lse_t = mt + __logf(et), lse_s = ms + __logf(es);
+  float l = 0.0f, unused = 0.0f;
+  for (int i = t; i < K; i += NT) {
+    const float lt = se.tv[i] - lse_t, ls = se.sv[i] - lse_s;
+    l += REVERSE ? __expf(ls) * (ls - lt) : __expf(lt) * (lt - ls);
+  }
+  block_reduce2<NT, false>(l, unused, sh, par);
+  const float loss = l;
+  const bool ok = valid ? valid[row] != 0 : true;
+  const float scale = ok ? inv_n[0] : 0.0f;
+  for (int i = t; i < K; i += NT) {
+    const float lt = se.tv[i] - lse_t, ls = se.sv[i] - lse_s;
+    const float ps = __expf(ls);
+    const float g = REVERSE ? ps * ((ls - lt) - loss) : ps - __expf(lt);
+    out_idx[row * (size_t)K + i] = se.idx[i];
+    out_grad[row * (size_t)K + i] = g * scale;
+  }
+  if (t == 0) loss_tok[row] = ok ? loss : 0.0f;
+}
 
+
+// Exact selection by histograms: two 256-bin passes over the key's high and
+// low byte find the K-th largest key; a third pass compacts the selection in
+// vocabulary order (per-chunk block scans) and stops once K are in. Reads the
+// row three times; used when the sampled bracket does not hold.
+__device__ __forceinline__ void select_hist(KLShared &sh, KLBig &big,
+                                            const uint4 *__restrict__ trow, uint32_t nvec, int K) {
+  KLHist &hs = big.hs;
+  KLSel &se = big.sel;   // written only after the histograms are done with
+  const int t = threadIdx.x, wave = t >> 6;
   // pass 1: histogram of the key's high byte
-  zero_hist(sh);
+  zero_hist(hs);
   for (uint32_t v = t; v < nvec; v += kKT) {
     const uint4 q = trow[v];
     const uint32_t w[4] = {q.x, q.y, q.z, q.w};
 #pragma unroll
     for (int h = 0; h < 8; ++h) {
       const uint32_t key = order_key((w[h >> 1] >> (16 * (h & 1))) & 0xFFFFu);
-      atomicAdd(&sh.hist[wave][key >> 8], 1u);
+      atomicAdd(&hs.hist[wave][key >> 8], 1u);
     }
   }
   __syncthreads();
-  find_bin(sh, (uint32_t)K);
-  const uint32_t hi = sh.sel_bin, above_hi = sh.sel_above;
+  find_bin(hs, (uint32_t)K);
+  const uint32_t hi = hs.sel_bin, above_hi = hs.sel_above;
 
   // pass 2: histogram of the low byte inside the chosen high byte
-  zero_hist(sh);
+  zero_hist(hs);
   for (uint32_t v = t; v < nvec; v += kKT) {
     const uint4 q = trow[v];
     const uint32_t w[4] = {q.x, q.y, q.z, q.w};
 #pragma unroll
     for (int h = 0; h < 8; ++h) {
       const uint32_t key = order_key((w[h >> 1] >> (16 * (h & 1))) & 0xFFFFu);
-      if ((key >> 8) == hi) atomicAdd(&sh.hist[wave][key & 0xFFu], 1u);
+      if ((key >> 8) == hi) atomicAdd(&hs.hist[wave][key & 0xFFu], 1u);
     }
   }
   __syncthreads();
-  find_bin(sh, (uint32_t)K - above_hi);
-  const uint32_t tau = (hi << 8) | sh.sel_bin;            // key of the K-th largest
-  const uint32_t need_ties = (uint32_t)K - above_hi - sh.sel_above;
+  find_bin(hs, (uint32_t)K - above_hi);
+  const uint32_t tau = (hi << 8) | hs.sel_bin;            // key of the K-th largest
+  const uint32_t need_ties = (uint32_t)K - above_hi - hs.sel_above;
 
   // pass 3: keys above tau, then the first need_ties keys equal to tau, in
   // vocabulary order, compacted into LDS; stops once K are in
@@ -209,7 +280,7 @@ __global__ __launch_bounds__(kKT) void k_topk_kl(const uint16_t *__restrict__ st
       for (int h = 0; h < 8; ++h) key[h] = raw[h] = 0u;
     }
     uint32_t tot;
-    const uint32_t ex = block_excl_scan((n_gt << 16) | n_eq, tot, sh);
+    const uint32_t ex = block_excl_scan<kKT>((n_gt << 16) | n_eq, tot, sh);
     const uint32_t r = need_ties - ties_taken;              // ties still to take
     const uint32_t ex_eq = ex & 0xFFFFu;
     uint32_t pos = taken + (ex >> 16) + min(ex_eq, r);
@@ -223,8 +294,8 @@ __global__ __launch_bounds__(kKT) void k_topk_kl(const uint16_t *__restrict__ st
           ++tie_rank;
         }
         if (take) {
-          sh.idx[pos] = (int32_t)(8u * v + h);
-          sh.tv[pos] = bf16_to_f32(raw[h]);
+          se.idx[pos] = (int32_t)(8u * v + h);
+          se.tv[pos] = bf16_to_f32(raw[h]);
           ++pos;
         }
       }
@@ -235,42 +306,276 @@ __global__ __launch_bounds__(kKT) void k_topk_kl(const uint16_t *__restrict__ st
   }
   __syncthreads();
 
-  // the student's logits at the selected entries; both restricted softmaxes
-  const uint16_t *srow = student + row * (size_t)V;
-  float mt = -INFINITY, ms = -INFINITY;
-  for (int i = t; i < K; i += kKT) {
-    // (the clamp only guards the address; every index is in [0, V) by construction)
-    const float zs = bf16_to_f32(srow[min(max(sh.idx[i], 0), V - 1)]);
-    sh.sv[i] = zs;
-    mt = fmaxf(mt, sh.tv[i]);
-    ms = fmaxf(ms, zs);
+}
+
+// Inclusive prefix sum over the 64 lanes on DPP moves (rows of 16 lanes
+// shifted 1, 2, 4, 8, then the row broadcasts of lanes 15 and 31). Every lane
+// must be active.
+__device__ __forceinline__ uint32_t wave_scan_dpp(uint32_t v) {
+  v += __builtin_amdgcn_update_dpp(0u, v, 0x111, 0xf, 0xf, true);   // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0u, v, 0x112, 0xf, 0xf, true);   // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0u, v, 0x114, 0xf, 0xf, true);   // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0u, v, 0x118, 0xf, 0xf, true);   // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0u, v, 0x142, 0xa, 0xf, false);  // row_bcast:15
+  v += __builtin_amdgcn_update_dpp(0u, v, 0x143, 0xc, 0xf, false);  // row_bcast:31
+  return v;
+}
+
+// Block total of per-lane booleans, counted with ballots (one barrier;
+// alternating scratch rows).
+__device__ __forceinline__ uint32_t wave_count(bool f) {
+  return (uint32_t)__popcll(__ballot(f));
+}
+
+// One token row per workgroup, the row streamed once. A strided sample of the
+// row (one 8-logit vector per thread) gives a key L a little below the
+// sample's share of the top K. The stream appends the vocabulary index of
+// every entry with key >= L to an LDS list in vocabulary order (a block-wide
+// prefix sum per step of 4 vectors per thread). When the list holds at least
+// K entries and fits (the usual case) it alone decides the exact K-th largest
+// key, the ties (lower index first) and the ordered selection. Otherwise the
+// row is selected again by histograms (select_hist). Exact either way.
+template <bool REVERSE>
+__global__ __launch_bounds__(kKT) void k_topk_kl(const uint16_t *__restrict__ student,
+                                                 const uint16_t *__restrict__ teacher, int V,
+                                                 int K, const uint8_t *__restrict__ valid,
+                                                 const float *__restrict__ inv_n,
+                                                 int32_t *__restrict__ out_idx,
+                                                 float *__restrict__ out_grad,
+                                                 float *__restrict__ loss_tok) {
+  __shared__ KLShared sh;
+  __shared__ KLBig xs;
+  __shared__ uint32_t wt[2][kKW][2];   // per-wave totals of the packed step counts
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const size_t row = blockIdx.x;
+  const uint4 *trow = reinterpret_cast<const uint4 *>(teacher + row * (size_t)V);
+  const uint32_t nvec = (uint32_t)V / 8u;
+  int par = 0;
+  // block total of a per-thread count (wave sums on DPP, one barrier)
+  auto bsum = [&](uint32_t c) {
+    c = __builtin_amdgcn_readlane(wave_scan_dpp(c), 63);
+    if (lane == 0) sh.cnt[par][wave] = c;
+    __syncthreads();
+    uint32_t s = 0;
+#pragma unroll
+    for (int w = 0; w < kKW; ++w) s += sh.cnt[par][w];
+    par ^= 1;
+    return s;
+  };
+
+  // sample: one vector per thread, spread over the row
+  const uint32_t vs = nvec >= (uint32_t)kKT ? (uint32_t)(((unsigned long long)t * nvec) / kKT)
+                                            : (uint32_t)t;
+  const bool has_s = vs < nvec;
+  uint32_t sk[8];
+  {
+    const uint4 q = trow[min(vs, nvec - 1u)];
+    const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+    for (int h = 0; h < 8; ++h)
+      sk[h] = has_s ? order_key((w[h >> 1] >> (16 * (h & 1))) & 0xFFFFu) : 0u;
   }
-  mt = block_max(mt, sh);
-  ms = block_max(ms, sh);
-  float et = 0.0f, es = 0.0f;
-  for (int i = t; i < K; i += kKT) {
-    et += __expf(sh.tv[i] - mt);
-    es += __expf(sh.sv[i] - ms);
+  const uint32_t n_smp = bsum(has_s ? 8u : 0u);
+  // k' = the sample's expected share mu of the top K plus six standard
+  // deviations and 4 (so count(key >= L) >= K all but never fails, and the
+  // list stays near K + 6 sqrt(K V / n_smp)); at most n_smp, and the sample
+  // holds n_smp >= 8 keys >= 1, so lo = 1 satisfies count >= k'
+  const float mu = (float)K * (float)n_smp / (float)V;
+  const uint32_t kq = min(n_smp, (uint32_t)ceilf(mu + 6.0f * sqrtf(mu) + 4.0f));
+  uint32_t lo = 1, hi = 65536;
+  while (hi - lo > 1) {
+    const uint32_t mid = (lo + hi) >> 1;
+    uint32_t c = 0;
+#pragma unroll
+    for (int h = 0; h < 8; ++h) c += wave_count(sk[h] >= mid);
+    if (lane == 0) sh.cnt[par][wave] = c;
+    __syncthreads();
+    uint32_t tot = 0;
+#pragma unroll
+    for (int w = 0; w < kKW; ++w) tot += sh.cnt[par][w];
+    par ^= 1;
+    if (tot >= kq) lo = mid;
+    else hi = mid;
   }
-  et = block_sum(et, sh);
-  es = block_sum(es, sh);
-  const float lse_t = mt + __logf(et), lse_s = ms + __logf(es);
-  float l = 0.0f;
-  for (int i = t; i < K; i += kKT) {
-    const float lt = sh.tv[i] - lse_t, ls = sh.sv[i] - lse_s;
-    l += REVERSE ? __expf(ls) * (ls - lt) : __expf(lt) * (lt - ls);
+  const uint32_t L = lo;
+
+  // the stream: wave w owns the contiguous vectors [w * nv_w, (w + 1) * nv_w)
+  // and appends the indices of its entries with key >= L, in vocabulary
+  // order, to its own part of the list (wave-level prefix sums only)
+  const uint32_t nv_w = (nvec + kKW - 1) / kKW;
+  const uint32_t wv0 = min(nvec, (uint32_t)wave * nv_w), wv1 = min(nvec, wv0 + nv_w);
+  uint32_t wn = 0;                                           // this wave's count (wave-uniform)
+  uint32_t *wl = xs.cand + wave * kWaveCand;
+  for (uint32_t v0 = wv0; v0 < wv1; v0 += 4u * 64u) {
+    uint4 q[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) q[u] = trow[min(v0 + (uint32_t)u * 64u + lane, wv1 - 1u)];
+    uint32_t f[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const bool in = v0 + (uint32_t)u * 64u + lane < wv1;
+      const uint32_t w[4] = {q[u].x, q[u].y, q[u].z, q[u].w};
+#pragma unroll
+      for (int h = 0; h < 8; ++h) {
+        const uint32_t k = order_key((w[h >> 1] >> (16 * (h & 1))) & 0xFFFFu);
+        f[u] |= (uint32_t)(in && k >= L) << h;
+      }
+    }
+    // counts of the 4 steps, two 16-bit fields per word (at most 8 * 64 each)
+    const uint32_t c01 = __popc(f[0]) | (__popc(f[1]) << 16);
+    const uint32_t c23 = __popc(f[2]) | (__popc(f[3]) << 16);
+    const uint32_t i01 = wave_scan_dpp(c01), i23 = wave_scan_dpp(c23);
+    const uint32_t t01 = __builtin_amdgcn_readlane(i01, 63);
+    const uint32_t t23 = __builtin_amdgcn_readlane(i23, 63);
+    const uint32_t e01 = i01 - c01, e23 = i23 - c23;
+    const uint32_t tot0 = t01 & 0xFFFFu, tot1 = t01 >> 16, tot2 = t23 & 0xFFFFu;
+    const uint32_t pos0[4] = {wn + (e01 & 0xFFFFu), wn + tot0 + (e01 >> 16),
+                              wn + tot0 + tot1 + (e23 & 0xFFFFu),
+                              wn + tot0 + tot1 + tot2 + (e23 >> 16)};
+    wn += tot0 + tot1 + tot2 + (t23 >> 16);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      uint32_t m = f[u], p = pos0[u];
+      const uint32_t vb = 8u * (v0 + (uint32_t)u * 64u + lane);
+      while (m) {
+        const uint32_t h = __builtin_ctz(m);
+        m &= m - 1u;
+        if (p < (uint32_t)kWaveCand) wl[p] = vb + h;
+        ++p;
+      }
+    }
   }
-  const float loss = block_sum(l, sh);
-  const bool ok = valid ? valid[row] != 0 : true;
-  const float scale = ok ? inv_n[0] : 0.0f;
-  for (int i = t; i < K; i += kKT) {
-    const float lt = sh.tv[i] - lse_t, ls = sh.sv[i] - lse_s;
-    const float ps = __expf(ls);
-    const float g = REVERSE ? ps * ((ls - lt) - loss) : ps - __expf(lt);
-    out_idx[row * (size_t)K + i] = sh.idx[i];
-    out_grad[row * (size_t)K + i] = g * scale;
+  if (lane == 0) sh.cnt[par][wave] = wn;
+  __syncthreads();
+  uint32_t wbase[kKW + 1];
+  wbase[0] = 0;
+  bool overflow = false;
+#pragma unroll
+  for (int w = 0; w < kKW; ++w) {
+    const uint32_t c = sh.cnt[par][w];
+    wbase[w + 1] = wbase[w] + c;
+    overflow |= c > (uint32_t)kWaveCand;
   }
-  if (t == 0) loss_tok[row] = ok ? loss : 0.0f;
+  par ^= 1;
+  const uint32_t n = wbase[kKW];
+  // list entry i lives at wave w's part, offset i - wbase[w]
+  auto list_at = [&](uint32_t i) {
+    uint32_t w = 0;
+#pragma unroll
+    for (int x = 1; x < kKW; ++x) w += i >= wbase[x];
+    return xs.cand[w * kWaveCand + (i - wbase[w])];
+  };
+
+  if (n >= (uint32_t)K && !overflow && n <= (uint32_t)kCandMax) {
+    // this thread's contiguous slice of the list and its keys (re-read from
+    // the teacher row: a few entries per thread)
+    constexpr int kPer = kCandMax / kKT;
+    const uint32_t per = (n + kKT - 1) / kKT;
+    const uint32_t c0 = min(n, (uint32_t)t * per), c1 = min(n, c0 + per);
+    const uint16_t *trow16 = teacher + row * (size_t)V;
+    uint32_t ci[kPer], ck[kPer];
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) ci[u] = (c0 + u < c1) ? list_at(c0 + u) : 0u;
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) ck[u] = trow16[ci[u]];
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) ck[u] = (c0 + u < c1) ? order_key(ck[u]) : 0u;
+    // the K-th largest key among the list (every key >= it is listed: the
+    // list holds all keys >= L, at least K of them): a count per key value
+    // from L up (the list is in registers now, its memory is free)
+    uint32_t kmax = 0;
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) kmax = max(kmax, ck[u]);
+    for (int o = 32; o > 0; o >>= 1) kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, o, 64));
+    if (lane == 0) sh.cnt[par][wave] = kmax;
+    __syncthreads();
+    kmax = 0;
+#pragma unroll
+    for (int w = 0; w < kKW; ++w) kmax = max(kmax, sh.cnt[par][w]);
+    par ^= 1;
+    uint32_t tau;
+    if (kmax - L < (uint32_t)kHistBins) {
+      uint32_t *hb = xs.cand;                                // kHistBins counters
+      for (int i = t; i < kHistBins; i += kKT) hb[i] = 0u;
+      __syncthreads();
+#pragma unroll
+      for (int u = 0; u < kPer; ++u)
+        if (ck[u] >= L) atomicAdd(&hb[ck[u] - L], 1u);
+      __syncthreads();
+      // thread t sums bins from the top: its kHistBins / kKT bins, highest first
+      constexpr int kB = kHistBins / kKT;
+      const uint32_t top = kHistBins - 1 - t * kB;           // this thread's highest bin
+      uint32_t bc[kB], sum = 0;
+#pragma unroll
+      for (int j = 0; j < kB; ++j) {
+        bc[j] = hb[top - j];
+        sum += bc[j];
+      }
+      uint32_t total;
+      uint32_t acc = block_excl_scan<kKT>(sum, total, sh);    // entries in higher bins
+#pragma unroll
+      for (int j = 0; j < kB; ++j) {
+        if (acc < (uint32_t)K && acc + bc[j] >= (uint32_t)K) sh.cnt[par][0] = L + top - j;
+        acc += bc[j];
+      }
+      __syncthreads();
+      tau = sh.cnt[par][0];
+      par ^= 1;
+    } else {
+      uint32_t lo2 = L, hi2 = 65536;
+      while (hi2 - lo2 > 1) {
+        const uint32_t mid = (lo2 + hi2) >> 1;
+        uint32_t c = 0;
+#pragma unroll
+        for (int u = 0; u < kPer; ++u)
+          if ((uint32_t)u < per) c += wave_count(ck[u] >= mid);   // (block-uniform test)
+        if (lane == 0) sh.cnt[par][wave] = c;
+        __syncthreads();
+        uint32_t tot = 0;
+#pragma unroll
+        for (int w = 0; w < kKW; ++w) tot += sh.cnt[par][w];
+        par ^= 1;
+        if (tot >= (uint32_t)K) lo2 = mid;
+        else hi2 = mid;
+      }
+      tau = lo2;
+    }
+    // ordered selection: keys above tau, then the first ties
+    uint32_t n_gt = 0, n_eq = 0;
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      n_gt += ck[u] > tau;
+      n_eq += ck[u] == tau;     // (keys past the slice are 0, never equal to tau >= 1)
+    }
+    uint32_t tot;
+    const uint32_t ex = block_excl_scan<kKT>((n_gt << 16) | n_eq, tot, sh);
+    const uint32_t need_ties = (uint32_t)K - (tot >> 16);
+    uint32_t p = (ex >> 16) + min(ex & 0xFFFFu, need_ties);
+    uint32_t tie_rank = ex & 0xFFFFu;
+    uint32_t npick = 0;
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      bool take = ck[u] > tau;
+      if (ck[u] == tau) {
+        take = tie_rank < need_ties;
+        ++tie_rank;
+      }
+      npick |= (uint32_t)take << u;
+    }
+    __syncthreads();   // the selected entries overwrite the list's memory
+#pragma unroll
+    for (int u = 0; u < kPer; ++u)
+      if ((npick >> u) & 1u) {
+        xs.sel.idx[p] = (int32_t)ci[u];
+        xs.sel.tv[p] = bf16_to_f32(raw_of_key(ck[u]));
+        ++p;
+      }
+  } else {
+    select_hist(sh, xs, trow, nvec, K);
+  }
+  __syncthreads();
+  kl_tail<kKT, REVERSE>(sh, xs.sel, student, row, V, K, valid, inv_n, out_idx, out_grad,
+                        loss_tok);
 }
 
 // loss_mean = (sum over tokens of loss_tok, fixed order) * inv_n

@@ -102,6 +102,24 @@ def test_topk_kl_identical_logits_and_all_equal_rows():
     assert np.array_equal(idx, O.topk_set(t, K))
 
 
+@pytest.mark.parametrize("reverse", [False, True])
+def test_topk_kl_histogram_path(reverse):
+    """Rows whose sampled bracket admits more candidates than LDS holds (long
+    runs of equal logits) take the histogram selection; mixed with rows that
+    take the sampled path in the same launch."""
+    print(f"[kd] histogram path reverse={reverse}", flush=True)
+    rng = np.random.default_rng(77)
+    T, V, K = 6, 16384 + 8 * 37, 300
+    t = _ties(rng, T, V, 0.25)
+    t[1] = O.f32_to_bf16(np.full(V, -0.5, np.float32))                 # all equal
+    z = np.where(rng.random(V) < 0.7, 2.0, rng.standard_normal(V))      # 70 % tied at the top
+    t[3] = O.f32_to_bf16(z.astype(np.float32))
+    s = O.f32_to_bf16((O.bf16_to_f32(t) + rng.standard_normal((T, V)) * 0.3).astype(np.float32))
+    got = _run(s, t, K, reverse)
+    _check(s, t, K, reverse, None, got)
+    assert np.array_equal(got[0][1], np.arange(K))
+
+
 def test_topk_kl_full_workload_sampled():
     """kd-topk1000-t4096-v151936: the whole batch on the GPU, sampled tokens
     against the oracle, the mean against the GPU's own per-token losses."""

@@ -73,6 +73,9 @@ def parse():
     ap.add_argument("--weight-scales", choices=["default", "per-tensor"], default="default",
                     help="per-tensor: one scale per expert matrix (fp8 workload only)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the measurements outside the step (export decode, self-teacher "
+                         "forward, top-K KL)")
     ap.add_argument("--cpu-sample-experts", type=int, default=6)
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
@@ -330,8 +333,10 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    export = measure_export(torch, F, layer, fmt)
-    distill = measure_distill(torch, F, W, layer, x, ids, probs)
+    export = distill = None
+    if not args.no_extras:
+        export = measure_export(torch, F, layer, fmt)
+        distill = measure_distill(torch, F, W, layer, x, ids, probs)
 
     cpu = None
     if not args.no_cpu_baseline:

@@ -57,22 +57,18 @@ constexpr int kStageBytes = 256 * BK * 2;  // one operand, one stage: 32 KiB
 
 enum Mode { FWD = 0, DGRAD = 1, WGRAD = 2 };
 
-// The ring: distinct LDS objects per stage and operand, so that the compiler
-// can tell a stage being read from the stages being filled.
-__shared__ __attribute__((aligned(1024))) char g_p0[kStageBytes];
-__shared__ __attribute__((aligned(1024))) char g_p1[kStageBytes];
-
-__shared__ __attribute__((aligned(1024))) char g_q0[kStageBytes];
-__shared__ __attribute__((aligned(1024))) char g_q1[kStageBytes];
-
+// The ring: one LDS object holding both stages of both operands, so that the
+// stage and operand offsets of every fragment read are compile-time
+// immediates on one base address.
+__shared__ __attribute__((aligned(1024))) char g_ring[4 * kStageBytes];
 
 template <int S>
 __device__ __forceinline__ char *stage_p() {
-  return S == 0 ? g_p0 : g_p1;
+  return g_ring + S * kStageBytes;
 }
 template <int S>
 __device__ __forceinline__ char *stage_q() {
-  return S == 0 ? g_q0 : g_q1;
+  return g_ring + (2 + S) * kStageBytes;
 }
 
 // Contraction-contiguous layout: row idx (0..255) of 8 16-byte chunks (8
@@ -95,13 +91,23 @@ __device__ __forceinline__ uint32_t trn_off(uint32_t c, uint32_t chunk) {
   return c * 512u + ((chunk ^ tr_sw(c)) << 4);
 }
 
-// 16 bytes per lane from global memory into LDS at lds_wave_base + 16 * lane.
+// 16 bytes per lane from global memory into LDS at lds_wave_base + 16 * lane:
+// the lane reads base + off (base uniform, held in scalar registers).
 // Issued as inline asm: the compiler then does not model the LDS write and
 // inserts no wait before reads of the other stages; the ring's own
-// vmcnt waits and barriers order the accesses.
-__device__ __forceinline__ void dma16(const char *g, char *lds_wave_base) {
+// vmcnt waits and barriers order the accesses. The compiler's hazard pass
+// does not look inside the asm, so it starts with the wait states the
+// hardware needs when the instruction just before wrote M0 (one) or, as a
+// vector instruction (v_readfirstlane), one of the base registers (five).
+__device__ __forceinline__ void dma16(const char *base, uint32_t off, char *lds_wave_base) {
   const uint32_t m0v = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_wave_base);
-  asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(g), "{m0}"(m0v) : "memory");
+  // readfirstlane returns a signed int: widen through uint32_t (no sign extension)
+  const uint64_t b = (uint64_t)(uintptr_t)base;
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b);
+  const uint64_t sb = ((uint64_t)hi << 32) | (uint64_t)lo;
+  asm volatile("s_nop 4\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(sb), "{m0}"(m0v)
+               : "memory");
 }
 
 // One barrier for the whole block without a memory fence (a fence would wait
@@ -334,7 +340,7 @@ struct NormalDMA {  // contraction-contiguous: instr covers 8 rows x 128 B
   template <int S>
   __device__ __forceinline__ void issue(const char *base, char *stage, int c0, int wave) const {
 #pragma unroll
-    for (int ii = 0; ii < 4; ++ii) dma16(base + off[ii] + c0 * 2, stage + (4 * wave + ii) * 1024);
+    for (int ii = 0; ii < 4; ++ii) dma16(base + c0 * 2, off[ii], stage + (4 * wave + ii) * 1024);
   }
 };
 struct TransDMA {  // transposed: instr covers 2 contraction rows x 512 B
@@ -355,7 +361,7 @@ struct TransDMA {  // transposed: instr covers 2 contraction rows x 512 B
     for (int ii = 0; ii < 4; ++ii) {
       const int c = c0 + crow[ii];
       const int cc = c < c_end ? c : c0;
-      dma16(base + (size_t)cc * ld * 2 + col_off[ii], stage + (4 * wave + ii) * 1024);
+      dma16(base, (uint32_t)cc * (ld * 2) + col_off[ii], stage + (4 * wave + ii) * 1024);
     }
   }
 };
@@ -486,7 +492,7 @@ template <int MODE, int WFMT>
 __device__ __forceinline__ void run_tile(const GemmArgs &a, const int *tile_start, const Tile &tl,
                                          bool pre, int next_w) {
   const int t = threadIdx.x;
-  const int lane = t & 63, wave = t >> 6;
+  const int lane = t & 63, wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int wi = wave & 1, wj = wave >> 1;  // 2 x 4 waves: 128 (i) x 64 (j) each
   const int e = tl.e, i0 = tl.i0, j0 = tl.j0, j_end = tl.j_end;
   const TileLoads<MODE> ld(a, tl, wave, lane);
@@ -513,18 +519,15 @@ __device__ __forceinline__ void run_tile(const GemmArgs &a, const int *tile_star
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[s][u][v] = 0.0f;
 
-  // FWD / DGRAD: a wave whose 64 rows all lie past the expert's last row (the
-  // ragged last row tile) skips its fragment reads and MFMAs; it still takes
-  // part in the loads and barriers.
-  const bool live = MODE == WGRAD || j0 + wj * WJ_TILE < j_end;
-
   // MFMA fragments of one 16-deep step: 4 P sub-tiles, 2 Q sub-tiles
   struct Frags {
     bf16x8v p[4], q[2];
   };
-  auto read_frags = [&](auto stage_tag, int kt, int ks, Frags &f) {
+  // TAIL: WGRAD's last stage, whose contraction rows past the chunk's last
+  // routed row are zeroed in the fragments
+  auto read_frags = [&](auto stage_tag, auto tail_tag, int kt, int ks, Frags &f) {
     constexpr int S = decltype(stage_tag)::value;
-    if (!live) return;
+    constexpr bool TAIL = decltype(tail_tag)::value;
     const char *sp = stage_p<S>();
     const char *sq = stage_q<S>();
 #pragma unroll
@@ -535,7 +538,7 @@ __device__ __forceinline__ void run_tile(const GemmArgs &a, const int *tile_star
     for (int u = 0; u < 2; ++u)
       f.q[u] = (MODE == WGRAD) ? frag_trans(sq, wj * WJ_TILE + u * 32, ks, lane)
                                : frag_normal(sq, wj * WJ_TILE + u * 32, ks, lane);
-    if (MODE == WGRAD && (kt + 1) * BK > c_total) {  // ragged tail of the routed rows
+    if (TAIL && (kt + 1) * BK > c_total) {
       const int cfirst = kt * BK + 16 * ks + 8 * (lane >> 5);
 #pragma unroll
       for (int s = 0; s < 4; ++s) f.p[s] = zero_tail(f.p[s], cfirst, c_total);
@@ -544,7 +547,6 @@ __device__ __forceinline__ void run_tile(const GemmArgs &a, const int *tile_star
     }
   };
   auto mfmas = [&](const Frags &f) {
-    if (!live) return;
 #pragma unroll
     for (int s = 0; s < 4; ++s)
 #pragma unroll
@@ -554,23 +556,53 @@ __device__ __forceinline__ void run_tile(const GemmArgs &a, const int *tile_star
   // Two-stage ring: stage kt lives in buffer kt % 2. After this wave's loads
   // of stage kt have landed, one barrier both publishes stage kt to every wave
   // and retires the reads of stage kt-1, whose buffer then takes stage kt+1
-  // while stage kt is multiplied.
-  auto step = [&](auto stage_tag, int kt) {
+  // while stage kt is multiplied. FWD / DGRAD read the fragments of step
+  // ks + 1 while the MFMAs of step ks run. LIVE / TAIL are compile-time so that each
+  // stage is one straight block of LDS reads and MFMAs.
+  auto step = [&](auto stage_tag, auto live_tag, auto tail_tag, int kt) {
     constexpr int S = decltype(stage_tag)::value;
+    constexpr bool LIVE = decltype(live_tag)::value;
     wait_vm<0>();
     block_barrier();
     if (kt + 1 < nk) issue(std::integral_constant<int, S ^ 1>{}, kt + 1);
+    if (!LIVE) return;
+    if (MODE == WGRAD) {  // measured faster without the second fragment set
+#pragma unroll
+      for (int ks = 0; ks < BK / 16; ++ks) {
+        Frags f;
+        read_frags(stage_tag, tail_tag, kt, ks, f);
+        mfmas(f);
+      }
+      return;
+    }
+    Frags f[2];
+    read_frags(stage_tag, tail_tag, kt, 0, f[0]);
 #pragma unroll
     for (int ks = 0; ks < BK / 16; ++ks) {
-      Frags f;
-      read_frags(stage_tag, kt, ks, f);
-      mfmas(f);
+      if (ks + 1 < BK / 16) read_frags(stage_tag, tail_tag, kt, ks + 1, f[(ks + 1) & 1]);
+      __builtin_amdgcn_sched_barrier(0);
+      mfmas(f[ks & 1]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  // FWD / DGRAD: a wave whose 64 rows all lie past the expert's last row (the
+  // ragged last row tile) skips its fragment reads and MFMAs; it still takes
+  // part in the loads and barriers.
+  const bool live = MODE == WGRAD || j0 + wj * WJ_TILE < j_end;
+  auto step_any = [&](auto stage_tag, int kt) {
+    using T_ = std::true_type;
+    using F_ = std::false_type;
+    if (MODE == WGRAD) {
+      step(stage_tag, T_{}, T_{}, kt);
+    } else {
+      if (live) step(stage_tag, T_{}, F_{}, kt);
+      else step(stage_tag, F_{}, F_{}, kt);
     }
   };
   if (nk > 0 && !pre) issue(std::integral_constant<int, 0>{}, 0);
   for (int kt = 0; kt < nk; kt += NSTAGE) {
-    step(std::integral_constant<int, 0>{}, kt);
-    if (kt + 1 < nk) step(std::integral_constant<int, 1>{}, kt + 1);
+    step_any(std::integral_constant<int, 0>{}, kt);
+    if (kt + 1 < nk) step_any(std::integral_constant<int, 1>{}, kt + 1);
   }
 
   // accumulator (s, u, v) of this lane: i = i0 + wi*128 + s*32 + 8*(v/4) + 4*(lane/32) + v%4,

@@ -62,8 +62,16 @@ __device__ __forceinline__ uint32_t e2m1_code_of_mag(float v) {
 
 // Two values z0, z1 rounded to E2M1 on the converter: values (sign of z kept,
 // |z| > 6 saturates) and the packed codes, z0 in the low nibble.
+// An unspecified register value, made by no instruction: the converters below
+// write only the low byte / half-word of their destination and keep the rest,
+// which is never read, so the kept bits need not be cleared first.
+__device__ __forceinline__ uint32_t undef_u32() {
+  uint32_t u;
+  asm volatile("" : "=v"(u));
+  return u;
+}
 __device__ __forceinline__ uint32_t e2m1_pair(float z0, float z1, float &v0, float &v1) {
-  const uint32_t c = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, z0, z1, 1.0f, 0);
+  const uint32_t c = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(undef_u32(), z0, z1, 1.0f, 0);
   const f32x2_t v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, 1.0f, 0);
   v0 = v.x;
   v1 = v.y;
@@ -72,7 +80,7 @@ __device__ __forceinline__ uint32_t e2m1_pair(float z0, float z1, float &v0, flo
 // Two values already clamped to [-448, 448] rounded to E4M3: values and the
 // packed codes, z0 in the low byte.
 __device__ __forceinline__ uint32_t e4m3_pair(float z0, float z1, float &v0, float &v1) {
-  const uint32_t c = __builtin_amdgcn_cvt_pk_fp8_f32(z0, z1, 0u, false);
+  const uint32_t c = __builtin_amdgcn_cvt_pk_fp8_f32(z0, z1, undef_u32(), false);
   const f32x2_t v = __builtin_amdgcn_cvt_pk_f32_fp8(c, false);
   v0 = v.x;
   v1 = v.y;

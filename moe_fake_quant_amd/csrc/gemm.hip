@@ -226,18 +226,31 @@ __device__ __forceinline__ void wgrad_epilogue(const GemmArgs &a, const f32x16 (
   // 16-blocks k0 + 16 j (every group is a multiple of 16 long)
   float sc8[8], r8[8], fac8[8], zp8[8];
   if (WFMT == FQ_FMT_NVFP4) {
-    // theta of the eight blocks in two 16-byte loads, rounded to E4M3 two at a time
-    const float4 *tp = reinterpret_cast<const float4 *>(a.scale + srow + k0 / 16);
-    const float4 t0 = tp[0], t1 = tp[1];
-    const float th[8] = {t0.x, t0.y, t0.z, t0.w, t1.x, t1.y, t1.z, t1.w};
+    // lane halves share n and all eight blocks: each half derives four of
+    // them (theta rounded to E4M3, its reciprocal, the theta factor) and
+    // takes the other four from lane ^ 32
+    const int h = lane >> 5;
+    const float4 t4 = *reinterpret_cast<const float4 *>(a.scale + srow + k0 / 16 + 4 * h);
+    const float th[4] = {t4.x, t4.y, t4.z, t4.w};
+    float rm[4], fm[4];
 #pragma unroll
-    for (int j = 0; j < 8; j += 2) {
+    for (int j = 0; j < 4; j += 2) {
       float v0, v1;
       e4m3_pair(fminf(fmaxf(th[j], 0.0f), kE4M3Max), fminf(fmaxf(th[j + 1], 0.0f), kE4M3Max), v0, v1);
-      sc8[j] = v0 * g_e;
-      sc8[j + 1] = v1 * g_e;
-      fac8[j] = nvfp4_theta_factor(th[j], g_e);
-      fac8[j + 1] = nvfp4_theta_factor(th[j + 1], g_e);
+      rm[j] = safe_recip(v0 * g_e);
+      rm[j + 1] = safe_recip(v1 * g_e);
+      fm[j] = nvfp4_theta_factor(th[j], g_e);
+      fm[j + 1] = nvfp4_theta_factor(th[j + 1], g_e);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float ro = __shfl_xor(rm[j], 32, 64), fo = __shfl_xor(fm[j], 32, 64);
+      r8[j] = h ? ro : rm[j];
+      r8[4 + j] = h ? rm[j] : ro;
+      fac8[j] = h ? fo : fm[j];
+      fac8[4 + j] = h ? fm[j] : fo;
+      sc8[j] = sc8[4 + j] = 0.0f;  // the E2M1 factor needs only the reciprocal
+      zp8[j] = zp8[4 + j] = 0.0f;
     }
   } else {
 #pragma unroll
@@ -246,12 +259,12 @@ __device__ __forceinline__ void wgrad_epilogue(const GemmArgs &a, const f32x16 (
       sc8[j] = a.scale[srow + gi];
       if (WFMT == FQ_FMT_INT4) zp8[j] = fminf(fmaxf(rintf(a.zero_point[srow + gi]), 0.0f), 15.0f);
     }
-  }
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    r8[j] = safe_recip(sc8[j]);
-    if (WFMT != FQ_FMT_INT4) zp8[j] = 0.0f;
-    if (WFMT != FQ_FMT_NVFP4) fac8[j] = 1.0f;
+    for (int j = 0; j < 8; ++j) {
+      r8[j] = safe_recip(sc8[j]);
+      if (WFMT != FQ_FMT_INT4) zp8[j] = 0.0f;
+      fac8[j] = 1.0f;
+    }
   }
   float part_s[4], part_z[4];
 #pragma unroll

@@ -27,11 +27,12 @@ struct KLShared {
   uint32_t cnt[2][kKW];
   float red2[2][kKW][2];
 };
-// The selected entries of a row.
+// The selected entries of a row (K <= KM).
+template <int KM>
 struct KLSel {
-  int32_t idx[kTopKMax];
-  float tv[kTopKMax];
-  float sv[kTopKMax];
+  int32_t idx[KM];
+  float tv[KM];
+  float sv[KM];
 };
 // Histograms of the histogram selection.
 struct KLHist {
@@ -42,11 +43,13 @@ constexpr int kCandMax = 8192;     // candidates of the sampled selection
 constexpr int kWaveCand = kCandMax / kKW;   // one part per wave
 constexpr int kHistBins = 4096;    // key-value counters of the threshold search
 // The big LDS arrays share one region: candidates (or histograms) while the
-// row is selected, then the selected entries.
+// row is selected, then the selected entries. Sized for K <= KM: the smaller
+// instance (K <= 1024) leaves room for four rows' workgroups per CU.
+template <int KM>
 union KLBig {
   uint32_t cand[kCandMax];             // vocabulary indices
   KLHist hs;
-  KLSel sel;
+  KLSel<KM> sel;
 };
 
 // bf16 bits -> 16-bit key whose unsigned order is the value order (-0 and +0
@@ -169,8 +172,8 @@ __global__ __launch_bounds__(256) void k_count_valid(const uint8_t *__restrict__
 
 // The K selected entries (se.idx, se.tv) of one row -> the student's logits
 // there, both restricted softmaxes, the loss and the scaled gradient.
-template <int NT, bool REVERSE>
-__device__ __forceinline__ void kl_tail(KLShared &sh, KLSel &se,
+template <int NT, bool REVERSE, int KM>
+__device__ __forceinline__ void kl_tail(KLShared &sh, KLSel<KM> &se,
                                         const uint16_t *__restrict__ student,
                                         size_t row, int V, int K,
                                         const uint8_t *__restrict__ valid,
@@ -222,10 +225,11 @@ __device__ __forceinline__ void kl_tail(KLShared &sh, KLSel &se,
 // low byte find the K-th largest key; a third pass compacts the selection in
 // vocabulary order (per-chunk block scans) and stops once K are in. Reads the
 // row three times; used when the sampled bracket does not hold.
-__device__ __forceinline__ void select_hist(KLShared &sh, KLBig &big,
+template <int KM>
+__device__ __forceinline__ void select_hist(KLShared &sh, KLBig<KM> &big,
                                             const uint4 *__restrict__ trow, uint32_t nvec, int K) {
   KLHist &hs = big.hs;
-  KLSel &se = big.sel;   // written only after the histograms are done with
+  KLSel<KM> &se = big.sel;   // written only after the histograms are done with
   const int t = threadIdx.x, wave = t >> 6;
   // pass 1: histogram of the key's high byte
   zero_hist(hs);
@@ -335,8 +339,8 @@ __device__ __forceinline__ uint32_t wave_count(bool f) {
 // K entries and fits (the usual case) it alone decides the exact K-th largest
 // key, the ties (lower index first) and the ordered selection. Otherwise the
 // row is selected again by histograms (select_hist). Exact either way.
-template <bool REVERSE>
-__global__ __launch_bounds__(kKT) void k_topk_kl(const uint16_t *__restrict__ student,
+template <bool REVERSE, int KM>
+__global__ __launch_bounds__(kKT) __attribute__((amdgpu_waves_per_eu(KM <= 1024 ? 8 : 6))) void k_topk_kl(const uint16_t *__restrict__ student,
                                                  const uint16_t *__restrict__ teacher, int V,
                                                  int K, const uint8_t *__restrict__ valid,
                                                  const float *__restrict__ inv_n,
@@ -344,7 +348,7 @@ __global__ __launch_bounds__(kKT) void k_topk_kl(const uint16_t *__restrict__ st
                                                  float *__restrict__ out_grad,
                                                  float *__restrict__ loss_tok) {
   __shared__ KLShared sh;
-  __shared__ KLBig xs;
+  __shared__ KLBig<KM> xs;
   __shared__ uint32_t wt[2][kKW][2];   // per-wave totals of the packed step counts
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const size_t row = blockIdx.x;
@@ -574,7 +578,7 @@ __global__ __launch_bounds__(kKT) void k_topk_kl(const uint16_t *__restrict__ st
     select_hist(sh, xs, trow, nvec, K);
   }
   __syncthreads();
-  kl_tail<kKT, REVERSE>(sh, xs.sel, student, row, V, K, valid, inv_n, out_idx, out_grad,
+  kl_tail<kKT, REVERSE, KM>(sh, xs.sel, student, row, V, K, valid, inv_n, out_idx, out_grad,
                         loss_tok);
 }
 
@@ -603,12 +607,10 @@ void launch_topk_kl(const uint16_t *student, const uint16_t *teacher, int T, int
                     float *loss_mean, float *inv_n, hipStream_t st) {
   hipLaunchKernelGGL(k_count_valid, dim3(1), dim3(256), 0, st, valid, T, inv_n);
   if (T > 0) {
-    if (reverse)
-      hipLaunchKernelGGL(k_topk_kl<true>, dim3(T), dim3(kKT), 0, st, student, teacher, V, K, valid,
-                         inv_n, idx, grad, loss_tok);
-    else
-      hipLaunchKernelGGL(k_topk_kl<false>, dim3(T), dim3(kKT), 0, st, student, teacher, V, K,
-                         valid, inv_n, idx, grad, loss_tok);
+    auto k = reverse ? (K <= 1024 ? k_topk_kl<true, 1024> : k_topk_kl<true, kTopKMax>)
+                     : (K <= 1024 ? k_topk_kl<false, 1024> : k_topk_kl<false, kTopKMax>);
+    hipLaunchKernelGGL(k, dim3(T), dim3(kKT), 0, st, student, teacher, V, K, valid, inv_n, idx,
+                       grad, loss_tok);
   }
   hipLaunchKernelGGL(k_kl_mean, dim3(1), dim3(1024), 0, st, loss_tok, T, inv_n, loss_mean);
 }

@@ -18,6 +18,8 @@ namespace fq {
 
 namespace {
 
+typedef short s16x2 __attribute__((ext_vector_type(2)));
+
 constexpr int kKT = 512;           // threads per row
 constexpr int kKW = kKT / 64;      // waves per row
 
@@ -410,19 +412,48 @@ __global__ __launch_bounds__(kKT) __attribute__((amdgpu_waves_per_eu(KM <= 1024 
   const uint32_t wv0 = min(nvec, (uint32_t)wave * nv_w), wv1 = min(nvec, wv0 + nv_w);
   uint32_t wn = 0;                                           // this wave's count (wave-uniform)
   uint32_t *wl = xs.cand + wave * kWaveCand;
+  // A bound above +0 (the usual case: the top of a logit row) is tested on
+  // the raw bits: for such a bound, key >= L holds exactly when the bf16
+  // pattern, read as a signed 16-bit integer, is >= the bound's pattern b
+  // (negative values and -0 read as negative integers). Per 32-bit word, one
+  // packed saturating subtract (b - 1) - x gives both halves' answers in
+  // their sign bits; v_perm's sign-replicating selectors gather the eight
+  // signs of a vector into bytes in element order, and two byte dot
+  // products with one bit per byte pack them into the 8-bit flag mask.
+  const bool pos_bound = L > 0x8000u;
+  const uint32_t bm1 = (raw_of_key(L) - 1u) & 0xFFFFu;
+  const s16x2 bm1x2 = __builtin_bit_cast(s16x2, bm1 | (bm1 << 16));
   for (uint32_t v0 = wv0; v0 < wv1; v0 += 4u * 64u) {
     uint4 q[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) q[u] = trow[min(v0 + (uint32_t)u * 64u + lane, wv1 - 1u)];
     uint32_t f[4] = {0u, 0u, 0u, 0u};
+    if (pos_bound) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const bool in = v0 + (uint32_t)u * 64u + lane < wv1;
-      const uint32_t w[4] = {q[u].x, q[u].y, q[u].z, q[u].w};
+      for (int u = 0; u < 4; ++u) {
+        const bool in = v0 + (uint32_t)u * 64u + lane < wv1;
+        const uint32_t w[4] = {q[u].x, q[u].y, q[u].z, q[u].w};
+        uint32_t d[4];
 #pragma unroll
-      for (int h = 0; h < 8; ++h) {
-        const uint32_t k = order_key((w[h >> 1] >> (16 * (h & 1))) & 0xFFFFu);
-        f[u] |= (uint32_t)(in && k >= L) << h;
+        for (int p = 0; p < 4; ++p)
+          d[p] = __builtin_bit_cast(
+              uint32_t, __builtin_elementwise_sub_sat(bm1x2, __builtin_bit_cast(s16x2, w[p])));
+        const uint32_t lo = __builtin_amdgcn_perm(d[1], d[0], 0x0B0A0908u) & 0x08040201u;
+        const uint32_t hi = __builtin_amdgcn_perm(d[3], d[2], 0x0B0A0908u) & 0x80402010u;
+        const uint32_t fu =
+            __builtin_amdgcn_udot4(hi, 0x01010101u, __builtin_amdgcn_udot4(lo, 0x01010101u, 0u, false), false);
+        f[u] = in ? fu : 0u;
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const bool in = v0 + (uint32_t)u * 64u + lane < wv1;
+        const uint32_t w[4] = {q[u].x, q[u].y, q[u].z, q[u].w};
+#pragma unroll
+        for (int h = 0; h < 8; ++h) {
+          const uint32_t k = order_key((w[h >> 1] >> (16 * (h & 1))) & 0xFFFFu);
+          f[u] |= (uint32_t)(in && k >= L) << h;
+        }
       }
     }
     // counts of the 4 steps, two 16-bit fields per word (at most 8 * 64 each)

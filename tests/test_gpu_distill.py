@@ -103,6 +103,29 @@ def test_topk_kl_identical_logits_and_all_equal_rows():
 
 
 @pytest.mark.parametrize("reverse", [False, True])
+def test_topk_kl_negative_and_positive_bounds(reverse):
+    """Rows whose K-th largest logit is negative (log-probability-like rows:
+    every logit < 0) take the general key compare in the stream; rows with a
+    positive one take the raw-bits compare; both in one launch, with ties and
+    signed zeros."""
+    print(f"[kd] negative / positive bounds reverse={reverse}", flush=True)
+    rng = np.random.default_rng(31)
+    T, V, K = 12, 8 * 2503, 211
+    t = _ties(rng, T, V, 0.25)
+    z = O.bf16_to_f32(t).astype(np.float64)
+    neg = np.arange(T) % 2 == 1
+    z[neg] = -np.abs(z[neg]) - 3.0                        # every logit negative
+    z[4] = -np.abs(z[4])                                  # 100 positives, then half zeros:
+    z[4, :V // 2] = 0.0                                   # the K-th largest is +-0
+    z[4, rng.choice(V, 100, replace=False)] = 1.5
+    t = O.f32_to_bf16(z.astype(np.float32))
+    t[4, :V // 2] = np.where(rng.random(V // 2) < 0.5, 0x8000, 0)
+    s = O.f32_to_bf16((O.bf16_to_f32(t) + rng.standard_normal((T, V)) * 0.3).astype(np.float32))
+    got = _run(s, t, K, reverse)
+    _check(s, t, K, reverse, None, got)
+
+
+@pytest.mark.parametrize("reverse", [False, True])
 def test_topk_kl_histogram_path(reverse):
     """Rows whose sampled bracket admits more candidates than LDS holds (long
     runs of equal logits) take the histogram selection; mixed with rows that

@@ -12,6 +12,8 @@
 // over an order-preserving 16-bit key of the bf16 logits (select_hist). The
 // student logits are gathered at the K selected indices; both restricted
 // softmaxes, the loss and the gradient come from LDS.
+#include <type_traits>
+
 #include "internal.hpp"
 
 namespace fq {
@@ -420,6 +422,10 @@ __global__ __launch_bounds__(kKT) __attribute__((amdgpu_waves_per_eu(KM <= 1024 
   // their sign bits; v_perm's sign-replicating selectors gather the eight
   // signs of a vector into bytes in element order, and two byte dot
   // products with one bit per byte pack them into the 8-bit flag mask.
+  // list entries: the vocabulary index, or (when every wave's stretch of the
+  // row has at most 65536 entries) the index within the stretch << 16 | key,
+  // so that the keys need not be read again
+  const bool packed = nv_w * 8u <= 65536u;
   const bool pos_bound = L > 0x8000u;
   const uint32_t bm1 = (raw_of_key(L) - 1u) & 0xFFFFu;
   const s16x2 bm1x2 = __builtin_bit_cast(s16x2, bm1 | (bm1 << 16));
@@ -475,7 +481,12 @@ __global__ __launch_bounds__(kKT) __attribute__((amdgpu_waves_per_eu(KM <= 1024 
       while (m) {
         const uint32_t h = __builtin_ctz(m);
         m &= m - 1u;
-        if (p < (uint32_t)kWaveCand) wl[p] = vb + h;
+        uint32_t e = vb + h;
+        if (packed) {
+          const uint32_t word = h < 4 ? (h < 2 ? q[u].x : q[u].y) : (h < 6 ? q[u].z : q[u].w);
+          e = ((e - 8u * wv0) << 16) | order_key((word >> (16u * (h & 1u))) & 0xFFFFu);
+        }
+        if (p < (uint32_t)kWaveCand) wl[p] = e;
         ++p;
       }
     }
@@ -493,28 +504,41 @@ __global__ __launch_bounds__(kKT) __attribute__((amdgpu_waves_per_eu(KM <= 1024 
   }
   par ^= 1;
   const uint32_t n = wbase[kKW];
-  // list entry i lives at wave w's part, offset i - wbase[w]
-  auto list_at = [&](uint32_t i) {
+  // list entry i lives at wave w's part, offset i - wbase[w]: its vocabulary
+  // index and, for packed entries, its key (else 0)
+  auto list_at = [&](uint32_t i, uint32_t &key) {
     uint32_t w = 0;
 #pragma unroll
     for (int x = 1; x < kKW; ++x) w += i >= wbase[x];
-    return xs.cand[w * kWaveCand + (i - wbase[w])];
+    const uint32_t e = xs.cand[w * kWaveCand + (i - wbase[w])];
+    if (!packed) {
+      key = 0u;
+      return e;
+    }
+    key = e & 0xFFFFu;
+    return 8u * min(nvec, w * nv_w) + (e >> 16);
   };
 
-  if (n >= (uint32_t)K && !overflow && n <= (uint32_t)kCandMax) {
-    // this thread's contiguous slice of the list and its keys (re-read from
-    // the teacher row: a few entries per thread)
-    constexpr int kPer = kCandMax / kKT;
+  // the sampled selection with kPer list entries per thread (8 when the list
+  // fits, else 16)
+  auto fast = [&](auto kper_tag) {
+    constexpr int kPer = decltype(kper_tag)::value;
+    // this thread's contiguous slice of the list and its keys (packed in the
+    // list, else re-read from the teacher row: a few entries per thread)
     const uint32_t per = (n + kKT - 1) / kKT;
     const uint32_t c0 = min(n, (uint32_t)t * per), c1 = min(n, c0 + per);
     const uint16_t *trow16 = teacher + row * (size_t)V;
     uint32_t ci[kPer], ck[kPer];
 #pragma unroll
-    for (int u = 0; u < kPer; ++u) ci[u] = (c0 + u < c1) ? list_at(c0 + u) : 0u;
+    for (int u = 0; u < kPer; ++u) ci[u] = (c0 + u < c1) ? list_at(c0 + u, ck[u]) : 0u;
+    if (!packed) {
 #pragma unroll
-    for (int u = 0; u < kPer; ++u) ck[u] = trow16[ci[u]];
+      for (int u = 0; u < kPer; ++u) ck[u] = trow16[ci[u]];
 #pragma unroll
-    for (int u = 0; u < kPer; ++u) ck[u] = (c0 + u < c1) ? order_key(ck[u]) : 0u;
+      for (int u = 0; u < kPer; ++u) ck[u] = order_key(ck[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) ck[u] = (c0 + u < c1) ? ck[u] : 0u;
     // the K-th largest key among the list (every key >= it is listed: the
     // list holds all keys >= L, at least K of them): a count per key value
     // from L up (the list is in registers now, its memory is free)
@@ -605,6 +629,10 @@ __global__ __launch_bounds__(kKT) __attribute__((amdgpu_waves_per_eu(KM <= 1024 
         xs.sel.tv[p] = bf16_to_f32(raw_of_key(ck[u]));
         ++p;
       }
+  };
+  if (n >= (uint32_t)K && !overflow && n <= (uint32_t)kCandMax) {
+    if (n <= 8u * kKT) fast(std::integral_constant<int, 8>{});
+    else fast(std::integral_constant<int, kCandMax / kKT>{});
   } else {
     select_hist(sh, xs, trow, nvec, K);
   }

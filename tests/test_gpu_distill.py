@@ -73,8 +73,11 @@ def _ties(rng, T, V, step):
 
 @pytest.mark.parametrize("reverse", [False, True])
 @pytest.mark.parametrize("K,V,step", [(100, 8000, 0.25), (1, 4096, 0.5), (4096, 8 * 1031, 0.0),
-                                      (512, 512, 0.125), (777, 20008, 1.0)])
+                                      (512, 512, 0.125), (777, 20008, 1.0),
+                                      (1024, 8 * 751, 0.25), (1025, 8 * 751, 0.25)])
 def test_topk_kl_parity(K, V, step, reverse):
+    """K = 1024 and 1025 sit either side of the smaller selection-storage
+    instance of the kernel."""
     print(f"[kd] K={K} V={V} step={step} reverse={reverse}", flush=True)
     rng = np.random.default_rng(K + V)
     T = 37

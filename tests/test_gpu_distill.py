@@ -128,6 +128,19 @@ def test_topk_kl_negative_and_positive_bounds(reverse):
     _check(s, t, K, reverse, None, got)
 
 
+def test_topk_kl_long_rows():
+    """Rows longer than 8 x 65536 entries: the candidate list holds plain
+    vocabulary indices (a wave's stretch of the row no longer fits the packed
+    16-bit index) and the keys are read again from the teacher row."""
+    print("[kd] long rows", flush=True)
+    rng = np.random.default_rng(5)
+    T, V, K = 3, 8 * 65600, 1000
+    t = _ties(rng, T, V, 0.0)
+    s = O.f32_to_bf16((O.bf16_to_f32(t) + rng.standard_normal((T, V)) * 0.3).astype(np.float32))
+    got = _run(s, t, K, False)
+    _check(s, t, K, False, None, got)
+
+
 @pytest.mark.parametrize("reverse", [False, True])
 def test_topk_kl_histogram_path(reverse):
     """Rows whose sampled bracket admits more candidates than LDS holds (long

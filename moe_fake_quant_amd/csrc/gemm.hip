@@ -621,23 +621,46 @@ __device__ __forceinline__ void run_tile(const GemmArgs &a, const int *tile_star
   // accumulator (s, u, v) of this lane: i = i0 + wi*128 + s*32 + 8*(v/4) + 4*(lane/32) + v%4,
   //                                     j = j0 + wj*64 + u*32 + lane%32
   if (MODE != WGRAD) {
-    prefetch_next();
+    // The bf16 tile goes out through LDS: each wave writes its 128 (i) x 32 (j)
+    // half-slab row by row into ring buffer 1 (free until the next tile's
+    // second stage; waves 0-3 in the P half, 4-7 in the Q half, 8 KiB each),
+    // then stores whole 256-byte row segments, 16 bytes per lane. Direct
+    // stores from the accumulator layout would write each 128-byte line in
+    // 16-byte pieces from eight instructions. Row r of the slab is 16 chunks
+    // of 16 bytes; chunk c sits at c ^ (r & 15), so the lanes of a write (32
+    // rows, one chunk) and of a read (one row per 16 lanes) spread over the
+    // banks.
+    if (next_w >= 0) prefetch_next();  // (its barrier also retires buffer 1)
+    else block_barrier();
     const int ldo = (MODE == FWD) ? a.N : a.K;
+    char *slab = (wave < 4 ? stage_p<1>() : stage_q<1>()) + (wave & 3) * 8192;
+    // lane terms formed here (an empty asm keeps the compiler from hoisting
+    // the addresses derived from them into the contraction loop's registers)
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    const int h = ln >> 5, jr = ln & 31;
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-      const int j = j0 + wj * WJ_TILE + u * 32 + (lane & 31);
-      if (j >= j_end) continue;
-      uint16_t *orow = a.out + (size_t)j * ldo;
+      if (!live) break;
 #pragma unroll
       for (int s = 0; s < 4; ++s)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const int i = i0 + wi * 128 + s * 32 + 8 * q + 4 * (lane >> 5);
           uint2 pk;
           pk.x = pack_bf16(acc[s][u][4 * q + 0], acc[s][u][4 * q + 1]);
           pk.y = pack_bf16(acc[s][u][4 * q + 2], acc[s][u][4 * q + 3]);
-          *reinterpret_cast<uint2 *>(orow + i) = pk;
+          const uint32_t c = (uint32_t)(4 * s + q) ^ (uint32_t)(jr & 15);
+          *reinterpret_cast<uint2 *>(slab + jr * 256 + c * 16 + h * 8) = pk;
         }
+      const int jb = j0 + wj * WJ_TILE + u * 32;
+      uint16_t *obase = a.out + (size_t)i0 + wi * 128 + (ln & 15) * 8;
+#pragma unroll
+      for (int it = 0; it < 8; ++it) {
+        const int r = 4 * it + (ln >> 4);
+        const uint4 v = *reinterpret_cast<const uint4 *>(
+            slab + r * 256 + (((uint32_t)(ln & 15) ^ (uint32_t)(r & 15)) << 4));
+        if (jb + r < j_end) *reinterpret_cast<uint4 *>(obase + (size_t)(jb + r) * ldo) = v;
+      }
     }
     return;
   }

@@ -267,6 +267,7 @@ __device__ __forceinline__ void wgrad_epilogue(const GemmArgs &a, const f32x16 (
     }
   }
   float part_s[4], part_z[4];
+  float o16[8], z16[8];  // group 16: the eight block sums of this lane's row
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
     float ps16[2], pz16[2];  // the sub-tile's two 16-blocks
@@ -299,17 +300,33 @@ __device__ __forceinline__ void wgrad_epilogue(const GemmArgs &a, const f32x16 (
       ps16[b2] += __shfl_xor(ps16[b2], 32, 64);
       if (WFMT == FQ_FMT_INT4) pz16[b2] += __shfl_xor(pz16[b2], 32, 64);
     }
-    if (a.group == 16 && lane < 32) {
-      const int kb = (k0 + s * 32) / 16;
-      ds_out[orow + kb] = ps16[0];
-      ds_out[orow + kb + 1] = ps16[1];
-      if (WFMT == FQ_FMT_INT4 && dz_out) {
-        dz_out[orow + kb] = pz16[0];
-        dz_out[orow + kb + 1] = pz16[1];
-      }
-    }
+    o16[2 * s] = ps16[0];
+    o16[2 * s + 1] = ps16[1];
+    z16[2 * s] = pz16[0];
+    z16[2 * s + 1] = pz16[1];
     part_s[s] = ps16[0] + ps16[1];
     part_z[s] = pz16[0] + pz16[1];
+  }
+  if (a.group == 16) {
+    // both lane halves hold the row's eight sums: half h stores blocks
+    // 4h .. 4h+3 as one 16-byte store (the 32 rows x 32 bytes in one
+    // instruction instead of eight 4-byte ones)
+    const int h = lane >> 5;
+    const size_t o = orow + k0 / 16 + 4 * h;
+    float4 v;
+    v.x = h ? o16[4] : o16[0];
+    v.y = h ? o16[5] : o16[1];
+    v.z = h ? o16[6] : o16[2];
+    v.w = h ? o16[7] : o16[3];
+    *reinterpret_cast<float4 *>(ds_out + o) = v;
+    if (WFMT == FQ_FMT_INT4 && dz_out) {
+      float4 z;
+      z.x = h ? z16[4] : z16[0];
+      z.y = h ? z16[5] : z16[1];
+      z.z = h ? z16[6] : z16[2];
+      z.w = h ? z16[7] : z16[3];
+      *reinterpret_cast<float4 *>(dz_out + o) = z;
+    }
   }
   if (lane < 32 && a.group != 16) {
     if (a.group == 32) {

@@ -114,6 +114,10 @@ __device__ __forceinline__ void dma16(const char *base, uint32_t off, char *lds_
 // for every outstanding load, draining the ring).
 __device__ __forceinline__ void block_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
+// s_waitcnt lgkmcnt(0) leaving the other counters alone (gfx9 encoding): this
+// wave's LDS reads have returned
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
 // s_waitcnt vmcnt(n) leaving the other counters alone (gfx9 encoding)
 template <int N>
 __device__ __forceinline__ void wait_vm() {
@@ -197,16 +201,30 @@ __device__ __forceinline__ int expert_of_tile(const int *tile_start, int E, int 
 // acc[s][U][4q + v]. Each dWq element is weighted by its straight-through
 // factor and summed over its quantization group in a fixed order.
 // this lane's raw weights of the slab: k = k0 + 32s + 8q + 4h + v
-__device__ __forceinline__ void wgrad_load_w(const GemmArgs &a, int e, int k0, int n0, int lane,
-                                             uint2 (&wv)[4][4]) {
-  const int n = n0 + (lane & 31);
-  const int h = lane >> 5;
-  const uint16_t *wrow = a.w + ((size_t)e * a.N + n) * a.K;
+// The raw weights of the slab rows n0 .. n0+31, k0 .. k0+127 (32 x 256 bytes)
+// into this wave's 8 KiB of LDS with whole-row DMA, row r at byte 256 r, its
+// 16-byte chunk c at position c ^ (r & 15) (the reads below, 32 rows at one
+// chunk, then spread over the banks).
+__device__ __forceinline__ void wgrad_dma_w(const GemmArgs &a, int e, int k0, int n0, int lane,
+                                            char *slab) {
+  const char *wbase = reinterpret_cast<const char *>(a.w + ((size_t)e * a.N + n0) * a.K + k0);
+#pragma unroll
+  for (int ii = 0; ii < 8; ++ii) {
+    const uint32_t r = 4u * ii + (uint32_t)(lane >> 4);
+    const uint32_t c = (uint32_t)(lane & 15) ^ (r & 15u);
+    dma16(wbase, (r * (uint32_t)a.K + c * 8u) * 2u, slab + ii * 1024);
+  }
+}
+// this lane's raw weights of the slab: k = k0 + 32s + 8q + 4h + v, n = n0 + lane%32
+__device__ __forceinline__ void wgrad_read_w(const char *slab, int lane, uint2 (&wv)[4][4]) {
+  const uint32_t jr = lane & 31, h = lane >> 5;
 #pragma unroll
   for (int s = 0; s < 4; ++s)
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
-      wv[s][q] = *reinterpret_cast<const uint2 *>(wrow + k0 + s * 32 + 8 * q + 4 * h);
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t c = (uint32_t)(4 * s + q) ^ (jr & 15u);
+      wv[s][q] = *reinterpret_cast<const uint2 *>(slab + jr * 256 + (c << 4) + h * 8);
+    }
 }
 // `chunk` < 0: this tile's dScale sums are final and go to dscale / dzp;
 // otherwise they are partials of row chunk `chunk` (blocks of min(group, 128)).
@@ -532,13 +550,20 @@ __device__ __forceinline__ void run_tile(const GemmArgs &a, const int *tile_star
     constexpr int S = decltype(stage_tag)::value;
     ld.template issue<S>(a, kt, wave);
   };
-  // stage 0 of the next tile, after every wave has left this tile's buffers
+  // stage 0 of the next tile into buffer 0 (every wave must have left this
+  // tile's buffers); true if its eight DMA instructions were issued
+  auto prefetch_issue = [&]() {
+    if (next_w < 0) return false;
+    const Tile nt = decode_tile<MODE>(a, tile_start, next_w);
+    const TileLoads<MODE> nl(a, nt, wave, lane);
+    if (nl.nk <= 0) return false;
+    nl.template issue<0>(a, 0, wave);
+    return true;
+  };
   auto prefetch_next = [&]() {
     if (next_w < 0) return;
     block_barrier();
-    const Tile nt = decode_tile<MODE>(a, tile_start, next_w);
-    const TileLoads<MODE> nl(a, nt, wave, lane);
-    if (nl.nk > 0) nl.template issue<0>(a, 0, wave);
+    prefetch_issue();
   };
 
   f32x16 acc[4][2];
@@ -684,12 +709,24 @@ __device__ __forceinline__ void run_tile(const GemmArgs &a, const int *tile_star
 
   // ---- WGRAD epilogue: i = k, j = n of expert e. dS over groups along k.
   {
+    // The raw weights come in through ring buffer 1 (free once every wave has
+    // left the contraction loop, until the next tile's second stage), each
+    // wave's two 32-row slabs one after the other in its own 8 KiB: whole-row
+    // DMA instead of 8-byte loads from 32 rows per instruction. Only the wave
+    // itself reads its slab, so its own waits order the accesses.
     const int k0 = i0 + wi * 128, n0 = j0 + wj * WJ_TILE;
+    char *slab = (wave < 4 ? stage_p<1>() : stage_q<1>()) + (wave & 3) * 8192;
     uint2 wv[4][4];
-    wgrad_load_w(a, e, k0, n0, lane, wv);  // issued before the prefetch: its waits stay short
-    prefetch_next();
+    block_barrier();
+    wgrad_dma_w(a, e, k0, n0, lane, slab);
+    if (prefetch_issue()) wait_vm<8>();  // the slab, not the next tile's stage 0
+    else wait_vm<0>();
+    wgrad_read_w(slab, lane, wv);
+    wait_lgkm0();                          // read back before the slab is reused
+    wgrad_dma_w(a, e, k0, n0 + 32, lane, slab);
     wgrad_epilogue<WFMT, 0>(a, acc, e, k0, n0, lane, wv, tl.chunk);
-    wgrad_load_w(a, e, k0, n0 + 32, lane, wv);
+    wait_vm<0>();
+    wgrad_read_w(slab, lane, wv);
     wgrad_epilogue<WFMT, 1>(a, acc, e, k0, n0 + 32, lane, wv, tl.chunk);
   }
 }

@@ -317,7 +317,7 @@ fq_status fq_grouped_gemm_bwd_scale(const uint16_t *dy_bf16, const uint16_t *x_b
  * fq_moe_combine_bwd: do[row_of[t,j]] = bf16(p[t,j] * dout[t]) for every
  *   routed slot; each dout row is read once.
  * fq_moe_unpermute_reduce: dx[t] = bf16(m_a(x[t]) * sum_j dxq[row_of[t,j]]).
- * All require H (resp. F) % 16 == 0 and T * H (resp. R_max * F) < 2^36.
+ * All require H (resp. F) % 16 == 0 and T * H (resp. R_max * F) < 2^35.
  * T == 0 launches nothing (the token pointers may then be NULL).
  *
  * Learnable activation scale (fq_swiglu_bwd, fq_moe_unpermute_reduce): the

@@ -421,7 +421,7 @@ fq_status fq_moe_gather_actfq(const uint16_t *x, int32_t T, int32_t H, const int
   FQ_CHECK_ARG(H % 16 == 0, "H must be a multiple of 16");
   FQ_CHECK_ARG(T == 0 || (x && row_of && xq), "NULL pointer");
   FQ_CHECK_ARG((!x || aligned16(x)) && (!xq || aligned16(xq)), "bf16 tensors must be 16-byte aligned");
-  FQ_CHECK_ARG((long)T * H < (1l << 36), "too many elements");
+  FQ_CHECK_ARG((long)T * H < (1l << 35), "too many elements");
   FQ_TRY(check_act_q(aq, H));
   launch_gather_actfq(x, T, H, row_of, topk, act_fmt(aq), aq ? aq->scale : nullptr, xq, S(stream));
   FQ_CHECK_LAUNCH("fq_moe_gather_actfq");
@@ -431,6 +431,7 @@ fq_status fq_moe_gather_actfq(const uint16_t *x, int32_t T, int32_t H, const int
 fq_status fq_swiglu_actfq(const uint16_t *h, int32_t R_max, const int32_t *n_rows, int32_t F,
                           const fq_act_q *aq, uint16_t *a, uint16_t *aqo, fq_stream stream) {
   FQ_CHECK_ARG(R_max >= 0 && F > 0 && F % 16 == 0, "bad sizes (F must be a multiple of 16)");
+  FQ_CHECK_ARG((long)R_max * F < (1l << 35), "too many elements");
   FQ_CHECK_ARG(n_rows && (R_max == 0 || (h && aqo)), "NULL pointer");
   FQ_CHECK_ARG((!h || aligned16(h)) && (!a || aligned16(a)) && (!aqo || aligned16(aqo)),
                "bf16 tensors must be 16-byte aligned");
@@ -444,7 +445,7 @@ fq_status fq_swiglu_bwd(const uint16_t *daq, const uint16_t *h, int32_t R_max, c
                         int32_t F, const fq_act_q *aq, uint16_t *dh, float *dscale_a, void *ws,
                         size_t ws_bytes, fq_stream stream) {
   FQ_CHECK_ARG(R_max >= 0 && F > 0 && F % 16 == 0, "bad sizes (F must be a multiple of 16)");
-  FQ_CHECK_ARG((long)R_max * F < (1l << 36), "too many elements");
+  FQ_CHECK_ARG((long)R_max * F < (1l << 35), "too many elements");
   FQ_CHECK_ARG(n_rows && (R_max == 0 || (h && daq && dh)), "NULL pointer");
   FQ_CHECK_ARG((!h || aligned16(h)) && (!daq || aligned16(daq)) && (!dh || aligned16(dh)),
                "bf16 tensors must be 16-byte aligned");
@@ -459,7 +460,7 @@ fq_status fq_swiglu_bwd(const uint16_t *daq, const uint16_t *h, int32_t R_max, c
 fq_status fq_moe_combine(const uint16_t *o, const float *probs, const int32_t *row_of, int32_t T,
                          int32_t topk, int32_t H, uint16_t *out, fq_stream stream) {
   FQ_CHECK_ARG(T >= 0 && topk > 0 && H > 0 && H % 16 == 0, "bad sizes (H must be a multiple of 16)");
-  FQ_CHECK_ARG((long)T * H < (1l << 36), "too many elements");
+  FQ_CHECK_ARG((long)T * H < (1l << 35), "too many elements");
   FQ_CHECK_ARG(T == 0 || (o && probs && row_of && out), "NULL pointer");
   FQ_CHECK_ARG((!o || aligned16(o)) && (!out || aligned16(out)), "bf16 tensors must be 16-byte aligned");
   launch_combine(o, probs, row_of, T, topk, H, out, S(stream));
@@ -470,7 +471,7 @@ fq_status fq_moe_combine(const uint16_t *o, const float *probs, const int32_t *r
 fq_status fq_moe_combine_bwd(const uint16_t *dout, const float *probs, const int32_t *row_of,
                              int32_t T, int32_t topk, int32_t H, uint16_t *dO, fq_stream stream) {
   FQ_CHECK_ARG(T >= 0 && topk > 0 && H > 0 && H % 16 == 0, "bad sizes (H must be a multiple of 16)");
-  FQ_CHECK_ARG((long)T * H < (1l << 36), "too many elements");
+  FQ_CHECK_ARG((long)T * H < (1l << 35), "too many elements");
   FQ_CHECK_ARG(T == 0 || (dout && probs && row_of && dO), "NULL pointer");
   FQ_CHECK_ARG((!dout || aligned16(dout)) && (!dO || aligned16(dO)),
                "bf16 tensors must be 16-byte aligned");
@@ -484,7 +485,7 @@ fq_status fq_moe_unpermute_reduce(const uint16_t *dxq, const int32_t *row_of, co
                                   uint16_t *dx, float *dscale_a, void *ws, size_t ws_bytes,
                                   fq_stream stream) {
   FQ_CHECK_ARG(T >= 0 && topk > 0 && H > 0 && H % 16 == 0, "bad sizes (H must be a multiple of 16)");
-  FQ_CHECK_ARG((long)T * H < (1l << 36), "too many elements");
+  FQ_CHECK_ARG((long)T * H < (1l << 35), "too many elements");
   FQ_CHECK_ARG(T == 0 || (dxq && row_of && dx), "NULL pointer");
   FQ_TRY(check_act_q(aq, H));
   FQ_CHECK_ARG(act_fmt(aq) == FQ_FMT_NONE || T == 0 || x, "x is NULL");

@@ -353,6 +353,51 @@ __device__ __forceinline__ uint32_t act_fq16(const ActQ &q, float *x) {
   return mask;
 }
 
+// 8 consecutive elements along K, one half of a 16-element block; the other
+// half is on lane ^ 1, which must run the same call (NVFP4 takes the block
+// amax over both halves, so the result equals act_fq16 on the whole block).
+// Values in place, 8 mask bits out.
+__device__ __forceinline__ uint32_t act_fq8_pair(const ActQ &q, float *x) {
+  uint32_t mask = 0;
+  if (q.fmt == FQ_FMT_NONE) return 0xFFu;
+  if (q.fmt == FQ_FMT_NVFP4 || q.fmt == FQ_FMT_FP8_E4M3) {
+    float s = q.s, r = q.r;
+    const float mx = q.fmt == FQ_FMT_NVFP4 ? kE2M1Max : kE4M3Max;
+    if (q.fmt == FQ_FMT_NVFP4) {
+      float amax = 0.0f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(x[j]));
+      amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
+      s = nvfp4_dynamic_scale(amax, q.s);
+      if (s == 0.0f) {  // zero block: +0.0, mask 0
+#pragma unroll
+        for (int j = 0; j < 8; ++j) x[j] = 0.0f;
+        return 0u;
+      }
+      r = 1.0f / s;
+    }
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const float z0 = x[2 * p] * r, z1 = x[2 * p + 1] * r;
+      float v0, v1;
+      if (q.fmt == FQ_FMT_NVFP4) e2m1_pair(z0, z1, v0, v1);
+      else e4m3_pair(clamp448(z0), clamp448(z1), v0, v1);
+      mask |= (uint32_t)(fabsf(z0) <= mx) << (2 * p);
+      mask |= (uint32_t)(fabsf(z1) <= mx) << (2 * p + 1);
+      x[2 * p] = v0 * s;
+      x[2 * p + 1] = v1 * s;
+    }
+    return mask;
+  }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    FQElem e = fq_int8(x[j], q.s, q.r);
+    x[j] = e.v;
+    mask |= (uint32_t)e.m << j;
+  }
+  return mask;
+}
+
 __device__ __forceinline__ void load16(const bf16x8_t *p, float *x) {
   bf16x8_t a = p[0], b = p[1];
   unpack8(a, x);
@@ -479,22 +524,27 @@ __global__ __launch_bounds__(kThreads) void k_act_mask(bf16x8_t *__restrict__ dx
 
 // xq[r] = FQ_a(x[perm[r] / topk]) for r < n_rows[0]
 // Per token: x[t] is read and fake-quantized once, then stored to each of its
-// routed rows xq[row_of[t, j]] (j ascending; -1 = not routed here).
+// routed rows xq[row_of[t, j]] (j ascending; -1 = not routed here). One
+// 16-byte vector per lane, so every store instruction of a wave covers 1 KiB
+// of one routed row (32-byte pieces per lane scatter ~9 % slower); a 16-block
+// spans the lane pair (2m, 2m + 1). The grid stride and the vector count are
+// even, so both lanes of a pair run every iteration together.
 __global__ __launch_bounds__(kThreads) void k_gather_actfq(
     const bf16x8_t *__restrict__ x, const int32_t *__restrict__ row_of, int topk,
-    FastDiv chunks_per_row, uint32_t nchunk, int afmt, const float *__restrict__ ascale,
+    FastDiv vec_per_row, uint32_t nvec, int afmt, const float *__restrict__ ascale,
     bf16x8_t *__restrict__ xq) {
   ActQ q = load_actq(afmt, ascale);
-  const uint32_t cpr = chunks_per_row.d;
-  for (uint32_t c = blockIdx.x * blockDim.x + threadIdx.x; c < nchunk; c += gridDim.x * blockDim.x) {
-    const uint32_t t = chunks_per_row.div(c);
-    const uint32_t cc = c - t * cpr;
-    float f[16];
-    load16(x + 2 * (size_t)c, f);
-    act_fq16(q, f);
+  const uint32_t vpr = vec_per_row.d;
+  for (uint32_t c = blockIdx.x * blockDim.x + threadIdx.x; c < nvec; c += gridDim.x * blockDim.x) {
+    const uint32_t t = vec_per_row.div(c);
+    const uint32_t cc = c - t * vpr;
+    float f[8];
+    unpack8(x[c], f);
+    act_fq8_pair(q, f);
+    const bf16x8_t v = pack8(f);
     for (int j = 0; j < topk; ++j) {
       const int r = row_of[t * topk + j];
-      if (r >= 0) store16(xq + 2 * ((size_t)r * cpr + cc), f);
+      if (r >= 0) xq[(size_t)r * vpr + cc] = v;
     }
   }
 }
@@ -515,25 +565,29 @@ __device__ __forceinline__ void swiglu16(const float *g, const float *u, float *
   }
 }
 
-// h [R, 2F] -> a [R, F] (optional), aq [R, F]
+// h [R, 2F] -> a [R, F] (optional), aq [R, F]. One 16-byte vector of each
+// output per lane (1 KiB per wave store); a 16-block spans a lane pair, as in
+// the gather.
 __global__ __launch_bounds__(kThreads) void k_swiglu_actfq(
-    const bf16x8_t *__restrict__ h, FastDiv chunks_per_row, uint32_t max_chunks,
+    const bf16x8_t *__restrict__ h, FastDiv vec_per_row, uint32_t max_vec,
     const int32_t *__restrict__ n_rows, int afmt, const float *__restrict__ ascale,
     bf16x8_t *__restrict__ a_out, bf16x8_t *__restrict__ aq_out) {
   ActQ q = load_actq(afmt, ascale);
-  const uint32_t cpr = chunks_per_row.d;  // F / 16
-  const uint32_t nchunk = min((uint32_t)n_rows[0] * cpr, max_chunks);
-  for (uint32_t c = blockIdx.x * blockDim.x + threadIdx.x; c < nchunk; c += gridDim.x * blockDim.x) {
-    uint32_t r = chunks_per_row.div(c);
-    uint32_t cc = c - r * cpr;
-    const bf16x8_t *hr = h + 2 * ((size_t)r * 2 * cpr);
-    float g[16], u[16], a[16], sg[16];
-    load16(hr + 2 * cc, g);
-    load16(hr + 2 * (cpr + cc), u);
-    swiglu16(g, u, a, sg);
-    if (a_out) store16(a_out + 2 * (size_t)c, a);
-    act_fq16(q, a);
-    store16(aq_out + 2 * (size_t)c, a);
+  const uint32_t vpr = vec_per_row.d;  // F / 8
+  const uint32_t nvec = min((uint32_t)n_rows[0] * vpr, max_vec);
+  for (uint32_t c = blockIdx.x * blockDim.x + threadIdx.x; c < nvec; c += gridDim.x * blockDim.x) {
+    const uint32_t r = vec_per_row.div(c);
+    const uint32_t cc = c - r * vpr;
+    const bf16x8_t *hr = h + (size_t)r * 2 * vpr;
+    float g[8], u[8], a[8];
+    unpack8(hr[cc], g);
+    unpack8(hr[vpr + cc], u);
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      a[j] = bf16_to_f32(f32_to_bf16((g[j] * sigmoid_hw(g[j])) * u[j]));
+    if (a_out) a_out[c] = pack8(a);
+    act_fq8_pair(q, a);
+    aq_out[c] = pack8(a);
   }
 }
 
@@ -613,25 +667,26 @@ __global__ __launch_bounds__(kThreads) void k_combine(const bf16x8_t *__restrict
 
 // do[r] = bf16(p[t,j] * dout[t]), f = perm[r]
 // Per token: dout[t] is read once and dO[row_of[t, j]] = bf16(p[t,j] * dout[t])
-// stored for each routed slot j.
+// stored for each routed slot j; one 16-byte vector per lane (1 KiB of one
+// routed row per wave store).
 __global__ __launch_bounds__(kThreads) void k_combine_bwd(
     const bf16x8_t *__restrict__ dout, const float *__restrict__ probs,
-    const int32_t *__restrict__ row_of, int topk, FastDiv chunks_per_row, uint32_t nchunk,
+    const int32_t *__restrict__ row_of, int topk, FastDiv vec_per_row, uint32_t nvec,
     bf16x8_t *__restrict__ dO) {
-  const uint32_t cpr = chunks_per_row.d;
-  for (uint32_t c = blockIdx.x * blockDim.x + threadIdx.x; c < nchunk; c += gridDim.x * blockDim.x) {
-    const uint32_t t = chunks_per_row.div(c);
-    const uint32_t cc = c - t * cpr;
-    float d[16];
-    load16(dout + 2 * (size_t)c, d);
+  const uint32_t vpr = vec_per_row.d;
+  for (uint32_t c = blockIdx.x * blockDim.x + threadIdx.x; c < nvec; c += gridDim.x * blockDim.x) {
+    const uint32_t t = vec_per_row.div(c);
+    const uint32_t cc = c - t * vpr;
+    float d[8];
+    unpack8(dout[c], d);
     for (int j = 0; j < topk; ++j) {
       const int r = row_of[t * topk + j];
       if (r < 0) continue;
       const float p = probs[t * topk + j];
-      float o[16];
+      float o[8];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) o[i] = p * d[i];
-      store16(dO + 2 * ((size_t)r * cpr + cc), o);
+      for (int i = 0; i < 8; ++i) o[i] = p * d[i];
+      dO[(size_t)r * vpr + cc] = pack8(o);
     }
   }
 }
@@ -796,19 +851,19 @@ void launch_act_mask(uint16_t *dx, const uint16_t *x, size_t M, int K, const int
 
 void launch_gather_actfq(const uint16_t *x, int T, int H, const int32_t *row_of, int topk,
                          int afmt, const float *ascale, uint16_t *xq, hipStream_t st) {
-  const uint32_t nchunk = (uint32_t)((size_t)T * H / 16);
-  if (!nchunk) return;
-  hipLaunchKernelGGL(k_gather_actfq, dim3(grid_for(nchunk)), dim3(kThreads), 0, st,
-                     reinterpret_cast<const bf16x8_t *>(x), row_of, topk, FastDiv(H / 16), nchunk,
+  const uint32_t nvec = (uint32_t)((size_t)T * H / 8);
+  if (!nvec) return;
+  hipLaunchKernelGGL(k_gather_actfq, dim3(grid_for(nvec)), dim3(kThreads), 0, st,
+                     reinterpret_cast<const bf16x8_t *>(x), row_of, topk, FastDiv(H / 8), nvec,
                      afmt, ascale, reinterpret_cast<bf16x8_t *>(xq));
 }
 
 void launch_swiglu_actfq(const uint16_t *h, int R_max, const int32_t *n_rows, int F, int afmt,
                          const float *ascale, uint16_t *a, uint16_t *aq, hipStream_t st) {
-  uint32_t maxc = (uint32_t)((size_t)R_max * F / 16);
-  if (!maxc) return;
-  hipLaunchKernelGGL(k_swiglu_actfq, dim3(grid_for(maxc)), dim3(kThreads), 0, st,
-                     reinterpret_cast<const bf16x8_t *>(h), FastDiv(F / 16), maxc, n_rows, afmt, ascale,
+  const uint32_t maxv = (uint32_t)((size_t)R_max * F / 8);
+  if (!maxv) return;
+  hipLaunchKernelGGL(k_swiglu_actfq, dim3(grid_for(maxv)), dim3(kThreads), 0, st,
+                     reinterpret_cast<const bf16x8_t *>(h), FastDiv(F / 8), maxv, n_rows, afmt, ascale,
                      reinterpret_cast<bf16x8_t *>(a), reinterpret_cast<bf16x8_t *>(aq));
 }
 
@@ -846,11 +901,11 @@ void launch_combine(const uint16_t *o, const float *probs, const int32_t *row_of
 
 void launch_combine_bwd(const uint16_t *dout, const float *probs, const int32_t *row_of, int T,
                         int topk, int H, uint16_t *dO, hipStream_t st) {
-  const uint32_t nchunk = (uint32_t)((size_t)T * H / 16);
-  if (!nchunk) return;
-  hipLaunchKernelGGL(k_combine_bwd, dim3(grid_for(nchunk)), dim3(kThreads), 0, st,
-                     reinterpret_cast<const bf16x8_t *>(dout), probs, row_of, topk, FastDiv(H / 16),
-                     nchunk, reinterpret_cast<bf16x8_t *>(dO));
+  const uint32_t nvec = (uint32_t)((size_t)T * H / 8);
+  if (!nvec) return;
+  hipLaunchKernelGGL(k_combine_bwd, dim3(grid_for(nvec)), dim3(kThreads), 0, st,
+                     reinterpret_cast<const bf16x8_t *>(dout), probs, row_of, topk, FastDiv(H / 8),
+                     nvec, reinterpret_cast<bf16x8_t *>(dO));
 }
 
 void launch_unpermute_reduce(const uint16_t *dxq, const int32_t *row_of, const uint16_t *x, int T,

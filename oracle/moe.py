@@ -44,7 +44,9 @@ def gather_actfq(x_bits, perm, topk: int, afmt: int, act_scale):
 
 
 def _sigmoid(g):
-    return 1.0 / (1.0 + np.exp(-g))
+    # exp(-g) overflows to inf for g below about -709, and 1 / inf = 0 is the limit
+    with np.errstate(over="ignore"):
+        return 1.0 / (1.0 + np.exp(-g))
 
 
 def swiglu_fwd(h_bits):

@@ -134,3 +134,74 @@ def test_learnable_act_scales_with_zero_tokens():
     L.step(x[:0], ids[:0], dev_f32(case.probs)[:0], dev_bf16(case.dout)[:0])
     torch.cuda.synchronize()
     assert float(L.ds_a1.cpu()[0]) == 0.0 and float(L.ds_a2.cpu()[0]) == 0.0
+
+
+def _block_pattern_rows(rng, rows, cols):
+    """bf16 rows whose 16-blocks take one of: all zero, one nonzero element in
+    the first half, one in the second half, random normal, all equal, tiny
+    (subnormal-range) values, or a wide spread of magnitudes."""
+    x = np.zeros((rows, cols), np.float32)
+    for r in range(rows):
+        for b in range(cols // 16):
+            kind = rng.integers(0, 7)
+            blk = np.zeros(16, np.float32)
+            if kind == 1:
+                blk[rng.integers(0, 8)] = rng.standard_normal() * 3
+            elif kind == 2:
+                blk[8 + rng.integers(0, 8)] = rng.standard_normal() * 3
+            elif kind == 3:
+                blk = rng.standard_normal(16).astype(np.float32)
+            elif kind == 4:
+                blk[:] = rng.choice([-1.5, 0.75, 2.0])
+            elif kind == 5:
+                blk = (rng.standard_normal(16) * 1e-38).astype(np.float32)
+            elif kind == 6:
+                blk = (rng.standard_normal(16) * 10.0 ** rng.integers(-3, 4, 16)).astype(np.float32)
+            x[r, 16 * b:16 * b + 16] = blk
+    return O.f32_to_bf16(x)
+
+
+@pytest.mark.parametrize("afmt", [O.FMT_NVFP4, O.FMT_FP8, O.FMT_INT8, O.FMT_NONE])
+@pytest.mark.parametrize("scale_mul", [1.0, 0.25])
+def test_gather_and_swiglu_act_fq_block_halves(afmt, scale_mul):
+    """The gather and SwiGLU-forward kernels hold one 16-byte vector per lane,
+    so an NVFP4 16-block spans two lanes: blocks that are zero, whose amax sits
+    in either half, ties, tiny and wide-range values, an odd token count, and
+    slots not routed here; a quarter of the calibrated scale drives blocks into
+    the E4M3 clamp. Bit-exact against the oracle."""
+    print(f"[edge] block halves afmt={afmt} scale_mul={scale_mul}", flush=True)
+    rng = np.random.default_rng(77)
+    T, H, k, F2 = 37, 64, 3, 64
+    x = _block_pattern_rows(rng, T, H)
+    routed = rng.random((T, k)) < 0.8
+    R = int(routed.sum())
+    row_of = np.full((T, k), -1, np.int32)
+    row_of[routed] = rng.permutation(R).astype(np.int32)
+    perm = np.zeros(R, np.int64)
+    for t in range(T):
+        for j in range(k):
+            if row_of[t, j] >= 0:
+                perm[row_of[t, j]] = t * k + j
+    s1 = np.float32(O.observer_act(x, afmt) * np.float32(scale_mul)) if afmt else np.float32(1.0)
+    aq1 = F.ActQ(afmt, dev_f32([s1])) if afmt else None
+    xq = torch.zeros((R, H), dtype=torch.bfloat16, device="cuda")
+    F.fq_moe_gather_actfq(dev_bf16(x), T, H, dev_i32(row_of), k, aq1, xq)
+    torch.cuda.synchronize()
+    assert np.array_equal(host_bits(xq), O.gather_actfq(x, perm, k, afmt, s1).bits)
+
+    h = _block_pattern_rows(rng, R, F2)
+    Fh = F2 // 2
+    a_ref = O.swiglu_fwd(h)
+    s2 = np.float32(O.observer_act(a_ref, afmt) * np.float32(scale_mul)) if afmt else np.float32(1.0)
+    aq2 = F.ActQ(afmt, dev_f32([s2])) if afmt else None
+    a = torch.zeros((R + 5, Fh), dtype=torch.bfloat16, device="cuda")
+    aq = torch.zeros((R + 5, Fh), dtype=torch.bfloat16, device="cuda")
+    hd = torch.zeros((R + 5, F2), dtype=torch.bfloat16, device="cuda")
+    hd[:R] = dev_bf16(h)
+    F.fq_swiglu_actfq(hd, R + 5, dev_i32([R]), Fh, aq2, a, aq)
+    torch.cuda.synchronize()
+    a_gpu = host_bits(a)
+    check_gemm_tol(a_gpu[:R], a_ref, "a")
+    assert np.array_equal(host_bits(aq)[:R], O.fq_act(a_gpu[:R], afmt, s2).bits)
+    # rows past the device row count are never written
+    assert not host_bits(aq)[R:].any() and not a_gpu[R:].any()

@@ -371,9 +371,19 @@ __global__ __launch_bounds__(kKT) __attribute__((amdgpu_waves_per_eu(KM <= 1024 
     return s;
   };
 
-  // sample: one vector per thread, spread over the row
-  const uint32_t vs = nvec >= (uint32_t)kKT ? (uint32_t)(((unsigned long long)t * nvec) / kKT)
-                                            : (uint32_t)t;
+  // sample: one vector per thread. KM <= 1024: the eight threads of a group
+  // read one whole 128-byte line (8 consecutive vectors), the 64 lines spread
+  // over the row (a line starts at a multiple of 8 vectors, at most nvec -
+  // nvec / 64 <= nvec - 8 when nvec >= 512, so the group stays in the row);
+  // 4-5 % faster at K = 1000 than one scattered vector per thread. The larger
+  // selection (three rows per CU instead of four) keeps the scattered
+  // vectors (the line sample measured 6 % slower there): their lines are
+  // already cached when the stream reaches them.
+  const uint32_t vs =
+      nvec < (uint32_t)kKT ? (uint32_t)t
+      : KM <= 1024
+          ? ((uint32_t)(((unsigned long long)(t >> 3) * nvec) / (kKT / 8)) & ~7u) + (uint32_t)(t & 7)
+          : (uint32_t)(((unsigned long long)t * nvec) / kKT);
   const bool has_s = vs < nvec;
   uint32_t sk[8];
   {

@@ -4,8 +4,8 @@
 // [tokens, vocab] probabilities (AngelSlim mcore_qad article, section 二.5;
 // the forward / reverse top-K variants of the QAT + ZeRO-3 page's loss table).
 //
-// One workgroup per token row; the teacher row is streamed once. A strided
-// sample bounds the K-th largest logit from below; the stream keeps the
+// One workgroup per token row; the teacher row is streamed once. A sample
+// spread over the row bounds the K-th largest logit from below; the stream keeps the
 // (few) entries above that bound, in vocabulary order, and the exact K-th
 // largest, the ties (lower index first) and the selection come from them
 // (k_topk_kl). Rows where the bound fails are selected exactly by histograms
@@ -335,8 +335,8 @@ __device__ __forceinline__ uint32_t wave_count(bool f) {
   return (uint32_t)__popcll(__ballot(f));
 }
 
-// One token row per workgroup, the row streamed once. A strided sample of the
-// row (one 8-logit vector per thread) gives a key L a little below the
+// One token row per workgroup, the row streamed once. A sample spread over
+// the row (one 8-logit vector per thread) gives a key L a little below the
 // sample's share of the top K. The stream appends the vocabulary index of
 // every entry with key >= L to an LDS list in vocabulary order (a block-wide
 // prefix sum per step of 4 vectors per thread). When the list holds at least

@@ -213,6 +213,18 @@ def test_permute_and_elementwise_reject_bad_arguments(pkg):
         pkg.FQ_ERR_INVALID_ARGUMENT                                   # misaligned out
     assert L.fq_moe_combine_bwd(FAKE, FAKE, FAKE, 16, 0, 64, FAKE, None) == \
         pkg.FQ_ERR_INVALID_ARGUMENT                                   # topk 0
+    # 2^35 elements and more are refused before launch (32-bit vector counts
+    # of 8 elements inside the kernels)
+    big_t, h = (1 << 35) // 2048, 2048
+    assert L.fq_moe_gather_actfq(FAKE, big_t, h, FAKE, 8, None, FAKE, None) == \
+        pkg.FQ_ERR_INVALID_ARGUMENT
+    assert b"too many elements" in L.fq_last_error()
+    assert L.fq_swiglu_actfq(FAKE, big_t, FAKE, h, None, None, FAKE, None) == \
+        pkg.FQ_ERR_INVALID_ARGUMENT
+    assert b"too many elements" in L.fq_last_error()
+    assert L.fq_moe_combine_bwd(FAKE, FAKE, FAKE, big_t, 8, h, FAKE, None) == \
+        pkg.FQ_ERR_INVALID_ARGUMENT
+    assert b"too many elements" in L.fq_last_error()
     aq = ctypes.byref(pkg.fq_act_q(pkg.FMT_FP8_E4M3, FAKE))
     assert L.fq_moe_unpermute_reduce(FAKE, FAKE, None, 16, 8, 64, aq, FAKE, None, None, 0,
                                      None) == pkg.FQ_ERR_INVALID_ARGUMENT  # act mask needs x

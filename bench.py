@@ -208,8 +208,9 @@ def measure_distill(torch, F, W, layer, x, ids, probs, reps=10):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the expert-parallel "
-              "multi-GPU path is a design, not part of this build.", file=sys.stderr)
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}): the library has no "
+              "multi-GPU path (expert parallelism across GPUs is designed, not implemented).",
+              file=sys.stderr)
         sys.exit(2)
     import torch
     import moe_fake_quant_amd as F

@@ -5,7 +5,7 @@ cross-compiles, no GPU needed).
   not look into) is immediately preceded by the five wait states it carries
   itself: a base register written by a vector instruction just before needs
   five, an M0 write just before needs one;
-- no packed fp32 VALU instructions anywhere (the build disables the feature);
+- no packed fp32 VALU instructions anywhere (the compile flags disable the feature);
 - the grouped-GEMM kernels keep everything in registers (no scratch).
 """
 import concurrent.futures as cf

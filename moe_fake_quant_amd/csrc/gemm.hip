@@ -25,7 +25,10 @@
 // FWD / DGRAD store bf16 rows; WGRAD never stores dW: its epilogue
 // multiplies each dWq element by the straight-through factor dv/ds
 // (recomputed from the raw weight and its scale) and reduces over the
-// quantization group (dScale), deterministically.
+// quantization group (dScale), deterministically. Both epilogues move whole
+// rows through the free stage buffer (the output tile out of it, the raw
+// weights into it): partial-line global accesses cost far more than the LDS
+// round trip.
 //
 // Scheduling: a persistent grid of one block per CU walks the tile list.
 // FWD / DGRAD tiles are (expert, row tile, i tile); the number of row tiles of

@@ -353,7 +353,6 @@ __global__ __launch_bounds__(kKT) __attribute__((amdgpu_waves_per_eu(KM <= 1024 
                                                  float *__restrict__ loss_tok) {
   __shared__ KLShared sh;
   __shared__ KLBig<KM> xs;
-  __shared__ uint32_t wt[2][kKW][2];   // per-wave totals of the packed step counts
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const size_t row = blockIdx.x;
   const uint4 *trow = reinterpret_cast<const uint4 *>(teacher + row * (size_t)V);

@@ -407,11 +407,6 @@ __device__ __forceinline__ void store16(bf16x8_t *p, const float *x) {
   p[0] = pack8(x);
   p[1] = pack8(x + 8);
 }
-// round each value to bf16 in place (what a bf16 store then reload would give)
-__device__ __forceinline__ void round_bf16_16(float *x) {
-#pragma unroll
-  for (int j = 0; j < 16; ++j) x[j] = bf16_to_f32(f32_to_bf16(x[j]));
-}
 
 // FP8 / INT8 activation fake-quant of 16 elements that also yields each
 // element's straight-through factor dv/ds_a = value(c) - m*z (the factor of a

@@ -13,7 +13,6 @@ import glob
 import importlib.util
 import os
 import re
-import shutil
 import subprocess
 
 import pytest

@@ -3,7 +3,6 @@ import numpy as np
 import pytest
 
 import oracle as O
-from oracle import codecs as C
 
 
 def _w(E, N, K, seed=0, std=0.02):

@@ -234,7 +234,7 @@ __device__ __forceinline__ void wgrad_read_w(const char *slab, int lane, uint2 (
 template <int WFMT, int U>
 __device__ __forceinline__ void wgrad_epilogue(const GemmArgs &a, const f32x16 (&acc)[4][2], int e,
                                                int k0, int n0, int lane, const uint2 (&wv)[4][4],
-                                               int chunk) {
+                                               int chunk, float4 t4) {
   const int n = n0 + (lane & 31);
   const int G = a.K / a.group;
   const float g_e = (WFMT == FQ_FMT_NVFP4) ? a.gscale[e] : 1.0f;
@@ -251,7 +251,6 @@ __device__ __forceinline__ void wgrad_epilogue(const GemmArgs &a, const f32x16 (
     // them (theta rounded to E4M3, its reciprocal, the theta factor) and
     // takes the other four from lane ^ 32
     const int h = lane >> 5;
-    const float4 t4 = *reinterpret_cast<const float4 *>(a.scale + srow + k0 / 16 + 4 * h);
     const float th[4] = {t4.x, t4.y, t4.z, t4.w};
     float rm[4], fm[4];
 #pragma unroll
@@ -720,6 +719,14 @@ __device__ __forceinline__ void run_tile(const GemmArgs &a, const int *tile_star
     const int k0 = i0 + wi * 128, n0 = j0 + wj * WJ_TILE;
     char *slab = (wave < 4 ? stage_p<1>() : stage_q<1>()) + (wave & 3) * 8192;
     uint2 wv[4][4];
+    // NVFP4 theta of this lane's row and eight blocks, loaded before the
+    // barrier so that its latency overlaps the wait for the slowest wave
+    auto load_theta = [&](int nn) {
+      if (WFMT != FQ_FMT_NVFP4) return float4{0.0f, 0.0f, 0.0f, 0.0f};
+      const size_t srow = ((size_t)e * a.N + nn + (lane & 31)) * (a.K / a.group);
+      return *reinterpret_cast<const float4 *>(a.scale + srow + k0 / 16 + 4 * (lane >> 5));
+    };
+    const float4 th0 = load_theta(n0);
     block_barrier();
     wgrad_dma_w(a, e, k0, n0, lane, slab);
     if (prefetch_issue()) wait_vm<8>();  // the slab, not the next tile's stage 0
@@ -727,10 +734,11 @@ __device__ __forceinline__ void run_tile(const GemmArgs &a, const int *tile_star
     wgrad_read_w(slab, lane, wv);
     wait_lgkm0();                          // read back before the slab is reused
     wgrad_dma_w(a, e, k0, n0 + 32, lane, slab);
-    wgrad_epilogue<WFMT, 0>(a, acc, e, k0, n0, lane, wv, tl.chunk);
+    const float4 th1 = load_theta(n0 + 32);
+    wgrad_epilogue<WFMT, 0>(a, acc, e, k0, n0, lane, wv, tl.chunk, th0);
     wait_vm<0>();
     wgrad_read_w(slab, lane, wv);
-    wgrad_epilogue<WFMT, 1>(a, acc, e, k0, n0 + 32, lane, wv, tl.chunk);
+    wgrad_epilogue<WFMT, 1>(a, acc, e, k0, n0 + 32, lane, wv, tl.chunk, th1);
   }
 }
 

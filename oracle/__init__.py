@@ -72,7 +72,7 @@ from .codecs import (  # noqa: F401
     FMT_NONE, FMT_INT8, FMT_INT4, FMT_FP8, FMT_NVFP4, FMT_NAMES, GROUP_TENSOR,
     E4M3_POS, E2M1_POS, E4M3_MAX, E2M1_MAX,
     e4m3_round, e2m1_round, e4m3_value_of_code, e2m1_value_of_code,
-    fq_int8, fq_int4, fq_fp8, fq_nvfp4, fq_nvfp4_act_dynamic,
+    fq_int8, fq_int4, fq_fp8, fq_nvfp4, fq_nvfp4_act_dynamic, nvfp4_dynamic_theta,
     fq_weight_stack, fq_act,
 )
 from .observer import observer_weight, observer_act  # noqa: F401

@@ -245,6 +245,25 @@ fq_status fq_moe_permute(const int32_t *expert_ids, int32_t T, int32_t topk,
                          fq_stream stream);
 
 /* ------------------------------------------------------------------------
+ * fq_moe_permute_noalloc -- fq_moe_permute for callers that cannot allocate
+ * or pass device memory of their own (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): the same arguments and
+ * results, bit for bit, without a workspace. Its scratch (the per-chunk
+ * counts and expert totals) is a static 4 MiB device array inside the
+ * library; each GPU holds its own copy from the first call on it until the
+ * process ends. The call allocates nothing.
+ *   Limit: 4 * E_local * (ceil(T*topk / 256) + 1) <= 4 MiB, e.g. T*topk up
+ *   to 2,096,896 pairs at E_local = 128. Larger requests return
+ *   FQ_ERR_WORKSPACE_TOO_SMALL before anything is enqueued.
+ *   Every call on one GPU shares that GPU's array: calls that can overlap
+ *   on the device (other streams, other host threads) race; serialize them
+ *   on one stream. A call overwrites what the last one left there.
+ * ---------------------------------------------------------------------- */
+fq_status fq_moe_permute_noalloc(const int32_t *expert_ids, int32_t T, int32_t topk,
+                                 int32_t expert_begin, int32_t E_local, int32_t *perm,
+                                 int32_t *row_of, int32_t *seg_offsets, fq_stream stream);
+
+/* ------------------------------------------------------------------------
  * fq_grouped_gemm_fwd -- Y[r, :] = FQ_a(X)[r, :] . FQ_w(W[e])^T for every
  * routed row r in segment e = [seg_offsets[e], seg_offsets[e+1]), fp32
  * accumulation on bf16 MFMA, bf16 output (mcore_qad article, sections 二.3

@@ -46,6 +46,7 @@ EXPORTED = (
     "fq_grouped_gemm_bwd_scale", "fq_moe_gather_actfq", "fq_swiglu_actfq", "fq_swiglu_bwd",
     "fq_moe_combine", "fq_moe_combine_bwd", "fq_moe_unpermute_reduce", "fq_workspace_bytes",
     "fq_last_error", "fq_abi_version", "fq_export_scales", "fq_dequantize_stacked", "fq_topk_kl",
+    "fq_moe_permute_noalloc",
 )
 
 
@@ -79,6 +80,7 @@ def _load() -> ctypes.CDLL:
         "observer_absmax_init": (st, [P, fq_shape, I32, I32, I32, P, P, P, P, SZ, P]),
         "fq_quantize_stacked": (st, [P, fq_shape, ctypes.POINTER(fq_weight_q), P, P, P]),
         "fq_moe_permute": (st, [P, I32, I32, I32, I32, P, P, P, P, SZ, P]),
+        "fq_moe_permute_noalloc": (st, [P, I32, I32, I32, I32, P, P, P, P]),
         "fq_grouped_gemm_fwd": (st, [P, I32, P, fq_shape, P, P, ctypes.POINTER(fq_weight_q),
                                      ctypes.POINTER(fq_act_q), P, P, SZ, P]),
         "fq_grouped_gemm_bwd_scale": (st, [P, P, I32, P, fq_shape, P, P,
@@ -192,6 +194,13 @@ def fq_moe_permute(expert_ids, T, topk, expert_begin, E_local, perm, row_of, seg
     _check(_lib.fq_moe_permute(_p(expert_ids), int(T), int(topk), int(expert_begin),
                                int(E_local), _p(perm), _p(row_of), _p(seg_offsets), _p(ws),
                                _nbytes(ws), _stream()))
+
+
+def fq_moe_permute_noalloc(expert_ids, T, topk, expert_begin, E_local, perm, row_of,
+                           seg_offsets):
+    _check(_lib.fq_moe_permute_noalloc(_p(expert_ids), int(T), int(topk), int(expert_begin),
+                                       int(E_local), _p(perm), _p(row_of), _p(seg_offsets),
+                                       _stream()))
 
 
 def fq_grouped_gemm_fwd(x, R_max, seg_offsets, shape, w, w_fq, wq: Optional[WeightQ],

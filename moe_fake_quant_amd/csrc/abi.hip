@@ -293,6 +293,27 @@ fq_status fq_moe_permute(const int32_t *ids, int32_t T, int32_t topk, int32_t eb
   return FQ_OK;
 }
 
+fq_status fq_moe_permute_noalloc(const int32_t *ids, int32_t T, int32_t topk, int32_t ebegin,
+                                 int32_t E, int32_t *perm, int32_t *row_of, int32_t *seg,
+                                 fq_stream stream) {
+  FQ_CHECK_ARG(T >= 0 && topk > 0 && E > 0 && ebegin >= 0, "bad sizes T=%d topk=%d E=%d", T, topk, E);
+  FQ_CHECK_ARG(seg != nullptr, "seg_offsets is NULL");
+  FQ_CHECK_ARG(T == 0 || (ids && perm && row_of), "expert_ids, perm and row_of must be non-NULL");
+  FQ_CHECK_ARG((long)T * topk < (1l << 31), "too many pairs");
+  size_t need = permute_workspace_bytes(E, (long)T * topk);
+  if (need > kPermuteScratchBytes) {
+    set_error("fq_moe_permute_noalloc: E_local=%d and T*topk=%ld need %zu bytes of scratch, the "
+              "static scratch holds %zu (use fq_moe_permute with a workspace)",
+              E, (long)T * topk, need, kPermuteScratchBytes);
+    return FQ_ERR_WORKSPACE_TOO_SMALL;
+  }
+  int32_t *scr = nullptr;
+  FQ_TRY(permute_scratch(&scr));
+  launch_permute(ids, T, topk, ebegin, E, perm, row_of, seg, scr, S(stream));
+  FQ_CHECK_LAUNCH("fq_moe_permute_noalloc");
+  return FQ_OK;
+}
+
 fq_status fq_grouped_gemm_fwd(const uint16_t *x, int32_t R_max, const int32_t *seg, fq_shape s,
                               const uint16_t *w, const uint16_t *w_fq, const fq_weight_q *wq,
                               const fq_act_q *aq, uint16_t *y, void *ws, size_t ws_bytes,

@@ -56,6 +56,10 @@ void launch_topk_kl(const uint16_t *student, const uint16_t *teacher, int T, int
                     float *loss_mean, float *inv_n, hipStream_t st);
 
 size_t permute_workspace_bytes(int E, long P);
+// Size of the permute scratch array the allocation-free entry point uses.
+constexpr size_t kPermuteScratchBytes = size_t(4) << 20;
+// Device address of that array on the current device (resolved once per device).
+fq_status permute_scratch(int32_t **out);
 void launch_permute(const int32_t *ids, int T, int topk, int ebegin, int E, int32_t *perm,
                     int32_t *row_of, int32_t *seg, void *ws, hipStream_t st);
 

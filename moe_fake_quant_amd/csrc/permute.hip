@@ -8,6 +8,8 @@
 //   pass 4  per chunk: stable rank of each pair among the chunk's pairs of
 //           the same expert, position = seg + chunk offset + rank
 // No atomics decide an order, so the result is unique and deterministic.
+#include <mutex>
+
 #include "internal.hpp"
 
 namespace fq {
@@ -111,6 +113,41 @@ __global__ __launch_bounds__(kChunk) void k_perm_scatter(const int32_t *__restri
 }
 
 }  // namespace
+
+// Scratch of the allocation-free permute entry point: the per-chunk counts
+// and expert totals live in this array instead of a caller workspace. Each
+// GPU the library runs on holds its own copy until the process ends. Every
+// entry of the counts and totals a call uses is written before it is read,
+// so nothing needs clearing between calls; calls that overlap on one GPU
+// share the array and race.
+static __device__ __align__(256) int32_t scratch[kPermuteScratchBytes / sizeof(int32_t)];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+int32_t *g_scratch_dev[kMaxDevices] = {};
+}  // namespace
+
+fq_status permute_scratch(int32_t **out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "permute scratch: hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) {
+    set_error("permute scratch: device %d outside 0..%d", dev, kMaxDevices - 1);
+    return FQ_ERR_UNSUPPORTED;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    // the array's device address on the current device (the host-side name
+    // is only a stand-in, never passed to a kernel)
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e, "permute scratch: hipGetSymbolAddress");
+    g_scratch_dev[dev] = static_cast<int32_t *>(p);
+  }
+  *out = g_scratch_dev[dev];
+  return FQ_OK;
+}
 
 size_t permute_workspace_bytes(int E, long P) {
   long nchunk = (P + kChunk - 1) / kChunk;

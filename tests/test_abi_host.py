@@ -201,6 +201,15 @@ def test_permute_and_elementwise_reject_bad_arguments(pkg):
         pkg.FQ_ERR_INVALID_ARGUMENT                                   # no seg_offsets
     assert L.fq_moe_permute(FAKE, 16, 8, 0, 4, FAKE, FAKE, FAKE, FAKE, 8, None) == \
         pkg.FQ_ERR_WORKSPACE_TOO_SMALL
+    # the allocation-free variant: same checks, and a request beyond its
+    # static scratch fails before anything touches a device
+    assert L.fq_moe_permute_noalloc(FAKE, 16, 0, 0, 4, FAKE, FAKE, FAKE, None) == \
+        pkg.FQ_ERR_INVALID_ARGUMENT                                   # topk 0
+    assert L.fq_moe_permute_noalloc(FAKE, 16, 8, 0, 4, FAKE, FAKE, None, None) == \
+        pkg.FQ_ERR_INVALID_ARGUMENT                                   # no seg_offsets
+    assert L.fq_moe_permute_noalloc(FAKE, 262144, 8, 0, 1024, FAKE, FAKE, FAKE, None) == \
+        pkg.FQ_ERR_WORKSPACE_TOO_SMALL                                # 33.6 MB > 4 MiB
+    assert b"static scratch" in L.fq_last_error()
     assert L.fq_moe_gather_actfq(FAKE, 16, 40, FAKE, 8, None, FAKE, None) == \
         pkg.FQ_ERR_INVALID_ARGUMENT                                   # H % 16
     assert L.fq_moe_gather_actfq(FAKE, 16, 64, None, 8, None, FAKE, None) == \

@@ -9,10 +9,14 @@ Workload (default): Qwen3-30B-A3B-shaped layer, 128 experts, hidden 2048,
 expert FFN 768, 16384 tokens x top-8, NVFP4 weights and activations,
 synthetic seeded inputs. Inputs are resident in HBM before timing starts.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 4]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 1..5]
 
-Prints one JSON line (rank 0). Per-kernel times are measured with HIP events
-on the launch stream inside the timed region.
+Prints one JSON line (rank 0). The headline step time comes from HIP events
+around the K timed steps only; the per-call breakdown comes from a separate
+pass with HIP events around every call, so the headline carries no
+instrumentation. --config 1 / 2 time the dense single-linear workloads (FQ
+pass + forward + scale-only backward through the same grouped-GEMM calls with
+one expert).
 """
 from __future__ import annotations
 
@@ -66,7 +70,11 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", type=int, default=4, choices=[3, 4, 5])
+    ap.add_argument("--config", type=int, default=4, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--breakdown-steps", type=int, default=10,
+                    help="steps of the separate instrumented pass (per-call times)")
+    ap.add_argument("--no-peaks", action="store_true",
+                    help="skip the measured MFMA-chain and copy peaks")
     ap.add_argument("--act-scales", choices=["frozen", "learnable"], default="frozen",
                     help="learnable: the backward also forms the activation-scale gradients "
                          "(fp8 workload only)")
@@ -205,6 +213,98 @@ def measure_distill(torch, F, W, layer, x, ids, probs, reps=10):
     return out
 
 
+def measured_peaks(torch, dev):
+    """The part's own ceilings, measured in the same run: a register-only chain
+    of bf16 MFMA 32x32x16 on every CU (1 wave per SIMD, 8 independent
+    accumulators; random operand bits and constant 1.0, since the clock under
+    MFMA load depends on the operand bits) and a plain 1 GiB device copy with
+    one 16-byte vector per thread (read + write bytes)."""
+    import ctypes
+    lib_path = os.path.join(ROOT, "moe_fake_quant_amd", "libfqpeaks.so")
+    if not os.path.exists(lib_path):
+        return None
+    lib = ctypes.CDLL(lib_path)
+    lib.fqp_mfma_chain.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                   ctypes.c_void_p]
+    lib.fqp_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    st = torch.cuda.current_stream().cuda_stream
+    n_cu = torch.cuda.get_device_properties(dev).multi_processor_count
+    blocks, iters = n_cu, 8000   # one 4-wave block per CU: one wave per SIMD
+    out = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
+    res = {}
+    for name, rnd in (("random_operands", 1), ("constant_operands", 0)):
+        assert lib.fqp_mfma_chain(out.data_ptr(), blocks, 20, rnd, st) == 0
+        torch.cuda.synchronize()
+        s0 = torch.cuda.Event(enable_timing=True)
+        e0 = torch.cuda.Event(enable_timing=True)
+        s0.record()
+        assert lib.fqp_mfma_chain(out.data_ptr(), blocks, iters, rnd, st) == 0
+        e0.record()
+        torch.cuda.synchronize()
+        ms = s0.elapsed_time(e0)
+        flops = 32 * 32 * 16 * 2 * 8 * iters * blocks * 4
+        res[name] = round(flops / (ms * 1e-3) / 1e12, 1)
+    nbytes = 1 << 30
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    assert lib.fqp_copy(src.data_ptr(), dst.data_ptr(), nbytes, st) == 0
+    torch.cuda.synchronize()
+    s1 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    s1.record()
+    for _ in range(5):
+        assert lib.fqp_copy(src.data_ptr(), dst.data_ptr(), nbytes, st) == 0
+    e1.record()
+    torch.cuda.synchronize()
+    copy_gbs = 2 * nbytes * 5 / (s1.elapsed_time(e1) * 1e-3) / 1e9
+    del src, dst, out
+    return {"mfma_bf16_chain_TFLOP/s": res,
+            "mfma_bf16_chain_pct_of_spec": round(100 * res["random_operands"] / MI355X_BF16_PEAK_TFLOPS, 1),
+            "copy_GB/s": round(copy_gbs, 1),
+            "copy_pct_of_spec": round(100 * copy_gbs / MI355X_HBM_PEAK_GBS, 1)}
+
+
+def host_description():
+    """CPU model and the cores this process may run on (the GPU machine's host)."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    model = ln.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        cpus = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cpus = os.cpu_count()
+    return model, cpus
+
+
+def blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        return max([p["num_threads"] for p in threadpool_info() if p.get("user_api") == "blas"]
+                   or [1])
+    except Exception:
+        return 1
+
+
+def time_steps(torch, step, steps):
+    """HIP events around `steps` calls of step() on the current stream."""
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record()
+    for _ in range(steps):
+        step()
+    end.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / steps, time.perf_counter() - t0
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -212,6 +312,8 @@ def main():
               "multi-GPU path (expert parallelism across GPUs is designed, not implemented).",
               file=sys.stderr)
         sys.exit(2)
+    if args.config in (1, 2):
+        return dense_main(args)
     import torch
     import moe_fake_quant_amd as F
     import workloads as W
@@ -235,6 +337,8 @@ def main():
     dout = bf(case.dout)
     t_gen = time.time() - t_gen
 
+    # the part's own ceilings first, before the workload has heated it
+    peaks = None if args.no_peaks else measured_peaks(torch, dev)
     layer = F.MoEFakeQuantLayer(w_gu, w_d, fmt, fmt, case.T, case.topk, case.expert_begin, group,
                                 learn_act_scales=learn)
     layer.init_weight_scales()
@@ -243,9 +347,10 @@ def main():
     R = int(layer.seg[layer.E].item())
     E, H, Fh = layer.E, layer.H, layer.F
 
-    # Events around every ABI call the layer makes. Each GEMM call launches one
-    # kernel: fwd -> k_grouped_gemm<FWD>, bwd with dx -> <DGRAD>, bwd with
-    # dscale -> <WGRAD> (dScale epilogue); the FQ pass is one kernel per stack.
+    # Events around every ABI call the layer makes, in the breakdown pass
+    # only. Each GEMM call launches one kernel: fwd -> k_grouped_gemm<FWD>,
+    # bwd with dx -> <DGRAD>, bwd with dscale -> <WGRAD> (dScale epilogue);
+    # the FQ pass is one kernel per stack.
     timer = KernelTimer(torch)
     import moe_fake_quant_amd.layer as LM
     keys = {
@@ -259,24 +364,21 @@ def main():
                  "fq_moe_unpermute_reduce"):
         setattr(LM, name, timer.wrap(keys.get(name, lambda a, n=name: n), getattr(LM, name)))
 
+    step = lambda: layer.step(x, ids, probs, dout)  # noqa: E731
     for _ in range(args.warmup):
-        layer.step(x, ids, probs, dout)
+        step()
     torch.cuda.synchronize()
 
-    # timed region: K whole steps bracketed by device syncs, events on the stream
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    timer.enabled = True
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    start.record()
-    for _ in range(args.steps):
-        layer.step(x, ids, probs, dout)
-    end.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    # headline: K whole steps bracketed by device syncs, events on the stream,
+    # nothing else recorded inside
     timer.enabled = False
-    ms_step = start.elapsed_time(end) / args.steps
+    ms_step, wall = time_steps(torch, step, args.steps)
+
+    # breakdown: a separate pass with events around each call
+    nb = max(args.breakdown_steps, 1)
+    timer.enabled = True
+    ms_step_instr, _ = time_steps(torch, step, nb)
+    timer.enabled = False
     per = timer.collect()
 
     flops_step = FLOPS_PER_ROW * R
@@ -287,8 +389,8 @@ def main():
     kernels = {}
     for kind in ("gemm_fwd", "gemm_dgrad", "gemm_wgrad_dscale"):
         t = per.get(kind, [])
-        ms = sum(t) / args.steps
-        kernels[kind] = {"launches_per_step": len(t) // args.steps, "ms_per_step": round(ms, 4),
+        ms = sum(t) / nb
+        kernels[kind] = {"launches_per_step": len(t) // nb, "ms_per_step": round(ms, 4),
                          "avg_launch_ms": round(sum(t) / max(len(t), 1), 4),
                          "TFLOP/s": round(kind_flops / (ms * 1e-3) / 1e12, 2)}
     dom = max(kernels, key=lambda k: kernels[k]["ms_per_step"])
@@ -303,7 +405,7 @@ def main():
     else:
         scale_bytes = E * (2 * Fh + H) * 4
     fq_bytes = nel * 4 + scale_bytes
-    fq_ms = sum(per.get("fq_quantize_stacked", [0.0])) / args.steps
+    fq_ms = sum(per.get("fq_quantize_stacked", [0.0])) / nb
     fq_gbs = fq_bytes / (fq_ms * 1e-3) / 1e9
 
     traffic = None
@@ -316,14 +418,14 @@ def main():
 
     passes = {}
     for name, nbytes in hbm_pass_bytes(case.T, H, Fh, R, case.topk).items():
-        ms = sum(per.get(name, [0.0])) / args.steps
+        ms = sum(per.get(name, [0.0])) / nb
         if ms > 0:
             passes[name] = {"bytes": nbytes, "ms": round(ms, 4),
                             "GB/s": round(nbytes / (ms * 1e-3) / 1e9, 1),
                             "pct_hbm_peak": round(100 * nbytes / (ms * 1e-3) / 1e9 / MI355X_HBM_PEAK_GBS, 1)}
     gemm_ms = sum(kernels[k]["ms_per_step"] for k in kernels)
 
-    breakdown = {n: round(sum(v) / args.steps, 4) for n, v in sorted(per.items())}
+    breakdown = {n: round(sum(v) / nb, 4) for n, v in sorted(per.items())}
 
     if args.copy_calibration_mb > 0:
         n = args.copy_calibration_mb * (1 << 20) // 4
@@ -378,15 +480,122 @@ def main():
             "frac": round(achieved / MI355X_BF16_PEAK_TFLOPS, 4),
             "traffic": traffic,
         },
+        "timing": {"headline": "HIP events around the timed steps, no per-call events",
+                   "breakdown_steps": nb, "breakdown_ms_per_step": round(ms_step_instr, 4)},
         "gemm_kernels": kernels,
         "gemm_only": {"ms_per_step": round(gemm_ms, 4),
                       "TFLOP/s": round(flops_step / (gemm_ms * 1e-3) / 1e12, 2)},
         "hbm_passes": passes,
+        "measured_peaks": peaks,
         "export_decode": export,
         "distill": distill,
         "ms_per_step_by_call": breakdown,
         "cpu_baseline": cpu,
         "input_gen_s": round(t_gen, 1),
+        "wall_s_timed": round(wall, 3),
+    }
+    print(json.dumps(line), flush=True)
+
+
+def dense_main(args):
+    """The dense single-linear workloads (one expert, seg = [0, M]): one step =
+    FQ pass over W, forward Y = X . FQ(W)^T, backward dX and dScale (weights
+    frozen), through the same grouped-GEMM calls as the MoE path."""
+    import torch
+    import moe_fake_quant_amd as F
+    import workloads as W
+
+    dev = torch.device("cuda:0")
+    case = W.config(args.config, seed=args.seed)
+    fmt = {1: F.FMT_INT8, 2: F.FMT_INT4}[args.config]
+    bf = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)  # noqa: E731
+    N, K = case.w.shape
+    M = case.x.shape[0]
+    shape = (1, N, K)
+    group = case.group
+    G = K // group
+    w, x, dy = bf(case.w[None]), bf(case.x), bf(case.dy)
+    s = torch.empty(1, N, G, device=dev)
+    zp = torch.empty(1, N, G, device=dev) if fmt == F.FMT_INT4 else None
+    F.observer_absmax_init(w, shape, fmt, group, 0, s, zp, None)
+    q = F.WeightQ(fmt, group, s, zp, None)
+    seg = torch.tensor([0, M], dtype=torch.int32, device=dev)
+    wfq = torch.empty_like(w)
+    ws = torch.empty(max(F.fq_workspace_bytes(F.FQ_OP_GEMM_FWD, shape, M, 0),
+                         F.fq_workspace_bytes(F.FQ_OP_GEMM_BWD, shape, M, 0), 256),
+                     dtype=torch.uint8, device=dev)
+    y = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
+    dx = torch.empty(M, K, dtype=torch.bfloat16, device=dev)
+    ds = torch.empty(1, N, G, device=dev)
+    dzp = torch.empty(1, N, G, device=dev) if fmt == F.FMT_INT4 else None
+
+    calls = {
+        "fq_quantize_stacked": lambda: F.fq_quantize_stacked(w, shape, q, wfq),
+        "gemm_fwd": lambda: F.fq_grouped_gemm_fwd(x, M, seg, shape, None, wfq, q, None, y, ws),
+        "gemm_dgrad": lambda: F.fq_grouped_gemm_bwd_scale(dy, x, M, seg, shape, w, wfq, q, None,
+                                                          dx, None, None, ws),
+        "gemm_wgrad_dscale": lambda: F.fq_grouped_gemm_bwd_scale(dy, x, M, seg, shape, w, wfq, q,
+                                                                 None, None, ds, dzp, ws),
+    }
+
+    def step():
+        for fn in calls.values():
+            fn()
+
+    peaks = None if args.no_peaks else measured_peaks(torch, dev)
+    steps = args.steps * (50 if args.config == 1 else 1)   # the latency case: more reps
+    for _ in range(args.warmup):
+        step()
+    ms_step, wall = time_steps(torch, step, steps)
+    # per-call breakdown in a separate pass
+    per = {}
+    nb = max(args.breakdown_steps, 1) * (50 if args.config == 1 else 1)
+    for name, fn in calls.items():
+        ms, _ = time_steps(torch, fn, nb)
+        per[name] = ms
+    flops_step = 6 * M * N * K
+    tflops = flops_step / (ms_step * 1e-3) / 1e12
+    kind_flops = 2 * M * N * K
+    kernels = {k: {"ms_per_step": round(per[k], 4), "avg_launch_ms": round(per[k], 4),
+                   "TFLOP/s": round(kind_flops / (per[k] * 1e-3) / 1e12, 2)}
+               for k in ("gemm_fwd", "gemm_dgrad", "gemm_wgrad_dscale")}
+    dom = max(kernels, key=lambda k: kernels[k]["ms_per_step"])
+    nel = N * K
+    scale_bytes = N * G * 4 * (2 if fmt == F.FMT_INT4 else 1)
+    fq_bytes = nel * 4 + scale_bytes
+    fq_gbs = fq_bytes / (per["fq_quantize_stacked"] * 1e-3) / 1e9
+    cpu = None if args.no_cpu_baseline else cpu_baseline_dense(case, args.config)
+    line = {
+        "metric": "MoE fake-quant grouped-GEMM fwd+bwd TFLOP/s; % bf16 MFMA peak; FQ pass GB/s",
+        "value": round(tflops, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "us_per_step": round(ms_step * 1e3, 2),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": W.CONFIG_NAMES[args.config], "M": M, "N": N, "K": K,
+                   "weight_format": {1: "int8", 2: "int4"}[args.config],
+                   "weight_scales": "per-channel" if group == K else f"group{group}",
+                   "act_format": "none", "flops_per_step": flops_step},
+        "pct_bf16_peak": round(100 * tflops / MI355X_BF16_PEAK_TFLOPS, 3),
+        "fq_pass": {"GB/s": round(fq_gbs, 1), "pct_hbm_peak": round(100 * fq_gbs / MI355X_HBM_PEAK_GBS, 2),
+                    "bytes_per_step": fq_bytes, "ms_per_step": round(per["fq_quantize_stacked"], 5)},
+        "roofline": {"kernel": dom, "bound": "mfma", "achieved": kernels[dom]["TFLOP/s"],
+                     "peak": MI355X_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(kernels[dom]["TFLOP/s"] / MI355X_BF16_PEAK_TFLOPS, 4),
+                     "traffic": None},
+        "timing": {"headline": "HIP events around the timed steps, no per-call events",
+                   "breakdown": "each call timed alone over the same number of reps"},
+        "gemm_kernels": kernels,
+        "measured_peaks": peaks,
+        "ms_per_step_by_call": {k: round(v, 5) for k, v in per.items()},
+        "cpu_baseline": cpu,
         "wall_s_timed": round(wall, 3),
     }
     print(json.dumps(line), flush=True)
@@ -404,22 +613,41 @@ def cpu_baseline(case, fmt, group, n_experts):
     wfmt = O.FMT_NVFP4 if fmt == 4 else O.FMT_FP8
     _, _, seg = O.moe_permute(case.expert_ids, 0, E)
     R = int(seg[-1])
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([p["num_threads"] for p in threadpool_info() if p.get("user_api") == "blas"]
-                    or [1])
-    except Exception:
-        cores = 1
+    model, cpus = host_description()
     t0 = time.perf_counter()
     # group: 16 (nvfp4 blocks), None (one scale per output channel) or the
     # per-tensor marker, the same values the oracle takes
     O.moe_layer(sub, wfmt, group, wfmt)
     dt = time.perf_counter() - t0
     flops = FLOPS_PER_ROW * R
-    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": cores,
-            "kind": "oracle", "seconds": round(dt, 2),
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": blas_threads(),
+            "kind": "oracle", "seconds": round(dt, 2), "cpu_model": model,
+            "affinity_cpus": cpus,
             "sample": f"experts 0..{E - 1} of the same layer and their {R} routed rows "
                       f"(full fwd+bwd incl. observer init), {flops / 1e9:.1f} GFLOP"}
+
+
+def cpu_baseline_dense(case, cfg):
+    """The oracle on the whole dense workload: observer, FQ pass, forward and
+    the scale-only backward (float64 GEMMs through NumPy's BLAS)."""
+    import oracle as O
+    fmt = {1: O.FMT_INT8, 2: O.FMT_INT4}[cfg]
+    N, K = case.w.shape
+    M = case.x.shape[0]
+    model, cpus = host_description()
+    seg = np.array([0, M])
+    t0 = time.perf_counter()
+    wq = O.observer_weight(case.w[None], fmt, case.group)
+    O.fq_weight_stack(case.w[None], fmt, case.group, *wq)
+    O.grouped_gemm_fwd(case.x, seg, case.w[None], fmt, case.group, *wq)
+    O.grouped_gemm_bwd(case.dy, case.x, seg, case.w[None], fmt, case.group, *wq)
+    dt = time.perf_counter() - t0
+    flops = 6 * M * N * K
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": blas_threads(),
+            "kind": "oracle", "seconds": round(dt, 3), "cpu_model": model,
+            "affinity_cpus": cpus,
+            "sample": f"the whole workload (M={M}, N={N}, K={K}): observer, FQ pass, forward, "
+                      f"dX and dScale, {flops / 1e9:.2f} GFLOP"}
 
 
 if __name__ == "__main__":

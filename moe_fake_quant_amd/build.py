@@ -58,6 +58,26 @@ def build(verbose: bool = False, extra=()) -> str:
     return LIB
 
 
+PEAKS_SRC = os.path.join(HERE, "peaks", "peaks.hip")
+PEAKS_LIB = os.path.join(HERE, "libfqpeaks.so")
+
+
+def build_peaks(verbose: bool = False) -> str:
+    """The benchmark's measured-peak probes (MFMA chain, device copy): a
+    separate small library, not part of libfq's path."""
+    tmp = PEAKS_LIB + ".tmp"
+    cmd = [hipcc(), *flags(), "-o", tmp, PEAKS_SRC]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    noise = "is not a recognized feature for this target"
+    lines = [ln for ln in (res.stdout + res.stderr).splitlines() if noise not in ln]
+    if res.returncode != 0:
+        raise RuntimeError("hipcc failed:\n" + "\n".join(lines))
+    os.replace(tmp, PEAKS_LIB)
+    return PEAKS_LIB
+
+
 if __name__ == "__main__":
     build(verbose=True, extra=sys.argv[1:])
     print(LIB)

@@ -534,13 +534,15 @@ struct TileLoads {
   }
 };
 
-// One 256 x 256 output tile: the contraction loop and the epilogue. If
-// `pre` is set, stage 0 of this tile is already in flight; if next_w >= 0,
-// stage 0 of tile next_w is issued once every wave is done with this tile's
-// LDS buffers, so that its loads run under this tile's epilogue.
+// WGRAD tile, all eight waves in step (the wgrad loop measured faster this
+// way than in the ping-pong below: its wider epilogue leaves the ping-pong's
+// registers short). If `pre` is set, stage 0 of this tile is already in
+// flight; if next_w >= 0, stage 0 of tile next_w is issued once every wave
+// is done with this tile's LDS buffers, so that its loads run under this
+// tile's epilogue.
 template <int MODE, int WFMT>
-__device__ __forceinline__ void run_tile(const GemmArgs &a, const int *tile_start, const Tile &tl,
-                                         bool pre, int next_w) {
+__device__ __forceinline__ void run_tile_lockstep(const GemmArgs &a, const int *tile_start,
+                                                  const Tile &tl, bool pre, int next_w) {
   const int t = threadIdx.x;
   const int lane = t & 63, wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int wi = wave & 1, wj = wave >> 1;  // 2 x 4 waves: 128 (i) x 64 (j) each
@@ -742,6 +744,254 @@ __device__ __forceinline__ void run_tile(const GemmArgs &a, const int *tile_star
   }
 }
 
+// One 256 x 256 output tile: the contraction loop and the epilogue. The
+// first `pre` stages of this tile (0, 1 or 2) are already in flight. If
+// next_w >= 0, the first two stages of tile next_w are issued as this tile's
+// buffers free up (stage 0 before the epilogue, stage 1 after it), so that
+// their loads run under the epilogue; the return value is the number of them
+// issued.
+//
+// Ping-pong: waves w and w + 4 share a SIMD (the hardware's placement of an
+// 8-wave workgroup), so group A = waves 0-3 and group B = waves 4-7 hold one
+// wave of each SIMD. The groups run a quarter stage apart. Between two block
+// barriers one group multiplies half a stage (two 16-deep steps) from
+// registers while the other reads its fragments of the next half from LDS
+// (and, twice a stage, issues its share of the loads two stages ahead), so
+// every SIMD always has a wave with MFMAs to issue, and the LDS read latency
+// and the barrier wait sit under them. With h = 0, 1 the halves of stage t:
+//   phase 4t     : A multiplies t.0  | B reads t.0
+//   phase 4t + 1 : B multiplies t.0  | A reads t.1
+//   phase 4t + 2 : A multiplies t.1  | B reads t.1,  loads its share of t+2
+//   phase 4t + 3 : B multiplies t.1  | A reads t+1.0, loads its share of t+2
+// Stage t lives in buffer t % 2; after phase 4t + 2 nobody reads it again, so
+// each wave loads into it once its own reads of it have returned. Each wave
+// waits for its own loads of a stage before the barrier that opens the
+// first phase reading it. A's epilogue runs while B multiplies the last half.
+template <int MODE, int WFMT>
+__device__ __forceinline__ int run_tile(const GemmArgs &a, const int *tile_start, const Tile &tl,
+                                        int pre, int next_w) {
+  const int t = threadIdx.x;
+  const int lane = t & 63, wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int wi = wave & 1, wj = wave >> 1;  // 2 x 4 waves: 128 (i) x 64 (j) each
+  const bool grp_b = wave >= 4;             // j columns 128..255 of the tile
+  const int e = tl.e, i0 = tl.i0, j0 = tl.j0, j_end = tl.j_end;
+  const TileLoads<MODE> ld(a, tl, wave, lane);
+  const int c_total = ld.c_total, nk = ld.nk;
+  // FWD / DGRAD: a wave whose 64 rows all lie past the expert's last row (the
+  // ragged last row tile) skips its fragment reads and MFMAs; it still takes
+  // part in the loads and barriers.
+  const bool live = MODE == WGRAD || j0 + wj * WJ_TILE < j_end;
+
+  f32x16 acc[4][2];
+#pragma unroll
+  for (int s = 0; s < 4; ++s)
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[s][u][v] = 0.0f;
+
+  // MFMA fragments of one 16-deep step: 4 P sub-tiles, 2 Q sub-tiles; a
+  // wave holds half a stage (2 steps) between its read and multiply phases
+  struct Frags {
+    bf16x8v p[4], q[2];
+  };
+  Frags f[2];
+  // half h of stage kt from buffer S; WGRAD's last stage: contraction rows
+  // past the chunk's last routed row are zeroed in the fragments
+  auto read_half = [&](auto stage_tag, int kt, int h) {
+    constexpr int S = decltype(stage_tag)::value;
+    const char *sp = stage_p<S>();
+    const char *sq = stage_q<S>();
+#pragma unroll
+    for (int k2 = 0; k2 < 2; ++k2) {
+      const int ks = 2 * h + k2;
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+        f[k2].p[s] = (MODE == FWD) ? frag_normal(sp, wi * 128 + s * 32, ks, lane)
+                                   : frag_trans(sp, wi * 128 + s * 32, ks, lane);
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+        f[k2].q[u] = (MODE == WGRAD) ? frag_trans(sq, wj * WJ_TILE + u * 32, ks, lane)
+                                     : frag_normal(sq, wj * WJ_TILE + u * 32, ks, lane);
+    }
+    if (MODE == WGRAD && (kt + 1) * BK > c_total) {
+#pragma unroll
+      for (int k2 = 0; k2 < 2; ++k2) {
+        const int cfirst = kt * BK + 16 * (2 * h + k2) + 8 * (lane >> 5);
+#pragma unroll
+        for (int s = 0; s < 4; ++s) f[k2].p[s] = zero_tail(f[k2].p[s], cfirst, c_total);
+#pragma unroll
+        for (int u = 0; u < 2; ++u) f[k2].q[u] = zero_tail(f[k2].q[u], cfirst, c_total);
+      }
+    }
+  };
+  auto multiply = [&]() {
+#pragma unroll
+    for (int k2 = 0; k2 < 2; ++k2)
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+          acc[s][u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f[k2].p[s], f[k2].q[u], acc[s][u], 0,
+                                                              0, 0);
+  };
+  // a block barrier that the scheduler moves nothing across (MFMAs would
+  // otherwise drift into the other group's phase)
+  auto phase_barrier = [&]() {
+    __builtin_amdgcn_sched_barrier(0);
+    block_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  // group A, stage kt in buffer S (its first half already read)
+  auto a_step = [&](auto stage_tag, int kt) {
+    constexpr int S = decltype(stage_tag)::value;
+    phase_barrier();  // 4kt
+    if (live) multiply();
+    phase_barrier();  // 4kt+1
+    if (live) read_half(stage_tag, kt, 1);
+    wait_lgkm0();
+    phase_barrier();  // 4kt+2
+    if (live) multiply();
+    if (kt + 1 < nk) {
+      wait_vm<0>();  // this wave's share of stage kt+1
+      phase_barrier();  // 4kt+3
+      if (live) read_half(std::integral_constant<int, S ^ 1>{}, kt + 1, 0);
+      wait_lgkm0();
+      if (kt + 2 < nk) ld.template issue<S>(a, kt + 2, wave);
+    }
+  };
+  // group B, stage kt in buffer S
+  auto b_step = [&](auto stage_tag, int kt) {
+    constexpr int S = decltype(stage_tag)::value;
+    phase_barrier();  // 4kt
+    if (live) read_half(stage_tag, kt, 0);
+    wait_lgkm0();
+    phase_barrier();  // 4kt+1
+    if (live) multiply();
+    phase_barrier();  // 4kt+2
+    if (live) read_half(stage_tag, kt, 1);
+    wait_lgkm0();
+    if (kt + 2 < nk) {
+      ld.template issue<S>(a, kt + 2, wave);
+      wait_vm<8>();  // this wave's share of stage kt+1 (read by A next phase)
+    } else {
+      wait_vm<0>();
+    }
+    phase_barrier();  // 4kt+3
+    if (live) multiply();
+  };
+
+  if (nk > 0) {
+    if (pre < 1) ld.template issue<0>(a, 0, wave);
+    if (pre < 2 && nk > 1) ld.template issue<1>(a, 1, wave);
+    if (nk > 1) wait_vm<8>();  // this wave's share of stage 0
+    else wait_vm<0>();
+    phase_barrier();
+    if (!grp_b) {
+      if (live) read_half(std::integral_constant<int, 0>{}, 0, 0);
+      wait_lgkm0();
+      for (int kt = 0; kt < nk; kt += 2) {
+        a_step(std::integral_constant<int, 0>{}, kt);
+        if (kt + 1 < nk) a_step(std::integral_constant<int, 1>{}, kt + 1);
+      }
+      phase_barrier();  // opens phase 4nk-1, B's last multiply
+    } else {
+      for (int kt = 0; kt < nk; kt += 2) {
+        b_step(std::integral_constant<int, 0>{}, kt);
+        if (kt + 1 < nk) b_step(std::integral_constant<int, 1>{}, kt + 1);
+      }
+    }
+  }
+
+  // Both buffers are free from here on for this wave's group: the other
+  // group no longer reads them. Stage 0 of the next tile goes to buffer 0
+  // now; buffer 1 serves as this group's staging (A the P half, B the Q
+  // half) and takes stage 1 of the next tile after the closing barrier.
+  auto issue_next = [&](auto stage_tag) -> bool {
+    constexpr int S = decltype(stage_tag)::value;
+    if (next_w < 0) return false;
+    const Tile nt = decode_tile<MODE>(a, tile_start, next_w);
+    const TileLoads<MODE> nl(a, nt, wave, lane);
+    if (nl.nk <= S) return false;
+    nl.template issue<S>(a, S, wave);
+    return true;
+  };
+  char *slab = (wave < 4 ? stage_p<1>() : stage_q<1>()) + (wave & 3) * 8192;
+
+  // accumulator (s, u, v) of this lane: i = i0 + wi*128 + s*32 + 8*(v/4) + 4*(lane/32) + v%4,
+  //                                     j = j0 + wj*64 + u*32 + lane%32
+  if (MODE != WGRAD) {
+    (void)issue_next(std::integral_constant<int, 0>{});
+    // The bf16 tile goes out through LDS: each wave writes its 128 (i) x 32 (j)
+    // half-slab row by row into its 8 KiB of buffer 1, then stores whole
+    // 256-byte row segments, 16 bytes per lane. Direct stores from the
+    // accumulator layout would write each 128-byte line in 16-byte pieces
+    // from eight instructions. Row r of the slab is 16 chunks of 16 bytes;
+    // chunk c sits at c ^ (r & 15), so the lanes of a write (32 rows, one
+    // chunk) and of a read (one row per 16 lanes) spread over the banks.
+    const int ldo = (MODE == FWD) ? a.N : a.K;
+    // lane terms formed here (an empty asm keeps the compiler from hoisting
+    // the addresses derived from them into the contraction loop's registers)
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    const int h = ln >> 5, jr = ln & 31;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      if (!live) break;
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          uint2 pk;
+          pk.x = pack_bf16(acc[s][u][4 * q + 0], acc[s][u][4 * q + 1]);
+          pk.y = pack_bf16(acc[s][u][4 * q + 2], acc[s][u][4 * q + 3]);
+          const uint32_t c = (uint32_t)(4 * s + q) ^ (uint32_t)(jr & 15);
+          *reinterpret_cast<uint2 *>(slab + jr * 256 + c * 16 + h * 8) = pk;
+        }
+      const int jb = j0 + wj * WJ_TILE + u * 32;
+      uint16_t *obase = a.out + (size_t)i0 + wi * 128 + (ln & 15) * 8;
+#pragma unroll
+      for (int it = 0; it < 8; ++it) {
+        const int r = 4 * it + (ln >> 4);
+        const uint4 v = *reinterpret_cast<const uint4 *>(
+            slab + r * 256 + (((uint32_t)(ln & 15) ^ (uint32_t)(r & 15)) << 4));
+        if (jb + r < j_end) *reinterpret_cast<uint4 *>(obase + (size_t)(jb + r) * ldo) = v;
+      }
+    }
+    wait_lgkm0();  // the slab is read back before buffer 1 takes the next tile's stage 1
+  } else {
+    // ---- WGRAD epilogue: i = k, j = n of expert e. dS over groups along k.
+    // The raw weights come in through this wave's 8 KiB of buffer 1, its two
+    // 32-row slabs one after the other: whole-row DMA instead of 8-byte loads
+    // from 32 rows per instruction. Only the wave itself reads its slab, so
+    // its own waits order the accesses.
+    const int k0 = i0 + wi * 128, n0 = j0 + wj * WJ_TILE;
+    uint2 wv[4][4];
+    auto load_theta = [&](int nn) {
+      if (WFMT != FQ_FMT_NVFP4) return float4{0.0f, 0.0f, 0.0f, 0.0f};
+      const size_t srow = ((size_t)e * a.N + nn + (lane & 31)) * (a.K / a.group);
+      return *reinterpret_cast<const float4 *>(a.scale + srow + k0 / 16 + 4 * (lane >> 5));
+    };
+    const float4 th0 = load_theta(n0);
+    wgrad_dma_w(a, e, k0, n0, lane, slab);
+    if (issue_next(std::integral_constant<int, 0>{})) wait_vm<8>();  // the slab, not the next stage
+    else wait_vm<0>();
+    wgrad_read_w(slab, lane, wv);
+    wait_lgkm0();  // read back before the slab is reused
+    wgrad_dma_w(a, e, k0, n0 + 32, lane, slab);
+    const float4 th1 = load_theta(n0 + 32);
+    wgrad_epilogue<WFMT, 0>(a, acc, e, k0, n0, lane, wv, tl.chunk, th0);
+    wait_vm<0>();
+    wgrad_read_w(slab, lane, wv);
+    wgrad_epilogue<WFMT, 1>(a, acc, e, k0, n0 + 32, lane, wv, tl.chunk, th1);
+    wait_lgkm0();
+  }
+  // every wave's staging in buffer 1 is done: stage 1 of the next tile
+  block_barrier();
+  if (next_w < 0) return 0;
+  return issue_next(std::integral_constant<int, 1>{}) ? 2 : 1;
+}
+
 // Persistent grid: one block per CU (the 128 KiB LDS ring allows one). The
 // hardware deals block b to XCD b % 8, so XCD x runs blocks x, x+8, ...; it
 // owns one contiguous eighth of the tile list and its blocks take tiles
@@ -765,11 +1015,16 @@ __global__ __launch_bounds__(NT) void k_grouped_gemm(GemmArgs a) {
   const int nslot = gridDim.x >> 3, xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
   const int chunk = (total + 7) >> 3;
   const int w_end = min((xcd + 1) * chunk, total);
-  bool pre = false;
+  int pre = 0;  // stages of the coming tile already in flight
   for (int w = xcd * chunk + slot; w < w_end; w += nslot) {
     const int next = w + nslot < w_end ? w + nslot : -1;
-    run_tile<MODE, WFMT>(a, tile_start, decode_tile<MODE>(a, tile_start, w), pre, next);
-    pre = next >= 0;
+    const Tile tl = decode_tile<MODE>(a, tile_start, w);
+    if (MODE == WGRAD) {
+      run_tile_lockstep<MODE, WFMT>(a, tile_start, tl, pre != 0, next);
+      pre = next >= 0;
+    } else {
+      pre = run_tile<MODE, WFMT>(a, tile_start, tl, pre, next);
+    }
   }
 }
 

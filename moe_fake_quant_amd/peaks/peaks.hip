@@ -1,0 +1,88 @@
+// Measured peaks of the part, for the benchmark's roofline context (not part
+// of the fake-quant path): a register-only chain of bf16 MFMAs and a plain
+// device copy. C ABI, launched on the caller's stream; the caller times them.
+#include <hip/hip_runtime.h>
+
+#include <stdint.h>
+
+namespace {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8v;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+
+__device__ __forceinline__ uint32_t mix(uint32_t x) {
+  x ^= x >> 16;
+  x *= 0x7feb352du;
+  x ^= x >> 15;
+  x *= 0x846ca68bu;
+  x ^= x >> 16;
+  return x;
+}
+
+// bf16 operand pair: varied values around 0.1 .. 1 with random signs
+// (random_data != 0), or all 1.0. The MFMA clock under load depends on the
+// operand bits, so both are reported.
+__device__ __forceinline__ uint32_t operand_word(uint32_t i, int random_data) {
+  if (!random_data) return 0x3f803f80u;
+  const uint32_t h = mix(i * 2654435761u + 12345u);
+  const uint32_t lo = (0x3dc0u + (h & 0x1ffu)) | (((h >> 18) & 1u) << 15);
+  const uint32_t hi = (0x3dc0u + ((h >> 9) & 0x1ffu)) | (((h >> 19) & 1u) << 15);
+  return lo | (hi << 16);
+}
+
+// 8 independent accumulators per wave, `iters` rounds of 8 MFMA 32x32x16
+__global__ __launch_bounds__(256) void k_mfma_chain(float *out, int iters, int random_data) {
+  uint32_t wa[4], wb[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    wa[i] = operand_word(threadIdx.x * 8u + i + blockIdx.x * 4096u, random_data);
+    wb[i] = operand_word(threadIdx.x * 8u + 4u + i + blockIdx.x * 4096u + 777u, random_data);
+  }
+  bf16x8v a, b;
+  __builtin_memcpy(&a, wa, 16);
+  __builtin_memcpy(&b, wb, 16);
+  f32x16 acc[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc[j][v] = 0.0f;
+  for (int it = 0; it < iters; ++it)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[j], 0, 0, 0);
+  float s = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) s += acc[j][0];
+  out[blockIdx.x * blockDim.x + threadIdx.x] = s;
+}
+
+// one 16-byte vector per thread
+__global__ __launch_bounds__(256) void k_copy16(const uint4 *__restrict__ src, uint4 *__restrict__ dst,
+                                                size_t n16) {
+  const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n16) dst[i] = src[i];
+}
+
+}  // namespace
+
+extern "C" {
+
+// flops = 32*32*16*2 * 8 * iters * blocks * 4 waves. out: blocks * 256 floats.
+int fqp_mfma_chain(float *out, int blocks, int iters, int random_data, void *stream) {
+  if (!out || blocks <= 0 || iters <= 0) return 1;
+  hipLaunchKernelGGL(k_mfma_chain, dim3(blocks), dim3(256), 0, (hipStream_t)stream, out, iters,
+                     random_data);
+  return hipGetLastError() == hipSuccess ? 0 : 4;
+}
+
+// bytes: a multiple of 16; src and dst 16-byte aligned device buffers
+int fqp_copy(const void *src, void *dst, size_t bytes, void *stream) {
+  if (!src || !dst || bytes % 16 != 0) return 1;
+  const size_t n16 = bytes / 16;
+  if (n16 == 0) return 0;
+  const size_t blocks = (n16 + 255) / 256;
+  hipLaunchKernelGGL(k_copy16, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream,
+                     (const uint4 *)src, (uint4 *)dst, n16);
+  return hipGetLastError() == hipSuccess ? 0 : 4;
+}
+
+}  // extern "C"

@@ -264,6 +264,38 @@ fq_status fq_moe_permute_noalloc(const int32_t *expert_ids, int32_t T, int32_t t
                                  int32_t *row_of, int32_t *seg_offsets, fq_stream stream);
 
 /* ------------------------------------------------------------------------
+ * fq_validate -- debug check of the device-data preconditions that the other
+ * calls assume and do not check (their host checks see only sizes and
+ * pointers): the quantizer's parameters are scales of a fake-quant grid
+ * (mcore_qad article, section 二.3) and must be usable as such, and the
+ * routing feeds one grouped GEMM over per-expert segments (section 二.4).
+ *   expert_ids [T, topk] (NULL: skipped): every id in [0, n_experts).
+ *   seg_offsets [E+1] (NULL: skipped): seg[0] == 0, non-decreasing,
+ *              0 <= seg[E] <= R_max.
+ *   wq (NULL: skipped), with shape: scales finite and > 0 (INT8 / INT4 /
+ *              FP8), NVFP4 theta finite and >= 0, zero points finite, NVFP4
+ *              global scales finite and > 0.
+ *   aq (NULL or fmt NONE: skipped): the activation scale finite and > 0.
+ *   status     one device uint32, overwritten with the OR of the FQ_BAD_*
+ *              bits of the failed conditions (0: all hold).
+ * The kernels only read their inputs: a bad input is reported, never
+ * faulted on. Enqueued on `stream`; read status after synchronizing. Host
+ * errors (NULL status, bad sizes) return before anything is enqueued.
+ * ---------------------------------------------------------------------- */
+#define FQ_BAD_EXPERT_ID 0x01u
+#define FQ_BAD_SEG_START 0x02u
+#define FQ_BAD_SEG_ORDER 0x04u
+#define FQ_BAD_SEG_END 0x08u
+#define FQ_BAD_SCALE 0x10u
+#define FQ_BAD_ZERO_POINT 0x20u
+#define FQ_BAD_GLOBAL_SCALE 0x40u
+#define FQ_BAD_ACT_SCALE 0x80u
+fq_status fq_validate(const int32_t *expert_ids, int32_t T, int32_t topk, int32_t n_experts,
+                      const int32_t *seg_offsets, int32_t E, int32_t R_max, fq_shape shape,
+                      const fq_weight_q *wq, const fq_act_q *aq, uint32_t *status,
+                      fq_stream stream);
+
+/* ------------------------------------------------------------------------
  * fq_grouped_gemm_fwd -- Y[r, :] = FQ_a(X)[r, :] . FQ_w(W[e])^T for every
  * routed row r in segment e = [seg_offsets[e], seg_offsets[e+1]), fp32
  * accumulation on bf16 MFMA, bf16 output (mcore_qad article, sections 二.3

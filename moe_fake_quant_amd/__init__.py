@@ -46,8 +46,17 @@ EXPORTED = (
     "fq_grouped_gemm_bwd_scale", "fq_moe_gather_actfq", "fq_swiglu_actfq", "fq_swiglu_bwd",
     "fq_moe_combine", "fq_moe_combine_bwd", "fq_moe_unpermute_reduce", "fq_workspace_bytes",
     "fq_last_error", "fq_abi_version", "fq_export_scales", "fq_dequantize_stacked", "fq_topk_kl",
-    "fq_moe_permute_noalloc",
+    "fq_moe_permute_noalloc", "fq_validate",
 )
+
+FQ_BAD_EXPERT_ID = 0x01
+FQ_BAD_SEG_START = 0x02
+FQ_BAD_SEG_ORDER = 0x04
+FQ_BAD_SEG_END = 0x08
+FQ_BAD_SCALE = 0x10
+FQ_BAD_ZERO_POINT = 0x20
+FQ_BAD_GLOBAL_SCALE = 0x40
+FQ_BAD_ACT_SCALE = 0x80
 
 
 class FQError(RuntimeError):
@@ -81,6 +90,8 @@ def _load() -> ctypes.CDLL:
         "fq_quantize_stacked": (st, [P, fq_shape, ctypes.POINTER(fq_weight_q), P, P, P]),
         "fq_moe_permute": (st, [P, I32, I32, I32, I32, P, P, P, P, SZ, P]),
         "fq_moe_permute_noalloc": (st, [P, I32, I32, I32, I32, P, P, P, P]),
+        "fq_validate": (st, [P, I32, I32, I32, P, I32, I32, fq_shape, ctypes.POINTER(fq_weight_q),
+                             ctypes.POINTER(fq_act_q), P, P]),
         "fq_grouped_gemm_fwd": (st, [P, I32, P, fq_shape, P, P, ctypes.POINTER(fq_weight_q),
                                      ctypes.POINTER(fq_act_q), P, P, SZ, P]),
         "fq_grouped_gemm_bwd_scale": (st, [P, P, I32, P, fq_shape, P, P,
@@ -201,6 +212,17 @@ def fq_moe_permute_noalloc(expert_ids, T, topk, expert_begin, E_local, perm, row
     _check(_lib.fq_moe_permute_noalloc(_p(expert_ids), int(T), int(topk), int(expert_begin),
                                        int(E_local), _p(perm), _p(row_of), _p(seg_offsets),
                                        _stream()))
+
+
+def fq_validate(status, expert_ids=None, T=0, topk=0, n_experts=0, seg_offsets=None, E=0,
+                R_max=0, shape=(1, 1, 1), wq: Optional[WeightQ] = None, aq: Optional[ActQ] = None):
+    """Enqueue the device-data checks; `status` (one int32/uint32 device
+    element) receives the OR of the FQ_BAD_* bits of failed conditions."""
+    _check(_lib.fq_validate(_p(expert_ids), int(T), int(topk), int(n_experts), _p(seg_offsets),
+                            int(E), int(R_max), _shape(*shape),
+                            ctypes.byref(wq.c()) if wq is not None else None,
+                            ctypes.byref(aq.c()) if aq is not None else None, _p(status),
+                            _stream()))
 
 
 def fq_grouped_gemm_fwd(x, R_max, seg_offsets, shape, w, w_fq, wq: Optional[WeightQ],

@@ -293,6 +293,33 @@ fq_status fq_moe_permute(const int32_t *ids, int32_t T, int32_t topk, int32_t eb
   return FQ_OK;
 }
 
+fq_status fq_validate(const int32_t *ids, int32_t T, int32_t topk, int32_t n_experts,
+                      const int32_t *seg, int32_t E, int32_t R_max, fq_shape s,
+                      const fq_weight_q *wq, const fq_act_q *aq, uint32_t *status,
+                      fq_stream stream) {
+  FQ_CHECK_ARG(status != nullptr, "status is NULL");
+  if (ids) FQ_CHECK_ARG(T >= 0 && topk > 0 && n_experts > 0, "bad routing sizes T=%d topk=%d n=%d",
+                        T, topk, n_experts);
+  if (seg) FQ_CHECK_ARG(E > 0 && R_max >= 0, "bad segment sizes E=%d R_max=%d", E, R_max);
+  long n_scale = 0;
+  int scale_mode = 0;
+  if (wq) {
+    FQ_TRY(check_shape(s));
+    FQ_TRY(check_weight_q(wq, s, true));
+    n_scale = wq->group == FQ_GROUP_TENSOR ? (long)s.E : (long)s.E * s.N * (s.K / wq->group);
+    scale_mode = wq->fmt == FQ_FMT_NVFP4 ? 1 : 0;
+  }
+  const bool act = aq && aq->fmt != FQ_FMT_NONE;
+  if (act) FQ_TRY(check_act_q(aq, 16));
+  launch_validate(ids, ids ? (long)T * topk : 0, n_experts, seg, E, R_max,
+                  wq ? wq->scale : nullptr, n_scale, scale_mode,
+                  wq && wq->fmt == FQ_FMT_INT4 ? wq->zero_point : nullptr,
+                  wq && wq->fmt == FQ_FMT_NVFP4 ? wq->global_scale : nullptr, wq ? s.E : 0,
+                  act ? aq->scale : nullptr, status, S(stream));
+  FQ_CHECK_LAUNCH("fq_validate");
+  return FQ_OK;
+}
+
 fq_status fq_moe_permute_noalloc(const int32_t *ids, int32_t T, int32_t topk, int32_t ebegin,
                                  int32_t E, int32_t *perm, int32_t *row_of, int32_t *seg,
                                  fq_stream stream) {

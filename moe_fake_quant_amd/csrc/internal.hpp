@@ -55,6 +55,12 @@ void launch_topk_kl(const uint16_t *student, const uint16_t *teacher, int T, int
                     bool reverse, const uint8_t *valid, int32_t *idx, float *grad, float *loss_tok,
                     float *loss_mean, float *inv_n, hipStream_t st);
 
+// device-data precondition checks: status = OR of FQ_BAD_* bits (cleared first)
+void launch_validate(const int32_t *ids, long n_ids, int n_experts, const int32_t *seg, int E,
+                     int R_max, const float *scale, long n_scale, int scale_mode,
+                     const float *zero_point, const float *gscale, int n_g, const float *act_scale,
+                     uint32_t *status, hipStream_t st);
+
 size_t permute_workspace_bytes(int E, long P);
 // Size of the permute scratch array the allocation-free entry point uses.
 constexpr size_t kPermuteScratchBytes = size_t(4) << 20;

@@ -54,3 +54,37 @@ def check_act_dscale_tol(gpu, ref, abs_terms, what="", tol=ACT_DSCALE_TOL):
     err = abs(float(gpu) - float(ref))
     assert err <= tol * abs_terms, f"{what}: |err| {err:.4g} > {tol} * {abs_terms:.4g}"
     return err / max(abs_terms, 1e-30)
+
+
+def dscale_p99(gpu, ref):
+    """99th percentile of the element-wise error |gpu - ref| / max|ref| (the
+    normwise check bounds its maximum; R-15 reports the percentile too)."""
+    g = np.asarray(gpu, np.float64).reshape(-1)
+    r = np.asarray(ref, np.float64).reshape(-1)
+    scale = np.abs(r).max() if r.size else 0.0
+    if scale == 0.0:
+        return 0.0
+    return float(np.percentile(np.abs(g - r), 99) / scale)
+
+
+def check_dscale_per_expert(gpu, ref, what=""):
+    """Normwise dScale tolerance for each expert's slice [e, ...] on its own
+    scale, so that an error in a cold expert cannot hide under the hottest
+    expert's magnitude; an expert whose reference is all zero must be exactly
+    zero. Prints the worst ratio and the tensor's p99 element-wise error."""
+    g = np.asarray(gpu, np.float64)
+    r = np.asarray(ref, np.float64)
+    worst = 0.0
+    for e in range(r.shape[0]):
+        se = np.abs(r[e]).max()
+        ee = np.abs(g[e] - r[e]).max()
+        if se == 0.0:
+            assert ee == 0.0, f"{what}: expert {e} reference is zero, gpu max|.| {ee:.4g}"
+            continue
+        assert ee <= DSCALE_TOL * se, \
+            f"{what}: expert {e} max|err| {ee:.4g} > {DSCALE_TOL} * {se:.4g}"
+        worst = max(worst, ee / se)
+    p99 = dscale_p99(g, r)
+    print(f"[dscale] {what}: worst per-expert max|err|/max|ref| {worst:.3g}, "
+          f"p99 element-wise |err|/max|ref| {p99:.3g}", flush=True)
+    return worst, p99

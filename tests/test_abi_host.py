@@ -210,6 +210,13 @@ def test_permute_and_elementwise_reject_bad_arguments(pkg):
     assert L.fq_moe_permute_noalloc(FAKE, 262144, 8, 0, 1024, FAKE, FAKE, FAKE, None) == \
         pkg.FQ_ERR_WORKSPACE_TOO_SMALL                                # 33.6 MB > 4 MiB
     assert b"static scratch" in L.fq_last_error()
+    S = pkg.fq_shape
+    assert L.fq_validate(None, 0, 0, 0, None, 0, 0, S(1, 1, 1), None, None, None, None) == \
+        pkg.FQ_ERR_INVALID_ARGUMENT                                   # no status word
+    assert L.fq_validate(FAKE, 16, 0, 8, None, 0, 0, S(1, 1, 1), None, None, FAKE, None) == \
+        pkg.FQ_ERR_INVALID_ARGUMENT                                   # routing with topk 0
+    assert L.fq_validate(None, 0, 0, 0, FAKE, 0, 10, S(1, 1, 1), None, None, FAKE, None) == \
+        pkg.FQ_ERR_INVALID_ARGUMENT                                   # segments of 0 experts
     assert L.fq_moe_gather_actfq(FAKE, 16, 40, FAKE, 8, None, FAKE, None) == \
         pkg.FQ_ERR_INVALID_ARGUMENT                                   # H % 16
     assert L.fq_moe_gather_actfq(FAKE, 16, 64, None, 8, None, FAKE, None) == \

@@ -26,7 +26,7 @@ import torch
 
 import oracle as O
 import workloads as W
-from helpers import (ACT_DSCALE_TOL, bf16_vals, check_act_dscale_tol, check_dscale_tol,
+from helpers import (ACT_DSCALE_TOL, bf16_vals, check_act_dscale_tol, check_dscale_tol, dscale_p99,
                      check_gemm_tol, dev_bf16, dev_f32, dev_i32, host_bits)
 
 pytestmark = pytest.mark.gpu
@@ -169,7 +169,9 @@ def test_moe_full_size_sampled(cfg, fmt, group):
             ch = _sample_channels(rng, w.shape[1])
             _, ref, _ = O.grouped_gemm_bwd(dy_all[lo:hi][:, ch], x_all[lo:hi], full,
                                            w[:, ch], fmt, grp, *_sub_q(q, [i], ch))
-            check_dscale_tol(ds[e][ch], ref[0], f"{name} e{e}")
+            rel = check_dscale_tol(ds[e][ch], ref[0], f"{name} e{e}")
+            print(f"[dscale] {name} e{e}: max|err|/max|ref| {rel:.3g}, p99 element-wise "
+                  f"{dscale_p99(ds[e][ch], ref[0]):.3g}", flush=True)
 
     # combine and unpermute-reduce on sampled tokens (GPU's O and dXq rows)
     tok = np.unique(np.concatenate([[0, T - 1], rng.choice(T, 256, replace=False)]))

@@ -8,8 +8,8 @@ import torch
 
 import oracle as O
 import workloads as W
-from helpers import (bf16_vals, check_dscale_tol, check_gemm_tol, dev_bf16, dev_f32, dev_i32,
-                     host_bits)
+from helpers import (bf16_vals, check_dscale_per_expert, check_dscale_tol, check_gemm_tol,
+                     dev_bf16, dev_f32, dev_i32, host_bits)
 
 pytestmark = pytest.mark.gpu
 
@@ -239,10 +239,12 @@ def test_gemm_fwd_prequantized_weights_match():
 # --------------------------------------------------- grouped GEMM backward --
 @pytest.mark.parametrize("name,fmt", FMTS)
 @pytest.mark.parametrize("afmt", [O.FMT_NONE, O.FMT_FP8, O.FMT_NVFP4])
-@pytest.mark.parametrize("grouping", ["default", "per_channel"])
+@pytest.mark.parametrize("grouping", ["default", "per_channel", "g16", "g32"])
 def test_gemm_bwd_parity(name, fmt, afmt, grouping):
     if grouping == "per_channel" and fmt in (O.FMT_NVFP4, O.FMT_INT4):
         pytest.skip("block / group formats")
+    if grouping in ("g16", "g32") and fmt == O.FMT_NVFP4:
+        pytest.skip("nvfp4 blocks are always 16")
     rng = np.random.default_rng(700 + 10 * fmt + afmt)
     E, N, K = 4, 256, 512
     sizes = [90, 0, 301, 33]
@@ -252,6 +254,8 @@ def test_gemm_bwd_parity(name, fmt, afmt, grouping):
     group = K if grouping == "per_channel" else _group(fmt, K)
     if fmt in (O.FMT_INT8, O.FMT_FP8) and grouping == "default":
         group = 64
+    if grouping in ("g16", "g32"):
+        group = int(grouping[1:])
     w = _rand_w(rng, E, N, K)
     s, zp, g = O.observer_weight(w, fmt, group)
     s = (s * rng.uniform(0.7, 1.1, s.shape)).astype(np.float32)
@@ -277,9 +281,48 @@ def test_gemm_bwd_parity(name, fmt, afmt, grouping):
     assert np.all(bf16_vals(dxb[R:]) == 7.0)
     dsh = ds.cpu().numpy()
     check_dscale_tol(dsh, ds_ref, "dscale")
+    check_dscale_per_expert(dsh, ds_ref, "dscale")
     assert np.all(dsh[1] == 0)                         # empty expert
     if dzp is not None:
         check_dscale_tol(dzp.cpu().numpy(), dzp_ref, "dzero_point")
+        check_dscale_per_expert(dzp.cpu().numpy(), dzp_ref, "dzero_point")
+
+
+@pytest.mark.parametrize("name,fmt,group", [("nvfp4", O.FMT_NVFP4, 16), ("int4", O.FMT_INT4, 128),
+                                            ("int4_g16", O.FMT_INT4, 16),
+                                            ("int8_g32", O.FMT_INT8, 32),
+                                            ("fp8_pc", O.FMT_FP8, 256)])
+def test_gemm_bwd_rows_beyond_one_chunk(name, fmt, group):
+    """Experts above 2048 routed rows: the wgrad contraction runs in row chunks
+    whose partial sums per block are added in chunk order afterwards. Both
+    hot experts' dScale (and dZP) and dX against the oracle, per expert."""
+    rng = np.random.default_rng(900 + fmt + group)
+    E, N, K = 4, 256, 256
+    sizes = [2600, 0, 4500, 37]                       # 2 and 3 chunks, empty, ragged
+    seg = _segments(rng, E, sizes)
+    R = int(seg[-1])
+    w = _rand_w(rng, E, N, K)
+    s, zp, g = O.observer_weight(w, fmt, group)
+    s = (s * rng.uniform(0.7, 1.1, s.shape)).astype(np.float32)
+    x = O.f32_to_bf16(rng.standard_normal((R, K)).astype(np.float32))
+    dy = O.f32_to_bf16(rng.standard_normal((R, N)).astype(np.float32))
+    dx_ref, ds_ref, dzp_ref = O.grouped_gemm_bwd(dy, x, seg, w, fmt, group, s, zp, g)
+    wq = _wq(fmt, group, s, zp, g)
+    G = K // group
+    dx = torch.empty((R, K), dtype=torch.bfloat16, device="cuda")
+    ds = torch.full((E, N, G), 7.0, device="cuda")
+    dzp = torch.full((E, N, G), 7.0, device="cuda") if fmt == O.FMT_INT4 else None
+    ws = torch.empty(F.fq_workspace_bytes(F.FQ_OP_GEMM_BWD, (E, N, K), R, fmt), dtype=torch.uint8,
+                     device="cuda")
+    F.fq_grouped_gemm_bwd_scale(dev_bf16(dy), dev_bf16(x), R, dev_i32(seg), (E, N, K),
+                                dev_bf16(w), None, wq, None, dx, ds, dzp, ws)
+    torch.cuda.synchronize()
+    check_gemm_tol(host_bits(dx), dx_ref, "dx")
+    dsh = ds.cpu().numpy()
+    check_dscale_per_expert(dsh, ds_ref, "dscale")
+    assert np.all(dsh[1] == 0)
+    if dzp is not None:
+        check_dscale_per_expert(dzp.cpu().numpy(), dzp_ref, "dzero_point")
 
 
 @pytest.mark.parametrize("name,fmt", [("int8", O.FMT_INT8), ("fp8", O.FMT_FP8)])

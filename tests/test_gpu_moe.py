@@ -8,8 +8,8 @@ import torch
 
 import oracle as O
 import workloads as W
-from helpers import (bf16_vals, check_act_dscale_tol, check_dscale_tol, check_gemm_tol, dev_bf16,
-                     dev_f32, dev_i32, host_bits)
+from helpers import (bf16_vals, check_act_dscale_tol, check_dscale_per_expert, check_dscale_tol,
+                     check_gemm_tol, dev_bf16, dev_f32, dev_i32, host_bits)
 
 pytestmark = pytest.mark.gpu
 
@@ -99,15 +99,19 @@ def test_moe_layer_stagewise_and_end_to_end(name, wfmt, afmt, group, T, Eg, El, 
     daq = host_bits(L.daq)[:R]
     check_gemm_tol(daq, daq_ref, "daq")
     check_dscale_tol(L.ds_d.cpu().numpy(), ds_d_ref, "ds_d")
+    check_dscale_per_expert(L.ds_d.cpu().numpy(), ds_d_ref, "ds_d")
     dh = host_bits(L.dh)[:R]
     check_gemm_tol(dh, O.swiglu_bwd(daq, h, afmt, s2, a_bits=a), "dh")
     dxq_ref, ds_gu_ref, dzp_gu_ref = O.grouped_gemm_bwd(dh, xq, seg, case.w_gu, wfmt, g_gu, *wq_gu)
     dxq = host_bits(L.dxq)[:R]
     check_gemm_tol(dxq, dxq_ref, "dxq")
     check_dscale_tol(L.ds_gu.cpu().numpy(), ds_gu_ref, "ds_gu")
+    check_dscale_per_expert(L.ds_gu.cpu().numpy(), ds_gu_ref, "ds_gu")
     if wfmt == O.FMT_INT4:
         check_dscale_tol(L.dzp_gu.cpu().numpy(), dzp_gu_ref, "dzp_gu")
         check_dscale_tol(L.dzp_d.cpu().numpy(), dzp_d_ref, "dzp_d")
+        check_dscale_per_expert(L.dzp_gu.cpu().numpy(), dzp_gu_ref, "dzp_gu")
+        check_dscale_per_expert(L.dzp_d.cpu().numpy(), dzp_d_ref, "dzp_d")
     dx = host_bits(L.dx)[:T]
     check_gemm_tol(dx, O.unpermute_reduce(dxq, row_of, case.x, afmt, s1), "dx")
     if learn:

@@ -364,6 +364,9 @@ def main():
                  "fq_moe_unpermute_reduce"):
         setattr(LM, name, timer.wrap(keys.get(name, lambda a, n=name: n), getattr(LM, name)))
 
+    # FQ_BENCH_OVERLAP=0 keeps the wgrad calls on the launch stream (an A/B switch)
+    layer.overlap_wgrad = os.environ.get("FQ_BENCH_OVERLAP", "1") != "0"
+    overlap = layer.overlap_wgrad
     step = lambda: layer.step(x, ids, probs, dout)  # noqa: E731
     for _ in range(args.warmup):
         step()
@@ -374,11 +377,15 @@ def main():
     timer.enabled = False
     ms_step, wall = time_steps(torch, step, args.steps)
 
-    # breakdown: a separate pass with events around each call
+    # breakdown: a separate pass with events around each call, the backward's
+    # wgrad calls serialized on the launch stream so that every call's events
+    # bracket its kernels alone
     nb = max(args.breakdown_steps, 1)
+    layer.overlap_wgrad = False
     timer.enabled = True
     ms_step_instr, _ = time_steps(torch, step, nb)
     timer.enabled = False
+    layer.overlap_wgrad = overlap
     per = timer.collect()
 
     flops_step = FLOPS_PER_ROW * R
@@ -480,7 +487,9 @@ def main():
             "frac": round(achieved / MI355X_BF16_PEAK_TFLOPS, 4),
             "traffic": traffic,
         },
-        "timing": {"headline": "HIP events around the timed steps, no per-call events",
+        "timing": {"headline": "HIP events around the timed steps, no per-call events; the wgrad "
+                               "calls on a second stream",
+                   "breakdown": "a separate pass with events around each call, all on one stream",
                    "breakdown_steps": nb, "breakdown_ms_per_step": round(ms_step_instr, 4)},
         "gemm_kernels": kernels,
         "gemm_only": {"ms_per_step": round(gemm_ms, 4),

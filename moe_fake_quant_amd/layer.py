@@ -15,6 +15,12 @@ Activation scales are frozen after calibration unless ``learn_act_scales``
 (FP8 / INT8 activations), in which case the backward also returns their
 gradients in ``ds_a1`` (input of gate_up) and ``ds_a2`` (input of down).
 All buffers are allocated once; a step allocates nothing.
+
+With ``overlap_wgrad`` (the default) the two wgrad -> dScale calls run on a
+second stream of the same priority, each behind the producer of its inputs,
+while the dgrad chain continues on the caller's stream: their persistent
+grids then take over the CUs that a dgrad kernel's last partial round of
+tiles leaves idle. The second stream has a workspace of its own.
 """
 from __future__ import annotations
 
@@ -103,6 +109,11 @@ class MoEFakeQuantLayer:
                  fq_workspace_bytes(FQ_OP_GEMM_BWD, self.shape_gu, R, 0),
                  fq_workspace_bytes(FQ_OP_GEMM_BWD, self.shape_d, R, 0), 256)
         self.ws = torch.empty(ws, dtype=torch.uint8, device=self.dev)
+        self.ws2 = torch.empty(ws, dtype=torch.uint8, device=self.dev)
+        self.side = torch.cuda.Stream(device=self.dev)   # default priority
+        self.ev_do = torch.cuda.Event()
+        self.ev_dh = torch.cuda.Event()
+        self.overlap_wgrad = True
         self.T = 0
 
     # ------------------------------------------------------------- setup --
@@ -178,23 +189,47 @@ class MoEFakeQuantLayer:
         fq_moe_combine(self.t_o, probs, self.row_of[:T], T, self.topk, self.H, self.t_out[:T])
         return self.t_out[:T]
 
+    def _wgrad(self, ready, dy, x_rows, shape, w, wfq, q, ds, dzp):
+        """wgrad -> dScale of one stack: on the side stream once event `ready`
+        (recorded right after dy's producer) has passed (overlap_wgrad), else
+        inline on the caller's stream."""
+        if not self.overlap_wgrad:
+            fq_grouped_gemm_bwd_scale(dy, x_rows, self.R_max, self.seg, shape, w, wfq, q, None,
+                                      None, ds, dzp, self.ws)
+            return
+        self.side.wait_event(ready)
+        with torch.cuda.stream(self.side):
+            fq_grouped_gemm_bwd_scale(dy, x_rows, self.R_max, self.seg, shape, w, wfq, q, None,
+                                      None, ds, dzp, self.ws2)
+
     def backward(self, x: torch.Tensor, probs: torch.Tensor, dout: torch.Tensor):
         T = x.shape[0]
+        main = torch.cuda.current_stream(self.dev)
+        if self.overlap_wgrad:
+            # the side stream's previous step (and anything else the caller
+            # enqueued before this backward) is complete before it reuses ws2
+            self.side.wait_stream(main)
         fq_moe_combine_bwd(dout, probs, self.row_of[:T], T, self.topk, self.H, self.do)
-        # dgrad and wgrad -> dScale as two calls (one GEMM kernel each)
+        self.ev_do.record(main)
+        # dgrad and wgrad -> dScale as separate calls (one GEMM kernel each);
+        # the dgrad is enqueued first: it leads the chain to dX
         fq_grouped_gemm_bwd_scale(self.do, self.aq, self.R_max, self.seg, self.shape_d, self.w_d,
                                   self.wfq_d, self.q_d, None, self.daq, None, None, self.ws)
-        fq_grouped_gemm_bwd_scale(self.do, self.aq, self.R_max, self.seg, self.shape_d, self.w_d,
-                                  self.wfq_d, self.q_d, None, None, self.ds_d, self.dzp_d, self.ws)
+        self._wgrad(self.ev_do, self.do, self.aq, self.shape_d, self.w_d, self.wfq_d, self.q_d,
+                    self.ds_d, self.dzp_d)
         fq_swiglu_bwd(self.daq, self.h, self.R_max, self.n_rows, self.F, self.aq2, self.dh,
                       self.ds_a2, self.ws)
+        self.ev_dh.record(main)
         fq_grouped_gemm_bwd_scale(self.dh, self.xq, self.R_max, self.seg, self.shape_gu, self.w_gu,
                                   self.wfq_gu, self.q_gu, None, self.dxq, None, None, self.ws)
-        fq_grouped_gemm_bwd_scale(self.dh, self.xq, self.R_max, self.seg, self.shape_gu, self.w_gu,
-                                  self.wfq_gu, self.q_gu, None, None, self.ds_gu, self.dzp_gu,
-                                  self.ws)
+        self._wgrad(self.ev_dh, self.dh, self.xq, self.shape_gu, self.w_gu, self.wfq_gu, self.q_gu,
+                    self.ds_gu, self.dzp_gu)
         fq_moe_unpermute_reduce(self.dxq, self.row_of[:T], x, T, self.topk, self.H, self.aq1,
                                 self.dx[:T], self.ds_a1, self.ws)
+        if self.overlap_wgrad:
+            # the caller's stream sees both dScale results, and the next step's
+            # forward cannot overwrite xq / aq / do / dh under a wgrad still running
+            main.wait_stream(self.side)
         return self.dx[:T], self.ds_gu, self.ds_d
 
     def step(self, x, expert_ids, probs, dout):

@@ -264,6 +264,37 @@ def measured_peaks(torch, dev):
             "copy_pct_of_spec": round(100 * copy_gbs / MI355X_HBM_PEAK_GBS, 1)}
 
 
+def scattered_rows_floor(torch, dev, rows, row_of, T, topk, H):
+    """The floor of the per-token reductions over routed rows (combine,
+    unpermute-reduce): a plain kernel with their access pattern (per token
+    row written, its topk routed rows read at the real routing positions, 16
+    bytes per thread) timed on the same buffers. Bytes = 2RH + 2TH + 4Tk."""
+    import ctypes
+    lib_path = os.path.join(ROOT, "moe_fake_quant_amd", "libfqpeaks.so")
+    if not os.path.exists(lib_path):
+        return None
+    lib = ctypes.CDLL(lib_path)
+    lib.fqp_scattered_rows.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+                                       ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    st = torch.cuda.current_stream().cuda_stream
+    out = torch.empty(T, H, dtype=torch.bfloat16, device=dev)
+    args = (rows.data_ptr(), row_of.data_ptr(), T, topk, 2 * H, out.data_ptr(), st)
+    assert lib.fqp_scattered_rows(*args) == 0
+    torch.cuda.synchronize()
+    s0 = torch.cuda.Event(enable_timing=True)
+    e0 = torch.cuda.Event(enable_timing=True)
+    s0.record()
+    for _ in range(10):
+        assert lib.fqp_scattered_rows(*args) == 0
+    e0.record()
+    torch.cuda.synchronize()
+    ms = s0.elapsed_time(e0) / 10
+    R = int((row_of[:T] >= 0).sum().item())
+    nbytes = 2 * R * H + 2 * T * H + 4 * T * topk
+    del out
+    return {"ms": round(ms, 4), "bytes": nbytes, "GB/s": round(nbytes / (ms * 1e-3) / 1e9, 1)}
+
+
 def host_description():
     """CPU model and the cores this process may run on (the GPU machine's host)."""
     model = None
@@ -433,6 +464,15 @@ def main():
     gemm_ms = sum(kernels[k]["ms_per_step"] for k in kernels)
 
     breakdown = {n: round(sum(v) / nb, 4) for n, v in sorted(per.items())}
+    floor = None if args.no_peaks else scattered_rows_floor(torch, dev, layer.o, layer.row_of,
+                                                            case.T, case.topk, H)
+    if floor:
+        for name in ("fq_moe_combine", "fq_moe_unpermute_reduce"):
+            if name in passes:
+                passes[name]["pct_of_scattered_rows_floor"] = round(
+                    100 * passes[name]["GB/s"] / floor["GB/s"], 1)
+        if peaks is not None:
+            peaks["scattered_rows_GB/s"] = floor["GB/s"]
 
     if args.copy_calibration_mb > 0:
         n = args.copy_calibration_mb * (1 << 20) // 4

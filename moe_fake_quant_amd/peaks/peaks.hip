@@ -62,6 +62,29 @@ __global__ __launch_bounds__(256) void k_copy16(const uint4 *__restrict__ src, u
   if (i < n16) dst[i] = src[i];
 }
 
+// out[t] = XOR over the routed rows r = row_of[t, j] (j < topk, r >= 0) of
+// rows[r]: the access pattern of the per-token reductions over routed rows
+// (topk scattered row reads per row written), 16 bytes per thread, with no
+// arithmetic to speak of.
+__global__ __launch_bounds__(256) void k_scattered_rows(const uint4 *__restrict__ rows,
+                                                        const int32_t *__restrict__ row_of, int T,
+                                                        int topk, int cpr, uint4 *__restrict__ out) {
+  const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= (size_t)T * cpr) return;
+  const int t = (int)(i / cpr), c = (int)(i - (size_t)t * cpr);
+  uint4 acc = make_uint4(0u, 0u, 0u, 0u);
+  for (int j = 0; j < topk; ++j) {
+    const int r = row_of[(size_t)t * topk + j];
+    if (r < 0) continue;
+    const uint4 v = rows[(size_t)r * cpr + c];
+    acc.x ^= v.x;
+    acc.y ^= v.y;
+    acc.z ^= v.z;
+    acc.w ^= v.w;
+  }
+  out[i] = acc;
+}
+
 }  // namespace
 
 extern "C" {
@@ -82,6 +105,20 @@ int fqp_copy(const void *src, void *dst, size_t bytes, void *stream) {
   const size_t blocks = (n16 + 255) / 256;
   hipLaunchKernelGGL(k_copy16, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream,
                      (const uint4 *)src, (uint4 *)dst, n16);
+  return hipGetLastError() == hipSuccess ? 0 : 4;
+}
+
+// rows: [R, row_bytes] with R > every row_of entry; out: [T, row_bytes];
+// row_bytes a multiple of 16
+int fqp_scattered_rows(const void *rows, const int32_t *row_of, int T, int topk, int row_bytes,
+                       void *out, void *stream) {
+  if (!rows || !row_of || !out || T < 0 || topk <= 0 || row_bytes <= 0 || row_bytes % 16 != 0)
+    return 1;
+  const int cpr = row_bytes / 16;
+  const size_t n = (size_t)T * cpr;
+  if (n == 0) return 0;
+  hipLaunchKernelGGL(k_scattered_rows, dim3((unsigned)((n + 255) / 256)), dim3(256), 0,
+                     (hipStream_t)stream, (const uint4 *)rows, row_of, T, topk, cpr, (uint4 *)out);
   return hipGetLastError() == hipSuccess ? 0 : 4;
 }
 

@@ -311,8 +311,12 @@ fq_status fq_validate(const int32_t *expert_ids, int32_t T, int32_t topk, int32_
  *           article, section 一).
  *   aq      activation quantizer applied to x first (NULL = NONE).
  *   y_bf16  [R_max, N].
- * Requires N % 256 == 0 and K % 64 == 0 (K % 16 for nvfp4 activations).
- * Workspace: fq_workspace_bytes(FQ_OP_GEMM_FWD, shape, R_max, wq->fmt | aq->fmt << 8).
+ * Requires N % 16 == 0 and K % 16 == 0. The kernels work on N % 256 == 0,
+ * K % 64 == 0; other shapes run on zero-padded copies of W_fq, x and y in
+ * the workspace (the padded K columns add nothing, the padded N rows are
+ * not copied back), at the cost of those copies.
+ * Workspace: fq_workspace_bytes(FQ_OP_GEMM_FWD, shape, R_max, wq->fmt | aq->fmt << 8)
+ * (0 for a tile-aligned shape with w_fq given and no activation FQ).
  * ---------------------------------------------------------------------- */
 fq_status fq_grouped_gemm_fwd(const uint16_t *x_bf16, int32_t R_max, const int32_t *seg_offsets,
                               fq_shape shape, const uint16_t *w_bf16, const uint16_t *w_fq,
@@ -337,8 +341,13 @@ fq_status fq_grouped_gemm_fwd(const uint16_t *x_bf16, int32_t R_max, const int32
  * contracted in chunks of at most 2048, each chunk's partial sums summed in
  * chunk order.
  *   dy_bf16 [R_max, N]; x_bf16 [R_max, K] raw (pre activation fake-quant).
- * Requires N % 256 == 0 and K % 256 == 0; for dScale a group of 16, 32, 64
- * or a multiple of 128, and (nvfp4) theta 16-byte aligned.
+ * Requires N % 16 == 0 and K % 16 == 0; for dScale a group of 16, 32, 64
+ * or a multiple of 128 (a per-channel group may be any K), and (nvfp4) theta
+ * 16-byte aligned. The kernels work on N % 256 == 0, K % 256 == 0; other
+ * shapes run on zero-padded copies in the workspace (a padded weight element
+ * is 0 with a neutral scale: 1 on the integer / FP8 grids, theta 0 for
+ * NVFP4, zero point 0, so its straight-through factor is 0), and only the
+ * call's own region of dx, dscale and dzero_point is written.
  * Workspace: fq_workspace_bytes(FQ_OP_GEMM_BWD, shape, R_max, wq->fmt | aq->fmt << 8).
  * ---------------------------------------------------------------------- */
 fq_status fq_grouped_gemm_bwd_scale(const uint16_t *dy_bf16, const uint16_t *x_bf16,

@@ -110,7 +110,25 @@ inline hipStream_t S(fq_stream s) { return reinterpret_cast<hipStream_t>(s); }
     if (st_ != FQ_OK) return st_;    \
   } while (0)
 
-size_t gemm_ws(int op, fq_shape s, int R_max, int fmts) {
+// The shape the GEMM kernels run on: N a multiple of 256, K of 64 (forward)
+// or 256 (backward). Other shapes (multiples of 16) run zero-padded to it.
+fq_shape gemm_pad_shape(int op, fq_shape s) {
+  fq_shape p = s;
+  p.N = (s.N + 255) / 256 * 256;
+  const int kq = op == FQ_OP_GEMM_FWD ? 64 : 256;
+  p.K = (s.K + kq - 1) / kq * kq;
+  return p;
+}
+bool gemm_needs_pad(int op, fq_shape s) {
+  const fq_shape p = gemm_pad_shape(op, s);
+  return p.N != s.N || p.K != s.K;
+}
+// a per-channel scale (group = K) spans the padded row
+int padded_group(int group, fq_shape s, fq_shape p) {
+  return group == s.K ? p.K : group;
+}
+
+size_t gemm_ws_core(int op, fq_shape s, int R_max, int fmts) {
   int wfmt = fmts & 0xFF, afmt = (fmts >> 8) & 0xFF;
   size_t b = 0;
   if (wfmt != FQ_FMT_NONE) b += align_up((size_t)s.E * s.N * s.K * 2);
@@ -125,6 +143,26 @@ size_t gemm_ws(int op, fq_shape s, int R_max, int fmts) {
     b += 2 * align_up((size_t)s.E * s.N * 4);
   }
   return b;
+}
+
+// Padded shapes: the call's own W_fq (if materialized), the zero-padded
+// operands, outputs and scales, then the padded problem's own workspace.
+size_t gemm_ws(int op, fq_shape s, int R_max, int fmts) {
+  if (!gemm_needs_pad(op, s)) return gemm_ws_core(op, s, R_max, fmts);
+  const fq_shape p = gemm_pad_shape(op, s);
+  const int wfmt = fmts & 0xFF, afmt = (fmts >> 8) & 0xFF;
+  const size_t E = (size_t)s.E, Rm = (size_t)(R_max > 0 ? R_max : 0);
+  size_t b = 0;
+  if (wfmt != FQ_FMT_NONE) b += align_up(E * s.N * s.K * 2);   // W_fq at the call's shape
+  b += align_up(E * p.N * p.K * 2);                             // padded W_fq
+  b += align_up(Rm * p.K * 2);                                  // padded x
+  b += align_up(Rm * p.N * 2);                                  // padded y / dy
+  if (op == FQ_OP_GEMM_BWD) {
+    b += align_up(E * p.N * p.K * 2);                           // padded raw w
+    b += align_up(Rm * p.K * 2);                                // padded dx
+    b += 4 * align_up(E * p.N * (p.K / 16) * 4);                // scale, zp, dscale, dzp
+  }
+  return b + gemm_ws_core(op, p, R_max, wfmt | (afmt << 8));
 }
 
 // A learnable activation scale's gradient: only the static per-tensor formats
@@ -341,33 +379,14 @@ fq_status fq_moe_permute_noalloc(const int32_t *ids, int32_t T, int32_t topk, in
   return FQ_OK;
 }
 
-fq_status fq_grouped_gemm_fwd(const uint16_t *x, int32_t R_max, const int32_t *seg, fq_shape s,
-                              const uint16_t *w, const uint16_t *w_fq, const fq_weight_q *wq,
-                              const fq_act_q *aq, uint16_t *y, void *ws, size_t ws_bytes,
-                              fq_stream stream) {
-  FQ_TRY(check_shape(s));
-  FQ_CHECK_ARG(R_max >= 0, "R_max < 0");
-  FQ_CHECK_ARG(seg && y && (x || R_max == 0), "x, seg_offsets and y must be non-NULL");
-  FQ_CHECK_ARG(w || w_fq, "w or w_fq must be non-NULL");
-  FQ_CHECK_ARG(wq || w_fq, "wq may be NULL only with w_fq (weights used as given)");
-  if (wq) FQ_TRY(check_weight_q(wq, s, w_fq == nullptr));
-  FQ_TRY(check_act_q(aq, s.K));
-  FQ_CHECK_SUPPORTED(s.N % 256 == 0 && s.K % 64 == 0,
-                     "grouped GEMM forward needs N %% 256 == 0 and K %% 64 == 0 (N=%d K=%d)", s.N, s.K);
-  FQ_CHECK_SUPPORTED(s.E <= 1024, "grouped GEMM supports up to 1024 experts per stack (E=%d)", s.E);
-  FQ_CHECK_SUPPORTED((size_t)R_max * s.K * 2 < (1ull << 32) && (size_t)s.N * s.K * 2 < (1ull << 32),
-                     "operands must stay below 4 GiB (32-bit tile offsets)");
-  FQ_CHECK_ARG((!x || aligned16(x)) && aligned16(y) && (!w || aligned16(w)) &&
-                   (!w_fq || aligned16(w_fq)),
-               "bf16 tensors must be 16-byte aligned");
+namespace {
+
+// The forward on a shape the kernels take (N % 256 == 0, K % 64 == 0);
+// arguments already checked, workspace large enough.
+void gemm_fwd_core(const uint16_t *x, int R_max, const int32_t *seg, fq_shape s, const uint16_t *w,
+                   const uint16_t *w_fq, const fq_weight_q *wq, const fq_act_q *aq, uint16_t *y,
+                   void *ws, hipStream_t st) {
   const int afmt = act_fmt(aq);
-  size_t need = gemm_ws(FQ_OP_GEMM_FWD, s, R_max,
-                        (w_fq ? 0 : wq->fmt) | (afmt << 8));
-  if (need > 0 && (ws_bytes < need || !ws)) {
-    set_error("fq_grouped_gemm_fwd: workspace %zu bytes < %zu needed", ws_bytes, need);
-    return FQ_ERR_WORKSPACE_TOO_SMALL;
-  }
-  hipStream_t st = S(stream);
   Carver c(ws);
   const uint16_t *wfq = w_fq;
   if (!wfq) {
@@ -382,48 +401,74 @@ fq_status fq_grouped_gemm_fwd(const uint16_t *x, int32_t R_max, const int32_t *s
     xq = t;
   }
   launch_gemm_fwd(xq, R_max, seg, s, wfq, y, st);
+}
+
+}  // namespace
+
+fq_status fq_grouped_gemm_fwd(const uint16_t *x, int32_t R_max, const int32_t *seg, fq_shape s,
+                              const uint16_t *w, const uint16_t *w_fq, const fq_weight_q *wq,
+                              const fq_act_q *aq, uint16_t *y, void *ws, size_t ws_bytes,
+                              fq_stream stream) {
+  FQ_TRY(check_shape(s));
+  FQ_CHECK_ARG(R_max >= 0, "R_max < 0");
+  FQ_CHECK_ARG(seg && y && (x || R_max == 0), "x, seg_offsets and y must be non-NULL");
+  FQ_CHECK_ARG(w || w_fq, "w or w_fq must be non-NULL");
+  FQ_CHECK_ARG(wq || w_fq, "wq may be NULL only with w_fq (weights used as given)");
+  if (wq) FQ_TRY(check_weight_q(wq, s, w_fq == nullptr));
+  FQ_TRY(check_act_q(aq, s.K));
+  FQ_CHECK_SUPPORTED(s.N % 16 == 0 && s.K % 16 == 0,
+                     "grouped GEMM needs N %% 16 == 0 and K %% 16 == 0 (N=%d K=%d)", s.N, s.K);
+  FQ_CHECK_SUPPORTED(s.E <= 1024, "grouped GEMM supports up to 1024 experts per stack (E=%d)", s.E);
+  const fq_shape p = gemm_pad_shape(FQ_OP_GEMM_FWD, s);
+  FQ_CHECK_SUPPORTED((size_t)R_max * p.K * 2 < (1ull << 32) && (size_t)p.N * p.K * 2 < (1ull << 32),
+                     "operands must stay below 4 GiB (32-bit tile offsets)");
+  FQ_CHECK_ARG((!x || aligned16(x)) && aligned16(y) && (!w || aligned16(w)) &&
+                   (!w_fq || aligned16(w_fq)),
+               "bf16 tensors must be 16-byte aligned");
+  const int afmt = act_fmt(aq);
+  const int fmts = (w_fq ? 0 : wq->fmt) | (afmt << 8);
+  size_t need = gemm_ws(FQ_OP_GEMM_FWD, s, R_max, fmts);
+  if (need > 0 && (ws_bytes < need || !ws)) {
+    set_error("fq_grouped_gemm_fwd: workspace %zu bytes < %zu needed", ws_bytes, need);
+    return FQ_ERR_WORKSPACE_TOO_SMALL;
+  }
+  hipStream_t st = S(stream);
+  if (!gemm_needs_pad(FQ_OP_GEMM_FWD, s)) {
+    gemm_fwd_core(x, R_max, seg, s, w, w_fq, wq, aq, y, ws, st);
+    FQ_CHECK_LAUNCH("fq_grouped_gemm_fwd");
+    return FQ_OK;
+  }
+  // zero-padded to the kernels' shape: padded K columns add nothing, padded
+  // N rows give outputs that are not copied back
+  Carver c(ws);
+  const uint16_t *wfq = w_fq;
+  if (!wfq) {
+    uint16_t *t = c.take<uint16_t>((size_t)s.E * s.N * s.K * 2);
+    launch_quantize_stacked(w, s, as_groups(*wq, s), t, nullptr, st);
+    wfq = t;
+  }
+  uint16_t *wfq_p = c.take<uint16_t>((size_t)s.E * p.N * p.K * 2);
+  launch_reshape_u16(wfq, s.E, s.N, s.K, wfq_p, p.N, p.K, nullptr, st);
+  uint16_t *x_p = c.take<uint16_t>((size_t)R_max * p.K * 2);
+  uint16_t *y_p = c.take<uint16_t>((size_t)R_max * p.N * 2);
+  if (R_max > 0) launch_reshape_u16(x, 1, R_max, s.K, x_p, R_max, p.K, seg + s.E, st);
+  gemm_fwd_core(x_p, R_max, seg, p, nullptr, wfq_p, nullptr, aq, y_p, c.base + c.used, st);
+  if (R_max > 0) launch_reshape_u16(y_p, 1, R_max, p.N, y, R_max, s.N, seg + s.E, st);
   FQ_CHECK_LAUNCH("fq_grouped_gemm_fwd");
   return FQ_OK;
 }
 
-fq_status fq_grouped_gemm_bwd_scale(const uint16_t *dy, const uint16_t *x, int32_t R_max,
-                                    const int32_t *seg, fq_shape s, const uint16_t *w,
-                                    const uint16_t *w_fq, const fq_weight_q *wq, const fq_act_q *aq,
-                                    uint16_t *dx, float *dscale, float *dzp, void *ws,
-                                    size_t ws_bytes, fq_stream stream) {
-  FQ_TRY(check_shape(s));
-  FQ_CHECK_ARG(R_max >= 0, "R_max < 0");
-  FQ_CHECK_ARG(seg != nullptr, "seg_offsets is NULL");
-  FQ_CHECK_ARG(dy || R_max == 0, "dy is NULL");
+namespace {
+
+// The backward on a shape the kernels take (N % 256 == 0, K % 256 == 0);
+// arguments already checked, workspace large enough.
+void gemm_bwd_core(const uint16_t *dy, const uint16_t *x, int R_max, const int32_t *seg, fq_shape s,
+                   const uint16_t *w, const uint16_t *w_fq, const fq_weight_q *wq,
+                   const fq_act_q *aq, uint16_t *dx, float *dscale, float *dzp, void *ws,
+                   hipStream_t st) {
   const bool want_ds = dscale || dzp;
-  FQ_TRY(check_weight_q(wq, s, true));
-  FQ_TRY(check_act_q(aq, s.K));
-  FQ_CHECK_ARG(w != nullptr, "w (raw weights) is NULL");
-  FQ_CHECK_ARG(!want_ds || x || R_max == 0, "x is NULL");
-  FQ_CHECK_ARG(!dzp || wq->fmt == FQ_FMT_INT4, "dzero_point only exists for int4");
-  FQ_CHECK_ARG(!dzp || dscale, "dzero_point needs dscale too");
-  FQ_CHECK_SUPPORTED(s.N % 256 == 0 && s.K % 256 == 0,
-                     "grouped GEMM backward needs N %% 256 == 0 and K %% 256 == 0 (N=%d K=%d)", s.N,
-                     s.K);
-  FQ_CHECK_SUPPORTED(s.E <= 1024, "grouped GEMM supports up to 1024 experts per stack (E=%d)", s.E);
-  FQ_CHECK_SUPPORTED((size_t)R_max * (s.K > s.N ? s.K : s.N) * 2 < (1ull << 32) &&
-                         (size_t)s.N * s.K * 2 < (1ull << 32),
-                     "operands must stay below 4 GiB (32-bit tile offsets)");
   const bool per_tensor = wq->group == FQ_GROUP_TENSOR;
-  FQ_CHECK_SUPPORTED(!want_ds || per_tensor || group_ok_for_dscale(wq->group),
-                     "dScale needs group 16, 32, 64 or a multiple of 128 (group=%d)", wq->group);
-  FQ_CHECK_ARG(!want_ds || wq->fmt != FQ_FMT_NVFP4 || aligned16(wq->scale),
-               "nvfp4 theta must be 16-byte aligned");
-  FQ_CHECK_ARG((!dy || aligned16(dy)) && (!x || aligned16(x)) && aligned16(w) &&
-                   (!w_fq || aligned16(w_fq)) && (!dx || aligned16(dx)),
-               "bf16 tensors must be 16-byte aligned");
   const int afmt = act_fmt(aq);
-  size_t need = gemm_ws(FQ_OP_GEMM_BWD, s, R_max, (w_fq ? 0 : wq->fmt) | (afmt << 8));
-  if (ws_bytes < need || !ws) {
-    set_error("fq_grouped_gemm_bwd_scale: workspace %zu bytes < %zu needed", ws_bytes, need);
-    return FQ_ERR_WORKSPACE_TOO_SMALL;
-  }
-  hipStream_t st = S(stream);
   Carver c(ws);
   const uint16_t *wfq = w_fq;
   if (!wfq && dx) {
@@ -459,6 +504,102 @@ fq_status fq_grouped_gemm_bwd_scale(const uint16_t *dy, const uint16_t *x, int32
                                st);
     }
   }
+}
+
+}  // namespace
+
+fq_status fq_grouped_gemm_bwd_scale(const uint16_t *dy, const uint16_t *x, int32_t R_max,
+                                    const int32_t *seg, fq_shape s, const uint16_t *w,
+                                    const uint16_t *w_fq, const fq_weight_q *wq, const fq_act_q *aq,
+                                    uint16_t *dx, float *dscale, float *dzp, void *ws,
+                                    size_t ws_bytes, fq_stream stream) {
+  FQ_TRY(check_shape(s));
+  FQ_CHECK_ARG(R_max >= 0, "R_max < 0");
+  FQ_CHECK_ARG(seg != nullptr, "seg_offsets is NULL");
+  FQ_CHECK_ARG(dy || R_max == 0, "dy is NULL");
+  const bool want_ds = dscale || dzp;
+  FQ_TRY(check_weight_q(wq, s, true));
+  FQ_TRY(check_act_q(aq, s.K));
+  FQ_CHECK_ARG(w != nullptr, "w (raw weights) is NULL");
+  FQ_CHECK_ARG(!want_ds || x || R_max == 0, "x is NULL");
+  FQ_CHECK_ARG(!dzp || wq->fmt == FQ_FMT_INT4, "dzero_point only exists for int4");
+  FQ_CHECK_ARG(!dzp || dscale, "dzero_point needs dscale too");
+  FQ_CHECK_SUPPORTED(s.N % 16 == 0 && s.K % 16 == 0,
+                     "grouped GEMM needs N %% 16 == 0 and K %% 16 == 0 (N=%d K=%d)", s.N, s.K);
+  FQ_CHECK_SUPPORTED(s.E <= 1024, "grouped GEMM supports up to 1024 experts per stack (E=%d)", s.E);
+  const fq_shape p = gemm_pad_shape(FQ_OP_GEMM_BWD, s);
+  FQ_CHECK_SUPPORTED((size_t)R_max * (p.K > p.N ? p.K : p.N) * 2 < (1ull << 32) &&
+                         (size_t)p.N * p.K * 2 < (1ull << 32),
+                     "operands must stay below 4 GiB (32-bit tile offsets)");
+  const bool per_tensor = wq->group == FQ_GROUP_TENSOR;
+  const int group_p = per_tensor ? FQ_GROUP_TENSOR : padded_group(wq->group, s, p);
+  FQ_CHECK_SUPPORTED(!want_ds || per_tensor || group_ok_for_dscale(group_p),
+                     "dScale needs group 16, 32, 64 or a multiple of 128 (group=%d)", wq->group);
+  FQ_CHECK_ARG(!want_ds || wq->fmt != FQ_FMT_NVFP4 || aligned16(wq->scale),
+               "nvfp4 theta must be 16-byte aligned");
+  FQ_CHECK_ARG((!dy || aligned16(dy)) && (!x || aligned16(x)) && aligned16(w) &&
+                   (!w_fq || aligned16(w_fq)) && (!dx || aligned16(dx)),
+               "bf16 tensors must be 16-byte aligned");
+  const int afmt = act_fmt(aq);
+  size_t need = gemm_ws(FQ_OP_GEMM_BWD, s, R_max, (w_fq ? 0 : wq->fmt) | (afmt << 8));
+  if (ws_bytes < need || !ws) {
+    set_error("fq_grouped_gemm_bwd_scale: workspace %zu bytes < %zu needed", ws_bytes, need);
+    return FQ_ERR_WORKSPACE_TOO_SMALL;
+  }
+  hipStream_t st = S(stream);
+  if (!gemm_needs_pad(FQ_OP_GEMM_BWD, s)) {
+    gemm_bwd_core(dy, x, R_max, seg, s, w, w_fq, wq, aq, dx, dscale, dzp, ws, st);
+    FQ_CHECK_LAUNCH("fq_grouped_gemm_bwd_scale");
+    return FQ_OK;
+  }
+  // Zero-padded to the kernels' shape. A padded weight element is 0 with a
+  // neutral scale (1 for the integer / FP8 grids, theta 0 for NVFP4, zero
+  // point 0), so its straight-through factor is 0; padded contraction
+  // columns add nothing; only the call's own region is copied back.
+  Carver c(ws);
+  const int G = per_tensor ? 0 : s.K / wq->group, Gp = per_tensor ? 0 : p.K / group_p;
+  uint16_t *wfq_p = nullptr;
+  if (dx) {
+    const uint16_t *wfq = w_fq;
+    if (!wfq) {
+      uint16_t *t = c.take<uint16_t>((size_t)s.E * s.N * s.K * 2);
+      launch_quantize_stacked(w, s, as_groups(*wq, s), t, nullptr, st);
+      wfq = t;
+    }
+    wfq_p = c.take<uint16_t>((size_t)s.E * p.N * p.K * 2);
+    launch_reshape_u16(wfq, s.E, s.N, s.K, wfq_p, p.N, p.K, nullptr, st);
+  }
+  uint16_t *w_p = c.take<uint16_t>((size_t)s.E * p.N * p.K * 2);
+  launch_reshape_u16(w, s.E, s.N, s.K, w_p, p.N, p.K, nullptr, st);
+  uint16_t *x_p = c.take<uint16_t>((size_t)R_max * p.K * 2);
+  uint16_t *dy_p = c.take<uint16_t>((size_t)R_max * p.N * 2);
+  uint16_t *dx_p = c.take<uint16_t>((size_t)R_max * p.K * 2);
+  if (R_max > 0) {
+    if (x) launch_reshape_u16(x, 1, R_max, s.K, x_p, R_max, p.K, seg + s.E, st);
+    launch_reshape_u16(dy, 1, R_max, s.N, dy_p, R_max, p.N, seg + s.E, st);
+  }
+  const size_t nsc = (size_t)s.E * p.N * (p.K / 16) * 4;
+  float *sc_p = c.take<float>(nsc), *zp_p = c.take<float>(nsc);
+  float *ds_p = c.take<float>(nsc), *dzp_p = c.take<float>(nsc);
+  fq_weight_q wq_p = *wq;
+  wq_p.group = group_p;
+  if (!per_tensor) {
+    launch_reshape_f32(wq->scale, s.E, s.N, G, sc_p, p.N, Gp,
+                       wq->fmt == FQ_FMT_NVFP4 ? 0.0f : 1.0f, st);
+    wq_p.scale = sc_p;
+    if (wq->fmt == FQ_FMT_INT4) {
+      launch_reshape_f32(wq->zero_point, s.E, s.N, G, zp_p, p.N, Gp, 0.0f, st);
+      wq_p.zero_point = zp_p;
+    }
+  }
+  // per-tensor dScale is [E] already, written in place
+  float *ds_out = dscale ? (per_tensor ? dscale : ds_p) : nullptr;
+  float *dzp_out = dzp ? dzp_p : nullptr;
+  gemm_bwd_core(dy_p, x ? x_p : nullptr, R_max, seg, p, w_p, wfq_p, &wq_p, aq,
+                dx ? dx_p : nullptr, ds_out, dzp_out, c.base + c.used, st);
+  if (dx && R_max > 0) launch_reshape_u16(dx_p, 1, R_max, p.K, dx, R_max, s.K, seg + s.E, st);
+  if (dscale && !per_tensor) launch_reshape_f32(ds_p, s.E, p.N, Gp, dscale, s.N, G, 0.0f, st);
+  if (dzp) launch_reshape_f32(dzp_p, s.E, p.N, Gp, dzp, s.N, G, 0.0f, st);
   FQ_CHECK_LAUNCH("fq_grouped_gemm_bwd_scale");
   return FQ_OK;
 }

@@ -736,6 +736,45 @@ __global__ __launch_bounds__(kThreads) void k_unpermute_reduce(
 }  // namespace
 
 // ========================================================= launchers =======
+// dst[e][r][c] = src[e][r][c] inside src's [rows_s, cols_s], else `fill`, for
+// dst of [E, rows_d, cols_d]: zero-pads (rows_d >= rows_s, cols_d >= cols_s) or
+// crops (<=) a stack of row-major matrices. n_rows (device, may be NULL): only
+// the dst rows below n_rows[0] are written (routed-row tensors).
+template <typename T>
+__global__ __launch_bounds__(kThreads) void k_reshape_copy(const T *__restrict__ src, int rows_s,
+                                                           int cols_s, T *__restrict__ dst,
+                                                           size_t n, int rows_d, int cols_d,
+                                                           T fill, const int32_t *n_rows) {
+  const int limit = n_rows ? *n_rows : rows_d;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (size_t)gridDim.x * blockDim.x) {
+    const size_t er = i / (size_t)cols_d;
+    const int c = (int)(i - er * (size_t)cols_d);
+    const size_t e = er / (size_t)rows_d;
+    const int r = (int)(er - e * (size_t)rows_d);
+    if (r >= limit) continue;
+    dst[i] = (r < rows_s && c < cols_s) ? src[(e * rows_s + r) * (size_t)cols_s + c] : fill;
+  }
+}
+
+void launch_reshape_u16(const uint16_t *src, int E, int rows_s, int cols_s, uint16_t *dst,
+                        int rows_d, int cols_d, const int32_t *n_rows, hipStream_t st) {
+  const size_t n = (size_t)E * rows_d * cols_d;
+  if (!n) return;
+  hipLaunchKernelGGL(k_reshape_copy<uint16_t>, dim3(grid_for((long)n, kThreads, 1 << 16)),
+                     dim3(kThreads), 0, st, src, rows_s, cols_s, dst, n, rows_d, cols_d,
+                     (uint16_t)0, n_rows);
+}
+
+void launch_reshape_f32(const float *src, int E, int rows_s, int cols_s, float *dst, int rows_d,
+                        int cols_d, float fill, hipStream_t st) {
+  const size_t n = (size_t)E * rows_d * cols_d;
+  if (!n) return;
+  hipLaunchKernelGGL(k_reshape_copy<float>, dim3(grid_for((long)n, kThreads, 1 << 16)),
+                     dim3(kThreads), 0, st, src, rows_s, cols_s, dst, n, rows_d, cols_d, fill,
+                     (const int32_t *)nullptr);
+}
+
 void launch_fill_u32(uint32_t *p, uint32_t v, long n, hipStream_t st) {
   if (n <= 0) return;
   hipLaunchKernelGGL(k_fill_u32, dim3(grid_for(n)), dim3(kThreads), 0, st, p, v, n);

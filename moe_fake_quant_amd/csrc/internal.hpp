@@ -7,6 +7,12 @@
 namespace fq {
 
 void launch_fill_u32(uint32_t *p, uint32_t v, long n, hipStream_t st);
+// [E, rows_s, cols_s] -> [E, rows_d, cols_d], zero fill outside the source (pad) or
+// crop; n_rows (device, may be NULL): only dst rows below n_rows[0] are written
+void launch_reshape_u16(const uint16_t *src, int E, int rows_s, int cols_s, uint16_t *dst,
+                        int rows_d, int cols_d, const int32_t *n_rows, hipStream_t st);
+void launch_reshape_f32(const float *src, int E, int rows_s, int cols_s, float *dst, int rows_d,
+                        int cols_d, float fill, hipStream_t st);
 // out[r * n + i] = v[r] for r < rows, i < n
 void launch_repeat_rows(const float *v, int rows, int n, float *out, hipStream_t st);
 // out[r] = sum over i < n of in[r * n + i], in a fixed order (bitwise reproducible)

@@ -161,19 +161,29 @@ def test_quantize_stacked_rejects_bad_arguments(pkg):
 def test_grouped_gemm_rejects_unsupported_shapes(pkg):
     S = pkg.fq_shape
     q = _wq(pkg, pkg.FMT_FP8_E4M3, 256)
-    # forward tiles need N % 256 and K % 64
-    st = _status(pkg, "fq_grouped_gemm_fwd", FAKE, 64, FAKE, S(2, 128, 256), None, FAKE, q, None,
+    # N and K must be multiples of 16 (the block of the grids)
+    st = _status(pkg, "fq_grouped_gemm_fwd", FAKE, 64, FAKE, S(2, 120, 256), None, FAKE, q, None,
                  FAKE, None, 0, None)
     assert st == pkg.FQ_ERR_UNSUPPORTED
-    assert b"256" in pkg.lib().fq_last_error()
+    assert b"16" in pkg.lib().fq_last_error()
+    # other multiples of 16 run zero-padded to the tile shape, in workspace
+    # memory: with none given the call says how much it needs
+    st = _status(pkg, "fq_grouped_gemm_fwd", FAKE, 64, FAKE, S(2, 128, 256), None, FAKE, q, None,
+                 FAKE, None, 0, None)
+    assert st == pkg.FQ_ERR_WORKSPACE_TOO_SMALL
+    need = pkg.lib().fq_workspace_bytes(pkg.FQ_OP_GEMM_FWD, S(2, 128, 256), 64, 0)
+    assert need >= 2 * 256 * 256 * 2 + 64 * 256 * 2 * 2          # padded W_fq, x and y
+    assert pkg.lib().fq_workspace_bytes(pkg.FQ_OP_GEMM_FWD, S(2, 256, 256), 64, 0) == 0
     # more experts than the tile scheduler holds
     st = _status(pkg, "fq_grouped_gemm_fwd", FAKE, 64, FAKE, S(1025, 256, 256), None, FAKE, q,
                  None, FAKE, None, 0, None)
     assert st == pkg.FQ_ERR_UNSUPPORTED
-    # backward needs K % 256; dScale group must be reducible by the epilogue
-    st = _status(pkg, "fq_grouped_gemm_bwd_scale", FAKE, FAKE, 64, FAKE, S(2, 256, 192), FAKE,
-                 FAKE, _wq(pkg, pkg.FMT_FP8_E4M3, 192), None, FAKE, None, None, FAKE, 1 << 30, None)
-    assert st == pkg.FQ_ERR_UNSUPPORTED
+    # backward: K a multiple of 16; dScale group must be reducible by the epilogue
+    st = _status(pkg, "fq_grouped_gemm_bwd_scale", FAKE, FAKE, 64, FAKE, S(2, 256, 200), FAKE,
+                 FAKE, _wq(pkg, pkg.FMT_FP8_E4M3, 200), None, FAKE, None, None, FAKE, 1 << 30, None)
+    assert st in (pkg.FQ_ERR_UNSUPPORTED, pkg.FQ_ERR_INVALID_ARGUMENT)   # refused before launch
+    assert pkg.lib().fq_workspace_bytes(pkg.FQ_OP_GEMM_BWD, S(2, 80, 48), 64, 0) > \
+        pkg.lib().fq_workspace_bytes(pkg.FQ_OP_GEMM_BWD, S(2, 256, 256), 64, 0)
     st = _status(pkg, "fq_grouped_gemm_bwd_scale", FAKE, FAKE, 64, FAKE, S(2, 256, 768), FAKE,
                  FAKE, _wq(pkg, pkg.FMT_INT8, 48), None, None, FAKE, None, FAKE, 1 << 30, None)
     assert st == pkg.FQ_ERR_UNSUPPORTED

@@ -325,6 +325,59 @@ def test_gemm_bwd_rows_beyond_one_chunk(name, fmt, group):
         check_dscale_per_expert(dzp.cpu().numpy(), dzp_ref, "dzero_point")
 
 
+@pytest.mark.parametrize("name,fmt,grp", [("int8_pc", O.FMT_INT8, "K"), ("int4_g16", O.FMT_INT4, 16),
+                                          ("fp8_pc", O.FMT_FP8, "K"), ("nvfp4", O.FMT_NVFP4, 16),
+                                          ("int8_pt", O.FMT_INT8, "T")])
+@pytest.mark.parametrize("afmt", [O.FMT_NONE, O.FMT_NVFP4])
+@pytest.mark.parametrize("N,K", [(80, 48), (272, 208)])
+def test_gemm_shapes_not_multiple_of_tiles(name, fmt, grp, afmt, N, K):
+    """N and K multiples of 16 but not of the tile sizes: the calls pad the
+    operands with zeros (neutral scales) in the workspace and copy back only
+    their own region. Forward and backward against the oracle; rows past the
+    routed rows stay untouched."""
+    rng = np.random.default_rng(1000 + 7 * fmt + afmt + N + K)
+    E = 3
+    seg = _segments(rng, E, [70, 0, 33])
+    R = int(seg[-1])
+    R_max = R + 5
+    group = K if grp == "K" else (O.GROUP_TENSOR if grp == "T" else grp)
+    w = _rand_w(rng, E, N, K)
+    s, zp, g = O.observer_weight(w, fmt, group)
+    x = O.f32_to_bf16(rng.standard_normal((R_max, K)).astype(np.float32))
+    dy = O.f32_to_bf16(rng.standard_normal((R_max, N)).astype(np.float32))
+    sa = O.observer_act(x[:R], afmt) if afmt else np.float32(1.0)
+    y_ref = O.grouped_gemm_fwd(x, seg, w, fmt, group, s, zp, g, afmt, sa)
+    dx_ref, ds_ref, dzp_ref = O.grouped_gemm_bwd(dy, x, seg, w, fmt, group, s, zp, g, afmt, sa)
+    gq = F.FQ_GROUP_TENSOR if group == O.GROUP_TENSOR else group
+    wq = _wq(fmt, gq, s, zp, g)
+    aq = F.ActQ(afmt, dev_f32([sa])) if afmt else None
+    fmts = fmt | (afmt << 8)
+    ws = torch.empty(max(F.fq_workspace_bytes(F.FQ_OP_GEMM_FWD, (E, N, K), R_max, fmts),
+                         F.fq_workspace_bytes(F.FQ_OP_GEMM_BWD, (E, N, K), R_max, fmts)),
+                     dtype=torch.uint8, device="cuda")
+    y = torch.full((R_max, N), 7.0, dtype=torch.bfloat16, device="cuda")
+    wd = dev_bf16(w)
+    F.fq_grouped_gemm_fwd(dev_bf16(x), R_max, dev_i32(seg), (E, N, K), wd, None, wq, aq, y, ws)
+    dx = torch.full((R_max, K), 7.0, dtype=torch.bfloat16, device="cuda")
+    ds = torch.full(s.shape, 7.0, device="cuda")
+    dzp = torch.full(s.shape, 7.0, device="cuda") if fmt == O.FMT_INT4 else None
+    F.fq_grouped_gemm_bwd_scale(dev_bf16(dy), dev_bf16(x), R_max, dev_i32(seg), (E, N, K), wd,
+                                None, wq, aq, dx, ds, dzp, ws)
+    torch.cuda.synchronize()
+    yb, dxb = host_bits(y), host_bits(dx)
+    check_gemm_tol(yb[:R], y_ref, "y")
+    assert np.all(bf16_vals(yb[R:]) == 7.0)
+    check_gemm_tol(dxb[:R], dx_ref, "dx")
+    assert np.all(bf16_vals(dxb[R:]) == 7.0)
+    dsh = ds.cpu().numpy()
+    check_dscale_tol(dsh, ds_ref, "dscale")
+    if group != O.GROUP_TENSOR:
+        check_dscale_per_expert(dsh, ds_ref, "dscale")
+    assert np.all(dsh[1] == 0)                         # the empty expert
+    if dzp is not None:
+        check_dscale_per_expert(dzp.cpu().numpy(), dzp_ref, "dzero_point")
+
+
 @pytest.mark.parametrize("name,fmt", [("int8", O.FMT_INT8), ("fp8", O.FMT_FP8)])
 def test_per_tensor_weight_scales(name, fmt):
     """One scale per expert matrix: observer and FQ pass bit-exact, forward

@@ -376,42 +376,42 @@ __device__ __forceinline__ void wgrad_epilogue(const GemmArgs &a, const f32x16 (
 // Per-lane global byte offsets of the operand rows this lane streams, fixed
 // for a tile. A wave issues 4 DMA instructions per operand per stage, each
 // filling 1 KiB of LDS (lane l -> byte 16 l of it).
-struct NormalDMA {  // contraction-contiguous: instr covers 8 rows x 128 B
+struct NormalDMA {  // contraction-contiguous: instr covers 8 rows x 128 B; slot = 32 rows
   uint32_t off[4];
-  __device__ __forceinline__ void init(size_t ld, int row0, int row_last, int wave, int lane) {
+  __device__ __forceinline__ void init(size_t ld, int row0, int row_last, int slot, int lane) {
 #pragma unroll
     for (int ii = 0; ii < 4; ++ii) {
-      const uint32_t idx = 8 * (4 * wave + ii) + (lane >> 3);
+      const uint32_t idx = 8 * (4 * slot + ii) + (lane >> 3);
       const uint32_t kc = (lane & 7) ^ nrm_sw(idx);
       const int r = min(row0 + (int)idx, row_last);
       off[ii] = (uint32_t)(((size_t)r * ld + kc * 8) * 2);
     }
   }
   template <int S>
-  __device__ __forceinline__ void issue(const char *base, char *stage, int c0, int wave) const {
+  __device__ __forceinline__ void issue(const char *base, char *stage, int c0, int slot) const {
 #pragma unroll
-    for (int ii = 0; ii < 4; ++ii) dma16(base + c0 * 2, off[ii], stage + (4 * wave + ii) * 1024);
+    for (int ii = 0; ii < 4; ++ii) dma16(base + c0 * 2, off[ii], stage + (4 * slot + ii) * 1024);
   }
 };
-struct TransDMA {  // transposed: instr covers 2 contraction rows x 512 B
+struct TransDMA {  // transposed: instr covers 2 contraction rows x 512 B; slot = 8 rows
   uint32_t col_off[4];
   int crow[4];
-  __device__ __forceinline__ void init(int idx0, int wave, int lane) {
+  __device__ __forceinline__ void init(int idx0, int slot, int lane) {
 #pragma unroll
     for (int ii = 0; ii < 4; ++ii) {
-      crow[ii] = 2 * (4 * wave + ii) + (lane >> 5);
+      crow[ii] = 2 * (4 * slot + ii) + (lane >> 5);
       const uint32_t q = (lane & 31) ^ tr_sw(crow[ii]);
       col_off[ii] = (uint32_t)((idx0 + 8 * q) * 2);
     }
   }
   // rows c >= c_end are read from row c0 (valid memory) and zeroed later
   __device__ __forceinline__ void issue(const char *base, uint32_t ld, char *stage, int c0,
-                                        int c_end, int wave) const {
+                                        int c_end, int slot) const {
 #pragma unroll
     for (int ii = 0; ii < 4; ++ii) {
       const int c = c0 + crow[ii];
       const int cc = c < c_end ? c : c0;
-      dma16(base, (uint32_t)cc * (ld * 2) + col_off[ii], stage + (4 * wave + ii) * 1024);
+      dma16(base, (uint32_t)cc * (ld * 2) + col_off[ii], stage + (4 * slot + ii) * 1024);
     }
   }
 };
@@ -489,7 +489,24 @@ __device__ __forceinline__ Tile decode_tile(const GemmArgs &a, const int *tile_s
 }
 
 // The operand streams of one tile: bases, per-lane offsets and the
-// contraction length. issue<S>(kt) loads stage kt into LDS buffer S.
+// contraction length. issue<S>(kt) loads this wave's share of stage kt into
+// LDS buffer S.
+//
+// Shares. A stage of each operand is 8 slots of 4 DMA instructions (4 KiB).
+// WGRAD (all waves in step): wave w loads slot w of P and of Q. FWD / DGRAD
+// (the ping-pong below): each group loads the LDS locations that it does not
+// read in the phase where it issues the loads. Wave w loads Q slot w ^ 4, so
+// group B fills the Q rows that group A multiplies (rows 0-127) and A those
+// of B. DGRAD's transposed P slot s holds contraction rows 8s..8s+7 of every
+// column: wave w loads P slot w ^ 4, so B fills the first half of the stage
+// depth, which it has read already, and A the second. FWD's P slot holds 32
+// full-depth rows that waves of both groups read, so group A loads all of P
+// (slots 2w and 2w + 1) and B none.
+template <int MODE>
+constexpr int kVmPerStageA = MODE == FWD ? 12 : 8;  // DMA instructions per wave and stage
+template <int MODE>
+constexpr int kVmPerStageB = MODE == FWD ? 4 : 8;
+
 template <int MODE>
 struct TileLoads {
   const char *pbase, *qbase;
@@ -501,16 +518,19 @@ struct TileLoads {
     c_total = (MODE == WGRAD) ? t.r1 - t.r0 : (MODE == FWD) ? a.K : a.N;
     nk = (c_total + BK - 1) / BK;
     const size_t NK = (size_t)a.N * a.K;
+    const int xs = wave ^ 4;
     if (MODE == FWD) {
       pbase = reinterpret_cast<const char *>(a.p + t.e * NK);  // W_fq[e] [N][K], rows i = n
       qbase = reinterpret_cast<const char *>(a.q);             // Xq rows (absolute)
-      pn.init(a.K, t.i0, a.N - 1, wave, lane);
-      qn.init(a.K, t.j0, t.j_end - 1, wave, lane);
+      // slot 2w here; slot 2w + 1 is the same offsets 32 rows on (N is a
+      // multiple of 256, so no P row of a tile is clamped)
+      pn.init(a.K, t.i0, a.N - 1, 2 * (wave & 3), lane);
+      qn.init(a.K, t.j0, t.j_end - 1, xs, lane);
     } else if (MODE == DGRAD) {
       pbase = reinterpret_cast<const char *>(a.p + t.e * NK);  // W_fq[e] as (c = n, idx = k)
       qbase = reinterpret_cast<const char *>(a.q);             // dY rows (absolute)
-      pt.init(t.i0, wave, lane);
-      qn.init(a.N, t.j0, t.j_end - 1, wave, lane);
+      pt.init(t.i0, xs, lane);
+      qn.init(a.N, t.j0, t.j_end - 1, xs, lane);
     } else {
       pbase = reinterpret_cast<const char *>(a.p + (size_t)seg_lo * a.K);  // Xq: (c = r, idx = k)
       qbase = reinterpret_cast<const char *>(a.q + (size_t)seg_lo * a.N);  // dY: (c = r, idx = n)
@@ -521,12 +541,16 @@ struct TileLoads {
   template <int S>
   __device__ __forceinline__ void issue(const GemmArgs &a, int kt, int wave) const {
     const int c0 = kt * BK;
+    const int xs = wave ^ 4;
     if (MODE == FWD) {
-      pn.template issue<S>(pbase, stage_p<S>(), c0, wave);
-      qn.template issue<S>(qbase, stage_q<S>(), c0, wave);
+      if (wave < 4) {
+        pn.template issue<S>(pbase, stage_p<S>(), c0, 2 * wave);
+        pn.template issue<S>(pbase + (size_t)64 * a.K, stage_p<S>(), c0, 2 * wave + 1);
+      }
+      qn.template issue<S>(qbase, stage_q<S>(), c0, xs);
     } else if (MODE == DGRAD) {
-      pt.issue(pbase, a.K, stage_p<S>(), c0, c_total, wave);
-      qn.template issue<S>(qbase, stage_q<S>(), c0, wave);
+      pt.issue(pbase, a.K, stage_p<S>(), c0, c_total, xs);
+      qn.template issue<S>(qbase, stage_q<S>(), c0, xs);
     } else {
       pt.issue(pbase, a.K, stage_p<S>(), c0, c_total, wave);
       qt.issue(qbase, a.N, stage_q<S>(), c0, c_total, wave);
@@ -761,12 +785,18 @@ __device__ __forceinline__ void run_tile_lockstep(const GemmArgs &a, const int *
 // and the barrier wait sit under them. With h = 0, 1 the halves of stage t:
 //   phase 4t     : A multiplies t.0  | B reads t.0
 //   phase 4t + 1 : B multiplies t.0  | A reads t.1
-//   phase 4t + 2 : A multiplies t.1  | B reads t.1,  loads its share of t+2
+//   phase 4t + 2 : A multiplies t.1  | B reads t.1,   loads its share of t+2
 //   phase 4t + 3 : B multiplies t.1  | A reads t+1.0, loads its share of t+2
-// Stage t lives in buffer t % 2; after phase 4t + 2 nobody reads it again, so
-// each wave loads into it once its own reads of it have returned. Each wave
-// waits for its own loads of a stage before the barrier that opens the
-// first phase reading it. A's epilogue runs while B multiplies the last half.
+// Stage t lives in buffer t % 2. A load may land in LDS as soon as it is
+// issued, so a wave issues a load only into locations that no wave reads in
+// that phase or later; its own returned reads are not enough, since the
+// other waves of its group read the same phase. The shares (TileLoads) make
+// this hold: in phase 4t + 2 group B loads only locations of buffer t % 2
+// that nobody reads from then on (the Q rows of group A, and for DGRAD the
+// first half of the stage depth), and in phase 4t + 3 group A loads the rest,
+// after the last read of stage t. Each wave waits for its own loads of a
+// stage before the barrier that opens the first phase reading it. A's
+// epilogue runs while B multiplies the last half.
 template <int MODE, int WFMT>
 __device__ __forceinline__ int run_tile(const GemmArgs &a, const int *tile_start, const Tile &tl,
                                         int pre, int next_w) {
@@ -873,7 +903,7 @@ __device__ __forceinline__ int run_tile(const GemmArgs &a, const int *tile_start
     wait_lgkm0();
     if (kt + 2 < nk) {
       ld.template issue<S>(a, kt + 2, wave);
-      wait_vm<8>();  // this wave's share of stage kt+1 (read by A next phase)
+      wait_vm<kVmPerStageB<MODE>>();  // this wave's share of stage kt+1 (read by A next phase)
     } else {
       wait_vm<0>();
     }
@@ -884,8 +914,9 @@ __device__ __forceinline__ int run_tile(const GemmArgs &a, const int *tile_start
   if (nk > 0) {
     if (pre < 1) ld.template issue<0>(a, 0, wave);
     if (pre < 2 && nk > 1) ld.template issue<1>(a, 1, wave);
-    if (nk > 1) wait_vm<8>();  // this wave's share of stage 0
-    else wait_vm<0>();
+    if (nk <= 1) wait_vm<0>();  // this wave's share of stage 0
+    else if (grp_b) wait_vm<kVmPerStageB<MODE>>();
+    else wait_vm<kVmPerStageA<MODE>>();
     phase_barrier();
     if (!grp_b) {
       if (live) read_half(std::integral_constant<int, 0>{}, 0, 0);

@@ -454,6 +454,49 @@ def test_bwd_deterministic_run_to_run():
     assert torch.equal(outs[0][1], outs[1][1])
 
 
+@pytest.mark.parametrize("N,K", [(256, 256), (512, 512)])
+def test_gemm_ragged_tiles_every_launch(N, K):
+    """FWD and DGRAD on experts whose last 256-row tile leaves waves without
+    rows in every pattern (1..64, 65..128, 129..191, 192..255 valid rows of
+    the tile). A wave with no rows skips its LDS reads and reaches its next
+    loads early; the loads of a stage may not land in a buffer that another
+    wave still reads. Every launch is checked: bitwise equal to the first,
+    the first against the oracle."""
+    rng = np.random.default_rng(850 + N)
+    sizes = [189, 0, 129, 191, 65, 257, 320, 1, 450, 146, 64, 192, 255, 128]
+    E = len(sizes)
+    seg = _segments(rng, E, sizes)
+    R = int(seg[-1])
+    w = _rand_w(rng, E, N, K)
+    s, _, g = O.observer_weight(w, O.FMT_NVFP4, 16)
+    wq = _wq(O.FMT_NVFP4, 16, s, None, g)
+    wd = dev_bf16(w)
+    wfq = torch.empty_like(wd)
+    F.fq_quantize_stacked(wd, (E, N, K), wq, wfq)
+    wsb = F.fq_workspace_bytes(F.FQ_OP_GEMM_BWD, (E, N, K), R, 0)
+    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device="cuda")
+    x = O.f32_to_bf16(rng.standard_normal((R, K)).astype(np.float32))
+    dy = O.f32_to_bf16(rng.standard_normal((R, N)).astype(np.float32))
+    xd, dyd, segd = dev_bf16(x), dev_bf16(dy), dev_i32(seg)
+    y_ref = O.grouped_gemm_fwd(x, seg, w, O.FMT_NVFP4, 16, s, None, g)
+    dx_ref, _, _ = O.grouped_gemm_bwd(dy, x, seg, w, O.FMT_NVFP4, 16, s, None, g)
+    ys, dxs = [], []
+    for _ in range(12):
+        y = torch.full((R, N), 7.0, dtype=torch.bfloat16, device="cuda")
+        dx = torch.full((R, K), 7.0, dtype=torch.bfloat16, device="cuda")
+        F.fq_grouped_gemm_fwd(xd, R, segd, (E, N, K), None, wfq, wq, None, y, None)
+        F.fq_grouped_gemm_bwd_scale(dyd, xd, R, segd, (E, N, K), wd, wfq, wq, None, dx, None,
+                                    None, ws)
+        ys.append(y)
+        dxs.append(dx)
+    torch.cuda.synchronize()
+    check_gemm_tol(host_bits(ys[0]), y_ref, "y")
+    check_gemm_tol(host_bits(dxs[0]), dx_ref, "dx")
+    for i in range(1, len(ys)):
+        assert torch.equal(ys[i].view(torch.int16), ys[0].view(torch.int16)), f"y launch {i}"
+        assert torch.equal(dxs[i].view(torch.int16), dxs[0].view(torch.int16)), f"dx launch {i}"
+
+
 # ------------------------------------------------------- error handling --
 def test_errors_are_reported_before_launch():
     E, N, K = 2, 256, 250      # K not a multiple of 16

@@ -75,6 +75,9 @@ def parse():
                     help="steps of the separate instrumented pass (per-call times)")
     ap.add_argument("--no-peaks", action="store_true",
                     help="skip the measured MFMA-chain and copy peaks")
+    ap.add_argument("--no-overlap", action="store_true",
+                    help="keep the wgrad calls on the launch stream in the timed steps too "
+                         "(for kernel traces whose per-kernel durations are their own)")
     ap.add_argument("--act-scales", choices=["frozen", "learnable"], default="frozen",
                     help="learnable: the backward also forms the activation-scale gradients "
                          "(fp8 workload only)")
@@ -395,8 +398,7 @@ def main():
                  "fq_moe_unpermute_reduce"):
         setattr(LM, name, timer.wrap(keys.get(name, lambda a, n=name: n), getattr(LM, name)))
 
-    # FQ_BENCH_OVERLAP=0 keeps the wgrad calls on the launch stream (an A/B switch)
-    layer.overlap_wgrad = os.environ.get("FQ_BENCH_OVERLAP", "1") != "0"
+    layer.overlap_wgrad = not args.no_overlap
     overlap = layer.overlap_wgrad
     step = lambda: layer.step(x, ids, probs, dout)  # noqa: E731
     for _ in range(args.warmup):
@@ -528,7 +530,8 @@ def main():
             "traffic": traffic,
         },
         "timing": {"headline": "HIP events around the timed steps, no per-call events; the wgrad "
-                               "calls on a second stream",
+                               + ("calls on a second stream" if overlap else
+                                  "calls on the launch stream (--no-overlap)"),
                    "breakdown": "a separate pass with events around each call, all on one stream",
                    "breakdown_steps": nb, "breakdown_ms_per_step": round(ms_step_instr, 4)},
         "gemm_kernels": kernels,

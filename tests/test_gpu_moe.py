@@ -142,3 +142,34 @@ def test_moe_layer_stagewise_and_end_to_end(name, wfmt, afmt, group, T, Eg, El, 
             # the oracle's own dXq / dAq differ from the GPU's by GEMM rounding
             check_act_dscale_tol(ds_a1, ref["ds_a1"], sc1, "ds_a1 e2e", tol=1e-2)
             check_act_dscale_tol(ds_a2, ref["ds_a2"], sc2, "ds_a2 e2e", tol=1e-2)
+
+
+@pytest.mark.parametrize("name,wfmt,afmt,group,learn", [("nvfp4", O.FMT_NVFP4, O.FMT_NVFP4, 16, False),
+                                                       ("fp8", O.FMT_FP8, O.FMT_FP8, None, True)])
+def test_overlapped_step_is_bitwise_the_serial_step(name, wfmt, afmt, group, learn):
+    """layer.step() with the wgrad -> dScale calls on the side stream beside
+    the dgrads gives the same bits as the serialized step, twice in a row
+    (every kernel is deterministic)."""
+    case = W.moe_case(T=700, fmt=name, E_global=16, H=256, F=256, topk=4, seed=13)
+    x, ids = dev_bf16(case.x), dev_i32(case.expert_ids)
+    p, dout = dev_f32(case.probs), dev_bf16(case.dout)
+    outs = []
+    for overlap in (False, True):
+        L = F.MoEFakeQuantLayer(dev_bf16(case.w_gu), dev_bf16(case.w_d), wfmt, afmt, case.T,
+                                case.topk, 0, group, learn_act_scales=learn)
+        L.init_weight_scales()
+        L.calibrate(x, ids)
+        L.overlap_wgrad = overlap
+        got = []
+        for _ in range(2):
+            L.step(x, ids, p, dout)
+            torch.cuda.synchronize()
+            t = [host_bits(L.out[:case.T]), host_bits(L.dx[:case.T]), L.ds_gu.cpu().numpy(),
+                 L.ds_d.cpu().numpy()]
+            if learn:
+                t += [L.ds_a1.cpu().numpy(), L.ds_a2.cpu().numpy()]
+            got.append(t)
+        outs.append(got)
+    for a, b in zip(outs[0], outs[1]):
+        for u, v in zip(a, b):
+            assert np.array_equal(np.asarray(u).view(np.uint8), np.asarray(v).view(np.uint8))

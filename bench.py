@@ -212,8 +212,51 @@ def measure_distill(torch, F, W, layer, x, ids, probs, reps=10):
             "GB/s": round(nbytes / (ms * 1e-3) / 1e9, 1),
             "pct_hbm_peak": round(100 * nbytes / (ms * 1e-3) / 1e9 / MI355X_HBM_PEAK_GBS, 1),
             "loss_mean": round(float(lm.cpu()[0]), 6)}
+    floor = kl_pattern_floor(torch, te, st, idx, T, V, K, reps)
+    if floor is not None:
+        out["kl_pattern_floor"] = floor
+        for key in ("kl_top_K", "r_kl_top_K"):
+            out[key]["pct_of_pattern_floor"] = round(100 * floor["ms"] / out[key]["ms"], 1)
     del st, te
     return out
+
+
+def kl_pattern_floor(torch, teacher, student, idx, T, V, K, reps):
+    """The floor of the top-K KL kernel's memory pattern: a plain kernel that
+    reads each teacher row once, the student at the K indices the KL kernel
+    selected, and writes 8K + 4 bytes per token, with no selection or softmax
+    work. Bytes = T (2V + 2K + 4K + 8K + 4) (it also reads the indices)."""
+    import ctypes
+    lib_path = os.path.join(ROOT, "moe_fake_quant_amd", "libfqpeaks.so")
+    if not os.path.exists(lib_path):
+        return None
+    # the probe reads student[t, idx[t, k]]: every index must lie in the row
+    lo, hi = int(idx.min().item()), int(idx.max().item())
+    if lo < 0 or hi >= V:
+        return None
+    lib = ctypes.CDLL(lib_path)
+    lib.fqp_stream_gather.argtypes = [ctypes.c_void_p] * 3 + [ctypes.c_int] * 3 + \
+        [ctypes.c_void_p] * 4
+    dev = teacher.device
+    oi = torch.empty(T, K, dtype=torch.int32, device=dev)
+    of = torch.empty(T, K, device=dev)
+    ol = torch.empty(T, dtype=torch.int32, device=dev)
+    st = torch.cuda.current_stream().cuda_stream
+    args = (teacher.data_ptr(), student.data_ptr(), idx.data_ptr(), T, V, K, oi.data_ptr(),
+            of.data_ptr(), ol.data_ptr(), st)
+    assert lib.fqp_stream_gather(*args) == 0
+    torch.cuda.synchronize()
+    s0 = torch.cuda.Event(enable_timing=True)
+    e0 = torch.cuda.Event(enable_timing=True)
+    s0.record()
+    for _ in range(reps):
+        assert lib.fqp_stream_gather(*args) == 0
+    e0.record()
+    torch.cuda.synchronize()
+    ms = s0.elapsed_time(e0) / reps
+    nbytes = T * (2 * V + 2 * K + 4 * K + 8 * K + 4)
+    del oi, of, ol
+    return {"ms": round(ms, 4), "bytes": nbytes, "GB/s": round(nbytes / (ms * 1e-3) / 1e9, 1)}
 
 
 def measured_peaks(torch, dev):
@@ -268,10 +311,12 @@ def measured_peaks(torch, dev):
 
 
 def scattered_rows_floor(torch, dev, rows, row_of, T, topk, H):
-    """The floor of the per-token reductions over routed rows (combine,
-    unpermute-reduce): a plain kernel with their access pattern (per token
-    row written, its topk routed rows read at the real routing positions, 16
-    bytes per thread) timed on the same buffers. Bytes = 2RH + 2TH + 4Tk."""
+    """The floor of the per-token passes over routed rows: a plain kernel with
+    their access pattern timed on the same buffers, 16 bytes per thread. Read
+    direction (combine, unpermute-reduce): per token row written, its topk
+    routed rows read at the real routing positions. Write direction (combine
+    backward): per token row read, written to its topk routed rows. Bytes =
+    2RH + 2TH + 4Tk either way."""
     import ctypes
     lib_path = os.path.join(ROOT, "moe_fake_quant_amd", "libfqpeaks.so")
     if not os.path.exists(lib_path):
@@ -294,8 +339,21 @@ def scattered_rows_floor(torch, dev, rows, row_of, T, topk, H):
     ms = s0.elapsed_time(e0) / 10
     R = int((row_of[:T] >= 0).sum().item())
     nbytes = 2 * R * H + 2 * T * H + 4 * T * topk
-    del out
-    return {"ms": round(ms, 4), "bytes": nbytes, "GB/s": round(nbytes / (ms * 1e-3) / 1e9, 1)}
+    # write direction: the token rows of `out` to fresh routed rows
+    lib.fqp_scattered_rows_w.argtypes = lib.fqp_scattered_rows.argtypes
+    dst = torch.empty_like(rows)
+    wargs = (out.data_ptr(), row_of.data_ptr(), T, topk, 2 * H, dst.data_ptr(), st)
+    assert lib.fqp_scattered_rows_w(*wargs) == 0
+    torch.cuda.synchronize()
+    s0.record()
+    for _ in range(10):
+        assert lib.fqp_scattered_rows_w(*wargs) == 0
+    e0.record()
+    torch.cuda.synchronize()
+    ms_w = s0.elapsed_time(e0) / 10
+    del out, dst
+    return {"ms": round(ms, 4), "bytes": nbytes, "GB/s": round(nbytes / (ms * 1e-3) / 1e9, 1),
+            "write_ms": round(ms_w, 4), "write_GB/s": round(nbytes / (ms_w * 1e-3) / 1e9, 1)}
 
 
 def host_description():
@@ -469,12 +527,14 @@ def main():
     floor = None if args.no_peaks else scattered_rows_floor(torch, dev, layer.o, layer.row_of,
                                                             case.T, case.topk, H)
     if floor:
-        for name in ("fq_moe_combine", "fq_moe_unpermute_reduce"):
+        for name, key in (("fq_moe_combine", "GB/s"), ("fq_moe_unpermute_reduce", "GB/s"),
+                          ("fq_moe_combine_bwd", "write_GB/s")):
             if name in passes:
                 passes[name]["pct_of_scattered_rows_floor"] = round(
-                    100 * passes[name]["GB/s"] / floor["GB/s"], 1)
+                    100 * passes[name]["GB/s"] / floor[key], 1)
         if peaks is not None:
             peaks["scattered_rows_GB/s"] = floor["GB/s"]
+            peaks["scattered_rows_write_GB/s"] = floor["write_GB/s"]
 
     if args.copy_calibration_mb > 0:
         n = args.copy_calibration_mb * (1 << 20) // 4

@@ -85,6 +85,62 @@ __global__ __launch_bounds__(256) void k_scattered_rows(const uint4 *__restrict_
   out[i] = acc;
 }
 
+// rows[r] = src[t] for the routed rows r = row_of[t, j] (j < topk, r >= 0):
+// the mirror pattern (one token row read, topk scattered row writes), as
+// the combine backward moves its rows.
+__global__ __launch_bounds__(256) void k_scattered_rows_w(const uint4 *__restrict__ src,
+                                                          const int32_t *__restrict__ row_of, int T,
+                                                          int topk, int cpr,
+                                                          uint4 *__restrict__ rows) {
+  const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= (size_t)T * cpr) return;
+  const int t = (int)(i / cpr), c = (int)(i - (size_t)t * cpr);
+  const uint4 v = src[i];
+  for (int j = 0; j < topk; ++j) {
+    const int r = row_of[(size_t)t * topk + j];
+    if (r >= 0) rows[(size_t)r * cpr + c] = v;
+  }
+}
+
+// The memory pattern of the top-K KL kernel with none of its selection or
+// softmax work. One workgroup per token: the teacher row is read once
+// (coalesced, 16 bytes per lane, four loads in flight) and folded into x;
+// then student[t, idx[t, k]] is read for k < K (K scattered 2-byte reads);
+// the outputs are 8K + 4 bytes per token like the KL kernel's (an index and
+// an fp32 value per entry, one fp32 per token). V is a multiple of 8.
+__global__ __launch_bounds__(512) void k_stream_gather(const uint4 *__restrict__ teacher,
+                                                       const uint16_t *__restrict__ student,
+                                                       const int32_t *__restrict__ idx, int V, int K,
+                                                       int32_t *__restrict__ out_i,
+                                                       float *__restrict__ out_f,
+                                                       uint32_t *__restrict__ out_l) {
+  __shared__ uint32_t red[8];
+  const int t = blockIdx.x;
+  const int n16 = V / 8;
+  const uint4 *row = teacher + (size_t)t * n16;
+  uint32_t x = 0;
+  int i = threadIdx.x;
+  for (; i + 3 * 512 < n16; i += 4 * 512) {
+    const uint4 a = row[i], b = row[i + 512], c = row[i + 1024], d = row[i + 1536];
+    x ^= a.x ^ a.y ^ a.z ^ a.w ^ b.x ^ b.y ^ b.z ^ b.w ^ c.x ^ c.y ^ c.z ^ c.w ^ d.x ^ d.y ^ d.z ^ d.w;
+  }
+  for (; i < n16; i += 512) {
+    const uint4 a = row[i];
+    x ^= a.x ^ a.y ^ a.z ^ a.w;
+  }
+  for (int o = 32; o > 0; o >>= 1) x ^= __shfl_xor(x, o, 64);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = x;
+  __syncthreads();
+  x = red[0] ^ red[1] ^ red[2] ^ red[3] ^ red[4] ^ red[5] ^ red[6] ^ red[7];
+  const uint16_t *srow = student + (size_t)t * V;
+  for (int k = threadIdx.x; k < K; k += 512) {
+    const int j = idx[(size_t)t * K + k];
+    out_i[(size_t)t * K + k] = j ^ (int)(x & 1u);
+    out_f[(size_t)t * K + k] = __uint_as_float((uint32_t)srow[j] << 16);
+  }
+  if (threadIdx.x == 0) out_l[t] = x;
+}
+
 }  // namespace
 
 extern "C" {
@@ -119,6 +175,35 @@ int fqp_scattered_rows(const void *rows, const int32_t *row_of, int T, int topk,
   if (n == 0) return 0;
   hipLaunchKernelGGL(k_scattered_rows, dim3((unsigned)((n + 255) / 256)), dim3(256), 0,
                      (hipStream_t)stream, (const uint4 *)rows, row_of, T, topk, cpr, (uint4 *)out);
+  return hipGetLastError() == hipSuccess ? 0 : 4;
+}
+
+
+// src: [T, row_bytes]; rows: [R, row_bytes] with R > every row_of entry;
+// row_bytes a multiple of 16
+int fqp_scattered_rows_w(const void *src, const int32_t *row_of, int T, int topk, int row_bytes,
+                         void *rows, void *stream) {
+  if (!src || !row_of || !rows || T < 0 || topk <= 0 || row_bytes <= 0 || row_bytes % 16 != 0)
+    return 1;
+  const int cpr = row_bytes / 16;
+  const size_t n = (size_t)T * cpr;
+  if (n == 0) return 0;
+  hipLaunchKernelGGL(k_scattered_rows_w, dim3((unsigned)((n + 255) / 256)), dim3(256), 0,
+                     (hipStream_t)stream, (const uint4 *)src, row_of, T, topk, cpr, (uint4 *)rows);
+  return hipGetLastError() == hipSuccess ? 0 : 4;
+}
+
+// teacher, student: [T, V] bf16, V a multiple of 8, rows 16-byte aligned;
+// idx: [T, K] int32, every entry in [0, V) (the caller checks); out_i, out_f:
+// [T, K]; out_l: [T]
+int fqp_stream_gather(const void *teacher, const uint16_t *student, const int32_t *idx, int T,
+                      int V, int K, int32_t *out_i, float *out_f, uint32_t *out_l, void *stream) {
+  if (!teacher || !student || !idx || !out_i || !out_f || !out_l || T < 0 || V <= 0 || V % 8 != 0 ||
+      K <= 0 || K > V)
+    return 1;
+  if (T == 0) return 0;
+  hipLaunchKernelGGL(k_stream_gather, dim3((unsigned)T), dim3(512), 0, (hipStream_t)stream,
+                     (const uint4 *)teacher, student, idx, V, K, out_i, out_f, out_l);
   return hipGetLastError() == hipSuccess ? 0 : 4;
 }
 

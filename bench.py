@@ -732,11 +732,27 @@ def cpu_baseline(case, fmt, group, n_experts):
     O.moe_layer(sub, wfmt, group, wfmt)
     dt = time.perf_counter() - t0
     flops = FLOPS_PER_ROW * R
+    # the oracle's weight codec alone (the FQ pass) on the same sampled
+    # stacks, scales from the observer beforehand; bytes as the GPU FQ pass
+    # counts them: 2 B read + 2 B written per element, plus the NVFP4 theta
+    stacks = []
+    for w in (sub.w_gu, sub.w_d):
+        g = group or w.shape[2]
+        stacks.append((w, g, O.observer_weight(w, wfmt, g)))
+    t1 = time.perf_counter()
+    for w, g, wq in stacks:
+        O.fq_weight_stack(w, wfmt, g, *wq)
+    dt_codec = time.perf_counter() - t1
+    n_el = sum(w.size for w, _, _ in stacks)
+    codec_bytes = 4 * n_el + (n_el // 16 * 4 if wfmt == O.FMT_NVFP4 else 0)
     return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": blas_threads(),
             "kind": "oracle", "seconds": round(dt, 2), "cpu_model": model,
             "affinity_cpus": cpus,
             "sample": f"experts 0..{E - 1} of the same layer and their {R} routed rows "
-                      f"(full fwd+bwd incl. observer init), {flops / 1e9:.1f} GFLOP"}
+                      f"(full fwd+bwd incl. observer init), {flops / 1e9:.1f} GFLOP",
+            "codec_GB/s": round(codec_bytes / dt_codec / 1e9, 3),
+            "codec_sample": f"the oracle's weight FQ over the same {E} experts' gate_up and down "
+                            f"stacks, {codec_bytes / 1e9:.3f} GB in {dt_codec:.2f} s"}
 
 
 def cpu_baseline_dense(case, cfg):

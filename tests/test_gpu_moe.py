@@ -56,8 +56,21 @@ def _abs_bits(bits):
 @pytest.mark.parametrize("name,wfmt,afmt,group,T,Eg,El,begin,zipf,learn", CASES)
 def test_moe_layer_stagewise_and_end_to_end(name, wfmt, afmt, group, T, Eg, El, begin, zipf,
                                             learn):
-    print(f"[moe] {name}", flush=True)
-    case = W.moe_case(T=T, fmt=name, E_global=Eg, H=256, F=256, topk=4, seed=11,
+    _check_layer(name, wfmt, afmt, group, T, Eg, El, begin, zipf, learn, 256, 256)
+
+
+@pytest.mark.parametrize("name,wfmt,afmt,group", [("nvfp4", O.FMT_NVFP4, O.FMT_NVFP4, 16),
+                                                  ("w8a8-int8", O.FMT_INT8, O.FMT_INT8, None)])
+def test_moe_layer_ffn_not_multiple_of_256(name, wfmt, afmt, group):
+    """The whole layer with hidden 272 and expert FFN 208 (2F = 416): every
+    GEMM runs on zero-padded copies inside its call; every stage is checked
+    against the oracle as in the layer test above."""
+    _check_layer(name, wfmt, afmt, group, 300, 8, 8, 0, None, False, 272, 208)
+
+
+def _check_layer(name, wfmt, afmt, group, T, Eg, El, begin, zipf, learn, H, Fh):
+    print(f"[moe] {name} H={H} F={Fh}", flush=True)
+    case = W.moe_case(T=T, fmt=name, E_global=Eg, H=H, F=Fh, topk=4, seed=11,
                       expert_begin=begin, E_local=El, zipf_s=zipf,
                       zero_experts=(3,) if zipf else ())
     L = _run_layer(case, wfmt, afmt, group, learn)

@@ -986,7 +986,15 @@ __device__ __forceinline__ int run_tile(const GemmArgs &a, const int *tile_start
         const int r = 4 * it + (ln >> 4);
         const uint4 v = *reinterpret_cast<const uint4 *>(
             slab + r * 256 + (((uint32_t)(ln & 15) ^ (uint32_t)(r & 15)) << 4));
-        if (jb + r < j_end) *reinterpret_cast<uint4 *>(obase + (size_t)(jb + r) * ldo) = v;
+        // whole 128-byte lines, stored non-temporally so that the output
+        // stream does not displace operand lines from the L2
+        if (jb + r < j_end) {
+          uint4 *dst = reinterpret_cast<uint4 *>(obase + (size_t)(jb + r) * ldo);
+          __builtin_nontemporal_store(v.x, &dst->x);
+          __builtin_nontemporal_store(v.y, &dst->y);
+          __builtin_nontemporal_store(v.z, &dst->z);
+          __builtin_nontemporal_store(v.w, &dst->w);
+        }
       }
     }
     wait_lgkm0();  // the slab is read back before buffer 1 takes the next tile's stage 1

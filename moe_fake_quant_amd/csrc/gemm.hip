@@ -565,12 +565,13 @@ struct TileLoads {
 // is done with this tile's LDS buffers, so that its loads run under this
 // tile's epilogue.
 template <int MODE, int WFMT>
-__device__ __forceinline__ void run_tile_lockstep(const GemmArgs &a, const int *tile_start,
-                                                  const Tile &tl, bool pre, int next_w) {
+__device__ __forceinline__ void run_tile_wgrad(const GemmArgs &a, const int *tile_start,
+                                               const Tile &tl, bool pre, int next_w) {
+  static_assert(MODE == WGRAD, "the lockstep loop serves the wgrad tiles");
   const int t = threadIdx.x;
   const int lane = t & 63, wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int wi = wave & 1, wj = wave >> 1;  // 2 x 4 waves: 128 (i) x 64 (j) each
-  const int e = tl.e, i0 = tl.i0, j0 = tl.j0, j_end = tl.j_end;
+  const int e = tl.e, i0 = tl.i0, j0 = tl.j0;
   const TileLoads<MODE> ld(a, tl, wave, lane);
   const int c_total = ld.c_total, nk = ld.nk;
 
@@ -588,11 +589,6 @@ __device__ __forceinline__ void run_tile_lockstep(const GemmArgs &a, const int *
     nl.template issue<0>(a, 0, wave);
     return true;
   };
-  auto prefetch_next = [&]() {
-    if (next_w < 0) return;
-    block_barrier();
-    prefetch_issue();
-  };
 
   f32x16 acc[4][2];
 #pragma unroll
@@ -606,22 +602,17 @@ __device__ __forceinline__ void run_tile_lockstep(const GemmArgs &a, const int *
   struct Frags {
     bf16x8v p[4], q[2];
   };
-  // TAIL: WGRAD's last stage, whose contraction rows past the chunk's last
-  // routed row are zeroed in the fragments
-  auto read_frags = [&](auto stage_tag, auto tail_tag, int kt, int ks, Frags &f) {
+  // contraction rows past the chunk's last routed row (its last stage) are
+  // zeroed in the fragments
+  auto read_frags = [&](auto stage_tag, int kt, int ks, Frags &f) {
     constexpr int S = decltype(stage_tag)::value;
-    constexpr bool TAIL = decltype(tail_tag)::value;
     const char *sp = stage_p<S>();
     const char *sq = stage_q<S>();
 #pragma unroll
-    for (int s = 0; s < 4; ++s)
-      f.p[s] = (MODE == FWD) ? frag_normal(sp, wi * 128 + s * 32, ks, lane)
-                             : frag_trans(sp, wi * 128 + s * 32, ks, lane);
+    for (int s = 0; s < 4; ++s) f.p[s] = frag_trans(sp, wi * 128 + s * 32, ks, lane);
 #pragma unroll
-    for (int u = 0; u < 2; ++u)
-      f.q[u] = (MODE == WGRAD) ? frag_trans(sq, wj * WJ_TILE + u * 32, ks, lane)
-                               : frag_normal(sq, wj * WJ_TILE + u * 32, ks, lane);
-    if (TAIL && (kt + 1) * BK > c_total) {
+    for (int u = 0; u < 2; ++u) f.q[u] = frag_trans(sq, wj * WJ_TILE + u * 32, ks, lane);
+    if ((kt + 1) * BK > c_total) {
       const int cfirst = kt * BK + 16 * ks + 8 * (lane >> 5);
 #pragma unroll
       for (int s = 0; s < 4; ++s) f.p[s] = zero_tail(f.p[s], cfirst, c_total);
@@ -639,102 +630,27 @@ __device__ __forceinline__ void run_tile_lockstep(const GemmArgs &a, const int *
   // Two-stage ring: stage kt lives in buffer kt % 2. After this wave's loads
   // of stage kt have landed, one barrier both publishes stage kt to every wave
   // and retires the reads of stage kt-1, whose buffer then takes stage kt+1
-  // while stage kt is multiplied. FWD / DGRAD read the fragments of step
-  // ks + 1 while the MFMAs of step ks run. LIVE / TAIL are compile-time so that each
-  // stage is one straight block of LDS reads and MFMAs.
-  auto step = [&](auto stage_tag, auto live_tag, auto tail_tag, int kt) {
+  // while stage kt is multiplied. One fragment set (two measured slower).
+  auto step = [&](auto stage_tag, int kt) {
     constexpr int S = decltype(stage_tag)::value;
-    constexpr bool LIVE = decltype(live_tag)::value;
     wait_vm<0>();
     block_barrier();
     if (kt + 1 < nk) issue(std::integral_constant<int, S ^ 1>{}, kt + 1);
-    if (!LIVE) return;
-    if (MODE == WGRAD) {  // measured faster without the second fragment set
-#pragma unroll
-      for (int ks = 0; ks < BK / 16; ++ks) {
-        Frags f;
-        read_frags(stage_tag, tail_tag, kt, ks, f);
-        mfmas(f);
-      }
-      return;
-    }
-    Frags f[2];
-    read_frags(stage_tag, tail_tag, kt, 0, f[0]);
 #pragma unroll
     for (int ks = 0; ks < BK / 16; ++ks) {
-      if (ks + 1 < BK / 16) read_frags(stage_tag, tail_tag, kt, ks + 1, f[(ks + 1) & 1]);
-      __builtin_amdgcn_sched_barrier(0);
-      mfmas(f[ks & 1]);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  };
-  // FWD / DGRAD: a wave whose 64 rows all lie past the expert's last row (the
-  // ragged last row tile) skips its fragment reads and MFMAs; it still takes
-  // part in the loads and barriers.
-  const bool live = MODE == WGRAD || j0 + wj * WJ_TILE < j_end;
-  auto step_any = [&](auto stage_tag, int kt) {
-    using T_ = std::true_type;
-    using F_ = std::false_type;
-    if (MODE == WGRAD) {
-      step(stage_tag, T_{}, T_{}, kt);
-    } else {
-      if (live) step(stage_tag, T_{}, F_{}, kt);
-      else step(stage_tag, F_{}, F_{}, kt);
+      Frags f;
+      read_frags(stage_tag, kt, ks, f);
+      mfmas(f);
     }
   };
   if (nk > 0 && !pre) issue(std::integral_constant<int, 0>{}, 0);
   for (int kt = 0; kt < nk; kt += NSTAGE) {
-    step_any(std::integral_constant<int, 0>{}, kt);
-    if (kt + 1 < nk) step_any(std::integral_constant<int, 1>{}, kt + 1);
+    step(std::integral_constant<int, 0>{}, kt);
+    if (kt + 1 < nk) step(std::integral_constant<int, 1>{}, kt + 1);
   }
 
   // accumulator (s, u, v) of this lane: i = i0 + wi*128 + s*32 + 8*(v/4) + 4*(lane/32) + v%4,
   //                                     j = j0 + wj*64 + u*32 + lane%32
-  if (MODE != WGRAD) {
-    // The bf16 tile goes out through LDS: each wave writes its 128 (i) x 32 (j)
-    // half-slab row by row into ring buffer 1 (free until the next tile's
-    // second stage; waves 0-3 in the P half, 4-7 in the Q half, 8 KiB each),
-    // then stores whole 256-byte row segments, 16 bytes per lane. Direct
-    // stores from the accumulator layout would write each 128-byte line in
-    // 16-byte pieces from eight instructions. Row r of the slab is 16 chunks
-    // of 16 bytes; chunk c sits at c ^ (r & 15), so the lanes of a write (32
-    // rows, one chunk) and of a read (one row per 16 lanes) spread over the
-    // banks.
-    if (next_w >= 0) prefetch_next();  // (its barrier also retires buffer 1)
-    else block_barrier();
-    const int ldo = (MODE == FWD) ? a.N : a.K;
-    char *slab = (wave < 4 ? stage_p<1>() : stage_q<1>()) + (wave & 3) * 8192;
-    // lane terms formed here (an empty asm keeps the compiler from hoisting
-    // the addresses derived from them into the contraction loop's registers)
-    int ln = lane;
-    asm volatile("" : "+v"(ln));
-    const int h = ln >> 5, jr = ln & 31;
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      if (!live) break;
-#pragma unroll
-      for (int s = 0; s < 4; ++s)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          uint2 pk;
-          pk.x = pack_bf16(acc[s][u][4 * q + 0], acc[s][u][4 * q + 1]);
-          pk.y = pack_bf16(acc[s][u][4 * q + 2], acc[s][u][4 * q + 3]);
-          const uint32_t c = (uint32_t)(4 * s + q) ^ (uint32_t)(jr & 15);
-          *reinterpret_cast<uint2 *>(slab + jr * 256 + c * 16 + h * 8) = pk;
-        }
-      const int jb = j0 + wj * WJ_TILE + u * 32;
-      uint16_t *obase = a.out + (size_t)i0 + wi * 128 + (ln & 15) * 8;
-#pragma unroll
-      for (int it = 0; it < 8; ++it) {
-        const int r = 4 * it + (ln >> 4);
-        const uint4 v = *reinterpret_cast<const uint4 *>(
-            slab + r * 256 + (((uint32_t)(ln & 15) ^ (uint32_t)(r & 15)) << 4));
-        if (jb + r < j_end) *reinterpret_cast<uint4 *>(obase + (size_t)(jb + r) * ldo) = v;
-      }
-    }
-    return;
-  }
-
   // ---- WGRAD epilogue: i = k, j = n of expert e. dS over groups along k.
   {
     // The raw weights come in through ring buffer 1 (free once every wave has
@@ -800,17 +716,18 @@ __device__ __forceinline__ void run_tile_lockstep(const GemmArgs &a, const int *
 template <int MODE, int WFMT>
 __device__ __forceinline__ int run_tile(const GemmArgs &a, const int *tile_start, const Tile &tl,
                                         int pre, int next_w) {
+  static_assert(MODE != WGRAD, "the ping-pong serves the forward and dgrad tiles");
   const int t = threadIdx.x;
   const int lane = t & 63, wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int wi = wave & 1, wj = wave >> 1;  // 2 x 4 waves: 128 (i) x 64 (j) each
   const bool grp_b = wave >= 4;             // j columns 128..255 of the tile
-  const int e = tl.e, i0 = tl.i0, j0 = tl.j0, j_end = tl.j_end;
+  const int i0 = tl.i0, j0 = tl.j0, j_end = tl.j_end;
   const TileLoads<MODE> ld(a, tl, wave, lane);
-  const int c_total = ld.c_total, nk = ld.nk;
-  // FWD / DGRAD: a wave whose 64 rows all lie past the expert's last row (the
-  // ragged last row tile) skips its fragment reads and MFMAs; it still takes
-  // part in the loads and barriers.
-  const bool live = MODE == WGRAD || j0 + wj * WJ_TILE < j_end;
+  const int nk = ld.nk;
+  // a wave whose 64 rows all lie past the expert's last row (the ragged last
+  // row tile) skips its fragment reads and MFMAs; it still takes part in the
+  // loads and barriers
+  const bool live = j0 + wj * WJ_TILE < j_end;
 
   f32x16 acc[4][2];
 #pragma unroll
@@ -826,9 +743,8 @@ __device__ __forceinline__ int run_tile(const GemmArgs &a, const int *tile_start
     bf16x8v p[4], q[2];
   };
   Frags f[2];
-  // half h of stage kt from buffer S; WGRAD's last stage: contraction rows
-  // past the chunk's last routed row are zeroed in the fragments
-  auto read_half = [&](auto stage_tag, int kt, int h) {
+  // half h of stage kt from buffer S
+  auto read_half = [&](auto stage_tag, int h) {
     constexpr int S = decltype(stage_tag)::value;
     const char *sp = stage_p<S>();
     const char *sq = stage_q<S>();
@@ -840,19 +756,7 @@ __device__ __forceinline__ int run_tile(const GemmArgs &a, const int *tile_start
         f[k2].p[s] = (MODE == FWD) ? frag_normal(sp, wi * 128 + s * 32, ks, lane)
                                    : frag_trans(sp, wi * 128 + s * 32, ks, lane);
 #pragma unroll
-      for (int u = 0; u < 2; ++u)
-        f[k2].q[u] = (MODE == WGRAD) ? frag_trans(sq, wj * WJ_TILE + u * 32, ks, lane)
-                                     : frag_normal(sq, wj * WJ_TILE + u * 32, ks, lane);
-    }
-    if (MODE == WGRAD && (kt + 1) * BK > c_total) {
-#pragma unroll
-      for (int k2 = 0; k2 < 2; ++k2) {
-        const int cfirst = kt * BK + 16 * (2 * h + k2) + 8 * (lane >> 5);
-#pragma unroll
-        for (int s = 0; s < 4; ++s) f[k2].p[s] = zero_tail(f[k2].p[s], cfirst, c_total);
-#pragma unroll
-        for (int u = 0; u < 2; ++u) f[k2].q[u] = zero_tail(f[k2].q[u], cfirst, c_total);
-      }
+      for (int u = 0; u < 2; ++u) f[k2].q[u] = frag_normal(sq, wj * WJ_TILE + u * 32, ks, lane);
     }
   };
   auto multiply = [&]() {
@@ -878,14 +782,14 @@ __device__ __forceinline__ int run_tile(const GemmArgs &a, const int *tile_start
     phase_barrier();  // 4kt
     if (live) multiply();
     phase_barrier();  // 4kt+1
-    if (live) read_half(stage_tag, kt, 1);
+    if (live) read_half(stage_tag, 1);
     wait_lgkm0();
     phase_barrier();  // 4kt+2
     if (live) multiply();
     if (kt + 1 < nk) {
       wait_vm<0>();  // this wave's share of stage kt+1
       phase_barrier();  // 4kt+3
-      if (live) read_half(std::integral_constant<int, S ^ 1>{}, kt + 1, 0);
+      if (live) read_half(std::integral_constant<int, S ^ 1>{}, 0);
       wait_lgkm0();
       if (kt + 2 < nk) ld.template issue<S>(a, kt + 2, wave);
     }
@@ -894,12 +798,12 @@ __device__ __forceinline__ int run_tile(const GemmArgs &a, const int *tile_start
   auto b_step = [&](auto stage_tag, int kt) {
     constexpr int S = decltype(stage_tag)::value;
     phase_barrier();  // 4kt
-    if (live) read_half(stage_tag, kt, 0);
+    if (live) read_half(stage_tag, 0);
     wait_lgkm0();
     phase_barrier();  // 4kt+1
     if (live) multiply();
     phase_barrier();  // 4kt+2
-    if (live) read_half(stage_tag, kt, 1);
+    if (live) read_half(stage_tag, 1);
     wait_lgkm0();
     if (kt + 2 < nk) {
       ld.template issue<S>(a, kt + 2, wave);
@@ -919,7 +823,7 @@ __device__ __forceinline__ int run_tile(const GemmArgs &a, const int *tile_start
     else wait_vm<kVmPerStageA<MODE>>();
     phase_barrier();
     if (!grp_b) {
-      if (live) read_half(std::integral_constant<int, 0>{}, 0, 0);
+      if (live) read_half(std::integral_constant<int, 0>{}, 0);
       wait_lgkm0();
       for (int kt = 0; kt < nk; kt += 2) {
         a_step(std::integral_constant<int, 0>{}, kt);
@@ -951,7 +855,7 @@ __device__ __forceinline__ int run_tile(const GemmArgs &a, const int *tile_start
 
   // accumulator (s, u, v) of this lane: i = i0 + wi*128 + s*32 + 8*(v/4) + 4*(lane/32) + v%4,
   //                                     j = j0 + wj*64 + u*32 + lane%32
-  if (MODE != WGRAD) {
+  {
     (void)issue_next(std::integral_constant<int, 0>{});
     // The bf16 tile goes out through LDS: each wave writes its 128 (i) x 32 (j)
     // half-slab row by row into its 8 KiB of buffer 1, then stores whole
@@ -998,32 +902,6 @@ __device__ __forceinline__ int run_tile(const GemmArgs &a, const int *tile_start
       }
     }
     wait_lgkm0();  // the slab is read back before buffer 1 takes the next tile's stage 1
-  } else {
-    // ---- WGRAD epilogue: i = k, j = n of expert e. dS over groups along k.
-    // The raw weights come in through this wave's 8 KiB of buffer 1, its two
-    // 32-row slabs one after the other: whole-row DMA instead of 8-byte loads
-    // from 32 rows per instruction. Only the wave itself reads its slab, so
-    // its own waits order the accesses.
-    const int k0 = i0 + wi * 128, n0 = j0 + wj * WJ_TILE;
-    uint2 wv[4][4];
-    auto load_theta = [&](int nn) {
-      if (WFMT != FQ_FMT_NVFP4) return float4{0.0f, 0.0f, 0.0f, 0.0f};
-      const size_t srow = ((size_t)e * a.N + nn + (lane & 31)) * (a.K / a.group);
-      return *reinterpret_cast<const float4 *>(a.scale + srow + k0 / 16 + 4 * (lane >> 5));
-    };
-    const float4 th0 = load_theta(n0);
-    wgrad_dma_w(a, e, k0, n0, lane, slab);
-    if (issue_next(std::integral_constant<int, 0>{})) wait_vm<8>();  // the slab, not the next stage
-    else wait_vm<0>();
-    wgrad_read_w(slab, lane, wv);
-    wait_lgkm0();  // read back before the slab is reused
-    wgrad_dma_w(a, e, k0, n0 + 32, lane, slab);
-    const float4 th1 = load_theta(n0 + 32);
-    wgrad_epilogue<WFMT, 0>(a, acc, e, k0, n0, lane, wv, tl.chunk, th0);
-    wait_vm<0>();
-    wgrad_read_w(slab, lane, wv);
-    wgrad_epilogue<WFMT, 1>(a, acc, e, k0, n0 + 32, lane, wv, tl.chunk, th1);
-    wait_lgkm0();
   }
   // every wave's staging in buffer 1 is done: stage 1 of the next tile
   block_barrier();
@@ -1058,8 +936,8 @@ __global__ __launch_bounds__(NT) void k_grouped_gemm(GemmArgs a) {
   for (int w = xcd * chunk + slot; w < w_end; w += nslot) {
     const int next = w + nslot < w_end ? w + nslot : -1;
     const Tile tl = decode_tile<MODE>(a, tile_start, w);
-    if (MODE == WGRAD) {
-      run_tile_lockstep<MODE, WFMT>(a, tile_start, tl, pre != 0, next);
+    if constexpr (MODE == WGRAD) {
+      run_tile_wgrad<MODE, WFMT>(a, tile_start, tl, pre != 0, next);
       pre = next >= 0;
     } else {
       pre = run_tile<MODE, WFMT>(a, tile_start, tl, pre, next);

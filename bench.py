@@ -609,6 +609,35 @@ def main():
     print(json.dumps(line), flush=True)
 
 
+def graph_replay(torch, step, outs, steps, flops_step):
+    """The same step captured once in a HIP graph (torch.cuda.CUDAGraph over
+    the ABI calls) and replayed `steps` times between the same device syncs:
+    the rate without the host's per-kernel launch cost, which is most of a
+    small step. The replay's outputs are compared bit for bit with the eager
+    step's before it is timed."""
+    torch.cuda.synchronize()
+    eager = [t.clone() for t in outs]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for t in outs:
+        t.zero_()
+    g.replay()
+    torch.cuda.synchronize()
+    same = all(torch.equal(a.view(torch.uint8), b.view(torch.uint8)) for a, b in zip(outs, eager))
+    for _ in range(3):
+        g.replay()
+    ms, _ = time_steps(torch, g.replay, steps)
+    return {"us_per_step": round(ms * 1e3, 2), "TFLOP/s": round(flops_step / (ms * 1e-3) / 1e12, 3),
+            "bitwise_equal_to_eager": same}
+
+
 def dense_main(args):
     """The dense single-linear workloads (one expert, seg = [0, M]): one step =
     FQ pass over W, forward Y = X . FQ(W)^T, backward dX and dScale (weights
@@ -667,6 +696,8 @@ def dense_main(args):
         per[name] = ms
     flops_step = 6 * M * N * K
     tflops = flops_step / (ms_step * 1e-3) / 1e12
+    graph = graph_replay(torch, step, tuple(t for t in (wfq, y, dx, ds, dzp) if t is not None),
+                         steps, flops_step)
     kind_flops = 2 * M * N * K
     kernels = {k: {"ms_per_step": round(per[k], 4), "avg_launch_ms": round(per[k], 4),
                    "TFLOP/s": round(kind_flops / (per[k] * 1e-3) / 1e12, 2)}
@@ -705,6 +736,7 @@ def dense_main(args):
         "timing": {"headline": "HIP events around the timed steps, no per-call events",
                    "breakdown": "each call timed alone over the same number of reps"},
         "gemm_kernels": kernels,
+        "graph_replay": graph,
         "measured_peaks": peaks,
         "ms_per_step_by_call": {k: round(v, 5) for k, v in per.items()},
         "cpu_baseline": cpu,

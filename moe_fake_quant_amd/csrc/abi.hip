@@ -497,10 +497,10 @@ void gemm_bwd_core(const uint16_t *dy, const uint16_t *x, int R_max, const int32
       float *dch = c.take<float>((size_t)s.E * s.N * 4);
       launch_repeat_rows(wq->scale, s.E, s.N, rep, st);
       fq_weight_q qc{wq->fmt, s.K, rep, nullptr, nullptr};
-      launch_gemm_wgrad_dscale(dy, xq, seg, s, w, qc, dch, nullptr, ps, nullptr, cs, st);
+      launch_gemm_wgrad_dscale(dy, xq, R_max, seg, s, w, qc, dch, nullptr, ps, nullptr, cs, st);
       launch_sum_rows(dch, s.E, s.N, dscale, st);
     } else {
-      launch_gemm_wgrad_dscale(dy, xq, seg, s, w, *wq, dscale, dzp, ps, dzp ? pz : nullptr, cs,
+      launch_gemm_wgrad_dscale(dy, xq, R_max, seg, s, w, *wq, dscale, dzp, ps, dzp ? pz : nullptr, cs,
                                st);
     }
   }

@@ -36,6 +36,7 @@
 // LDS), so empty experts cost nothing and no host sync is needed. Each of the
 // 8 XCDs owns a contiguous eighth of the tiles, keeping the panels its blocks
 // share in its own L2.
+#include <atomic>
 #include <type_traits>
 
 #include "internal.hpp"
@@ -981,13 +982,32 @@ __global__ __launch_bounds__(256) void k_reduce_dscale(const float *__restrict__
 }  // namespace
 
 // ============================================================ launchers ====
-// one block per CU, a multiple of 8 (the XCD count)
-static int persistent_grid() {
-  int dev = 0, cus = 256;
-  if (hipGetDevice(&dev) == hipSuccess)
-    (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+// One block per CU, a multiple of 8 (the XCD count), but no more blocks than
+// an upper bound on the work units of the call (a small call then launches a
+// small grid). The CU count is read once per device.
+static int gemm_grid(size_t max_units) {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<int> cached[kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) dev = -1;
+  int cus = dev >= 0 ? cached[dev].load(std::memory_order_relaxed) : 0;
+  if (cus <= 0) {
+    cus = 256;
+    if (dev >= 0) {
+      (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+      cached[dev].store(cus, std::memory_order_relaxed);
+    }
+  }
   cus = cus / 8 * 8;
-  return cus > 0 ? cus : 8;
+  if (cus <= 0) cus = 8;
+  const size_t units8 = (max_units + 7) / 8 * 8;
+  return (int)(units8 < (size_t)cus ? (units8 > 0 ? units8 : 8) : (size_t)cus);
+}
+
+// FWD / DGRAD units: row tiles (at most ceil(R_max / BJ) + E, one partial
+// tile per expert) times the i tiles
+static size_t rowtile_units(int R_max, int E, int n_it) {
+  return ((size_t)(R_max + BJ - 1) / BJ + (size_t)E) * (size_t)n_it;
 }
 
 void launch_gemm_fwd(const uint16_t *xq, int R_max, const int32_t *seg, fq_shape s,
@@ -1002,7 +1022,8 @@ void launch_gemm_fwd(const uint16_t *xq, int R_max, const int32_t *seg, fq_shape
   a.n_it = s.N / BI;
   a.out = y;
   if (R_max <= 0) return;
-  hipLaunchKernelGGL((k_grouped_gemm<FWD, 0>), dim3(persistent_grid()), dim3(NT), 0, st, a);
+  hipLaunchKernelGGL((k_grouped_gemm<FWD, 0>), dim3(gemm_grid(rowtile_units(R_max, s.E, a.n_it))),
+                     dim3(NT), 0, st, a);
 }
 
 void launch_gemm_dgrad(const uint16_t *dy, int R_max, const int32_t *seg, fq_shape s,
@@ -1017,14 +1038,16 @@ void launch_gemm_dgrad(const uint16_t *dy, int R_max, const int32_t *seg, fq_sha
   a.n_it = s.K / BI;
   a.out = dx;
   if (R_max <= 0) return;
-  hipLaunchKernelGGL((k_grouped_gemm<DGRAD, 0>), dim3(persistent_grid()), dim3(NT), 0, st, a);
+  hipLaunchKernelGGL((k_grouped_gemm<DGRAD, 0>), dim3(gemm_grid(rowtile_units(R_max, s.E, a.n_it))),
+                     dim3(NT), 0, st, a);
 }
 
 size_t wgrad_max_chunks(int E, int R_max) {
   return (size_t)(R_max + kWgradChunkRows - 1) / kWgradChunkRows + E;
 }
 
-void launch_gemm_wgrad_dscale(const uint16_t *dy, const uint16_t *xq, const int32_t *seg, fq_shape s,
+void launch_gemm_wgrad_dscale(const uint16_t *dy, const uint16_t *xq, int R_max, const int32_t *seg,
+                              fq_shape s,
                               const uint16_t *w, const fq_weight_q &q, float *dscale, float *dzp,
                               float *part_s, float *part_z, int *chunk_start, hipStream_t st) {
   GemmArgs a{};
@@ -1049,7 +1072,7 @@ void launch_gemm_wgrad_dscale(const uint16_t *dy, const uint16_t *xq, const int3
   a.part_s = part_s;
   a.part_z = part_z;
   a.chunk_start_out = chunk_start;
-  dim3 grid(persistent_grid()), block(NT);
+  dim3 grid(gemm_grid(wgrad_max_chunks(s.E, R_max) * (size_t)a.n_it * (size_t)a.n_jt)), block(NT);
   switch (q.fmt) {
     case FQ_FMT_INT8: hipLaunchKernelGGL((k_grouped_gemm<WGRAD, FQ_FMT_INT8>), grid, block, 0, st, a); break;
     case FQ_FMT_INT4: hipLaunchKernelGGL((k_grouped_gemm<WGRAD, FQ_FMT_INT4>), grid, block, 0, st, a); break;

@@ -86,7 +86,8 @@ constexpr int kWgradChunkRows = 2048;
 size_t wgrad_max_chunks(int E, int R_max);
 // part_s / part_z: [wgrad_max_chunks, N, K / min(group, 128)] fp32 scratch;
 // chunk_start: [E+1] int scratch. dzp / part_z only for int4.
-void launch_gemm_wgrad_dscale(const uint16_t *dy, const uint16_t *xq, const int32_t *seg, fq_shape s,
+void launch_gemm_wgrad_dscale(const uint16_t *dy, const uint16_t *xq, int R_max, const int32_t *seg,
+                              fq_shape s,
                               const uint16_t *w, const fq_weight_q &q, float *dscale, float *dzp,
                               float *part_s, float *part_z, int *chunk_start, hipStream_t st);
 

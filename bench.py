@@ -1,8 +1,9 @@
 """Benchmark of the scale-only fake-quant MoE hot path on one MI355X.
 
 One step = the whole routed-expert path of one MoE layer: the stacked
-fake-quant pass over both weight stacks, permutation, gather + activation FQ,
-gate_up grouped GEMM, SwiGLU + activation FQ, down grouped GEMM, combine, and
+fake-quant pass over both weight stacks, permutation, activation FQ of each
+token row, gate_up grouped GEMM (routed rows read as token rows through the
+routing), SwiGLU + activation FQ, down grouped GEMM, combine, and
 the backward to dX and the weight-scale gradients (dScale) only.
 
 Workload (default): Qwen3-30B-A3B-shaped layer, 128 experts, hidden 2048,
@@ -56,7 +57,7 @@ def hbm_pass_bytes(T, H, Fh, R, topk):
     once, every output written once (bf16 2 B, fp32 / int32 4 B)."""
     return {
         "fq_moe_permute": 12 * T * topk,
-        "fq_moe_gather_actfq": 2 * T * H + 2 * R * H + 4 * T * topk,
+        "fq_actfq": 4 * T * H,
         "fq_swiglu_actfq": R * (4 * Fh + 2 * Fh),
         "fq_moe_combine": 2 * R * H + 8 * T * topk + 2 * T * H,
         "fq_moe_combine_bwd": 2 * T * H + 8 * T * topk + 2 * R * H,
@@ -447,13 +448,15 @@ def main():
     import moe_fake_quant_amd.layer as LM
     keys = {
         "fq_grouped_gemm_fwd": lambda a: "gemm_fwd",
+        "fq_grouped_gemm_fwd_tokens": lambda a: "gemm_fwd",
         "fq_grouped_gemm_bwd_scale": lambda a: "gemm_dgrad" if a[9] is not None else "gemm_wgrad_dscale",
+        "fq_grouped_gemm_wgrad_tokens": lambda a: "gemm_wgrad_dscale",
         "fq_quantize_stacked": lambda a: "fq_quantize_stacked",
     }
-    for name in ("fq_quantize_stacked", "fq_moe_permute", "fq_moe_gather_actfq",
-                 "fq_grouped_gemm_fwd", "fq_swiglu_actfq", "fq_moe_combine",
-                 "fq_moe_combine_bwd", "fq_grouped_gemm_bwd_scale", "fq_swiglu_bwd",
-                 "fq_moe_unpermute_reduce"):
+    for name in ("fq_quantize_stacked", "fq_moe_permute", "fq_actfq",
+                 "fq_grouped_gemm_fwd", "fq_grouped_gemm_fwd_tokens", "fq_swiglu_actfq",
+                 "fq_moe_combine", "fq_moe_combine_bwd", "fq_grouped_gemm_bwd_scale",
+                 "fq_grouped_gemm_wgrad_tokens", "fq_swiglu_bwd", "fq_moe_unpermute_reduce"):
         setattr(LM, name, timer.wrap(keys.get(name, lambda a, n=name: n), getattr(LM, name)))
 
     layer.overlap_wgrad = not args.no_overlap

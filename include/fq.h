@@ -358,6 +358,44 @@ fq_status fq_grouped_gemm_bwd_scale(const uint16_t *dy_bf16, const uint16_t *x_b
                                     void *ws, size_t ws_bytes, fq_stream stream);
 
 /* ------------------------------------------------------------------------
+ * The expert input as token rows. The forward pre-hook fake-quantizes a
+ * token's input once, however many experts it is routed to (mcore_qad
+ * article, section 二.3). The grouped GEMM (section 二.4) can then read
+ * routed row r as token row perm[r] / topk, and the [R, K] gathered copy is
+ * never formed.
+ *
+ * fq_actfq: xq = FQ_a(x), row by row (NVFP4: 16-blocks along K).
+ *   x, xq [rows, K] bf16, K % 16 == 0. aq NULL or FMT_NONE copies x.
+ * fq_grouped_gemm_fwd_tokens: fq_grouped_gemm_fwd with, for every routed
+ *   row r < seg_offsets[E], x_bf16[r] = x_tok[perm[r] / topk].
+ *   x_tok [T, K] is already fake-quantized, so the call takes no
+ *   activation quantizer. perm [>= seg_offsets[E]] is fq_moe_permute's
+ *   (the (token, slot) pair index of each routed row), topk its slot count.
+ * fq_grouped_gemm_wgrad_tokens: the dScale (and int4 dzero_point) part of
+ *   fq_grouped_gemm_bwd_scale, with the same row map for x. dX does not
+ *   read x, so it stays with fq_grouped_gemm_bwd_scale.
+ * Results are bitwise those of the plain calls on the gathered rows.
+ * Requirements and errors are the plain calls', plus T >= 0, topk > 0, and
+ * perm / x_tok non-NULL unless R_max == 0.
+ * Workspace: fq_workspace_bytes(FQ_OP_GEMM_FWD, shape, max(R_max, T),
+ *   w_fq ? 0 : wq->fmt), resp. fq_workspace_bytes(FQ_OP_GEMM_BWD, shape,
+ *   max(R_max, T), 0); the zero-padded path copies the T token rows.
+ * ---------------------------------------------------------------------- */
+fq_status fq_actfq(const uint16_t *x_bf16, int32_t rows, int32_t K, const fq_act_q *aq,
+                   uint16_t *xq_bf16, fq_stream stream);
+fq_status fq_grouped_gemm_fwd_tokens(const uint16_t *x_tok_bf16, int32_t T, const int32_t *perm,
+                                     int32_t topk, int32_t R_max, const int32_t *seg_offsets,
+                                     fq_shape shape, const uint16_t *w_bf16, const uint16_t *w_fq,
+                                     const fq_weight_q *wq, uint16_t *y_bf16, void *ws,
+                                     size_t ws_bytes, fq_stream stream);
+fq_status fq_grouped_gemm_wgrad_tokens(const uint16_t *dy_bf16, const uint16_t *x_tok_bf16,
+                                       int32_t T, const int32_t *perm, int32_t topk,
+                                       int32_t R_max, const int32_t *seg_offsets, fq_shape shape,
+                                       const uint16_t *w_bf16, const fq_weight_q *wq,
+                                       float *dscale, float *dzero_point, void *ws,
+                                       size_t ws_bytes, fq_stream stream);
+
+/* ------------------------------------------------------------------------
  * MoE-layer elementwise steps around the grouped GEMMs (the routed-expert
  * path of one layer: gather -> gate_up GEMM -> SwiGLU -> down GEMM ->
  * combine, and its backward). R = seg_offsets[E] is read on the device

@@ -46,7 +46,8 @@ EXPORTED = (
     "fq_grouped_gemm_bwd_scale", "fq_moe_gather_actfq", "fq_swiglu_actfq", "fq_swiglu_bwd",
     "fq_moe_combine", "fq_moe_combine_bwd", "fq_moe_unpermute_reduce", "fq_workspace_bytes",
     "fq_last_error", "fq_abi_version", "fq_export_scales", "fq_dequantize_stacked", "fq_topk_kl",
-    "fq_moe_permute_noalloc", "fq_validate",
+    "fq_moe_permute_noalloc", "fq_validate", "fq_actfq", "fq_grouped_gemm_fwd_tokens",
+    "fq_grouped_gemm_wgrad_tokens",
 )
 
 FQ_BAD_EXPERT_ID = 0x01
@@ -97,6 +98,11 @@ def _load() -> ctypes.CDLL:
         "fq_grouped_gemm_bwd_scale": (st, [P, P, I32, P, fq_shape, P, P,
                                            ctypes.POINTER(fq_weight_q), ctypes.POINTER(fq_act_q),
                                            P, P, P, P, SZ, P]),
+        "fq_actfq": (st, [P, I32, I32, ctypes.POINTER(fq_act_q), P, P]),
+        "fq_grouped_gemm_fwd_tokens": (st, [P, I32, P, I32, I32, P, fq_shape, P, P,
+                                            ctypes.POINTER(fq_weight_q), P, P, SZ, P]),
+        "fq_grouped_gemm_wgrad_tokens": (st, [P, P, I32, P, I32, I32, P, fq_shape, P,
+                                              ctypes.POINTER(fq_weight_q), P, P, P, SZ, P]),
         "fq_moe_gather_actfq": (st, [P, I32, I32, P, I32, ctypes.POINTER(fq_act_q), P, P]),
         "fq_swiglu_actfq": (st, [P, I32, P, I32, ctypes.POINTER(fq_act_q), P, P, P]),
         "fq_swiglu_bwd": (st, [P, P, I32, P, I32, ctypes.POINTER(fq_act_q), P, P, P, SZ, P]),
@@ -239,6 +245,26 @@ def fq_grouped_gemm_bwd_scale(dy, x, R_max, seg_offsets, shape, w, w_fq, wq: Wei
                                           _shape(*shape), _p(w), _p(w_fq), ctypes.byref(wq.c()),
                                           _aq(aq), _p(dx), _p(dscale), _p(dzero_point), _p(ws),
                                           _nbytes(ws), _stream()))
+
+
+def fq_actfq(x, rows, K, aq: Optional[ActQ], xq):
+    _check(_lib.fq_actfq(_p(x), int(rows), int(K), _aq(aq), _p(xq), _stream()))
+
+
+def fq_grouped_gemm_fwd_tokens(x_tok, T, perm, topk, R_max, seg_offsets, shape, w, w_fq,
+                               wq: Optional[WeightQ], y, ws=None):
+    _check(_lib.fq_grouped_gemm_fwd_tokens(_p(x_tok), int(T), _p(perm), int(topk), int(R_max),
+                                           _p(seg_offsets), _shape(*shape), _p(w), _p(w_fq),
+                                           ctypes.byref(wq.c()) if wq is not None else None,
+                                           _p(y), _p(ws), _nbytes(ws), _stream()))
+
+
+def fq_grouped_gemm_wgrad_tokens(dy, x_tok, T, perm, topk, R_max, seg_offsets, shape, w,
+                                 wq: WeightQ, dscale, dzero_point=None, ws=None):
+    _check(_lib.fq_grouped_gemm_wgrad_tokens(_p(dy), _p(x_tok), int(T), _p(perm), int(topk),
+                                             int(R_max), _p(seg_offsets), _shape(*shape), _p(w),
+                                             ctypes.byref(wq.c()), _p(dscale), _p(dzero_point),
+                                             _p(ws), _nbytes(ws), _stream()))
 
 
 def fq_moe_gather_actfq(x, T, H, row_of, topk, aq: Optional[ActQ], xq):

@@ -385,7 +385,7 @@ namespace {
 // arguments already checked, workspace large enough.
 void gemm_fwd_core(const uint16_t *x, int R_max, const int32_t *seg, fq_shape s, const uint16_t *w,
                    const uint16_t *w_fq, const fq_weight_q *wq, const fq_act_q *aq, uint16_t *y,
-                   void *ws, hipStream_t st) {
+                   void *ws, hipStream_t st, const int32_t *xperm, int topk) {
   const int afmt = act_fmt(aq);
   Carver c(ws);
   const uint16_t *wfq = w_fq;
@@ -400,15 +400,16 @@ void gemm_fwd_core(const uint16_t *x, int R_max, const int32_t *seg, fq_shape s,
     launch_act_fq(x, R_max, s.K, seg + s.E, afmt, aq->scale, t, st);
     xq = t;
   }
-  launch_gemm_fwd(xq, R_max, seg, s, wfq, y, st);
+  launch_gemm_fwd(xq, R_max, seg, s, wfq, y, st, xperm, topk);
 }
 
-}  // namespace
-
-fq_status fq_grouped_gemm_fwd(const uint16_t *x, int32_t R_max, const int32_t *seg, fq_shape s,
-                              const uint16_t *w, const uint16_t *w_fq, const fq_weight_q *wq,
-                              const fq_act_q *aq, uint16_t *y, void *ws, size_t ws_bytes,
-                              fq_stream stream) {
+// fq_grouped_gemm_fwd and its routed-X form: x has x_rows rows; with xperm
+// routed row r reads row xperm[r] / topk of x (then aq is NULL)
+fq_status gemm_fwd_call(const char *fn, const uint16_t *x, int32_t x_rows, const int32_t *xperm,
+                        int32_t topk, int32_t R_max, const int32_t *seg, fq_shape s,
+                        const uint16_t *w, const uint16_t *w_fq, const fq_weight_q *wq,
+                        const fq_act_q *aq, uint16_t *y, void *ws, size_t ws_bytes,
+                        fq_stream stream) {
   FQ_TRY(check_shape(s));
   FQ_CHECK_ARG(R_max >= 0, "R_max < 0");
   FQ_CHECK_ARG(seg && y && (x || R_max == 0), "x, seg_offsets and y must be non-NULL");
@@ -420,22 +421,23 @@ fq_status fq_grouped_gemm_fwd(const uint16_t *x, int32_t R_max, const int32_t *s
                      "grouped GEMM needs N %% 16 == 0 and K %% 16 == 0 (N=%d K=%d)", s.N, s.K);
   FQ_CHECK_SUPPORTED(s.E <= 1024, "grouped GEMM supports up to 1024 experts per stack (E=%d)", s.E);
   const fq_shape p = gemm_pad_shape(FQ_OP_GEMM_FWD, s);
-  FQ_CHECK_SUPPORTED((size_t)R_max * p.K * 2 < (1ull << 32) && (size_t)p.N * p.K * 2 < (1ull << 32),
+  const int32_t rows_ws = x_rows > R_max ? x_rows : R_max;
+  FQ_CHECK_SUPPORTED((size_t)rows_ws * p.K * 2 < (1ull << 32) && (size_t)p.N * p.K * 2 < (1ull << 32),
                      "operands must stay below 4 GiB (32-bit tile offsets)");
   FQ_CHECK_ARG((!x || aligned16(x)) && aligned16(y) && (!w || aligned16(w)) &&
                    (!w_fq || aligned16(w_fq)),
                "bf16 tensors must be 16-byte aligned");
   const int afmt = act_fmt(aq);
   const int fmts = (w_fq ? 0 : wq->fmt) | (afmt << 8);
-  size_t need = gemm_ws(FQ_OP_GEMM_FWD, s, R_max, fmts);
+  size_t need = gemm_ws(FQ_OP_GEMM_FWD, s, rows_ws, fmts);
   if (need > 0 && (ws_bytes < need || !ws)) {
-    set_error("fq_grouped_gemm_fwd: workspace %zu bytes < %zu needed", ws_bytes, need);
+    set_error("%s: workspace %zu bytes < %zu needed", fn, ws_bytes, need);
     return FQ_ERR_WORKSPACE_TOO_SMALL;
   }
   hipStream_t st = S(stream);
   if (!gemm_needs_pad(FQ_OP_GEMM_FWD, s)) {
-    gemm_fwd_core(x, R_max, seg, s, w, w_fq, wq, aq, y, ws, st);
-    FQ_CHECK_LAUNCH("fq_grouped_gemm_fwd");
+    gemm_fwd_core(x, R_max, seg, s, w, w_fq, wq, aq, y, ws, st, xperm, topk);
+    FQ_CHECK_LAUNCH(fn);
     return FQ_OK;
   }
   // zero-padded to the kernels' shape: padded K columns add nothing, padded
@@ -449,13 +451,37 @@ fq_status fq_grouped_gemm_fwd(const uint16_t *x, int32_t R_max, const int32_t *s
   }
   uint16_t *wfq_p = c.take<uint16_t>((size_t)s.E * p.N * p.K * 2);
   launch_reshape_u16(wfq, s.E, s.N, s.K, wfq_p, p.N, p.K, nullptr, st);
-  uint16_t *x_p = c.take<uint16_t>((size_t)R_max * p.K * 2);
+  uint16_t *x_p = c.take<uint16_t>((size_t)x_rows * p.K * 2);
   uint16_t *y_p = c.take<uint16_t>((size_t)R_max * p.N * 2);
-  if (R_max > 0) launch_reshape_u16(x, 1, R_max, s.K, x_p, R_max, p.K, seg + s.E, st);
-  gemm_fwd_core(x_p, R_max, seg, p, nullptr, wfq_p, nullptr, aq, y_p, c.base + c.used, st);
+  // routed X: every token row is copied (rows are not in segment order)
+  if (x_rows > 0)
+    launch_reshape_u16(x, 1, x_rows, s.K, x_p, x_rows, p.K, xperm ? nullptr : seg + s.E, st);
+  gemm_fwd_core(x_p, R_max, seg, p, nullptr, wfq_p, nullptr, aq, y_p, c.base + c.used, st, xperm,
+                topk);
   if (R_max > 0) launch_reshape_u16(y_p, 1, R_max, p.N, y, R_max, s.N, seg + s.E, st);
-  FQ_CHECK_LAUNCH("fq_grouped_gemm_fwd");
+  FQ_CHECK_LAUNCH(fn);
   return FQ_OK;
+}
+
+}  // namespace
+
+fq_status fq_grouped_gemm_fwd(const uint16_t *x, int32_t R_max, const int32_t *seg, fq_shape s,
+                              const uint16_t *w, const uint16_t *w_fq, const fq_weight_q *wq,
+                              const fq_act_q *aq, uint16_t *y, void *ws, size_t ws_bytes,
+                              fq_stream stream) {
+  return gemm_fwd_call("fq_grouped_gemm_fwd", x, R_max, nullptr, 1, R_max, seg, s, w, w_fq, wq, aq,
+                       y, ws, ws_bytes, stream);
+}
+
+fq_status fq_grouped_gemm_fwd_tokens(const uint16_t *x_tok, int32_t T, const int32_t *perm,
+                                     int32_t topk, int32_t R_max, const int32_t *seg, fq_shape s,
+                                     const uint16_t *w, const uint16_t *w_fq,
+                                     const fq_weight_q *wq, uint16_t *y, void *ws, size_t ws_bytes,
+                                     fq_stream stream) {
+  FQ_CHECK_ARG(T >= 0 && topk > 0, "bad sizes (T=%d topk=%d)", T, topk);
+  FQ_CHECK_ARG(R_max == 0 || (perm && x_tok), "perm and x_tok must be non-NULL");
+  return gemm_fwd_call("fq_grouped_gemm_fwd_tokens", x_tok, T, perm, topk, R_max, seg, s, w, w_fq,
+                       wq, nullptr, y, ws, ws_bytes, stream);
 }
 
 namespace {
@@ -465,7 +491,7 @@ namespace {
 void gemm_bwd_core(const uint16_t *dy, const uint16_t *x, int R_max, const int32_t *seg, fq_shape s,
                    const uint16_t *w, const uint16_t *w_fq, const fq_weight_q *wq,
                    const fq_act_q *aq, uint16_t *dx, float *dscale, float *dzp, void *ws,
-                   hipStream_t st) {
+                   hipStream_t st, const int32_t *xperm, int topk) {
   const bool want_ds = dscale || dzp;
   const bool per_tensor = wq->group == FQ_GROUP_TENSOR;
   const int afmt = act_fmt(aq);
@@ -497,22 +523,27 @@ void gemm_bwd_core(const uint16_t *dy, const uint16_t *x, int R_max, const int32
       float *dch = c.take<float>((size_t)s.E * s.N * 4);
       launch_repeat_rows(wq->scale, s.E, s.N, rep, st);
       fq_weight_q qc{wq->fmt, s.K, rep, nullptr, nullptr};
-      launch_gemm_wgrad_dscale(dy, xq, R_max, seg, s, w, qc, dch, nullptr, ps, nullptr, cs, st);
+      launch_gemm_wgrad_dscale(dy, xq, R_max, seg, s, w, qc, dch, nullptr, ps, nullptr, cs, st,
+                               xperm, topk);
       launch_sum_rows(dch, s.E, s.N, dscale, st);
     } else {
       launch_gemm_wgrad_dscale(dy, xq, R_max, seg, s, w, *wq, dscale, dzp, ps, dzp ? pz : nullptr, cs,
-                               st);
+                               st, xperm, topk);
     }
   }
 }
 
 }  // namespace
 
-fq_status fq_grouped_gemm_bwd_scale(const uint16_t *dy, const uint16_t *x, int32_t R_max,
-                                    const int32_t *seg, fq_shape s, const uint16_t *w,
-                                    const uint16_t *w_fq, const fq_weight_q *wq, const fq_act_q *aq,
-                                    uint16_t *dx, float *dscale, float *dzp, void *ws,
-                                    size_t ws_bytes, fq_stream stream) {
+namespace {
+
+// fq_grouped_gemm_bwd_scale and its routed-X form (see gemm_fwd_call; with
+// xperm, aq and dx are NULL)
+fq_status gemm_bwd_call(const char *fn, const uint16_t *dy, const uint16_t *x, int32_t x_rows,
+                        const int32_t *xperm, int32_t topk, int32_t R_max, const int32_t *seg,
+                        fq_shape s, const uint16_t *w, const uint16_t *w_fq, const fq_weight_q *wq,
+                        const fq_act_q *aq, uint16_t *dx, float *dscale, float *dzp, void *ws,
+                        size_t ws_bytes, fq_stream stream) {
   FQ_TRY(check_shape(s));
   FQ_CHECK_ARG(R_max >= 0, "R_max < 0");
   FQ_CHECK_ARG(seg != nullptr, "seg_offsets is NULL");
@@ -528,7 +559,8 @@ fq_status fq_grouped_gemm_bwd_scale(const uint16_t *dy, const uint16_t *x, int32
                      "grouped GEMM needs N %% 16 == 0 and K %% 16 == 0 (N=%d K=%d)", s.N, s.K);
   FQ_CHECK_SUPPORTED(s.E <= 1024, "grouped GEMM supports up to 1024 experts per stack (E=%d)", s.E);
   const fq_shape p = gemm_pad_shape(FQ_OP_GEMM_BWD, s);
-  FQ_CHECK_SUPPORTED((size_t)R_max * (p.K > p.N ? p.K : p.N) * 2 < (1ull << 32) &&
+  const int32_t rows_ws = x_rows > R_max ? x_rows : R_max;
+  FQ_CHECK_SUPPORTED((size_t)rows_ws * (p.K > p.N ? p.K : p.N) * 2 < (1ull << 32) &&
                          (size_t)p.N * p.K * 2 < (1ull << 32),
                      "operands must stay below 4 GiB (32-bit tile offsets)");
   const bool per_tensor = wq->group == FQ_GROUP_TENSOR;
@@ -541,15 +573,16 @@ fq_status fq_grouped_gemm_bwd_scale(const uint16_t *dy, const uint16_t *x, int32
                    (!w_fq || aligned16(w_fq)) && (!dx || aligned16(dx)),
                "bf16 tensors must be 16-byte aligned");
   const int afmt = act_fmt(aq);
-  size_t need = gemm_ws(FQ_OP_GEMM_BWD, s, R_max, (w_fq ? 0 : wq->fmt) | (afmt << 8));
+  // FQ_w(W) is materialized only for dX
+  size_t need = gemm_ws(FQ_OP_GEMM_BWD, s, rows_ws, ((w_fq || !dx) ? 0 : wq->fmt) | (afmt << 8));
   if (ws_bytes < need || !ws) {
-    set_error("fq_grouped_gemm_bwd_scale: workspace %zu bytes < %zu needed", ws_bytes, need);
+    set_error("%s: workspace %zu bytes < %zu needed", fn, ws_bytes, need);
     return FQ_ERR_WORKSPACE_TOO_SMALL;
   }
   hipStream_t st = S(stream);
   if (!gemm_needs_pad(FQ_OP_GEMM_BWD, s)) {
-    gemm_bwd_core(dy, x, R_max, seg, s, w, w_fq, wq, aq, dx, dscale, dzp, ws, st);
-    FQ_CHECK_LAUNCH("fq_grouped_gemm_bwd_scale");
+    gemm_bwd_core(dy, x, R_max, seg, s, w, w_fq, wq, aq, dx, dscale, dzp, ws, st, xperm, topk);
+    FQ_CHECK_LAUNCH(fn);
     return FQ_OK;
   }
   // Zero-padded to the kernels' shape. A padded weight element is 0 with a
@@ -571,13 +604,12 @@ fq_status fq_grouped_gemm_bwd_scale(const uint16_t *dy, const uint16_t *x, int32
   }
   uint16_t *w_p = c.take<uint16_t>((size_t)s.E * p.N * p.K * 2);
   launch_reshape_u16(w, s.E, s.N, s.K, w_p, p.N, p.K, nullptr, st);
-  uint16_t *x_p = c.take<uint16_t>((size_t)R_max * p.K * 2);
+  uint16_t *x_p = c.take<uint16_t>((size_t)x_rows * p.K * 2);
   uint16_t *dy_p = c.take<uint16_t>((size_t)R_max * p.N * 2);
   uint16_t *dx_p = c.take<uint16_t>((size_t)R_max * p.K * 2);
-  if (R_max > 0) {
-    if (x) launch_reshape_u16(x, 1, R_max, s.K, x_p, R_max, p.K, seg + s.E, st);
-    launch_reshape_u16(dy, 1, R_max, s.N, dy_p, R_max, p.N, seg + s.E, st);
-  }
+  if (x && x_rows > 0)
+    launch_reshape_u16(x, 1, x_rows, s.K, x_p, x_rows, p.K, xperm ? nullptr : seg + s.E, st);
+  if (R_max > 0) launch_reshape_u16(dy, 1, R_max, s.N, dy_p, R_max, p.N, seg + s.E, st);
   const size_t nsc = (size_t)s.E * p.N * (p.K / 16) * 4;
   float *sc_p = c.take<float>(nsc), *zp_p = c.take<float>(nsc);
   float *ds_p = c.take<float>(nsc), *dzp_p = c.take<float>(nsc);
@@ -596,11 +628,45 @@ fq_status fq_grouped_gemm_bwd_scale(const uint16_t *dy, const uint16_t *x, int32
   float *ds_out = dscale ? (per_tensor ? dscale : ds_p) : nullptr;
   float *dzp_out = dzp ? dzp_p : nullptr;
   gemm_bwd_core(dy_p, x ? x_p : nullptr, R_max, seg, p, w_p, wfq_p, &wq_p, aq,
-                dx ? dx_p : nullptr, ds_out, dzp_out, c.base + c.used, st);
+                dx ? dx_p : nullptr, ds_out, dzp_out, c.base + c.used, st, xperm, topk);
   if (dx && R_max > 0) launch_reshape_u16(dx_p, 1, R_max, p.K, dx, R_max, s.K, seg + s.E, st);
   if (dscale && !per_tensor) launch_reshape_f32(ds_p, s.E, p.N, Gp, dscale, s.N, G, 0.0f, st);
   if (dzp) launch_reshape_f32(dzp_p, s.E, p.N, Gp, dzp, s.N, G, 0.0f, st);
-  FQ_CHECK_LAUNCH("fq_grouped_gemm_bwd_scale");
+  FQ_CHECK_LAUNCH(fn);
+  return FQ_OK;
+}
+
+}  // namespace
+
+fq_status fq_grouped_gemm_bwd_scale(const uint16_t *dy, const uint16_t *x, int32_t R_max,
+                                    const int32_t *seg, fq_shape s, const uint16_t *w,
+                                    const uint16_t *w_fq, const fq_weight_q *wq, const fq_act_q *aq,
+                                    uint16_t *dx, float *dscale, float *dzp, void *ws,
+                                    size_t ws_bytes, fq_stream stream) {
+  return gemm_bwd_call("fq_grouped_gemm_bwd_scale", dy, x, R_max, nullptr, 1, R_max, seg, s, w, w_fq,
+                       wq, aq, dx, dscale, dzp, ws, ws_bytes, stream);
+}
+
+fq_status fq_grouped_gemm_wgrad_tokens(const uint16_t *dy, const uint16_t *x_tok, int32_t T,
+                                       const int32_t *perm, int32_t topk, int32_t R_max,
+                                       const int32_t *seg, fq_shape s, const uint16_t *w,
+                                       const fq_weight_q *wq, float *dscale, float *dzp, void *ws,
+                                       size_t ws_bytes, fq_stream stream) {
+  FQ_CHECK_ARG(T >= 0 && topk > 0, "bad sizes (T=%d topk=%d)", T, topk);
+  FQ_CHECK_ARG(R_max == 0 || (perm && x_tok), "perm and x_tok must be non-NULL");
+  return gemm_bwd_call("fq_grouped_gemm_wgrad_tokens", dy, x_tok, T, perm, topk, R_max, seg, s, w,
+                       nullptr, wq, nullptr, nullptr, dscale, dzp, ws, ws_bytes, stream);
+}
+
+fq_status fq_actfq(const uint16_t *x, int32_t rows, int32_t K, const fq_act_q *aq, uint16_t *xq,
+                   fq_stream stream) {
+  FQ_CHECK_ARG(rows >= 0 && K > 0 && K % 16 == 0, "bad sizes (rows=%d K=%d; K %% 16 == 0)", rows, K);
+  FQ_CHECK_ARG(rows == 0 || (x && xq), "NULL pointer");
+  FQ_CHECK_ARG((!x || aligned16(x)) && (!xq || aligned16(xq)), "bf16 tensors must be 16-byte aligned");
+  FQ_CHECK_ARG((long)rows * K < (1l << 35), "too many elements");
+  FQ_TRY(check_act_q(aq, K));
+  launch_act_fq(x, (size_t)rows, K, nullptr, act_fmt(aq), aq ? aq->scale : nullptr, xq, S(stream));
+  FQ_CHECK_LAUNCH("fq_actfq");
   return FQ_OK;
 }
 

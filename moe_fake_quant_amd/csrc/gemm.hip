@@ -151,6 +151,10 @@ struct GemmArgs {
   FastDiv gdiv16;          // division by group / 16
   float *part_s, *part_z;
   int *chunk_start_out;    // [E+1] chunk prefix, written by block 0
+  // X rows through the routing (FWD's Q, WGRAD's P): routed row r reads row
+  // xperm[r] / topk of a token-indexed X; NULL = X is indexed by routed row
+  const int32_t *xperm;
+  FastDiv xtopk;
 };
 
 constexpr int kMaxExperts = 1024;
@@ -388,6 +392,18 @@ struct NormalDMA {  // contraction-contiguous: instr covers 8 rows x 128 B; slot
       off[ii] = (uint32_t)(((size_t)r * ld + kc * 8) * 2);
     }
   }
+  // the same rows taken through the routing: row r of the tile reads row
+  // perm[r] / topk of the operand
+  __device__ __forceinline__ void init_routed(size_t ld, int row0, int row_last, int slot,
+                                              int lane, const int32_t *perm, FastDiv topk) {
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii) {
+      const uint32_t idx = 8 * (4 * slot + ii) + (lane >> 3);
+      const uint32_t kc = (lane & 7) ^ nrm_sw(idx);
+      const uint32_t r = topk.div((uint32_t)perm[min(row0 + (int)idx, row_last)]);
+      off[ii] = (uint32_t)(((size_t)r * ld + kc * 8) * 2);
+    }
+  }
   template <int S>
   __device__ __forceinline__ void issue(const char *base, char *stage, int c0, int slot) const {
 #pragma unroll
@@ -396,12 +412,13 @@ struct NormalDMA {  // contraction-contiguous: instr covers 8 rows x 128 B; slot
 };
 struct TransDMA {  // transposed: instr covers 2 contraction rows x 512 B; slot = 8 rows
   uint32_t col_off[4];
-  int crow[4];
+  int crow0;  // contraction row of instruction ii within the stage: crow0 + 2 ii
+  __device__ __forceinline__ int crow(int ii) const { return crow0 + 2 * ii; }
   __device__ __forceinline__ void init(int idx0, int slot, int lane) {
+    crow0 = 8 * slot + (lane >> 5);
 #pragma unroll
     for (int ii = 0; ii < 4; ++ii) {
-      crow[ii] = 2 * (4 * slot + ii) + (lane >> 5);
-      const uint32_t q = (lane & 31) ^ tr_sw(crow[ii]);
+      const uint32_t q = (lane & 31) ^ tr_sw(crow(ii));
       col_off[ii] = (uint32_t)((idx0 + 8 * q) * 2);
     }
   }
@@ -410,9 +427,25 @@ struct TransDMA {  // transposed: instr covers 2 contraction rows x 512 B; slot 
                                         int c_end, int slot) const {
 #pragma unroll
     for (int ii = 0; ii < 4; ++ii) {
-      const int c = c0 + crow[ii];
+      const int c = c0 + crow(ii);
       const int cc = c < c_end ? c : c0;
       dma16(base, (uint32_t)cc * (ld * 2) + col_off[ii], stage + (4 * slot + ii) * 1024);
+    }
+  }
+  // routed rows: lane m (m < 8) of `pair` holds the (token, slot) pair index
+  // of the slot's row crow0 - crow0 % 8 + m, looked up a stage ahead;
+  // instruction ii reads operand row pair / topk of its row. Each lane turns
+  // its pair into a row offset once and instruction ii takes the offset from
+  // lane crow0 % 8 + 2 ii. Dividing here, not at the lookup, keeps the
+  // lookup's load from being waited on before this stage.
+  __device__ __forceinline__ void issue_rows(const char *base, uint32_t ld, char *stage,
+                                             uint32_t pair, FastDiv topk, int slot,
+                                             int lane) const {
+    const int row_off = (int)(topk.div(pair) * (ld * 2));
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii) {
+      const uint32_t off = (uint32_t)__shfl(row_off, 2 * ii + (lane >> 5), 64);
+      dma16(base, off + col_off[ii], stage + (4 * slot + ii) * 1024);
     }
   }
 };
@@ -508,14 +541,24 @@ constexpr int kVmPerStageA = MODE == FWD ? 12 : 8;  // DMA instructions per wave
 template <int MODE>
 constexpr int kVmPerStageB = MODE == FWD ? 4 : 8;
 
-template <int MODE>
+// ROUTED: X (FWD's Q, WGRAD's P) is read by token row through a.xperm
+// (compile time, so the kernels without it keep their registers).
+template <int MODE, bool ROUTED>
 struct TileLoads {
   const char *pbase, *qbase;
   int c_total, nk;
   NormalDMA pn, qn;
   TransDMA pt, qt;
-  __device__ __forceinline__ TileLoads(const GemmArgs &a, const Tile &t, int wave, int lane) {
-    const int seg_lo = (MODE == WGRAD) ? t.r0 : 0;
+  // WGRAD with routed X: the (token, slot) pair indices of this wave's eight
+  // P rows of the next stage to issue (row 8 wave + lane % 8), loaded one
+  // stage ahead so that no DMA issue waits on them
+  int seg_lo;
+  uint32_t ppair;
+  // first_kt: the first stage this object will issue (WGRAD: 1 when the
+  // previous tile already issued stage 0)
+  __device__ __forceinline__ TileLoads(const GemmArgs &a, const Tile &t, int wave, int lane,
+                                       int first_kt = 0) {
+    seg_lo = (MODE == WGRAD) ? t.r0 : 0;
     c_total = (MODE == WGRAD) ? t.r1 - t.r0 : (MODE == FWD) ? a.K : a.N;
     nk = (c_total + BK - 1) / BK;
     const size_t NK = (size_t)a.N * a.K;
@@ -526,21 +569,35 @@ struct TileLoads {
       // slot 2w here; slot 2w + 1 is the same offsets 32 rows on (N is a
       // multiple of 256, so no P row of a tile is clamped)
       pn.init(a.K, t.i0, a.N - 1, 2 * (wave & 3), lane);
-      qn.init(a.K, t.j0, t.j_end - 1, xs, lane);
+      if constexpr (ROUTED) qn.init_routed(a.K, t.j0, t.j_end - 1, xs, lane, a.xperm, a.xtopk);
+      else qn.init(a.K, t.j0, t.j_end - 1, xs, lane);
     } else if (MODE == DGRAD) {
       pbase = reinterpret_cast<const char *>(a.p + t.e * NK);  // W_fq[e] as (c = n, idx = k)
       qbase = reinterpret_cast<const char *>(a.q);             // dY rows (absolute)
       pt.init(t.i0, xs, lane);
       qn.init(a.N, t.j0, t.j_end - 1, xs, lane);
     } else {
-      pbase = reinterpret_cast<const char *>(a.p + (size_t)seg_lo * a.K);  // Xq: (c = r, idx = k)
+      // Xq: (c = r, idx = k), by routed row or (routed X) by token row
+      pbase = reinterpret_cast<const char *>(ROUTED ? a.p : a.p + (size_t)seg_lo * a.K);
       qbase = reinterpret_cast<const char *>(a.q + (size_t)seg_lo * a.N);  // dY: (c = r, idx = n)
       pt.init(t.i0, wave, lane);
       qt.init(t.j0, wave, lane);
+      if constexpr (ROUTED) {
+        if (first_kt < nk) look_ahead(a, first_kt);
+      }
     }
   }
+  // WGRAD, routed X: the pair indices of stage kt's P rows, one row per
+  // lane (rows past the chunk's end read row c0, as in TransDMA::issue)
+  __device__ __forceinline__ void look_ahead(const GemmArgs &a, int kt) {
+    const int c0 = kt * BK;
+    const int c = c0 + (pt.crow0 & ~7) + (int)(threadIdx.x & 7);
+    const int cc = c < c_total ? c : c0;
+    ppair = (uint32_t)a.xperm[seg_lo + cc];
+  }
+  // stages are issued in order kt = first_kt, first_kt + 1, ...
   template <int S>
-  __device__ __forceinline__ void issue(const GemmArgs &a, int kt, int wave) const {
+  __device__ __forceinline__ void issue(const GemmArgs &a, int kt, int wave) {
     const int c0 = kt * BK;
     const int xs = wave ^ 4;
     if (MODE == FWD) {
@@ -553,7 +610,12 @@ struct TileLoads {
       pt.issue(pbase, a.K, stage_p<S>(), c0, c_total, xs);
       qn.template issue<S>(qbase, stage_q<S>(), c0, xs);
     } else {
-      pt.issue(pbase, a.K, stage_p<S>(), c0, c_total, wave);
+      if constexpr (ROUTED) {
+        pt.issue_rows(pbase, a.K, stage_p<S>(), ppair, a.xtopk, wave, (int)(threadIdx.x & 63));
+        if (kt + 1 < nk) look_ahead(a, kt + 1);
+      } else {
+        pt.issue(pbase, a.K, stage_p<S>(), c0, c_total, wave);
+      }
       qt.issue(qbase, a.N, stage_q<S>(), c0, c_total, wave);
     }
   }
@@ -565,7 +627,7 @@ struct TileLoads {
 // flight; if next_w >= 0, stage 0 of tile next_w is issued once every wave
 // is done with this tile's LDS buffers, so that its loads run under this
 // tile's epilogue.
-template <int MODE, int WFMT>
+template <int MODE, int WFMT, bool ROUTED>
 __device__ __forceinline__ void run_tile_wgrad(const GemmArgs &a, const int *tile_start,
                                                const Tile &tl, bool pre, int next_w) {
   static_assert(MODE == WGRAD, "the lockstep loop serves the wgrad tiles");
@@ -573,7 +635,7 @@ __device__ __forceinline__ void run_tile_wgrad(const GemmArgs &a, const int *til
   const int lane = t & 63, wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int wi = wave & 1, wj = wave >> 1;  // 2 x 4 waves: 128 (i) x 64 (j) each
   const int e = tl.e, i0 = tl.i0, j0 = tl.j0;
-  const TileLoads<MODE> ld(a, tl, wave, lane);
+  TileLoads<MODE, ROUTED> ld(a, tl, wave, lane, pre ? 1 : 0);
   const int c_total = ld.c_total, nk = ld.nk;
 
   auto issue = [&](auto stage_tag, int kt) {
@@ -585,7 +647,7 @@ __device__ __forceinline__ void run_tile_wgrad(const GemmArgs &a, const int *til
   auto prefetch_issue = [&]() {
     if (next_w < 0) return false;
     const Tile nt = decode_tile<MODE>(a, tile_start, next_w);
-    const TileLoads<MODE> nl(a, nt, wave, lane);
+    TileLoads<MODE, ROUTED> nl(a, nt, wave, lane);
     if (nl.nk <= 0) return false;
     nl.template issue<0>(a, 0, wave);
     return true;
@@ -714,7 +776,7 @@ __device__ __forceinline__ void run_tile_wgrad(const GemmArgs &a, const int *til
 // after the last read of stage t. Each wave waits for its own loads of a
 // stage before the barrier that opens the first phase reading it. A's
 // epilogue runs while B multiplies the last half.
-template <int MODE, int WFMT>
+template <int MODE, int WFMT, bool ROUTED>
 __device__ __forceinline__ int run_tile(const GemmArgs &a, const int *tile_start, const Tile &tl,
                                         int pre, int next_w) {
   static_assert(MODE != WGRAD, "the ping-pong serves the forward and dgrad tiles");
@@ -723,7 +785,7 @@ __device__ __forceinline__ int run_tile(const GemmArgs &a, const int *tile_start
   const int wi = wave & 1, wj = wave >> 1;  // 2 x 4 waves: 128 (i) x 64 (j) each
   const bool grp_b = wave >= 4;             // j columns 128..255 of the tile
   const int i0 = tl.i0, j0 = tl.j0, j_end = tl.j_end;
-  const TileLoads<MODE> ld(a, tl, wave, lane);
+  TileLoads<MODE, ROUTED> ld(a, tl, wave, lane);
   const int nk = ld.nk;
   // a wave whose 64 rows all lie past the expert's last row (the ragged last
   // row tile) skips its fragment reads and MFMAs; it still takes part in the
@@ -843,11 +905,13 @@ __device__ __forceinline__ int run_tile(const GemmArgs &a, const int *tile_start
   // group no longer reads them. Stage 0 of the next tile goes to buffer 0
   // now; buffer 1 serves as this group's staging (A the P half, B the Q
   // half) and takes stage 1 of the next tile after the closing barrier.
+  // The next tile's loads are set up once, here, for both stages (with
+  // routed rows that means one lookup, made while no store is in flight).
+  TileLoads<MODE, ROUTED> nl(a, next_w >= 0 ? decode_tile<MODE>(a, tile_start, next_w) : tl, wave,
+                             lane);
   auto issue_next = [&](auto stage_tag) -> bool {
     constexpr int S = decltype(stage_tag)::value;
     if (next_w < 0) return false;
-    const Tile nt = decode_tile<MODE>(a, tile_start, next_w);
-    const TileLoads<MODE> nl(a, nt, wave, lane);
     if (nl.nk <= S) return false;
     nl.template issue<S>(a, S, wave);
     return true;
@@ -917,7 +981,7 @@ __device__ __forceinline__ int run_tile(const GemmArgs &a, const int *tile_start
 // operand panels in that XCD's L2. FWD / DGRAD tiles: (row tile, i tile)
 // with i fastest; the row tiles of each expert follow from seg_offsets.
 // WGRAD tiles: (expert, j tile, i tile).
-template <int MODE, int WFMT>
+template <int MODE, int WFMT, bool ROUTED>
 __global__ __launch_bounds__(NT) void k_grouped_gemm(GemmArgs a) {
   __shared__ int tile_start[kMaxExperts + 1];
   int total;
@@ -938,10 +1002,10 @@ __global__ __launch_bounds__(NT) void k_grouped_gemm(GemmArgs a) {
     const int next = w + nslot < w_end ? w + nslot : -1;
     const Tile tl = decode_tile<MODE>(a, tile_start, w);
     if constexpr (MODE == WGRAD) {
-      run_tile_wgrad<MODE, WFMT>(a, tile_start, tl, pre != 0, next);
+      run_tile_wgrad<MODE, WFMT, ROUTED>(a, tile_start, tl, pre != 0, next);
       pre = next >= 0;
     } else {
-      pre = run_tile<MODE, WFMT>(a, tile_start, tl, pre, next);
+      pre = run_tile<MODE, WFMT, ROUTED>(a, tile_start, tl, pre, next);
     }
   }
 }
@@ -1011,10 +1075,13 @@ static size_t rowtile_units(int R_max, int E, int n_it) {
 }
 
 void launch_gemm_fwd(const uint16_t *xq, int R_max, const int32_t *seg, fq_shape s,
-                     const uint16_t *wfq, uint16_t *y, hipStream_t st) {
+                     const uint16_t *wfq, uint16_t *y, hipStream_t st, const int32_t *xperm,
+                     int topk) {
   GemmArgs a{};
   a.p = wfq;
   a.q = xq;
+  a.xperm = xperm;
+  a.xtopk = FastDiv((uint32_t)(topk > 0 ? topk : 1));
   a.seg = seg;
   a.E = s.E;
   a.N = s.N;
@@ -1022,8 +1089,9 @@ void launch_gemm_fwd(const uint16_t *xq, int R_max, const int32_t *seg, fq_shape
   a.n_it = s.N / BI;
   a.out = y;
   if (R_max <= 0) return;
-  hipLaunchKernelGGL((k_grouped_gemm<FWD, 0>), dim3(gemm_grid(rowtile_units(R_max, s.E, a.n_it))),
-                     dim3(NT), 0, st, a);
+  const dim3 grid(gemm_grid(rowtile_units(R_max, s.E, a.n_it)));
+  if (xperm) hipLaunchKernelGGL((k_grouped_gemm<FWD, 0, true>), grid, dim3(NT), 0, st, a);
+  else hipLaunchKernelGGL((k_grouped_gemm<FWD, 0, false>), grid, dim3(NT), 0, st, a);
 }
 
 void launch_gemm_dgrad(const uint16_t *dy, int R_max, const int32_t *seg, fq_shape s,
@@ -1038,21 +1106,42 @@ void launch_gemm_dgrad(const uint16_t *dy, int R_max, const int32_t *seg, fq_sha
   a.n_it = s.K / BI;
   a.out = dx;
   if (R_max <= 0) return;
-  hipLaunchKernelGGL((k_grouped_gemm<DGRAD, 0>), dim3(gemm_grid(rowtile_units(R_max, s.E, a.n_it))),
-                     dim3(NT), 0, st, a);
+  hipLaunchKernelGGL((k_grouped_gemm<DGRAD, 0, false>),
+                     dim3(gemm_grid(rowtile_units(R_max, s.E, a.n_it))), dim3(NT), 0, st, a);
 }
 
 size_t wgrad_max_chunks(int E, int R_max) {
   return (size_t)(R_max + kWgradChunkRows - 1) / kWgradChunkRows + E;
 }
 
+template <bool ROUTED>
+static void launch_wgrad_kernel(int fmt, dim3 grid, dim3 block, hipStream_t st, const GemmArgs &a) {
+  switch (fmt) {
+    case FQ_FMT_INT8:
+      hipLaunchKernelGGL((k_grouped_gemm<WGRAD, FQ_FMT_INT8, ROUTED>), grid, block, 0, st, a);
+      break;
+    case FQ_FMT_INT4:
+      hipLaunchKernelGGL((k_grouped_gemm<WGRAD, FQ_FMT_INT4, ROUTED>), grid, block, 0, st, a);
+      break;
+    case FQ_FMT_FP8_E4M3:
+      hipLaunchKernelGGL((k_grouped_gemm<WGRAD, FQ_FMT_FP8_E4M3, ROUTED>), grid, block, 0, st, a);
+      break;
+    default:
+      hipLaunchKernelGGL((k_grouped_gemm<WGRAD, FQ_FMT_NVFP4, ROUTED>), grid, block, 0, st, a);
+      break;
+  }
+}
+
 void launch_gemm_wgrad_dscale(const uint16_t *dy, const uint16_t *xq, int R_max, const int32_t *seg,
                               fq_shape s,
                               const uint16_t *w, const fq_weight_q &q, float *dscale, float *dzp,
-                              float *part_s, float *part_z, int *chunk_start, hipStream_t st) {
+                              float *part_s, float *part_z, int *chunk_start, hipStream_t st,
+                              const int32_t *xperm, int topk) {
   GemmArgs a{};
   a.p = xq;
   a.q = dy;
+  a.xperm = xperm;
+  a.xtopk = FastDiv((uint32_t)(topk > 0 ? topk : 1));
   a.seg = seg;
   a.E = s.E;
   a.N = s.N;
@@ -1073,14 +1162,8 @@ void launch_gemm_wgrad_dscale(const uint16_t *dy, const uint16_t *xq, int R_max,
   a.part_z = part_z;
   a.chunk_start_out = chunk_start;
   dim3 grid(gemm_grid(wgrad_max_chunks(s.E, R_max) * (size_t)a.n_it * (size_t)a.n_jt)), block(NT);
-  switch (q.fmt) {
-    case FQ_FMT_INT8: hipLaunchKernelGGL((k_grouped_gemm<WGRAD, FQ_FMT_INT8>), grid, block, 0, st, a); break;
-    case FQ_FMT_INT4: hipLaunchKernelGGL((k_grouped_gemm<WGRAD, FQ_FMT_INT4>), grid, block, 0, st, a); break;
-    case FQ_FMT_FP8_E4M3:
-      hipLaunchKernelGGL((k_grouped_gemm<WGRAD, FQ_FMT_FP8_E4M3>), grid, block, 0, st, a);
-      break;
-    default: hipLaunchKernelGGL((k_grouped_gemm<WGRAD, FQ_FMT_NVFP4>), grid, block, 0, st, a); break;
-  }
+  if (xperm) launch_wgrad_kernel<true>(q.fmt, grid, block, st, a);
+  else launch_wgrad_kernel<false>(q.fmt, grid, block, st, a);
   const int G = s.K / q.group;
   hipLaunchKernelGGL(k_reduce_dscale, dim3(ceil_div((long)s.N * G, 256 * 4), s.E), dim3(256), 0, st,
                      part_s, part_z, chunk_start, s.N, s.K, q.group, dscale, dzp);

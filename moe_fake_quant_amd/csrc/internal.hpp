@@ -75,8 +75,11 @@ fq_status permute_scratch(int32_t **out);
 void launch_permute(const int32_t *ids, int T, int topk, int ebegin, int E, int32_t *perm,
                     int32_t *row_of, int32_t *seg, void *ws, hipStream_t st);
 
+// xperm / topk: routed row r of X is row xperm[r] / topk of a token-indexed
+// xq (FWD's X operand, WGRAD's X operand); NULL = xq indexed by routed row.
 void launch_gemm_fwd(const uint16_t *xq, int R_max, const int32_t *seg, fq_shape s,
-                     const uint16_t *wfq, uint16_t *y, hipStream_t st);
+                     const uint16_t *wfq, uint16_t *y, hipStream_t st,
+                     const int32_t *xperm = nullptr, int topk = 1);
 void launch_gemm_dgrad(const uint16_t *dy, int R_max, const int32_t *seg, fq_shape s,
                        const uint16_t *wfq, uint16_t *dx, hipStream_t st);
 // The wgrad contraction over an expert's rows runs in chunks of at most this
@@ -89,6 +92,7 @@ size_t wgrad_max_chunks(int E, int R_max);
 void launch_gemm_wgrad_dscale(const uint16_t *dy, const uint16_t *xq, int R_max, const int32_t *seg,
                               fq_shape s,
                               const uint16_t *w, const fq_weight_q &q, float *dscale, float *dzp,
-                              float *part_s, float *part_z, int *chunk_start, hipStream_t st);
+                              float *part_s, float *part_z, int *chunk_start, hipStream_t st,
+                              const int32_t *xperm = nullptr, int topk = 1);
 
 }  // namespace fq

@@ -6,8 +6,10 @@ grouped GEMM; weights are frozen and only quantizer scales train (section 一).
 This class holds the device buffers of that path and calls the C ABI in
 order; it computes nothing itself.
 
-Forward:  FQ pass on both stacks -> permute -> gather + act FQ -> gate_up GEMM
-          -> SwiGLU + act FQ -> down GEMM -> combine
+Forward:  FQ pass on both stacks -> permute -> act FQ of each token row ->
+          gate_up GEMM (routed row r read as token row perm[r] / topk, so the
+          gathered [R, H] input is never formed) -> SwiGLU + act FQ -> down
+          GEMM -> combine
 Backward: combine bwd -> down dgrad + dScale -> SwiGLU bwd (with the act-FQ
           mask; + dS_a2) -> gate_up dgrad + dScale -> unpermute-reduce (with
           the input act-FQ mask; + dS_a1)
@@ -29,10 +31,11 @@ from typing import Optional
 import torch
 
 from . import (ActQ, FMT_FP8_E4M3, FMT_INT4, FMT_INT8, FMT_NONE, FMT_NVFP4, FQ_GROUP_TENSOR,
-               FQ_OP_ACT_SCALE_GRAD, FQ_OP_GEMM_BWD, FQ_OP_GEMM_FWD, FQ_OP_PERMUTE, WeightQ, fq_grouped_gemm_bwd_scale, fq_grouped_gemm_fwd,
-               fq_moe_combine, fq_moe_combine_bwd, fq_moe_gather_actfq, fq_moe_permute,
-               fq_moe_unpermute_reduce, fq_quantize_stacked, fq_swiglu_actfq, fq_swiglu_bwd,
-               fq_workspace_bytes, observer_absmax_init)
+               FQ_OP_ACT_SCALE_GRAD, FQ_OP_GEMM_BWD, FQ_OP_GEMM_FWD, FQ_OP_PERMUTE, WeightQ,
+               fq_actfq, fq_grouped_gemm_bwd_scale, fq_grouped_gemm_fwd,
+               fq_grouped_gemm_fwd_tokens, fq_grouped_gemm_wgrad_tokens, fq_moe_combine,
+               fq_moe_combine_bwd, fq_moe_permute, fq_moe_unpermute_reduce, fq_quantize_stacked,
+               fq_swiglu_actfq, fq_swiglu_bwd, fq_workspace_bytes, observer_absmax_init)
 
 
 def _weight_q(E, N, K, fmt, group, dev) -> WeightQ:
@@ -81,7 +84,10 @@ class MoEFakeQuantLayer:
         self.row_of = torch.empty(T_max, topk, **i32)
         self.seg = torch.empty(self.E + 1, **i32)
         self.n_rows = self.seg[self.E:]
-        self.xq = torch.empty(R, H, **bf)
+        # the expert input as token rows: FQ_a(x) once per token; the gate_up
+        # GEMMs read routed row r as token row perm[r] / topk
+        self.xq_tok = torch.empty(T_max, H, **bf)
+        self._x_tok = None
         self.h = torch.empty(R, 2 * F, **bf)
         self.a = torch.empty(R, F, **bf)
         self.aq = torch.empty(R, F, **bf)
@@ -143,21 +149,28 @@ class MoEFakeQuantLayer:
         self.quantize_weights()
         self.route(expert_ids)
         R = int(self.seg[self.E].item())
-        fq_moe_gather_actfq(x, T, self.H, self.row_of[:T], self.topk, self.aq1, self.xq)
-        fq_grouped_gemm_fwd(self.xq, self.R_max, self.seg, self.shape_gu, None, self.wfq_gu,
-                            self.q_gu, None, self.h, self.ws)
+        self._gate_up_fwd(x, T)
         fq_swiglu_actfq(self.h, self.R_max, self.n_rows, self.F, None, self.a, self.aq)
         if R > 0:
             observer_absmax_init(self.a[:R], (1, R, self.F), self.afmt, 16, 1, self.aq2.scale)
 
     # ---------------------------------------------------------- hot path --
+    def _gate_up_fwd(self, x: torch.Tensor, T: int):
+        """FQ_a of each token row once (the rows themselves without an
+        activation format), then the gate_up GEMM over the routed rows."""
+        if self.afmt == FMT_NONE:
+            self._x_tok = x
+        else:
+            fq_actfq(x, T, self.H, self.aq1, self.xq_tok)
+            self._x_tok = self.xq_tok
+        fq_grouped_gemm_fwd_tokens(self._x_tok, T, self.perm, self.topk, self.R_max, self.seg,
+                                   self.shape_gu, None, self.wfq_gu, self.q_gu, self.h, self.ws)
+
     def forward(self, x: torch.Tensor, expert_ids: torch.Tensor, probs: torch.Tensor,
                 keep_a: bool = False) -> torch.Tensor:
         T = x.shape[0]
         self.route(expert_ids)
-        fq_moe_gather_actfq(x, T, self.H, self.row_of[:T], self.topk, self.aq1, self.xq)
-        fq_grouped_gemm_fwd(self.xq, self.R_max, self.seg, self.shape_gu, None, self.wfq_gu,
-                            self.q_gu, None, self.h, self.ws)
+        self._gate_up_fwd(x, T)
         fq_swiglu_actfq(self.h, self.R_max, self.n_rows, self.F, self.aq2,
                         self.a if keep_a else None, self.aq)
         fq_grouped_gemm_fwd(self.aq, self.R_max, self.seg, self.shape_d, None, self.wfq_d,
@@ -167,40 +180,37 @@ class MoEFakeQuantLayer:
 
     def teacher_forward(self, x: torch.Tensor, expert_ids: torch.Tensor,
                         probs: torch.Tensor) -> torch.Tensor:
-        """The self-teacher: this layer with quantization off (plain gather, the
-        frozen bf16 weights as the GEMM operands, SwiGLU, combine), into
-        buffers of its own so a student forward's saved activations survive."""
+        """The self-teacher: this layer with quantization off (the raw token
+        rows through the routing, the frozen bf16 weights as the GEMM operands,
+        SwiGLU, combine), into buffers of its own so a student forward's saved
+        activations survive."""
         T = x.shape[0]
-        if not hasattr(self, "t_xq"):
+        if not hasattr(self, "t_h"):
             bf = dict(dtype=torch.bfloat16, device=self.dev)
             R, H, F = self.R_max, self.H, self.F
-            self.t_xq = torch.empty(R, H, **bf)
             self.t_h = torch.empty(R, 2 * F, **bf)
             self.t_a = torch.empty(R, F, **bf)
             self.t_o = torch.empty(R, H, **bf)
             self.t_out = torch.empty(self.T_max, H, **bf)
         self.route(expert_ids)
-        fq_moe_gather_actfq(x, T, self.H, self.row_of[:T], self.topk, None, self.t_xq)
-        fq_grouped_gemm_fwd(self.t_xq, self.R_max, self.seg, self.shape_gu, None, self.w_gu, None,
-                            None, self.t_h, None)
+        fq_grouped_gemm_fwd_tokens(x, T, self.perm, self.topk, self.R_max, self.seg,
+                                   self.shape_gu, None, self.w_gu, None, self.t_h, self.ws)
         fq_swiglu_actfq(self.t_h, self.R_max, self.n_rows, self.F, None, None, self.t_a)
         fq_grouped_gemm_fwd(self.t_a, self.R_max, self.seg, self.shape_d, None, self.w_d, None,
                             None, self.t_o, None)
         fq_moe_combine(self.t_o, probs, self.row_of[:T], T, self.topk, self.H, self.t_out[:T])
         return self.t_out[:T]
 
-    def _wgrad(self, ready, dy, x_rows, shape, w, wfq, q, ds, dzp):
-        """wgrad -> dScale of one stack: on the side stream once event `ready`
-        (recorded right after dy's producer) has passed (overlap_wgrad), else
-        inline on the caller's stream."""
+    def _wgrad(self, ready, launch):
+        """One wgrad -> dScale call, launch(ws): on the side stream once event
+        `ready` (recorded right after its dy's producer) has passed
+        (overlap_wgrad), else inline on the caller's stream."""
         if not self.overlap_wgrad:
-            fq_grouped_gemm_bwd_scale(dy, x_rows, self.R_max, self.seg, shape, w, wfq, q, None,
-                                      None, ds, dzp, self.ws)
+            launch(self.ws)
             return
         self.side.wait_event(ready)
         with torch.cuda.stream(self.side):
-            fq_grouped_gemm_bwd_scale(dy, x_rows, self.R_max, self.seg, shape, w, wfq, q, None,
-                                      None, ds, dzp, self.ws2)
+            launch(self.ws2)
 
     def backward(self, x: torch.Tensor, probs: torch.Tensor, dout: torch.Tensor):
         T = x.shape[0]
@@ -213,22 +223,25 @@ class MoEFakeQuantLayer:
         self.ev_do.record(main)
         # dgrad and wgrad -> dScale as separate calls (one GEMM kernel each);
         # the dgrad is enqueued first: it leads the chain to dX
-        fq_grouped_gemm_bwd_scale(self.do, self.aq, self.R_max, self.seg, self.shape_d, self.w_d,
+        fq_grouped_gemm_bwd_scale(self.do, None, self.R_max, self.seg, self.shape_d, self.w_d,
                                   self.wfq_d, self.q_d, None, self.daq, None, None, self.ws)
-        self._wgrad(self.ev_do, self.do, self.aq, self.shape_d, self.w_d, self.wfq_d, self.q_d,
-                    self.ds_d, self.dzp_d)
+        self._wgrad(self.ev_do, lambda ws: fq_grouped_gemm_bwd_scale(
+            self.do, self.aq, self.R_max, self.seg, self.shape_d, self.w_d, self.wfq_d, self.q_d,
+            None, None, self.ds_d, self.dzp_d, ws))
         fq_swiglu_bwd(self.daq, self.h, self.R_max, self.n_rows, self.F, self.aq2, self.dh,
                       self.ds_a2, self.ws)
         self.ev_dh.record(main)
-        fq_grouped_gemm_bwd_scale(self.dh, self.xq, self.R_max, self.seg, self.shape_gu, self.w_gu,
+        fq_grouped_gemm_bwd_scale(self.dh, None, self.R_max, self.seg, self.shape_gu, self.w_gu,
                                   self.wfq_gu, self.q_gu, None, self.dxq, None, None, self.ws)
-        self._wgrad(self.ev_dh, self.dh, self.xq, self.shape_gu, self.w_gu, self.wfq_gu, self.q_gu,
-                    self.ds_gu, self.dzp_gu)
+        x_tok = self._x_tok
+        self._wgrad(self.ev_dh, lambda ws: fq_grouped_gemm_wgrad_tokens(
+            self.dh, x_tok, T, self.perm, self.topk, self.R_max, self.seg, self.shape_gu,
+            self.w_gu, self.q_gu, self.ds_gu, self.dzp_gu, ws))
         fq_moe_unpermute_reduce(self.dxq, self.row_of[:T], x, T, self.topk, self.H, self.aq1,
                                 self.dx[:T], self.ds_a1, self.ws)
         if self.overlap_wgrad:
             # the caller's stream sees both dScale results, and the next step's
-            # forward cannot overwrite xq / aq / do / dh under a wgrad still running
+            # forward cannot overwrite xq_tok / aq / do / dh under a wgrad still running
             main.wait_stream(self.side)
         return self.dx[:T], self.ds_gu, self.ds_d
 

@@ -128,7 +128,13 @@ def test_moe_full_size_sampled(cfg, fmt, group):
     assert np.array_equal(wfq_gu, O.fq_weight_stack(case.w_gu[S], fmt, g_gu, *wq_gu).bits)
     assert np.array_equal(wfq_d, O.fq_weight_stack(case.w_d[S], fmt, g_d, *wq_d).bits)
 
-    xq_all, h_all, aq_all = host_bits(L.xq), host_bits(L.h), host_bits(L.aq)
+    # the expert input as token rows, read by the gate_up GEMMs through the
+    # routing: token rows bit-exact, then the routed rows they stand for
+    xq_tok = host_bits(L.xq_tok)[:T]
+    toks = rng.choice(T, 64, replace=False)
+    assert np.array_equal(xq_tok[toks], O.fq_act(case.x[toks], fmt, s1).bits)
+    xq_all = xq_tok[perm // k]
+    h_all, aq_all = host_bits(L.h), host_bits(L.aq)
     o_all, do_all, daq_all = host_bits(L.o), host_bits(L.do), host_bits(L.daq)
     dh_all, dxq_all = host_bits(L.dh), host_bits(L.dxq)
     ds_gu, ds_d = L.ds_gu.cpu().numpy(), L.ds_d.cpu().numpy()

@@ -497,6 +497,122 @@ def test_gemm_ragged_tiles_every_launch(N, K):
         assert torch.equal(dxs[i].view(torch.int16), dxs[0].view(torch.int16)), f"dx launch {i}"
 
 
+# ------------------------------------------- the expert input as token rows --
+def _routing(rng, T, topk, E, hot=None):
+    """Routing over E local experts (expert 1 empty; `hot` takes most rows)."""
+    ids = np.empty((T, topk), np.int32)
+    for t in range(T):
+        pool = [e for e in range(E) if e != 1]
+        if hot is not None and rng.random() < 0.8:
+            first = [hot]
+            pool = [e for e in pool if e != hot]
+            ids[t] = first + list(rng.choice(pool, topk - 1, replace=False))
+        else:
+            ids[t] = rng.choice(pool, topk, replace=False)
+    perm, _, seg = O.moe_permute(ids, 0, E)
+    return perm, seg
+
+
+@pytest.mark.parametrize("afmt", [O.FMT_NONE, O.FMT_FP8, O.FMT_INT8, O.FMT_NVFP4])
+def test_actfq_bitexact(afmt):
+    rng = np.random.default_rng(900 + afmt)
+    T, K = 300, 272
+    x = _rand_w(rng, 1, T, K, std=1.0)[0]
+    s = O.observer_act(x, afmt) if afmt else np.float32(1.0)
+    xq = torch.full((T, K), 7.0, dtype=torch.bfloat16, device="cuda")
+    F.fq_actfq(dev_bf16(x), T, K, F.ActQ(afmt, dev_f32([s])) if afmt else None, xq)
+    torch.cuda.synchronize()
+    assert np.array_equal(host_bits(xq), O.fq_act(x, afmt, s).bits)
+
+
+@pytest.mark.parametrize("name,fmt,group", [("nvfp4", O.FMT_NVFP4, 16), ("int4", O.FMT_INT4, 128),
+                                            ("fp8", O.FMT_FP8, None)])
+@pytest.mark.parametrize("N,K", [(512, 384), (272, 208)])
+@pytest.mark.parametrize("prequantized", [True, False])
+def test_gemm_fwd_tokens_is_the_gathered_fwd(name, fmt, group, N, K, prequantized):
+    """Routed row r read as token row perm[r] / topk gives the bits of the
+    plain call on the gathered rows, and matches the oracle."""
+    rng = np.random.default_rng(910 + fmt + N)
+    T, topk, E = 400, 4, 6
+    if group is not None and K % group:
+        group = 16
+    g = group or K
+    perm, seg = _routing(rng, T, topk, E, hot=2)
+    R = int(seg[-1])
+    R_max = R + 24
+    w = _rand_w(rng, E, N, K)
+    s, zp, gs = O.observer_weight(w, fmt, g)
+    wq = _wq(fmt, g, s, zp, gs)
+    x_tok = O.f32_to_bf16(rng.standard_normal((T, K)).astype(np.float32))
+    x_rows = np.zeros((R_max, K), np.uint16)
+    x_rows[:R] = x_tok[perm // topk]
+    wd = dev_bf16(w)
+    wfq = None
+    if prequantized:
+        wfq = torch.empty_like(wd)
+        F.fq_quantize_stacked(wd, (E, N, K), wq, wfq)
+    fmts = 0 if prequantized else fmt
+    ws = torch.empty(max(F.fq_workspace_bytes(F.FQ_OP_GEMM_FWD, (E, N, K), max(R_max, T), fmts), 1),
+                     dtype=torch.uint8, device="cuda")
+    y1 = torch.full((R_max, N), 7.0, dtype=torch.bfloat16, device="cuda")
+    y2 = torch.full((R_max, N), 7.0, dtype=torch.bfloat16, device="cuda")
+    segd, permd = dev_i32(seg), dev_i32(perm)
+    F.fq_grouped_gemm_fwd(dev_bf16(x_rows), R_max, segd, (E, N, K), wd, wfq, wq, None, y1, ws)
+    F.fq_grouped_gemm_fwd_tokens(dev_bf16(x_tok), T, permd, topk, R_max, segd, (E, N, K), wd, wfq,
+                                 wq, y2, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
+    check_gemm_tol(host_bits(y2)[:R], O.grouped_gemm_fwd(x_rows[:R], seg, w, fmt, g, s, zp, gs), "y")
+    assert np.all(bf16_vals(host_bits(y2)[R:]) == 7.0)
+
+
+@pytest.mark.parametrize("name,fmt,group", [("nvfp4", O.FMT_NVFP4, 16), ("int4", O.FMT_INT4, 128),
+                                            ("fp8", O.FMT_FP8, None), ("int8_g32", O.FMT_INT8, 32)])
+@pytest.mark.parametrize("N,K,T", [(256, 512, 400), (272, 208, 400), (256, 256, 2800)])
+def test_gemm_wgrad_tokens_is_the_gathered_wgrad(name, fmt, group, N, K, T):
+    """dScale (and dzero_point) of the routed-X wgrad equal the plain call's
+    on the gathered rows bit for bit, and match the oracle. T = 2800 with a
+    hot expert puts more than 2048 rows on it (the chunked partial sums)."""
+    rng = np.random.default_rng(920 + fmt + N + T)
+    topk, E = 2, 4
+    if group is not None and K % group:
+        group = 16
+    g = group or K
+    perm, seg = _routing(rng, T, topk, E, hot=3)
+    R = int(seg[-1])
+    R_max = R + 8
+    if T == 2800:
+        assert seg[4] - seg[3] > 2048
+    w = _rand_w(rng, E, N, K)
+    s, zp, gs = O.observer_weight(w, fmt, g)
+    wq = _wq(fmt, g, s, zp, gs)
+    x_tok = O.f32_to_bf16(rng.standard_normal((T, K)).astype(np.float32))
+    x_rows = np.zeros((R_max, K), np.uint16)
+    x_rows[:R] = x_tok[perm // topk]
+    dy = O.f32_to_bf16(rng.standard_normal((R_max, N)).astype(np.float32))
+    ws = torch.empty(F.fq_workspace_bytes(F.FQ_OP_GEMM_BWD, (E, N, K), max(R_max, T), fmt),
+                     dtype=torch.uint8, device="cuda")
+    wd, segd, dyd = dev_bf16(w), dev_i32(seg), dev_bf16(dy)
+    shp = (E, N, K // g)
+    ds1 = torch.full(shp, 7.0, device="cuda")
+    ds2 = torch.full(shp, 7.0, device="cuda")
+    dz1 = torch.full(shp, 7.0, device="cuda") if fmt == O.FMT_INT4 else None
+    dz2 = torch.full(shp, 7.0, device="cuda") if fmt == O.FMT_INT4 else None
+    F.fq_grouped_gemm_bwd_scale(dyd, dev_bf16(x_rows), R_max, segd, (E, N, K), wd, None, wq, None,
+                                None, ds1, dz1, ws)
+    F.fq_grouped_gemm_wgrad_tokens(dyd, dev_bf16(x_tok), T, dev_i32(perm), topk, R_max, segd,
+                                   (E, N, K), wd, wq, ds2, dz2, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(ds1, ds2)
+    if dz1 is not None:
+        assert torch.equal(dz1, dz2)
+    _, ds_ref, dz_ref = O.grouped_gemm_bwd(dy, x_rows, seg, w, fmt, g, s, zp, gs)
+    check_dscale_tol(ds2.cpu().numpy(), ds_ref, "ds")
+    check_dscale_per_expert(ds2.cpu().numpy(), ds_ref, "ds")
+    if dz1 is not None:
+        check_dscale_tol(dz2.cpu().numpy(), dz_ref, "dzp")
+
+
 # ------------------------------------------------------- error handling --
 def test_errors_are_reported_before_launch():
     E, N, K = 2, 256, 250      # K not a multiple of 16

@@ -92,8 +92,13 @@ def _check_layer(name, wfmt, afmt, group, T, Eg, El, begin, zipf, learn, H, Fh):
     s2 = L.aq2.scale.cpu().numpy()[0]
     if afmt:
         assert s1 == O.observer_act(case.x, afmt)
-    # stage by stage, each oracle step fed the GPU's inputs of that step
-    xq = host_bits(L.xq)[:R]
+    # stage by stage, each oracle step fed the GPU's inputs of that step.
+    # The expert input as token rows: FQ_a of each token once (bit-exact); the
+    # gate_up GEMMs read routed row r as token row perm[r] / topk, which is
+    # the oracle's gather bit for bit.
+    xq_tok = host_bits(L.xq_tok)[:T] if afmt else case.x
+    assert np.array_equal(xq_tok, O.fq_act(case.x, afmt, s1).bits)
+    xq = xq_tok[perm // k]
     assert np.array_equal(xq, O.gather_actfq(case.x, perm, k, afmt, s1).bits)
     h = host_bits(L.h)[:R]
     check_gemm_tol(h, O.grouped_gemm_fwd(xq, seg, case.w_gu, wfmt, g_gu, *wq_gu), "h")

@@ -85,6 +85,8 @@ def parse():
     ap.add_argument("--weight-scales", choices=["default", "per-tensor"], default="default",
                     help="per-tensor: one scale per expert matrix (fp8 workload only)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="skip the graph-replay figure of the MoE step")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the measurements outside the step (export decode, self-teacher "
                          "forward, top-K KL)")
@@ -471,6 +473,15 @@ def main():
     timer.enabled = False
     ms_step, wall = time_steps(torch, step, args.steps)
 
+    # the same step captured once in a HIP graph and replayed (reported beside
+    # the eager headline, after a bit-for-bit check against the eager step)
+    graph = None
+    if not args.no_graph:
+        outs = (layer.out[:case.T], layer.dx[:case.T], layer.ds_gu, layer.ds_d, layer.wfq_gu,
+                layer.wfq_d)
+        graph = graph_replay(torch, step, outs, args.steps, FLOPS_PER_ROW * R)
+        graph["ms_per_step"] = round(graph.pop("us_per_step") / 1e3, 4)
+
     # breakdown: a separate pass with events around each call, the backward's
     # wgrad calls serialized on the launch stream so that every call's events
     # bracket its kernels alone
@@ -597,6 +608,7 @@ def main():
                                   "calls on the launch stream (--no-overlap)"),
                    "breakdown": "a separate pass with events around each call, all on one stream",
                    "breakdown_steps": nb, "breakdown_ms_per_step": round(ms_step_instr, 4)},
+        "graph_replay": graph,
         "gemm_kernels": kernels,
         "gemm_only": {"ms_per_step": round(gemm_ms, 4),
                       "TFLOP/s": round(flops_step / (gemm_ms * 1e-3) / 1e12, 2)},

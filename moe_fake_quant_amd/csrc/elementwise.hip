@@ -482,18 +482,21 @@ __device__ __forceinline__ uint32_t live_chunks(uint32_t max_chunks, const int32
   return n_rows ? min((uint32_t)n_rows[0] * chunks_per_row, max_chunks) : max_chunks;
 }
 
-// x [M, K] -> xq [M, K]; chunks of 16 elements
-__global__ __launch_bounds__(kThreads) void k_act_fq(const bf16x8_t *__restrict__ x, uint32_t max_chunks,
-                                                     const int32_t *__restrict__ n_rows, uint32_t cpr,
+// x [M, K] -> xq [M, K]. One 16-byte vector (8 elements) per lane, so each
+// wave load and store covers 1 KiB; a 16-block spans the lane pair
+// (2m, 2m + 1). The grid stride and the vector count are even, so both lanes
+// of a pair run every iteration together.
+__global__ __launch_bounds__(kThreads) void k_act_fq(const bf16x8_t *__restrict__ x, uint32_t max_vec,
+                                                     const int32_t *__restrict__ n_rows, uint32_t vpr,
                                                      int afmt, const float *__restrict__ ascale,
                                                      bf16x8_t *__restrict__ xq) {
   ActQ q = load_actq(afmt, ascale);
-  const uint32_t nchunk = live_chunks(max_chunks, n_rows, cpr);
-  for (uint32_t c = blockIdx.x * blockDim.x + threadIdx.x; c < nchunk; c += gridDim.x * blockDim.x) {
-    float f[16];
-    load16(x + 2 * (size_t)c, f);
-    act_fq16(q, f);
-    store16(xq + 2 * (size_t)c, f);
+  const uint32_t nvec = live_chunks(max_vec, n_rows, vpr);
+  for (uint32_t c = blockIdx.x * blockDim.x + threadIdx.x; c < nvec; c += gridDim.x * blockDim.x) {
+    float f[8];
+    unpack8(x[c], f);
+    act_fq8_pair(q, f);
+    xq[c] = pack8(f);
   }
 }
 
@@ -867,10 +870,10 @@ void launch_observer_tensor(const uint16_t *x, size_t n, int fmt, float *scale, 
 
 void launch_act_fq(const uint16_t *x, size_t M, int K, const int32_t *n_rows, int afmt,
                    const float *ascale, uint16_t *xq, hipStream_t st) {
-  uint32_t nchunk = (uint32_t)(M * K / 16);
-  if (!nchunk) return;
-  hipLaunchKernelGGL(k_act_fq, dim3(grid_for(nchunk)), dim3(kThreads), 0, st,
-                     reinterpret_cast<const bf16x8_t *>(x), nchunk, n_rows, (uint32_t)(K / 16), afmt,
+  uint32_t nvec = (uint32_t)(M * K / 8);
+  if (!nvec) return;
+  hipLaunchKernelGGL(k_act_fq, dim3(grid_for(nvec)), dim3(kThreads), 0, st,
+                     reinterpret_cast<const bf16x8_t *>(x), nvec, n_rows, (uint32_t)(K / 8), afmt,
                      ascale, reinterpret_cast<bf16x8_t *>(xq));
 }
 

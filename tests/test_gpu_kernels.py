@@ -613,6 +613,49 @@ def test_gemm_wgrad_tokens_is_the_gathered_wgrad(name, fmt, group, N, K, T):
         check_dscale_tol(dz2.cpu().numpy(), dz_ref, "dzp")
 
 
+@pytest.mark.parametrize("topk", [1, 8])
+def test_gemm_tokens_calls_at_top1_and_top8(topk):
+    """Both token-row calls with one routed slot per token (the row divisor
+    is 1) and with eight (the bench routing): bitwise the gathered calls."""
+    rng = np.random.default_rng(930 + topk)
+    T, E, N, K, g = 350, 10, 256, 256, 16
+    perm, seg = _routing(rng, T, topk, E)
+    R = int(seg[-1])
+    R_max = R + 5
+    w = _rand_w(rng, E, N, K)
+    s, zp, gs = O.observer_weight(w, O.FMT_NVFP4, g)
+    wq = _wq(O.FMT_NVFP4, g, s, zp, gs)
+    x_tok = O.f32_to_bf16(rng.standard_normal((T, K)).astype(np.float32))
+    x_rows = np.zeros((R_max, K), np.uint16)
+    x_rows[:R] = x_tok[perm // topk]
+    dy = O.f32_to_bf16(rng.standard_normal((R_max, N)).astype(np.float32))
+    nb = max(F.fq_workspace_bytes(F.FQ_OP_GEMM_FWD, (E, N, K), max(R_max, T), 0),
+             F.fq_workspace_bytes(F.FQ_OP_GEMM_BWD, (E, N, K), max(R_max, T), O.FMT_NVFP4), 1)
+    ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
+    wd, segd, permd = dev_bf16(w), dev_i32(seg), dev_i32(perm)
+    wfq = torch.empty_like(wd)
+    F.fq_quantize_stacked(wd, (E, N, K), wq, wfq)
+    y1 = torch.full((R_max, N), 7.0, dtype=torch.bfloat16, device="cuda")
+    y2 = torch.full((R_max, N), 7.0, dtype=torch.bfloat16, device="cuda")
+    F.fq_grouped_gemm_fwd(dev_bf16(x_rows), R_max, segd, (E, N, K), wd, wfq, wq, None, y1, ws)
+    F.fq_grouped_gemm_fwd_tokens(dev_bf16(x_tok), T, permd, topk, R_max, segd, (E, N, K), wd, wfq,
+                                 wq, y2, ws)
+    shp = (E, N, K // g)
+    ds1 = torch.full(shp, 7.0, device="cuda")
+    ds2 = torch.full(shp, 7.0, device="cuda")
+    F.fq_grouped_gemm_bwd_scale(dev_bf16(dy), dev_bf16(x_rows), R_max, segd, (E, N, K), wd, None, wq,
+                                None, None, ds1, None, ws)
+    F.fq_grouped_gemm_wgrad_tokens(dev_bf16(dy), dev_bf16(x_tok), T, permd, topk, R_max, segd,
+                                   (E, N, K), wd, wq, ds2, None, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
+    assert torch.equal(ds1, ds2)
+    check_gemm_tol(host_bits(y2)[:R], O.grouped_gemm_fwd(x_rows[:R], seg, w, O.FMT_NVFP4, g, s, zp,
+                                                         gs), "y")
+    _, ds_ref, _ = O.grouped_gemm_bwd(dy, x_rows, seg, w, O.FMT_NVFP4, g, s, zp, gs)
+    check_dscale_per_expert(ds2.cpu().numpy(), ds_ref, "ds")
+
+
 # ------------------------------------------------------- error handling --
 def test_errors_are_reported_before_launch():
     E, N, K = 2, 256, 250      # K not a multiple of 16

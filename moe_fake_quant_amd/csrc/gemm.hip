@@ -234,15 +234,52 @@ __device__ __forceinline__ void wgrad_read_w(const char *slab, int lane, uint2 (
       wv[s][q] = *reinterpret_cast<const uint2 *>(slab + jr * 256 + (c << 4) + h * 8);
     }
 }
+// The scale parameters of one epilogue half (rows n0 .. n0+31, this lane's
+// row and eight 16-blocks k0 + 16 j). They are loaded before the epilogue's
+// barrier and completed before its first DMA: the compiler does not see the
+// DMAs, so a wait it inserts for a load issued among them would drain them.
+struct WgradEpiIn {
+  float4 th;    // NVFP4: theta of the eight blocks (this lane half's four)
+  float g;      // NVFP4: the expert's tensor scale
+  float sc[8];  // FP8 / INT8: scale of each block's group
+};
+template <int WFMT>
+__device__ __forceinline__ WgradEpiIn wgrad_epi_load(const GemmArgs &a, int e, int k0, int n0,
+                                                     int lane) {
+  WgradEpiIn in;
+  const size_t srow = ((size_t)e * a.N + n0 + (lane & 31)) * (a.K / a.group);
+  if (WFMT == FQ_FMT_NVFP4) {
+    in.th = *reinterpret_cast<const float4 *>(a.scale + srow + k0 / 16 + 4 * (lane >> 5));
+    in.g = a.gscale[e];
+  } else if (WFMT != FQ_FMT_INT4) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint32_t gi = a.gdiv16.div((uint32_t)(k0 / 16 + j));
+      in.sc[j] = a.scale[srow + gi];
+    }
+  }
+  return in;
+}
+// the loads of `in` complete here (an empty asm that reads and writes them)
+template <int WFMT>
+__device__ __forceinline__ void wgrad_epi_ready(WgradEpiIn &in) {
+  if (WFMT == FQ_FMT_NVFP4) {
+    asm volatile("" : "+v"(in.th.x), "+v"(in.th.y), "+v"(in.th.z), "+v"(in.th.w), "+v"(in.g));
+  } else if (WFMT != FQ_FMT_INT4) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) asm volatile("" : "+v"(in.sc[j]));
+  }
+}
+
 // `chunk` < 0: this tile's dScale sums are final and go to dscale / dzp;
 // otherwise they are partials of row chunk `chunk` (blocks of min(group, 128)).
 template <int WFMT, int U>
 __device__ __forceinline__ void wgrad_epilogue(const GemmArgs &a, const f32x16 (&acc)[4][2], int e,
                                                int k0, int n0, int lane, const uint2 (&wv)[4][4],
-                                               int chunk, float4 t4) {
+                                               int chunk, const WgradEpiIn &in) {
   const int n = n0 + (lane & 31);
   const int G = a.K / a.group;
-  const float g_e = (WFMT == FQ_FMT_NVFP4) ? a.gscale[e] : 1.0f;
+  const float g_e = (WFMT == FQ_FMT_NVFP4) ? in.g : 1.0f;
   const size_t srow = ((size_t)e * a.N + n) * G;
   const int blk = a.group < 128 ? a.group : 128;
   const size_t orow = chunk < 0 ? srow : ((size_t)chunk * a.N + n) * (a.K / blk);
@@ -256,7 +293,7 @@ __device__ __forceinline__ void wgrad_epilogue(const GemmArgs &a, const f32x16 (
     // them (theta rounded to E4M3, its reciprocal, the theta factor) and
     // takes the other four from lane ^ 32
     const int h = lane >> 5;
-    const float th[4] = {t4.x, t4.y, t4.z, t4.w};
+    const float th[4] = {in.th.x, in.th.y, in.th.z, in.th.w};
     float rm[4], fm[4];
 #pragma unroll
     for (int j = 0; j < 4; j += 2) {
@@ -280,9 +317,13 @@ __device__ __forceinline__ void wgrad_epilogue(const GemmArgs &a, const f32x16 (
   } else {
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const uint32_t gi = a.gdiv16.div((uint32_t)(k0 / 16 + j));
-      sc8[j] = a.scale[srow + gi];
-      if (WFMT == FQ_FMT_INT4) zp8[j] = fminf(fmaxf(rintf(a.zero_point[srow + gi]), 0.0f), 15.0f);
+      if (WFMT == FQ_FMT_INT4) {  // loaded here (see the caller)
+        const uint32_t gi = a.gdiv16.div((uint32_t)(k0 / 16 + j));
+        sc8[j] = a.scale[srow + gi];
+        zp8[j] = fminf(fmaxf(rintf(a.zero_point[srow + gi]), 0.0f), 15.0f);
+      } else {
+        sc8[j] = in.sc[j];
+      }
     }
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
@@ -724,26 +765,31 @@ __device__ __forceinline__ void run_tile_wgrad(const GemmArgs &a, const int *til
     const int k0 = i0 + wi * 128, n0 = j0 + wj * WJ_TILE;
     char *slab = (wave < 4 ? stage_p<1>() : stage_q<1>()) + (wave & 3) * 8192;
     uint2 wv[4][4];
-    // NVFP4 theta of this lane's row and eight blocks, loaded before the
-    // barrier so that its latency overlaps the wait for the slowest wave
-    auto load_theta = [&](int nn) {
-      if (WFMT != FQ_FMT_NVFP4) return float4{0.0f, 0.0f, 0.0f, 0.0f};
-      const size_t srow = ((size_t)e * a.N + nn + (lane & 31)) * (a.K / a.group);
-      return *reinterpret_cast<const float4 *>(a.scale + srow + k0 / 16 + 4 * (lane >> 5));
-    };
-    const float4 th0 = load_theta(n0);
+    // The scale parameters: NVFP4 loads both halves' (5 values each) before
+    // the barrier, so that their latency overlaps the wait for the slowest
+    // wave, and completes them before the first DMA, so that the first
+    // half's arithmetic runs while the second slab and the next tile's stage
+    // 0 are in flight. FP8 / INT8 do so for the first half (8 values). INT4
+    // (scales and zero points) loads inside each half's arithmetic: held
+    // across the DMA set-up, they would spill.
+    constexpr bool kEarly0 = WFMT != FQ_FMT_INT4, kEarly1 = WFMT == FQ_FMT_NVFP4;
+    WgradEpiIn in0, in1;
+    if constexpr (kEarly0) in0 = wgrad_epi_load<WFMT>(a, e, k0, n0, lane);
+    if constexpr (kEarly1) in1 = wgrad_epi_load<WFMT>(a, e, k0, n0 + 32, lane);
     block_barrier();
+    if constexpr (kEarly0) wgrad_epi_ready<WFMT>(in0);
+    if constexpr (kEarly1) wgrad_epi_ready<WFMT>(in1);
     wgrad_dma_w(a, e, k0, n0, lane, slab);
     if (prefetch_issue()) wait_vm<8>();  // the slab, not the next tile's stage 0
     else wait_vm<0>();
     wgrad_read_w(slab, lane, wv);
     wait_lgkm0();                          // read back before the slab is reused
     wgrad_dma_w(a, e, k0, n0 + 32, lane, slab);
-    const float4 th1 = load_theta(n0 + 32);
-    wgrad_epilogue<WFMT, 0>(a, acc, e, k0, n0, lane, wv, tl.chunk, th0);
+    wgrad_epilogue<WFMT, 0>(a, acc, e, k0, n0, lane, wv, tl.chunk, in0);
     wait_vm<0>();
+    if constexpr (!kEarly1 && WFMT != FQ_FMT_INT4) in1 = wgrad_epi_load<WFMT>(a, e, k0, n0 + 32, lane);
     wgrad_read_w(slab, lane, wv);
-    wgrad_epilogue<WFMT, 1>(a, acc, e, k0, n0 + 32, lane, wv, tl.chunk, th1);
+    wgrad_epilogue<WFMT, 1>(a, acc, e, k0, n0 + 32, lane, wv, tl.chunk, in1);
   }
 }
 

@@ -44,11 +44,17 @@ GEMM_SOURCES = ("gemm.hip", "codec.hpp", "common.hpp", "internal.hpp")
 
 
 def gemm_source_hash() -> str:
+    """SHA-256 of the GEMM sources' code: comments removed and whitespace
+    collapsed, so that a change to the comments alone keeps the hash."""
     import hashlib
+    import re
     h = hashlib.sha256()
     for name in GEMM_SOURCES:
-        with open(os.path.join(ROOT, "moe_fake_quant_amd", "csrc", name), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, "moe_fake_quant_amd", "csrc", name)) as f:
+            txt = f.read()
+        txt = re.sub(r"/\*.*?\*/", " ", txt, flags=re.S)
+        txt = re.sub(r"//[^\n]*", "", txt)
+        h.update(" ".join(txt.split()).encode())
     return h.hexdigest()
 
 

@@ -10,11 +10,15 @@
 //   DGRAD  W_fq[e] [n][k]: i = k         dY rows r (N-contig)          n
 //   WGRAD  X rows: i = k                 dY rows: j = n                routed rows r
 //
+// X can also be token-ordered (ROUTED): routed row r is then read from token
+// row perm[r] / topk, in the load addresses, so no gathered copy is needed.
+//
 // Operands stream from global memory straight into LDS (global_load_lds,
-// 16 bytes per lane, no staging registers) through two stages of 64
-// contraction elements, one stage ahead of the MFMAs; one barrier per stage.
-// (Measured against four 32-deep stages: full 128-byte row segments per load
-// and half the barriers gain more than the deeper lookahead.) A
+// 16 bytes per lane, no staging registers) through a ring of two stages of
+// 64 contraction elements: WGRAD loads one stage ahead with one barrier per
+// stage, FWD / DGRAD two stages ahead in the ping-pong schedule described at
+// run_tile. (Measured against four 32-deep stages: full 128-byte row
+// segments per load and fewer barriers gain more than the deeper lookahead.) A
 // contraction-contiguous operand is stored as 256 rows x 128 B and read with
 // ds_read_b128; a transposed operand (contraction is its row) keeps its
 // natural layout, 64 rows x 512 B, and the MFMA fragments are gathered

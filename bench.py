@@ -272,8 +272,9 @@ def measured_peaks(torch, dev):
     """The part's own ceilings, measured in the same run: a register-only chain
     of bf16 MFMA 32x32x16 on every CU (1 wave per SIMD, 8 independent
     accumulators; random operand bits and constant 1.0, since the clock under
-    MFMA load depends on the operand bits) and a plain 1 GiB device copy with
-    one 16-byte vector per thread (read + write bytes)."""
+    MFMA load depends on the operand bits), a plain 1 GiB device copy with
+    one 16-byte vector per thread (read + write bytes), and the grouped
+    GEMM's operand stream without its MFMAs."""
     import ctypes
     lib_path = os.path.join(ROOT, "moe_fake_quant_amd", "libfqpeaks.so")
     if not os.path.exists(lib_path):
@@ -313,10 +314,35 @@ def measured_peaks(torch, dev):
     torch.cuda.synchronize()
     copy_gbs = 2 * nbytes * 5 / (s1.elapsed_time(e1) * 1e-3) / 1e9
     del src, dst, out
+    # the grouped GEMM's operand stream alone (its two-stage LDS ring, 64 KiB per
+    # 64-deep stage of a 256 x 256 tile, panels shared as the forward shares
+    # them): the rate a tile of this design cannot beat, as TFLOP/s of the tile
+    lib.fqp_operand_stream.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+                                       ctypes.c_int, ctypes.c_void_p]
+    panels, ntiles = 512, 12
+    xs = torch.empty(panels << 20, dtype=torch.uint8, device=dev)
+    ws = torch.empty(panels << 20, dtype=torch.uint8, device=dev)
+    xs.fill_(0x3c)
+    ws.fill_(0x3c)
+    assert lib.fqp_operand_stream(xs.data_ptr(), ws.data_ptr(), panels, n_cu, 2, st) == 0
+    torch.cuda.synchronize()
+    s2 = torch.cuda.Event(enable_timing=True)
+    e2 = torch.cuda.Event(enable_timing=True)
+    s2.record()
+    for _ in range(3):
+        assert lib.fqp_operand_stream(xs.data_ptr(), ws.data_ptr(), panels, n_cu, ntiles, st) == 0
+    e2.record()
+    torch.cuda.synchronize()
+    ms_s = s2.elapsed_time(e2) / 3
+    del xs, ws
+    stages = ntiles * 32
+    tile_tflops = 2 * 256 * 256 * 64 * n_cu * stages / (ms_s * 1e-3) / 1e12
     return {"mfma_bf16_chain_TFLOP/s": res,
             "mfma_bf16_chain_pct_of_spec": round(100 * res["random_operands"] / MI355X_BF16_PEAK_TFLOPS, 1),
             "copy_GB/s": round(copy_gbs, 1),
-            "copy_pct_of_spec": round(100 * copy_gbs / MI355X_HBM_PEAK_GBS, 1)}
+            "copy_pct_of_spec": round(100 * copy_gbs / MI355X_HBM_PEAK_GBS, 1),
+            "gemm_operand_stream": {"us_per_stage": round(ms_s * 1e3 / stages, 3),
+                                    "tile_TFLOP/s": round(tile_tflops, 1)}}
 
 
 def scattered_rows_floor(torch, dev, rows, row_of, T, topk, H):
@@ -513,6 +539,11 @@ def main():
                          "TFLOP/s": round(kind_flops / (ms * 1e-3) / 1e12, 2)}
     dom = max(kernels, key=lambda k: kernels[k]["ms_per_step"])
     achieved = kernels[dom]["TFLOP/s"]
+    if peaks and peaks.get("gemm_operand_stream"):
+        # the forward against the stream its own tiles need (both stacks' launches,
+        # partial last rounds and ragged tails included)
+        kernels["gemm_fwd"]["pct_of_operand_stream"] = round(
+            100 * kernels["gemm_fwd"]["TFLOP/s"] / peaks["gemm_operand_stream"]["tile_TFLOP/s"], 1)
 
     # FQ pass over both stacks: read bf16 + write bf16 + read the scales
     nel = E * (2 * Fh * H + H * Fh)

@@ -141,9 +141,69 @@ __global__ __launch_bounds__(512) void k_stream_gather(const uint4 *__restrict__
   if (threadIdx.x == 0) out_l[t] = x;
 }
 
+// 16 bytes per lane from global memory into LDS (lds_wave_base + 16 * lane),
+// the lane reading base + off, base uniform in scalar registers; the asm
+// starts with the wait states a base register or M0 written just before need.
+__device__ __forceinline__ void dma16(const char *base, uint32_t off, char *lds_wave_base) {
+  const uint32_t m0v = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_wave_base);
+  const uint64_t b = (uint64_t)(uintptr_t)base;
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b);
+  const uint64_t sb = ((uint64_t)hi << 32) | (uint64_t)lo;
+  asm volatile("s_nop 4\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(sb), "{m0}"(m0v)
+               : "memory");
+}
+
+constexpr size_t kStreamPanel = (size_t)256 * 4096;  // 256 rows of 4 KiB
+
+// The forward grouped GEMM's operand stream alone, with its ring and its
+// panel sharing: per 64-deep stage each 8-wave block moves 256 rows x 128 B
+// of an X panel and of a W panel (4 KiB rows, as at hidden 2048) into a
+// two-stage LDS ring with global_load_lds, waits for the stage, and issues
+// the next; no MFMAs. A tile is 32 stages. On each XCD (blocks b % 8) the X
+// panel of a tile is shared by 6 consecutive blocks and its W panel by every
+// 6th, as the forward's (row tile, i tile) list shares them.
+__global__ __launch_bounds__(512) void k_operand_stream(const char *xs, const char *ws, int npx,
+                                                       int npw, int ntiles) {
+  __shared__ __attribute__((aligned(1024))) char ring[2 * 65536];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+  const int nst = ntiles * 32;
+  auto issue = [&](int t) {
+    const int tile = t >> 5, kt = t & 31;
+    const int px = ((tile * 8 + xcd) * 6 + slot / 6) % npx;
+    const int pw = ((tile * 8 + xcd) * 6 + slot % 6) % npw;
+    char *st = ring + (t & 1) * 65536;
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii) {
+      const uint32_t off =
+          (uint32_t)(((wave * 4 + ii) * 8 + (lane >> 3)) * 4096 + kt * 128 + (lane & 7) * 16);
+      dma16(xs + (size_t)px * kStreamPanel, off, st + (wave * 4 + ii) * 1024);
+      dma16(ws + (size_t)pw * kStreamPanel, off, st + 32768 + (wave * 4 + ii) * 1024);
+    }
+  };
+  issue(0);
+  for (int t = 0; t < nst; ++t) {
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's loads of stage t
+    asm volatile("s_barrier" ::: "memory");
+    if (t + 1 < nst) issue(t + 1);
+  }
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+}
+
 }  // namespace
 
 extern "C" {
+
+// xs, ws: device buffers of at least panels * 1 MiB each (panels >= 1);
+// blocks a multiple of 8. Moves blocks * ntiles * 32 * 64 KiB.
+int fqp_operand_stream(const void *xs, const void *ws, int panels, int blocks, int ntiles,
+                       void *stream) {
+  if (!xs || !ws || panels <= 0 || blocks <= 0 || blocks % 8 != 0 || ntiles <= 0) return 1;
+  hipLaunchKernelGGL(k_operand_stream, dim3(blocks), dim3(512), 0, (hipStream_t)stream,
+                     (const char *)xs, (const char *)ws, panels, panels, ntiles);
+  return hipGetLastError() == hipSuccess ? 0 : 4;
+}
 
 // flops = 32*32*16*2 * 8 * iters * blocks * 4 waves. out: blocks * 256 floats.
 int fqp_mfma_chain(float *out, int blocks, int iters, int random_data, void *stream) {

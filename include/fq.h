@@ -315,8 +315,14 @@ fq_status fq_validate(const int32_t *expert_ids, int32_t T, int32_t topk, int32_
  * K % 64 == 0; other shapes run on zero-padded copies of W_fq, x and y in
  * the workspace (the padded K columns add nothing, the padded N rows are
  * not copied back), at the cost of those copies.
- * Workspace: fq_workspace_bytes(FQ_OP_GEMM_FWD, shape, R_max, wq->fmt | aq->fmt << 8)
- * (0 for a tile-aligned shape with w_fq given and no activation FQ).
+ * Workspace: fq_workspace_bytes(FQ_OP_GEMM_FWD, shape, R_max, wq->fmt | aq->fmt << 8).
+ * A call whose 256 x 256 output tiles would leave half of the GPU's CUs or
+ * more idle splits each tile's contraction into 2-8 parts and adds the
+ * parts' fp32 sums in part order afterwards (S * R_max * N * 4 bytes of the
+ * workspace). The split is optional: a workspace that holds everything
+ * else but not these sums runs the call unsplit (so a tile-aligned shape
+ * with w_fq given and no activation FQ may pass no workspace). Results are
+ * deterministic for a given R_max, shape, workspace size and device.
  * ---------------------------------------------------------------------- */
 fq_status fq_grouped_gemm_fwd(const uint16_t *x_bf16, int32_t R_max, const int32_t *seg_offsets,
                               fq_shape shape, const uint16_t *w_bf16, const uint16_t *w_fq,
@@ -348,7 +354,9 @@ fq_status fq_grouped_gemm_fwd(const uint16_t *x_bf16, int32_t R_max, const int32
  * is 0 with a neutral scale: 1 on the integer / FP8 grids, theta 0 for
  * NVFP4, zero point 0, so its straight-through factor is 0), and only the
  * call's own region of dx, dscale and dzero_point is written.
- * Workspace: fq_workspace_bytes(FQ_OP_GEMM_BWD, shape, R_max, wq->fmt | aq->fmt << 8).
+ * Workspace: fq_workspace_bytes(FQ_OP_GEMM_BWD, shape, R_max, wq->fmt | aq->fmt << 8);
+ * dX of a small call splits its contraction as the forward does (optional
+ * in the same way: S * R_max * K * 4 bytes).
  * ---------------------------------------------------------------------- */
 fq_status fq_grouped_gemm_bwd_scale(const uint16_t *dy_bf16, const uint16_t *x_bf16,
                                     int32_t R_max, const int32_t *seg_offsets, fq_shape shape,
@@ -379,7 +387,11 @@ fq_status fq_grouped_gemm_bwd_scale(const uint16_t *dy_bf16, const uint16_t *x_b
  * perm / x_tok non-NULL unless R_max == 0.
  * Workspace: fq_workspace_bytes(FQ_OP_GEMM_FWD, shape, max(R_max, T),
  *   w_fq ? 0 : wq->fmt), resp. fq_workspace_bytes(FQ_OP_GEMM_BWD, shape,
- *   max(R_max, T), 0); the zero-padded path copies the T token rows.
+ *   max(R_max, T), 0); the zero-padded path copies the T token rows. The
+ *   forward splits its contraction (see fq_grouped_gemm_fwd) when the
+ *   workspace also holds the parts' sums for R_max rows, which the size
+ *   for max(R_max, T) = R_max does; the bits then equal the plain call's
+ *   with the same workspace.
  * ---------------------------------------------------------------------- */
 fq_status fq_actfq(const uint16_t *x_bf16, int32_t rows, int32_t K, const fq_act_q *aq,
                    uint16_t *xq_bf16, fq_stream stream);

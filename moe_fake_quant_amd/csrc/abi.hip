@@ -128,11 +128,15 @@ int padded_group(int group, fq_shape s, fq_shape p) {
   return group == s.K ? p.K : group;
 }
 
-size_t gemm_ws_core(int op, fq_shape s, int R_max, int fmts) {
+// split_rows: with the scratch of the contraction split of a small call of
+// that many routed rows (FWD, or the backward's DGRAD), which a call uses only
+// when its workspace holds it; 0 = without
+size_t gemm_ws_core(int op, fq_shape s, int R_max, int fmts, int split_rows) {
   int wfmt = fmts & 0xFF, afmt = (fmts >> 8) & 0xFF;
   size_t b = 0;
   if (wfmt != FQ_FMT_NONE) b += align_up((size_t)s.E * s.N * s.K * 2);
   if (afmt != FQ_FMT_NONE) b += align_up((size_t)R_max * s.K * 2);
+  b += align_up(gemm_ksplit_bytes(op == FQ_OP_GEMM_FWD, s, split_rows));
   if (op == FQ_OP_GEMM_BWD) {
     // dScale partials per row chunk and 16-block (the finest group), for the
     // scale and the zero point, and the chunk prefix
@@ -147,8 +151,8 @@ size_t gemm_ws_core(int op, fq_shape s, int R_max, int fmts) {
 
 // Padded shapes: the call's own W_fq (if materialized), the zero-padded
 // operands, outputs and scales, then the padded problem's own workspace.
-size_t gemm_ws(int op, fq_shape s, int R_max, int fmts) {
-  if (!gemm_needs_pad(op, s)) return gemm_ws_core(op, s, R_max, fmts);
+size_t gemm_ws(int op, fq_shape s, int R_max, int fmts, int split_rows) {
+  if (!gemm_needs_pad(op, s)) return gemm_ws_core(op, s, R_max, fmts, split_rows);
   const fq_shape p = gemm_pad_shape(op, s);
   const int wfmt = fmts & 0xFF, afmt = (fmts >> 8) & 0xFF;
   const size_t E = (size_t)s.E, Rm = (size_t)(R_max > 0 ? R_max : 0);
@@ -162,7 +166,7 @@ size_t gemm_ws(int op, fq_shape s, int R_max, int fmts) {
     b += align_up(Rm * p.K * 2);                                // padded dx
     b += 4 * align_up(E * p.N * (p.K / 16) * 4);                // scale, zp, dscale, dzp
   }
-  return b + gemm_ws_core(op, p, R_max, wfmt | (afmt << 8));
+  return b + gemm_ws_core(op, p, R_max, wfmt | (afmt << 8), split_rows);
 }
 
 // A learnable activation scale's gradient: only the static per-tensor formats
@@ -193,7 +197,7 @@ const char *fq_last_error(void) { return g_last_error.c_str(); }
 
 size_t fq_workspace_bytes(int32_t op, fq_shape shape, int32_t R_max, int32_t fmts) {
   if (op == FQ_OP_PERMUTE) return permute_workspace_bytes(shape.E > 0 ? shape.E : 1, R_max);
-  if (op == FQ_OP_GEMM_FWD || op == FQ_OP_GEMM_BWD) return gemm_ws(op, shape, R_max, fmts);
+  if (op == FQ_OP_GEMM_FWD || op == FQ_OP_GEMM_BWD) return gemm_ws(op, shape, R_max, fmts, R_max);
   if (op == FQ_OP_TOPK_KL) return kAlign;
   if (op == FQ_OP_ACT_SCALE_GRAD) {
     if (shape.N < 0 || shape.K <= 0) return 0;
@@ -385,7 +389,7 @@ namespace {
 // arguments already checked, workspace large enough.
 void gemm_fwd_core(const uint16_t *x, int R_max, const int32_t *seg, fq_shape s, const uint16_t *w,
                    const uint16_t *w_fq, const fq_weight_q *wq, const fq_act_q *aq, uint16_t *y,
-                   void *ws, hipStream_t st, const int32_t *xperm, int topk) {
+                   void *ws, bool split, hipStream_t st, const int32_t *xperm, int topk) {
   const int afmt = act_fmt(aq);
   Carver c(ws);
   const uint16_t *wfq = w_fq;
@@ -400,7 +404,9 @@ void gemm_fwd_core(const uint16_t *x, int R_max, const int32_t *seg, fq_shape s,
     launch_act_fq(x, R_max, s.K, seg + s.E, afmt, aq->scale, t, st);
     xq = t;
   }
-  launch_gemm_fwd(xq, R_max, seg, s, wfq, y, st, xperm, topk);
+  const size_t part_bytes = split ? gemm_ksplit_bytes(true, s, R_max) : 0;
+  float *part = part_bytes ? c.take<float>(part_bytes) : nullptr;
+  launch_gemm_fwd(xq, R_max, seg, s, wfq, y, part, st, xperm, topk);
 }
 
 // fq_grouped_gemm_fwd and its routed-X form: x has x_rows rows; with xperm
@@ -429,14 +435,16 @@ fq_status gemm_fwd_call(const char *fn, const uint16_t *x, int32_t x_rows, const
                "bf16 tensors must be 16-byte aligned");
   const int afmt = act_fmt(aq);
   const int fmts = (w_fq ? 0 : wq->fmt) | (afmt << 8);
-  size_t need = gemm_ws(FQ_OP_GEMM_FWD, s, rows_ws, fmts);
-  if (need > 0 && (ws_bytes < need || !ws)) {
+  const size_t need = gemm_ws(FQ_OP_GEMM_FWD, s, rows_ws, fmts, R_max);
+  const size_t need_min = gemm_ws(FQ_OP_GEMM_FWD, s, rows_ws, fmts, 0);
+  if (need_min > 0 && (ws_bytes < need_min || !ws)) {
     set_error("%s: workspace %zu bytes < %zu needed", fn, ws_bytes, need);
     return FQ_ERR_WORKSPACE_TOO_SMALL;
   }
+  const bool split = ws && ws_bytes >= need;
   hipStream_t st = S(stream);
   if (!gemm_needs_pad(FQ_OP_GEMM_FWD, s)) {
-    gemm_fwd_core(x, R_max, seg, s, w, w_fq, wq, aq, y, ws, st, xperm, topk);
+    gemm_fwd_core(x, R_max, seg, s, w, w_fq, wq, aq, y, ws, split, st, xperm, topk);
     FQ_CHECK_LAUNCH(fn);
     return FQ_OK;
   }
@@ -456,8 +464,8 @@ fq_status gemm_fwd_call(const char *fn, const uint16_t *x, int32_t x_rows, const
   // routed X: every token row is copied (rows are not in segment order)
   if (x_rows > 0)
     launch_reshape_u16(x, 1, x_rows, s.K, x_p, x_rows, p.K, xperm ? nullptr : seg + s.E, st);
-  gemm_fwd_core(x_p, R_max, seg, p, nullptr, wfq_p, nullptr, aq, y_p, c.base + c.used, st, xperm,
-                topk);
+  gemm_fwd_core(x_p, R_max, seg, p, nullptr, wfq_p, nullptr, aq, y_p, c.base + c.used, split, st,
+                xperm, topk);
   if (R_max > 0) launch_reshape_u16(y_p, 1, R_max, p.N, y, R_max, s.N, seg + s.E, st);
   FQ_CHECK_LAUNCH(fn);
   return FQ_OK;
@@ -491,7 +499,7 @@ namespace {
 void gemm_bwd_core(const uint16_t *dy, const uint16_t *x, int R_max, const int32_t *seg, fq_shape s,
                    const uint16_t *w, const uint16_t *w_fq, const fq_weight_q *wq,
                    const fq_act_q *aq, uint16_t *dx, float *dscale, float *dzp, void *ws,
-                   hipStream_t st, const int32_t *xperm, int topk) {
+                   bool split, hipStream_t st, const int32_t *xperm, int topk) {
   const bool want_ds = dscale || dzp;
   const bool per_tensor = wq->group == FQ_GROUP_TENSOR;
   const int afmt = act_fmt(aq);
@@ -503,7 +511,9 @@ void gemm_bwd_core(const uint16_t *dy, const uint16_t *x, int R_max, const int32
     wfq = t;
   }
   if (dx && R_max > 0) {
-    launch_gemm_dgrad(dy, R_max, seg, s, wfq, dx, st);
+    const size_t part_bytes = split ? gemm_ksplit_bytes(false, s, R_max) : 0;
+    float *part = part_bytes ? c.take<float>(part_bytes) : nullptr;
+    launch_gemm_dgrad(dy, R_max, seg, s, wfq, dx, part, st);
     if (afmt != FQ_FMT_NONE) launch_act_mask(dx, x, R_max, s.K, seg + s.E, afmt, aq->scale, st);
   }
   if (want_ds) {
@@ -574,14 +584,18 @@ fq_status gemm_bwd_call(const char *fn, const uint16_t *dy, const uint16_t *x, i
                "bf16 tensors must be 16-byte aligned");
   const int afmt = act_fmt(aq);
   // FQ_w(W) is materialized only for dX
-  size_t need = gemm_ws(FQ_OP_GEMM_BWD, s, rows_ws, ((w_fq || !dx) ? 0 : wq->fmt) | (afmt << 8));
-  if (ws_bytes < need || !ws) {
+  const int fmts = ((w_fq || !dx) ? 0 : wq->fmt) | (afmt << 8);
+  const size_t need = gemm_ws(FQ_OP_GEMM_BWD, s, rows_ws, fmts, dx ? R_max : 0);
+  const size_t need_min = gemm_ws(FQ_OP_GEMM_BWD, s, rows_ws, fmts, 0);
+  if (ws_bytes < need_min || !ws) {
     set_error("%s: workspace %zu bytes < %zu needed", fn, ws_bytes, need);
     return FQ_ERR_WORKSPACE_TOO_SMALL;
   }
+  const bool split = ws_bytes >= need;
   hipStream_t st = S(stream);
   if (!gemm_needs_pad(FQ_OP_GEMM_BWD, s)) {
-    gemm_bwd_core(dy, x, R_max, seg, s, w, w_fq, wq, aq, dx, dscale, dzp, ws, st, xperm, topk);
+    gemm_bwd_core(dy, x, R_max, seg, s, w, w_fq, wq, aq, dx, dscale, dzp, ws, split, st, xperm,
+                  topk);
     FQ_CHECK_LAUNCH(fn);
     return FQ_OK;
   }
@@ -628,7 +642,7 @@ fq_status gemm_bwd_call(const char *fn, const uint16_t *dy, const uint16_t *x, i
   float *ds_out = dscale ? (per_tensor ? dscale : ds_p) : nullptr;
   float *dzp_out = dzp ? dzp_p : nullptr;
   gemm_bwd_core(dy_p, x ? x_p : nullptr, R_max, seg, p, w_p, wfq_p, &wq_p, aq,
-                dx ? dx_p : nullptr, ds_out, dzp_out, c.base + c.used, st, xperm, topk);
+                dx ? dx_p : nullptr, ds_out, dzp_out, c.base + c.used, split, st, xperm, topk);
   if (dx && R_max > 0) launch_reshape_u16(dx_p, 1, R_max, p.K, dx, R_max, s.K, seg + s.E, st);
   if (dscale && !per_tensor) launch_reshape_f32(ds_p, s.E, p.N, Gp, dscale, s.N, G, 0.0f, st);
   if (dzp) launch_reshape_f32(dzp_p, s.E, p.N, Gp, dzp, s.N, G, 0.0f, st);

@@ -159,6 +159,15 @@ struct GemmArgs {
   // xperm[r] / topk of a token-indexed X; NULL = X is indexed by routed row
   const int32_t *xperm;
   FastDiv xtopk;
+  // FWD / DGRAD split along the contraction (small calls that would leave CUs
+  // idle): each tile's contraction runs as ksplit parts of kper stages, part
+  // s writing fp32 sums to part[s, R_max, ldo], added afterwards in part order
+  int ksplit, kper;
+  float *part;
+  int part_rows;
+  // FWD / DGRAD tile order: groups of gm row tiles, each group's tiles with
+  // the row tile fastest (gm = 1: i fastest)
+  int gm;
 };
 
 constexpr int kMaxExperts = 1024;
@@ -534,15 +543,25 @@ struct Tile {
   int e, i0, j0, j_end;
   int r0, r1;  // WGRAD: the routed rows [r0, r1) of this row chunk
   int chunk;   // WGRAD: -1 = dScale written directly, else the partial row
+  int ks;      // FWD / DGRAD split along the contraction: the part
 };
 
-// Tile w of the list. FWD / DGRAD tiles: (row tile, i tile) with i fastest,
-// the row tiles of each expert from tile_start; WGRAD: (expert, j tile, i tile).
-template <int MODE>
+// Tile w of the list. FWD / DGRAD tiles: (row tile, i tile), the row tiles
+// of each expert from tile_start, in groups of gm row tiles: a group's tiles
+// run i tile by i tile, its row tiles fastest (gm = 1: i fastest), so that
+// the tiles in flight on an XCD form a block that shares both operands'
+// panels (GROUPED; the routed-X kernels, short of registers, keep gm = 1).
+// WGRAD: (expert, j tile, i tile).
+template <int MODE, bool SPLIT = false, bool GROUPED = false>
 __device__ __forceinline__ Tile decode_tile(const GemmArgs &a, const int *tile_start, int w) {
   Tile t;
   t.j_end = 0;
   t.chunk = -1;
+  t.ks = 0;
+  if constexpr (SPLIT) {  // unit (tile, part), parts fastest
+    t.ks = w % a.ksplit;
+    w /= a.ksplit;
+  }
   if (MODE == WGRAD) {
     // unit (row chunk c, j tile, i tile); tile_start holds the chunk prefix
     const int per_c = a.n_it * a.n_jt;
@@ -558,8 +577,20 @@ __device__ __forceinline__ Tile decode_tile(const GemmArgs &a, const int *tile_s
     const bool single = tile_start[t.e + 1] - tile_start[t.e] == 1;
     t.chunk = (single && a.group <= 128) ? -1 : c;
   } else {
-    const int tile = w / a.n_it;
-    t.i0 = (w - tile * a.n_it) * BI;
+    int tile;
+    if constexpr (GROUPED) {
+      const int gsz = a.gm * a.n_it;  // units per group
+      const int g = w / gsz;
+      const int rt0 = g * a.gm;
+      const int gs = min(a.gm, tile_start[a.E] - rt0);
+      const int win = w - g * gsz;
+      const int it = win / gs;
+      tile = rt0 + (win - it * gs);
+      t.i0 = it * BI;
+    } else {
+      tile = w / a.n_it;
+      t.i0 = (w - tile * a.n_it) * BI;
+    }
     t.e = expert_of_tile(tile_start, a.E, tile);
     t.j0 = a.seg[t.e] + (tile - tile_start[t.e]) * BJ;
     t.j_end = a.seg[t.e + 1];
@@ -588,10 +619,11 @@ constexpr int kVmPerStageB = MODE == FWD ? 4 : 8;
 
 // ROUTED: X (FWD's Q, WGRAD's P) is read by token row through a.xperm
 // (compile time, so the kernels without it keep their registers).
-template <int MODE, bool ROUTED>
+template <int MODE, bool ROUTED, bool SPLIT = false>
 struct TileLoads {
   const char *pbase, *qbase;
   int c_total, nk;
+  int c_lo;  // SPLIT: the first contraction element of this part
   NormalDMA pn, qn;
   TransDMA pt, qt;
   // WGRAD with routed X: the (token, slot) pair indices of this wave's eight
@@ -605,6 +637,11 @@ struct TileLoads {
                                        int first_kt = 0) {
     seg_lo = (MODE == WGRAD) ? t.r0 : 0;
     c_total = (MODE == WGRAD) ? t.r1 - t.r0 : (MODE == FWD) ? a.K : a.N;
+    c_lo = 0;
+    if constexpr (SPLIT) {
+      c_lo = t.ks * a.kper * BK;
+      c_total = min(a.kper * BK, c_total - c_lo);
+    }
     nk = (c_total + BK - 1) / BK;
     const size_t NK = (size_t)a.N * a.K;
     const int xs = wave ^ 4;
@@ -643,7 +680,7 @@ struct TileLoads {
   // stages are issued in order kt = first_kt, first_kt + 1, ...
   template <int S>
   __device__ __forceinline__ void issue(const GemmArgs &a, int kt, int wave) {
-    const int c0 = kt * BK;
+    const int c0 = (SPLIT ? c_lo : 0) + kt * BK;
     const int xs = wave ^ 4;
     if (MODE == FWD) {
       if (wave < 4) {
@@ -652,7 +689,7 @@ struct TileLoads {
       }
       qn.template issue<S>(qbase, stage_q<S>(), c0, xs);
     } else if (MODE == DGRAD) {
-      pt.issue(pbase, a.K, stage_p<S>(), c0, c_total, xs);
+      pt.issue(pbase, a.K, stage_p<S>(), c0, (SPLIT ? c_lo : 0) + c_total, xs);
       qn.template issue<S>(qbase, stage_q<S>(), c0, xs);
     } else {
       if constexpr (ROUTED) {
@@ -826,7 +863,7 @@ __device__ __forceinline__ void run_tile_wgrad(const GemmArgs &a, const int *til
 // after the last read of stage t. Each wave waits for its own loads of a
 // stage before the barrier that opens the first phase reading it. A's
 // epilogue runs while B multiplies the last half.
-template <int MODE, int WFMT, bool ROUTED>
+template <int MODE, int WFMT, bool ROUTED, bool SPLIT>
 __device__ __forceinline__ int run_tile(const GemmArgs &a, const int *tile_start, const Tile &tl,
                                         int pre, int next_w) {
   static_assert(MODE != WGRAD, "the ping-pong serves the forward and dgrad tiles");
@@ -835,7 +872,7 @@ __device__ __forceinline__ int run_tile(const GemmArgs &a, const int *tile_start
   const int wi = wave & 1, wj = wave >> 1;  // 2 x 4 waves: 128 (i) x 64 (j) each
   const bool grp_b = wave >= 4;             // j columns 128..255 of the tile
   const int i0 = tl.i0, j0 = tl.j0, j_end = tl.j_end;
-  TileLoads<MODE, ROUTED> ld(a, tl, wave, lane);
+  TileLoads<MODE, ROUTED, SPLIT> ld(a, tl, wave, lane);
   const int nk = ld.nk;
   // a wave whose 64 rows all lie past the expert's last row (the ragged last
   // row tile) skips its fragment reads and MFMAs; it still takes part in the
@@ -957,8 +994,8 @@ __device__ __forceinline__ int run_tile(const GemmArgs &a, const int *tile_start
   // half) and takes stage 1 of the next tile after the closing barrier.
   // The next tile's loads are set up once, here, for both stages (with
   // routed rows that means one lookup, made while no store is in flight).
-  TileLoads<MODE, ROUTED> nl(a, next_w >= 0 ? decode_tile<MODE>(a, tile_start, next_w) : tl, wave,
-                             lane);
+  TileLoads<MODE, ROUTED, SPLIT> nl(
+      a, next_w >= 0 ? decode_tile<MODE, SPLIT, SPLIT && !ROUTED>(a, tile_start, next_w) : tl, wave, lane);
   auto issue_next = [&](auto stage_tag) -> bool {
     constexpr int S = decltype(stage_tag)::value;
     if (next_w < 0) return false;
@@ -970,7 +1007,30 @@ __device__ __forceinline__ int run_tile(const GemmArgs &a, const int *tile_start
 
   // accumulator (s, u, v) of this lane: i = i0 + wi*128 + s*32 + 8*(v/4) + 4*(lane/32) + v%4,
   //                                     j = j0 + wj*64 + u*32 + lane%32
-  {
+  if constexpr (SPLIT) {
+    // fp32 sums of this part straight from the accumulators: four
+    // consecutive i per lane (one 16-byte store), row j per lane % 32
+    (void)issue_next(std::integral_constant<int, 0>{});
+    const int ldo = (MODE == FWD) ? a.N : a.K;
+    if (live) {
+      float *pb = a.part + (size_t)tl.ks * a.part_rows * ldo + i0 + wi * 128 + 4 * (lane >> 5);
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int j = j0 + wj * WJ_TILE + u * 32 + (lane & 31);
+        if (j < j_end) {
+          float *prow = pb + (size_t)j * ldo;
+#pragma unroll
+          for (int s = 0; s < 4; ++s)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const float4 v = make_float4(acc[s][u][4 * q], acc[s][u][4 * q + 1],
+                                           acc[s][u][4 * q + 2], acc[s][u][4 * q + 3]);
+              *reinterpret_cast<float4 *>(prow + s * 32 + 8 * q) = v;
+            }
+        }
+      }
+    }
+  } else {
     (void)issue_next(std::integral_constant<int, 0>{});
     // The bf16 tile goes out through LDS: each wave writes its 128 (i) x 32 (j)
     // half-slab row by row into its 8 KiB of buffer 1, then stores whole
@@ -1031,7 +1091,7 @@ __device__ __forceinline__ int run_tile(const GemmArgs &a, const int *tile_start
 // operand panels in that XCD's L2. FWD / DGRAD tiles: (row tile, i tile)
 // with i fastest; the row tiles of each expert follow from seg_offsets.
 // WGRAD tiles: (expert, j tile, i tile).
-template <int MODE, int WFMT, bool ROUTED>
+template <int MODE, int WFMT, bool ROUTED, bool SPLIT = false>
 __global__ __launch_bounds__(NT) void k_grouped_gemm(GemmArgs a) {
   __shared__ int tile_start[kMaxExperts + 1];
   int total;
@@ -1042,7 +1102,7 @@ __global__ __launch_bounds__(NT) void k_grouped_gemm(GemmArgs a) {
       for (int e = threadIdx.x; e <= a.E; e += NT) a.chunk_start_out[e] = tile_start[e];
   } else {
     build_tile_prefix(a.seg, a.E, BJ, 0, tile_start);
-    total = tile_start[a.E] * a.n_it;
+    total = tile_start[a.E] * a.n_it * (SPLIT ? a.ksplit : 1);
   }
   const int nslot = gridDim.x >> 3, xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
   const int chunk = (total + 7) >> 3;
@@ -1050,12 +1110,12 @@ __global__ __launch_bounds__(NT) void k_grouped_gemm(GemmArgs a) {
   int pre = 0;  // stages of the coming tile already in flight
   for (int w = xcd * chunk + slot; w < w_end; w += nslot) {
     const int next = w + nslot < w_end ? w + nslot : -1;
-    const Tile tl = decode_tile<MODE>(a, tile_start, w);
+    const Tile tl = decode_tile<MODE, SPLIT, SPLIT && !ROUTED>(a, tile_start, w);
     if constexpr (MODE == WGRAD) {
       run_tile_wgrad<MODE, WFMT, ROUTED>(a, tile_start, tl, pre != 0, next);
       pre = next >= 0;
     } else {
-      pre = run_tile<MODE, WFMT, ROUTED>(a, tile_start, tl, pre, next);
+      pre = run_tile<MODE, WFMT, ROUTED, SPLIT>(a, tile_start, tl, pre, next);
     }
   }
 }
@@ -1093,13 +1153,44 @@ __global__ __launch_bounds__(256) void k_reduce_dscale(const float *__restrict__
   }
 }
 
+// A contraction split into S parts: out[j, i] = bf16(sum over s = 0..S-1, in
+// that order, of part[s, j, i]) for the rows [seg[0], seg[E]) the tiles
+// cover. Eight columns per thread (two 16-byte loads per part, one 16-byte
+// store), grid-stride.
+__global__ __launch_bounds__(256) void k_ksplit_reduce(const float *__restrict__ part, int S,
+                                                       int part_rows, int ldo,
+                                                       const int32_t *__restrict__ seg, int E,
+                                                       uint16_t *__restrict__ out) {
+  const int r0 = seg[0], r1 = seg[E];
+  const int cpr = ldo >> 3;
+  const int n = (r1 - r0) * cpr;
+  const size_t plane = (size_t)part_rows * ldo;
+  for (int idx = blockIdx.x * 256 + threadIdx.x; idx < n; idx += gridDim.x * 256) {
+    const int j = r0 + idx / cpr, c = idx - (idx / cpr) * cpr;
+    const size_t o = (size_t)j * ldo + (size_t)c * 8;
+    float4 lo = *reinterpret_cast<const float4 *>(part + o);
+    float4 hi = *reinterpret_cast<const float4 *>(part + o + 4);
+    for (int k = 1; k < S; ++k) {
+      const float4 a = *reinterpret_cast<const float4 *>(part + k * plane + o);
+      const float4 b = *reinterpret_cast<const float4 *>(part + k * plane + o + 4);
+      lo.x += a.x; lo.y += a.y; lo.z += a.z; lo.w += a.w;
+      hi.x += b.x; hi.y += b.y; hi.z += b.z; hi.w += b.w;
+    }
+    uint4 v;
+    v.x = pack_bf16(lo.x, lo.y);
+    v.y = pack_bf16(lo.z, lo.w);
+    v.z = pack_bf16(hi.x, hi.y);
+    v.w = pack_bf16(hi.z, hi.w);
+    *reinterpret_cast<uint4 *>(out + o) = v;
+  }
+}
+
 }  // namespace
 
 // ============================================================ launchers ====
-// One block per CU, a multiple of 8 (the XCD count), but no more blocks than
-// an upper bound on the work units of the call (a small call then launches a
-// small grid). The CU count is read once per device.
-static int gemm_grid(size_t max_units) {
+// The current device's CU count rounded down to a multiple of 8 (the XCD
+// count), read once per device (256 when there is no device).
+static int device_cus() {
   constexpr int kMaxDevices = 64;
   static std::atomic<int> cached[kMaxDevices];
   int dev = 0;
@@ -1108,25 +1199,104 @@ static int gemm_grid(size_t max_units) {
   if (cus <= 0) {
     cus = 256;
     if (dev >= 0) {
-      (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+      if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        cus = 256;
       cached[dev].store(cus, std::memory_order_relaxed);
     }
   }
   cus = cus / 8 * 8;
-  if (cus <= 0) cus = 8;
+  return cus > 0 ? cus : 8;
+}
+
+// One block per CU, a multiple of 8, but no more blocks than an upper bound
+// on the work units of the call (a small call then launches a small grid).
+static int gemm_grid(size_t max_units) {
+  const int cus = device_cus();
   const size_t units8 = (max_units + 7) / 8 * 8;
   return (int)(units8 < (size_t)cus ? (units8 > 0 ? units8 : 8) : (size_t)cus);
 }
 
-// FWD / DGRAD units: row tiles (at most ceil(R_max / BJ) + E, one partial
-// tile per expert) times the i tiles
+// FWD / DGRAD row tiles of R rows over E experts, at most: with m non-empty
+// experts (m <= min(E, R)) each holds 256 (q_e - 1) + 1 rows or more for its
+// q_e tiles, so the tiles number at most (R - m) / 256 + m, largest at
+// m = min(E, R)
+static size_t rowtile_bound(int R, int E) {
+  if (R <= 0) return 0;
+  const int m = E < R ? E : R;
+  return (size_t)((R - m) / BJ) + (size_t)m;
+}
 static size_t rowtile_units(int R_max, int E, int n_it) {
-  return ((size_t)(R_max + BJ - 1) / BJ + (size_t)E) * (size_t)n_it;
+  return rowtile_bound(R_max, E) * (size_t)n_it;
+}
+
+// FWD / DGRAD split along the contraction. A call whose tiles would leave at
+// least half of the CUs idle runs each tile as S = CUs / units parts (at most
+// 8, each at least 8 stages), all tiles' parts in one grid; the parts' fp32
+// sums are added in part order afterwards. 1 = no split.
+// S parts asked for, at most 8 and at least 8 stages each (the sums' second
+// pass costs about as much as two stages), as the parts of ceil(nk / S)
+// stages that cover nk stages
+static int ksplit_parts(int S, int nk) {
+  S = S < 8 ? S : 8;
+  S = S < nk / 8 ? S : nk / 8;
+  if (S < 2) return 1;
+  const int per = (nk + S - 1) / S;
+  return (nk + per - 1) / per;
+}
+static int ksplit_for_units(size_t units, int nk) {
+  const int cus = device_cus();
+  if (units == 0 || units * 2 > (size_t)cus) return 1;
+  return ksplit_parts((int)((size_t)cus / units), nk);
+}
+size_t gemm_ksplit_bytes(bool fwd, fq_shape s, int R_max) {
+  const int n_it = (fwd ? s.N : s.K) / BI, ldo = fwd ? s.N : s.K;
+  const int nk = ((fwd ? s.K : s.N) + BK - 1) / BK;
+  if (R_max <= 0 || n_it <= 0) return 0;
+  const int S = ksplit_for_units(rowtile_units(R_max, s.E, n_it), nk);
+  return S > 1 ? (size_t)S * (size_t)R_max * (size_t)ldo * 4 : 0;
+}
+
+// launches the row-tile kernel, split along the contraction when the call is
+// small enough (then `part` holds the parts' sums and a reduce writes `out`)
+// Row tiles per group of the tile order: with T tiles in flight per XCD,
+// about sqrt(T) (a square block), but 1 (i fastest) unless a row tile has at
+// least twice that many i tiles; otherwise the tiles in flight already span
+// sqrt(T) row tiles or more.
+static int rowtile_group(int grid, int S, int n_it) {
+  const int tiles = grid / 8 / S;
+  int g = 1;
+  while ((g + 1) * (g + 1) <= tiles) ++g;
+  return n_it >= 2 * g ? g : 1;
+}
+
+template <int MODE, bool ROUTED>
+static void launch_rowtile_gemm(GemmArgs &a, int R_max, float *part, hipStream_t st) {
+  const size_t units = rowtile_units(R_max, a.E, a.n_it);
+  const int nk = ((MODE == FWD ? a.K : a.N) + BK - 1) / BK;
+  const int S = part ? ksplit_for_units(units, nk) : 1;
+  if (S < 2) {
+    const int grid = gemm_grid(units);
+    a.gm = ROUTED ? 1 : rowtile_group(grid, 1, a.n_it);
+    hipLaunchKernelGGL((k_grouped_gemm<MODE, 0, ROUTED>), dim3(grid), dim3(NT), 0, st, a);
+    return;
+  }
+  a.ksplit = S;
+  a.kper = (nk + S - 1) / S;
+  a.part = part;
+  a.part_rows = R_max;
+  const int grid = gemm_grid(units * S);
+  a.gm = ROUTED ? 1 : rowtile_group(grid, S, a.n_it);
+  hipLaunchKernelGGL((k_grouped_gemm<MODE, 0, ROUTED, true>), dim3(grid), dim3(NT), 0, st, a);
+  const int ldo = MODE == FWD ? a.N : a.K;
+  const long vecs = (long)R_max * (ldo / 8);
+  const int blocks = (int)std::min<long>((vecs + 255) / 256, (long)device_cus() * 8);
+  hipLaunchKernelGGL(k_ksplit_reduce, dim3(blocks > 0 ? blocks : 1), dim3(256), 0, st, part, S,
+                     R_max, ldo, a.seg, a.E, a.out);
 }
 
 void launch_gemm_fwd(const uint16_t *xq, int R_max, const int32_t *seg, fq_shape s,
-                     const uint16_t *wfq, uint16_t *y, hipStream_t st, const int32_t *xperm,
-                     int topk) {
+                     const uint16_t *wfq, uint16_t *y, float *part, hipStream_t st,
+                     const int32_t *xperm, int topk) {
   GemmArgs a{};
   a.p = wfq;
   a.q = xq;
@@ -1139,13 +1309,12 @@ void launch_gemm_fwd(const uint16_t *xq, int R_max, const int32_t *seg, fq_shape
   a.n_it = s.N / BI;
   a.out = y;
   if (R_max <= 0) return;
-  const dim3 grid(gemm_grid(rowtile_units(R_max, s.E, a.n_it)));
-  if (xperm) hipLaunchKernelGGL((k_grouped_gemm<FWD, 0, true>), grid, dim3(NT), 0, st, a);
-  else hipLaunchKernelGGL((k_grouped_gemm<FWD, 0, false>), grid, dim3(NT), 0, st, a);
+  if (xperm) launch_rowtile_gemm<FWD, true>(a, R_max, part, st);
+  else launch_rowtile_gemm<FWD, false>(a, R_max, part, st);
 }
 
 void launch_gemm_dgrad(const uint16_t *dy, int R_max, const int32_t *seg, fq_shape s,
-                       const uint16_t *wfq, uint16_t *dx, hipStream_t st) {
+                       const uint16_t *wfq, uint16_t *dx, float *part, hipStream_t st) {
   GemmArgs a{};
   a.p = wfq;
   a.q = dy;
@@ -1156,8 +1325,7 @@ void launch_gemm_dgrad(const uint16_t *dy, int R_max, const int32_t *seg, fq_sha
   a.n_it = s.K / BI;
   a.out = dx;
   if (R_max <= 0) return;
-  hipLaunchKernelGGL((k_grouped_gemm<DGRAD, 0, false>),
-                     dim3(gemm_grid(rowtile_units(R_max, s.E, a.n_it))), dim3(NT), 0, st, a);
+  launch_rowtile_gemm<DGRAD, false>(a, R_max, part, st);
 }
 
 size_t wgrad_max_chunks(int E, int R_max) {

@@ -77,11 +77,16 @@ void launch_permute(const int32_t *ids, int T, int topk, int ebegin, int E, int3
 
 // xperm / topk: routed row r of X is row xperm[r] / topk of a token-indexed
 // xq (FWD's X operand, WGRAD's X operand); NULL = xq indexed by routed row.
+// part: fp32 scratch of gemm_ksplit_bytes for a call small enough to split
+// along the contraction; NULL = never split.
 void launch_gemm_fwd(const uint16_t *xq, int R_max, const int32_t *seg, fq_shape s,
-                     const uint16_t *wfq, uint16_t *y, hipStream_t st,
+                     const uint16_t *wfq, uint16_t *y, float *part, hipStream_t st,
                      const int32_t *xperm = nullptr, int topk = 1);
 void launch_gemm_dgrad(const uint16_t *dy, int R_max, const int32_t *seg, fq_shape s,
-                       const uint16_t *wfq, uint16_t *dx, hipStream_t st);
+                       const uint16_t *wfq, uint16_t *dx, float *part, hipStream_t st);
+// scratch bytes of the FWD (fwd) or DGRAD contraction split of a call of
+// R_max routed rows on the current device (0: the call does not split)
+size_t gemm_ksplit_bytes(bool fwd, fq_shape s, int R_max);
 // The wgrad contraction over an expert's rows runs in chunks of at most this
 // many rows, so that one hot expert cannot serialize the grid.
 constexpr int kWgradChunkRows = 2048;

@@ -101,7 +101,9 @@ def _up(x):
 
 
 def test_workspace_sizes(pkg):
-    E, N, K, R = 8, 512, 256, 1000
+    # enough rows for the 256 x 256 tiles to fill a 256-CU (or 304-CU) part:
+    # no call splits its contraction, the sizes are the plain buffers
+    E, N, K, R = 8, 512, 256, 40000
     # forward: prequantized weights and no activation FQ need nothing
     assert _ws(pkg, pkg.FQ_OP_GEMM_FWD, (E, N, K), R) == 0
     # weight FQ inside the call: one bf16 W_fq stack; act FQ: one bf16 [R, K]
@@ -112,10 +114,22 @@ def test_workspace_sizes(pkg):
     # at most 2048 rows (every expert has at least one) and 16-block of K,
     # plus the chunk prefix, plus (per-tensor scales) the scale repeated per
     # channel and the per-channel dScale
-    chunks = (R + 2047) // 2048 + E
-    part = _up(chunks * N * (K // 16) * 4)
-    assert _ws(pkg, pkg.FQ_OP_GEMM_BWD, (E, N, K), R) == \
-        2 * part + _up((E + 1) * 4) + 2 * _up(E * N * 4)
+    def bwd_plain(R):
+        chunks = (R + 2047) // 2048 + E
+        part = _up(chunks * N * (K // 16) * 4)
+        return 2 * part + _up((E + 1) * 4) + 2 * _up(E * N * 4)
+    assert _ws(pkg, pkg.FQ_OP_GEMM_BWD, (E, N, K), R) == bwd_plain(R)
+    # a small call with a long contraction (1000 rows: at most 44 forward and
+    # 88 dX tiles; 32 and 16 stages of 64) also holds the fp32 sums of the
+    # parts its tiles' contraction is split into: 2 to 8 parts of [rows, N]
+    # (forward) or [rows, K] (dX)
+    E, N, K, r = 8, 1024, 2048, 1000
+    fwd = _ws(pkg, pkg.FQ_OP_GEMM_FWD, (E, N, K), r)
+    assert fwd % _up(r * N * 4) == 0 and 2 <= fwd // _up(r * N * 4) <= 8
+    bwd = _ws(pkg, pkg.FQ_OP_GEMM_BWD, (E, N, K), r) - bwd_plain(r)
+    assert bwd % _up(r * K * 4) == 0 and 2 <= bwd // _up(r * K * 4) <= 8
+    # a short contraction (256: 4 stages) is not split
+    assert _ws(pkg, pkg.FQ_OP_GEMM_FWD, (E, N, 256), r) == 0
     # permute: grows with the pair count, positive for any expert count
     a = _ws(pkg, pkg.FQ_OP_PERMUTE, (4, 0, 0), 1000)
     b = _ws(pkg, pkg.FQ_OP_PERMUTE, (4, 0, 0), 100000)

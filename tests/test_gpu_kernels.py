@@ -224,14 +224,16 @@ def test_gemm_fwd_prequantized_weights_match():
     y1 = torch.empty(R, N, dtype=torch.bfloat16, device="cuda")
     y2 = torch.empty_like(y1)
     F.fq_grouped_gemm_fwd(dev_bf16(x), R, dev_i32(seg), (E, N, K), wd, None, wq, None, y1, ws)
-    F.fq_grouped_gemm_fwd(dev_bf16(x), R, dev_i32(seg), (E, N, K), None, wfq, wq, None, y2, None)
+    # the same workspace: a call this small splits its contraction when the
+    # workspace holds the parts' sums, and runs unsplit without them
+    F.fq_grouped_gemm_fwd(dev_bf16(x), R, dev_i32(seg), (E, N, K), None, wfq, wq, None, y2, ws)
     torch.cuda.synchronize()
     assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
     # rows are independent: a row's output does not depend on its neighbours
     x2 = x.copy()
     x2[1::2] = 0
     y3 = torch.empty_like(y1)
-    F.fq_grouped_gemm_fwd(dev_bf16(x2), R, dev_i32(seg), (E, N, K), None, wfq, wq, None, y3, None)
+    F.fq_grouped_gemm_fwd(dev_bf16(x2), R, dev_i32(seg), (E, N, K), None, wfq, wq, None, y3, ws)
     torch.cuda.synchronize()
     assert torch.equal(y3[0::2].view(torch.int16), y2[0::2].view(torch.int16))
 
@@ -496,6 +498,64 @@ def test_gemm_ragged_tiles_every_launch(N, K):
         assert torch.equal(ys[i].view(torch.int16), ys[0].view(torch.int16)), f"y launch {i}"
         assert torch.equal(dxs[i].view(torch.int16), dxs[0].view(torch.int16)), f"dx launch {i}"
 
+
+
+@pytest.mark.parametrize("E,sizes,N,K", [
+    (1, [300], 1024, 4096),          # FWD 8 tiles in 8 parts, DGRAD 32 tiles in 2 parts
+    (3, [200, 0, 45], 1024, 1520),   # ragged experts, one empty; K zero-padded to 1536:
+                                     # FWD 12 tiles in 3 parts, DGRAD 18 tiles in 2 parts
+    (1, [64], 256, 8192),            # FWD one tile in 8 parts; DGRAD (4 stages) unsplit
+])
+def test_gemm_small_calls_split_along_the_contraction(E, sizes, N, K):
+    """Calls whose 256 x 256 tiles would leave most CUs idle run each tile's
+    contraction (when it is 16 stages of 64 or more) as several parts, the
+    parts' fp32 sums added in part order by a second kernel. Forward and dX
+    against the oracle, bitwise equal from launch to launch, rows past the
+    experts untouched; the forward given no workspace (then unsplit) within
+    the same tolerance."""
+    rng = np.random.default_rng(1200 + N + K + E)
+    seg = _segments(rng, E, sizes)
+    R = int(seg[-1])
+    R_max = R + 16
+    fmt, g = O.FMT_INT8, K
+    w = _rand_w(rng, E, N, K)
+    s, zp, gs = O.observer_weight(w, fmt, g)
+    wq = _wq(fmt, g, s, zp, gs)
+    x = O.f32_to_bf16(rng.standard_normal((R_max, K)).astype(np.float32))
+    dy = O.f32_to_bf16(rng.standard_normal((R_max, N)).astype(np.float32))
+    wd, xd, dyd, segd = dev_bf16(w), dev_bf16(x), dev_bf16(dy), dev_i32(seg)
+    wfq = torch.empty_like(wd)
+    F.fq_quantize_stacked(wd, (E, N, K), wq, wfq)
+    nbf = F.fq_workspace_bytes(F.FQ_OP_GEMM_FWD, (E, N, K), R_max, 0)
+    assert nbf > 0                 # the parts' sums (and the padded copies)
+    ws_f = torch.empty(nbf, dtype=torch.uint8, device="cuda")
+    ws_b = torch.empty(F.fq_workspace_bytes(F.FQ_OP_GEMM_BWD, (E, N, K), R_max, 0),
+                       dtype=torch.uint8, device="cuda")
+    ys, dxs = [], []
+    for _ in range(3):
+        y = torch.full((R_max, N), 7.0, dtype=torch.bfloat16, device="cuda")
+        dx = torch.full((R_max, K), 7.0, dtype=torch.bfloat16, device="cuda")
+        F.fq_grouped_gemm_fwd(xd, R_max, segd, (E, N, K), None, wfq, wq, None, y, ws_f)
+        F.fq_grouped_gemm_bwd_scale(dyd, xd, R_max, segd, (E, N, K), wd, wfq, wq, None, dx, None,
+                                    None, ws_b)
+        ys.append(y)
+        dxs.append(dx)
+    y_one = torch.full((R_max, N), 7.0, dtype=torch.bfloat16, device="cuda")
+    if K % 64 == 0 and N % 256 == 0:
+        F.fq_grouped_gemm_fwd(xd, R_max, segd, (E, N, K), None, wfq, wq, None, y_one, None)
+    else:
+        F.fq_grouped_gemm_fwd(xd, R_max, segd, (E, N, K), None, wfq, wq, None, y_one, ws_f)
+    torch.cuda.synchronize()
+    y_ref = O.grouped_gemm_fwd(x, seg, w, fmt, g, s, zp, gs)
+    dx_ref, _, _ = O.grouped_gemm_bwd(dy, x, seg, w, fmt, g, s, zp, gs)
+    check_gemm_tol(host_bits(ys[0])[:R], y_ref, "y")
+    check_gemm_tol(host_bits(dxs[0])[:R], dx_ref, "dx")
+    check_gemm_tol(host_bits(y_one)[:R], y_ref, "y unsplit")
+    for i in range(1, len(ys)):
+        assert torch.equal(ys[i].view(torch.int16), ys[0].view(torch.int16)), f"y launch {i}"
+        assert torch.equal(dxs[i].view(torch.int16), dxs[0].view(torch.int16)), f"dx launch {i}"
+    assert np.all(bf16_vals(host_bits(ys[0])[R:]) == 7.0)
+    assert np.all(bf16_vals(host_bits(dxs[0])[R:]) == 7.0)
 
 # ------------------------------------------- the expert input as token rows --
 def _routing(rng, T, topk, E, hot=None):

@@ -587,11 +587,12 @@ def test_actfq_bitexact(afmt):
 
 @pytest.mark.parametrize("name,fmt,group", [("nvfp4", O.FMT_NVFP4, 16), ("int4", O.FMT_INT4, 128),
                                             ("fp8", O.FMT_FP8, None)])
-@pytest.mark.parametrize("N,K", [(512, 384), (272, 208)])
+@pytest.mark.parametrize("N,K", [(512, 384), (272, 208), (512, 2048)])
 @pytest.mark.parametrize("prequantized", [True, False])
 def test_gemm_fwd_tokens_is_the_gathered_fwd(name, fmt, group, N, K, prequantized):
     """Routed row r read as token row perm[r] / topk gives the bits of the
-    plain call on the gathered rows, and matches the oracle."""
+    plain call on the gathered rows, and matches the oracle. K = 2048 (32
+    stages over at most 24 tiles) splits the contraction into 4 parts."""
     rng = np.random.default_rng(910 + fmt + N)
     T, topk, E = 400, 4, 6
     if group is not None and K % group:

@@ -39,7 +39,9 @@
 // each expert comes from seg_offsets on the device (a block-wide scan in
 // LDS), so empty experts cost nothing and no host sync is needed. Each of the
 // 8 XCDs owns a contiguous eighth of the tiles, keeping the panels its blocks
-// share in its own L2.
+// share in its own L2. A FWD / DGRAD call too small to fill the CUs runs each
+// tile's contraction as several parts (the SPLIT kernels), whose fp32 sums a
+// second kernel adds in part order.
 #include <atomic>
 #include <type_traits>
 

@@ -505,6 +505,8 @@ def test_gemm_ragged_tiles_every_launch(N, K):
     (3, [200, 0, 45], 1024, 1520),   # ragged experts, one empty; K zero-padded to 1536:
                                      # FWD 12 tiles in 3 parts, DGRAD 18 tiles in 2 parts
     (1, [64], 256, 8192),            # FWD one tile in 8 parts; DGRAD (4 stages) unsplit
+    (2, [150, 90], 512, 1088),       # FWD 17 stages as parts of 9 and 8 (odd, uneven);
+                                     # DGRAD zero-padded to K = 1280, unsplit
 ])
 def test_gemm_small_calls_split_along_the_contraction(E, sizes, N, K):
     """Calls whose 256 x 256 tiles would leave most CUs idle run each tile's

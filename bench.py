@@ -345,6 +345,38 @@ def measured_peaks(torch, dev):
                                     "tile_TFLOP/s": round(tile_tflops, 1)}}
 
 
+def library_gemm(torch, dev, shapes, reps=20):
+    """A vendor-library reference: torch's bf16 GEMM (hipBLASLt) on the
+    forward's shapes, timed in the same run. shapes: (batch, M, N, K) each, a
+    batched product over `batch` equal problems (random operands, the right
+    one contiguous [batch, K, N]); the rate is over all of them together. For
+    the MoE workloads this is the forward of both stacks with every expert
+    given the mean row count: no routing, no ragged tails, no fake-quant."""
+    ops = []
+    for b, m, n, k in shapes:
+        a = torch.randn(b, m, k, device=dev, dtype=torch.bfloat16)
+        w = torch.randn(b, k, n, device=dev, dtype=torch.bfloat16)
+        ops.append((a, w))
+    def run():
+        for a, w in ops:
+            torch.bmm(a, w)
+    for _ in range(3):
+        run()
+    torch.cuda.synchronize()
+    s0 = torch.cuda.Event(enable_timing=True)
+    e0 = torch.cuda.Event(enable_timing=True)
+    s0.record()
+    for _ in range(reps):
+        run()
+    e0.record()
+    torch.cuda.synchronize()
+    ms = s0.elapsed_time(e0) / reps
+    flops = sum(2.0 * b * m * n * k for b, m, n, k in shapes)
+    del ops
+    return {"TFLOP/s": round(flops / (ms * 1e-3) / 1e12, 1), "ms": round(ms, 4),
+            "shapes_batch_m_n_k": [list(t) for t in shapes]}
+
+
 def scattered_rows_floor(torch, dev, rows, row_of, T, topk, H):
     """The floor of the per-token passes over routed rows: a plain kernel with
     their access pattern timed on the same buffers, 16 bytes per thread. Read
@@ -466,6 +498,12 @@ def main():
 
     # the part's own ceilings first, before the workload has heated it
     peaks = None if args.no_peaks else measured_peaks(torch, dev)
+    if peaks:
+        E_l, F2, H_ = case.w_gu.shape
+        local = (case.expert_ids >= case.expert_begin) & (case.expert_ids < case.expert_begin + E_l)
+        rows_e = max(int(local.sum()) // E_l, 1)
+        peaks["library_batched_gemm"] = library_gemm(
+            torch, dev, [(E_l, rows_e, F2, H_), (E_l, rows_e, H_, F2 // 2)])
     layer = F.MoEFakeQuantLayer(w_gu, w_d, fmt, fmt, case.T, case.topk, case.expert_begin, group,
                                 learn_act_scales=learn)
     layer.init_weight_scales()
@@ -544,6 +582,9 @@ def main():
         # partial last rounds and ragged tails included)
         kernels["gemm_fwd"]["pct_of_operand_stream"] = round(
             100 * kernels["gemm_fwd"]["TFLOP/s"] / peaks["gemm_operand_stream"]["tile_TFLOP/s"], 1)
+    if peaks and peaks.get("library_batched_gemm"):
+        kernels["gemm_fwd"]["pct_of_library_batched_gemm"] = round(
+            100 * kernels["gemm_fwd"]["TFLOP/s"] / peaks["library_batched_gemm"]["TFLOP/s"], 1)
 
     # FQ pass over both stacks: read bf16 + write bf16 + read the scales
     nel = E * (2 * Fh * H + H * Fh)
@@ -736,6 +777,8 @@ def dense_main(args):
             fn()
 
     peaks = None if args.no_peaks else measured_peaks(torch, dev)
+    if peaks:
+        peaks["library_batched_gemm"] = library_gemm(torch, dev, [(1, M, N, K)])
     steps = args.steps * (50 if args.config == 1 else 1)   # the latency case: more reps
     for _ in range(args.warmup):
         step()
@@ -755,6 +798,9 @@ def dense_main(args):
                    "TFLOP/s": round(kind_flops / (per[k] * 1e-3) / 1e12, 2)}
                for k in ("gemm_fwd", "gemm_dgrad", "gemm_wgrad_dscale")}
     dom = max(kernels, key=lambda k: kernels[k]["ms_per_step"])
+    if peaks and peaks.get("library_batched_gemm"):
+        kernels["gemm_fwd"]["pct_of_library_batched_gemm"] = round(
+            100 * kernels["gemm_fwd"]["TFLOP/s"] / peaks["library_batched_gemm"]["TFLOP/s"], 1)
     nel = N * K
     scale_bytes = N * G * 4 * (2 if fmt == F.FMT_INT4 else 1)
     fq_bytes = nel * 4 + scale_bytes

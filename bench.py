@@ -346,12 +346,10 @@ def measured_peaks(torch, dev):
 
 
 def library_gemm(torch, dev, shapes, reps=20):
-    """A vendor-library reference: torch's bf16 GEMM (hipBLASLt) on the
-    forward's shapes, timed in the same run. shapes: (batch, M, N, K) each, a
-    batched product over `batch` equal problems (random operands, the right
-    one contiguous [batch, K, N]); the rate is over all of them together. For
-    the MoE workloads this is the forward of both stacks with every expert
-    given the mean row count: no routing, no ragged tails, no fake-quant."""
+    """A vendor-library reference: torch's bf16 GEMM (hipBLASLt) timed in the
+    same run. shapes: (batch, M, N, K) each, a batched product over `batch`
+    equal problems (random operands, both contiguous: [batch, M, K] and
+    [batch, K, N]); the rate is over all of them together."""
     ops = []
     for b, m, n, k in shapes:
         a = torch.randn(b, m, k, device=dev, dtype=torch.bfloat16)
@@ -499,11 +497,16 @@ def main():
     # the part's own ceilings first, before the workload has heated it
     peaks = None if args.no_peaks else measured_peaks(torch, dev)
     if peaks:
+        # each GEMM kind of both stacks with every expert given the mean row
+        # count: no routing, no ragged tails, no fake-quant, and for wgrad the
+        # plain dW product without the dScale epilogue
         E_l, F2, H_ = case.w_gu.shape
         local = (case.expert_ids >= case.expert_begin) & (case.expert_ids < case.expert_begin + E_l)
-        rows_e = max(int(local.sum()) // E_l, 1)
-        peaks["library_batched_gemm"] = library_gemm(
-            torch, dev, [(E_l, rows_e, F2, H_), (E_l, rows_e, H_, F2 // 2)])
+        r = max(int(local.sum()) // E_l, 1)
+        peaks["library_batched_gemm"] = {
+            "gemm_fwd": library_gemm(torch, dev, [(E_l, r, F2, H_), (E_l, r, H_, F2 // 2)]),
+            "gemm_dgrad": library_gemm(torch, dev, [(E_l, r, H_, F2), (E_l, r, F2 // 2, H_)]),
+            "gemm_wgrad_dscale": library_gemm(torch, dev, [(E_l, F2, H_, r), (E_l, H_, F2 // 2, r)])}
     layer = F.MoEFakeQuantLayer(w_gu, w_d, fmt, fmt, case.T, case.topk, case.expert_begin, group,
                                 learn_act_scales=learn)
     layer.init_weight_scales()
@@ -583,8 +586,8 @@ def main():
         kernels["gemm_fwd"]["pct_of_operand_stream"] = round(
             100 * kernels["gemm_fwd"]["TFLOP/s"] / peaks["gemm_operand_stream"]["tile_TFLOP/s"], 1)
     if peaks and peaks.get("library_batched_gemm"):
-        kernels["gemm_fwd"]["pct_of_library_batched_gemm"] = round(
-            100 * kernels["gemm_fwd"]["TFLOP/s"] / peaks["library_batched_gemm"]["TFLOP/s"], 1)
+        for k, ref in peaks["library_batched_gemm"].items():
+            kernels[k]["pct_of_library_batched_gemm"] = round(100 * kernels[k]["TFLOP/s"] / ref["TFLOP/s"], 1)
 
     # FQ pass over both stacks: read bf16 + write bf16 + read the scales
     nel = E * (2 * Fh * H + H * Fh)
@@ -778,7 +781,10 @@ def dense_main(args):
 
     peaks = None if args.no_peaks else measured_peaks(torch, dev)
     if peaks:
-        peaks["library_batched_gemm"] = library_gemm(torch, dev, [(1, M, N, K)])
+        peaks["library_batched_gemm"] = {
+            "gemm_fwd": library_gemm(torch, dev, [(1, M, N, K)]),
+            "gemm_dgrad": library_gemm(torch, dev, [(1, M, K, N)]),
+            "gemm_wgrad_dscale": library_gemm(torch, dev, [(1, N, K, M)])}
     steps = args.steps * (50 if args.config == 1 else 1)   # the latency case: more reps
     for _ in range(args.warmup):
         step()
@@ -799,8 +805,8 @@ def dense_main(args):
                for k in ("gemm_fwd", "gemm_dgrad", "gemm_wgrad_dscale")}
     dom = max(kernels, key=lambda k: kernels[k]["ms_per_step"])
     if peaks and peaks.get("library_batched_gemm"):
-        kernels["gemm_fwd"]["pct_of_library_batched_gemm"] = round(
-            100 * kernels["gemm_fwd"]["TFLOP/s"] / peaks["library_batched_gemm"]["TFLOP/s"], 1)
+        for k, ref in peaks["library_batched_gemm"].items():
+            kernels[k]["pct_of_library_batched_gemm"] = round(100 * kernels[k]["TFLOP/s"] / ref["TFLOP/s"], 1)
     nel = N * K
     scale_bytes = N * G * 4 * (2 if fmt == F.FMT_INT4 else 1)
     fq_bytes = nel * 4 + scale_bytes

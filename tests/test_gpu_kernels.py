@@ -559,6 +559,57 @@ def test_gemm_small_calls_split_along_the_contraction(E, sizes, N, K):
     assert np.all(bf16_vals(host_bits(ys[0])[R:]) == 7.0)
     assert np.all(bf16_vals(host_bits(dxs[0])[R:]) == 7.0)
 
+
+@pytest.mark.parametrize("seed", range(8))
+def test_gemm_split_random_shapes(seed):
+    """Seeded random small calls with long contractions (mostly split along
+    it: 1-5 experts, ragged and empty segments, N and K multiples of 16 that
+    the calls zero-pad, 16-96 stages): forward and dX against the oracle,
+    and the forward given no workspace (unsplit where the shape is
+    tile-aligned) within the same tolerance."""
+    rng = np.random.default_rng(1300 + seed)
+    E = int(rng.integers(1, 6))
+    sizes = [int(v) for v in rng.integers(0, 400, E)]
+    sizes[int(rng.integers(0, E))] = int(rng.integers(1, 300))      # at least one non-empty expert
+    if E > 2:
+        sizes[int(rng.integers(0, E))] = 0                            # an empty one
+    N = int(rng.choice([256, 512, 272, 768, 1040]))
+    K = int(rng.choice([1024, 1536, 2048, 3072, 6144, 1488, 2064]))
+    seg = _segments(rng, E, sizes)
+    R = int(seg[-1])
+    R_max = R + int(rng.integers(0, 40))
+    fmt, g = O.FMT_INT8, K
+    w = _rand_w(rng, E, N, K)
+    s_, zp, gs = O.observer_weight(w, fmt, g)
+    wq = _wq(fmt, g, s_, zp, gs)
+    x = O.f32_to_bf16(rng.standard_normal((R_max, K)).astype(np.float32))
+    dy = O.f32_to_bf16(rng.standard_normal((R_max, N)).astype(np.float32))
+    wd, xd, dyd, segd = dev_bf16(w), dev_bf16(x), dev_bf16(dy), dev_i32(seg)
+    wfq = torch.empty_like(wd)
+    F.fq_quantize_stacked(wd, (E, N, K), wq, wfq)
+    ws_f = torch.empty(max(F.fq_workspace_bytes(F.FQ_OP_GEMM_FWD, (E, N, K), R_max, 0), 1),
+                       dtype=torch.uint8, device="cuda")
+    ws_b = torch.empty(F.fq_workspace_bytes(F.FQ_OP_GEMM_BWD, (E, N, K), R_max, 0),
+                       dtype=torch.uint8, device="cuda")
+    y = torch.full((R_max, N), 7.0, dtype=torch.bfloat16, device="cuda")
+    dx = torch.full((R_max, K), 7.0, dtype=torch.bfloat16, device="cuda")
+    F.fq_grouped_gemm_fwd(xd, R_max, segd, (E, N, K), None, wfq, wq, None, y, ws_f)
+    F.fq_grouped_gemm_bwd_scale(dyd, xd, R_max, segd, (E, N, K), wd, wfq, wq, None, dx, None,
+                                None, ws_b)
+    y_one = torch.full((R_max, N), 7.0, dtype=torch.bfloat16, device="cuda")
+    aligned = K % 64 == 0 and N % 256 == 0
+    F.fq_grouped_gemm_fwd(xd, R_max, segd, (E, N, K), None, wfq, wq, None, y_one,
+                          None if aligned else ws_f)
+    torch.cuda.synchronize()
+    y_ref = O.grouped_gemm_fwd(x, seg, w, fmt, g, s_, zp, gs)
+    dx_ref, _, _ = O.grouped_gemm_bwd(dy, x, seg, w, fmt, g, s_, zp, gs)
+    case = f"E={E} sizes={sizes} N={N} K={K} R_max={R_max}"
+    check_gemm_tol(host_bits(y)[:R], y_ref, f"y ({case})")
+    check_gemm_tol(host_bits(dx)[:R], dx_ref, f"dx ({case})")
+    check_gemm_tol(host_bits(y_one)[:R], y_ref, f"y unsplit ({case})")
+    assert np.all(bf16_vals(host_bits(y)[R:]) == 7.0), case
+    assert np.all(bf16_vals(host_bits(dx)[R:]) == 7.0), case
+
 # ------------------------------------------- the expert input as token rows --
 def _routing(rng, T, topk, E, hot=None):
     """Routing over E local experts (expert 1 empty; `hot` takes most rows)."""

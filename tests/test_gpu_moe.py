@@ -60,6 +60,16 @@ def test_moe_layer_stagewise_and_end_to_end(name, wfmt, afmt, group, T, Eg, El, 
 
 
 @pytest.mark.parametrize("name,wfmt,afmt,group", [("nvfp4", O.FMT_NVFP4, O.FMT_NVFP4, 16),
+                                                   ("fp8", O.FMT_FP8, O.FMT_FP8, None)])
+def test_moe_layer_small_calls_split_the_contraction(name, wfmt, afmt, group):
+    """A small layer (200 tokens x top-4 over 8 experts) with H = 1024 and
+    F = 512: the gate_up forward (routed X) and both dgrads have too few
+    tiles for the CUs and 16 stages each, so they run split along the
+    contraction; every stage still matches the oracle."""
+    _check_layer(name + "-split", wfmt, afmt, group, 200, 8, 8, 0, None, False, 1024, 512)
+
+
+@pytest.mark.parametrize("name,wfmt,afmt,group", [("nvfp4", O.FMT_NVFP4, O.FMT_NVFP4, 16),
                                                   ("w8a8-int8", O.FMT_INT8, O.FMT_INT8, None)])
 def test_moe_layer_ffn_not_multiple_of_256(name, wfmt, afmt, group):
     """The whole layer with hidden 272 and expert FFN 208 (2F = 416): every

@@ -1231,10 +1231,6 @@ static size_t rowtile_units(int R_max, int E, int n_it) {
   return rowtile_bound(R_max, E) * (size_t)n_it;
 }
 
-// FWD / DGRAD split along the contraction. A call whose tiles would leave at
-// least half of the CUs idle runs each tile as S = CUs / units parts (at most
-// 8, each at least 8 stages), all tiles' parts in one grid; the parts' fp32
-// sums are added in part order afterwards. 1 = no split.
 // S parts asked for, at most 8 and at least 8 stages each (the sums' second
 // pass costs about as much as two stages), as the parts of ceil(nk / S)
 // stages that cover nk stages
@@ -1245,6 +1241,10 @@ static int ksplit_parts(int S, int nk) {
   const int per = (nk + S - 1) / S;
   return (nk + per - 1) / per;
 }
+// FWD / DGRAD split along the contraction. A call whose tiles would leave at
+// least half of the CUs idle runs each tile as S = CUs / units parts (see
+// ksplit_parts), all tiles' parts in one grid; the parts' fp32 sums are added
+// in part order afterwards. 1 = no split.
 static int ksplit_for_units(size_t units, int nk) {
   const int cus = device_cus();
   if (units == 0 || units * 2 > (size_t)cus) return 1;
@@ -1258,8 +1258,6 @@ size_t gemm_ksplit_bytes(bool fwd, fq_shape s, int R_max) {
   return S > 1 ? (size_t)S * (size_t)R_max * (size_t)ldo * 4 : 0;
 }
 
-// launches the row-tile kernel, split along the contraction when the call is
-// small enough (then `part` holds the parts' sums and a reduce writes `out`)
 // Row tiles per group of the tile order: with T tiles in flight per XCD,
 // about sqrt(T) (a square block), but 1 (i fastest) unless a row tile has at
 // least twice that many i tiles; otherwise the tiles in flight already span
@@ -1271,6 +1269,8 @@ static int rowtile_group(int grid, int S, int n_it) {
   return n_it >= 2 * g ? g : 1;
 }
 
+// launches the row-tile kernel, split along the contraction when the call is
+// small enough (then `part` holds the parts' sums and a reduce writes `out`)
 template <int MODE, bool ROUTED>
 static void launch_rowtile_gemm(GemmArgs &a, int R_max, float *part, hipStream_t st) {
   const size_t units = rowtile_units(R_max, a.E, a.n_it);
